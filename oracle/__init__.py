@@ -1,0 +1,63 @@
+"""Oracle for paged decode attention and the paged KV-cache writes.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it.  The library under ``paged_kv_cache_29_amd/`` never imports,
+links or calls anything here, and this package imports nothing from it: the
+two share no code.  The only thing both sides consume is the seeded input
+data built by ``paged_kv_cache_29_amd.workloads``, which holds none of the
+method's arithmetic.
+
+Everything here is a plain, slow, obviously-correct CPU definition:
+
+* floating point is fp64, except the int8 quantiser, which is fp32 on purpose
+  (its result is an integer code, so both sides must decide it in the same
+  precision);
+* gathers go through the block table one logical block at a time;
+* attention is the textbook ``softmax(scale * K q) V`` per query head.
+
+Sources (web pages, cited by title and section):
+
+* [ENG5] "LLM Engineering (5): core techniques of inference optimization"
+  (chenk.top), sections "Two phases with very different characteristics",
+  "Paged attention", "Block manager: how paging works",
+  "INT8 weight-only quantization" and "KV-cache quantization".
+* [LAYERS] the four-layer inference-optimization article (gsyq.cn/news/366077),
+  section 2.1 (KV-cache size formula and its 7B worked number), 2.2
+  (PagedAttention, block size 16/32) and 2.3 (KV-cache quantization with
+  per-token scales, K and V quantized separately).
+
+Parity status: every function below is pinned by ``-m "not gpu"`` tests in
+``tests/test_oracle_pins.py`` (worked examples, closed forms, brute force,
+a library routine) and ``tests/test_oracle_mutations.py`` (planted mistakes
+are caught).  No function is "parity unpinned".
+"""
+
+from .attention import (
+    n_blocks,
+    rows_in_block,
+    token_location,
+    kv_head_of,
+    widen,
+    gather_kv,
+    attend_one,
+    decode_attention,
+)
+from .cache import cache_write, quantize_int8, cache_write_int8
+from .closed_forms import kv_cache_bytes, decode_kv_bytes
+
+__all__ = [
+    "n_blocks",
+    "rows_in_block",
+    "token_location",
+    "kv_head_of",
+    "widen",
+    "gather_kv",
+    "attend_one",
+    "decode_attention",
+    "cache_write",
+    "quantize_int8",
+    "cache_write_int8",
+    "kv_cache_bytes",
+    "decode_kv_bytes",
+]

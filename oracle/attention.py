@@ -1,0 +1,176 @@
+"""fp64 definition of single-token decode attention over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+What is computed, and where the pages fix it:
+
+* The KV cache lives in fixed-size physical blocks of ``block_size`` tokens,
+  and each sequence owns a block table mapping its logical blocks to physical
+  ones, like OS page tables ([ENG5] "Paged attention").  A request of 47 tokens
+  occupies 3 blocks filled 16+16+15; only the last block can be partial
+  ([ENG5] "Paged attention", worked example and the near-zero-waste remark).
+* A decode step attends the one new query token of each sequence over all of
+  that sequence's cached keys and values ([ENG5] "Two phases with very
+  different characteristics": every decode step reads the whole KV cache).
+* Attention itself is the textbook ``out = softmax(scale * K q) V`` per query
+  head, over the sequence's ``context_len`` tokens.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+
+* Cache layout (the pages print sizes, not an order): ``k_cache`` is
+  ``[num_blocks, num_kv_heads, block_size, head_dim]`` (each token a row) and
+  ``v_cache`` is ``[num_blocks, num_kv_heads, head_dim, block_size]`` (each
+  tile stored dim-major).  The oracle reads both by index, token by token
+  within a block, so its arithmetic does not depend on the layout.
+* GQA grouping: query head ``h`` reads kv-head ``h // (H / Hkv)``.
+* ``context_len == 0`` gives an all-zero output row.
+* int8 cache: the value of a stored code ``c`` with scale ``s`` is ``c * s``
+  ([LAYERS] 2.3, per-token scales; [ENG5] "KV-cache quantization",
+  per-token-per-head scales), evaluated exactly in fp64.
+* bf16 elements are given as their 16-bit patterns (``uint16``); their value
+  is the fp32 number whose upper half is that pattern.
+"""
+
+import numpy as np
+
+KV_DTYPES = ("f32", "bf16", "i8")
+
+
+def n_blocks(context_len, block_size):
+    """Number of physical blocks a sequence of ``context_len`` tokens occupies.
+
+    ceil(L / bs): 47 tokens -> 3 blocks, 200 tokens -> 13 blocks at bs = 16
+    ([ENG5] "Paged attention", worked example).
+    """
+    context_len = int(context_len)
+    block_size = int(block_size)
+    if context_len <= 0:
+        return 0
+    return (context_len + block_size - 1) // block_size
+
+
+def rows_in_block(context_len, block_size, j):
+    """Valid token rows held by logical block ``j`` of a sequence.
+
+    Every block but the last is full; the last holds ``L - (n - 1) * bs``
+    ([ENG5] "Paged attention": only the last block may be partial).
+    """
+    n = n_blocks(context_len, block_size)
+    if j < 0 or j >= n:
+        return 0
+    if j < n - 1:
+        return int(block_size)
+    return int(context_len) - (n - 1) * int(block_size)
+
+
+def token_location(t, block_table, block_size):
+    """(physical block, row) that holds logical token ``t`` of a sequence.
+
+    The block table maps logical block ``t // bs`` to a physical block; the
+    token sits at row ``t % bs`` inside it ([ENG5] "Paged attention").
+    """
+    t = int(t)
+    block_size = int(block_size)
+    return int(block_table[t // block_size]), t % block_size
+
+
+def kv_head_of(h, num_heads, num_kv_heads):
+    """KV head read by query head ``h``: contiguous groups of ``H / Hkv``."""
+    group = int(num_heads) // int(num_kv_heads)
+    return int(h) // group
+
+
+def widen(x, kind):
+    """Exact fp64 value of stored elements ``x`` of element type ``kind``."""
+    x = np.asarray(x)
+    if kind == "bf16":
+        bits = x.astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if kind == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    if kind == "i8":
+        return x.astype(np.int8).astype(np.float64)
+    raise ValueError(f"unknown element type {kind!r}")
+
+
+def gather_kv(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+              kv_dtype, k_scale=None, v_scale=None):
+    """Contiguous fp64 ``K[L, D]`` and ``V[L, D]`` of one sequence and kv-head.
+
+    Walks the sequence's logical blocks in order; logical block ``j`` lives in
+    physical block ``block_table[j]`` and contributes its first
+    ``rows_in_block(L, bs, j)`` rows.  Table entries past the last logical
+    block are never read.  For an int8 cache each element's value is its code
+    times its token's scale.
+    """
+    L = int(context_len)
+    bs = int(block_size)
+    D = k_cache.shape[-1]
+    K = np.zeros((L, D), dtype=np.float64)
+    V = np.zeros((L, D), dtype=np.float64)
+    for j in range(n_blocks(L, bs)):
+        rows = rows_in_block(L, bs, j)
+        blk = int(block_table[j])
+        k_rows = widen(k_cache[blk, kv_head, :rows, :], kv_dtype)        # [rows, D]
+        v_rows = widen(v_cache[blk, kv_head, :, :rows], kv_dtype).T      # [rows, D]
+        if kv_dtype == "i8":
+            ks = np.asarray(k_scale[blk, kv_head, :rows], dtype=np.float32).astype(np.float64)
+            vs = np.asarray(v_scale[blk, kv_head, :rows], dtype=np.float32).astype(np.float64)
+            k_rows = k_rows * ks[:, None]
+            v_rows = v_rows * vs[:, None]
+        K[j * bs: j * bs + rows] = k_rows
+        V[j * bs: j * bs + rows] = v_rows
+    return K, V
+
+
+def attend_one(q_vec, K, V, scale):
+    """Textbook attention of one query vector over contiguous K, V (fp64).
+
+    ``s = scale * K q``; ``p = exp(s - max s)``; ``out = (p V) / sum(p)``.
+    Subtracting the maximum does not change the result and keeps exp finite.
+    An empty context gives zeros.
+    """
+    q_vec = np.asarray(q_vec, dtype=np.float64)
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    s = float(scale) * (K @ q_vec)
+    p = np.exp(s - s.max())
+    return (p @ V) / p.sum()
+
+
+def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
+                     num_heads, num_kv_heads, head_dim, block_size,
+                     kv_dtype, q_dtype, k_scale=None, v_scale=None,
+                     samples=None):
+    """fp64 decode attention for a batch of sequences (one query token each).
+
+    Shapes: ``q[B, H, D]``; ``k_cache[NB, Hkv, bs, D]``;
+    ``v_cache[NB, Hkv, D, bs]``; ``block_tables[B, MB]``; ``context_lens[B]``;
+    int8 scales ``[NB, Hkv, bs]``.  ``q_dtype`` / ``kv_dtype`` name the stored
+    element types ("f32", "bf16", "i8").
+
+    Returns ``out[B, H, D]`` in fp64.  With ``samples`` (an iterable of
+    ``(b, h)`` pairs) only those rows are computed and the others are NaN.
+    """
+    if kv_dtype not in KV_DTYPES:
+        raise ValueError(kv_dtype)
+    H, Hkv, D = int(num_heads), int(num_kv_heads), int(head_dim)
+    if H % Hkv != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    B = len(context_lens)
+    if samples is None:
+        out = np.zeros((B, H, D), dtype=np.float64)
+        wanted = {(b, h) for b in range(B) for h in range(H)}
+    else:
+        out = np.full((B, H, D), np.nan, dtype=np.float64)
+        wanted = {(int(b), int(h)) for b, h in samples}
+    by_group = {}
+    for b, h in wanted:
+        by_group.setdefault((b, kv_head_of(h, H, Hkv)), []).append(h)
+    for (b, g), heads in sorted(by_group.items()):
+        K, V = gather_kv(k_cache, v_cache, block_tables[b], context_lens[b],
+                         block_size, g, kv_dtype, k_scale, v_scale)
+        for h in heads:
+            q_vec = widen(q[b, h, :D], q_dtype)
+            out[b, h] = attend_one(q_vec, K, V, scale)
+    return out

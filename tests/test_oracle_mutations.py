@@ -1,0 +1,139 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and require a pin to fail.
+
+A pin suite that passes a broken oracle proves nothing; each mutation below is
+an error a careful reader could still make (a transposed operand, a dropped
+term, an off-by-one, a wrong rounding rule), and at least one check in
+``oracle_pin_checks.ALL_CHECKS`` must reject it.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as oatt
+from oracle import cache as ocache
+from oracle_pin_checks import ALL_CHECKS
+
+
+def _gather_table_off_by_one(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                             kv_dtype, k_scale=None, v_scale=None):
+    L, bs = int(context_len), int(block_size)
+    D = k_cache.shape[-1]
+    K = np.zeros((L, D))
+    V = np.zeros((L, D))
+    for j in range(oatt.n_blocks(L, bs)):
+        rows = oatt.rows_in_block(L, bs, j)
+        blk = int(block_table[min(j + 1, len(block_table) - 1)])
+        K[j * bs:j * bs + rows] = oatt.widen(k_cache[blk, kv_head, :rows, :], kv_dtype)
+        V[j * bs:j * bs + rows] = oatt.widen(v_cache[blk, kv_head, :, :rows], kv_dtype).T
+    return K, V
+
+
+def _gather_no_v_scale(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                       kv_dtype, k_scale=None, v_scale=None):
+    if kv_dtype == "i8":
+        v_scale = np.ones_like(v_scale)
+    return _orig_gather(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                        kv_dtype, k_scale, v_scale)
+
+
+def _gather_v_rows_as_columns(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                              kv_dtype, k_scale=None, v_scale=None):
+    # reads V tiles as if they were stored token-major like K (a transposed operand)
+    K, _ = _orig_gather(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                        kv_dtype, k_scale, v_scale)
+    L, bs = int(context_len), int(block_size)
+    D = v_cache.shape[2]
+    V = np.zeros((L, D))
+    for j in range(oatt.n_blocks(L, bs)):
+        rows = oatt.rows_in_block(L, bs, j)
+        blk = int(block_table[j])
+        flat = oatt.widen(v_cache[blk, kv_head], kv_dtype).reshape(-1)   # [D * bs]
+        V[j * bs:j * bs + rows] = flat.reshape(bs, D)[:rows]
+    return K, V
+
+
+def _attend_no_scale(q_vec, K, V, scale):
+    return _orig_attend(q_vec, K, V, 1.0)
+
+
+def _attend_mean_norm(q_vec, K, V, scale):
+    s = scale * (K @ np.asarray(q_vec, np.float64))
+    p = np.exp(s - s.max())
+    return (p @ V) / len(p)
+
+
+def _attend_keys_as_values(q_vec, K, V, scale):
+    return _orig_attend(q_vec, K, K, scale)
+
+
+def _quant_half_away(x):
+    x = np.asarray(x, np.float32)
+    a = np.max(np.abs(x), axis=-1)
+    s = (a / np.float32(127)).astype(np.float32)
+    safe = np.where(a > 0, s, np.float32(1)).astype(np.float32)
+    r = (x / safe[..., None]).astype(np.float32)
+    c = np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -127, 127)
+    c = np.where(a[..., None] > 0, c, 0).astype(np.int8)
+    return c, np.where(a > 0, s, 0).astype(np.float32)
+
+
+def _quant_scale_128(x):
+    x = np.asarray(x, np.float32)
+    a = np.max(np.abs(x), axis=-1)
+    s = (a / np.float32(128)).astype(np.float32)
+    safe = np.where(a > 0, s, np.float32(1)).astype(np.float32)
+    c = np.clip(np.rint((x / safe[..., None]).astype(np.float32)), -127, 127)
+    c = np.where(a[..., None] > 0, c, 0).astype(np.int8)
+    return c, np.where(a > 0, s, 0).astype(np.float32)
+
+
+def _cache_write_row_shift(k, v, k_cache, v_cache, slot_mapping, block_size):
+    shifted = np.where(np.asarray(slot_mapping) >= 0, np.asarray(slot_mapping) + 1, -1)
+    return _orig_cache_write(k, v, k_cache, v_cache, shifted, block_size)
+
+
+def _widen_bf16_shift15(x, kind):
+    if kind == "bf16":
+        bits = np.asarray(x).astype(np.uint32) << np.uint32(15)
+        return bits.view(np.float32).astype(np.float64)
+    return _orig_widen(x, kind)
+
+
+_orig_gather = oatt.gather_kv
+_orig_attend = oatt.attend_one
+_orig_widen = oatt.widen
+_orig_cache_write = ocache.cache_write
+
+MUTATIONS = {
+    "gqa_interleaved_heads": [(oatt, "kv_head_of", lambda h, H, Hkv: int(h) % int(Hkv))],
+    "last_block_one_row_too_many": [
+        (oatt, "rows_in_block",
+         lambda L, bs, j: 0 if (j < 0 or j >= oatt.n_blocks(L, bs)) else min(int(bs), int(L) - j * int(bs) + 1))],
+    "block_count_floor": [(oatt, "n_blocks", lambda L, bs: int(L) // int(bs))],
+    "block_table_off_by_one": [(oatt, "gather_kv", _gather_table_off_by_one)],
+    "v_tile_read_token_major": [(oatt, "gather_kv", _gather_v_rows_as_columns)],
+    "int8_v_scale_dropped": [(oatt, "gather_kv", _gather_no_v_scale)],
+    "scale_dropped": [(oatt, "attend_one", _attend_no_scale)],
+    "normalised_by_length": [(oatt, "attend_one", _attend_mean_norm)],
+    "keys_used_as_values": [(oatt, "attend_one", _attend_keys_as_values)],
+    "bf16_widen_wrong_shift": [(oatt, "widen", _widen_bf16_shift15)],
+    "quant_round_half_away": [(ocache, "quantize_int8", _quant_half_away)],
+    "quant_scale_over_128": [(ocache, "quantize_int8", _quant_scale_128)],
+    "cache_write_row_shift": [(ocache, "cache_write", _cache_write_row_shift)],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    for module, attr, repl in MUTATIONS[name]:
+        monkeypatch.setattr(module, attr, repl)
+        if hasattr(oracle, attr):
+            monkeypatch.setattr(oracle, attr, repl)
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check()
+        except Exception:  # AssertionError or a shape error caused by the mistake
+            failed.append(check.__name__)
+    assert failed, f"mutation {name!r} passed every pin"
