@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for paged KV-cache attention on one MI355X.
+
+One step = the hot path once over one batch: write each sequence's new
+token into its tail-block slot (kv_cache_write, or the int8 quantising write)
+then attend every sequence's new query over its whole paged context
+(paged_attention_decode: the partition kernel, then the split-context
+reduce).  Inputs are seeded synthetic data already resident in HBM.
+
+Prints ONE JSON line.  ``value`` is the KV bytes a step must read divided by
+the measured step time (GB/s) on the 7B-shaped MHA workload (batch 32,
+2048-token contexts, 32 heads x 128 dims, bf16, 16-token blocks).  The
+70B-shaped GQA workloads (bf16, and int8 KV) are reported under
+``secondary``.  Per-kernel times come from HIP events recorded on the
+stream the kernels run on.
+
+Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1),
+--configs (which workloads), --partition-tokens, --cpu-seconds (bound of the
+CPU oracle baseline; 0 disables it), --copy-calibration (only run a 1 GiB
+device copy, for scaling rocprofv3 byte counters).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "paged decode-attn KV read GB/s (% of HBM peak) + µs/step, 7B & 70B shapes"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+KERNEL_SOURCES = ["decode_mfma.hip", "pkv_device.hpp", "pkv_kernels.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.txt")
+
+DESCRIPTIONS = {
+    1: "tiny_f32: B=4 L={47,200,16,1} H=Hkv=4 D=64 bs=16 fp32",
+    2: "mha7b_bf16: B=32 L=2048 H=Hkv=32 D=128 bs=16 bf16",
+    3: "gqa70b_bf16: B=50 L~logU[1024,32768] H=64 Hkv=8 D=128 bs=16 bf16",
+    4: "prefix_bf16: B=256 shared 2000-token prefix + U{50..500} H=32 Hkv=8 D=128",
+    5: "int8_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 int8 KV, bf16 q",
+}
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_29_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_name):
+    """HBM bytes per launch of the partition kernel from the committed counter
+    summary, or None if absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha = kernel_source_sha()
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            m = re.match(r"^TRAFFIC\s+(\S+)\s+(\S+)\s+(\d+)\s+(\d+)\s*$", line.strip())
+            if m and m.group(1) == workload_name and m.group(2) == sha:
+                return int(m.group(3)) + int(m.group(4))
+    return None
+
+
+def kv_bytes(w):
+    elem = 1 if w.kv_dtype == "i8" else (4 if w.kv_dtype == "f32" else 2)
+    scale = 4 if w.kv_dtype == "i8" else 0
+    return 2 * w.num_kv_heads * (w.head_dim * elem + scale) * w.attended_tokens
+
+
+def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
+    w = workloads.make_config(cfg, seed=0, block_size=block_size)
+    dev = torch.device("cuda:0")
+    store = "bf16" if w.kv_dtype == "bf16" else "f32"
+
+    def up(a, kind):
+        import numpy as np
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if kind == "bf16" else torch.from_numpy(a)
+        return t.to(dev)
+
+    q = up(w.q, w.q_dtype)
+    bt = torch.from_numpy(w.block_tables).to(dev)
+    cl = torch.from_numpy(w.context_lens).to(dev)
+    slot = torch.from_numpy(w.slot_new).to(dev)
+    k_new, v_new = up(w.k_new, store), up(w.v_new, store)
+    ks = vs = None
+    if w.kv_dtype == "i8":
+        NB, Hkv, bs, D = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
+        kc = torch.zeros((NB, Hkv, bs, D), dtype=torch.int8, device=dev)
+        vc = torch.zeros((NB, Hkv, D, bs), dtype=torch.int8, device=dev)
+        ks = torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=dev)
+        vs = torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=dev)
+        kf, vf, sf = up(w.k_fill, "f32"), up(w.v_fill, "f32"), torch.from_numpy(w.slot_fill).to(dev)
+        pkv.kv_cache_write_int8(kf, vf, kc, vc, ks, vs, sf)   # fill the cache once
+        torch.cuda.synchronize()
+        del kf, vf, sf
+    else:
+        kc, vc = up(w.k_cache, store), up(w.v_cache, store)
+    out = torch.empty_like(q)
+    pt = args.partition_tokens
+    need = pkv.workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                              w.block_tables.shape[1], pt)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    dargs = (out, q, kc, vc, bt, cl, w.scale, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size)
+    dkw = dict(k_scale=ks, v_scale=vs, partition_tokens=pt, workspace=ws)
+
+    def write():
+        if w.kv_dtype == "i8":
+            pkv.kv_cache_write_int8(k_new, v_new, kc, vc, ks, vs, slot)
+        else:
+            pkv.kv_cache_write(k_new, v_new, kc, vc, slot)
+
+    def step(evs=None):
+        if evs:
+            evs[0].record()
+        write()
+        if evs:
+            evs[1].record()
+        pkv.paged_attention_decode_partitions(*dargs, **dkw)
+        if evs:
+            evs[2].record()
+        pkv.paged_attention_decode_reduce(*dargs, **dkw)
+        if evs:
+            evs[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step time: K back-to-back steps between two events
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    # per-kernel times: events between the launches, same stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    per = [[e[i].elapsed_time(e[i + 1]) * 1e3 for i in range(3)] for e in evs]
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    write_us = med([p[0] for p in per])
+    part_us = [p[1] for p in per]
+    red_us = med([p[2] for p in per])
+    part_avg = sum(part_us) / len(part_us)
+    nbytes = kv_bytes(w)
+    res = {
+        "workload": DESCRIPTIONS[cfg] + (f" bs={block_size}" if block_size else ""),
+        "name": w.name,
+        "kv_bytes_per_step": nbytes,
+        "attended_tokens": w.attended_tokens,
+        "us_per_step": ms_per_step * 1e3,
+        "kv_gbs": nbytes / (ms_per_step * 1e-3) / 1e9,
+        "pct_hbm_peak": 100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "tokens_per_s": w.attended_tokens / (ms_per_step * 1e-3),
+        "kernel_us": {"kv_cache_write": write_us, "decode_partitions_avg": part_avg,
+                      "decode_partitions_median": med(part_us), "decode_reduce": red_us},
+        "partition_tokens": pkv.partition_tokens(w.num_seqs, w.num_kv_heads, w.block_size,
+                                                 w.block_tables.shape[1], pt),
+    }
+    achieved = nbytes / (part_avg * 1e-6) / 1e9
+    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(w.name),
+                       "kernel": "decode_mfma_kernel" if w.kv_dtype != "f32" else "decode_f32_kernel"}
+    res["_w"] = w
+    return res
+
+
+def cpu_baseline(w, seconds):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import oracle
+    from oracle import cache as ocache
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    kc, vc = ocache.cache_write(w.k_new, w.v_new, w.k_cache, w.v_cache, w.slot_new, w.block_size)
+    done_tokens = 0
+    done_seqs = 0
+    t_start = time.perf_counter()
+    b = 0
+    while b < w.num_seqs:
+        oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.num_heads,
+                                w.num_kv_heads, w.head_dim, w.block_size, w.kv_dtype, w.q_dtype,
+                                samples=[(b, h) for h in range(w.num_heads)])
+        done_tokens += int(w.context_lens[b])
+        done_seqs += 1
+        b += 1
+        if time.perf_counter() - t_start >= seconds:
+            break
+    el = time.perf_counter() - t_start
+    elem = 4 if w.kv_dtype == "f32" else 2
+    nbytes = 2 * w.num_kv_heads * w.head_dim * elem * done_tokens
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done_seqs} of {w.num_seqs} sequences x all {w.num_heads} heads "
+                      f"({done_tokens} context tokens) of {w.name}, {el:.1f} s; "
+                      f"cpu_count={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"}
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_dispatch": n,
+                      "copy_calibration_bytes_written_per_dispatch": n}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--configs", default="2,3,5", help="first is the headline workload")
+    ap.add_argument("--block-size", type=int, default=None, help="for config 4")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path; the per-GPU kernel is what is measured.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+    sys.path.insert(0, ROOT)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return 0
+    import paged_kv_cache_29_amd as pkv
+    from paged_kv_cache_29_amd import workloads
+    pkv.load_library()
+    cfgs = [int(c) for c in args.configs.split(",") if c]
+    results = []
+    for c in cfgs:
+        print(f"[bench] config {c} ...", file=sys.stderr, flush=True)
+        r = run_workload(c, args, torch, pkv, workloads, args.block_size if c == 4 else None)
+        print(f"[bench] config {c}: {r['us_per_step']:.1f} us/step, {r['kv_gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        results.append(r)
+        torch.cuda.empty_cache()
+    head = results[0]
+    w = head.pop("_w")
+    for r in results[1:]:
+        r.pop("_w")
+    line = {
+        "metric": METRIC,
+        "value": round(head["kv_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["us_per_step"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "i8": "i8", "f32": "f32"}[w.kv_dtype],
+        "data": "synthetic (seeded N(0,1) K/V/q, shuffled block tables)",
+        "config": {"workload": head["workload"], "num_seqs": w.num_seqs,
+                   "context_len": int(w.context_lens.max()), "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "partition_tokens": head["partition_tokens"]},
+        "us_per_step": head["us_per_step"],
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "tokens_per_s": head["tokens_per_s"],
+        "kv_bytes_per_step": head["kv_bytes_per_step"],
+        "kernel_us": head["kernel_us"],
+        "roofline": head["roofline"],
+        "kernel_source_sha": kernel_source_sha(),
+        "secondary": [{k: v for k, v in r.items()} for r in results[1:]],
+    }
+    if args.cpu_seconds > 0 and w.kv_dtype != "i8":
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,193 @@
+/*
+ * pagedkv — paged KV cache decode attention for AMD MI355X (gfx950).
+ *
+ * C ABI of libpagedkv.so.  Every pointer argument is device memory owned by
+ * the caller unless stated otherwise; the library never allocates, frees or
+ * retains a pointer after a call returns.  Every call is asynchronous on the
+ * given HIP stream (a hipStream_t passed as void*, NULL = the default stream)
+ * and never synchronises it.  A non-OK return launches nothing and has no
+ * side effects, except PKV_ERR_HIP, which reports a failed launch.  Errors
+ * that happen while a kernel runs surface at the caller's next
+ * synchronisation.  pkv_last_error() gives the text of the last failure on
+ * the calling thread.
+ *
+ * Sources the operations follow (web pages, cited by title and section):
+ *   [ENG5]   "LLM Engineering (5): core techniques of inference
+ *            optimization" (chenk.top): "Two phases with very different
+ *            characteristics" (decode reads the whole KV cache each step),
+ *            "Paged attention" (fixed 16-token blocks, per-sequence block
+ *            tables, 47 tokens -> 16+16+15), "Block manager: how paging
+ *            works" (append a block to the table, copy-on-write sharing),
+ *            "KV-cache quantization" (per-token-per-head scales computed
+ *            online), "INT8 weight-only quantization" (q = round(x / s)).
+ *   [LAYERS] four-layer inference-optimization article
+ *            (gsyq.cn/news/366077), 2.2 (block size 16 or 32) and 2.3
+ *            (per-token scales; K and V quantized separately).
+ *
+ * Data layout (shared by all entry points).  Notation: NB = num_blocks,
+ * Hkv = num_kv_heads, bs = block_size, D = head_dim, H = num_heads,
+ * G = H / Hkv, B = num_seqs, MB = max_blocks_per_seq, T = num_tokens.
+ *   k_cache      [NB][Hkv][bs][D]   one row of D elements per token
+ *   v_cache      [NB][Hkv][D][bs]   each (block, kv-head) tile dim-major:
+ *                                   element (token row r, dim d) at d*bs + r
+ *   k_scale,
+ *   v_scale      [NB][Hkv][bs] fp32 (int8 caches only)
+ *   block_tables [B][MB] int32      logical block j of sequence b lives in
+ *                                   physical block block_tables[b*MB + j];
+ *                                   entries past the sequence's last block
+ *                                   are never read
+ *   context_lens [B] int32          tokens to attend, including the newest
+ *   slot_mapping [T] int64          slot = physical_block * bs + row; < 0: skip
+ *   q, out       [B][H][D]          query head h reads kv-head h / G
+ *   new k, v     [T][Hkv][D]
+ * All arrays are dense and row-major with exactly these shapes.
+ *
+ * Device-data preconditions that are NOT checked (a violation is undefined
+ * behaviour, typically a memory fault): every block id a sequence uses is in
+ * [0, NB); context_lens[b] <= MB * bs; every slot is < NB * bs; no two
+ * tokens of one write call share a slot (they would race).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = 1,      /* bad pointer, size or scalar argument        */
+  PKV_ERR_UNSUPPORTED = 2,  /* valid, but not a built variant              */
+  PKV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required  */
+  PKV_ERR_HIP = 4           /* the HIP runtime refused a launch            */
+} pkv_status;
+
+typedef enum {
+  PKV_F32 = 0,   /* IEEE binary32                         */
+  PKV_BF16 = 1,  /* bfloat16, 16-bit patterns             */
+  PKV_I8 = 2     /* int8 codes with an fp32 per-row scale */
+} pkv_dtype;
+
+/*
+ * Slot-scatter cache write ([ENG5] "Block manager: how paging works": a new
+ * token goes to the next slot of its sequence's tail block).
+ *   For every token t with s = slot_mapping[t] >= 0 and every kv-head h:
+ *     k_cache[s / bs][h][s % bs][:] = k[t][h][:]
+ *     v_cache[s / bs][h][:][s % bs] = v[t][h][:]
+ *   The copy is bit-exact.  dtype is PKV_F32 or PKV_BF16 (the element type of
+ *   k, v and both caches).  head_dim in {64, 128}; block_size in {16, 32};
+ *   num_tokens >= 0 (0: no-op).  Errors: PKV_ERR_INVALID for null pointers
+ *   or non-positive sizes, PKV_ERR_UNSUPPORTED for other dtypes or sizes.
+ */
+pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping, int64_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, pkv_dtype dtype, void* stream);
+
+/*
+ * Quantising cache write for an int8 KV cache ([ENG5] "KV-cache
+ * quantization", [LAYERS] 2.3, [ENG5] "INT8 weight-only quantization").
+ *   Each (token, kv-head) row x of k (and, separately, of v), fp32, becomes
+ *     a = max_d |x_d|;  s = a / 127 (IEEE fp32 division);
+ *     code_d = clamp(rint(x_d / s), -127, 127)  (round half to even);
+ *     s == 0 (a == 0, or a / 127 underflows) gives all codes 0.
+ *   Codes go to the slot as in pkv_kv_cache_write; s goes to
+ *   k_scale[s_slot / bs][h][s_slot % bs] (v_scale likewise).  Inputs must be
+ *   finite.  Bit-exact: identical codes and scales for identical inputs.
+ */
+pkv_status pkv_kv_cache_write_int8(const float* k, const float* v, int8_t* k_cache,
+                                   int8_t* v_cache, float* k_scale, float* v_scale,
+                                   const int64_t* slot_mapping, int64_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, void* stream);
+
+/*
+ * Bytes of device workspace pkv_paged_attention_decode needs for these
+ * sizes (0 when every sequence fits one partition, in which case the
+ * workspace pointer may be NULL).  partition_tokens as for decode.  Returns
+ * 0 also for invalid sizes (decode then reports the error).
+ */
+size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_blocks_per_seq,
+                                          int32_t partition_tokens);
+
+/*
+ * Token count per context partition the library would use for these sizes
+ * when partition_tokens is 0 (the automatic choice); 0 for invalid sizes.
+ */
+int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                             int32_t block_size, int32_t max_blocks_per_seq,
+                                             int32_t partition_tokens);
+
+/*
+ * Single-token decode attention over the paged cache ([ENG5] "Two phases
+ * with very different characteristics": each decode step attends the new
+ * token over the whole cached context; [ENG5] "Paged attention").
+ *   For each sequence b with L = context_lens[b] and query head h (kv-head
+ *   g = h / G), with K_b, V_b the L tokens gathered through the block table:
+ *     out[b][h][:] = softmax(scale * K_b q[b][h]) V_b,  accumulated in fp32;
+ *   L == 0 gives zeros.  For an int8 cache each K/V element's value is its
+ *   code times the token's scale.
+ * Supported: (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16), (BF16, I8)};
+ * out has q's dtype; head_dim in {64, 128}; block_size in {16, 32};
+ * G in {1, 2, 4, 8, 16}.  k_scale and v_scale are required for I8 and must
+ * be NULL otherwise.  num_seqs == 0 is a no-op.  scale must be finite.
+ * partition_tokens: 0 for the automatic choice, else a multiple of 32 in
+ * [32, 64 * block_size]; long contexts are split into partitions of that
+ * many tokens whose partial results a second kernel combines.
+ * workspace / workspace_bytes: device scratch of at least
+ * pkv_paged_attention_workspace_size(...) bytes, 256-byte aligned.
+ */
+pkv_status pkv_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const float* k_scale,
+                                      const float* v_scale, const int32_t* block_tables,
+                                      const int32_t* context_lens, float scale,
+                                      int32_t num_seqs, int32_t num_heads,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, pkv_dtype q_dtype,
+                                      pkv_dtype kv_dtype, int32_t partition_tokens,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two launches pkv_paged_attention_decode is made of, for callers that
+ * schedule or time them separately.  Same arguments and preconditions.
+ * _partitions: attends each context partition; a sequence that fits one
+ * partition gets its final output here, longer ones leave per-partition
+ * (max, sum, unnormalised output) partials in the workspace.
+ * _reduce: combines those partials into out (nothing to do, and no launch,
+ * when every sequence fits one partition).  Call _partitions first, on the
+ * same stream.
+ */
+pkv_status pkv_paged_attention_decode_partitions(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, pkv_dtype q_dtype,
+    pkv_dtype kv_dtype, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+pkv_status pkv_paged_attention_decode_reduce(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, pkv_dtype q_dtype,
+    pkv_dtype kv_dtype, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* Text of the last failure on this thread ("" after a successful call).
+ * The pointer stays valid until the next call on the same thread. */
+const char* pkv_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

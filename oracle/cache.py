@@ -16,8 +16,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   [LAYERS] 2.3: per-token scales, K and V quantized separately), using
   ``q = round(x / s)`` ([ENG5] "INT8 weight-only quantization") with
   ``s = absmax / 127``.  Readings taken: fp32 throughout (IEEE division);
-  round half to even; clamp to [-127, 127]; an all-zero row gets
-  ``s = 0`` and codes 0.  Inputs are assumed finite.
+  round half to even; clamp to [-127, 127]; a row whose scale is zero
+  (all-zero, or so tiny that absmax / 127 underflows) gets ``s = 0`` and
+  codes 0.  Inputs are assumed finite.
 """
 
 import numpy as np
@@ -51,11 +52,12 @@ def quantize_int8(x):
     x = np.asarray(x, dtype=np.float32)
     a = np.max(np.abs(x), axis=-1)                       # exact in fp32
     s = (a / np.float32(127.0)).astype(np.float32)       # IEEE fp32 division
-    safe = np.where(a > 0, s, np.float32(1.0)).astype(np.float32)
+    nz = s > 0                                           # a == 0, or a/127 underflowed
+    safe = np.where(nz, s, np.float32(1.0)).astype(np.float32)
     ratio = (x / safe[..., None]).astype(np.float32)     # IEEE fp32 division
     codes = np.clip(np.rint(ratio), -127, 127)           # rint: half to even
-    codes = np.where(a[..., None] > 0, codes, 0).astype(np.int8)
-    s = np.where(a > 0, s, np.float32(0.0)).astype(np.float32)
+    codes = np.where(nz[..., None], codes, 0).astype(np.int8)
+    s = np.where(nz, s, np.float32(0.0)).astype(np.float32)
     return codes, s
 
 

@@ -1,1 +1,21 @@
-"""Paged decode attention for MI355X (gfx950)."""
+"""Paged decode attention over a paged KV cache for AMD MI355X (gfx950).
+
+The work is done by ``libpagedkv.so`` (hand-written HIP kernels behind the C
+ABI in ``include/pagedkv.h``); this package marshals torch tensors into that
+ABI.  ``workloads`` builds seeded synthetic inputs and ``blocks`` is a host
+block allocator (free list, refcounts, copy-on-write).
+"""
+
+from ._lib import (  # noqa: F401
+    kv_cache_write,
+    kv_cache_write_int8,
+    paged_attention_decode,
+    paged_attention_decode_partitions,
+    paged_attention_decode_reduce,
+    partition_tokens,
+    workspace_size,
+    load as load_library,
+    LIB_PATH,
+)
+
+__version__ = "0.1.0"

@@ -1,0 +1,75 @@
+// Split-context combine: merges the per-partition partials of sequences
+// longer than one partition into the final output.
+//
+// Partition p of a (sequence, head) left M_p (max scaled score, log2
+// domain), S_p = sum_t exp2(s_t - M_p) and A_p = sum_t exp2(s_t - M_p) v_t.
+// With M = max_p M_p and w_p = exp2(M_p - M):
+//   out = (sum_p w_p A_p) / (sum_p w_p S_p),
+// which equals softmax over the whole context exactly (up to rounding), so
+// the split never changes the definition.
+//
+// One wave per (sequence, query head); a lane owns dims lane, lane + 64.
+
+#include "pkv_device.hpp"
+#include "pkv_kernels.hpp"
+
+namespace pkv {
+namespace {
+
+template <int D, bool kOutBf16>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
+  constexpr int ND = D / kWave;
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / p.num_heads;
+  const int L = p.context_lens[b];
+  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  if (nparts <= 1) return;  // written by the partition kernel
+  const size_t base = static_cast<size_t>(bh) * p.num_parts;
+  const float* m = p.ws_m + base;
+  const float* l = p.ws_l + base;
+  const float* a = p.ws_acc + base * D;
+
+  float M = -INFINITY;
+  for (int i = lane; i < nparts; i += kWave) M = fmaxf(M, m[i]);
+  M = wave_max(M);
+  float den = 0.f;
+  for (int i = lane; i < nparts; i += kWave) den += exp2f(m[i] - M) * l[i];
+  den = wave_sum(den);
+
+  float num[ND];
+#pragma unroll
+  for (int k = 0; k < ND; ++k) num[k] = 0.f;
+  for (int i = 0; i < nparts; ++i) {
+    const float w = exp2f(m[i] - M);
+#pragma unroll
+    for (int k = 0; k < ND; ++k) num[k] = fmaf(w, a[static_cast<size_t>(i) * D + lane + kWave * k], num[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < ND; ++k) {
+    const float o = num[k] / den;
+    const size_t idx = static_cast<size_t>(bh) * D + lane + kWave * k;
+    if constexpr (kOutBf16)
+      static_cast<uint16_t*>(p.out)[idx] = f32_to_bf16(o);
+    else
+      static_cast<float*>(p.out)[idx] = o;
+  }
+}
+
+template <int D>
+hipError_t launch_t(const DecodeParams& p, bool out_bf16, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(p.num_seqs * p.num_heads));
+  if (out_bf16)
+    hipLaunchKernelGGL((decode_reduce_kernel<D, true>), grid, dim3(kWave), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<D, false>), grid, dim3(kWave), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, hipStream_t s) {
+  return p.head_dim == 128 ? launch_t<128>(p, out_bf16, s) : launch_t<64>(p, out_bf16, s);
+}
+
+}  // namespace pkv

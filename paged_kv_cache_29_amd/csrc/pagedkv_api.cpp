@@ -1,0 +1,321 @@
+// C ABI of libpagedkv: argument validation, variant dispatch, partition
+// sizing and error reporting.  Every check here runs before any HIP call, so
+// an invalid call launches nothing and has no side effect.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/pagedkv.h"
+#include "pkv_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32; }
+bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+constexpr int kChunk = 32;           // tokens per wave iteration
+constexpr int kMaxPartBlocks = 64;   // block ids of one partition live in one VGPR
+
+// Automatic partition length: the smallest of 256 / 512 / 1024 tokens that
+// still gives the launch enough work per workgroup, but never so large that
+// short batches leave the GPU idle.
+int32_t auto_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                         int32_t max_blocks_per_seq) {
+  const int64_t ctx = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  int32_t pt = 512;
+  // few (sequence, kv-head) pairs: split finer so >= ~4 workgroups per CU exist
+  if (units * ((ctx + pt - 1) / pt) < 1024 * 4) pt = 256;
+  if (pt > kMaxPartBlocks * block_size) pt = kMaxPartBlocks * block_size;
+  return pt;
+}
+
+// Validated partition length, or 0 if `requested` is not acceptable.
+int32_t part_tokens_for(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                        int32_t max_blocks_per_seq, int32_t requested) {
+  if (requested == 0) return auto_part_tokens(num_seqs, num_kv_heads, block_size, max_blocks_per_seq);
+  if (requested < kChunk || requested % kChunk != 0 || requested > kMaxPartBlocks * block_size)
+    return 0;
+  return requested;
+}
+
+int32_t num_parts_for(int32_t block_size, int32_t max_blocks_per_seq, int32_t pt) {
+  const int64_t ctx = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  return static_cast<int32_t>((ctx + pt - 1) / pt);
+}
+
+size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t nparts) {
+  if (nparts <= 1) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * nparts;
+  size_t acc = rows * head_dim * sizeof(float);
+  acc = (acc + 255) & ~size_t(255);
+  size_t ml = rows * sizeof(float);
+  ml = (ml + 255) & ~size_t(255);
+  return acc + 2 * ml;
+}
+
+struct DecodeSetup {
+  pkv::DecodeParams p;
+  pkv::KvKind kv;
+  bool out_bf16;
+};
+
+pkv_status validate_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                           int64_t num_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype,
+                           int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                           DecodeSetup* st) {
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_heads <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID, "num_heads and num_kv_heads must be positive");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_heads (%d) must be a multiple of num_kv_heads (%d)",
+                num_heads, num_kv_heads);
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID, "max_blocks_per_seq must be positive");
+  if (num_blocks <= 0) return fail(PKV_ERR_INVALID, "num_blocks must be positive");
+  if (head_dim <= 0 || block_size <= 0)
+    return fail(PKV_ERR_INVALID, "head_dim and block_size must be positive");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID, "scale must be finite");
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > (int64_t(1) << 30))
+    return fail(PKV_ERR_INVALID, "max_blocks_per_seq * block_size too large");
+  if (!head_dim_ok(head_dim)) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (!block_size_ok(block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", block_size);
+  if (!group_ok(num_heads / num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "num_heads / num_kv_heads = %d not in {1, 2, 4, 8, 16}",
+                num_heads / num_kv_heads);
+  pkv::KvKind kv;
+  if (q_dtype == PKV_F32 && kv_dtype == PKV_F32) {
+    kv = pkv::KvKind::F32;
+  } else if (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) {
+    kv = pkv::KvKind::BF16;
+  } else if (q_dtype == PKV_BF16 && kv_dtype == PKV_I8) {
+    kv = pkv::KvKind::I8;
+  } else {
+    return fail(PKV_ERR_UNSUPPORTED, "(q_dtype, kv_dtype) = (%d, %d) is not supported",
+                static_cast<int>(q_dtype), static_cast<int>(kv_dtype));
+  }
+  const int32_t pt = part_tokens_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
+                                     partition_tokens);
+  if (pt == 0)
+    return fail(PKV_ERR_INVALID,
+                "partition_tokens %d must be 0 or a multiple of %d in [%d, %d]",
+                partition_tokens, kChunk, kChunk, kMaxPartBlocks * block_size);
+  const int32_t nparts = num_parts_for(block_size, max_blocks_per_seq, pt);
+  if (nparts > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many context partitions (%d)", nparts);
+  if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffff)
+    return fail(PKV_ERR_UNSUPPORTED, "num_seqs * num_kv_heads too large");
+  if (num_seqs > 0) {
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+      return fail(PKV_ERR_INVALID, "null pointer among out, q, k_cache, v_cache, block_tables, context_lens");
+  }
+  if (kv == pkv::KvKind::I8) {
+    if (num_seqs > 0 && (!k_scale || !v_scale))
+      return fail(PKV_ERR_INVALID, "int8 cache needs k_scale and v_scale");
+  } else if (k_scale || v_scale) {
+    return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL unless kv_dtype is PKV_I8");
+  }
+  const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, nparts);
+  if (need > 0 && num_seqs > 0) {
+    if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+      return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  pkv::DecodeParams& p = st->p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * nparts;
+  size_t acc_bytes = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
+  size_t ml_bytes = (rows * sizeof(float) + 255) & ~size_t(255);
+  char* ws = static_cast<char*>(workspace);
+  p.ws_acc = need ? reinterpret_cast<float*>(ws) : nullptr;
+  p.ws_m = need ? reinterpret_cast<float*>(ws + acc_bytes) : nullptr;
+  p.ws_l = need ? reinterpret_cast<float*>(ws + acc_bytes + ml_bytes) : nullptr;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.part_tokens = pt;
+  p.num_parts = nparts;
+  st->kv = kv;
+  st->out_bf16 = q_dtype == PKV_BF16;
+  return PKV_OK;
+}
+
+pkv_status launch_partitions(const DecodeSetup& st, hipStream_t stream) {
+  hipError_t e = st.kv == pkv::KvKind::F32 ? pkv::launch_decode_f32(st.p, stream)
+                                           : pkv::launch_decode_mfma(st.p, st.kv, stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "partition kernel launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+pkv_status launch_reduce(const DecodeSetup& st, hipStream_t stream) {
+  if (st.p.num_parts <= 1) return PKV_OK;
+  hipError_t e = pkv::launch_decode_reduce(st.p, st.out_bf16, stream);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+pkv_status validate_write(const void* k, const void* v, const void* k_cache, const void* v_cache,
+                          const int64_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int64_t num_blocks) {
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID, "num_tokens must be >= 0");
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID, "num_kv_heads, head_dim, block_size and num_blocks must be positive");
+  if (!head_dim_ok(head_dim)) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", head_dim);
+  if (!block_size_ok(block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not in {16, 32}", block_size);
+  if (num_tokens > 0 && (!k || !v || !k_cache || !v_cache || !slot_mapping))
+    return fail(PKV_ERR_INVALID, "null pointer among k, v, k_cache, v_cache, slot_mapping");
+  if (num_tokens > (int64_t(1) << 40) / (num_kv_heads * int64_t(head_dim)))
+    return fail(PKV_ERR_INVALID, "num_tokens too large");
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const int64_t* slot_mapping, int64_t num_tokens,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, pkv_dtype dtype, void* stream) {
+  pkv_status st = validate_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                                 head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (dtype != PKV_F32 && dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write dtype must be PKV_F32 or PKV_BF16");
+  if (num_tokens == 0) return ok();
+  pkv::WriteParams p{k, v, k_cache, v_cache, nullptr, nullptr, slot_mapping, num_tokens,
+                     num_kv_heads, head_dim, block_size};
+  hipError_t e = pkv::launch_cache_write(p, dtype == PKV_F32 ? pkv::KvKind::F32 : pkv::KvKind::BF16,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "kv_cache_write launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pkv_status pkv_kv_cache_write_int8(const float* k, const float* v, int8_t* k_cache,
+                                   int8_t* v_cache, float* k_scale, float* v_scale,
+                                   const int64_t* slot_mapping, int64_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, void* stream) {
+  pkv_status st = validate_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                                 head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (num_tokens > 0 && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "null k_scale or v_scale");
+  if (num_tokens == 0) return ok();
+  pkv::WriteParams p{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens,
+                     num_kv_heads, head_dim, block_size};
+  hipError_t e = pkv::launch_cache_write_int8(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "kv_cache_write_int8 launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                             int32_t block_size, int32_t max_blocks_per_seq,
+                                             int32_t partition_tokens) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || !block_size_ok(block_size) || max_blocks_per_seq <= 0)
+    return 0;
+  return part_tokens_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, partition_tokens);
+}
+
+size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_blocks_per_seq,
+                                          int32_t partition_tokens) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || !head_dim_ok(head_dim) ||
+      !block_size_ok(block_size) || max_blocks_per_seq <= 0)
+    return 0;
+  const int32_t pt = part_tokens_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
+                                     partition_tokens);
+  if (pt == 0) return 0;
+  return workspace_bytes_for(num_seqs, num_heads, head_dim,
+                             num_parts_for(block_size, max_blocks_per_seq, pt));
+}
+
+#define PKV_DECODE_ARGS                                                                       \
+  out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale, num_seqs,    \
+      num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, q_dtype, \
+      kv_dtype, partition_tokens, workspace, workspace_bytes
+
+#define PKV_DECODE_PARAMS                                                                    \
+  void *out, const void *q, const void *k_cache, const void *v_cache, const float *k_scale,  \
+      const float *v_scale, const int32_t *block_tables, const int32_t *context_lens,        \
+      float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,                \
+      int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,  \
+      pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t partition_tokens, void *workspace,      \
+      size_t workspace_bytes, void *stream
+
+pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
+  DecodeSetup st;
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, &st);
+  if (s != PKV_OK) return s;
+  if (num_seqs == 0) return ok();
+  s = launch_partitions(st, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
+  s = launch_reduce(st, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
+  return ok();
+}
+
+pkv_status pkv_paged_attention_decode_partitions(PKV_DECODE_PARAMS) {
+  DecodeSetup st;
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, &st);
+  if (s != PKV_OK) return s;
+  if (num_seqs == 0) return ok();
+  s = launch_partitions(st, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
+  return ok();
+}
+
+pkv_status pkv_paged_attention_decode_reduce(PKV_DECODE_PARAMS) {
+  DecodeSetup st;
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, &st);
+  if (s != PKV_OK) return s;
+  if (num_seqs == 0) return ok();
+  s = launch_reduce(st, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
+  return ok();
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+const char* pkv_version(void) { return "0.1.0"; }
+
+}  // extern "C"

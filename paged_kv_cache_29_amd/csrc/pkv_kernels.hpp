@@ -1,0 +1,63 @@
+// Kernel parameter blocks and launchers of libpagedkv (host + device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// One decode launch.  Partials of sequences longer than one partition go to
+// the workspace:
+//   ws_acc [B][H][P][D]  unnormalised sum_t p_t v_t of the partition
+//   ws_m   [B][H][P]     max over the partition of scale*log2(e)*score
+//   ws_l   [B][H][P]     sum_t p_t,  p_t = exp2(scaled score - ws_m)
+// where P = num_parts = ceil(max_blocks_per_seq * block_size / part_tokens).
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_acc;
+  float* ws_m;
+  float* ws_l;
+  float scale_log2;  // scale * log2(e)
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t part_tokens;
+  int32_t num_parts;
+};
+
+struct WriteParams {
+  const void* k;
+  const void* v;
+  void* k_cache;
+  void* v_cache;
+  float* k_scale;
+  float* v_scale;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+};
+
+enum class KvKind { F32 = 0, BF16 = 1, I8 = 2 };
+
+// Waves per workgroup of the partition kernels.
+constexpr int kDecodeWaves = 4;
+
+hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, hipStream_t s);
+hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
+hipError_t launch_cache_write_int8(const WriteParams& p, hipStream_t s);
+
+}  // namespace pkv

@@ -137,6 +137,9 @@ def _allocate(lens, bs, num_blocks, order, prefix=0):
     new_slots = np.empty(len(lens), dtype=np.int64)
     for i, (sid, L) in enumerate(zip(sids, lens)):
         L = int(L)
+        if L == 0 and prefix == 0:         # empty context: no blocks, no new token
+            new_slots[i] = -1
+            continue
         have = alloc.length(sid)
         if L - 1 > have:
             fill_slots[i] = np.concatenate([fill_slots[i], alloc.append(sid, L - 1 - have)])
