@@ -137,7 +137,7 @@ int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_he
  * G in {1, 2, 4, 8, 16}.  k_scale and v_scale are required for I8 and must
  * be NULL otherwise.  num_seqs == 0 is a no-op.  scale must be finite.
  * partition_tokens: 0 for the automatic choice, else a multiple of 32 in
- * [32, 64 * block_size]; long contexts are split into partitions of that
+ * [32, 128 * block_size]; long contexts are split into partitions of that
  * many tokens whose partial results a second kernel combines.
  * workspace / workspace_bytes: device scratch of at least
  * pkv_paged_attention_workspace_size(...) bytes, 256-byte aligned.

@@ -16,21 +16,28 @@
 // keeping its own online-softmax state; the states are merged through LDS at
 // the end.  A sequence that fits one partition is finished here; longer ones
 // leave (max, sum, unnormalised output) partials for the reduce kernel.
+// Each wave issues the loads of two chunks before consuming either, so 32 KB
+// (bf16, two waves per SIMD) or 16.5 KB (int8, three waves per SIMD) per wave
+// are in flight.
 //
-// Per 32-token chunk (two 16-token sub-tiles, from two blocks at bs=16 or
-// one block at bs=32), one wave does:
+// Per 32-token chunk (two 16-token sub-tiles: two blocks at bs=16, the two
+// halves of one block at bs=32), one wave does:
 //   S^T[16 tok x 16 heads] = K_sub[16 x D] . Q^T[D x 16]   D/32 MFMAs per sub-tile
-//     A operand: lane l holds row (l % 16) of the K sub-tile, 8 dims; loaded
-//     straight from HBM as 16 bytes (bf16) or 16 bytes = two operands (int8).
-//     B operand: Q^T, built once per workgroup (heads >= G are zero).
-//   online softmax on the 8 scores a lane holds (head l%16, tokens
-//     4*(l/16)+i of each sub-tile), max across the 4 lane groups by shuffles.
-//   O^T[D x 16 heads] += V^T[D x 32 tok] . P^T[32 tok x 16 heads]   D/16 MFMAs
+//     A operand: lane l holds row l % 16 of the K sub-tile, 8 dims, loaded
+//     straight from HBM (16 bytes); B operand Q^T is built once (heads >= G
+//     are zero).  The accumulator gives lane group g = l / 16 the scores of
+//     sub-tile tokens 4g .. 4g+3 for head l % 16.
+//   online softmax on the 8 scores a lane holds, max across the 4 lane
+//     groups by shuffles.
+//   O^T[D x 16 heads] += V^T[D x 32 tok] . P^T[32 tok x 16 heads]   2 * D/16 MFMAs
 //     A operand: V tiles are stored dim-major (element (r, d) at d*bs + r),
-//     so the 4 tokens a lane needs per sub-tile are 8 contiguous bytes.
+//     so the 4 tokens a lane needs from each sub-tile are 8 contiguous bytes.
 //     B operand: the lane's own 8 probabilities, split into a bf16 hi/lo
 //     pair (two MFMAs) so the weights keep ~16 bits; no shuffle is needed
 //     because the score layout already matches.
+// Every load address is a uniform block base (scalar registers) plus a
+// loop-invariant lane offset, so prefetching a chunk needs no vector
+// address arithmetic.
 // The contraction index of each MFMA is a free pairing of (lane group,
 // element) to (dim or token); A and B use the same pairing, so only the row
 // / column / accumulator layouts of the instruction matter here.
@@ -51,14 +58,11 @@ __device__ __forceinline__ u32x4 load_u32x4(const void* p) {
 __device__ __forceinline__ u32x2 load_u32x2(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
 }
-__device__ __forceinline__ uint32_t load_u32(const void* p) {
-  return *reinterpret_cast<const uint32_t*>(p);
-}
 __device__ __forceinline__ f32x4 load_f32x4(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
-// Two int8 codes (bytes 0 and 1 of w >> (16*half)) -> packed bf16 pair.
+// Two int8 codes (bytes 2*half and 2*half+1 of w) -> packed bf16 pair.
 // |code| <= 128 has at most 8 significant bits, so the conversion is exact.
 __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int half) {
   const int32_t lo = static_cast<int32_t>(w << (24 - 16 * half)) >> 24;
@@ -68,19 +72,10 @@ __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int half) {
   return (flo >> 16) | (fhi & 0xffff0000u);
 }
 
-// 16 int8 codes -> two bf16x8 operands (codes 0..7 and 8..15).
-__device__ __forceinline__ void i8x16_to_bf16(u32x4 w, bf16x8& a, bf16x8& b) {
-  u32x4 lo, hi;
-  lo.x = i8pair_to_bf16x2(w.x, 0);
-  lo.y = i8pair_to_bf16x2(w.x, 1);
-  lo.z = i8pair_to_bf16x2(w.y, 0);
-  lo.w = i8pair_to_bf16x2(w.y, 1);
-  hi.x = i8pair_to_bf16x2(w.z, 0);
-  hi.y = i8pair_to_bf16x2(w.z, 1);
-  hi.z = i8pair_to_bf16x2(w.w, 0);
-  hi.w = i8pair_to_bf16x2(w.w, 1);
-  a = as_bf16x8(lo);
-  b = as_bf16x8(hi);
+// 8 int8 codes -> one bf16x8 operand.
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  return as_bf16x8(u32x4{i8pair_to_bf16x2(w0, 0), i8pair_to_bf16x2(w0, 1),
+                         i8pair_to_bf16x2(w1, 0), i8pair_to_bf16x2(w1, 1)});
 }
 
 // Zero the bf16 elements (pairs packed in w) whose token is >= t_end.
@@ -90,20 +85,115 @@ __device__ __forceinline__ uint32_t mask_pair(uint32_t w, int tok, int t_end) {
   return lo | hi;
 }
 
+// Raw loads of one 32-token chunk for one lane.  The chunk is two 16-token
+// sub-tiles h = 0, 1 (two blocks at bs = 16, the two halves of one block at
+// bs = 32).
+template <bool kInt8, int D>
+struct Chunk {
+  static constexpr int NJ = D / 32;
+  static constexpr int NN = D / 16;
+  // K rows: per sub-tile h, NJ operands of 8 dims (bf16: 16 B each; int8:
+  // one 16-byte load feeds two operands, so NJ/2 loads)
+  u32x4 k[2][kInt8 ? NJ / 2 : NJ];
+  // V^T: per sub-tile h and dim block n, tokens 4g .. 4g+3 of dim 16n + c
+  // (bf16: 8 B; int8: 4 B)
+  typename std::conditional<kInt8, uint32_t, u32x2>::type v[2][NN];
+  f32x4 ks[2], vs[2];  // int8 scales of sub-tile tokens 4g .. 4g+3
+};
+
+// Buffer-resource word 3 for raw (untyped, unswizzled) buffers on gfx9-class
+// GPUs: 32-bit data format, no stride.
+constexpr int kBufferFlags = 0x00020000;
+
+template <bool kInt8, int D, int BS>
+struct ChunkLoader {
+  using KT = typename std::conditional<kInt8, int8_t, uint16_t>::type;
+  static constexpr uint32_t kElem = sizeof(KT);
+  static constexpr uint32_t kTileBytes = BS * D * kElem;
+  const char* kc;   // cache base addresses (bytes)
+  const char* vc;
+  const char* ksc;  // int8 scale arrays (bytes)
+  const char* vsc;
+  int Hkv, kvh;
+  // loop-invariant per-lane byte offsets inside a (block, kv-head) tile
+  uint32_t koff, voff, soff;
+
+  __device__ __forceinline__ ChunkLoader(const DecodeParams& p, int kvh_, int c, int g)
+      : kc(static_cast<const char*>(p.k_cache)), vc(static_cast<const char*>(p.v_cache)),
+        ksc(reinterpret_cast<const char*>(p.k_scale)), vsc(reinterpret_cast<const char*>(p.v_scale)),
+        Hkv(p.num_kv_heads), kvh(kvh_) {
+    // K: row c of the sub-tile; dims 32j + 8g (bf16) or 64jj + 16g (int8)
+    koff = (static_cast<uint32_t>(c) * D + (kInt8 ? 16u : 8u) * g) * kElem;
+    // V^T: dim c (+16n per load), tokens 4g .. 4g+3
+    voff = (static_cast<uint32_t>(c) * BS + 4u * g) * kElem;
+    soff = 4u * g * 4u;
+  }
+
+  // Buffer resource over one (block, kv-head) tile: the base is uniform, so
+  // the descriptor lives in scalar registers and every load is
+  // "descriptor + 32-bit lane offset", with no vector address arithmetic.
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t tile(const char* base, size_t off, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), static_cast<short>(0),
+                                             static_cast<int>(bytes), kBufferFlags);
+  }
+
+  // blk[h]: physical block of sub-tile h; row0[h]: its first row in the block.
+  __device__ __forceinline__ void load(Chunk<kInt8, D>& ch, const int blk[2], const int row0[2]) const {
+    constexpr int NJ = D / 32;
+    constexpr int NN = D / 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const size_t t = static_cast<size_t>(blk[h]) * Hkv + kvh;
+      const __amdgpu_buffer_rsrc_t rk = tile(kc, t * kTileBytes, kTileBytes);
+      const __amdgpu_buffer_rsrc_t rv = tile(vc, t * kTileBytes, kTileBytes);
+      // uniform offsets (row of the sub-tile, per-load constants) go in the
+      // scalar offset operand, so the lane offset is the only vector input
+      const int ks_row = row0[h] * D * kElem;
+      const int vs_row = row0[h] * kElem;
+      if constexpr (kInt8) {
+#pragma unroll
+        for (int jj = 0; jj < NJ / 2; ++jj)
+          ch.k[h][jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, ks_row + 64 * jj, 0));
+#pragma unroll
+        for (int n = 0; n < NN; ++n)
+          ch.v[h][n] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, vs_row + 16 * n * BS, 0);
+        const __amdgpu_buffer_rsrc_t rks = tile(ksc, t * BS * 4, BS * 4);
+        const __amdgpu_buffer_rsrc_t rvs = tile(vsc, t * BS * 4, BS * 4);
+        ch.ks[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, soff, row0[h] * 4, 0));
+        ch.vs[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, soff, row0[h] * 4, 0));
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          ch.k[h][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, ks_row + 64 * j, 0));
+#pragma unroll
+        for (int n = 0; n < NN; ++n)
+          ch.v[h][n] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, vs_row + 32 * n * BS, 0));
+      }
+    }
+  }
+};
+
+// Block ids one partition may span (its context / block_size).
+constexpr int kMaxPartBlocks = 128;
+
 template <bool kInt8, int D, int BS, int W>
-__global__ __launch_bounds__(W * kWave) void decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(W * kWave)
+// two chunk buffers per wave: bf16 fits two waves per SIMD, int8 three
+__attribute__((amdgpu_waves_per_eu(kInt8 ? 3 : 2, kInt8 ? 3 : 2)))
+void decode_mfma_kernel(DecodeParams p) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
-  constexpr int NJ = D / 32;  // QK MFMAs per 16-token sub-tile
-  constexpr int NN = D / 16;  // PV MFMAs per 32-token chunk
+  constexpr int NJ = D / 32;  // QK MFMAs per score tile
+  constexpr int NN = D / 16;  // PV MFMA pairs per chunk
 
   __shared__ float red_acc[W > 1 ? W - 1 : 1][NN * 4][kWave];
   __shared__ float red_m[W][kWave];
   __shared__ float red_l[W][kWave];
+  __shared__ int blk_ids[W][kMaxPartBlocks];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int c = lane & 15;  // head column
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int c = lane & 15;  // head column / row in the MFMA tiles
   const int g = lane >> 4;  // lane group
 
   const int Hkv = p.num_kv_heads;
@@ -142,15 +232,35 @@ __global__ __launch_bounds__(W * kWave) void decode_mfma_kernel(DecodeParams p) 
     }
   }
 
-  // Physical block ids of the partition: lane i holds entry i.
+  // Physical block ids of the partition, staged in this wave's LDS slice so
+  // that reading them later waits on LDS traffic only, never on the K/V loads
+  // in flight.
   const int nblk = (t_end - t_begin + BS - 1) / BS;
-  const int32_t* bt = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq + t_begin / BS;
-  const int my_blk = (lane < nblk) ? bt[lane] : 0;
+  {
+    const int32_t* bt = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq + t_begin / BS;
+    for (int i = lane; i < nblk; i += kWave) blk_ids[wave][i] = bt[i];  // nblk <= kMaxPartBlocks
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // wave-private slice: own stores only
+  const int* my_ids = blk_ids[wave];
 
-  using KT = typename std::conditional<kInt8, int8_t, uint16_t>::type;
-  const KT* kc = static_cast<const KT*>(p.k_cache);
-  const KT* vc = static_cast<const KT*>(p.v_cache);
-  const size_t tile = static_cast<size_t>(BS) * D;
+  const ChunkLoader<kInt8, D, BS> ld(p, kvh, c, g);
+
+  // Block ids of chunk `ch` (uniform).  Past the end of the context the
+  // second half reuses the first block: valid memory whose rows are masked.
+  auto chunk_blocks = [&](int ch, int blk[2], int row0[2]) {
+    const int t0 = t_begin + ch * 32;
+    if (BS == 16) {
+      const int lb = ch * 2;
+      blk[0] = __builtin_amdgcn_readfirstlane(my_ids[lb]);
+      blk[1] = (t0 + 16 < t_end) ? __builtin_amdgcn_readfirstlane(my_ids[lb + 1]) : blk[0];
+      row0[0] = 0;
+      row0[1] = 0;
+    } else {
+      blk[0] = blk[1] = __builtin_amdgcn_readfirstlane(my_ids[ch]);
+      row0[0] = 0;
+      row0[1] = 16;
+    }
+  };
 
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -158,123 +268,56 @@ __global__ __launch_bounds__(W * kWave) void decode_mfma_kernel(DecodeParams p) 
 #pragma unroll
   for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunks = (t_end - t_begin + 31) / 32;
-  for (int ch = wave; ch < nchunks; ch += W) {
+  auto consume = [&](const Chunk<kInt8, D>& cw, int ch) {
     const int t0 = t_begin + ch * 32;
-    const bool h1 = (t0 + 16) < t_end;
-    int blk0, blk1, row0, row1;
-    if (BS == 16) {
-      const int lb = (t0 - t_begin) >> 4;
-      blk0 = __builtin_amdgcn_readlane(my_blk, lb);
-      blk1 = h1 ? __builtin_amdgcn_readlane(my_blk, lb + 1) : blk0;
-      row0 = 0;
-      row1 = 0;
-    } else {
-      const int lb = (t0 - t_begin) >> 5;
-      blk0 = __builtin_amdgcn_readlane(my_blk, lb);
-      blk1 = blk0;
-      row0 = 0;
-      row1 = 16;
-    }
-    const size_t tb0 = (static_cast<size_t>(blk0) * Hkv + kvh) * tile;
-    const size_t tb1 = (static_cast<size_t>(blk1) * Hkv + kvh) * tile;
-
-    // ---- K sub-tiles -> scores
-    bf16x8 ka0[NJ], ka1[NJ];
-    {
-      const KT* k0 = kc + tb0 + static_cast<size_t>(row0 + c) * D;
-      const KT* k1 = kc + tb1 + static_cast<size_t>(row1 + c) * D;
+    // ---- scores: S^T of sub-tiles h = 0, 1
+    f32x4 s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (kInt8) {
 #pragma unroll
         for (int jj = 0; jj < NJ / 2; ++jj) {
-          i8x16_to_bf16(load_u32x4(k0 + 64 * jj + 16 * g), ka0[2 * jj], ka0[2 * jj + 1]);
-          u32x4 w1 = {0u, 0u, 0u, 0u};
-          if (h1) w1 = load_u32x4(k1 + 64 * jj + 16 * g);
-          i8x16_to_bf16(w1, ka1[2 * jj], ka1[2 * jj + 1]);
+          const u32x4 w = cw.k[h][jj];
+          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16(w.x, w.y), qf[2 * jj], s[h], 0, 0, 0);
+          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16(w.z, w.w), qf[2 * jj + 1], s[h], 0, 0, 0);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          ka0[j] = as_bf16x8(load_u32x4(k0 + 32 * j + 8 * g));
-          u32x4 w1 = {0u, 0u, 0u, 0u};
-          if (h1) w1 = load_u32x4(k1 + 32 * j + 8 * g);
-          ka1[j] = as_bf16x8(w1);
-        }
+        for (int j = 0; j < NJ; ++j)
+          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw.k[h][j]), qf[j], s[h], 0, 0, 0);
       }
     }
-    // ---- V sub-tiles (dim-major): lane needs dims 16n + c, tokens 4g..4g+3
-    uint32_t va0[NN][2], va1[NN][2];
-    {
-      const KT* v0 = vc + tb0 + static_cast<size_t>(c) * BS + row0 + 4 * g;
-      const KT* v1 = vc + tb1 + static_cast<size_t>(c) * BS + row1 + 4 * g;
-#pragma unroll
-      for (int n = 0; n < NN; ++n) {
-        if constexpr (kInt8) {
-          const uint32_t w0 = load_u32(v0 + 16 * n * BS);
-          const uint32_t w1 = h1 ? load_u32(v1 + 16 * n * BS) : 0u;
-          va0[n][0] = i8pair_to_bf16x2(w0, 0);
-          va0[n][1] = i8pair_to_bf16x2(w0, 1);
-          va1[n][0] = i8pair_to_bf16x2(w1, 0);
-          va1[n][1] = i8pair_to_bf16x2(w1, 1);
-        } else {
-          const u32x2 w0 = load_u32x2(v0 + 16 * n * BS);
-          u32x2 w1 = {0u, 0u};
-          if (h1) w1 = load_u32x2(v1 + 16 * n * BS);
-          va0[n][0] = w0.x;
-          va0[n][1] = w0.y;
-          va1[n][0] = w1.x;
-          va1[n][1] = w1.y;
-        }
-      }
-    }
-    f32x4 ks0 = {1.f, 1.f, 1.f, 1.f}, ks1 = ks0, vs0 = ks0, vs1 = ks0;
-    if constexpr (kInt8) {
-      const size_t sb0 = (static_cast<size_t>(blk0) * Hkv + kvh) * BS + row0 + 4 * g;
-      const size_t sb1 = (static_cast<size_t>(blk1) * Hkv + kvh) * BS + row1 + 4 * g;
-      ks0 = load_f32x4(p.k_scale + sb0);
-      vs0 = load_f32x4(p.v_scale + sb0);
-      if (h1) {
-        ks1 = load_f32x4(p.k_scale + sb1);
-        vs1 = load_f32x4(p.v_scale + sb1);
-      }
-    }
-
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0[j], qf[j], s0, 0, 0, 0);
-    if (h1) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1[j], qf[j], s1, 0, 0, 0);
-    }
-
-    // ---- online softmax (log2 domain); lane = head c, tokens 4g+i (+16)
+    // ---- online softmax (log2 domain); lane = head c, tokens 4g + i of
+    // sub-tile h (chunk token 16h + 4g + i), element e = 4h + i
     const bool tail = (t0 + 32) > t_end;
     float sc[8];
+    f32x4 vs[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = s0[i] * ks0[i] * p.scale_log2;
-      sc[4 + i] = s1[i] * ks1[i] * p.scale_log2;
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = s[h][i];
+        if constexpr (kInt8) {
+          x *= cw.ks[h][i];
+          vs[h][i] = cw.vs[h][i];
+        }
+        sc[4 * h + i] = x * p.scale_log2;
+      }
     }
     if (tail) {  // select, never multiply: masked rows may hold NaN
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (t0 + 4 * g + i >= t_end) {
-          sc[i] = -INFINITY;
-          vs0[i] = 0.f;
-        }
-        if (t0 + 16 + 4 * g + i >= t_end) {
-          sc[4 + i] = -INFINITY;
-          vs1[i] = 0.f;
+      for (int e = 0; e < 8; ++e) {
+        if (t0 + 16 * (e >> 2) + 4 * g + (e & 3) >= t_end) {
+          sc[e] = -INFINITY;
+          vs[e >> 2][e & 3] = 0.f;
         }
       }
     }
     float mx = sc[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+    mx = groups_max(mx);
     const float m_new = fmaxf(m_run, mx);
     if (__any(m_new > m_run)) {
       const float alpha = fast_exp2(m_run - m_new);
@@ -289,15 +332,12 @@ __global__ __launch_bounds__(W * kWave) void decode_mfma_kernel(DecodeParams p) 
     {
       float pr[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pr[i] = fast_exp2(sc[i] - m_run);
+      for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(sc[e] - m_run);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) l_run += pr[i];
+      for (int e = 0; e < 8; ++e) l_run += pr[e];
       if constexpr (kInt8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pr[i] *= vs0[i];
-          pr[4 + i] *= vs1[i];
-        }
+        for (int e = 0; e < 8; ++e) pr[e] *= vs[e >> 2][e & 3];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -307,29 +347,58 @@ __global__ __launch_bounds__(W * kWave) void decode_mfma_kernel(DecodeParams p) 
     }
     const bf16x8 pfh = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
     const bf16x8 pfl = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
-
-    if (tail) {  // masked tokens must contribute exact zeros, even over NaN
-      const int ta = t0 + 4 * g;
-      const int tb = t0 + 16 + 4 * g;
-#pragma unroll
-      for (int n = 0; n < NN; ++n) {
-        va0[n][0] = mask_pair(va0[n][0], ta, t_end);
-        va0[n][1] = mask_pair(va0[n][1], ta + 2, t_end);
-        va1[n][0] = mask_pair(va1[n][0], tb, t_end);
-        va1[n][1] = mask_pair(va1[n][1], tb + 2, t_end);
-      }
-    }
+    // ---- O^T += V^T . P^T
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
-      const bf16x8 va = as_bf16x8(u32x4{va0[n][0], va0[n][1], va1[n][0], va1[n][1]});
+      u32x4 vw;
+      if constexpr (kInt8) {
+        vw = u32x4{i8pair_to_bf16x2(cw.v[0][n], 0), i8pair_to_bf16x2(cw.v[0][n], 1),
+                   i8pair_to_bf16x2(cw.v[1][n], 0), i8pair_to_bf16x2(cw.v[1][n], 1)};
+      } else {
+        vw = u32x4{cw.v[0][n].x, cw.v[0][n].y, cw.v[1][n].x, cw.v[1][n].y};
+      }
+      if (tail) {  // masked tokens contribute exact zeros, even over NaN
+        const int ta = t0 + 4 * g;
+        vw.x = mask_pair(vw.x, ta, t_end);
+        vw.y = mask_pair(vw.y, ta + 2, t_end);
+        vw.z = mask_pair(vw.z, ta + 16, t_end);
+        vw.w = mask_pair(vw.w, ta + 18, t_end);
+      }
+      const bf16x8 va = as_bf16x8(vw);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc[n], 0, 0, 0);
       acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc[n], 0, 0, 0);
+    }
+  };
+
+  // ---- this wave's chunks ch = wave, wave + W, ... two at a time: the loads
+  // of both are issued before either is consumed, and no load stays pending
+  // across iterations, so every wait counts exactly the loads behind it.
+  const int nchunks = (t_end - t_begin + 31) / 32;
+  {
+    Chunk<kInt8, D> ca, cb;
+    int blk[2], row0[2];
+    // (The pair is loaded and consumed later chunk first, so the two branches
+    // share no leading code the compiler could hoist, together with its
+    // waits, above the second chunk's loads.)
+    for (int ch = wave; ch < nchunks; ch += 2 * W) {
+      if (ch + W < nchunks) {
+        chunk_blocks(ch + W, blk, row0);
+        ld.load(cb, blk, row0);
+        chunk_blocks(ch, blk, row0);
+        ld.load(ca, blk, row0);
+        __builtin_amdgcn_sched_barrier(0);  // keep both chunks' loads ahead of the math
+        consume(cb, ch + W);
+        consume(ca, ch);
+      } else {
+        chunk_blocks(ch, blk, row0);
+        ld.load(ca, blk, row0);
+        consume(ca, ch);
+      }
     }
   }
 
   // per-head sum over the 4 lane groups (each holds different tokens)
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
+  l_run = groups_sum(l_run);
 
   float M = m_run, Lsum = l_run;
   if constexpr (W > 1) {

@@ -34,7 +34,7 @@ bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32; }
 bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
 constexpr int kChunk = 32;           // tokens per wave iteration
-constexpr int kMaxPartBlocks = 64;   // block ids of one partition live in one VGPR
+constexpr int kMaxPartBlocks = 128;  // block ids of one partition staged in LDS
 
 // Automatic partition length: the smallest of 256 / 512 / 1024 tokens that
 // still gives the launch enough work per workgroup, but never so large that

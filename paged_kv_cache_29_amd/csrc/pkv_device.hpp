@@ -43,4 +43,24 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Combine a value across the four 16-lane groups of a wave (lanes l, l^16,
+// l^32, l^48), without lane-index registers: ds_swizzle swaps 16-lane
+// halves of each 32-lane group, v_permlane32_swap exchanges the two 32-lane
+// halves (each lane gets back its own value and its partner's).
+__device__ __forceinline__ float swap16(float v) {
+  return __uint_as_float(__builtin_amdgcn_ds_swizzle(__float_as_uint(v), 0x401F));
+}
+
+__device__ __forceinline__ float groups_max(float v) {
+  v = fmaxf(v, swap16(v));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float groups_sum(float v) {
+  v = v + swap16(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace pkv

@@ -84,7 +84,7 @@ def _decode(lib, **over):
     (dict(k_scale=_fake(7)), INVALID, "must be NULL"),
     (dict(partition_tokens=48), INVALID, "partition_tokens"),
     (dict(partition_tokens=16), INVALID, "partition_tokens"),
-    (dict(partition_tokens=2048), INVALID, "partition_tokens"),
+    (dict(partition_tokens=4096), INVALID, "partition_tokens"),
     (dict(max_blocks_per_seq=2048, partition_tokens=256), WORKSPACE, "workspace"),
 ])
 def test_decode_rejects(lib, over, code, frag):

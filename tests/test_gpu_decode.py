@@ -197,3 +197,13 @@ def test_repeated_steps_are_deterministic():
     a = dw.step()
     b = dw.step()
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("bs,pt", [(16, 2048), (32, 4096), (16, 1056)])
+def test_partitions_spanning_more_than_64_blocks(kv, bs, pt):
+    """A partition of up to 128 blocks: every block id is staged, none read stale."""
+    w = workloads.make_custom(17, [pt, pt + 1, 2 * pt + 37, 100, 1], 16, 2, 128, bs, kv_dtype=kv)
+    dw = DeviceWorkload(w)
+    got = dw.step(partition_tokens=pt)
+    assert_parity(got, oracle_out(w), kv, f"{kv} bs={bs} pt={pt}")
