@@ -8,7 +8,10 @@
 // which equals softmax over the whole context exactly (up to rounding), so
 // the split never changes the definition.
 //
-// One wave per (sequence, query head); a lane owns dims lane, lane + 64.
+// One wave per (sequence, query head); a lane owns dims lane and lane + 64.
+// The weights of up to 64 partitions are computed lane-parallel and read
+// back one by one with readlane, so the partial rows are independent loads
+// the unrolled loop keeps in flight together.
 
 #include "pkv_device.hpp"
 #include "pkv_kernels.hpp"
@@ -33,18 +36,37 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
   float M = -INFINITY;
   for (int i = lane; i < nparts; i += kWave) M = fmaxf(M, m[i]);
   M = wave_max(M);
-  float den = 0.f;
-  for (int i = lane; i < nparts; i += kWave) den += exp2f(m[i] - M) * l[i];
-  den = wave_sum(den);
 
   float num[ND];
 #pragma unroll
   for (int k = 0; k < ND; ++k) num[k] = 0.f;
-  for (int i = 0; i < nparts; ++i) {
-    const float w = exp2f(m[i] - M);
+  float den = 0.f;
+  for (int first = 0; first < nparts; first += kWave) {
+    const int i = first + lane;
+    const float wv = (i < nparts) ? exp2f(m[i] - M) : 0.f;
+    if (i < nparts) den = fmaf(wv, l[i], den);
+    const int cnt = min(kWave, nparts - first);
+    const float* row = a + static_cast<size_t>(first) * D + lane;
+    // groups of 8 rows: 8 independent loads per lane in flight; rows past
+    // cnt re-read the last valid row and get weight 0 (wv is 0 there)
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+      float x[8][ND];
 #pragma unroll
-    for (int k = 0; k < ND; ++k) num[k] = fmaf(w, a[static_cast<size_t>(i) * D + lane + kWave * k], num[k]);
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(j0 + u, cnt - 1);
+#pragma unroll
+        for (int k = 0; k < ND; ++k) x[u][k] = row[static_cast<size_t>(j) * D + kWave * k];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), (j0 + u) & (kWave - 1)));
+        const float wu = (j0 + u < cnt) ? w : 0.f;
+#pragma unroll
+        for (int k = 0; k < ND; ++k) num[k] = fmaf(wu, x[u][k], num[k]);
+      }
+    }
   }
+  den = wave_sum(den);
 #pragma unroll
   for (int k = 0; k < ND; ++k) {
     const float o = num[k] / den;

@@ -36,17 +36,24 @@ bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 1
 constexpr int kChunk = 32;           // tokens per wave iteration
 constexpr int kMaxPartBlocks = 128;  // block ids of one partition staged in LDS
 
-// Automatic partition length: the smallest of 256 / 512 / 1024 tokens that
-// still gives the launch enough work per workgroup, but never so large that
-// short batches leave the GPU idle.
+// Automatic partition length: the longest of 2048 / 1024 / 512 / 256 tokens
+// (at most kMaxPartBlocks blocks) that still gives the launch about two full
+// rounds of workgroups on the GPU (two 256-thread workgroups per CU, 256
+// CUs).  Longer partitions amortise each workgroup's fixed cost (query load,
+// block-id staging, the final merge) and leave fewer partials to reduce.
 int32_t auto_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                          int32_t max_blocks_per_seq) {
   const int64_t ctx = static_cast<int64_t>(max_blocks_per_seq) * block_size;
   const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  int32_t pt = 512;
-  // few (sequence, kv-head) pairs: split finer so >= ~4 workgroups per CU exist
-  if (units * ((ctx + pt - 1) / pt) < 1024 * 4) pt = 256;
-  if (pt > kMaxPartBlocks * block_size) pt = kMaxPartBlocks * block_size;
+  constexpr int64_t kTargetWorkgroups = 1024;
+  int32_t pt = 256;
+  for (int32_t cand : {2048, 1024, 512}) {
+    if (cand > kMaxPartBlocks * block_size) continue;
+    if (units * ((ctx + cand - 1) / cand) >= kTargetWorkgroups) {
+      pt = cand;
+      break;
+    }
+  }
   return pt;
 }
 

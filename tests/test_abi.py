@@ -115,7 +115,9 @@ def test_workspace_and_partition_queries(lib):
     pt = lib.pkv_paged_attention_partition_tokens
     # one partition covers the context -> no workspace
     assert ws(4, 4, 4, 64, 16, 13, 0) == 0
-    assert pt(4, 4, 16, 13, 0) in (256, 512)
+    assert pt(4, 4, 16, 13, 0) == 256
+    assert pt(32, 32, 16, 128, 0) == 2048     # 7B shape: one partition per sequence
+    assert pt(50, 8, 16, 2048, 0) == 2048
     # explicit partition length: B*H*P rows of (D + 2) floats, 256-byte aligned pieces
     P = 2048 * 16 // 512
     rows = 50 * 64 * P
