@@ -2,17 +2,21 @@
 """Decode-step benchmark for paged KV-cache attention on one MI355X.
 
 One step = the hot path once over one batch: write each sequence's new
-token into its tail-block slot (kv_cache_write, or the int8 quantising write)
-then attend every sequence's new query over its whole paged context
-(paged_attention_decode: the partition kernel, then the split-context
-reduce).  Inputs are seeded synthetic data already resident in HBM.
+token into its tail-block slot, then attend every sequence's new query over
+its whole paged context.  It is timed through the fused entry point
+(paged_attention_decode_step: the partition kernel appends the token and
+attends, then the split-context reduce runs when a context spans several
+partitions), and again as three launches (kv_cache_write or the int8
+quantising write, then paged_attention_decode's two kernels), reported under
+``unfused``.  Inputs are seeded synthetic data already resident in HBM.
 
 Prints ONE JSON line.  ``value`` is the KV bytes a step must read divided by
 the measured step time (GB/s) on the 7B-shaped MHA workload (batch 32,
 2048-token contexts, 32 heads x 128 dims, bf16, 16-token blocks).  The
 70B-shaped GQA workloads (bf16, and int8 KV) are reported under
 ``secondary``.  Per-kernel times come from HIP events recorded on the
-stream the kernels run on.
+stream the kernels run on: each kernel is also run alone, back to back, and
+its average duration is the roofline's time.
 
 Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1),
 --configs (which workloads), --partition-tokens, --cpu-seconds (bound of the
@@ -31,7 +35,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "paged decode-attn KV read GB/s (% of HBM peak) + µs/step, 7B & 70B shapes"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-KERNEL_SOURCES = ["decode_mfma.hip", "pkv_device.hpp", "pkv_kernels.hpp"]
+KERNEL_SOURCES = ["decode_mfma.hip", "decode_append.hpp", "pkv_device.hpp", "pkv_kernels.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.txt")
 
 DESCRIPTIONS = {
@@ -114,43 +118,41 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
         else:
             pkv.kv_cache_write(k_new, v_new, kc, vc, slot)
 
-    def step(evs=None):
-        if evs:
-            evs[0].record()
-        write()
-        if evs:
-            evs[1].record()
-        pkv.paged_attention_decode_partitions(*dargs, **dkw)
-        if evs:
-            evs[2].record()
-        pkv.paged_attention_decode_reduce(*dargs, **dkw)
-        if evs:
-            evs[3].record()
+    sargs = (out, q, k_new, v_new, kc, vc, bt, cl, w.scale, w.num_heads, w.num_kv_heads,
+             w.head_dim, w.block_size)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # whole-step time: K back-to-back steps between two events
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
-    # per-kernel times: events between the launches, same stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for e in evs:
-        step(e)
-    torch.cuda.synchronize()
-    per = [[e[i].elapsed_time(e[i + 1]) * 1e3 for i in range(3)] for e in evs]
-    med = lambda xs: sorted(xs)[len(xs) // 2]
-    write_us = med([p[0] for p in per])
-    part_us = [p[1] for p in per]
-    red_us = med([p[2] for p in per])
-    part_avg = sum(part_us) / len(part_us)
+    def step_fused():
+        # one step: append the new tokens and attend (+ reduce when split)
+        pkv.paged_attention_decode_step_partitions(*sargs, **dkw)
+        pkv.paged_attention_decode_reduce(*dargs, **dkw)
+
+    def step_unfused():
+        # the same step as three launches: cache write, partitions, reduce
+        write()
+        pkv.paged_attention_decode_partitions(*dargs, **dkw)
+        pkv.paged_attention_decode_reduce(*dargs, **dkw)
+
+    def loop_time(fn):
+        """Average duration of fn over K back-to-back launches (events on the launch stream)."""
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps * 1e3  # us
+
+    ms_per_step = loop_time(step_fused) / 1e3
+    ms_u = loop_time(step_unfused) / 1e3
+    # each kernel of the step alone, back to back (every launch is idempotent:
+    # the append and the cache write store the same token to the same slot)
+    part_avg = loop_time(lambda: pkv.paged_attention_decode_step_partitions(*sargs, **dkw))
+    red_us = loop_time(lambda: pkv.paged_attention_decode_reduce(*dargs, **dkw))
+    write_us = loop_time(write)
+    part_u_us = loop_time(lambda: pkv.paged_attention_decode_partitions(*dargs, **dkw))
     nbytes = kv_bytes(w)
     res = {
         "workload": DESCRIPTIONS[cfg] + (f" bs={block_size}" if block_size else ""),
@@ -161,15 +163,19 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
         "kv_gbs": nbytes / (ms_per_step * 1e-3) / 1e9,
         "pct_hbm_peak": 100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "tokens_per_s": w.attended_tokens / (ms_per_step * 1e-3),
-        "kernel_us": {"kv_cache_write": write_us, "decode_partitions_avg": part_avg,
-                      "decode_partitions_median": med(part_us), "decode_reduce": red_us},
+        "kernel_us": {"decode_step_partitions": part_avg, "decode_reduce": red_us},
+        "unfused": {"us_per_step": ms_u * 1e3,
+                    "kv_gbs": nbytes / (ms_u * 1e-3) / 1e9,
+                    "kernel_us": {"kv_cache_write": write_us, "decode_partitions": part_u_us,
+                                  "decode_reduce": red_us}},
         "partition_tokens": pkv.partition_tokens(w.num_seqs, w.num_kv_heads, w.block_size,
                                                  w.block_tables.shape[1], pt),
     }
     achieved = nbytes / (part_avg * 1e-6) / 1e9
     res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(w.name),
-                       "kernel": "decode_mfma_kernel" if w.kv_dtype != "f32" else "decode_f32_kernel"}
+                       "kernel": "decode_mfma_kernel (fused step: append + attend)"
+                       if w.kv_dtype != "f32" else "decode_f32_kernel (fused step)"}
     res["_w"] = w
     return res
 
@@ -284,6 +290,7 @@ def main():
         "tokens_per_s": head["tokens_per_s"],
         "kv_bytes_per_step": head["kv_bytes_per_step"],
         "kernel_us": head["kernel_us"],
+        "unfused": head["unfused"],
         "roofline": head["roofline"],
         "kernel_source_sha": kernel_source_sha(),
         "secondary": [{k: v for k, v in r.items()} for r in results[1:]],

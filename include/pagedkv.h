@@ -179,6 +179,42 @@ pkv_status pkv_paged_attention_decode_reduce(
     pkv_dtype kv_dtype, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
     void* stream);
 
+/*
+ * Fused decode step: append each sequence's new token, then attend.
+ *   For every sequence b with L = context_lens[b] >= 1, the token at
+ *   position L - 1 (its block is block_tables[b][(L-1) / bs], row
+ *   (L-1) % bs) receives k_new[b][h][:] and v_new[b][h][:] for every
+ *   kv-head h, exactly as pkv_kv_cache_write / pkv_kv_cache_write_int8 with
+ *   that slot would write it; then out is computed as by
+ *   pkv_paged_attention_decode over the updated cache.  One launch does
+ *   both (plus the reduce launch when a context spans several partitions):
+ *   the workgroups of the partition holding position L - 1 write the token
+ *   before attending, and nothing else reads it.
+ *   k_new, v_new: [B][Hkv][D], the cache element type (fp32 or bf16), or
+ *   fp32 for an int8 cache (quantised in the kernel).  The block holding
+ *   position L - 1 must belong to this sequence alone (copy it on write
+ *   first if it is shared).  Other arguments, errors and the workspace as
+ *   for pkv_paged_attention_decode; the caches (and int8 scales) are
+ *   written.
+ * _partitions: the first launch only (append + attend per partition); the
+ *   second is pkv_paged_attention_decode_reduce with the same arguments.
+ */
+pkv_status pkv_paged_attention_decode_step(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    float* k_scale, float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, pkv_dtype q_dtype,
+    pkv_dtype kv_dtype, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+pkv_status pkv_paged_attention_decode_step_partitions(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    float* k_scale, float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    float scale, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, pkv_dtype q_dtype,
+    pkv_dtype kv_dtype, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+    void* stream);
+
 /* Text of the last failure on this thread ("" after a successful call).
  * The pointer stays valid until the next call on the same thread. */
 const char* pkv_last_error(void);

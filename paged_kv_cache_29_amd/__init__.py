@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     paged_attention_decode,
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
+    paged_attention_decode_step,
+    paged_attention_decode_step_partitions,
     partition_tokens,
     workspace_size,
     load as load_library,

@@ -41,6 +41,8 @@ SIGNATURES = {
     "pkv_paged_attention_decode": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_partitions": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_reduce": (c_i32, _DECODE_ARGS),
+    "pkv_paged_attention_decode_step": (c_i32, _DECODE_ARGS[:2] + [c_vp, c_vp] + _DECODE_ARGS[2:]),
+    "pkv_paged_attention_decode_step_partitions": (c_i32, _DECODE_ARGS[:2] + [c_vp, c_vp] + _DECODE_ARGS[2:]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
@@ -234,3 +236,36 @@ def paged_attention_decode_reduce(*args, **kwargs):
     """Second of decode's two launches; same arguments as paged_attention_decode."""
     _check(load().pkv_paged_attention_decode_reduce(*_marshal_decode(*args, **kwargs)),
            "paged_attention_decode_reduce")
+
+
+def _marshal_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                  num_heads, num_kv_heads, head_dim, block_size, k_scale=None, v_scale=None,
+                  partition_tokens=0, workspace=None):
+    args = _marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_heads,
+                           num_kv_heads, head_dim, block_size, k_scale, v_scale, partition_tokens,
+                           workspace)
+    dev = q.device
+    want = torch.float32 if k_cache.dtype == torch.int8 else k_cache.dtype
+    for n, t in (("k_new", k_new), ("v_new", v_new)):
+        _dense_on(t, dev, n)
+        _need(tuple(t.shape) == (q.shape[0], num_kv_heads, head_dim), f"{n} must be [B, Hkv, D]")
+        _need(t.dtype == want, f"{n} must be {want}")
+    return args[:2] + (_ptr(k_new), _ptr(v_new)) + args[2:]
+
+
+def paged_attention_decode_step(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                context_lens, scale, num_heads, num_kv_heads, head_dim,
+                                block_size, k_scale=None, v_scale=None, partition_tokens=0,
+                                workspace=None):
+    """Fused decode step: append each sequence's new token at position L-1
+    (through its block table), then attend; writes ``out`` and the caches."""
+    args = _marshal_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                         num_heads, num_kv_heads, head_dim, block_size, k_scale, v_scale,
+                         partition_tokens, workspace)
+    _check(load().pkv_paged_attention_decode_step(*args), "paged_attention_decode_step")
+
+
+def paged_attention_decode_step_partitions(*args, **kwargs):
+    """First launch of the fused step; the second is paged_attention_decode_reduce."""
+    _check(load().pkv_paged_attention_decode_step_partitions(*_marshal_step(*args, **kwargs)),
+           "paged_attention_decode_step_partitions")

@@ -89,11 +89,7 @@ __global__ __launch_bounds__(256) void cache_write_int8_kernel(WriteParams p) {
     const float s = a / 127.0f;
     int codes[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float qv = 0.f;
-      if (s > 0.f) qv = fminf(fmaxf(rintf(x[e] / s), -127.f), 127.f);
-      codes[e] = static_cast<int>(qv);
-    }
+    for (int e = 0; e < 4; ++e) codes[e] = quantize_code(x[e], s);
     const int64_t blk = slot / BS;
     const int row = static_cast<int>(slot - blk * BS);
     const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * D;

@@ -1,0 +1,72 @@
+// Appending a sequence's new token inside a decode launch.
+//
+// The fused decode step writes each sequence's newest token (position
+// L - 1, through the block table) into the cache and then attends over the
+// whole context, in one launch.  Only the workgroups of the partition that
+// holds position L - 1 write, and each writes only its own kv-head's row, so
+// no other workgroup reads what is written.  The write is the same operation
+// as the slot-scatter cache write ("LLM Engineering (5)", "Block manager:
+// how paging works"); for an int8 cache it is the same quantisation as the
+// int8 cache write, through the same quantize_code().
+#pragma once
+
+#include <type_traits>
+
+#include "pkv_device.hpp"
+#include "pkv_kernels.hpp"
+
+namespace pkv {
+
+// Called by all threads of a workgroup of at least 2 * D threads (and at
+// least two waves); pos = L - 1 >= 0.
+template <typename KT, int D, int BS>
+__device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, int kvh, int pos) {
+  const int Hkv = p.num_kv_heads;
+  const int blk = p.block_tables[static_cast<size_t>(b) * p.max_blocks_per_seq + pos / BS];
+  const int row = pos % BS;
+  const size_t tile = (static_cast<size_t>(blk) * Hkv + kvh) * (static_cast<size_t>(BS) * D);
+  const size_t src = (static_cast<size_t>(b) * Hkv + kvh) * D;
+  KT* kc = static_cast<KT*>(const_cast<void*>(p.k_cache));
+  KT* vc = static_cast<KT*>(const_cast<void*>(p.v_cache));
+  const int t = threadIdx.x;
+  if constexpr (std::is_same<KT, int8_t>::value) {
+    // wave 0 quantises the K row, wave 1 the V row; lane owns dims lane + 64i
+    constexpr int ND = D / kWave;
+    const int wave = t / kWave;
+    const int lane = t % kWave;
+    if (wave < 2) {
+      const float* x = static_cast<const float*>(wave == 0 ? p.k_new : p.v_new) + src;
+      float v[ND];
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) {
+        v[i] = x[lane + kWave * i];
+        a = fmaxf(a, fabsf(v[i]));
+      }
+      a = wave_max(a);
+      const float s = a / 127.0f;
+#pragma unroll
+      for (int i = 0; i < ND; ++i) {
+        const int d = lane + kWave * i;
+        const int8_t code = static_cast<int8_t>(quantize_code(v[i], s));
+        if (wave == 0)
+          kc[tile + static_cast<size_t>(row) * D + d] = code;
+        else
+          vc[tile + static_cast<size_t>(d) * BS + row] = code;
+      }
+      if (lane == 0) {
+        float* sc = const_cast<float*>(wave == 0 ? p.k_scale : p.v_scale);
+        sc[(static_cast<size_t>(blk) * Hkv + kvh) * BS + row] = (s > 0.f) ? s : 0.f;
+      }
+    }
+  } else {
+    const KT* kn = static_cast<const KT*>(p.k_new) + src;
+    const KT* vn = static_cast<const KT*>(p.v_new) + src;
+    if (t < D)
+      kc[tile + static_cast<size_t>(row) * D + t] = kn[t];
+    else if (t < 2 * D)
+      vc[tile + static_cast<size_t>(t - D) * BS + row] = vn[t - D];
+  }
+}
+
+}  // namespace pkv

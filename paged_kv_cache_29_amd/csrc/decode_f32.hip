@@ -9,6 +9,7 @@
 // the online softmax of all G heads of the group (scores reduced across the
 // wave by shuffles).  The waves' states are merged through LDS.
 
+#include "decode_append.hpp"
 #include "pkv_device.hpp"
 #include "pkv_kernels.hpp"
 
@@ -45,6 +46,13 @@ __global__ __launch_bounds__(W * kWave) void decode_f32_kernel(DecodeParams p) {
   }
   const int t_end = min(L, t_begin + PT);
   const bool single = L <= PT;
+
+  // Fused step: the partition holding the newest token writes it first.
+  if (p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
+    append_new_token<float, D, BS>(p, b, kvh, L - 1);
+    __threadfence_block();
+    __syncthreads();
+  }
 
   float qv[kMaxGroup][ND];
   float m[kMaxGroup], l[kMaxGroup], acc[kMaxGroup][ND];

@@ -16,9 +16,8 @@
 // keeping its own online-softmax state; the states are merged through LDS at
 // the end.  A sequence that fits one partition is finished here; longer ones
 // leave (max, sum, unnormalised output) partials for the reduce kernel.
-// Each wave issues the loads of two chunks before consuming either, so 32 KB
-// (bf16, two waves per SIMD) or 16.5 KB (int8, three waves per SIMD) per wave
-// are in flight.
+// Each wave issues the loads of a batch of two chunks before consuming
+// either.
 //
 // Per 32-token chunk (two 16-token sub-tiles: two blocks at bs=16, the two
 // halves of one block at bs=32), one wave does:
@@ -44,6 +43,7 @@
 
 #include <type_traits>
 
+#include "decode_append.hpp"
 #include "pkv_device.hpp"
 #include "pkv_kernels.hpp"
 
@@ -63,13 +63,15 @@ __device__ __forceinline__ f32x4 load_f32x4(const float* p) {
 }
 
 // Two int8 codes (bytes 2*half and 2*half+1 of w) -> packed bf16 pair.
-// |code| <= 128 has at most 8 significant bits, so the conversion is exact.
+// |code| <= 128 has at most 8 significant bits, so the fp32 value is exact
+// and its upper half is the exact bf16; one byte permute packs both halves.
 __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int half) {
   const int32_t lo = static_cast<int32_t>(w << (24 - 16 * half)) >> 24;
   const int32_t hi = static_cast<int32_t>(w << (16 - 16 * half)) >> 24;
   const uint32_t flo = __float_as_uint(static_cast<float>(lo));
   const uint32_t fhi = __float_as_uint(static_cast<float>(hi));
-  return (flo >> 16) | (fhi & 0xffff0000u);
+  // result bytes (low to high): flo[2], flo[3], fhi[2], fhi[3]
+  return __builtin_amdgcn_perm(fhi, flo, 0x07060302u);
 }
 
 // 8 int8 codes -> one bf16x8 operand.
@@ -176,11 +178,16 @@ struct ChunkLoader {
 // Block ids one partition may span (its context / block_size).
 constexpr int kMaxPartBlocks = 128;
 
+// Chunks whose loads one wave issues together (32 KB of bf16 K/V, 16.5 KB of
+// int8 codes and scales), at two waves per SIMD.  Larger int8 batches were
+// measured slower.
+template <bool kInt8>
+constexpr int kBatch = 2;
+
 template <bool kInt8, int D, int BS, int W>
-__global__ __launch_bounds__(W * kWave)
-// two chunk buffers per wave: bf16 fits two waves per SIMD, int8 three
-__attribute__((amdgpu_waves_per_eu(kInt8 ? 3 : 2, kInt8 ? 3 : 2)))
+__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mfma_kernel(DecodeParams p) {
+  constexpr int NB = kBatch<kInt8>;
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
   constexpr int NJ = D / 32;  // QK MFMAs per score tile
@@ -217,6 +224,14 @@ void decode_mfma_kernel(DecodeParams p) {
   }
   const int t_end = min(L, t_begin + PT);
   const bool single = L <= PT;
+
+  // Fused step: the partition holding the newest token writes it first; the
+  // fence and barrier make the stores visible to this workgroup's loads.
+  if (p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
+    append_new_token<typename std::conditional<kInt8, int8_t, uint16_t>::type, D, BS>(p, b, kvh, L - 1);
+    __threadfence_block();
+    __syncthreads();
+  }
 
   // Q^T operand (B of the score MFMA): lane (c, g), MFMA j, 8 dims.
   bf16x8 qf[NJ];
@@ -370,29 +385,32 @@ void decode_mfma_kernel(DecodeParams p) {
     }
   };
 
-  // ---- this wave's chunks ch = wave, wave + W, ... two at a time: the loads
-  // of both are issued before either is consumed, and no load stays pending
-  // across iterations, so every wait counts exactly the loads behind it.
+  // ---- this wave's chunks ch = wave, wave + W, ... in batches of NB: the
+  // loads of the whole batch are issued before any chunk is consumed, and no
+  // load stays pending across iterations, so every wait counts exactly the
+  // loads behind it.  A batch is loaded and consumed last chunk first, so the
+  // full-batch and tail branches share no leading code the compiler could
+  // hoist, together with its waits, above the batch's other loads.
   const int nchunks = (t_end - t_begin + 31) / 32;
   {
-    Chunk<kInt8, D> ca, cb;
+    Chunk<kInt8, D> cb[NB];
     int blk[2], row0[2];
-    // (The pair is loaded and consumed later chunk first, so the two branches
-    // share no leading code the compiler could hoist, together with its
-    // waits, above the second chunk's loads.)
-    for (int ch = wave; ch < nchunks; ch += 2 * W) {
-      if (ch + W < nchunks) {
-        chunk_blocks(ch + W, blk, row0);
-        ld.load(cb, blk, row0);
-        chunk_blocks(ch, blk, row0);
-        ld.load(ca, blk, row0);
-        __builtin_amdgcn_sched_barrier(0);  // keep both chunks' loads ahead of the math
-        consume(cb, ch + W);
-        consume(ca, ch);
+    for (int ch = wave; ch < nchunks; ch += NB * W) {
+      if (ch + (NB - 1) * W < nchunks) {
+#pragma unroll
+        for (int k = NB - 1; k >= 0; --k) {
+          chunk_blocks(ch + k * W, blk, row0);
+          ld.load(cb[k], blk, row0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of the math
+#pragma unroll
+        for (int k = NB - 1; k >= 0; --k) consume(cb[k], ch + k * W);
       } else {
-        chunk_blocks(ch, blk, row0);
-        ld.load(ca, blk, row0);
-        consume(ca, ch);
+        for (int c2 = ch; c2 < nchunks; c2 += W) {
+          chunk_blocks(c2, blk, row0);
+          ld.load(cb[0], blk, row0);
+          consume(cb[0], c2);
+        }
       }
     }
   }

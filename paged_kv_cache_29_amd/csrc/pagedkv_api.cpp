@@ -94,7 +94,7 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                            int64_t num_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype,
                            int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                           DecodeSetup* st) {
+                           const void* k_new, const void* v_new, bool step, DecodeSetup* st) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
   if (num_heads <= 0 || num_kv_heads <= 0)
     return fail(PKV_ERR_INVALID, "num_heads and num_kv_heads must be positive");
@@ -139,6 +139,8 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
       return fail(PKV_ERR_INVALID, "null pointer among out, q, k_cache, v_cache, block_tables, context_lens");
   }
+  if (step && num_seqs > 0 && (!k_new || !v_new))
+    return fail(PKV_ERR_INVALID, "decode step needs k_new and v_new");
   if (kv == pkv::KvKind::I8) {
     if (num_seqs > 0 && (!k_scale || !v_scale))
       return fail(PKV_ERR_INVALID, "int8 cache needs k_scale and v_scale");
@@ -169,6 +171,8 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   p.ws_acc = need ? reinterpret_cast<float*>(ws) : nullptr;
   p.ws_m = need ? reinterpret_cast<float*>(ws + acc_bytes) : nullptr;
   p.ws_l = need ? reinterpret_cast<float*>(ws + acc_bytes + ml_bytes) : nullptr;
+  p.k_new = step ? k_new : nullptr;
+  p.v_new = step ? v_new : nullptr;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
@@ -291,7 +295,7 @@ size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads,
 
 pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
   DecodeSetup st;
-  pkv_status s = validate_decode(PKV_DECODE_ARGS, &st);
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
   s = launch_partitions(st, static_cast<hipStream_t>(stream));
@@ -303,7 +307,7 @@ pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
 
 pkv_status pkv_paged_attention_decode_partitions(PKV_DECODE_PARAMS) {
   DecodeSetup st;
-  pkv_status s = validate_decode(PKV_DECODE_ARGS, &st);
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
   s = launch_partitions(st, static_cast<hipStream_t>(stream));
@@ -313,10 +317,40 @@ pkv_status pkv_paged_attention_decode_partitions(PKV_DECODE_PARAMS) {
 
 pkv_status pkv_paged_attention_decode_reduce(PKV_DECODE_PARAMS) {
   DecodeSetup st;
-  pkv_status s = validate_decode(PKV_DECODE_ARGS, &st);
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
   s = launch_reduce(st, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
+  return ok();
+}
+
+#define PKV_STEP_PARAMS                                                                      \
+  void *out, const void *q, const void *k_new, const void *v_new, void *k_cache,             \
+      void *v_cache, float *k_scale, float *v_scale, const int32_t *block_tables,            \
+      const int32_t *context_lens, float scale, int32_t num_seqs, int32_t num_heads,         \
+      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, \
+      int64_t num_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t partition_tokens,   \
+      void *workspace, size_t workspace_bytes, void *stream
+
+pkv_status pkv_paged_attention_decode_step(PKV_STEP_PARAMS) {
+  DecodeSetup st;
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, k_new, v_new, true, &st);
+  if (s != PKV_OK) return s;
+  if (num_seqs == 0) return ok();
+  s = launch_partitions(st, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
+  s = launch_reduce(st, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
+  return ok();
+}
+
+pkv_status pkv_paged_attention_decode_step_partitions(PKV_STEP_PARAMS) {
+  DecodeSetup st;
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, k_new, v_new, true, &st);
+  if (s != PKV_OK) return s;
+  if (num_seqs == 0) return ok();
+  s = launch_partitions(st, static_cast<hipStream_t>(stream));
   if (s != PKV_OK) return s;
   return ok();
 }

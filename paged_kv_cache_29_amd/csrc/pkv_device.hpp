@@ -43,6 +43,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// int8 code of x for a row scale s = absmax / 127 (IEEE fp32 division, round
+// half to even, clamp to +-127); s == 0 means an all-zero (or underflowed)
+// row and gives 0.  Used by every int8 writer so their codes agree bit for bit.
+__device__ __forceinline__ int quantize_code(float x, float s) {
+  if (!(s > 0.f)) return 0;
+  return static_cast<int>(fminf(fmaxf(rintf(x / s), -127.f), 127.f));
+}
+
 // Combine a value across the four 16-lane groups of a wave (lanes l, l^16,
 // l^32, l^48), without lane-index registers: ds_swizzle swaps 16-lane
 // halves of each 32-lane group, v_permlane32_swap exchanges the two 32-lane

@@ -24,6 +24,11 @@ struct DecodeParams {
   float* ws_acc;
   float* ws_m;
   float* ws_l;
+  // Optional new token per sequence, [B][Hkv][D] (cache element type; fp32
+  // for an int8 cache): when non-null, the partition holding position L-1
+  // writes it there through the block table before attending.
+  const void* k_new;
+  const void* v_new;
   float scale_log2;  // scale * log2(e)
   int32_t num_seqs;
   int32_t num_heads;

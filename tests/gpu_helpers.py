@@ -87,6 +87,21 @@ class DeviceWorkload:
                                    v_scale=self.v_scale, partition_tokens=partition_tokens)
         return out
 
+    def step_fused(self, partition_tokens=0, out=None):
+        """The hot path in one call: append the new tokens, then attend."""
+        w = self.w
+        if w.kv_dtype == "i8" and not getattr(self, "_filled", False):
+            self.fill_int8()
+            self._filled = True
+        out = self.out if out is None else out
+        pkv.paged_attention_decode_step(out, self.q, self.k_new, self.v_new, self.k_cache,
+                                        self.v_cache, self.block_tables, self.context_lens,
+                                        w.scale, w.num_heads, w.num_kv_heads, w.head_dim,
+                                        w.block_size, k_scale=self.k_scale, v_scale=self.v_scale,
+                                        partition_tokens=partition_tokens)
+        torch.cuda.synchronize()
+        return out_f64(out)
+
     def step(self, partition_tokens=0):
         """The hot path: write the new tokens, then attend over the cache."""
         if self.w.kv_dtype == "i8" and not getattr(self, "_filled", False):

@@ -1,0 +1,49 @@
+"""GPU: the fused decode step (append the new token, then attend) equals
+the cache write followed by decode, and the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_29_amd import workloads
+
+from gpu_helpers import DeviceWorkload, assert_parity, bf16_bits_of, oracle_out
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 64, 100, 255, 256, 257, 700, 2049]
+
+
+def _cache_bytes(dw):
+    parts = [dw.k_cache.cpu().view(torch.uint8).numpy(), dw.v_cache.cpu().view(torch.uint8).numpy()]
+    if dw.k_scale is not None:
+        parts += [dw.k_scale.cpu().view(torch.int32).numpy(), dw.v_scale.cpu().view(torch.int32).numpy()]
+    return parts
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8", "f32"])
+@pytest.mark.parametrize("G,D,bs,pt", [(1, 128, 16, 0), (8, 128, 16, 64), (4, 64, 32, 0), (16, 128, 32, 512)])
+def test_fused_step_equals_write_then_decode(kv, G, D, bs, pt):
+    Hkv = 2
+    w = workloads.make_custom(200 + G + bs, RAGGED, G * Hkv, Hkv, D, bs, kv_dtype=kv)
+    a, b = DeviceWorkload(w), DeviceWorkload(w)
+    ref = a.step(partition_tokens=pt)            # write kernel, then decode
+    got = b.step_fused(partition_tokens=pt)      # one fused call
+    assert np.array_equal(got, ref), "fused step differs from write + decode"
+    for x, y in zip(_cache_bytes(a), _cache_bytes(b)):
+        assert np.array_equal(x, y), "caches differ after the step"
+    assert_parity(got, oracle_out(w), kv, f"fused {kv} G={G} D={D} bs={bs}")
+
+
+def test_fused_step_full_size_7b():
+    w = workloads.make_config(2, 0)
+    dw = DeviceWorkload(w)
+    got = dw.step_fused()
+    samples = [(0, 0), (5, 31), (31, 7), (17, 17)]
+    ref = oracle_out(w, samples=samples)
+    for bb, h in samples:
+        assert_parity(got[bb, h], ref[bb, h], "bf16", f"7B fused (b={bb}, h={h})")
+    # the new token landed in its slot
+    s = int(w.slot_new[3])
+    k_row = bf16_bits_of(dw.k_cache[s // 16, :, s % 16, :])
+    assert np.array_equal(k_row, w.k_new[3])
