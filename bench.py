@@ -145,15 +145,35 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / args.steps * 1e3  # us
 
+    def per_step(fn):
+        """Per-step durations: one event between consecutive steps."""
+        n = max(args.steps, 2)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs[0].record()
+        for i in range(n):
+            fn()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        d = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n))
+        q = lambda f: d[min(n - 1, int(round(f * (n - 1))))]
+        return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
+
     ms_per_step = loop_time(step_fused) / 1e3
     ms_u = loop_time(step_unfused) / 1e3
-    # each kernel of the step alone, back to back (every launch is idempotent:
-    # the append and the cache write store the same token to the same slot)
+    # the partition kernels alone, back to back (every launch is idempotent:
+    # the append and the cache write store the same token to the same slot).
+    # The few-microsecond kernels (reduce, cache write) are given as their
+    # share of the step: looped alone they would time the host's launch rate.
     part_avg = loop_time(lambda: pkv.paged_attention_decode_step_partitions(*sargs, **dkw))
-    red_us = loop_time(lambda: pkv.paged_attention_decode_reduce(*dargs, **dkw))
-    write_us = loop_time(write)
     part_u_us = loop_time(lambda: pkv.paged_attention_decode_partitions(*dargs, **dkw))
+    red_us = max(0.0, ms_per_step * 1e3 - part_avg)
+    write_us = max(0.0, ms_u * 1e3 - part_u_us - red_us)
+    dist = per_step(step_fused)
     nbytes = kv_bytes(w)
+    uniq = unique_tile_bytes(w)
     res = {
         "workload": DESCRIPTIONS[cfg] + (f" bs={block_size}" if block_size else ""),
         "name": w.name,
@@ -163,11 +183,14 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
         "kv_gbs": nbytes / (ms_per_step * 1e-3) / 1e9,
         "pct_hbm_peak": 100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "tokens_per_s": w.attended_tokens / (ms_per_step * 1e-3),
-        "kernel_us": {"decode_step_partitions": part_avg, "decode_reduce": red_us},
+        "us_per_step_events": dist,
+        "kernel_us": {"decode_step_partitions": part_avg, "decode_reduce_share": red_us},
         "unfused": {"us_per_step": ms_u * 1e3,
                     "kv_gbs": nbytes / (ms_u * 1e-3) / 1e9,
-                    "kernel_us": {"kv_cache_write": write_us, "decode_partitions": part_u_us,
-                                  "decode_reduce": red_us}},
+                    "kernel_us": {"kv_cache_write_share": write_us, "decode_partitions": part_u_us,
+                                  "decode_reduce_share": red_us}},
+        "unique_tile_bytes": uniq,
+        "unique_gbs": uniq / (ms_per_step * 1e-3) / 1e9,
         "partition_tokens": pkv.partition_tokens(w.num_seqs, w.num_kv_heads, w.block_size,
                                                  w.block_tables.shape[1], pt),
     }
@@ -178,6 +201,50 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
                        if w.kv_dtype != "f32" else "decode_f32_kernel (fused step)"}
     res["_w"] = w
     return res
+
+
+def unique_tile_bytes(w):
+    """K and V bytes of the distinct (block, kv-head) tiles the step touches:
+    what a step must read at least when shared blocks are read once."""
+    import numpy as np
+    bs = w.block_size
+    ids = set()
+    for b, L in enumerate(w.context_lens):
+        n = (int(L) + bs - 1) // bs
+        ids.update(int(x) for x in w.block_tables[b, :n])
+    elem = 1 if w.kv_dtype == "i8" else (4 if w.kv_dtype == "f32" else 2)
+    scale = 4 if w.kv_dtype == "i8" else 0
+    return int(len(ids) * 2 * w.num_kv_heads * bs * (w.head_dim * elem + scale))
+
+
+def read_ceiling(torch, pkv, steps=20):
+    """The device's read rate for the decode kernel's access pattern: 2 GiB
+    of 4 KB tiles gathered in a shuffled order by the tile-read probe (run
+    after the workloads, so the clocks are up; ids range-checked once)."""
+    import numpy as np
+    n = 2 << 30
+    pool = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    ids = torch.from_numpy(np.random.default_rng(0).permutation(n // 4096).astype(np.int32)).to("cuda:0")
+    best = None
+    for grid in (2048, 4096, 8192):
+        sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda:0")
+        pkv.probe_tile_read(pool, ids, sink, grid, check_ids=True)
+        for _ in range(3):
+            pkv.probe_tile_read(pool, ids, sink, grid, check_ids=False)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            pkv.probe_tile_read(pool, ids, sink, grid, check_ids=False)
+        t1.record()
+        torch.cuda.synchronize()
+        gbs = n / (t0.elapsed_time(t1) / steps * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": gbs, "grid": grid}
+    del pool, ids
+    torch.cuda.empty_cache()
+    best["probe"] = "pkv_probe_tile_read: 2 GiB of shuffled 4 KB tiles, best grid"
+    return best
 
 
 def cpu_baseline(w, seconds):
@@ -231,8 +298,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--configs", default="2,3,5", help="first is the headline workload")
-    ap.add_argument("--block-size", type=int, default=None, help="for config 4")
+    ap.add_argument("--configs", default="2,3,5,4", help="first is the headline workload")
+    ap.add_argument("--block-size", type=int, default=16, help="for config 4 (16 or 32)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -264,6 +331,10 @@ def main():
               file=sys.stderr, flush=True)
         results.append(r)
         torch.cuda.empty_cache()
+    print("[bench] read ceiling probe ...", file=sys.stderr, flush=True)
+    ceiling = read_ceiling(torch, pkv)
+    for r in results:
+        r["roofline"]["frac_of_read_ceiling"] = r["roofline"]["achieved"] / ceiling["gbs"]
     head = results[0]
     w = head.pop("_w")
     for r in results[1:]:
@@ -292,6 +363,8 @@ def main():
         "kernel_us": head["kernel_us"],
         "unfused": head["unfused"],
         "roofline": head["roofline"],
+        "us_per_step_events": head["us_per_step_events"],
+        "read_ceiling": ceiling,
         "kernel_source_sha": kernel_source_sha(),
         "secondary": [{k: v for k, v in r.items()} for r in results[1:]],
     }

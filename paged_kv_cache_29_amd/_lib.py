@@ -43,6 +43,7 @@ SIGNATURES = {
     "pkv_paged_attention_decode_reduce": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_step": (c_i32, _DECODE_ARGS[:2] + [c_vp, c_vp] + _DECODE_ARGS[2:]),
     "pkv_paged_attention_decode_step_partitions": (c_i32, _DECODE_ARGS[:2] + [c_vp, c_vp] + _DECODE_ARGS[2:]),
+    "pkv_probe_tile_read": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_vp, c_vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
@@ -269,3 +270,25 @@ def paged_attention_decode_step_partitions(*args, **kwargs):
     """First launch of the fused step; the second is paged_attention_decode_reduce."""
     _check(load().pkv_paged_attention_decode_step_partitions(*_marshal_step(*args, **kwargs)),
            "paged_attention_decode_step_partitions")
+
+
+def probe_tile_read(pool, tile_ids, sink, grid, check_ids=True):
+    """Measurement aid: read the 4096-byte tiles ``pool[4096*id : 4096*(id+1)]``
+    for every id in ``tile_ids`` (the decode kernel's access pattern, no
+    arithmetic); ``sink`` is uint32-sized ``[grid * 256]`` and is overwritten.
+
+    ``check_ids`` range-checks the ids first (a device reduction and a
+    synchronisation); a timing loop checks once and then passes False."""
+    dev = pool.device
+    for n, t in (("pool", pool), ("tile_ids", tile_ids), ("sink", sink)):
+        _dense_on(t, dev, n)
+    _need(tile_ids.dtype == torch.int32 and tile_ids.dim() == 1, "tile_ids must be int32 [N]")
+    _need(sink.numel() * sink.element_size() >= 4 * 256 * int(grid), "sink must hold grid * 256 uint32")
+    pool_tiles = pool.numel() * pool.element_size() // 4096
+    _need(pool.numel() * pool.element_size() % 4096 == 0, "pool must be whole 4096-byte tiles")
+    if check_ids and tile_ids.numel():  # an id outside the pool would be a memory fault
+        _need(int(tile_ids.min()) >= 0 and int(tile_ids.max()) < pool_tiles,
+              "tile_ids must name tiles inside pool")
+    st = load().pkv_probe_tile_read(_ptr(pool), _ptr(tile_ids), tile_ids.numel(), int(grid),
+                                    _ptr(sink), _stream(dev))
+    _check(st, "probe_tile_read")

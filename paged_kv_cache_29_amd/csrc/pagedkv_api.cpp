@@ -8,6 +8,7 @@
 #include <string>
 
 #include "../../include/pagedkv.h"
+#include "../../include/pagedkv_probe.h"
 #include "pkv_kernels.hpp"
 
 namespace {
@@ -352,6 +353,20 @@ pkv_status pkv_paged_attention_decode_step_partitions(PKV_STEP_PARAMS) {
   if (num_seqs == 0) return ok();
   s = launch_partitions(st, static_cast<hipStream_t>(stream));
   if (s != PKV_OK) return s;
+  return ok();
+}
+
+pkv_status pkv_probe_tile_read(const void* pool, const int32_t* tile_ids, int64_t num_tiles,
+                               int32_t grid, uint32_t* sink, void* stream) {
+  if (!pool || !tile_ids || !sink) return fail(PKV_ERR_INVALID, "probe_tile_read: null pointer");
+  if (reinterpret_cast<uintptr_t>(pool) % 4096 != 0)
+    return fail(PKV_ERR_INVALID, "probe_tile_read: pool is not 4096-byte aligned");
+  if (num_tiles < 0) return fail(PKV_ERR_INVALID, "probe_tile_read: num_tiles < 0");
+  if (grid < 1 || grid > 65536) return fail(PKV_ERR_INVALID, "probe_tile_read: grid %d not in [1, 65536]", grid);
+  if (num_tiles == 0) return ok();
+  const hipError_t e = pkv::launch_tile_read(pool, tile_ids, num_tiles, grid, sink,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "probe_tile_read launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

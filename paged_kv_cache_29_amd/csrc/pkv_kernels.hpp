@@ -64,5 +64,7 @@ hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, hipStream_t s);
 hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
 hipError_t launch_cache_write_int8(const WriteParams& p, hipStream_t s);
+hipError_t launch_tile_read(const void* pool, const int32_t* ids, int64_t ntiles, int grid,
+                            uint32_t* sink, hipStream_t s);
 
 }  // namespace pkv
