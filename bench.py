@@ -18,6 +18,10 @@ the measured step time (GB/s) on the 7B-shaped MHA workload (batch 32,
 stream the kernels run on: each kernel is also run alone, back to back, and
 its average duration is the roofline's time.
 
+Before each workload's warm-up steps the step also runs, untimed, for
+--settle-seconds (0.3 s): the GPU's clocks drop while the host builds a
+workload, and the first timed loop would otherwise measure their ramp.
+
 Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1),
 --configs (which workloads), --partition-tokens, --cpu-seconds (bound of the
 CPU oracle baseline; 0 disables it), --copy-calibration (only run a 1 GiB
@@ -161,6 +165,14 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
         q = lambda f: d[min(n - 1, int(round(f * (n - 1))))]
         return {"p10": q(0.1), "median": q(0.5), "p90": q(0.9)}
 
+    # Clocks drop while the host builds a workload; run untimed steps for a
+    # while so the first timed loop does not measure the ramp back up.
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for _ in range(10):
+            step_fused()
+        torch.cuda.synchronize()
+
     ms_per_step = loop_time(step_fused) / 1e3
     ms_u = loop_time(step_unfused) / 1e3
     # the partition kernels alone, back to back (every launch is idempotent:
@@ -302,6 +314,8 @@ def main():
     ap.add_argument("--block-size", type=int, default=16, help="for config 4 (16 or 32)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="untimed steps before each workload's first warm-up, so clocks have settled")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -19,7 +19,9 @@
  *            tables, 47 tokens -> 16+16+15), "Block manager: how paging
  *            works" (append a block to the table, copy-on-write sharing),
  *            "KV-cache quantization" (per-token-per-head scales computed
- *            online), "INT8 weight-only quantization" (q = round(x / s)).
+ *            online), "INT8 weight-only quantization" (q = round(x / s)),
+ *            "SGLang and RadixAttention" (the longest shared prefix is
+ *            reused, only the rest is computed per request).
  *   [LAYERS] four-layer inference-optimization article
  *            (gsyq.cn/news/366077), 2.2 (block size 16 or 32) and 2.3
  *            (per-token scales; K and V quantized separately).
@@ -214,6 +216,60 @@ pkv_status pkv_paged_attention_decode_step_partitions(
     int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks, pkv_dtype q_dtype,
     pkv_dtype kv_dtype, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
     void* stream);
+
+/*
+ * Shared-prefix ("cascade") decode: the same attention as
+ * pkv_paged_attention_decode, with the blocks a group of sequences shares
+ * read once for the whole group ([ENG5] "Paged attention": requests with a
+ * common prefix share physical blocks, the basis of prompt caching; [ENG5]
+ * "SGLang and RadixAttention": the longest shared prefix is reused and only
+ * the rest is computed per request).
+ *   Groups are contiguous ranges of sequences: group g is sequences
+ *   group_start[g] .. group_start[g+1]-1, with group_start[0] = 0,
+ *   non-decreasing, group_start[num_groups] = num_seqs (device int32
+ *   [num_groups + 1]).  group_shared_blocks[g] (device int32 [num_groups])
+ *   is how many leading block-table entries every member of group g has in
+ *   common with the group's first member.  The group's shared span is
+ *     S_g = min(group_shared_blocks[g], max_shared_blocks,
+ *               context_lens[first member] / block_size) * block_size
+ *   tokens; they are attended once per group (queries of all members
+ *   together), each member's remaining tokens S_g .. L-1 as in decode, and
+ *   the partials are merged per (sequence, head) by the split-context
+ *   combine, so out equals pkv_paged_attention_decode's result up to
+ *   rounding.  Groups of one sequence or with no shared blocks are plain
+ *   decode.
+ *   Host-side bounds (the grid is sized from them): num_groups in
+ *   [1, num_seqs]; max_group_size >= every group's size, <= num_seqs;
+ *   max_shared_blocks in [0, max_blocks_per_seq].
+ *   prefix_partition_tokens: tokens of the shared span per workgroup; 0 for
+ *   the automatic choice, else a multiple of 32 in [32, 128 * block_size].
+ *   partition_tokens as for decode (for the remaining tokens).
+ * Supported: (BF16, BF16) and (BF16, I8) with the sizes of decode; an fp32
+ * cache returns PKV_ERR_UNSUPPORTED.  The workspace size comes from
+ * pkv_paged_attention_cascade_workspace_size with the same sizes and is
+ * needed whenever num_seqs > 0.  Three launches: prefix kernel (skipped when
+ * max_shared_blocks is 0), partition kernel, reduce.
+ * Not checked (device data): the group arrays as stated above; every
+ * member's context_lens >= S_g; the shared entries really are equal (if not,
+ * the first member's blocks are used for the whole group).
+ */
+pkv_status pkv_paged_attention_decode_cascade(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* group_start, const int32_t* group_shared_blocks, float scale, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t max_shared_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t partition_tokens,
+    int32_t prefix_partition_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes of pkv_paged_attention_decode_cascade for these sizes
+ * (0 for invalid sizes, or num_seqs == 0).
+ */
+size_t pkv_paged_attention_cascade_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_groups, int32_t max_group_size,
+    int32_t max_shared_blocks, int32_t partition_tokens, int32_t prefix_partition_tokens);
 
 /* Text of the last failure on this thread ("" after a successful call).
  * The pointer stays valid until the next call on the same thread. */

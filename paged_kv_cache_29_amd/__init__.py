@@ -9,7 +9,9 @@ block allocator (free list, refcounts, copy-on-write).
 from ._lib import (  # noqa: F401
     kv_cache_write,
     kv_cache_write_int8,
+    cascade_workspace_size,
     paged_attention_decode,
+    paged_attention_decode_cascade,
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
     paged_attention_decode_step,

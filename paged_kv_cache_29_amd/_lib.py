@@ -43,6 +43,10 @@ SIGNATURES = {
     "pkv_paged_attention_decode_reduce": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_step": (c_i32, _DECODE_ARGS[:2] + [c_vp, c_vp] + _DECODE_ARGS[2:]),
     "pkv_paged_attention_decode_step_partitions": (c_i32, _DECODE_ARGS[:2] + [c_vp, c_vp] + _DECODE_ARGS[2:]),
+    "pkv_paged_attention_decode_cascade": (c_i32, _DECODE_ARGS[:8] + [c_vp, c_vp] + _DECODE_ARGS[8:16]
+                                           + [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                              c_vp, c_size, c_vp]),
+    "pkv_paged_attention_cascade_workspace_size": (c_size, [c_i32] * 11),
     "pkv_probe_tile_read": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_vp, c_vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
@@ -164,6 +168,7 @@ def workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_
 
 
 _ws_cache = {}
+_NO_WORKSPACE = object()
 
 
 def _workspace(device, nbytes):
@@ -204,6 +209,11 @@ def _marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
             _need(t.dtype == torch.float32 and tuple(t.shape) == (NB, num_kv_heads, block_size),
                   f"{n} must be float32 [NB, Hkv, bs]")
     MB = block_tables.shape[1]
+    if workspace is _NO_WORKSPACE:  # the caller sizes its own workspace
+        return (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                _ptr(k_scale if kd == PKV_I8 else None), _ptr(v_scale if kd == PKV_I8 else None),
+                _ptr(block_tables), _ptr(context_lens), float(scale), B, num_heads, num_kv_heads,
+                head_dim, block_size, MB, NB, qd, kd, int(partition_tokens), None, 0, _stream(dev))
     need = workspace_size(B, num_heads, num_kv_heads, head_dim, block_size, MB, partition_tokens)
     if workspace is None:
         workspace = _workspace(dev, need) if need else None
@@ -215,6 +225,52 @@ def _marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
             _ptr(block_tables), _ptr(context_lens), float(scale), B, num_heads, num_kv_heads,
             head_dim, block_size, MB, NB, qd, kd, int(partition_tokens), _ptr(workspace),
             ws_bytes, _stream(dev))
+
+
+def cascade_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                           max_blocks_per_seq, num_groups, max_group_size, max_shared_blocks,
+                           partition_tokens=0, prefix_partition_tokens=0):
+    return int(load().pkv_paged_attention_cascade_workspace_size(
+        num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_groups,
+        max_group_size, max_shared_blocks, partition_tokens, prefix_partition_tokens))
+
+
+def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   group_start, group_shared_blocks, scale, num_heads,
+                                   num_kv_heads, head_dim, block_size, max_group_size,
+                                   max_shared_blocks, k_scale=None, v_scale=None,
+                                   partition_tokens=0, prefix_partition_tokens=0,
+                                   workspace=None):
+    """Decode attention with each group's shared blocks read once for the group.
+
+    ``group_start`` (int32 ``[num_groups + 1]``) and ``group_shared_blocks``
+    (int32 ``[num_groups]``) are device tensors; ``max_group_size`` and
+    ``max_shared_blocks`` are host-side bounds on them (see
+    ``blocks.cascade_groups``, which computes all four from block tables)."""
+    dev = q.device
+    for n, t in (("group_start", group_start), ("group_shared_blocks", group_shared_blocks)):
+        _dense_on(t, dev, n)
+        _need(t.dtype == torch.int32 and t.dim() == 1, f"{n} must be int32 1-D")
+    G = group_shared_blocks.numel()
+    _need(group_start.numel() == G + 1, "group_start must have num_groups + 1 entries")
+    args = list(_marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                num_heads, num_kv_heads, head_dim, block_size, k_scale, v_scale,
+                                partition_tokens, workspace=_NO_WORKSPACE))
+    B, MB = q.shape[0], block_tables.shape[1]
+    need = cascade_workspace_size(B, num_heads, num_kv_heads, head_dim, block_size, MB, G,
+                                  max_group_size, max_shared_blocks, partition_tokens,
+                                  prefix_partition_tokens)
+    if workspace is None:
+        workspace = _workspace(dev, need) if need else None
+    else:
+        _dense_on(workspace, dev, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    # decode's arguments up to num_blocks, then the cascade's
+    st = load().pkv_paged_attention_decode_cascade(
+        *args[:8], _ptr(group_start), _ptr(group_shared_blocks), *args[8:16], G,
+        int(max_group_size), int(max_shared_blocks), args[16], args[17], args[18],
+        int(prefix_partition_tokens), _ptr(workspace), ws_bytes, args[21])
+    _check(st, "paged_attention_decode_cascade")
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,

@@ -152,3 +152,49 @@ class BlockAllocator:
         assert len(free) == len(self._free), "block on free list twice"
         assert free == {b for b in range(self.num_blocks) if ref[b] == 0}, "free list mismatch"
         return True
+
+
+def cascade_groups(block_tables, context_lens, block_size, min_shared_blocks=1):
+    """Groups of consecutive sequences that share leading blocks.
+
+    A group starts at a sequence (its first member); the next sequence
+    joins when it shares at least ``min_shared_blocks`` leading table
+    entries with the first member, which fixes the group's shared count; a
+    later sequence joins while it shares at least that many.  Only whole
+    blocks inside both contexts count.  Returns ``(group_start int32
+    [NG + 1], group_shared_blocks int32 [NG], max_group_size,
+    max_shared_blocks)``, the arguments of the shared-prefix decode
+    ([ENG5] "Paged attention": requests with a common prefix hold the same
+    physical blocks).  Sequences that share nothing are groups of one with
+    0 shared blocks.
+    """
+    tables = np.asarray(block_tables)
+    lens = np.asarray(context_lens, dtype=np.int64)
+    B = len(lens)
+    full = lens // int(block_size)
+
+    def common(a, b):
+        n = int(min(full[a], full[b]))
+        ta, tb = tables[a, :n], tables[b, :n]
+        diff = np.nonzero(ta != tb)[0]
+        return int(diff[0]) if len(diff) else n
+
+    starts, shared = [], []
+    b = 0
+    while b < B:
+        lead, cnt, size = b, 0, 1
+        b += 1
+        if b < B:
+            c = common(lead, b)
+            if c >= max(1, int(min_shared_blocks)):
+                cnt = c
+                while b < B and common(lead, b) >= cnt:
+                    b += 1
+                    size += 1
+        starts.append(lead)
+        shared.append(cnt)
+    group_start = np.array(starts + [B], dtype=np.int32)
+    group_shared = np.array(shared, dtype=np.int32)
+    sizes = np.diff(group_start)
+    return (group_start, group_shared, int(sizes.max()) if B else 0,
+            int(group_shared.max()) if B else 0)

@@ -44,139 +44,14 @@
 #include <type_traits>
 
 #include "decode_append.hpp"
+#include "decode_tile.hpp"
 #include "pkv_device.hpp"
 #include "pkv_kernels.hpp"
 
 namespace pkv {
 namespace {
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-__device__ __forceinline__ u32x4 load_u32x4(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ u32x2 load_u32x2(const void* p) {
-  return *reinterpret_cast<const u32x2*>(p);
-}
-__device__ __forceinline__ f32x4 load_f32x4(const float* p) {
-  return *reinterpret_cast<const f32x4*>(p);
-}
-
-// Two int8 codes (bytes 2*half and 2*half+1 of w) -> packed bf16 pair.
-// |code| <= 128 has at most 8 significant bits, so the fp32 value is exact
-// and its upper half is the exact bf16; one byte permute packs both halves.
-__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int half) {
-  const int32_t lo = static_cast<int32_t>(w << (24 - 16 * half)) >> 24;
-  const int32_t hi = static_cast<int32_t>(w << (16 - 16 * half)) >> 24;
-  const uint32_t flo = __float_as_uint(static_cast<float>(lo));
-  const uint32_t fhi = __float_as_uint(static_cast<float>(hi));
-  // result bytes (low to high): flo[2], flo[3], fhi[2], fhi[3]
-  return __builtin_amdgcn_perm(fhi, flo, 0x07060302u);
-}
-
-// 8 int8 codes -> one bf16x8 operand.
-__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  return as_bf16x8(u32x4{i8pair_to_bf16x2(w0, 0), i8pair_to_bf16x2(w0, 1),
-                         i8pair_to_bf16x2(w1, 0), i8pair_to_bf16x2(w1, 1)});
-}
-
-// Zero the bf16 elements (pairs packed in w) whose token is >= t_end.
-__device__ __forceinline__ uint32_t mask_pair(uint32_t w, int tok, int t_end) {
-  const uint32_t lo = (tok < t_end) ? (w & 0xffffu) : 0u;
-  const uint32_t hi = (tok + 1 < t_end) ? (w & 0xffff0000u) : 0u;
-  return lo | hi;
-}
-
-// Raw loads of one 32-token chunk for one lane.  The chunk is two 16-token
-// sub-tiles h = 0, 1 (two blocks at bs = 16, the two halves of one block at
-// bs = 32).
-template <bool kInt8, int D>
-struct Chunk {
-  static constexpr int NJ = D / 32;
-  static constexpr int NN = D / 16;
-  // K rows: per sub-tile h, NJ operands of 8 dims (bf16: 16 B each; int8:
-  // one 16-byte load feeds two operands, so NJ/2 loads)
-  u32x4 k[2][kInt8 ? NJ / 2 : NJ];
-  // V^T: per sub-tile h and dim block n, tokens 4g .. 4g+3 of dim 16n + c
-  // (bf16: 8 B; int8: 4 B)
-  typename std::conditional<kInt8, uint32_t, u32x2>::type v[2][NN];
-  f32x4 ks[2], vs[2];  // int8 scales of sub-tile tokens 4g .. 4g+3
-};
-
-// Buffer-resource word 3 for raw (untyped, unswizzled) buffers on gfx9-class
-// GPUs: 32-bit data format, no stride.
-constexpr int kBufferFlags = 0x00020000;
-
-template <bool kInt8, int D, int BS>
-struct ChunkLoader {
-  using KT = typename std::conditional<kInt8, int8_t, uint16_t>::type;
-  static constexpr uint32_t kElem = sizeof(KT);
-  static constexpr uint32_t kTileBytes = BS * D * kElem;
-  const char* kc;   // cache base addresses (bytes)
-  const char* vc;
-  const char* ksc;  // int8 scale arrays (bytes)
-  const char* vsc;
-  int Hkv, kvh;
-  // loop-invariant per-lane byte offsets inside a (block, kv-head) tile
-  uint32_t koff, voff, soff;
-
-  __device__ __forceinline__ ChunkLoader(const DecodeParams& p, int kvh_, int c, int g)
-      : kc(static_cast<const char*>(p.k_cache)), vc(static_cast<const char*>(p.v_cache)),
-        ksc(reinterpret_cast<const char*>(p.k_scale)), vsc(reinterpret_cast<const char*>(p.v_scale)),
-        Hkv(p.num_kv_heads), kvh(kvh_) {
-    // K: row c of the sub-tile; dims 32j + 8g (bf16) or 64jj + 16g (int8)
-    koff = (static_cast<uint32_t>(c) * D + (kInt8 ? 16u : 8u) * g) * kElem;
-    // V^T: dim c (+16n per load), tokens 4g .. 4g+3
-    voff = (static_cast<uint32_t>(c) * BS + 4u * g) * kElem;
-    soff = 4u * g * 4u;
-  }
-
-  // Buffer resource over one (block, kv-head) tile: the base is uniform, so
-  // the descriptor lives in scalar registers and every load is
-  // "descriptor + 32-bit lane offset", with no vector address arithmetic.
-  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t tile(const char* base, size_t off, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), static_cast<short>(0),
-                                             static_cast<int>(bytes), kBufferFlags);
-  }
-
-  // blk[h]: physical block of sub-tile h; row0[h]: its first row in the block.
-  __device__ __forceinline__ void load(Chunk<kInt8, D>& ch, const int blk[2], const int row0[2]) const {
-    constexpr int NJ = D / 32;
-    constexpr int NN = D / 16;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const size_t t = static_cast<size_t>(blk[h]) * Hkv + kvh;
-      const __amdgpu_buffer_rsrc_t rk = tile(kc, t * kTileBytes, kTileBytes);
-      const __amdgpu_buffer_rsrc_t rv = tile(vc, t * kTileBytes, kTileBytes);
-      // uniform offsets (row of the sub-tile, per-load constants) go in the
-      // scalar offset operand, so the lane offset is the only vector input
-      const int ks_row = row0[h] * D * kElem;
-      const int vs_row = row0[h] * kElem;
-      if constexpr (kInt8) {
-#pragma unroll
-        for (int jj = 0; jj < NJ / 2; ++jj)
-          ch.k[h][jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, ks_row + 64 * jj, 0));
-#pragma unroll
-        for (int n = 0; n < NN; ++n)
-          ch.v[h][n] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, vs_row + 16 * n * BS, 0);
-        const __amdgpu_buffer_rsrc_t rks = tile(ksc, t * BS * 4, BS * 4);
-        const __amdgpu_buffer_rsrc_t rvs = tile(vsc, t * BS * 4, BS * 4);
-        ch.ks[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, soff, row0[h] * 4, 0));
-        ch.vs[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, soff, row0[h] * 4, 0));
-      } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          ch.k[h][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, ks_row + 64 * j, 0));
-#pragma unroll
-        for (int n = 0; n < NN; ++n)
-          ch.v[h][n] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, vs_row + 32 * n * BS, 0));
-      }
-    }
-  }
-};
-
-// Block ids one partition may span (its context / block_size).
-constexpr int kMaxPartBlocks = 128;
 
 // Chunks whose loads one wave issues together (32 KB of bf16 K/V, 16.5 KB of
 // int8 codes and scales), at two waves per SIMD.  Larger int8 batches were
@@ -212,8 +87,10 @@ void decode_mfma_kernel(DecodeParams p) {
   const int PT = p.part_tokens;
 
   const int L = p.context_lens[b];
-  const int t_begin = part * PT;
-  if (part != 0 && t_begin >= L) return;  // uniform across the workgroup
+  // cascade: the group's shared tokens are attended by the prefix kernel
+  const bool cascade = p.group_start != nullptr;
+  const int t_begin = (cascade ? group_shared_tokens(p, group_of(p, b)) : 0) + part * PT;
+  if ((cascade || part != 0) && t_begin >= L) return;  // uniform across the workgroup
   const int h0 = kvh * G;
   uint16_t* out = static_cast<uint16_t*>(p.out);
 
@@ -223,7 +100,7 @@ void decode_mfma_kernel(DecodeParams p) {
     return;
   }
   const int t_end = min(L, t_begin + PT);
-  const bool single = L <= PT;
+  const bool single = !cascade && L <= PT;
 
   // Fused step: the partition holding the newest token writes it first; the
   // fence and barrier make the stores visible to this workgroup's loads.
@@ -460,7 +337,7 @@ void decode_mfma_kernel(DecodeParams p) {
       *reinterpret_cast<u32x2*>(orow + 16 * n + 4 * g) = w;
     }
   } else {
-    const size_t slot = bh * p.num_parts + part;
+    const size_t slot = bh * p.num_parts + (cascade ? p.prefix_parts : 0) + part;
     float* arow = p.ws_acc + slot * D;
 #pragma unroll
     for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[n];

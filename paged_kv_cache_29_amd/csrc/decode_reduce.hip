@@ -26,15 +26,38 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
   const int bh = blockIdx.x;
   const int b = bh / p.num_heads;
   const int L = p.context_lens[b];
-  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
-  if (nparts <= 1) return;  // written by the partition kernel
+  // Partials i = 0 .. nparts-1 live in workspace slots slot(i): partitions
+  // of the context, or (cascade) npre shared-prefix partitions in slots
+  // 0 .. npre-1 followed by the partitions of the rest of the context from
+  // slot prefix_parts on.
+  int npre = 0, nparts, skip = 0;
+  if (p.group_start != nullptr) {
+    const int S = group_shared_tokens(p, group_of(p, b));
+    npre = (S + p.prefix_part_tokens - 1) / p.prefix_part_tokens;
+    nparts = npre + (L > S ? (L - S + p.part_tokens - 1) / p.part_tokens : 0);
+    skip = p.prefix_parts - npre;
+    if (nparts == 0) {  // empty context: zero output
+      for (int k = lane; k < D; k += kWave) {
+        const size_t idx = static_cast<size_t>(bh) * D + k;
+        if constexpr (kOutBf16)
+          static_cast<uint16_t*>(p.out)[idx] = 0;
+        else
+          static_cast<float*>(p.out)[idx] = 0.f;
+      }
+      return;
+    }
+  } else {
+    nparts = (L + p.part_tokens - 1) / p.part_tokens;
+    if (nparts <= 1) return;  // written by the partition kernel
+  }
+  auto slot = [&](int i) { return i < npre ? i : i + skip; };
   const size_t base = static_cast<size_t>(bh) * p.num_parts;
   const float* m = p.ws_m + base;
   const float* l = p.ws_l + base;
   const float* a = p.ws_acc + base * D;
 
   float M = -INFINITY;
-  for (int i = lane; i < nparts; i += kWave) M = fmaxf(M, m[i]);
+  for (int i = lane; i < nparts; i += kWave) M = fmaxf(M, m[slot(i)]);
   M = wave_max(M);
 
   float num[ND];
@@ -43,17 +66,17 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
   float den = 0.f;
   for (int first = 0; first < nparts; first += kWave) {
     const int i = first + lane;
-    const float wv = (i < nparts) ? exp2f(m[i] - M) : 0.f;
-    if (i < nparts) den = fmaf(wv, l[i], den);
+    const float wv = (i < nparts) ? exp2f(m[slot(i)] - M) : 0.f;
+    if (i < nparts) den = fmaf(wv, l[slot(i)], den);
     const int cnt = min(kWave, nparts - first);
-    const float* row = a + static_cast<size_t>(first) * D + lane;
+    const float* row = a + lane;
     // groups of 8 rows: 8 independent loads per lane in flight; rows past
     // cnt re-read the last valid row and get weight 0 (wv is 0 there)
     for (int j0 = 0; j0 < cnt; j0 += 8) {
       float x[8][ND];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int j = min(j0 + u, cnt - 1);
+        const int j = slot(first + min(j0 + u, cnt - 1));
 #pragma unroll
         for (int k = 0; k < ND; ++k) x[u][k] = row[static_cast<size_t>(j) * D + kWave * k];
       }

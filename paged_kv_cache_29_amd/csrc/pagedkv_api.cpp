@@ -95,7 +95,8 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
                            int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                            int64_t num_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype,
                            int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                           const void* k_new, const void* v_new, bool step, DecodeSetup* st) {
+                           const void* k_new, const void* v_new, bool step, DecodeSetup* st,
+                           bool check_workspace = true) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
   if (num_heads <= 0 || num_kv_heads <= 0)
     return fail(PKV_ERR_INVALID, "num_heads and num_kv_heads must be positive");
@@ -148,7 +149,7 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   } else if (k_scale || v_scale) {
     return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL unless kv_dtype is PKV_I8");
   }
-  const size_t need = workspace_bytes_for(num_seqs, num_heads, head_dim, nparts);
+  const size_t need = check_workspace ? workspace_bytes_for(num_seqs, num_heads, head_dim, nparts) : 0;
   if (need > 0 && num_seqs > 0) {
     if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
     if (workspace_bytes < need)
@@ -174,6 +175,12 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   p.ws_l = need ? reinterpret_cast<float*>(ws + acc_bytes + ml_bytes) : nullptr;
   p.k_new = step ? k_new : nullptr;
   p.v_new = step ? v_new : nullptr;
+  p.group_start = nullptr;  // plain decode; the cascade entry point sets these
+  p.group_shared_blocks = nullptr;
+  p.num_groups = 0;
+  p.max_shared_blocks = 0;
+  p.prefix_part_tokens = 0;
+  p.prefix_parts = 0;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
@@ -200,6 +207,83 @@ pkv_status launch_reduce(const DecodeSetup& st, hipStream_t stream) {
   hipError_t e = pkv::launch_decode_reduce(st.p, st.out_bf16, stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
+}
+
+// Shared-prefix partition length: the longest of 2048 ... 32 tokens that
+// still gives the prefix kernel about 1024 workgroups (at most
+// kMaxPartBlocks blocks; a multiple of 32, hence of the block size).
+int32_t auto_prefix_part_tokens(int64_t prefix_units, int32_t block_size, int32_t max_shared_blocks) {
+  const int64_t span = static_cast<int64_t>(max_shared_blocks) * block_size;
+  int32_t pt = 32;
+  for (int32_t cand : {2048, 1024, 512, 256, 128, 64}) {
+    if (cand > kMaxPartBlocks * block_size) continue;
+    if (prefix_units * ((span + cand - 1) / cand) >= 1024) {
+      pt = cand;
+      break;
+    }
+  }
+  return pt;
+}
+
+constexpr int kPrefixQueries = 16 * pkv::kPrefixTiles;  // queries per prefix workgroup
+
+struct CascadeSizes {
+  int32_t ppt, pparts, spt, sparts, qtiles;
+};
+
+// Validated cascade sizes (returns PKV_OK and fills cs) for the calls below.
+pkv_status cascade_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                         int32_t block_size, int32_t max_blocks_per_seq, int32_t num_groups,
+                         int32_t max_group_size, int32_t max_shared_blocks,
+                         int32_t partition_tokens, int32_t prefix_partition_tokens,
+                         CascadeSizes* cs) {
+  if (num_groups < 0 || (num_seqs > 0 && num_groups < 1))
+    return fail(PKV_ERR_INVALID, "num_groups must be >= 1 when num_seqs > 0 (got %d)", num_groups);
+  if (num_groups > num_seqs)
+    return fail(PKV_ERR_INVALID, "num_groups (%d) exceeds num_seqs (%d)", num_groups, num_seqs);
+  if (max_group_size < 0 || max_group_size > num_seqs || (num_seqs > 0 && max_group_size < 1))
+    return fail(PKV_ERR_INVALID, "max_group_size must be in [1, num_seqs] (got %d)", max_group_size);
+  if (max_shared_blocks < 0 || max_shared_blocks > max_blocks_per_seq)
+    return fail(PKV_ERR_INVALID, "max_shared_blocks must be in [0, max_blocks_per_seq] (got %d)",
+                max_shared_blocks);
+  const int32_t G = num_heads / num_kv_heads;
+  const int64_t qtiles = (static_cast<int64_t>(max_group_size) * G + kPrefixQueries - 1) / kPrefixQueries;
+  if (qtiles > 65535) return fail(PKV_ERR_UNSUPPORTED, "max_group_size * G too large");
+  if (static_cast<int64_t>(num_groups) * num_kv_heads > 0x7fffffff)
+    return fail(PKV_ERR_UNSUPPORTED, "num_groups * num_kv_heads too large");
+  int32_t ppt = prefix_partition_tokens;
+  if (ppt == 0) {
+    ppt = auto_prefix_part_tokens(static_cast<int64_t>(num_groups) * num_kv_heads * qtiles,
+                                  block_size, max_shared_blocks);
+  } else if (ppt < kChunk || ppt % kChunk != 0 || ppt > kMaxPartBlocks * block_size) {
+    return fail(PKV_ERR_INVALID, "prefix_partition_tokens %d must be 0 or a multiple of %d in [%d, %d]",
+                ppt, kChunk, kChunk, kMaxPartBlocks * block_size);
+  }
+  const int32_t spt = part_tokens_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
+                                      partition_tokens);
+  if (spt == 0)
+    return fail(PKV_ERR_INVALID, "partition_tokens %d must be 0 or a multiple of %d in [%d, %d]",
+                partition_tokens, kChunk, kChunk, kMaxPartBlocks * block_size);
+  const int64_t span = static_cast<int64_t>(max_shared_blocks) * block_size;
+  cs->ppt = ppt;
+  cs->pparts = static_cast<int32_t>((span + ppt - 1) / ppt);
+  cs->spt = spt;
+  cs->sparts = num_parts_for(block_size, max_blocks_per_seq, spt);
+  cs->qtiles = static_cast<int32_t>(qtiles);
+  if (static_cast<int64_t>(cs->pparts) + cs->sparts > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "too many partitions (%d + %d)", cs->pparts, cs->sparts);
+  return PKV_OK;
+}
+
+// Workspace of the cascade: every (sequence, head) has pparts + sparts
+// partial slots, and the reduce always runs.
+size_t cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                               const CascadeSizes& cs) {
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * (cs.pparts + cs.sparts);
+  if (rows == 0) return 0;
+  const size_t acc = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
+  const size_t ml = (rows * sizeof(float) + 255) & ~size_t(255);
+  return acc + 2 * ml;
 }
 
 pkv_status validate_write(const void* k, const void* v, const void* k_cache, const void* v_cache,
@@ -353,6 +437,84 @@ pkv_status pkv_paged_attention_decode_step_partitions(PKV_STEP_PARAMS) {
   if (num_seqs == 0) return ok();
   s = launch_partitions(st, static_cast<hipStream_t>(stream));
   if (s != PKV_OK) return s;
+  return ok();
+}
+
+size_t pkv_paged_attention_cascade_workspace_size(
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+    int32_t block_size, int32_t max_blocks_per_seq, int32_t num_groups, int32_t max_group_size,
+    int32_t max_shared_blocks, int32_t partition_tokens, int32_t prefix_partition_tokens) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      !head_dim_ok(head_dim) || !block_size_ok(block_size) || max_blocks_per_seq <= 0)
+    return 0;
+  CascadeSizes cs;
+  const std::string saved = g_last_error;
+  const pkv_status s = cascade_sizes(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                                     num_groups, max_group_size, max_shared_blocks, partition_tokens,
+                                     prefix_partition_tokens, &cs);
+  g_last_error = saved;  // a size query leaves the last error alone
+  if (s != PKV_OK) return 0;
+  return cascade_workspace_bytes(num_seqs, num_heads, head_dim, cs);
+}
+
+pkv_status pkv_paged_attention_decode_cascade(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* group_start, const int32_t* group_shared_blocks, float scale, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t max_shared_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t partition_tokens,
+    int32_t prefix_partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  // the plain checks first (sizes, dtypes, pointers); the workspace is
+  // checked below against the cascade's own layout
+  DecodeSetup st;
+  pkv_status s = validate_decode(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                 context_lens, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                                 block_size, max_blocks_per_seq, num_blocks, q_dtype, kv_dtype,
+                                 partition_tokens, nullptr, 0, nullptr, nullptr, false, &st,
+                                 /*check_workspace=*/false);
+  if (s != PKV_OK) return s;
+  if (st.kv == pkv::KvKind::F32)
+    return fail(PKV_ERR_UNSUPPORTED, "cascade decode supports bf16 and int8 caches only");
+  CascadeSizes cs;
+  s = cascade_sizes(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq, num_groups,
+                    max_group_size, max_shared_blocks, partition_tokens, prefix_partition_tokens, &cs);
+  if (s != PKV_OK) return s;
+  if (num_seqs == 0) return ok();
+  if (!group_start || !group_shared_blocks)
+    return fail(PKV_ERR_INVALID, "cascade decode needs group_start and group_shared_blocks");
+  const size_t need = cascade_workspace_bytes(num_seqs, num_heads, head_dim, cs);
+  if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  pkv::DecodeParams& p = st.p;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * (cs.pparts + cs.sparts);
+  const size_t acc_bytes = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
+  const size_t ml_bytes = (rows * sizeof(float) + 255) & ~size_t(255);
+  char* ws = static_cast<char*>(workspace);
+  p.ws_acc = reinterpret_cast<float*>(ws);
+  p.ws_m = reinterpret_cast<float*>(ws + acc_bytes);
+  p.ws_l = reinterpret_cast<float*>(ws + acc_bytes + ml_bytes);
+  p.group_start = group_start;
+  p.group_shared_blocks = group_shared_blocks;
+  p.num_groups = num_groups;
+  p.max_shared_blocks = max_shared_blocks;
+  p.prefix_part_tokens = cs.ppt;
+  p.prefix_parts = cs.pparts;
+  p.part_tokens = cs.spt;
+  p.num_parts = cs.pparts + cs.sparts;
+  const hipStream_t strm = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (cs.pparts > 0) {
+    e = pkv::launch_cascade_prefix(p, st.kv, max_group_size, strm);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefix kernel launch failed: %s", hipGetErrorString(e));
+  }
+  e = pkv::launch_decode_mfma(p, st.kv, strm);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "partition kernel launch failed: %s", hipGetErrorString(e));
+  e = pkv::launch_decode_reduce(p, st.out_bf16, strm);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

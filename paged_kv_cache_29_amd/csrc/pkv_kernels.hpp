@@ -29,6 +29,19 @@ struct DecodeParams {
   // writes it there through the block table before attending.
   const void* k_new;
   const void* v_new;
+  // Shared-prefix (cascade) decode, or nullptr.  Sequences
+  // [group_start[g], group_start[g+1]) form group g and share their first
+  // group_shared_blocks[g] blocks; group_shared_tokens() gives the tokens
+  // attended once for the whole group.  Their partials fill workspace slots
+  // [0, prefix_parts) (partitions of prefix_part_tokens); the partition
+  // kernel attends each sequence's remaining tokens into slots
+  // prefix_parts + part, and the reduce always runs.
+  const int32_t* group_start;
+  const int32_t* group_shared_blocks;
+  int32_t num_groups;
+  int32_t max_shared_blocks;
+  int32_t prefix_part_tokens;
+  int32_t prefix_parts;
   float scale_log2;  // scale * log2(e)
   int32_t num_seqs;
   int32_t num_heads;
@@ -58,10 +71,35 @@ enum class KvKind { F32 = 0, BF16 = 1, I8 = 2 };
 
 // Waves per workgroup of the partition kernels.
 constexpr int kDecodeWaves = 4;
+// Query-column tiles (16 queries each) per workgroup of the shared-prefix kernel.
+constexpr int kPrefixTiles = 2;
+
+// Tokens of group g attended by the shared-prefix kernel: its shared
+// blocks, capped at the whole blocks of its first sequence's context (so
+// the span is block-aligned and every table entry it reads is in use) and at
+// max_shared_blocks (so its partials fit the prefix_parts slots).
+__device__ __forceinline__ int group_shared_tokens(const DecodeParams& p, int g) {
+  const int lead = p.group_start[g];
+  const int full = p.context_lens[lead] / p.block_size;
+  const int nb = min(min(max(p.group_shared_blocks[g], 0), full), p.max_shared_blocks);
+  return nb * p.block_size;
+}
+
+// Group of sequence b (groups are contiguous ranges; b is uniform, so the
+// search runs on scalar loads).
+__device__ __forceinline__ int group_of(const DecodeParams& p, int b) {
+  int lo = 0, hi = p.num_groups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.group_start[mid] <= b) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
 
 hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, hipStream_t s);
+hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group_size, hipStream_t s);
 hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
 hipError_t launch_cache_write_int8(const WriteParams& p, hipStream_t s);
 hipError_t launch_tile_read(const void* pool, const int32_t* ids, int64_t ntiles, int grid,

@@ -37,7 +37,12 @@ Layouts: ``k_cache[NB, Hkv, bs, D]``, ``v_cache[NB, Hkv, D, bs]``,
 patterns.  Unused blocks, unused rows and the new-token slots hold NaN.
 For the int8 workload the pool is not materialised: ``k_fill`` / ``v_fill``
 ``[T, Hkv, D]`` fp32 with ``slot_fill`` list every cached token but the new
-ones, for the consumer to quantise into its own int8 cache.
+ones, for the consumer to quantise into its own int8 cache (per sequence in
+order; with a shared prefix, once per distinct slot instead).
+
+A shared prefix (``prefix`` tokens) is held by every sequence, or by each
+consecutive group of ``prefix_group_size`` sequences with its own prefix
+blocks: the group's first sequence holds them and the others fork it.
 """
 
 from dataclasses import dataclass, field
@@ -121,16 +126,23 @@ def _poison(alloc, k_cache, v_cache, slots_new, kind):
         v_cache[s // bs, :, :, s % bs] = nan
 
 
-def _allocate(lens, bs, num_blocks, order, prefix=0):
-    """Allocate sequences; returns (alloc, sids, fill slots per seq, new slots)."""
+def _allocate(lens, bs, num_blocks, order, prefix=0, prefix_group_size=None):
+    """Allocate sequences; returns (alloc, sids, fill slots per seq, new slots).
+
+    With a prefix, consecutive groups of ``prefix_group_size`` sequences (all
+    sequences by default) each fork from a root holding its own prefix."""
     alloc = BlockAllocator(num_blocks, bs, order=order)
     sids = []
     fill_slots = []
     if prefix > 0:
-        root = alloc.new_sequence()
-        prefix_slots = alloc.append(root, prefix)
-        sids = [root] + [alloc.fork(root) for _ in range(len(lens) - 1)]
-        fill_slots = [prefix_slots.copy() for _ in sids]
+        size = len(lens) if prefix_group_size is None else int(prefix_group_size)
+        for start in range(0, len(lens), size):
+            root = alloc.new_sequence()
+            prefix_slots = alloc.append(root, prefix)
+            n = min(size, len(lens) - start)
+            group = [root] + [alloc.fork(root) for _ in range(n - 1)]
+            sids += group
+            fill_slots += [prefix_slots.copy() for _ in group]
     else:
         sids = [alloc.new_sequence() for _ in lens]
         fill_slots = [np.empty(0, dtype=np.int64) for _ in sids]
@@ -149,27 +161,28 @@ def _allocate(lens, bs, num_blocks, order, prefix=0):
     return alloc, sids, fill_slots, new_slots
 
 
-def _blocks_needed(lens, bs, prefix=0):
+def _blocks_needed(lens, bs, prefix=0, prefix_group_size=None):
     probe_pool = int(sum((int(L) + bs - 1) // bs for L in lens)) + 8
-    alloc, _, _, _ = _allocate(lens, bs, probe_pool, None, prefix)
+    alloc, _, _, _ = _allocate(lens, bs, probe_pool, None, prefix, prefix_group_size)
     return int(np.count_nonzero(alloc.refcount))
 
 
 def build(name, seed, lens, num_heads, num_kv_heads, head_dim, block_size,
           kv_dtype, q_dtype, scale=None, num_blocks=None, spare=0.125,
-          prefix=0, rng=None, max_blocks_per_seq=None, meta=None):
+          prefix=0, rng=None, max_blocks_per_seq=None, meta=None, prefix_group_size=None):
     """Build a workload for the given context lengths (already drawn)."""
     if rng is None:
         rng = np.random.default_rng(seed)
     lens = np.asarray(lens, dtype=np.int64)
     B, H, Hkv, D, bs = len(lens), num_heads, num_kv_heads, head_dim, block_size
     if num_blocks is None:
-        need = _blocks_needed(lens, bs, prefix)
+        need = _blocks_needed(lens, bs, prefix, prefix_group_size)
         num_blocks = max(1, int(math.ceil(need * (1.0 + spare))))
     if max_blocks_per_seq is None:
         max_blocks_per_seq = max(1, int(max((int(L) + bs - 1) // bs for L in lens)))
     perm = rng.permutation(num_blocks)
-    alloc, sids, fill_slots, new_slots = _allocate(lens, bs, num_blocks, perm, prefix)
+    alloc, sids, fill_slots, new_slots = _allocate(lens, bs, num_blocks, perm, prefix,
+                                                   prefix_group_size)
     alloc.check()
     tables = alloc.tables(sids, max_blocks_per_seq)
     store = "bf16" if kv_dtype == "bf16" else "f32"
@@ -181,8 +194,23 @@ def build(name, seed, lens, num_heads, num_kv_heads, head_dim, block_size,
         scale=float(scale if scale is not None else 1.0 / math.sqrt(D)),
         context_lens=lens.astype(np.int32), block_tables=tables, q=q,
         k_new=None, v_new=None, slot_new=new_slots, meta=dict(meta or {}))
-    w.meta.update(prefix=prefix, copies=list(alloc.copies))
-    if kv_dtype in ("f32", "bf16"):
+    w.meta.update(prefix=prefix, copies=list(alloc.copies), prefix_group_size=prefix_group_size)
+    if kv_dtype == "i8" and prefix:
+        # shared blocks: fp32 pools as for bf16 (copy-on-write duplicates
+        # included), then one fill row per distinct used slot
+        k_pool = _draw(rng, (num_blocks, Hkv, bs, D), "f32")
+        v_pool = _draw(rng, (num_blocks, Hkv, D, bs), "f32")
+        for src, dst, rows in alloc.copies:
+            k_pool[dst, :, :rows, :] = k_pool[src, :, :rows, :]
+            v_pool[dst, :, :, :rows] = v_pool[src, :, :, :rows]
+        used = [np.asarray(f, np.int64) for f in fill_slots]
+        used += [np.arange(dst * bs, dst * bs + rows, dtype=np.int64) for _, dst, rows in alloc.copies]
+        slot_fill = np.unique(np.concatenate(used)) if used else np.empty(0, np.int64)
+        w.k_fill = np.ascontiguousarray(k_pool[slot_fill // bs, :, slot_fill % bs, :])
+        w.v_fill = np.ascontiguousarray(v_pool[slot_fill // bs, :, :, slot_fill % bs])
+        w.slot_fill = slot_fill
+        w.meta["fill_per_sequence"] = False
+    elif kv_dtype in ("f32", "bf16"):
         k_cache = _draw(rng, (num_blocks, Hkv, bs, D), store)
         v_cache = _draw(rng, (num_blocks, Hkv, D, bs), store)
         for src, dst, rows in alloc.copies:        # copy-on-write duplicates
@@ -191,8 +219,7 @@ def build(name, seed, lens, num_heads, num_kv_heads, head_dim, block_size,
         _poison(alloc, k_cache, v_cache, new_slots[new_slots >= 0], store)
         w.k_cache, w.v_cache = k_cache, v_cache
     elif kv_dtype == "i8":
-        if prefix:
-            raise ValueError("shared prefixes are built for f32/bf16 pools only")
+        w.meta["fill_per_sequence"] = True
         slot_fill = np.concatenate(fill_slots) if fill_slots else np.empty(0, np.int64)
         T = len(slot_fill)
         w.k_fill = _draw(rng, (T, Hkv, D), "f32")
@@ -241,9 +268,11 @@ def make_config(config, seed=0, block_size=None):
 
 
 def make_custom(seed, lens, num_heads, num_kv_heads, head_dim, block_size,
-                kv_dtype="bf16", q_dtype=None, spare=0.25, prefix=0, scale=None):
+                kv_dtype="bf16", q_dtype=None, spare=0.25, prefix=0, scale=None,
+                prefix_group_size=None):
     """Small workload of arbitrary shape for tests (same recipe as above)."""
     if q_dtype is None:
         q_dtype = "f32" if kv_dtype == "f32" else "bf16"
     return build(f"custom_s{seed}", seed, lens, num_heads, num_kv_heads, head_dim,
-                 block_size, kv_dtype, q_dtype, spare=spare, prefix=prefix, scale=scale)
+                 block_size, kv_dtype, q_dtype, spare=spare, prefix=prefix, scale=scale,
+                 prefix_group_size=prefix_group_size)

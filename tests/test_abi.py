@@ -188,3 +188,63 @@ def test_probe_rejects_bad_arguments(lib):
     assert f(pool, ids, 1, 0, sink, None) == INVALID
     assert f(pool, ids, 1, 65537, sink, None) == INVALID
     assert f(pool, ids, 0, 1, sink, None) == OK  # nothing to read: no launch
+
+
+def _cascade(lib, **over):
+    a = dict(out=_fake(1), q=_fake(2), k_cache=_fake(3), v_cache=_fake(4), k_scale=None,
+             v_scale=None, block_tables=_fake(5), context_lens=_fake(6), group_start=_fake(7),
+             group_shared_blocks=_fake(8), scale=0.125, num_seqs=4, num_heads=8, num_kv_heads=2,
+             head_dim=64, block_size=16, max_blocks_per_seq=13, num_blocks=32, num_groups=2,
+             max_group_size=3, max_shared_blocks=5, q_dtype=BF16, kv_dtype=BF16,
+             partition_tokens=0, prefix_partition_tokens=0, workspace=None, workspace_bytes=0,
+             stream=None)
+    a.update(over)
+    st = lib.pkv_paged_attention_decode_cascade(*a.values())
+    return st, lib.pkv_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,frag", [
+    (dict(q_dtype=F32, kv_dtype=F32), UNSUPPORTED, "bf16 and int8"),
+    (dict(num_groups=0), INVALID, "num_groups"),
+    (dict(num_groups=5), INVALID, "num_groups"),
+    (dict(max_group_size=0), INVALID, "max_group_size"),
+    (dict(max_group_size=5), INVALID, "max_group_size"),
+    (dict(max_shared_blocks=-1), INVALID, "max_shared_blocks"),
+    (dict(max_shared_blocks=14), INVALID, "max_shared_blocks"),
+    (dict(group_start=None), INVALID, "group_start"),
+    (dict(group_shared_blocks=None), INVALID, "group_start"),
+    (dict(prefix_partition_tokens=48), INVALID, "prefix_partition_tokens"),
+    (dict(prefix_partition_tokens=4096), INVALID, "prefix_partition_tokens"),
+    (dict(partition_tokens=40), INVALID, "partition_tokens"),
+    (dict(out=None), INVALID, "null pointer"),
+    (dict(head_dim=96), UNSUPPORTED, "head_dim"),
+    (dict(kv_dtype=I8), INVALID, "k_scale"),
+])
+def test_cascade_rejects(lib, over, code, frag):
+    st, msg = _cascade(lib, **over)
+    assert st == code, msg
+    assert frag in msg
+
+
+def test_cascade_workspace(lib):
+    need = lib.pkv_paged_attention_cascade_workspace_size(4, 8, 2, 64, 16, 13, 2, 3, 5, 0, 0)
+    assert need > 0
+    st, msg = _cascade(lib)
+    assert st == WORKSPACE and "required" in msg
+    st, msg = _cascade(lib, workspace=ctypes.c_void_p(0x100000), workspace_bytes=need - 1)
+    assert st == WORKSPACE
+    st, msg = _cascade(lib, workspace=ctypes.c_void_p(0x100010), workspace_bytes=need)
+    assert st == WORKSPACE and "aligned" in msg
+    # no shared blocks: still one partial slot per partition, the reduce always runs
+    assert lib.pkv_paged_attention_cascade_workspace_size(4, 8, 2, 64, 16, 13, 4, 1, 0, 0, 0) > 0
+    assert lib.pkv_paged_attention_cascade_workspace_size(0, 8, 2, 64, 16, 13, 0, 0, 0, 0, 0) == 0
+    assert lib.pkv_paged_attention_cascade_workspace_size(4, 8, 2, 96, 16, 13, 2, 3, 5, 0, 0) == 0
+    # slot count = prefix partitions + partitions of the rest
+    rows = 4 * 8 * (-(-5 * 16 // 32) + -(-13 * 16 // 64))
+    want = -(-rows * 64 * 4 // 256) * 256 + 2 * (-(-rows * 4 // 256) * 256)
+    assert lib.pkv_paged_attention_cascade_workspace_size(4, 8, 2, 64, 16, 13, 2, 3, 5, 64, 32) == want
+
+
+def test_cascade_empty_batch_is_noop(lib):
+    st, msg = _cascade(lib, num_seqs=0, num_groups=0, max_group_size=0, max_shared_blocks=0)
+    assert st == OK, msg

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from paged_kv_cache_29_amd.blocks import BlockAllocator, OutOfBlocks
-from paged_kv_cache_29_amd import workloads
+from paged_kv_cache_29_amd import blocks, workloads
 
 
 def test_append_allocates_on_block_boundaries():
@@ -134,3 +134,70 @@ def test_bf16_rounding_nearest_even():
     got = workloads.bf16_bits(x)
     # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1.0); 1 + 3*2^-8 -> 1 + 2^-6
     assert got.tolist() == [0x3F80, 0x3F80, 0x3F82, 0xBF80, 0x3F81]
+
+
+# ---------------------------------------------------------------- cascade groups
+def _tables(rows, width=6):
+    t = np.full((len(rows), width), -1, np.int32)
+    for i, r in enumerate(rows):
+        t[i, :len(r)] = r
+    return t
+
+
+def test_cascade_groups_one_shared_prefix():
+    t = _tables([[7, 8, 9, 1], [7, 8, 9, 2], [7, 8, 9, 3, 4]])
+    gs, gsb, mg, ms = blocks.cascade_groups(t, [64, 60, 70], 16)
+    assert gs.tolist() == [0, 3] and gsb.tolist() == [3] and (mg, ms) == (3, 3)
+
+
+def test_cascade_groups_only_whole_blocks_inside_every_context_count():
+    # the second sequence ends inside block 9, so only blocks 7, 8 are whole in both
+    t = _tables([[7, 8, 9, 1], [7, 8, 9]])
+    gs, gsb, _, _ = blocks.cascade_groups(t, [64, 40], 16)
+    assert gsb.tolist() == [2]
+
+
+def test_cascade_groups_split_where_sharing_drops():
+    # 0-2 share 3 blocks; 3 shares only block 7 with 0, so it starts a group
+    # with 4 (which shares 2 blocks with it); 5 shares nothing
+    t = _tables([[7, 8, 9, 1], [7, 8, 9, 2], [7, 8, 9, 3], [7, 5, 6, 4], [7, 5, 3, 3], [11, 12]])
+    gs, gsb, mg, ms = blocks.cascade_groups(t, [64, 64, 64, 64, 64, 32], 16)
+    assert gs.tolist() == [0, 3, 5, 6]
+    assert gsb.tolist() == [3, 2, 0]
+    assert (mg, ms) == (3, 3)
+
+
+def test_cascade_groups_min_shared_blocks():
+    t = _tables([[7, 8, 1], [7, 9, 2]])
+    gs, gsb, _, _ = blocks.cascade_groups(t, [48, 48], 16, min_shared_blocks=2)
+    assert gs.tolist() == [0, 1, 2] and gsb.tolist() == [0, 0]
+    gs, gsb, _, _ = blocks.cascade_groups(t, [48, 48], 16)
+    assert gs.tolist() == [0, 2] and gsb.tolist() == [1]
+
+
+def test_cascade_groups_of_the_shared_prefix_workload():
+    # 2000-token prefix: 125 whole blocks at bs 16; at bs 32 the 63rd block is
+    # a per-sequence copy, so 62 blocks are shared
+    for bs, want in ((16, 125), (32, 62)):
+        w = workloads.build("p", 4, [2000 + 60, 2000 + 500, 2000 + 50, 2001], 4, 2, 8, bs,
+                            "bf16", "bf16", prefix=2000)
+        gs, gsb, mg, ms = blocks.cascade_groups(w.block_tables, w.context_lens, bs)
+        assert gs.tolist() == [0, 4] and gsb.tolist() == [want] and (mg, ms) == (4, want)
+
+
+def test_grouped_prefix_workload_layout():
+    w = workloads.make_custom(5, [300, 100, 200, 34, 40, 35, 60], 8, 2, 64, 16, prefix=33,
+                              prefix_group_size=3)
+    gs, gsb, mg, ms = blocks.cascade_groups(w.block_tables, w.context_lens, 16)
+    assert gs.tolist() == [0, 3, 6, 7] and gsb.tolist() == [2, 2, 0]
+    t = w.block_tables
+    assert t[0, 0] != t[3, 0]  # each group has its own prefix blocks
+    wi = workloads.make_custom(5, [300, 100, 200, 34, 40, 35, 60], 8, 2, 64, 16, kv_dtype="i8",
+                               prefix=33, prefix_group_size=3)
+    # int8 fills: one row per distinct used slot, every slot of a table covered
+    assert len(np.unique(wi.slot_fill)) == len(wi.slot_fill)
+    used = set()
+    for b, L in enumerate(wi.context_lens):
+        for tok in range(int(L) - 1):
+            used.add(int(wi.block_tables[b, tok // 16]) * 16 + tok % 16)
+    assert used <= set(wi.slot_fill.tolist())
