@@ -211,8 +211,43 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
                        "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(w.name),
                        "kernel": "decode_mfma_kernel (fused step: append + attend)"
                        if w.kv_dtype != "f32" else "decode_f32_kernel (fused step)"}
+    if w.meta.get("prefix"):
+        res["cascade"] = run_cascade(w, args, torch, pkv, loop_time, write, out, q, kc, vc, bt, cl,
+                                     ks, vs, nbytes, uniq, ms_per_step)
     res["_w"] = w
     return res
+
+
+def run_cascade(w, args, torch, pkv, loop_time, write, out, q, kc, vc, bt, cl, ks, vs, nbytes,
+                uniq, ms_fused):
+    """The same step with the shared blocks attended once per group: cache
+    write, then paged_attention_decode_cascade (prefix kernel, partition
+    kernel over each sequence's own tokens, reduce)."""
+    from paged_kv_cache_29_amd import blocks
+    gs, gsb, mg, msb = blocks.cascade_groups(w.block_tables, w.context_lens, w.block_size)
+    dev = q.device
+    gs_d, gsb_d = torch.from_numpy(gs).to(dev), torch.from_numpy(gsb).to(dev)
+    need = pkv.cascade_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                      w.block_size, w.block_tables.shape[1], len(gsb), mg, msb,
+                                      args.partition_tokens, 0)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def cascade():
+        pkv.paged_attention_decode_cascade(out, q, kc, vc, bt, cl, gs_d, gsb_d, w.scale,
+                                           w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                           mg, msb, k_scale=ks, v_scale=vs,
+                                           partition_tokens=args.partition_tokens, workspace=ws)
+
+    def step():
+        write()
+        cascade()
+
+    us = loop_time(step)
+    us_attn = loop_time(cascade)
+    return {"us_per_step": us, "kv_gbs": nbytes / (us * 1e-6) / 1e9,
+            "unique_gbs": uniq / (us * 1e-6) / 1e9, "attention_us": us_attn,
+            "speedup_vs_fused_step": ms_fused * 1e3 / us,
+            "groups": int(len(gsb)), "max_group_size": int(mg), "shared_blocks": int(msb)}
 
 
 def unique_tile_bytes(w):
@@ -378,6 +413,7 @@ def main():
         "unfused": head["unfused"],
         "roofline": head["roofline"],
         "us_per_step_events": head["us_per_step_events"],
+        "cascade": head.get("cascade"),
         "read_ceiling": ceiling,
         "kernel_source_sha": kernel_source_sha(),
         "secondary": [{k: v for k, v in r.items()} for r in results[1:]],

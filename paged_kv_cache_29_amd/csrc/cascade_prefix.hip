@@ -7,24 +7,33 @@
 // rests on; "SGLang and RadixAttention": the longest shared prefix is
 // reused and only the suffix is computed per request).  Plain decode reads
 // those blocks once per sequence.  Here each K/V chunk of the shared blocks
-// is loaded once per workgroup and contracted against the queries of
-// several sequences at a time: the matrix-core N dimension holds
-// (sequence, head) pairs of the group instead of one sequence's heads.
+// is read once per workgroup and contracted against the queries of many
+// sequences at once: the matrix-core N dimension holds (sequence, head)
+// pairs of the group instead of one sequence's heads.
 //
-// Each workgroup owns (group, kv-head, tile of 16 * kPrefixTiles queries,
-// partition of prefix_part_tokens shared tokens) and leaves, per query, the
-// partial (max, sum, unnormalised output) of its partition in workspace
-// slot `partition`; the reduce kernel merges them with the partials of each
-// sequence's own tokens by the same exact combine as split-context decode.
-// Query column q of the group is sequence group_start[g] + q / G, head
-// kv_head * G + q % G.  The kv-head index varies fastest in the grid, so with
-// 8 kv-heads each XCD's L2 serves one kv-head's shared blocks.
+// Each workgroup owns (group, kv-head, kPrefixQueries queries, partition of
+// prefix_part_tokens shared tokens) and leaves, per query, the partial (max,
+// sum, unnormalised output) of its partition in workspace slot `partition`;
+// the reduce kernel merges them with the partials of each sequence's own
+// tokens by the same exact combine as split-context decode.  Query column q
+// of the group is sequence group_start[g] + q / G, head kv_head * G + q % G.
+// The kv-head index varies fastest in the grid, so with 8 kv-heads each
+// XCD's L2 serves one kv-head's shared blocks.
 //
-// Operand layouts are those of the partition kernel (decode_tile.hpp);
-// per 32-token chunk one wave does, for each query tile t,
+// Work split: every wave owns 16 * kPrefixTiles queries and walks every
+// 32-token chunk of the partition.  A chunk is staged once in LDS: its four
+// pieces (K and V of the two 16-token sub-tiles, plus int8 scales) are
+// loaded by the four waves, one piece each, while the previous chunk is
+// being consumed (two LDS stages).  Each wave then reads its matrix-core
+// operands from LDS in the partition kernel's layouts (decode_tile.hpp) and,
+// for each of its query tiles t,
 //   S^T[16 tok x 16 q] = K_sub . Q_t^T, online softmax per query, and
 //   O_t^T += V^T . P_t^T (P as a bf16 hi/lo pair),
-// with the chunk's K and V operands (and int8 widening) shared by the tiles.
+// sharing the chunk's K and V operands (and int8 widening) between tiles.
+// LDS layout per stage: K sub-tiles as token rows padded by 16 bytes (the
+// 16 rows a wave reads together fall in distinct banks); V sub-tiles
+// dim-major as in the cache, bf16 rows with their two 8-byte halves of each
+// 16-byte unit swapped on every other group of 8 dims (same purpose).
 
 #include "decode_tile.hpp"
 #include "pkv_device.hpp"
@@ -33,19 +42,34 @@
 namespace pkv {
 namespace {
 
-template <bool kInt8, int D, int BS, int W, int NT>
-__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <bool kInt8, int D, int BS, int NT>
+struct PrefixLds {
+  static constexpr int kElem = kInt8 ? 1 : 2;
+  static constexpr int KROW = D * kElem + 16;         // padded K token row
+  static constexpr int KSUB = 16 * KROW;              // one 16-token K sub-tile
+  static constexpr int VROW = 16 * kElem;             // one dim's 16 tokens
+  static constexpr int VSUB = D * VROW;               // one 16-token V sub-tile
+  static constexpr int SC = kInt8 ? 4 * 64 : 0;       // k/v scales of both sub-tiles
+  static constexpr int STAGE = 2 * KSUB + 2 * VSUB + SC;
+  static constexpr int PIECE = 16 * D * kElem;        // bytes of one K or V sub-tile
+  static constexpr int UNITS = PIECE / (16 * kWave);  // 16-byte loads per lane per piece
+};
+
+template <bool kInt8, int D, int BS, int NT>
+__global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void cascade_prefix_kernel(DecodeParams p) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
+  static_assert(kDecodeWaves == 4, "one chunk piece per wave");
+  constexpr int W = kDecodeWaves;
   constexpr int NJ = D / 32;
   constexpr int NN = D / 16;
-  constexpr int QT = 16 * NT;
+  constexpr int QW = 16 * NT;  // queries per wave
+  using L = PrefixLds<kInt8, D, BS, NT>;
+  constexpr int kElem = L::kElem;
 
-  __shared__ float red_acc[W - 1][NT][NN * 4][kWave];
-  __shared__ float red_m[W][NT][kWave];
-  __shared__ float red_l[W][NT][kWave];
-  __shared__ int blk_ids[W][kMaxPartBlocks];
+  __shared__ __attribute__((aligned(16))) char lds[2][L::STAGE];
+  __shared__ int blk_ids[kMaxPartBlocks];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -57,16 +81,17 @@ void cascade_prefix_kernel(DecodeParams p) {
   const int G = H / Hkv;
   const int kvh = blockIdx.x % Hkv;
   const int grp = blockIdx.x / Hkv;
-  const int q0 = blockIdx.y * QT;
+  const int qwg = blockIdx.y * (W * QW);
   const int part = blockIdx.z;
 
   const int gs = p.group_start[grp];
   const int nq = (p.group_start[grp + 1] - gs) * G;
-  if (q0 >= nq) return;  // uniform
+  if (qwg >= nq) return;  // uniform across the workgroup
   const int S = group_shared_tokens(p, grp);
   const int t_begin = part * p.prefix_part_tokens;
-  if (t_begin >= S) return;  // uniform
+  if (t_begin >= S) return;  // uniform across the workgroup
   const int t_end = min(S, t_begin + p.prefix_part_tokens);  // block-aligned
+  const int q0 = qwg + wave * QW;  // this wave's first query
 
   // Q^T operands: tile t, lane (c, g), MFMA j: 8 dims from q_dim(j)
   auto q_dim = [&](int j) { return kInt8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g); };
@@ -84,29 +109,108 @@ void cascade_prefix_kernel(DecodeParams p) {
     }
   }
 
-  // the group's shared block ids (from its first sequence's table), staged
-  // per wave in LDS as in the partition kernel
+  // the group's shared block ids (its first sequence's table), once per workgroup
   const int nblk = (t_end - t_begin) / BS;
   {
     const int32_t* bt = p.block_tables + static_cast<size_t>(gs) * p.max_blocks_per_seq + t_begin / BS;
-    for (int i = lane; i < nblk; i += kWave) blk_ids[wave][i] = bt[i];  // nblk <= kMaxPartBlocks
+    for (int i = threadIdx.x; i < nblk; i += W * kWave) blk_ids[i] = bt[i];  // nblk <= kMaxPartBlocks
   }
-  __builtin_amdgcn_s_waitcnt(0);  // wave-private slice: own stores only
-  const int* my_ids = blk_ids[wave];
+  __syncthreads();
 
-  const ChunkLoader<kInt8, D, BS> ld(p, kvh, c, g);
+  // Blocks and first rows of chunk ch's two sub-tiles (uniform).  Past the
+  // end of the span the second sub-tile repeats the first: valid memory,
+  // masked.
   auto chunk_blocks = [&](int ch, int blk[2], int row0[2]) {
     const int t0 = t_begin + ch * 32;
     if (BS == 16) {
-      const int lb = ch * 2;
-      blk[0] = __builtin_amdgcn_readfirstlane(my_ids[lb]);
-      blk[1] = (t0 + 16 < t_end) ? __builtin_amdgcn_readfirstlane(my_ids[lb + 1]) : blk[0];
-      row0[0] = 0;
-      row0[1] = 0;
+      blk[0] = __builtin_amdgcn_readfirstlane(blk_ids[2 * ch]);
+      blk[1] = (t0 + 16 < t_end) ? __builtin_amdgcn_readfirstlane(blk_ids[2 * ch + 1]) : blk[0];
+      row0[0] = row0[1] = 0;
     } else {
-      blk[0] = blk[1] = __builtin_amdgcn_readfirstlane(my_ids[ch]);
+      blk[0] = blk[1] = __builtin_amdgcn_readfirstlane(blk_ids[ch]);
       row0[0] = 0;
       row0[1] = 16;
+    }
+  };
+
+  // ---- staging: wave w moves piece w of a chunk (0: K sub-tile 0, 1: K
+  // sub-tile 1, 2: V sub-tile 0, 3: V sub-tile 1; int8 also that piece's
+  // 16 scales, k for K pieces and v for V pieces)
+  const int ph = wave & 1;
+  const bool pv = wave >= 2;
+  u32x4 pu[L::UNITS];
+  u32x4 psc = {0u, 0u, 0u, 0u};
+  auto piece_load = [&](int ch) {
+    int blk[2], row0[2];
+    chunk_blocks(ch, blk, row0);
+    const size_t tile = static_cast<size_t>(blk[ph]) * Hkv + kvh;
+    const char* base = static_cast<const char*>(pv ? p.v_cache : p.k_cache) + tile * (BS * D * kElem);
+#pragma unroll
+    for (int i = 0; i < L::UNITS; ++i) {
+      const int u = i * kWave + lane;  // 16-byte unit of the piece
+      size_t off;
+      if (!pv) {
+        off = static_cast<size_t>(row0[ph]) * D * kElem + u * 16;
+      } else if (BS == 16) {
+        off = u * 16;
+      } else if (kInt8) {  // dim u: 16 tokens of a 32-token row
+        off = u * 32 + 16 * ph;
+      } else {  // dim u / 2, half u % 2 of the sub-tile's 32 bytes
+        off = (u >> 1) * 64 + 32 * ph + 16 * (u & 1);
+      }
+      pu[i] = load_u32x4(base + off);
+    }
+    if (kInt8 && lane < 4) {
+      const float* sc = pv ? p.v_scale : p.k_scale;
+      psc = load_u32x4(sc + tile * BS + row0[ph] + 4 * lane);
+    }
+  };
+  auto piece_store = [&](int st) {
+    char* dst = lds[st];
+#pragma unroll
+    for (int i = 0; i < L::UNITS; ++i) {
+      const int u = i * kWave + lane;
+      if (!pv) {
+        const int row = (u * 16) / (D * kElem);
+        const int col = (u * 16) % (D * kElem);
+        *reinterpret_cast<u32x4*>(dst + ph * L::KSUB + row * L::KROW + col) = pu[i];
+      } else {
+        u32x4 w = pu[i];
+        if (!kInt8 && (((u >> 1) >> 3) & 1)) w = u32x4{w.z, w.w, w.x, w.y};
+        *reinterpret_cast<u32x4*>(dst + 2 * L::KSUB + ph * L::VSUB + u * 16) = w;
+      }
+    }
+    if (kInt8 && lane < 4)
+      *reinterpret_cast<u32x4*>(dst + 2 * L::KSUB + 2 * L::VSUB + wave * 64 + lane * 16) = psc;
+  };
+  // this lane's operands of a staged chunk, in the partition kernel's layouts
+  auto lds_chunk = [&](int st, Chunk<kInt8, D>& cw) {
+    const char* src = lds[st];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const char* kr = src + h * L::KSUB + c * L::KROW;
+      if constexpr (kInt8) {
+#pragma unroll
+        for (int jj = 0; jj < NJ / 2; ++jj) cw.k[h][jj] = *reinterpret_cast<const u32x4*>(kr + 16 * g + 64 * jj);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) cw.k[h][j] = *reinterpret_cast<const u32x4*>(kr + (32 * j + 8 * g) * 2);
+      }
+      const char* vr = src + 2 * L::KSUB + h * L::VSUB;
+#pragma unroll
+      for (int n = 0; n < NN; ++n) {
+        if constexpr (kInt8) {
+          cw.v[h][n] = *reinterpret_cast<const uint32_t*>(vr + (16 * n + c) * L::VROW + 4 * g);
+        } else {
+          const int gg = g ^ ((c >> 3) & 1);
+          cw.v[h][n] = *reinterpret_cast<const u32x2*>(vr + (16 * n + c) * L::VROW + 8 * gg);
+        }
+      }
+      if constexpr (kInt8) {
+        const char* sc = src + 2 * L::KSUB + 2 * L::VSUB;
+        cw.ks[h] = *reinterpret_cast<const f32x4*>(sc + h * 64 + 16 * g);
+        cw.vs[h] = *reinterpret_cast<const f32x4*>(sc + (2 + h) * 64 + 16 * g);
+      }
     }
   };
 
@@ -224,51 +328,29 @@ void cascade_prefix_kernel(DecodeParams p) {
     }
   };
 
+
+  // ---- every chunk of the partition, two LDS stages: the next chunk's
+  // pieces are in flight while the current one is consumed
   const int nchunks = (t_end - t_begin + 31) / 32;
-  {
-    Chunk<kInt8, D> cb;
-    int blk[2], row0[2];
-    for (int ch = wave; ch < nchunks; ch += W) {
-      chunk_blocks(ch, blk, row0);
-      ld.load(cb, blk, row0);
-      consume(cb, ch);
+  piece_load(0);
+  piece_store(0);
+  __syncthreads();
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const bool more = ch + 1 < nchunks;
+    if (more) piece_load(ch + 1);
+    {
+      Chunk<kInt8, D> cw;
+      lds_chunk(ch & 1, cw);
+      consume(cw, ch);
     }
+    if (more) piece_store((ch + 1) & 1);
+    __syncthreads();
   }
 
-  // merge the waves' states per query (wave 0 keeps the result)
+  // ---- this wave's partials
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    l_run[t] = groups_sum(l_run[t]);
-    red_m[wave][t][lane] = m_run[t];
-    red_l[wave][t][lane] = l_run[t];
-    if (wave > 0) {
-#pragma unroll
-      for (int n = 0; n < NN; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red_acc[wave - 1][t][4 * n + i][lane] = acc[t][n][i];
-    }
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float M = m_run[t];
-#pragma unroll
-    for (int w = 1; w < W; ++w) M = fmaxf(M, red_m[w][t][lane]);
-    // M is finite: wave 0 always has chunk 0 (the partition is non-empty)
-    const float f0 = fast_exp2(m_run[t] - M);
-    float Lsum = l_run[t] * f0;
-#pragma unroll
-    for (int n = 0; n < NN; ++n) acc[t][n] *= f0;
-#pragma unroll
-    for (int w = 1; w < W; ++w) {
-      const float fw = fast_exp2(red_m[w][t][lane] - M);  // -inf (idle wave) -> 0
-      Lsum += fw * red_l[w][t][lane];
-#pragma unroll
-      for (int n = 0; n < NN; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][n][i] += fw * red_acc[w - 1][t][4 * n + i][lane];
-    }
+    const float Lsum = groups_sum(l_run[t]);
     const int r = q0 + 16 * t + c;
     if (r >= nq) continue;
     const size_t bh = static_cast<size_t>(gs + r / G) * H + kvh * G + r % G;
@@ -277,7 +359,7 @@ void cascade_prefix_kernel(DecodeParams p) {
 #pragma unroll
     for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[t][n];
     if (g == 0) {
-      p.ws_m[slot] = M;
+      p.ws_m[slot] = m_run[t];
       p.ws_l[slot] = Lsum;
     }
   }
@@ -286,10 +368,10 @@ void cascade_prefix_kernel(DecodeParams p) {
 template <bool kInt8, int D, int BS>
 hipError_t launch_t(const DecodeParams& p, int max_group_size, hipStream_t s) {
   const int G = p.num_heads / p.num_kv_heads;
-  const int qtiles = (max_group_size * G + 16 * kPrefixTiles - 1) / (16 * kPrefixTiles);
+  const int qtiles = (max_group_size * G + kPrefixQueries - 1) / kPrefixQueries;
   const dim3 grid(static_cast<unsigned>(p.num_groups * p.num_kv_heads), static_cast<unsigned>(qtiles),
                   static_cast<unsigned>(p.prefix_parts));
-  hipLaunchKernelGGL((cascade_prefix_kernel<kInt8, D, BS, kDecodeWaves, kPrefixTiles>), grid,
+  hipLaunchKernelGGL((cascade_prefix_kernel<kInt8, D, BS, kPrefixTiles>), grid,
                      dim3(kDecodeWaves * kWave), 0, s, p);
   return hipGetLastError();
 }

@@ -350,8 +350,9 @@ void decode_mfma_kernel(DecodeParams p) {
 
 template <bool kInt8, int D, int BS>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(p.num_seqs * p.num_kv_heads),
-                  static_cast<unsigned>(p.num_parts));
+  // cascade: slots [0, prefix_parts) belong to the shared-prefix kernel
+  const int parts = p.group_start != nullptr ? p.num_parts - p.prefix_parts : p.num_parts;
+  const dim3 grid(static_cast<unsigned>(p.num_seqs * p.num_kv_heads), static_cast<unsigned>(parts));
   hipLaunchKernelGGL((decode_mfma_kernel<kInt8, D, BS, kDecodeWaves>), grid,
                      dim3(kDecodeWaves * kWave), 0, s, p);
   return hipGetLastError();

@@ -210,14 +210,15 @@ pkv_status launch_reduce(const DecodeSetup& st, hipStream_t stream) {
 }
 
 // Shared-prefix partition length: the longest of 2048 ... 32 tokens that
-// still gives the prefix kernel about 1024 workgroups (at most
-// kMaxPartBlocks blocks; a multiple of 32, hence of the block size).
+// still gives the prefix kernel one full round of workgroups (two per CU on
+// 256 CUs; at most kMaxPartBlocks blocks; a multiple of 32, hence of the
+// block size).
 int32_t auto_prefix_part_tokens(int64_t prefix_units, int32_t block_size, int32_t max_shared_blocks) {
   const int64_t span = static_cast<int64_t>(max_shared_blocks) * block_size;
   int32_t pt = 32;
   for (int32_t cand : {2048, 1024, 512, 256, 128, 64}) {
     if (cand > kMaxPartBlocks * block_size) continue;
-    if (prefix_units * ((span + cand - 1) / cand) >= 1024) {
+    if (prefix_units * ((span + cand - 1) / cand) >= 512) {
       pt = cand;
       break;
     }
@@ -225,7 +226,7 @@ int32_t auto_prefix_part_tokens(int64_t prefix_units, int32_t block_size, int32_
   return pt;
 }
 
-constexpr int kPrefixQueries = 16 * pkv::kPrefixTiles;  // queries per prefix workgroup
+using pkv::kPrefixQueries;  // queries per prefix workgroup
 
 struct CascadeSizes {
   int32_t ppt, pparts, spt, sparts, qtiles;

@@ -71,8 +71,10 @@ enum class KvKind { F32 = 0, BF16 = 1, I8 = 2 };
 
 // Waves per workgroup of the partition kernels.
 constexpr int kDecodeWaves = 4;
-// Query-column tiles (16 queries each) per workgroup of the shared-prefix kernel.
+// Query-column tiles (16 queries each) per wave of the shared-prefix kernel,
+// and queries per workgroup.
 constexpr int kPrefixTiles = 2;
+constexpr int kPrefixQueries = 16 * kPrefixTiles * kDecodeWaves;
 
 // Tokens of group g attended by the shared-prefix kernel: its shared
 // blocks, capped at the whole blocks of its first sequence's context (so
