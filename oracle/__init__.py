@@ -10,9 +10,9 @@ method's arithmetic.
 
 Everything here is a plain, slow, obviously-correct CPU definition:
 
-* floating point is fp64, except the int8 quantiser, which is fp32 on purpose
-  (its result is an integer code, so both sides must decide it in the same
-  precision);
+* floating point is fp64, except the int8 and FP8 quantisers, which are fp32
+  on purpose (their results are codes, so both sides must decide them in the
+  same precision);
 * gathers go through the block table one logical block at a time;
 * attention is the textbook ``softmax(scale * K q) V`` per query head.
 
@@ -21,7 +21,8 @@ Sources (web pages, cited by title and section):
 * [ENG5] "LLM Engineering (5): core techniques of inference optimization"
   (chenk.top), sections "Two phases with very different characteristics",
   "Paged attention", "Block manager: how paging works",
-  "INT8 weight-only quantization" and "KV-cache quantization".
+  "INT8 weight-only quantization", "KV-cache quantization" (int8 and FP8
+  caches with per-token scales) and "SGLang and RadixAttention".
 * [LAYERS] the four-layer inference-optimization article (gsyq.cn/news/366077),
   section 2.1 (KV-cache size formula and its 7B worked number), 2.2
   (PagedAttention, block size 16/32) and 2.3 (KV-cache quantization with
@@ -44,6 +45,7 @@ from .attention import (
     decode_attention,
 )
 from .cache import cache_write, quantize_int8, cache_write_int8
+from .fp8 import e4m3_decode, e4m3_encode, quantize_fp8, cache_write_fp8
 from .closed_forms import kv_cache_bytes, decode_kv_bytes
 
 __all__ = [
@@ -58,6 +60,10 @@ __all__ = [
     "cache_write",
     "quantize_int8",
     "cache_write_int8",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quantize_fp8",
+    "cache_write_fp8",
     "kv_cache_bytes",
     "decode_kv_bytes",
 ]

@@ -33,7 +33,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
 
 import numpy as np
 
-KV_DTYPES = ("f32", "bf16", "i8")
+from . import fp8 as _fp8
+
+KV_DTYPES = ("f32", "bf16", "i8", "fp8")
 
 
 def n_blocks(context_len, block_size):
@@ -90,6 +92,8 @@ def widen(x, kind):
         return x.astype(np.float32).astype(np.float64)
     if kind == "i8":
         return x.astype(np.int8).astype(np.float64)
+    if kind == "fp8":
+        return _fp8.e4m3_decode(x.astype(np.uint8))
     raise ValueError(f"unknown element type {kind!r}")
 
 
@@ -100,8 +104,8 @@ def gather_kv(k_cache, v_cache, block_table, context_len, block_size, kv_head,
     Walks the sequence's logical blocks in order; logical block ``j`` lives in
     physical block ``block_table[j]`` and contributes its first
     ``rows_in_block(L, bs, j)`` rows.  Table entries past the last logical
-    block are never read.  For an int8 cache each element's value is its code
-    times its token's scale.
+    block are never read.  For an int8 or FP8 cache each element's value is
+    its code's value times its token's scale.
     """
     L = int(context_len)
     bs = int(block_size)
@@ -113,7 +117,7 @@ def gather_kv(k_cache, v_cache, block_table, context_len, block_size, kv_head,
         blk = int(block_table[j])
         k_rows = widen(k_cache[blk, kv_head, :rows, :], kv_dtype)        # [rows, D]
         v_rows = widen(v_cache[blk, kv_head, :, :rows], kv_dtype).T      # [rows, D]
-        if kv_dtype == "i8":
+        if kv_dtype in ("i8", "fp8"):
             ks = np.asarray(k_scale[blk, kv_head, :rows], dtype=np.float32).astype(np.float64)
             vs = np.asarray(v_scale[blk, kv_head, :rows], dtype=np.float32).astype(np.float64)
             k_rows = k_rows * ks[:, None]
@@ -147,7 +151,7 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
     Shapes: ``q[B, H, D]``; ``k_cache[NB, Hkv, bs, D]``;
     ``v_cache[NB, Hkv, D, bs]``; ``block_tables[B, MB]``; ``context_lens[B]``;
     int8 scales ``[NB, Hkv, bs]``.  ``q_dtype`` / ``kv_dtype`` name the stored
-    element types ("f32", "bf16", "i8").
+    element types ("f32", "bf16", "i8", "fp8").
 
     Returns ``out[B, H, D]`` in fp64.  With ``samples`` (an iterable of
     ``(b, h)`` pairs) only those rows are computed and the others are NaN.

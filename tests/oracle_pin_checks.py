@@ -17,6 +17,7 @@ import numpy as np
 import oracle
 from oracle import attention as oatt
 from oracle import cache as ocache
+from oracle import fp8 as ofp8
 from paged_kv_cache_29_amd import workloads
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -452,6 +453,149 @@ def check_int8_write_brute():
         assert np.isnan(ks2[s // bs, 0, s % bs])
 
 
+# ---------------------------------------------------------------- FP8 (E4M3) codes
+def check_fp8_decode_closed_forms():
+    # 1.0 = 2^0 (1 + 0): exponent field 7 -> 0x38; largest finite 1.75 * 2^8;
+    # smallest normal 2^-6; smallest subnormal 2^-9; sign bit; the NaN codes
+    want = {0x00: 0.0, 0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6,
+            0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x3C: 1.5, 0x40: 2.0, 0x30: 0.5, 0x77: 240.0}
+    got = ofp8.e4m3_decode(np.array(list(want), np.uint8))
+    assert got.tolist() == list(want.values())
+    assert np.isnan(ofp8.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    # values increase with the code over 0x00 .. 0x7E and are mirrored by the sign bit
+    pos = ofp8.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(ofp8.e4m3_decode(np.arange(0x80, 0xFF, dtype=np.uint8)), -pos)
+
+
+def check_fp8_decode_torch():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = ofp8.e4m3_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got)) and np.array_equal(ref[~nan], got[~nan])
+
+
+def check_fp8_encode_torch():
+    import torch
+    rng = np.random.default_rng(21)
+    v = np.concatenate([rng.standard_normal(100000).astype(np.float32) * np.float32(60),
+                        rng.uniform(-464, 464, 100000).astype(np.float32),
+                        rng.standard_normal(50000).astype(np.float32) * np.float32(3e-3)])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ofp8.e4m3_encode(v), ref)
+
+
+def check_fp8_encode_ties_and_saturation():
+    pos = ofp8.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    for c in range(0x7E):
+        mid = np.float32((pos[c] + pos[c + 1]) / 2)           # exact in fp32
+        assert float(mid) == (pos[c] + pos[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert int(ofp8.e4m3_encode(mid)) == even, c
+        assert int(ofp8.e4m3_encode(-mid)) == 0x80 | even, c
+        # just off the midpoint goes to the nearer side
+        assert int(ofp8.e4m3_encode(np.nextafter(mid, np.float32(0)))) == c
+        assert int(ofp8.e4m3_encode(np.nextafter(mid, np.float32(1e9)))) == c + 1
+    # every finite code is its own encoding
+    assert np.array_equal(ofp8.e4m3_encode(pos.astype(np.float32)), np.arange(0x7F, dtype=np.uint8))
+    # beyond the largest value: saturate (448 + anything, never the NaN code)
+    assert ofp8.e4m3_encode(np.float32(464.0)) == 0x7E
+    assert ofp8.e4m3_encode(np.float32(1e6)) == 0x7E and ofp8.e4m3_encode(np.float32(-1e6)) == 0xFE
+    assert ofp8.e4m3_encode(np.float32(-0.0)) == 0x80 and ofp8.e4m3_encode(np.float32(1e-30)) == 0
+
+
+def check_fp8_quantizer_closed_forms():
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((400, 128)).astype(np.float32) * rng.uniform(1e-3, 1e3, (400, 1)).astype(np.float32)
+    q, s = ofp8.quantize_fp8(x)
+    a = np.max(np.abs(x), axis=1)
+    i = np.argmax(np.abs(x), axis=1)
+    # the row maximum lands on +-448
+    top = q[np.arange(400), i]
+    assert np.all((top == 0x7E) | (top == 0xFE))
+    assert np.all(np.abs(np.float32(448) * s - a) <= 2 * np.spacing(a))
+    # reconstruction: relative half-step of E4M3 (2^-4) for normal codes,
+    # half of 2^-9 * s for subnormal ones
+    val = ofp8.e4m3_decode(q) * s[:, None].astype(np.float64)
+    err = np.abs(x.astype(np.float64) - val)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s[:, None]) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    # zero row, and row independence
+    q0, s0 = ofp8.quantize_fp8(np.zeros((1, 16), np.float32))
+    assert s0[0] == 0 and np.all(q0 == 0)
+    q1, s1 = ofp8.quantize_fp8(x[9:10])
+    assert np.array_equal(q1[0], q[9]) and s1[0] == s[9]
+
+
+def check_fp8_write_brute():
+    rng = np.random.default_rng(23)
+    NB, Hkv, bs, D, T = 4, 2, 16, 16, 9
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = (rng.standard_normal((T, Hkv, D)) * 1e-3).astype(np.float32)
+    k[3, 0] = 0.0
+    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
+    slots[5] = -1
+    kc = np.zeros((NB, Hkv, bs, D), np.uint8)
+    vc = np.zeros((NB, Hkv, D, bs), np.uint8)
+    ksc = np.full((NB, Hkv, bs), np.nan, np.float32)
+    vsc = np.full((NB, Hkv, bs), np.nan, np.float32)
+    k2, v2, ks2, vs2 = ofp8.cache_write_fp8(k, v, kc, vc, ksc, vsc, slots, bs)
+    values = [ofp8.e4m3_value(c) for c in range(0x7F)]
+    for t, sl in enumerate(slots.tolist()):
+        if sl < 0:
+            continue
+        blk, r = sl // bs, sl % bs
+        for h in range(Hkv):
+            for src, codes, sc in ((k[t, h], k2[blk, h, r, :], ks2[blk, h, r]),
+                                   (v[t, h], v2[blk, h, :, r], vs2[blk, h, r])):
+                a = float(np.max(np.abs(src)))
+                sref = np.float32(np.float32(a) / np.float32(448.0))
+                if a == 0:
+                    assert sc == 0 and np.all(codes == 0)
+                    continue
+                assert sc == sref
+                for d in range(D):
+                    ratio = float(np.float32(src[d] / sref))
+                    mag = min(abs(ratio), 448.0)
+                    best = min(range(0x7F), key=lambda c: (abs(values[c] - mag), c % 2))
+                    want = best | (0x80 if ratio < 0 or (ratio == 0 and math.copysign(1, ratio) < 0) else 0)
+                    assert int(codes[d]) == want, (t, h, d, ratio)
+    for sl in set(range(NB * bs)) - set(slots.tolist()):
+        assert np.isnan(ks2[sl // bs, 0, sl % bs])
+
+
+def check_brute_force_fp8():
+    """FP8 cache: value = E4M3 value of the code x per-token scale."""
+    rng = np.random.default_rng(24)
+    NB, Hkv, bs, D, H = 6, 2, 16, 8, 4
+    kc = rng.integers(0, 0x7F, size=(NB, Hkv, bs, D)).astype(np.uint8) | \
+        (rng.integers(0, 2, size=(NB, Hkv, bs, D)).astype(np.uint8) << 7)
+    vc = rng.integers(0, 0x7F, size=(NB, Hkv, D, bs)).astype(np.uint8)
+    ks = rng.uniform(1e-4, 3e-3, size=(NB, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(1e-4, 3e-3, size=(NB, Hkv, bs)).astype(np.float32)
+    tables = np.array([[2, 5, 0], [1, 4, -1]], dtype=np.int32)
+    lens = np.array([37, 17], dtype=np.int32)
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    out = oracle.decode_attention(q, kc, vc, tables, lens, 0.2, H, Hkv, D, bs, "fp8", "f32",
+                                  k_scale=ks, v_scale=vs)
+    for b in range(2):
+        for h in range(H):
+            g = h // 2
+            sc, rows = [], []
+            for t in range(int(lens[b])):
+                blk, r = int(tables[b][t // bs]), t % bs
+                kr = [ofp8.e4m3_value(kc[blk, g, r, d]) * float(ks[blk, g, r]) for d in range(D)]
+                vr = [ofp8.e4m3_value(vc[blk, g, d, r]) * float(vs[blk, g, r]) for d in range(D)]
+                sc.append(0.2 * sum(float(q[b, h, d]) * kr[d] for d in range(D)))
+                rows.append(vr)
+            m = max(sc)
+            ps = [math.exp(x - m) for x in sc]
+            ref = [sum(p * vr[d] for p, vr in zip(ps, rows)) / sum(ps) for d in range(D)]
+            np.testing.assert_allclose(out[b, h], ref, rtol=1e-12, atol=1e-14)
+
+
 ALL_CHECKS = [
     check_worked_example_blocks,
     check_worked_example_gather,
@@ -473,4 +617,11 @@ ALL_CHECKS = [
     check_quantizer_ties_and_clamp,
     check_quantizer_closed_forms,
     check_int8_write_brute,
+    check_fp8_decode_closed_forms,
+    check_fp8_decode_torch,
+    check_fp8_encode_torch,
+    check_fp8_encode_ties_and_saturation,
+    check_fp8_quantizer_closed_forms,
+    check_fp8_write_brute,
+    check_brute_force_fp8,
 ]

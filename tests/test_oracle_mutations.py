@@ -12,6 +12,7 @@ import pytest
 import oracle
 from oracle import attention as oatt
 from oracle import cache as ocache
+from oracle import fp8 as ofp8
 from oracle_pin_checks import ALL_CHECKS
 
 
@@ -100,6 +101,65 @@ def _widen_bf16_shift15(x, kind):
     return _orig_widen(x, kind)
 
 
+def _fp8_table(bias=7, sub_exp=-6):
+    vals = []
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 7
+        if e == 0xF and m == 7:
+            vals.append(float("nan"))
+        elif e == 0:
+            vals.append(sign * 2.0 ** sub_exp * m / 8.0)
+        else:
+            vals.append(sign * 2.0 ** (e - bias) * (1 + m / 8.0))
+    return np.array(vals)
+
+
+_T_BIAS8 = _fp8_table(bias=8, sub_exp=-7)
+_T_SUB = _fp8_table(sub_exp=-7)
+
+
+def _fp8_encode_ties_away(v):
+    v = np.asarray(v, dtype=np.float32)
+    out = _orig_e4m3_encode(v)
+    pos = _orig_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    a = np.abs(v).astype(np.float64)
+    for i in np.ndindex(v.shape):
+        c = int(out[i]) & 0x7F
+        for lo in (c - 1, c):  # a tie resolved toward the smaller neighbour moves up
+            if 0 <= lo < 0x7E and a[i] == (pos[lo] + pos[lo + 1]) / 2:
+                out[i] = (out[i] & 0x80) | (lo + 1)
+    return out
+
+
+def _fp8_encode_truncate(v):
+    v = np.asarray(v, dtype=np.float32)
+    pos = _orig_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    a = np.minimum(np.abs(v).astype(np.float64), 448.0)
+    code = np.searchsorted(pos, a, side="right") - 1
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def _fp8_quant_over_240(x):
+    x = np.asarray(x, dtype=np.float32)
+    a = np.max(np.abs(x), axis=-1)
+    s = (a / np.float32(240.0)).astype(np.float32)
+    nz = s > 0
+    safe = np.where(nz, s, np.float32(1.0)).astype(np.float32)
+    codes = np.where(nz[..., None], ofp8.e4m3_encode((x / safe[..., None]).astype(np.float32)), 0)
+    return codes.astype(np.uint8), np.where(nz, s, 0).astype(np.float32)
+
+
+def _gather_fp8_no_v_scale(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                           kv_dtype, k_scale=None, v_scale=None):
+    if kv_dtype == "fp8":
+        v_scale = np.ones_like(v_scale)
+    return _orig_gather(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                        kv_dtype, k_scale, v_scale)
+
+
+_orig_e4m3_encode = ofp8.e4m3_encode
+_orig_e4m3_decode = ofp8.e4m3_decode
 _orig_gather = oatt.gather_kv
 _orig_attend = oatt.attend_one
 _orig_widen = oatt.widen
@@ -121,6 +181,12 @@ MUTATIONS = {
     "quant_round_half_away": [(ocache, "quantize_int8", _quant_half_away)],
     "quant_scale_over_128": [(ocache, "quantize_int8", _quant_scale_128)],
     "cache_write_row_shift": [(ocache, "cache_write", _cache_write_row_shift)],
+    "fp8_exponent_bias_8": [(ofp8, "e4m3_decode", lambda c: _T_BIAS8[np.asarray(c, np.uint8)])],
+    "fp8_subnormal_scale": [(ofp8, "e4m3_decode", lambda c: _T_SUB[np.asarray(c, np.uint8)])],
+    "fp8_round_ties_away": [(ofp8, "e4m3_encode", _fp8_encode_ties_away)],
+    "fp8_truncate": [(ofp8, "e4m3_encode", _fp8_encode_truncate)],
+    "fp8_scale_over_240": [(ofp8, "quantize_fp8", _fp8_quant_over_240)],
+    "fp8_v_scale_dropped": [(oatt, "gather_kv", _gather_fp8_no_v_scale)],
 }
 
 
