@@ -13,7 +13,8 @@ quantising write, then paged_attention_decode's two kernels), reported under
 Prints ONE JSON line.  ``value`` is the KV bytes a step must read divided by
 the measured step time (GB/s) on the 7B-shaped MHA workload (batch 32,
 2048-token contexts, 32 heads x 128 dims, bf16, 16-token blocks).  The
-70B-shaped GQA workloads (bf16, and int8 KV) are reported under
+70B-shaped GQA workloads (bf16, int8 KV and FP8 KV) and the shared-prefix
+workload (with its cascade-decode leg) are reported under
 ``secondary``.  Per-kernel times come from HIP events recorded on the
 stream the kernels run on: each kernel is also run alone, back to back, and
 its average duration is the roofline's time.
@@ -41,6 +42,7 @@ METRIC = "paged decode-attn KV read GB/s (% of HBM peak) + µs/step, 7B & 70B sh
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL_SOURCES = ["decode_mfma.hip", "decode_append.hpp", "pkv_device.hpp", "pkv_kernels.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.txt")
+CODED = ("i8", "fp8")  # caches of byte codes with per-(token, kv-head) scales
 
 DESCRIPTIONS = {
     1: "tiny_f32: B=4 L={47,200,16,1} H=Hkv=4 D=64 bs=16 fp32",
@@ -48,6 +50,7 @@ DESCRIPTIONS = {
     3: "gqa70b_bf16: B=50 L~logU[1024,32768] H=64 Hkv=8 D=128 bs=16 bf16",
     4: "prefix_bf16: B=256 shared 2000-token prefix + U{50..500} H=32 Hkv=8 D=128",
     5: "int8_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 int8 KV, bf16 q",
+    6: "fp8_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 FP8 E4M3 KV, bf16 q",
 }
 
 
@@ -74,8 +77,8 @@ def read_traffic(workload_name):
 
 
 def kv_bytes(w):
-    elem = 1 if w.kv_dtype == "i8" else (4 if w.kv_dtype == "f32" else 2)
-    scale = 4 if w.kv_dtype == "i8" else 0
+    elem = 1 if w.kv_dtype in CODED else (4 if w.kv_dtype == "f32" else 2)
+    scale = 4 if w.kv_dtype in CODED else 0
     return 2 * w.num_kv_heads * (w.head_dim * elem + scale) * w.attended_tokens
 
 
@@ -96,14 +99,16 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
     slot = torch.from_numpy(w.slot_new).to(dev)
     k_new, v_new = up(w.k_new, store), up(w.v_new, store)
     ks = vs = None
-    if w.kv_dtype == "i8":
+    write_codes = pkv.kv_cache_write_fp8 if w.kv_dtype == "fp8" else pkv.kv_cache_write_int8
+    if w.kv_dtype in CODED:
         NB, Hkv, bs, D = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
-        kc = torch.zeros((NB, Hkv, bs, D), dtype=torch.int8, device=dev)
-        vc = torch.zeros((NB, Hkv, D, bs), dtype=torch.int8, device=dev)
+        cd = torch.float8_e4m3fn if w.kv_dtype == "fp8" else torch.int8
+        kc = torch.zeros((NB, Hkv, bs, D), dtype=torch.uint8, device=dev).view(cd)
+        vc = torch.zeros((NB, Hkv, D, bs), dtype=torch.uint8, device=dev).view(cd)
         ks = torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=dev)
         vs = torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=dev)
         kf, vf, sf = up(w.k_fill, "f32"), up(w.v_fill, "f32"), torch.from_numpy(w.slot_fill).to(dev)
-        pkv.kv_cache_write_int8(kf, vf, kc, vc, ks, vs, sf)   # fill the cache once
+        write_codes(kf, vf, kc, vc, ks, vs, sf)   # fill the cache once
         torch.cuda.synchronize()
         del kf, vf, sf
     else:
@@ -117,8 +122,8 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
     dkw = dict(k_scale=ks, v_scale=vs, partition_tokens=pt, workspace=ws)
 
     def write():
-        if w.kv_dtype == "i8":
-            pkv.kv_cache_write_int8(k_new, v_new, kc, vc, ks, vs, slot)
+        if w.kv_dtype in CODED:
+            write_codes(k_new, v_new, kc, vc, ks, vs, slot)
         else:
             pkv.kv_cache_write(k_new, v_new, kc, vc, slot)
 
@@ -259,8 +264,8 @@ def unique_tile_bytes(w):
     for b, L in enumerate(w.context_lens):
         n = (int(L) + bs - 1) // bs
         ids.update(int(x) for x in w.block_tables[b, :n])
-    elem = 1 if w.kv_dtype == "i8" else (4 if w.kv_dtype == "f32" else 2)
-    scale = 4 if w.kv_dtype == "i8" else 0
+    elem = 1 if w.kv_dtype in CODED else (4 if w.kv_dtype == "f32" else 2)
+    scale = 4 if w.kv_dtype in CODED else 0
     return int(len(ids) * 2 * w.num_kv_heads * bs * (w.head_dim * elem + scale))
 
 
@@ -345,7 +350,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--configs", default="2,3,5,4", help="first is the headline workload")
+    ap.add_argument("--configs", default="2,3,5,6,4", help="first is the headline workload")
     ap.add_argument("--block-size", type=int, default=16, help="for config 4 (16 or 32)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -399,7 +404,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "i8": "i8", "f32": "f32"}[w.kv_dtype],
+        "dtype": {"bf16": "bf16", "i8": "i8", "fp8": "fp8_e4m3", "f32": "f32"}[w.kv_dtype],
         "data": "synthetic (seeded N(0,1) K/V/q, shuffled block tables)",
         "config": {"workload": head["workload"], "num_seqs": w.num_seqs,
                    "context_len": int(w.context_lens.max()), "num_heads": w.num_heads,
@@ -418,7 +423,7 @@ def main():
         "kernel_source_sha": kernel_source_sha(),
         "secondary": [{k: v for k, v in r.items()} for r in results[1:]],
     }
-    if args.cpu_seconds > 0 and w.kv_dtype != "i8":
+    if args.cpu_seconds > 0 and w.kv_dtype not in CODED:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     else:

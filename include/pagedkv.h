@@ -33,7 +33,7 @@
  *   v_cache      [NB][Hkv][D][bs]   each (block, kv-head) tile dim-major:
  *                                   element (token row r, dim d) at d*bs + r
  *   k_scale,
- *   v_scale      [NB][Hkv][bs] fp32 (int8 caches only)
+ *   v_scale      [NB][Hkv][bs] fp32 (int8 and FP8 caches only)
  *   block_tables [B][MB] int32      logical block j of sequence b lives in
  *                                   physical block block_tables[b*MB + j];
  *                                   entries past the sequence's last block
@@ -70,7 +70,9 @@ typedef enum {
 typedef enum {
   PKV_F32 = 0,   /* IEEE binary32                         */
   PKV_BF16 = 1,  /* bfloat16, 16-bit patterns             */
-  PKV_I8 = 2     /* int8 codes with an fp32 per-row scale */
+  PKV_I8 = 2,    /* int8 codes with an fp32 per-row scale */
+  PKV_FP8 = 3    /* FP8 E4M3 codes (OCP: bias 7, largest finite 448, no
+                    infinities) with an fp32 per-row scale              */
 } pkv_dtype;
 
 /*
@@ -107,6 +109,26 @@ pkv_status pkv_kv_cache_write_int8(const float* k, const float* v, int8_t* k_cac
                                    int64_t num_blocks, void* stream);
 
 /*
+ * Quantising cache write for an FP8 KV cache ([ENG5] "KV-cache
+ * quantization": FP8 KV caches with per-token scales computed online;
+ * [LAYERS] 2.3: K and V quantized separately).
+ *   Each (token, kv-head) row x of k (and, separately, of v), fp32, becomes
+ *     a = max_d |x_d|;  s = a / 448 (IEEE fp32 division);
+ *     code_d = the E4M3 code nearest to x_d / s (ties to the even code;
+ *              |x_d / s| above 448, possible only through the rounding of
+ *              s, gives +-448; the sign of a zero is kept);
+ *     s == 0 (a == 0, or a / 448 underflows) gives all codes 0.
+ *   Codes and scales go to the slots as in pkv_kv_cache_write_int8.  Inputs
+ *   must be finite.  Bit-exact: identical codes and scales for identical
+ *   inputs.  Errors as for pkv_kv_cache_write_int8.
+ */
+pkv_status pkv_kv_cache_write_fp8(const float* k, const float* v, uint8_t* k_cache,
+                                  uint8_t* v_cache, float* k_scale, float* v_scale,
+                                  const int64_t* slot_mapping, int64_t num_tokens,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int64_t num_blocks, void* stream);
+
+/*
  * Bytes of device workspace pkv_paged_attention_decode needs for these
  * sizes (0 when every sequence fits one partition, in which case the
  * workspace pointer may be NULL).  partition_tokens as for decode.  Returns
@@ -132,11 +154,12 @@ int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_he
  *   For each sequence b with L = context_lens[b] and query head h (kv-head
  *   g = h / G), with K_b, V_b the L tokens gathered through the block table:
  *     out[b][h][:] = softmax(scale * K_b q[b][h]) V_b,  accumulated in fp32;
- *   L == 0 gives zeros.  For an int8 cache each K/V element's value is its
+ *   L == 0 gives zeros.  For an int8 or FP8 cache each K/V element's value is its
  *   code times the token's scale.
- * Supported: (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16), (BF16, I8)};
+ * Supported: (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16), (BF16, I8),
+ * (BF16, FP8)};
  * out has q's dtype; head_dim in {64, 128}; block_size in {16, 32};
- * G in {1, 2, 4, 8, 16}.  k_scale and v_scale are required for I8 and must
+ * G in {1, 2, 4, 8, 16}.  k_scale and v_scale are required for I8 and FP8 and must
  * be NULL otherwise.  num_seqs == 0 is a no-op.  scale must be finite.
  * partition_tokens: 0 for the automatic choice, else a multiple of 32 in
  * [32, 128 * block_size]; long contexts are split into partitions of that
@@ -193,7 +216,7 @@ pkv_status pkv_paged_attention_decode_reduce(
  *   the workgroups of the partition holding position L - 1 write the token
  *   before attending, and nothing else reads it.
  *   k_new, v_new: [B][Hkv][D], the cache element type (fp32 or bf16), or
- *   fp32 for an int8 cache (quantised in the kernel).  The block holding
+ *   fp32 for an int8 or FP8 cache (quantised in the kernel).  The block holding
  *   position L - 1 must belong to this sequence alone (copy it on write
  *   first if it is shared).  Other arguments, errors and the workspace as
  *   for pkv_paged_attention_decode; the caches (and int8 scales) are
@@ -244,7 +267,7 @@ pkv_status pkv_paged_attention_decode_step_partitions(
  *   prefix_partition_tokens: tokens of the shared span per workgroup; 0 for
  *   the automatic choice, else a multiple of 32 in [32, 128 * block_size].
  *   partition_tokens as for decode (for the remaining tokens).
- * Supported: (BF16, BF16) and (BF16, I8) with the sizes of decode; an fp32
+ * Supported: (BF16, BF16), (BF16, I8) and (BF16, FP8) with the sizes of decode; an fp32
  * cache returns PKV_ERR_UNSUPPORTED.  The workspace size comes from
  * pkv_paged_attention_cascade_workspace_size with the same sizes and is
  * needed whenever num_seqs > 0.  Three launches: prefix kernel (skipped when

@@ -16,9 +16,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
-PKV_F32, PKV_BF16, PKV_I8 = range(3)
+PKV_F32, PKV_BF16, PKV_I8, PKV_FP8 = range(4)
 
-_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_I8}
+_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_I8,
+           torch.float8_e4m3fn: PKV_FP8}
+_CODED = (PKV_I8, PKV_FP8)  # byte codes with per-(token, kv-head) scales
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -33,6 +35,8 @@ _DECODE_ARGS = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32,
 SIGNATURES = {
     "pkv_kv_cache_write": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32,
                                    c_i64, c_i32, c_vp]),
+    "pkv_kv_cache_write_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32,
+                                       c_i32, c_i32, c_i64, c_vp]),
     "pkv_kv_cache_write_int8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32,
                                         c_i32, c_i32, c_i64, c_vp]),
     "pkv_paged_attention_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
@@ -134,13 +138,25 @@ def kv_cache_write(k, v, k_cache, v_cache, slot_mapping):
 
 def kv_cache_write_int8(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping):
     """Quantise fp32 K/V rows to int8 + per-(token, kv-head) scale and scatter."""
+    _write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, torch.int8,
+                 "pkv_kv_cache_write_int8")
+
+
+def kv_cache_write_fp8(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping):
+    """Quantise fp32 K/V rows to FP8 (E4M3) + per-(token, kv-head) scale and
+    scatter; the caches are ``torch.float8_e4m3fn`` tensors."""
+    _write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, torch.float8_e4m3fn,
+                 "pkv_kv_cache_write_fp8")
+
+
+def _write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, cache_dtype, entry):
     dev = k_cache.device
     for n, t in (("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("k_scale", k_scale), ("v_scale", v_scale), ("slot_mapping", slot_mapping)):
         _dense_on(t, dev, n)
     NB, Hkv, bs, D = k_cache.shape
     _need(tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB, Hkv, D, bs]")
-    _need(k_cache.dtype == v_cache.dtype == torch.int8, "int8 caches expected")
+    _need(k_cache.dtype == v_cache.dtype == cache_dtype, f"{cache_dtype} caches expected")
     _need(k.dtype == v.dtype == torch.float32, "k, v must be float32")
     _need(k.dim() == 3 and tuple(k.shape[1:]) == (Hkv, D) and k.shape == v.shape,
           "k, v must be [T, Hkv, D]")
@@ -148,10 +164,10 @@ def kv_cache_write_int8(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping):
           and k_scale.dtype == v_scale.dtype == torch.float32, "scales must be float32 [NB, Hkv, bs]")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (k.shape[0],),
           "slot_mapping must be int64 [T]")
-    st = load().pkv_kv_cache_write_int8(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
-                                        _ptr(k_scale), _ptr(v_scale), _ptr(slot_mapping),
-                                        k.shape[0], Hkv, D, bs, NB, _stream(dev))
-    _check(st, "kv_cache_write_int8")
+    st = getattr(load(), entry)(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                _ptr(v_scale), _ptr(slot_mapping), k.shape[0], Hkv, D, bs, NB,
+                                _stream(dev))
+    _check(st, entry[4:])
 
 
 # ------------------------------------------------------------------ decode
@@ -203,7 +219,7 @@ def _marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
           "context_lens must be int32 [B]")
     qd, kd = _DTYPES.get(q.dtype), _DTYPES.get(k_cache.dtype)
     _need(qd is not None and kd is not None, "unsupported dtype")
-    if kd == PKV_I8:
+    if kd in _CODED:
         for n, t in (("k_scale", k_scale), ("v_scale", v_scale)):
             _dense_on(t, dev, n)
             _need(t.dtype == torch.float32 and tuple(t.shape) == (NB, num_kv_heads, block_size),
@@ -211,7 +227,7 @@ def _marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
     MB = block_tables.shape[1]
     if workspace is _NO_WORKSPACE:  # the caller sizes its own workspace
         return (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                _ptr(k_scale if kd == PKV_I8 else None), _ptr(v_scale if kd == PKV_I8 else None),
+                _ptr(k_scale if kd in _CODED else None), _ptr(v_scale if kd in _CODED else None),
                 _ptr(block_tables), _ptr(context_lens), float(scale), B, num_heads, num_kv_heads,
                 head_dim, block_size, MB, NB, qd, kd, int(partition_tokens), None, 0, _stream(dev))
     need = workspace_size(B, num_heads, num_kv_heads, head_dim, block_size, MB, partition_tokens)
@@ -221,7 +237,7 @@ def _marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
         _dense_on(workspace, dev, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     return (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-            _ptr(k_scale if kd == PKV_I8 else None), _ptr(v_scale if kd == PKV_I8 else None),
+            _ptr(k_scale if kd in _CODED else None), _ptr(v_scale if kd in _CODED else None),
             _ptr(block_tables), _ptr(context_lens), float(scale), B, num_heads, num_kv_heads,
             head_dim, block_size, MB, NB, qd, kd, int(partition_tokens), _ptr(workspace),
             ws_bytes, _stream(dev))
@@ -302,7 +318,7 @@ def _marshal_step(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_
                            num_kv_heads, head_dim, block_size, k_scale, v_scale, partition_tokens,
                            workspace)
     dev = q.device
-    want = torch.float32 if k_cache.dtype == torch.int8 else k_cache.dtype
+    want = torch.float32 if _DTYPES.get(k_cache.dtype) in _CODED else k_cache.dtype
     for n, t in (("k_new", k_new), ("v_new", v_new)):
         _dense_on(t, dev, n)
         _need(tuple(t.shape) == (q.shape[0], num_kv_heads, head_dim), f"{n} must be [B, Hkv, D]")

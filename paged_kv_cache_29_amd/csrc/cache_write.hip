@@ -11,7 +11,9 @@
 // code = clamp(rint(x / s), -127, 127); a row whose scale is 0 (all zero,
 // or absmax / 127 underflows) gets s = 0 and code 0
 // ("LLM Engineering (5)", "KV-cache quantization" and "INT8 weight-only
-// quantization"; four-layer inference-optimization article, 2.3).  This
+// quantization"; four-layer inference-optimization article, 2.3).
+// kv_cache_write_fp8 does the same with s = absmax / 448 and the nearest
+// OCP E4M3 code of x / s (the same section's FP8 KV caches).  This
 // translation unit is built without fast-math and with correctly rounded
 // fp32 division, so the codes and scales are bit-exact.
 
@@ -57,7 +59,9 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
 
 // One lane group of D/4 lanes per (token, kv-head, K-or-V) row, 4 values per
 // lane; rows alternate K, V.
-__global__ __launch_bounds__(256) void cache_write_int8_kernel(WriteParams p) {
+// KV: I8 (s = absmax / 127, quantize_code) or FP8 (s = absmax / 448, fp8_code).
+template <KvKind KV>
+__global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
   const int D = p.head_dim;
   const int BS = p.block_size;
   const int Hkv = p.num_kv_heads;
@@ -67,8 +71,8 @@ __global__ __launch_bounds__(256) void cache_write_int8_kernel(WriteParams p) {
   const int64_t total_rows = p.num_tokens * Hkv * 2;
   const float* k = static_cast<const float*>(p.k);
   const float* v = static_cast<const float*>(p.v);
-  int8_t* kc = static_cast<int8_t*>(p.k_cache);
-  int8_t* vc = static_cast<int8_t*>(p.v_cache);
+  uint8_t* kc = static_cast<uint8_t*>(p.k_cache);
+  uint8_t* vc = static_cast<uint8_t*>(p.v_cache);
   for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block; r0 < total_rows;
        r0 += static_cast<int64_t>(gridDim.x) * rows_per_block) {
     const int64_t r = r0 + threadIdx.x / group;
@@ -86,22 +90,23 @@ __global__ __launch_bounds__(256) void cache_write_int8_kernel(WriteParams p) {
     float a = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
     for (int o = group / 2; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
     if (slot < 0) continue;
-    const float s = a / 127.0f;
-    int codes[4];
+    const float s = a / (KV == KvKind::FP8 ? 448.0f : 127.0f);
+    uint32_t codes[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) codes[e] = quantize_code(x[e], s);
+    for (int e = 0; e < 4; ++e)
+      codes[e] = KV == KvKind::FP8 ? fp8_code(x[e], s) : static_cast<uint32_t>(quantize_code(x[e], s));
     const int64_t blk = slot / BS;
     const int row = static_cast<int>(slot - blk * BS);
     const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * D;
     const int d0 = 4 * sub;
     if (!is_v) {
-      const uint32_t packed = (uint32_t(codes[0]) & 0xffu) | ((uint32_t(codes[1]) & 0xffu) << 8) |
-                              ((uint32_t(codes[2]) & 0xffu) << 16) | ((uint32_t(codes[3]) & 0xffu) << 24);
+      const uint32_t packed = (codes[0] & 0xffu) | ((codes[1] & 0xffu) << 8) |
+                              ((codes[2] & 0xffu) << 16) | ((codes[3] & 0xffu) << 24);
       *reinterpret_cast<uint32_t*>(kc + tile + static_cast<int64_t>(row) * D + d0) = packed;
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        vc[tile + static_cast<int64_t>(d0 + e) * BS + row] = static_cast<int8_t>(codes[e]);
+        vc[tile + static_cast<int64_t>(d0 + e) * BS + row] = static_cast<uint8_t>(codes[e] & 0xffu);
     }
     if (sub == 0) {
       const float sc = (s > 0.f) ? s : 0.f;
@@ -129,10 +134,13 @@ hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_cache_write_int8(const WriteParams& p, hipStream_t s) {
+hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s) {
   const int rows_per_block = 256 / (p.head_dim / 4);
   const unsigned grid = grid_for(p.num_tokens * p.num_kv_heads * 2, rows_per_block);
-  hipLaunchKernelGGL(cache_write_int8_kernel, dim3(grid), dim3(256), 0, s, p);
+  if (kind == KvKind::FP8)
+    hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::FP8>, dim3(grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::I8>, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

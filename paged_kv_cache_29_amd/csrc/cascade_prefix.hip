@@ -55,9 +55,11 @@ struct PrefixLds {
   static constexpr int UNITS = PIECE / (16 * kWave);  // 16-byte loads per lane per piece
 };
 
-template <bool kInt8, int D, int BS, int NT>
+// KV: BF16, or byte codes with per-token scales (I8, FP8).
+template <KvKind KV, int D, int BS, int NT>
 __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void cascade_prefix_kernel(DecodeParams p) {
+  constexpr bool kInt8 = KV != KvKind::BF16;  // byte codes (int8 or FP8) with scales
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
   static_assert(kDecodeWaves == 4, "one chunk piece per wave");
@@ -232,8 +234,8 @@ void cascade_prefix_kernel(DecodeParams p) {
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
       if constexpr (kInt8) {
-        vw[n] = u32x4{i8pair_to_bf16x2(cw.v[0][n], 0), i8pair_to_bf16x2(cw.v[0][n], 1),
-                      i8pair_to_bf16x2(cw.v[1][n], 0), i8pair_to_bf16x2(cw.v[1][n], 1)};
+        vw[n] = u32x4{codes_to_bf16x2<KV, 0>(cw.v[0][n]), codes_to_bf16x2<KV, 1>(cw.v[0][n]),
+                      codes_to_bf16x2<KV, 0>(cw.v[1][n]), codes_to_bf16x2<KV, 1>(cw.v[1][n])};
       } else {
         vw[n] = u32x4{cw.v[0][n].x, cw.v[0][n].y, cw.v[1][n].x, cw.v[1][n].y};
       }
@@ -255,8 +257,8 @@ void cascade_prefix_kernel(DecodeParams p) {
 #pragma unroll
           for (int jj = 0; jj < NJ / 2; ++jj) {
             const u32x4 w = cw.k[h][jj];
-            s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16(w.x, w.y), qf[t][2 * jj], s[h], 0, 0, 0);
-            s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16(w.z, w.w), qf[t][2 * jj + 1], s[h], 0, 0, 0);
+            s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes8_to_bf16<KV>(w.x, w.y), qf[t][2 * jj], s[h], 0, 0, 0);
+            s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes8_to_bf16<KV>(w.z, w.w), qf[t][2 * jj + 1], s[h], 0, 0, 0);
           }
         } else {
 #pragma unroll
@@ -365,30 +367,32 @@ void cascade_prefix_kernel(DecodeParams p) {
   }
 }
 
-template <bool kInt8, int D, int BS>
+template <KvKind KV, int D, int BS>
 hipError_t launch_t(const DecodeParams& p, int max_group_size, hipStream_t s) {
   const int G = p.num_heads / p.num_kv_heads;
   const int qtiles = (max_group_size * G + kPrefixQueries - 1) / kPrefixQueries;
   const dim3 grid(static_cast<unsigned>(p.num_groups * p.num_kv_heads), static_cast<unsigned>(qtiles),
                   static_cast<unsigned>(p.prefix_parts));
-  hipLaunchKernelGGL((cascade_prefix_kernel<kInt8, D, BS, kPrefixTiles>), grid,
+  hipLaunchKernelGGL((cascade_prefix_kernel<KV, D, BS, kPrefixTiles>), grid,
                      dim3(kDecodeWaves * kWave), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool kInt8>
+template <KvKind KV>
 hipError_t launch_kv(const DecodeParams& p, int max_group_size, hipStream_t s) {
   if (p.head_dim == 128)
-    return p.block_size == 16 ? launch_t<kInt8, 128, 16>(p, max_group_size, s)
-                              : launch_t<kInt8, 128, 32>(p, max_group_size, s);
-  return p.block_size == 16 ? launch_t<kInt8, 64, 16>(p, max_group_size, s)
-                            : launch_t<kInt8, 64, 32>(p, max_group_size, s);
+    return p.block_size == 16 ? launch_t<KV, 128, 16>(p, max_group_size, s)
+                              : launch_t<KV, 128, 32>(p, max_group_size, s);
+  return p.block_size == 16 ? launch_t<KV, 64, 16>(p, max_group_size, s)
+                            : launch_t<KV, 64, 32>(p, max_group_size, s);
 }
 
 }  // namespace
 
 hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group_size, hipStream_t s) {
-  return kv == KvKind::I8 ? launch_kv<true>(p, max_group_size, s) : launch_kv<false>(p, max_group_size, s);
+  if (kv == KvKind::I8) return launch_kv<KvKind::I8>(p, max_group_size, s);
+  if (kv == KvKind::FP8) return launch_kv<KvKind::FP8>(p, max_group_size, s);
+  return launch_kv<KvKind::BF16>(p, max_group_size, s);
 }
 
 }  // namespace pkv

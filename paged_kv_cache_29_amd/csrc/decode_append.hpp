@@ -18,9 +18,13 @@
 namespace pkv {
 
 // Called by all threads of a workgroup of at least 2 * D threads (and at
-// least two waves); pos = L - 1 >= 0.
-template <typename KT, int D, int BS>
+// least two waves); pos = L - 1 >= 0.  KV: F32 or BF16 (bit copy), I8 or
+// FP8 (quantised from fp32 rows).
+template <KvKind KV, int D, int BS>
 __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, int kvh, int pos) {
+  using KT = typename std::conditional<
+      KV == KvKind::F32, float,
+      typename std::conditional<KV == KvKind::BF16, uint16_t, uint8_t>::type>::type;
   const int Hkv = p.num_kv_heads;
   const int blk = p.block_tables[static_cast<size_t>(b) * p.max_blocks_per_seq + pos / BS];
   const int row = pos % BS;
@@ -29,7 +33,7 @@ __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, i
   KT* kc = static_cast<KT*>(const_cast<void*>(p.k_cache));
   KT* vc = static_cast<KT*>(const_cast<void*>(p.v_cache));
   const int t = threadIdx.x;
-  if constexpr (std::is_same<KT, int8_t>::value) {
+  if constexpr (KV == KvKind::I8 || KV == KvKind::FP8) {
     // wave 0 quantises the K row, wave 1 the V row; lane owns dims lane + 64i
     constexpr int ND = D / kWave;
     const int wave = t / kWave;
@@ -44,11 +48,12 @@ __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, i
         a = fmaxf(a, fabsf(v[i]));
       }
       a = wave_max(a);
-      const float s = a / 127.0f;
+      const float s = a / (KV == KvKind::FP8 ? 448.0f : 127.0f);
 #pragma unroll
       for (int i = 0; i < ND; ++i) {
         const int d = lane + kWave * i;
-        const int8_t code = static_cast<int8_t>(quantize_code(v[i], s));
+        const KT code = KV == KvKind::FP8 ? static_cast<KT>(fp8_code(v[i], s))
+                                          : static_cast<KT>(quantize_code(v[i], s));
         if (wave == 0)
           kc[tile + static_cast<size_t>(row) * D + d] = code;
         else

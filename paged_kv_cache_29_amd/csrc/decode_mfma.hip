@@ -56,13 +56,15 @@ namespace {
 // Chunks whose loads one wave issues together (32 KB of bf16 K/V, 16.5 KB of
 // int8 codes and scales), at two waves per SIMD.  Larger int8 batches were
 // measured slower.
-template <bool kInt8>
+template <KvKind KV>
 constexpr int kBatch = 2;
 
-template <bool kInt8, int D, int BS, int W>
+// KV: BF16, or byte codes with per-token scales (I8, FP8).
+template <KvKind KV, int D, int BS, int W>
 __global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mfma_kernel(DecodeParams p) {
-  constexpr int NB = kBatch<kInt8>;
+  constexpr bool kInt8 = KV != KvKind::BF16;  // byte codes (int8 or FP8) with scales
+  constexpr int NB = kBatch<KV>;
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
   constexpr int NJ = D / 32;  // QK MFMAs per score tile
@@ -105,7 +107,7 @@ void decode_mfma_kernel(DecodeParams p) {
   // Fused step: the partition holding the newest token writes it first; the
   // fence and barrier make the stores visible to this workgroup's loads.
   if (p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
-    append_new_token<typename std::conditional<kInt8, int8_t, uint16_t>::type, D, BS>(p, b, kvh, L - 1);
+    append_new_token<KV, D, BS>(p, b, kvh, L - 1);
     __threadfence_block();
     __syncthreads();
   }
@@ -171,8 +173,8 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int jj = 0; jj < NJ / 2; ++jj) {
           const u32x4 w = cw.k[h][jj];
-          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16(w.x, w.y), qf[2 * jj], s[h], 0, 0, 0);
-          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(i8x8_to_bf16(w.z, w.w), qf[2 * jj + 1], s[h], 0, 0, 0);
+          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes8_to_bf16<KV>(w.x, w.y), qf[2 * jj], s[h], 0, 0, 0);
+          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes8_to_bf16<KV>(w.z, w.w), qf[2 * jj + 1], s[h], 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -244,8 +246,8 @@ void decode_mfma_kernel(DecodeParams p) {
     for (int n = 0; n < NN; ++n) {
       u32x4 vw;
       if constexpr (kInt8) {
-        vw = u32x4{i8pair_to_bf16x2(cw.v[0][n], 0), i8pair_to_bf16x2(cw.v[0][n], 1),
-                   i8pair_to_bf16x2(cw.v[1][n], 0), i8pair_to_bf16x2(cw.v[1][n], 1)};
+        vw = u32x4{codes_to_bf16x2<KV, 0>(cw.v[0][n]), codes_to_bf16x2<KV, 1>(cw.v[0][n]),
+                   codes_to_bf16x2<KV, 0>(cw.v[1][n]), codes_to_bf16x2<KV, 1>(cw.v[1][n])};
       } else {
         vw = u32x4{cw.v[0][n].x, cw.v[0][n].y, cw.v[1][n].x, cw.v[1][n].y};
       }
@@ -348,27 +350,29 @@ void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
-template <bool kInt8, int D, int BS>
+template <KvKind KV, int D, int BS>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   // cascade: slots [0, prefix_parts) belong to the shared-prefix kernel
   const int parts = p.group_start != nullptr ? p.num_parts - p.prefix_parts : p.num_parts;
   const dim3 grid(static_cast<unsigned>(p.num_seqs * p.num_kv_heads), static_cast<unsigned>(parts));
-  hipLaunchKernelGGL((decode_mfma_kernel<kInt8, D, BS, kDecodeWaves>), grid,
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves>), grid,
                      dim3(kDecodeWaves * kWave), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool kInt8>
+template <KvKind KV>
 hipError_t launch_kv(const DecodeParams& p, hipStream_t s) {
   if (p.head_dim == 128)
-    return p.block_size == 16 ? launch_t<kInt8, 128, 16>(p, s) : launch_t<kInt8, 128, 32>(p, s);
-  return p.block_size == 16 ? launch_t<kInt8, 64, 16>(p, s) : launch_t<kInt8, 64, 32>(p, s);
+    return p.block_size == 16 ? launch_t<KV, 128, 16>(p, s) : launch_t<KV, 128, 32>(p, s);
+  return p.block_size == 16 ? launch_t<KV, 64, 16>(p, s) : launch_t<KV, 64, 32>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s) {
-  return kv == KvKind::I8 ? launch_kv<true>(p, s) : launch_kv<false>(p, s);
+  if (kv == KvKind::I8) return launch_kv<KvKind::I8>(p, s);
+  if (kv == KvKind::FP8) return launch_kv<KvKind::FP8>(p, s);
+  return launch_kv<KvKind::BF16>(p, s);
 }
 
 }  // namespace pkv

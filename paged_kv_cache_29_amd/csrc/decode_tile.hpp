@@ -43,10 +43,28 @@ __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t w, int half) {
   return __builtin_amdgcn_perm(fhi, flo, 0x07060302u);
 }
 
-// 8 int8 codes -> one bf16x8 operand.
-__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  return as_bf16x8(u32x4{i8pair_to_bf16x2(w0, 0), i8pair_to_bf16x2(w0, 1),
-                         i8pair_to_bf16x2(w1, 0), i8pair_to_bf16x2(w1, 1)});
+// Two FP8 (OCP E4M3) codes (bytes 2*HALF and 2*HALF+1 of w) -> packed bf16
+// pair.  Every E4M3 value (subnormals included) is a bf16 value, so the
+// hardware conversion with scale 1 is exact.
+template <int HALF>
+__device__ __forceinline__ uint32_t fp8pair_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HALF != 0));
+}
+
+// Byte codes of a cache of kind KV (I8 or FP8) -> exact bf16 values.
+template <KvKind KV, int HALF>
+__device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t w) {
+  if constexpr (KV == KvKind::FP8)
+    return fp8pair_to_bf16x2<HALF>(w);
+  else
+    return i8pair_to_bf16x2(w, HALF);
+}
+
+// 8 byte codes -> one bf16x8 operand.
+template <KvKind KV>
+__device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t w0, uint32_t w1) {
+  return as_bf16x8(u32x4{codes_to_bf16x2<KV, 0>(w0), codes_to_bf16x2<KV, 1>(w0),
+                         codes_to_bf16x2<KV, 0>(w1), codes_to_bf16x2<KV, 1>(w1)});
 }
 
 // Zero the bf16 elements (pairs packed in w) whose token is >= t_end.

@@ -123,6 +123,8 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
     kv = pkv::KvKind::BF16;
   } else if (q_dtype == PKV_BF16 && kv_dtype == PKV_I8) {
     kv = pkv::KvKind::I8;
+  } else if (q_dtype == PKV_BF16 && kv_dtype == PKV_FP8) {
+    kv = pkv::KvKind::FP8;
   } else {
     return fail(PKV_ERR_UNSUPPORTED, "(q_dtype, kv_dtype) = (%d, %d) is not supported",
                 static_cast<int>(q_dtype), static_cast<int>(kv_dtype));
@@ -143,11 +145,11 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   }
   if (step && num_seqs > 0 && (!k_new || !v_new))
     return fail(PKV_ERR_INVALID, "decode step needs k_new and v_new");
-  if (kv == pkv::KvKind::I8) {
+  if (kv == pkv::KvKind::I8 || kv == pkv::KvKind::FP8) {
     if (num_seqs > 0 && (!k_scale || !v_scale))
       return fail(PKV_ERR_INVALID, "int8 cache needs k_scale and v_scale");
   } else if (k_scale || v_scale) {
-    return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL unless kv_dtype is PKV_I8");
+    return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL unless kv_dtype is PKV_I8 or PKV_FP8");
   }
   const size_t need = check_workspace ? workspace_bytes_for(num_seqs, num_heads, head_dim, nparts) : 0;
   if (need > 0 && num_seqs > 0) {
@@ -303,6 +305,24 @@ pkv_status validate_write(const void* k, const void* v, const void* k_cache, con
   return PKV_OK;
 }
 
+pkv_status write_codes(const float* k, const float* v, void* k_cache, void* v_cache,
+                       float* k_scale, float* v_scale, const int64_t* slot_mapping,
+                       int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int64_t num_blocks, pkv::KvKind kind, void* stream,
+                       const char* what) {
+  pkv_status st = validate_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                                 head_dim, block_size, num_blocks);
+  if (st != PKV_OK) return st;
+  if (num_tokens > 0 && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID, "null k_scale or v_scale");
+  if (num_tokens == 0) return ok();
+  pkv::WriteParams p{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens,
+                     num_kv_heads, head_dim, block_size};
+  hipError_t e = pkv::launch_cache_write_codes(p, kind, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -330,18 +350,19 @@ pkv_status pkv_kv_cache_write_int8(const float* k, const float* v, int8_t* k_cac
                                    const int64_t* slot_mapping, int64_t num_tokens,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                    int64_t num_blocks, void* stream) {
-  pkv_status st = validate_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
-                                 head_dim, block_size, num_blocks);
-  if (st != PKV_OK) return st;
-  if (num_tokens > 0 && (!k_scale || !v_scale))
-    return fail(PKV_ERR_INVALID, "null k_scale or v_scale");
-  if (num_tokens == 0) return ok();
-  pkv::WriteParams p{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens,
-                     num_kv_heads, head_dim, block_size};
-  hipError_t e = pkv::launch_cache_write_int8(p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess)
-    return fail(PKV_ERR_HIP, "kv_cache_write_int8 launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens,
+                     num_kv_heads, head_dim, block_size, num_blocks, pkv::KvKind::I8, stream,
+                     "kv_cache_write_int8");
+}
+
+pkv_status pkv_kv_cache_write_fp8(const float* k, const float* v, uint8_t* k_cache,
+                                  uint8_t* v_cache, float* k_scale, float* v_scale,
+                                  const int64_t* slot_mapping, int64_t num_tokens,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int64_t num_blocks, void* stream) {
+  return write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens,
+                     num_kv_heads, head_dim, block_size, num_blocks, pkv::KvKind::FP8, stream,
+                     "kv_cache_write_fp8");
 }
 
 int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,

@@ -51,6 +51,18 @@ __device__ __forceinline__ int quantize_code(float x, float s) {
   return static_cast<int>(fminf(fmaxf(rintf(x / s), -127.f), 127.f));
 }
 
+// FP8 code of x for scale s: x / s (IEEE fp32 division) rounded to the
+// nearest OCP E4M3 value (bias 7, largest finite 448, ties to the even code)
+// by the hardware conversion.  x / s is clamped to +-448 first: it can pass
+// 448 only through the rounding of s, where 448 is the nearest code anyway,
+// and the conversion does not saturate.  s == 0 (all-zero or underflowed
+// row) gives code 0.  Used by every FP8 writer so their codes agree.
+__device__ __forceinline__ uint32_t fp8_code(float x, float s) {
+  if (!(s > 0.f)) return 0u;
+  const float r = fminf(fmaxf(x / s, -448.f), 448.f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(r, 0.f, 0, false)) & 0xffu;
+}
+
 // Combine a value across the four 16-lane groups of a wave (lanes l, l^16,
 // l^32, l^48), without lane-index registers: ds_swizzle swaps 16-lane
 // halves of each 32-lane group, v_permlane32_swap exchanges the two 32-lane

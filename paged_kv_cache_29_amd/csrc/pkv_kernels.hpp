@@ -67,7 +67,7 @@ struct WriteParams {
   int32_t block_size;
 };
 
-enum class KvKind { F32 = 0, BF16 = 1, I8 = 2 };
+enum class KvKind { F32 = 0, BF16 = 1, I8 = 2, FP8 = 3 };
 
 // Waves per workgroup of the partition kernels.
 constexpr int kDecodeWaves = 4;
@@ -103,7 +103,8 @@ hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, hipStream_t s);
 hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group_size, hipStream_t s);
 hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
-hipError_t launch_cache_write_int8(const WriteParams& p, hipStream_t s);
+// Quantising write of fp32 rows into an int8 or FP8 cache (kind I8 or FP8).
+hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s);
 hipError_t launch_tile_read(const void* pool, const int32_t* ids, int64_t ntiles, int grid,
                             uint32_t* sink, hipStream_t s);
 

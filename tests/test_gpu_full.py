@@ -1,4 +1,4 @@
-"""GPU: the five workloads at full size, in the launch configuration the
+"""GPU: the six workloads at full size, in the launch configuration the
 benchmark times (automatic partition length), checked on sampled outputs the
 oracle computes one by one, plus properties that hold at any size."""
 
@@ -14,7 +14,8 @@ from gpu_helpers import (DeviceWorkload, assert_parity, bf16_bits_of, oracle_cac
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cfg,bs", [(1, None), (2, None), (3, None), (4, 16), (4, 32), (5, None)])
+@pytest.mark.parametrize("cfg,bs", [(1, None), (2, None), (3, None), (4, 16), (4, 32), (5, None),
+                                    (6, None)])
 def test_full_size_sampled(cfg, bs):
     w = workloads.make_config(cfg, 0, block_size=bs)
     print(f"\n[full] config {cfg} bs={w.block_size} B={w.num_seqs} H={w.num_heads} "
@@ -37,11 +38,13 @@ def test_full_size_sampled(cfg, bs):
         if kind == "bf16":
             assert np.array_equal(bf16_bits_of(dw.k_cache[blk, :, r, :]), caches[0][blk, :, r, :])
             assert np.array_equal(bf16_bits_of(dw.v_cache[blk, :, :, r]), caches[1][blk, :, :, r])
-        elif kind == "i8":
+        elif kind in ("i8", "fp8"):
             for j in range(int(np.ceil(w.context_lens[b] / bs_))):
                 pb = int(w.block_tables[b][j])
-                assert np.array_equal(dw.k_cache[pb].cpu().numpy(), caches[0][pb])
-                assert np.array_equal(dw.v_cache[pb].cpu().numpy(), caches[1][pb])
+                assert np.array_equal(dw.k_cache[pb].view(torch.uint8).cpu().numpy(),
+                                      caches[0][pb].view(np.uint8))
+                assert np.array_equal(dw.v_cache[pb].view(torch.uint8).cpu().numpy(),
+                                      caches[1][pb].view(np.uint8))
                 rows = min(bs_, int(w.context_lens[b]) - j * bs_)
                 assert np.array_equal(dw.k_scale[pb, :, :rows].cpu().numpy(), caches[2][pb, :, :rows])
                 assert np.array_equal(dw.v_scale[pb, :, :rows].cpu().numpy(), caches[3][pb, :, :rows])
