@@ -299,6 +299,50 @@ def read_ceiling(torch, pkv, steps=20):
     return best
 
 
+def block_moves(torch, pkv, steps=10):
+    """Whole-block copies of a 70B-shaped pool (8 kv-heads x 16 tokens x 128
+    dims, bf16: 64 KB of K + V per block): copy-on-write copies inside HBM,
+    and swapping blocks out to pinned host memory and back."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    Hkv, bs, D, NB, NH, n = 8, 16, 128, 12288, 4096, 4096
+    kc = torch.empty((NB, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty((NB, Hkv, D, bs), dtype=torch.bfloat16, device=dev)
+    hk = torch.empty((NH, Hkv, bs, D), dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty((NH, Hkv, D, bs), dtype=torch.bfloat16).pin_memory()
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(NB)
+    cow = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int32)).to(dev)
+    out = torch.from_numpy(np.stack([perm[:n], rng.permutation(NH)[:n]], 1).astype(np.int32)).to(dev)
+    back = torch.from_numpy(np.stack([out[:, 1].cpu().numpy(), perm[2 * n:3 * n]], 1).astype(np.int32)).to(dev)
+    block_bytes = 2 * Hkv * bs * D * 2
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e-3
+
+    t_cow = timed(lambda: pkv.copy_blocks((kc, vc), (kc, vc), cow))
+    t_out = timed(lambda: pkv.copy_blocks((hk, hv), (kc, vc), out))
+    t_in = timed(lambda: pkv.copy_blocks((kc, vc), (hk, hv), back))
+    moved = n * block_bytes
+    res = {"blocks_per_call": n, "block_bytes": block_bytes,
+           "copy_on_write": {"us": t_cow * 1e6, "gbs_read_plus_write": 2 * moved / t_cow / 1e9,
+                             "frac_of_hbm_peak": 2 * moved / t_cow / 1e9 / HBM_PEAK_GBS},
+           "swap_out_gbs": moved / t_out / 1e9, "swap_in_gbs": moved / t_in / 1e9,
+           "note": "swap rates are over the host link (PCIe Gen5 x16, 64 GB/s per direction nominal)"}
+    del kc, vc, hk, hv
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, seconds):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -387,6 +431,8 @@ def main():
         torch.cuda.empty_cache()
     print("[bench] read ceiling probe ...", file=sys.stderr, flush=True)
     ceiling = read_ceiling(torch, pkv)
+    print("[bench] block moves ...", file=sys.stderr, flush=True)
+    moves = block_moves(torch, pkv)
     for r in results:
         r["roofline"]["frac_of_read_ceiling"] = r["roofline"]["achieved"] / ceiling["gbs"]
     head = results[0]
@@ -420,6 +466,7 @@ def main():
         "us_per_step_events": head["us_per_step_events"],
         "cascade": head.get("cascade"),
         "read_ceiling": ceiling,
+        "block_moves": moves,
         "kernel_source_sha": kernel_source_sha(),
         "secondary": [{k: v for k, v in r.items()} for r in results[1:]],
     }

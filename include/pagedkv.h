@@ -64,7 +64,8 @@ typedef enum {
   PKV_ERR_INVALID = 1,      /* bad pointer, size or scalar argument        */
   PKV_ERR_UNSUPPORTED = 2,  /* valid, but not a built variant              */
   PKV_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required  */
-  PKV_ERR_HIP = 4           /* the HIP runtime refused a launch            */
+  PKV_ERR_HIP = 4,          /* the HIP runtime refused a launch            */
+  PKV_ERR_NO_BLOCKS = 5     /* block manager: a pool is out of free blocks */
 } pkv_status;
 
 typedef enum {

@@ -7,6 +7,7 @@ block allocator (free list, refcounts, copy-on-write).
 """
 
 from ._lib import (  # noqa: F401
+    copy_blocks,
     kv_cache_write,
     kv_cache_write_int8,
     kv_cache_write_fp8,
@@ -23,5 +24,7 @@ from ._lib import (  # noqa: F401
     load as load_library,
     LIB_PATH,
 )
+
+from .block_manager import BlockManager  # noqa: F401,E402
 
 __version__ = "0.1.0"

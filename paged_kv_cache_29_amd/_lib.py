@@ -15,7 +15,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
-PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP = range(5)
+PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_NO_BLOCKS = range(6)
 PKV_F32, PKV_BF16, PKV_I8, PKV_FP8 = range(4)
 
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_I8,
@@ -52,6 +52,20 @@ SIGNATURES = {
                                               c_vp, c_size, c_vp]),
     "pkv_paged_attention_cascade_workspace_size": (c_size, [c_i32] * 11),
     "pkv_probe_tile_read": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_vp, c_vp]),
+    "pkv_bm_create": (c_i32, [c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(c_vp)]),
+    "pkv_bm_destroy": (None, [c_vp]),
+    "pkv_bm_num_free": (c_i64, [c_vp]),
+    "pkv_bm_num_free_host": (c_i64, [c_vp]),
+    "pkv_bm_new_sequence": (c_i32, [c_vp, ctypes.POINTER(c_i64)]),
+    "pkv_bm_fork": (c_i32, [c_vp, c_i64, ctypes.POINTER(c_i64)]),
+    "pkv_bm_free_sequence": (c_i32, [c_vp, c_i64]),
+    "pkv_bm_append": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_vp, c_i32, ctypes.POINTER(c_i32)]),
+    "pkv_bm_length": (c_i64, [c_vp, c_i64]),
+    "pkv_bm_block_table": (c_i32, [c_vp, c_i64, c_vp, c_i32, ctypes.POINTER(c_i32)]),
+    "pkv_bm_refcounts": (c_i32, [c_vp, c_vp]),
+    "pkv_bm_swap_out": (c_i32, [c_vp, c_i64, c_vp, c_i32, ctypes.POINTER(c_i32)]),
+    "pkv_bm_swap_in": (c_i32, [c_vp, c_i64, c_vp, c_i32, ctypes.POINTER(c_i32)]),
+    "pkv_copy_blocks": (c_i32, [c_vp] * 9 + [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
@@ -91,6 +105,9 @@ def _check(status, what):
         raise ValueError(text)
     if status == PKV_ERR_UNSUPPORTED:
         raise NotImplementedError(text)
+    if status == PKV_ERR_NO_BLOCKS:
+        from .blocks import OutOfBlocks
+        raise OutOfBlocks(text)
     raise PagedKVError(text)
 
 
@@ -364,3 +381,38 @@ def probe_tile_read(pool, tile_ids, sink, grid, check_ids=True):
     st = load().pkv_probe_tile_read(_ptr(pool), _ptr(tile_ids), tile_ids.numel(), int(grid),
                                     _ptr(sink), _stream(dev))
     _check(st, "probe_tile_read")
+
+
+def copy_blocks(dst, src, pairs):
+    """Copy whole blocks from pool ``src`` to pool ``dst``: block ``pairs[i,
+    0]`` of ``src`` to block ``pairs[i, 1]`` of ``dst`` (K tiles, V tiles and,
+    for int8 / FP8 pools, scale rows).  A pool is ``(k_cache, v_cache)`` or
+    ``(k_cache, v_cache, k_scale, v_scale)``, on the device or in pinned host
+    memory (swapping); ``pairs`` is an int32 ``[n, 2]`` tensor on the device.
+    Runs on the current stream of the device pool's GPU."""
+    dst, src = tuple(dst), tuple(src)
+    _need(len(dst) == len(src) and len(dst) in (2, 4), "pools are (k, v) or (k, v, k_scale, v_scale)")
+    dev = pairs.device
+    _need(dev.type == "cuda", "pairs must be on the device")
+    _need(pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2 and
+          pairs.is_contiguous(), "pairs must be contiguous int32 [n, 2]")
+    for pool, name in ((dst, "dst"), (src, "src")):
+        for t in pool:
+            _need(isinstance(t, torch.Tensor) and t.is_contiguous(), f"{name} pool tensors must be contiguous")
+            _need(t.device == dev or (t.device.type == "cpu" and t.is_pinned()),
+                  f"{name} pool tensors must be on {dev} or in pinned host memory")
+    kd = _DTYPES.get(dst[0].dtype)
+    _need(kd is not None and all(_DTYPES.get(t.dtype) == kd for t in (dst[1], src[0], src[1])),
+          "pool dtypes must match")
+    coded = kd in _CODED
+    _need(coded == (len(dst) == 4), "int8 / FP8 pools carry scales; fp32 / bf16 pools do not")
+    k = dst[0]
+    _need(k.dim() == 4, "k_cache must be [NB, Hkv, bs, D]")
+    _, Hkv, bs, D = k.shape
+    for pool in (dst, src):
+        _need(tuple(pool[0].shape[1:]) == (Hkv, bs, D) and tuple(pool[1].shape[1:]) == (Hkv, D, bs),
+              "pools must share Hkv, bs and D")
+    sc = (lambda pool: (_ptr(pool[2]), _ptr(pool[3]))) if coded else (lambda pool: (_ptr(None), _ptr(None)))
+    st = load().pkv_copy_blocks(_ptr(dst[0]), _ptr(dst[1]), *sc(dst), _ptr(src[0]), _ptr(src[1]),
+                                *sc(src), _ptr(pairs), pairs.shape[0], Hkv, D, bs, kd, _stream(dev))
+    _check(st, "copy_blocks")

@@ -8,12 +8,16 @@
 #include <string>
 
 #include "../../include/pagedkv.h"
+#include "../../include/pagedkv_blocks.h"
 #include "../../include/pagedkv_probe.h"
+#include "pkv_host.hpp"
 #include "pkv_kernels.hpp"
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
+
+namespace pkv {
 
 pkv_status fail(pkv_status st, const char* fmt, ...) {
   char buf[512];
@@ -29,6 +33,13 @@ pkv_status ok() {
   g_last_error.clear();
   return PKV_OK;
 }
+
+}  // namespace pkv
+
+namespace {
+
+using pkv::fail;
+using pkv::ok;
 
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32; }
@@ -537,6 +548,69 @@ pkv_status pkv_paged_attention_decode_cascade(
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "partition kernel launch failed: %s", hipGetErrorString(e));
   e = pkv::launch_decode_reduce(p, st.out_bf16, strm);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pkv_status pkv_copy_blocks(void* dst_k, void* dst_v, float* dst_k_scale, float* dst_v_scale,
+                           const void* src_k, const void* src_v, const float* src_k_scale,
+                           const float* src_v_scale, const int32_t* pairs, int32_t n,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           pkv_dtype dtype, void* stream) {
+  if (n < 0) return fail(PKV_ERR_INVALID, "copy_blocks: n must be >= 0");
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0)
+    return fail(PKV_ERR_INVALID, "copy_blocks: sizes must be positive");
+  if (!head_dim_ok(head_dim)) return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: head_dim %d not in {64, 128}", head_dim);
+  if (!block_size_ok(block_size))
+    return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block_size %d not in {16, 32}", block_size);
+  int64_t elem;
+  const bool coded = dtype == PKV_I8 || dtype == PKV_FP8;
+  if (dtype == PKV_F32) elem = 4;
+  else if (dtype == PKV_BF16) elem = 2;
+  else if (coded) elem = 1;
+  else return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: unknown dtype %d", static_cast<int>(dtype));
+  if (n > 65535) return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: at most 65535 pairs per call");
+  if (n == 0) return ok();
+  if (!dst_k || !dst_v || !src_k || !src_v || !pairs)
+    return fail(PKV_ERR_INVALID, "copy_blocks: null pointer among the pools and pairs");
+  if (coded && (!dst_k_scale || !dst_v_scale || !src_k_scale || !src_v_scale))
+    return fail(PKV_ERR_INVALID, "copy_blocks: int8 / FP8 pools need all four scale pointers");
+  if (!coded && (dst_k_scale || dst_v_scale || src_k_scale || src_v_scale))
+    return fail(PKV_ERR_INVALID, "copy_blocks: scale pointers must be NULL for fp32 / bf16 pools");
+  // every pool must be device memory or host memory the device can address
+  // (pinned); host memory is passed on as its device-side address
+  const void* in[8] = {src_k, src_v, src_k_scale, src_v_scale, dst_k, dst_v, dst_k_scale, dst_v_scale};
+  const void* dv[8] = {};
+  for (int i = 0; i < 8; ++i) {
+    if (!in[i]) continue;
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, in[i]) != hipSuccess) {
+      (void)hipGetLastError();  // leave no error behind for later launches
+      return fail(PKV_ERR_INVALID, "copy_blocks: pool %d is neither device memory nor pinned host memory", i);
+    }
+    if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+      dv[i] = in[i];
+    } else if (a.type == hipMemoryTypeHost) {
+      void* d = nullptr;
+      if (hipHostGetDevicePointer(&d, const_cast<void*>(in[i]), 0) != hipSuccess || !d) {
+        (void)hipGetLastError();
+        return fail(PKV_ERR_INVALID, "copy_blocks: host pool %d has no device address", i);
+      }
+      dv[i] = d;
+    } else {
+      return fail(PKV_ERR_INVALID, "copy_blocks: pool %d is not addressable by the device", i);
+    }
+  }
+  pkv::CopyParams p{};
+  for (int i = 0; i < 4; ++i) {
+    p.src[i] = dv[i];
+    p.dst[i] = const_cast<void*>(dv[4 + i]);
+  }
+  p.pairs = pairs;
+  p.num_pairs = n;
+  p.tile_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem;
+  p.scale_bytes = coded ? static_cast<int64_t>(num_kv_heads) * block_size * 4 : 0;
+  const hipError_t e = pkv::launch_copy_blocks(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "copy_blocks launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -69,6 +69,18 @@ struct WriteParams {
 
 enum class KvKind { F32 = 0, BF16 = 1, I8 = 2, FP8 = 3 };
 
+// Whole-block copies between two pools: parts 0..3 are the K tiles, the V
+// tiles, the K scale rows and the V scale rows of a block (tile_bytes,
+// tile_bytes, scale_bytes, scale_bytes each; scale_bytes 0 without scales).
+struct CopyParams {
+  const void* src[4];
+  void* dst[4];
+  const int32_t* pairs;  // [num_pairs][2]: source block, destination block
+  int32_t num_pairs;
+  int64_t tile_bytes;
+  int64_t scale_bytes;
+};
+
 // Waves per workgroup of the partition kernels.
 constexpr int kDecodeWaves = 4;
 // Query-column tiles (16 queries each) per wave of the shared-prefix kernel,
@@ -105,6 +117,7 @@ hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group
 hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
 // Quantising write of fp32 rows into an int8 or FP8 cache (kind I8 or FP8).
 hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t s);
 hipError_t launch_tile_read(const void* pool, const int32_t* ids, int64_t ntiles, int grid,
                             uint32_t* sink, hipStream_t s);
 

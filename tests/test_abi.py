@@ -248,3 +248,34 @@ def test_cascade_workspace(lib):
 def test_cascade_empty_batch_is_noop(lib):
     st, msg = _cascade(lib, num_seqs=0, num_groups=0, max_group_size=0, max_shared_blocks=0)
     assert st == OK, msg
+
+
+def _copy(lib, **over):
+    a = dict(dst_k=_fake(1), dst_v=_fake(2), dst_ks=None, dst_vs=None, src_k=_fake(3), src_v=_fake(4),
+             src_ks=None, src_vs=None, pairs=_fake(5), n=3, num_kv_heads=2, head_dim=64, block_size=16,
+             dtype=BF16, stream=None)
+    a.update(over)
+    st = lib.pkv_copy_blocks(*a.values())
+    return st, lib.pkv_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,frag", [
+    (dict(n=-1), INVALID, "n must be"),
+    (dict(dtype=7), UNSUPPORTED, "dtype"),
+    (dict(head_dim=96), UNSUPPORTED, "head_dim"),
+    (dict(block_size=8), UNSUPPORTED, "block_size"),
+    (dict(pairs=None), INVALID, "null pointer"),
+    (dict(src_v=None), INVALID, "null pointer"),
+    (dict(dtype=I8), INVALID, "scale"),
+    (dict(dst_ks=_fake(6)), INVALID, "NULL"),
+    (dict(n=70000), UNSUPPORTED, "65535"),
+])
+def test_copy_blocks_rejects(lib, over, code, frag):
+    st, msg = _copy(lib, **over)
+    assert st == code, msg
+    assert frag in msg
+
+
+def test_copy_blocks_zero_pairs_is_noop(lib):
+    st, msg = _copy(lib, n=0, pairs=None)
+    assert st == OK, msg
