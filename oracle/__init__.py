@@ -22,7 +22,9 @@ Sources (web pages, cited by title and section):
   (chenk.top), sections "Two phases with very different characteristics",
   "Paged attention", "Block manager: how paging works",
   "INT8 weight-only quantization", "KV-cache quantization" (int8 and FP8
-  caches with per-token scales) and "SGLang and RadixAttention".
+  caches with per-token scales), "SGLang and RadixAttention", "Orca's
+  iteration-level scheduling" (chunked prefill) and "Speculative decoding"
+  (k + 1 positions scored in one pass).
 * [LAYERS] the four-layer inference-optimization article (gsyq.cn/news/366077),
   section 2.1 (KV-cache size formula and its 7B worked number), 2.2
   (PagedAttention, block size 16/32) and 2.3 (KV-cache quantization with
@@ -43,6 +45,7 @@ from .attention import (
     gather_kv,
     attend_one,
     decode_attention,
+    multi_query_attention,
 )
 from .cache import cache_write, quantize_int8, cache_write_int8
 from .fp8 import e4m3_decode, e4m3_encode, quantize_fp8, cache_write_fp8
@@ -57,6 +60,7 @@ __all__ = [
     "gather_kv",
     "attend_one",
     "decode_attention",
+    "multi_query_attention",
     "cache_write",
     "quantize_int8",
     "cache_write_int8",

@@ -178,3 +178,57 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
             q_vec = widen(q[b, h, :D], q_dtype)
             out[b, h] = attend_one(q_vec, K, V, scale)
     return out
+
+
+def multi_query_attention(q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+                          num_heads, num_kv_heads, head_dim, block_size, kv_dtype, q_dtype,
+                          k_scale=None, v_scale=None, samples=None):
+    """fp64 causal attention of several new query tokens per sequence.
+
+    A verification step of speculative decoding scores k + 1 proposed
+    positions in one pass, and a prefill chunk scores a run of new tokens,
+    instead of one token per step ([ENG5] "Speculative decoding", "Orca's
+    iteration-level scheduling": chunked prefill).  Reading taken: sequence
+    ``b`` has ``n_b = query_start[b+1] - query_start[b]`` new tokens, the last
+    ``n_b`` of its ``L_b = context_lens[b]`` cached tokens (their K/V already
+    written); its query row ``query_start[b] + i`` sits at position
+    ``p = L_b - n_b + i`` and attends to tokens ``0 .. p`` (causal), through
+    the block table exactly as decode does.
+
+    Shapes: ``q[T, H, D]`` with ``T = query_start[B]``; caches, tables and
+    scales as for ``decode_attention``.  Returns ``out[T, H, D]`` in fp64;
+    with ``samples`` (``(row, h)`` pairs) only those rows are computed, the
+    others are NaN.
+    """
+    if kv_dtype not in KV_DTYPES:
+        raise ValueError(kv_dtype)
+    H, Hkv, D = int(num_heads), int(num_kv_heads), int(head_dim)
+    if H % Hkv != 0:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    qs = [int(x) for x in query_start]
+    T = qs[-1]
+    if samples is None:
+        out = np.zeros((T, H, D), dtype=np.float64)
+        wanted = {(r, h) for r in range(T) for h in range(H)}
+    else:
+        out = np.full((T, H, D), np.nan, dtype=np.float64)
+        wanted = {(int(r), int(h)) for r, h in samples}
+    rows_of = {}
+    for b in range(len(qs) - 1):
+        for r in range(qs[b], qs[b + 1]):
+            rows_of[r] = b
+    by_group = {}
+    for r, h in wanted:
+        by_group.setdefault((rows_of[r], kv_head_of(h, H, Hkv)), []).append((r, h))
+    for (b, g), pairs in sorted(by_group.items()):
+        L = int(context_lens[b])
+        n = qs[b + 1] - qs[b]
+        if n > L:
+            raise ValueError("more new tokens than the context holds")
+        K, V = gather_kv(k_cache, v_cache, block_tables[b], L, block_size, g, kv_dtype,
+                         k_scale, v_scale)
+        for r, h in pairs:
+            pos = L - n + (r - qs[b])
+            q_vec = widen(q[r, h, :D], q_dtype)
+            out[r, h] = attend_one(q_vec, K[:pos + 1], V[:pos + 1], scale)
+    return out

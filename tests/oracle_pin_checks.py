@@ -596,6 +596,96 @@ def check_brute_force_fp8():
             np.testing.assert_allclose(out[b, h], ref, rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------- multi-query (causal)
+def _mq_case(seed=31, kv="bf16"):
+    w = workloads.make_custom(seed, [40, 17, 5, 70], 8, 2, 16, 16, kv_dtype="bf16" if kv == "bf16" else "f32")
+    n = [5, 1, 5, 33]                       # new tokens per sequence (the last n of each context)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((int(qs[-1]), w.num_heads, w.head_dim)).astype(np.float32)
+    if kv == "bf16":
+        q = workloads.bf16_bits(q)
+    kc, vc = ocache.cache_write(w.k_new, w.v_new, w.k_cache, w.v_cache, w.slot_new, w.block_size)
+    return w, q, qs, kc, vc
+
+
+def check_mq_single_token_is_decode():
+    w, _, _, kc, vc = _mq_case()
+    qs = np.arange(w.num_seqs + 1, dtype=np.int32)
+    q = workloads.bf16_bits(np.random.default_rng(2).standard_normal((w.num_seqs, w.num_heads, w.head_dim)).astype(np.float32))
+    a = oracle.multi_query_attention(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, w.num_heads,
+                                     w.num_kv_heads, w.head_dim, w.block_size, "bf16", "bf16")
+    b = oracle.decode_attention(q, kc, vc, w.block_tables, w.context_lens, w.scale, w.num_heads,
+                                w.num_kv_heads, w.head_dim, w.block_size, "bf16", "bf16")
+    assert np.array_equal(a, b)
+
+
+def check_mq_rows_are_decodes_of_truncated_contexts():
+    w, q, qs, kc, vc = _mq_case()
+    out = oracle.multi_query_attention(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, w.num_heads,
+                                       w.num_kv_heads, w.head_dim, w.block_size, "bf16", "bf16")
+    for b in range(w.num_seqs):
+        n = int(qs[b + 1] - qs[b])
+        L = int(w.context_lens[b])
+        for i in range(n):
+            r = int(qs[b]) + i
+            lens = w.context_lens.copy()
+            lens[b] = L - n + i + 1             # the context as it stood when token i was the newest
+            ref = oracle.decode_attention(q[r:r + 1].repeat(w.num_seqs, 0), kc, vc, w.block_tables, lens,
+                                          w.scale, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                                          "bf16", "bf16", samples=[(b, h) for h in range(w.num_heads)])
+            np.testing.assert_allclose(out[r], ref[b], rtol=1e-13, atol=1e-15)
+
+
+def check_mq_sdpa_bottom_right_causal():
+    """Contiguous K/V through an identity table equals SDPA with a causal
+    mask aligned to the end of the context (the new tokens are the last n)."""
+    import torch
+    rng = np.random.default_rng(33)
+    L, n, H, D, bs = 45, 7, 2, 16, 16
+    nb = (L + bs - 1) // bs
+    kc = rng.standard_normal((nb, 1, bs, D)).astype(np.float32)
+    vc = rng.standard_normal((nb, 1, D, bs)).astype(np.float32)
+    q = rng.standard_normal((n, H, D)).astype(np.float32)
+    out = oracle.multi_query_attention(q, kc, vc, np.arange(nb, dtype=np.int32)[None], np.array([L], np.int32),
+                                       np.array([0, n], np.int32), 0.3, H, 1, D, bs, "f32", "f32")
+    K = torch.from_numpy(kc[:, 0].reshape(-1, D)[:L].astype(np.float64))
+    V = torch.from_numpy(np.transpose(vc[:, 0], (0, 2, 1)).reshape(-1, D)[:L].astype(np.float64))
+    mask = torch.ones(n, L, dtype=torch.bool).tril(diagonal=L - n)
+    for h in range(H):
+        Q = torch.from_numpy(q[:, h].astype(np.float64))
+        ref = torch.nn.functional.scaled_dot_product_attention(Q[None, None], K[None, None], V[None, None],
+                                                               attn_mask=mask, scale=0.3)[0, 0]
+        np.testing.assert_allclose(out[:, h], ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def check_mq_brute_force_int8():
+    rng = np.random.default_rng(34)
+    NB, Hkv, bs, D, H = 5, 1, 16, 8, 2
+    kc = rng.integers(-127, 128, size=(NB, Hkv, bs, D)).astype(np.int8)
+    vc = rng.integers(-127, 128, size=(NB, Hkv, D, bs)).astype(np.int8)
+    ks = rng.uniform(0.001, 0.02, size=(NB, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0.001, 0.02, size=(NB, Hkv, bs)).astype(np.float32)
+    tables = np.array([[3, 0, 4]], dtype=np.int32)
+    L, n = 35, 4
+    q = rng.standard_normal((n, H, D)).astype(np.float32)
+    out = oracle.multi_query_attention(q, kc, vc, tables, np.array([L], np.int32), np.array([0, n], np.int32),
+                                       0.5, H, Hkv, D, bs, "i8", "f32", k_scale=ks, v_scale=vs)
+    for i in range(n):
+        pos = L - n + i
+        for h in range(H):
+            sc, rows = [], []
+            for t in range(pos + 1):
+                blk, r = int(tables[0][t // bs]), t % bs
+                kr = [float(kc[blk, 0, r, d]) * float(ks[blk, 0, r]) for d in range(D)]
+                sc.append(0.5 * sum(float(q[i, h, d]) * kr[d] for d in range(D)))
+                rows.append([float(vc[blk, 0, d, r]) * float(vs[blk, 0, r]) for d in range(D)])
+            m = max(sc)
+            ps = [math.exp(x - m) for x in sc]
+            ref = [sum(p * row[d] for p, row in zip(ps, rows)) / sum(ps) for d in range(D)]
+            np.testing.assert_allclose(out[i, h], ref, rtol=1e-12, atol=1e-14)
+
+
 ALL_CHECKS = [
     check_worked_example_blocks,
     check_worked_example_gather,
@@ -624,4 +714,8 @@ ALL_CHECKS = [
     check_fp8_quantizer_closed_forms,
     check_fp8_write_brute,
     check_brute_force_fp8,
+    check_mq_single_token_is_decode,
+    check_mq_rows_are_decodes_of_truncated_contexts,
+    check_mq_sdpa_bottom_right_causal,
+    check_mq_brute_force_int8,
 ]

@@ -158,6 +158,25 @@ def _gather_fp8_no_v_scale(k_cache, v_cache, block_table, context_len, block_siz
                         kv_dtype, k_scale, v_scale)
 
 
+def _mq_variant(shift=0, top_left=False, causal=True):
+    def mq(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, num_heads, num_kv_heads,
+           head_dim, block_size, kv_dtype, q_dtype, k_scale=None, v_scale=None, samples=None):
+        H, Hkv, D = int(num_heads), int(num_kv_heads), int(head_dim)
+        qs = [int(x) for x in query_start]
+        out = np.zeros((qs[-1], H, D))
+        for b in range(len(qs) - 1):
+            L, n = int(context_lens[b]), qs[b + 1] - qs[b]
+            for h in range(H):
+                K, V = oatt.gather_kv(k_cache, v_cache, block_tables[b], L, block_size, oatt.kv_head_of(h, H, Hkv),
+                                      kv_dtype, k_scale, v_scale)
+                for i in range(n):
+                    pos = (i if top_left else L - n + i) + shift
+                    stop = L if not causal else max(1, min(L, pos + 1))
+                    out[qs[b] + i, h] = oatt.attend_one(oatt.widen(q[qs[b] + i, h], q_dtype), K[:stop], V[:stop], scale)
+        return out
+    return mq
+
+
 _orig_e4m3_encode = ofp8.e4m3_encode
 _orig_e4m3_decode = ofp8.e4m3_decode
 _orig_gather = oatt.gather_kv
@@ -187,6 +206,9 @@ MUTATIONS = {
     "fp8_truncate": [(ofp8, "e4m3_encode", _fp8_encode_truncate)],
     "fp8_scale_over_240": [(ofp8, "quantize_fp8", _fp8_quant_over_240)],
     "fp8_v_scale_dropped": [(oatt, "gather_kv", _gather_fp8_no_v_scale)],
+    "mq_excludes_own_token": [(oatt, "multi_query_attention", _mq_variant(shift=-1))],
+    "mq_top_left_causal": [(oatt, "multi_query_attention", _mq_variant(top_left=True))],
+    "mq_not_causal": [(oatt, "multi_query_attention", _mq_variant(causal=False))],
 }
 
 
