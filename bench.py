@@ -216,11 +216,39 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
                        "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(w.name),
                        "kernel": "decode_mfma_kernel (fused step: append + attend)"
                        if w.kv_dtype != "f32" else "decode_f32_kernel (fused step)"}
+    if w.name == "gqa70b_bf16":
+        res["speculative_verify"] = run_multi_query(w, args, torch, pkv, loop_time, q, kc, vc, bt, cl,
+                                                    nbytes, ms_per_step)
     if w.meta.get("prefix"):
         res["cascade"] = run_cascade(w, args, torch, pkv, loop_time, write, out, q, kc, vc, bt, cl,
                                      ks, vs, nbytes, uniq, ms_per_step)
     res["_w"] = w
     return res
+
+
+def run_multi_query(w, args, torch, pkv, loop_time, q, kc, vc, bt, cl, nbytes, ms_decode, n=5):
+    """A speculative-decoding verification on the same contexts: the last
+    n = k + 1 tokens of every sequence scored in one call (causal), timed
+    like the decode step; the pages' point is that when decode is
+    memory-bound this costs about as much as one decode step."""
+    import numpy as np
+    dev = q.device
+    B = w.num_seqs
+    qs = torch.from_numpy((np.arange(B + 1) * n).astype(np.int32)).to(dev)
+    qm = q.repeat_interleave(n, dim=0).contiguous()
+    om = torch.empty_like(qm)
+    need = pkv.multi_query_workspace_size(B, B * n, n, w.num_heads, w.num_kv_heads, w.head_dim,
+                                          w.block_size, w.block_tables.shape[1], 0)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def verify():
+        pkv.paged_attention_multi_query(om, qm, kc, vc, bt, cl, qs, w.scale, w.num_heads,
+                                        w.num_kv_heads, w.head_dim, w.block_size, n, workspace=ws)
+
+    us = loop_time(verify)
+    return {"tokens_per_seq": n, "us_per_call": us, "kv_gbs": nbytes / (us * 1e-6) / 1e9,
+            "cost_vs_one_token_step": us / (ms_decode * 1e3),
+            "query_tokens_per_s": B * n / (us * 1e-6)}
 
 
 def run_cascade(w, args, torch, pkv, loop_time, write, out, q, kc, vc, bt, cl, ks, vs, nbytes,
@@ -465,6 +493,7 @@ def main():
         "roofline": head["roofline"],
         "us_per_step_events": head["us_per_step_events"],
         "cascade": head.get("cascade"),
+        "speculative_verify": head.get("speculative_verify"),
         "read_ceiling": ceiling,
         "block_moves": moves,
         "kernel_source_sha": kernel_source_sha(),

@@ -21,7 +21,9 @@
  *            "KV-cache quantization" (per-token-per-head scales computed
  *            online), "INT8 weight-only quantization" (q = round(x / s)),
  *            "SGLang and RadixAttention" (the longest shared prefix is
- *            reused, only the rest is computed per request).
+ *            reused, only the rest is computed per request), "Orca's
+ *            iteration-level scheduling" (chunked prefill) and
+ *            "Speculative decoding" (k + 1 positions in one pass).
  *   [LAYERS] four-layer inference-optimization article
  *            (gsyq.cn/news/366077), 2.2 (block size 16 or 32) and 2.3
  *            (per-token scales; K and V quantized separately).
@@ -294,6 +296,46 @@ size_t pkv_paged_attention_cascade_workspace_size(
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
     int32_t block_size, int32_t max_blocks_per_seq, int32_t num_groups, int32_t max_group_size,
     int32_t max_shared_blocks, int32_t partition_tokens, int32_t prefix_partition_tokens);
+
+/*
+ * Causal multi-query attention over the paged cache: several new tokens per
+ * sequence in one call, as a speculative-decoding verification (k + 1
+ * proposed positions scored in one pass, [ENG5] "Speculative decoding") or
+ * a prefill chunk interleaved with decode ([ENG5] "Orca's iteration-level
+ * scheduling", chunked prefill) needs.
+ *   Sequence b's new tokens are query rows query_start[b] ..
+ *   query_start[b+1]-1 of q and out ([T][H][D], T = num_query_tokens); with
+ *   n_b of them and L = context_lens[b], they are the last n_b positions of
+ *   its context (their K/V already written), and row query_start[b] + i
+ *   attends to tokens 0 .. L - n_b + i:
+ *     out[r][h][:] = softmax(scale * K_b[0..pos] q[r][h]) V_b[0..pos].
+ *   One query per sequence is exactly pkv_paged_attention_decode.
+ * query_start: device int32 [num_seqs + 1], query_start[0] = 0,
+ * non-decreasing, query_start[num_seqs] = num_query_tokens.
+ * max_queries_per_seq: host bound on every n_b, in [1, num_query_tokens].
+ * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8) with decode's sizes.
+ * partition_tokens: 0 for the automatic choice, else as for decode.
+ * Workspace: pkv_paged_attention_multi_query_workspace_size(...) bytes,
+ * 256-byte aligned, whenever num_query_tokens > 0.  Two launches (partials
+ * of every context partition, then the combine).
+ * Not checked (device data): query_start as stated; n_b <= context_lens[b];
+ * n_b <= max_queries_per_seq.
+ */
+pkv_status pkv_paged_attention_multi_query(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* query_start, float scale, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int64_t num_blocks, int32_t num_query_tokens, int32_t max_queries_per_seq, pkv_dtype q_dtype,
+    pkv_dtype kv_dtype, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/* Workspace bytes of pkv_paged_attention_multi_query (0 for invalid sizes
+ * or no query tokens). */
+size_t pkv_paged_attention_multi_query_workspace_size(
+    int32_t num_seqs, int32_t num_query_tokens, int32_t max_queries_per_seq, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t partition_tokens);
 
 /* Text of the last failure on this thread ("" after a successful call).
  * The pointer stays valid until the next call on the same thread. */

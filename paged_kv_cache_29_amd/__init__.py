@@ -14,6 +14,8 @@ from ._lib import (  # noqa: F401
     cascade_workspace_size,
     paged_attention_decode,
     paged_attention_decode_cascade,
+    paged_attention_multi_query,
+    multi_query_workspace_size,
     paged_attention_decode_partitions,
     paged_attention_decode_reduce,
     paged_attention_decode_step,

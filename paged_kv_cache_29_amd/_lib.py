@@ -51,6 +51,9 @@ SIGNATURES = {
                                            + [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                               c_vp, c_size, c_vp]),
     "pkv_paged_attention_cascade_workspace_size": (c_size, [c_i32] * 11),
+    "pkv_paged_attention_multi_query": (c_i32, _DECODE_ARGS[:8] + [c_vp] + _DECODE_ARGS[8:16]
+                                        + [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp]),
+    "pkv_paged_attention_multi_query_workspace_size": (c_size, [c_i32] * 9),
     "pkv_probe_tile_read": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_vp, c_vp]),
     "pkv_bm_create": (c_i32, [c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(c_vp)]),
     "pkv_bm_destroy": (None, [c_vp]),
@@ -304,6 +307,52 @@ def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, conte
         int(max_group_size), int(max_shared_blocks), args[16], args[17], args[18],
         int(prefix_partition_tokens), _ptr(workspace), ws_bytes, args[21])
     _check(st, "paged_attention_decode_cascade")
+
+
+def multi_query_workspace_size(num_seqs, num_query_tokens, max_queries_per_seq, num_heads,
+                               num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                               partition_tokens=0):
+    return int(load().pkv_paged_attention_multi_query_workspace_size(
+        num_seqs, num_query_tokens, max_queries_per_seq, num_heads, num_kv_heads, head_dim,
+        block_size, max_blocks_per_seq, partition_tokens))
+
+
+def paged_attention_multi_query(out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                                scale, num_heads, num_kv_heads, head_dim, block_size,
+                                max_queries_per_seq, k_scale=None, v_scale=None,
+                                partition_tokens=0, workspace=None):
+    """Causal attention of each sequence's new tokens (rows ``query_start[b]
+    .. query_start[b+1]-1`` of ``q`` / ``out``, ``[T, H, D]``), the last of its
+    context, over its paged context; ``query_start`` is a device int32
+    ``[B + 1]`` tensor and ``max_queries_per_seq`` a host bound on the
+    per-sequence counts."""
+    dev = q.device
+    for n, t in (("out", out), ("q", q), ("block_tables", block_tables),
+                 ("context_lens", context_lens), ("query_start", query_start)):
+        _dense_on(t, dev, n)
+    B = context_lens.shape[0]
+    _need(query_start.dtype == torch.int32 and tuple(query_start.shape) == (B + 1,),
+          "query_start must be int32 [B + 1]")
+    _need(q.dim() == 3 and tuple(q.shape[1:]) == (num_heads, head_dim), "q must be [T, H, D]")
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    T = q.shape[0]
+    # decode's checks on the caches and tables, with a stand-in [B, H, D] query
+    stand = torch.empty((B, num_heads, head_dim), dtype=q.dtype, device=dev) if B else q[:0]
+    args = list(_marshal_decode(stand, stand, k_cache, v_cache, block_tables, context_lens, scale,
+                                num_heads, num_kv_heads, head_dim, block_size, k_scale, v_scale,
+                                partition_tokens, workspace=_NO_WORKSPACE))
+    MB = block_tables.shape[1]
+    need = multi_query_workspace_size(B, T, max_queries_per_seq, num_heads, num_kv_heads, head_dim,
+                                      block_size, MB, partition_tokens)
+    if workspace is None:
+        workspace = _workspace(dev, need) if need else None
+    else:
+        _dense_on(workspace, dev, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().pkv_paged_attention_multi_query(
+        _ptr(out), _ptr(q), *args[2:8], _ptr(query_start), *args[8:16], T, int(max_queries_per_seq),
+        args[16], args[17], int(partition_tokens), _ptr(workspace), ws_bytes, args[21])
+    _check(st, "paged_attention_multi_query")
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,

@@ -55,8 +55,10 @@ struct PrefixLds {
   static constexpr int UNITS = PIECE / (16 * kWave);  // 16-byte loads per lane per piece
 };
 
-// KV: BF16, or byte codes with per-token scales (I8, FP8).
-template <KvKind KV, int D, int BS, int NT>
+// KV: BF16, or byte codes with per-token scales (I8, FP8).  kMQ: the
+// multi-query form (one sequence's new tokens x heads as the columns, its
+// whole context partitioned, each column masked causally at its position).
+template <KvKind KV, int D, int BS, int NT, bool kMQ>
 __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void cascade_prefix_kernel(DecodeParams p) {
   constexpr bool kInt8 = KV != KvKind::BF16;  // byte codes (int8 or FP8) with scales
@@ -86,14 +88,23 @@ void cascade_prefix_kernel(DecodeParams p) {
   const int qwg = blockIdx.y * (W * QW);
   const int part = blockIdx.z;
 
-  const int gs = p.group_start[grp];
-  const int nq = (p.group_start[grp + 1] - gs) * G;
+  // cascade: group grp's members x heads over its shared span; multi-query:
+  // sequence grp's new tokens x heads over its whole context
+  const int gs = kMQ ? grp : p.group_start[grp];             // whose block table
+  const int qrow0 = kMQ ? p.query_start[grp] : 0;             // first query row (multi-query)
+  const int nnew = kMQ ? p.query_start[grp + 1] - qrow0 : 0;
+  const int nq = kMQ ? nnew * G : (p.group_start[grp + 1] - gs) * G;
   if (qwg >= nq) return;  // uniform across the workgroup
-  const int S = group_shared_tokens(p, grp);
-  const int t_begin = part * p.prefix_part_tokens;
+  const int S = kMQ ? p.context_lens[grp] : group_shared_tokens(p, grp);
+  const int PTp = kMQ ? p.part_tokens : p.prefix_part_tokens;
+  const int t_begin = part * PTp;
   if (t_begin >= S) return;  // uniform across the workgroup
-  const int t_end = min(S, t_begin + p.prefix_part_tokens);  // block-aligned
+  const int t_end = min(S, t_begin + PTp);  // block-aligned in cascade mode
   const int q0 = qwg + wave * QW;  // this wave's first query
+  // multi-query: the last token column r may see (its position), per tile
+  int lim[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) lim[t] = S - nnew + (q0 + 16 * t + c) / G;
 
   // Q^T operands: tile t, lane (c, g), MFMA j: 8 dims from q_dim(j)
   auto q_dim = [&](int j) { return kInt8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g); };
@@ -101,8 +112,8 @@ void cascade_prefix_kernel(DecodeParams p) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int r = q0 + 16 * t + c;
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                           (static_cast<size_t>(gs + r / G) * H + kvh * G + r % G) * D;
+    const size_t qr = kMQ ? static_cast<size_t>(qrow0 + r / G) : static_cast<size_t>(gs + r / G);
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (qr * H + kvh * G + r % G) * D;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -111,8 +122,9 @@ void cascade_prefix_kernel(DecodeParams p) {
     }
   }
 
-  // the group's shared block ids (its first sequence's table), once per workgroup
-  const int nblk = (t_end - t_begin) / BS;
+  // block ids of the span (the group's first sequence's table, or the
+  // sequence's own), once per workgroup
+  const int nblk = (t_end - t_begin + BS - 1) / BS;
   {
     const int32_t* bt = p.block_tables + static_cast<size_t>(gs) * p.max_blocks_per_seq + t_begin / BS;
     for (int i = threadIdx.x; i < nblk; i += W * kWave) blk_ids[i] = bt[i];  // nblk <= kMaxPartBlocks
@@ -249,6 +261,9 @@ void cascade_prefix_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      // every column of the tile is padding (uniform): skip its arithmetic
+      // (not for int8 at D = 128, whose registers are too tight for the branch)
+      if (!(KV == KvKind::I8 && D == 128) && q0 + 16 * t >= nq) continue;
       f32x4 s[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -290,6 +305,13 @@ void cascade_prefix_kernel(DecodeParams p) {
           }
         }
       }
+      if constexpr (kMQ) {  // causal: column c sees tokens up to lim[t]
+        if (t0 + 31 > lim[t]) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (t0 + 16 * (e >> 2) + 4 * g + (e & 3) > lim[t]) sc[e] = -INFINITY;
+        }
+      }
       float mx = sc[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
@@ -307,6 +329,10 @@ void cascade_prefix_kernel(DecodeParams p) {
         float pr[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(sc[e] - m_run[t]);
+        if constexpr (kMQ) {  // a column can be masked throughout (m_run = -inf): exact zeros
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pr[e] = (sc[e] == -INFINITY) ? 0.f : pr[e];
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) l_run[t] += pr[e];
         if constexpr (kInt8) {
@@ -355,7 +381,8 @@ void cascade_prefix_kernel(DecodeParams p) {
     const float Lsum = groups_sum(l_run[t]);
     const int r = q0 + 16 * t + c;
     if (r >= nq) continue;
-    const size_t bh = static_cast<size_t>(gs + r / G) * H + kvh * G + r % G;
+    const size_t qr = kMQ ? static_cast<size_t>(qrow0 + r / G) : static_cast<size_t>(gs + r / G);
+    const size_t bh = qr * H + kvh * G + r % G;
     const size_t slot = bh * p.num_parts + part;
     float* arow = p.ws_acc + slot * D;
 #pragma unroll
@@ -367,32 +394,43 @@ void cascade_prefix_kernel(DecodeParams p) {
   }
 }
 
-template <KvKind KV, int D, int BS>
-hipError_t launch_t(const DecodeParams& p, int max_group_size, hipStream_t s) {
+// max_rows: largest group (cascade) or most new tokens per sequence
+// (multi-query); units: groups or sequences; parts: partitions of the span.
+template <KvKind KV, int D, int BS, bool kMQ>
+hipError_t launch_t(const DecodeParams& p, int units, int max_rows, int parts, hipStream_t s) {
   const int G = p.num_heads / p.num_kv_heads;
-  const int qtiles = (max_group_size * G + kPrefixQueries - 1) / kPrefixQueries;
-  const dim3 grid(static_cast<unsigned>(p.num_groups * p.num_kv_heads), static_cast<unsigned>(qtiles),
-                  static_cast<unsigned>(p.prefix_parts));
-  hipLaunchKernelGGL((cascade_prefix_kernel<KV, D, BS, kPrefixTiles>), grid,
+  const int qtiles = (max_rows * G + kPrefixQueries - 1) / kPrefixQueries;
+  const dim3 grid(static_cast<unsigned>(units * p.num_kv_heads), static_cast<unsigned>(qtiles),
+                  static_cast<unsigned>(parts));
+  hipLaunchKernelGGL((cascade_prefix_kernel<KV, D, BS, kPrefixTiles, kMQ>), grid,
                      dim3(kDecodeWaves * kWave), 0, s, p);
   return hipGetLastError();
 }
 
-template <KvKind KV>
-hipError_t launch_kv(const DecodeParams& p, int max_group_size, hipStream_t s) {
+template <KvKind KV, bool kMQ>
+hipError_t launch_kv(const DecodeParams& p, int units, int max_rows, int parts, hipStream_t s) {
   if (p.head_dim == 128)
-    return p.block_size == 16 ? launch_t<KV, 128, 16>(p, max_group_size, s)
-                              : launch_t<KV, 128, 32>(p, max_group_size, s);
-  return p.block_size == 16 ? launch_t<KV, 64, 16>(p, max_group_size, s)
-                            : launch_t<KV, 64, 32>(p, max_group_size, s);
+    return p.block_size == 16 ? launch_t<KV, 128, 16, kMQ>(p, units, max_rows, parts, s)
+                              : launch_t<KV, 128, 32, kMQ>(p, units, max_rows, parts, s);
+  return p.block_size == 16 ? launch_t<KV, 64, 16, kMQ>(p, units, max_rows, parts, s)
+                            : launch_t<KV, 64, 32, kMQ>(p, units, max_rows, parts, s);
+}
+
+template <bool kMQ>
+hipError_t launch_mode(const DecodeParams& p, KvKind kv, int units, int max_rows, int parts, hipStream_t s) {
+  if (kv == KvKind::I8) return launch_kv<KvKind::I8, kMQ>(p, units, max_rows, parts, s);
+  if (kv == KvKind::FP8) return launch_kv<KvKind::FP8, kMQ>(p, units, max_rows, parts, s);
+  return launch_kv<KvKind::BF16, kMQ>(p, units, max_rows, parts, s);
 }
 
 }  // namespace
 
 hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group_size, hipStream_t s) {
-  if (kv == KvKind::I8) return launch_kv<KvKind::I8>(p, max_group_size, s);
-  if (kv == KvKind::FP8) return launch_kv<KvKind::FP8>(p, max_group_size, s);
-  return launch_kv<KvKind::BF16>(p, max_group_size, s);
+  return launch_mode<false>(p, kv, p.num_groups, max_group_size, p.prefix_parts, s);
+}
+
+hipError_t launch_multi_query(const DecodeParams& p, KvKind kv, int max_queries, hipStream_t s) {
+  return launch_mode<true>(p, kv, p.num_seqs, max_queries, p.num_parts, s);
 }
 
 }  // namespace pkv

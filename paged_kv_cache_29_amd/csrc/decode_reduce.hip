@@ -23,8 +23,9 @@ template <int D, bool kOutBf16>
 __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
   constexpr int ND = D / kWave;
   const int lane = threadIdx.x;
-  const int bh = blockIdx.x;
-  const int b = bh / p.num_heads;
+  const int bh = blockIdx.x;  // (sequence, head), or (query row, head) in multi-query mode
+  const bool mq = p.query_start != nullptr;
+  const int b = mq ? range_of(p.query_start, p.num_seqs, bh / p.num_heads) : bh / p.num_heads;
   const int L = p.context_lens[b];
   // Partials i = 0 .. nparts-1 live in workspace slots slot(i): partitions
   // of the context, or (cascade) npre shared-prefix partitions in slots
@@ -46,6 +47,10 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
       }
       return;
     }
+  } else if (mq) {
+    // every partition of the context left a partial (empty ones: max -inf,
+    // sum 0); the first always holds token 0, which every query sees
+    nparts = (L + p.part_tokens - 1) / p.part_tokens;
   } else {
     nparts = (L + p.part_tokens - 1) / p.part_tokens;
     if (nparts <= 1) return;  // written by the partition kernel
@@ -103,7 +108,8 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
 
 template <int D>
 hipError_t launch_t(const DecodeParams& p, bool out_bf16, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(p.num_seqs * p.num_heads));
+  const int rows = p.query_start != nullptr ? p.num_query_rows : p.num_seqs;
+  const dim3 grid(static_cast<unsigned>(rows * p.num_heads));
   if (out_bf16)
     hipLaunchKernelGGL((decode_reduce_kernel<D, true>), grid, dim3(kWave), 0, s, p);
   else

@@ -194,6 +194,8 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   p.max_shared_blocks = 0;
   p.prefix_part_tokens = 0;
   p.prefix_parts = 0;
+  p.query_start = nullptr;  // plain decode; the multi-query entry point sets it
+  p.num_query_rows = 0;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
@@ -287,6 +289,62 @@ pkv_status cascade_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_hea
   if (static_cast<int64_t>(cs->pparts) + cs->sparts > 65535)
     return fail(PKV_ERR_UNSUPPORTED, "too many partitions (%d + %d)", cs->pparts, cs->sparts);
   return PKV_OK;
+}
+
+// Multi-query partition length: as auto_part_tokens, counting the query
+// tiles of the prefix-style kernel among the units of work.
+int32_t auto_mq_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t qtiles, int32_t block_size,
+                            int32_t max_blocks_per_seq) {
+  const int64_t ctx = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads * qtiles;
+  int32_t pt = 256;
+  for (int32_t cand : {2048, 1024, 512}) {
+    if (cand > kMaxPartBlocks * block_size) continue;
+    if (units * ((ctx + cand - 1) / cand) >= 1024) {
+      pt = cand;
+      break;
+    }
+  }
+  return pt;
+}
+
+struct MqSizes {
+  int32_t pt, parts, qtiles;
+};
+
+pkv_status mq_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t block_size,
+                    int32_t max_blocks_per_seq, int32_t num_query_tokens, int32_t max_queries,
+                    int32_t partition_tokens, MqSizes* ms) {
+  if (num_query_tokens < 0) return fail(PKV_ERR_INVALID, "num_query_tokens must be >= 0");
+  if (num_query_tokens > 0 && (max_queries < 1 || max_queries > num_query_tokens))
+    return fail(PKV_ERR_INVALID, "max_queries_per_seq must be in [1, num_query_tokens] (got %d)", max_queries);
+  if (static_cast<int64_t>(num_query_tokens) * num_heads > 0x7fffffff)
+    return fail(PKV_ERR_UNSUPPORTED, "num_query_tokens * num_heads too large");
+  const int32_t G = num_heads / num_kv_heads;
+  const int64_t qtiles = (static_cast<int64_t>(max_queries > 0 ? max_queries : 1) * G + kPrefixQueries - 1) /
+                         kPrefixQueries;
+  if (qtiles > 65535) return fail(PKV_ERR_UNSUPPORTED, "max_queries_per_seq * G too large");
+  int32_t pt = partition_tokens;
+  if (pt == 0) {
+    pt = auto_mq_part_tokens(num_seqs, num_kv_heads, static_cast<int32_t>(qtiles), block_size,
+                             max_blocks_per_seq);
+  } else if (pt < kChunk || pt % kChunk != 0 || pt > kMaxPartBlocks * block_size) {
+    return fail(PKV_ERR_INVALID, "partition_tokens %d must be 0 or a multiple of %d in [%d, %d]", pt,
+                kChunk, kChunk, kMaxPartBlocks * block_size);
+  }
+  ms->pt = pt;
+  ms->parts = num_parts_for(block_size, max_blocks_per_seq, pt);
+  ms->qtiles = static_cast<int32_t>(qtiles);
+  if (ms->parts > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many context partitions (%d)", ms->parts);
+  return PKV_OK;
+}
+
+size_t mq_workspace_bytes(int32_t num_query_tokens, int32_t num_heads, int32_t head_dim, int32_t parts) {
+  const size_t rows = static_cast<size_t>(num_query_tokens) * num_heads * parts;
+  if (rows == 0) return 0;
+  const size_t acc = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
+  const size_t ml = (rows * sizeof(float) + 255) & ~size_t(255);
+  return acc + 2 * ml;
 }
 
 // Workspace of the cascade: every (sequence, head) has pparts + sparts
@@ -611,6 +669,70 @@ pkv_status pkv_copy_blocks(void* dst_k, void* dst_v, float* dst_k_scale, float* 
   p.scale_bytes = coded ? static_cast<int64_t>(num_kv_heads) * block_size * 4 : 0;
   const hipError_t e = pkv::launch_copy_blocks(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "copy_blocks launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t pkv_paged_attention_multi_query_workspace_size(
+    int32_t num_seqs, int32_t num_query_tokens, int32_t max_queries_per_seq, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int32_t partition_tokens) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      !head_dim_ok(head_dim) || !block_size_ok(block_size) || max_blocks_per_seq <= 0)
+    return 0;
+  MqSizes ms;
+  const std::string saved = g_last_error;
+  const pkv_status s = mq_sizes(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                                num_query_tokens, max_queries_per_seq, partition_tokens, &ms);
+  g_last_error = saved;
+  if (s != PKV_OK) return 0;
+  return mq_workspace_bytes(num_query_tokens, num_heads, head_dim, ms.parts);
+}
+
+pkv_status pkv_paged_attention_multi_query(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* query_start, float scale, int32_t num_seqs, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+    int64_t num_blocks, int32_t num_query_tokens, int32_t max_queries_per_seq, pkv_dtype q_dtype,
+    pkv_dtype kv_dtype, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  DecodeSetup st;
+  pkv_status s = validate_decode(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                 context_lens, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                                 block_size, max_blocks_per_seq, num_blocks, q_dtype, kv_dtype, 0,
+                                 nullptr, 0, nullptr, nullptr, false, &st, /*check_workspace=*/false);
+  if (s != PKV_OK) return s;
+  if (st.kv == pkv::KvKind::F32)
+    return fail(PKV_ERR_UNSUPPORTED, "multi-query attention supports bf16, int8 and FP8 caches only");
+  MqSizes ms;
+  s = mq_sizes(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq, num_query_tokens,
+               max_queries_per_seq, partition_tokens, &ms);
+  if (s != PKV_OK) return s;
+  if (num_seqs == 0 || num_query_tokens == 0) return ok();
+  if (!query_start) return fail(PKV_ERR_INVALID, "multi-query attention needs query_start");
+  const size_t need = mq_workspace_bytes(num_query_tokens, num_heads, head_dim, ms.parts);
+  if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  pkv::DecodeParams& p = st.p;
+  const size_t rows = static_cast<size_t>(num_query_tokens) * num_heads * ms.parts;
+  const size_t acc_bytes = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
+  const size_t ml_bytes = (rows * sizeof(float) + 255) & ~size_t(255);
+  char* ws = static_cast<char*>(workspace);
+  p.ws_acc = reinterpret_cast<float*>(ws);
+  p.ws_m = reinterpret_cast<float*>(ws + acc_bytes);
+  p.ws_l = reinterpret_cast<float*>(ws + acc_bytes + ml_bytes);
+  p.query_start = query_start;
+  p.num_query_rows = num_query_tokens;
+  p.part_tokens = ms.pt;
+  p.num_parts = ms.parts;
+  const hipStream_t strm = static_cast<hipStream_t>(stream);
+  hipError_t e = pkv::launch_multi_query(p, st.kv, max_queries_per_seq, strm);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "multi-query kernel launch failed: %s", hipGetErrorString(e));
+  e = pkv::launch_decode_reduce(p, st.out_bf16, strm);
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

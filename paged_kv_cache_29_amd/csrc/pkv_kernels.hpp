@@ -42,6 +42,13 @@ struct DecodeParams {
   int32_t max_shared_blocks;
   int32_t prefix_part_tokens;
   int32_t prefix_parts;
+  // Multi-query (causal) attention, or nullptr: sequence b's query rows are
+  // query_start[b] .. query_start[b+1]-1 of q and out ([T][H][D]), for the
+  // last n_b positions of its context; row query_start[b] + i attends to
+  // tokens 0 .. L_b - n_b + i.  Partials of every partition go to the
+  // workspace ([T][H][P]) and the reduce always runs.
+  const int32_t* query_start;
+  int32_t num_query_rows;  // T (multi-query)
   float scale_log2;  // scale * log2(e)
   int32_t num_seqs;
   int32_t num_heads;
@@ -99,21 +106,29 @@ __device__ __forceinline__ int group_shared_tokens(const DecodeParams& p, int g)
   return nb * p.block_size;
 }
 
-// Group of sequence b (groups are contiguous ranges; b is uniform, so the
-// search runs on scalar loads).
-__device__ __forceinline__ int group_of(const DecodeParams& p, int b) {
-  int lo = 0, hi = p.num_groups - 1;
+// Index i in [0, n) with start[i] <= x < start[i + 1] of a non-decreasing
+// array (x uniform, so the search runs on scalar loads).
+__device__ __forceinline__ int range_of(const int32_t* start, int n, int x) {
+  int lo = 0, hi = n - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.group_start[mid] <= b) lo = mid; else hi = mid - 1;
+    if (start[mid] <= x) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Group of sequence b (groups are contiguous ranges).
+__device__ __forceinline__ int group_of(const DecodeParams& p, int b) {
+  return range_of(p.group_start, p.num_groups, b);
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s);
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, hipStream_t s);
 hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group_size, hipStream_t s);
+// Multi-query attention partials (query_start set): every partition of every
+// sequence's context for up to max_queries new tokens per sequence.
+hipError_t launch_multi_query(const DecodeParams& p, KvKind kv, int max_queries, hipStream_t s);
 hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
 // Quantising write of fp32 rows into an int8 or FP8 cache (kind I8 or FP8).
 hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s);

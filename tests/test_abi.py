@@ -279,3 +279,41 @@ def test_copy_blocks_rejects(lib, over, code, frag):
 def test_copy_blocks_zero_pairs_is_noop(lib):
     st, msg = _copy(lib, n=0, pairs=None)
     assert st == OK, msg
+
+
+def _mq(lib, **over):
+    a = dict(out=_fake(1), q=_fake(2), k_cache=_fake(3), v_cache=_fake(4), k_scale=None, v_scale=None,
+             block_tables=_fake(5), context_lens=_fake(6), query_start=_fake(7), scale=0.125,
+             num_seqs=4, num_heads=8, num_kv_heads=2, head_dim=64, block_size=16, max_blocks_per_seq=13,
+             num_blocks=32, num_query_tokens=20, max_queries_per_seq=5, q_dtype=BF16, kv_dtype=BF16,
+             partition_tokens=0, workspace=None, workspace_bytes=0, stream=None)
+    a.update(over)
+    st = lib.pkv_paged_attention_multi_query(*a.values())
+    return st, lib.pkv_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code,frag", [
+    (dict(q_dtype=F32, kv_dtype=F32), UNSUPPORTED, "bf16, int8 and FP8"),
+    (dict(num_query_tokens=-1), INVALID, "num_query_tokens"),
+    (dict(max_queries_per_seq=0), INVALID, "max_queries_per_seq"),
+    (dict(max_queries_per_seq=21), INVALID, "max_queries_per_seq"),
+    (dict(query_start=None), INVALID, "query_start"),
+    (dict(partition_tokens=40), INVALID, "partition_tokens"),
+    (dict(kv_dtype=I8), INVALID, "k_scale"),
+    (dict(out=None), INVALID, "null pointer"),
+])
+def test_multi_query_rejects(lib, over, code, frag):
+    st, msg = _mq(lib, **over)
+    assert st == code, msg
+    assert frag in msg
+
+
+def test_multi_query_workspace(lib):
+    st, msg = _mq(lib)
+    assert st == WORKSPACE
+    need = lib.pkv_paged_attention_multi_query_workspace_size(4, 20, 5, 8, 2, 64, 16, 13, 64)
+    rows = 20 * 8 * -(-13 * 16 // 64)
+    assert need == -(-rows * 64 * 4 // 256) * 256 + 2 * (-(-rows * 4 // 256) * 256)
+    assert lib.pkv_paged_attention_multi_query_workspace_size(4, 0, 0, 8, 2, 64, 16, 13, 0) == 0
+    st, msg = _mq(lib, num_query_tokens=0, max_queries_per_seq=0)
+    assert st == OK, msg

@@ -1,0 +1,84 @@
+"""GPU: causal multi-query attention (speculative-decoding verification,
+prefill chunks) against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_29_amd as pkv
+from paged_kv_cache_29_amd import workloads
+
+from gpu_helpers import DEV, DeviceWorkload, assert_parity, oracle_caches, out_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [5, 6, 15, 16, 17, 31, 32, 33, 100, 255, 700]
+
+
+def _run(w, n_per, seed=0, partition_tokens=0, samples=None):
+    dw = DeviceWorkload(w)
+    if w.kv_dtype in ("i8", "fp8"):
+        dw.fill_int8()
+    dw.write_new()                                    # every context token is now cached
+    qs = np.concatenate([[0], np.cumsum(n_per)]).astype(np.int32)
+    T = int(qs[-1])
+    q = workloads.bf16_bits(np.random.default_rng(seed).standard_normal((T, w.num_heads, w.head_dim)).astype(np.float32))
+    out = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
+    pkv.paged_attention_multi_query(out, to_dev(q, "bf16"), dw.k_cache, dw.v_cache, dw.block_tables,
+                                    dw.context_lens, torch.from_numpy(qs).to(DEV), w.scale, w.num_heads,
+                                    w.num_kv_heads, w.head_dim, w.block_size, max(1, max(n_per)),
+                                    k_scale=dw.k_scale, v_scale=dw.v_scale,
+                                    partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    kc, vc, ks, vs = oracle_caches(w)
+    ref = oracle.multi_query_attention(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, w.num_heads,
+                                       w.num_kv_heads, w.head_dim, w.block_size, w.kv_dtype, "bf16",
+                                       k_scale=ks, v_scale=vs, samples=samples)
+    return out_f64(out), ref, q, qs, dw
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+@pytest.mark.parametrize("G,D,bs", [(4, 128, 16), (8, 128, 32), (1, 64, 16), (2, 64, 32), (16, 128, 16)])
+@pytest.mark.parametrize("pt", [0, 64])
+def test_speculative_verify_five_tokens(kv, G, D, bs, pt):
+    w = workloads.make_custom(400 + G + bs, RAGGED, G * 2, 2, D, bs, kv_dtype=kv)
+    got, ref, *_ = _run(w, [5] * len(RAGGED), seed=G + D, partition_tokens=pt)
+    assert_parity(got, ref, kv, f"verify {kv} G={G} D={D} bs={bs} pt={pt}")
+
+
+def test_one_query_per_sequence_is_decode():
+    w = workloads.make_custom(8, RAGGED, 16, 2, 128, 16)
+    got, ref, q, qs, dw = _run(w, [1] * len(RAGGED), seed=4)
+    assert_parity(got, ref, "bf16", "one query")
+    dec = torch.empty((w.num_seqs, 16, 128), dtype=torch.bfloat16, device=DEV)
+    pkv.paged_attention_decode(dec, to_dev(q, "bf16"), dw.k_cache, dw.v_cache, dw.block_tables,
+                               dw.context_lens, w.scale, 16, 2, 128, 16)
+    d = out_f64(dec)
+    # two kernels, the same sums in different orders: within a bf16 unit
+    assert np.all(np.abs(got - d) <= 2.0 ** -7 * np.maximum(np.abs(got), np.abs(d)) + 1e-5)
+
+
+@pytest.mark.parametrize("pt", [0, 64, 256])
+def test_prefill_chunks(pt):
+    """Long runs of new tokens: later partitions hold no visible token for
+    the earliest queries (empty partials), the causal edge crosses chunks."""
+    w = workloads.make_custom(9, [300, 1500, 700, 260], 16, 2, 128, 16)
+    got, ref, *_ = _run(w, [260, 100, 300, 260], seed=7, partition_tokens=pt)
+    assert_parity(got, ref, "bf16", f"prefill pt={pt}")
+
+
+def test_mixed_counts_whole_prefill_and_none():
+    w = workloads.make_custom(10, [5, 40, 1, 17], 8, 2, 64, 16)
+    got, ref, *_ = _run(w, [0, 40, 1, 3], seed=2)         # 40 = a whole 40-token prefill
+    assert_parity(got, ref, "bf16", "mixed")
+
+
+def test_speculative_verify_70b_shape_sampled():
+    w = workloads.make_config(3, 0)
+    n = [5] * w.num_seqs
+    T = 5 * w.num_seqs
+    samples = [(0, 0), (4, 63), (T - 1, 7), (T - 5, 40), (123, 31)]
+    got, ref, *_ = _run(w, n, seed=11, samples=samples)
+    for r, h in samples:
+        assert_parity(got[r, h], ref[r, h], "bf16", f"70B verify (row {r}, head {h})")
