@@ -10,7 +10,7 @@ method's arithmetic.
 
 Everything here is a plain, slow, obviously-correct CPU definition:
 
-* floating point is fp64, except the int8 and FP8 quantisers, which are fp32
+* floating point is fp64, except the int8, FP8 and INT4 quantisers, which are fp32
   on purpose (their results are codes, so both sides must decide them in the
   same precision);
 * gathers go through the block table one logical block at a time;
@@ -21,8 +21,8 @@ Sources (web pages, cited by title and section):
 * [ENG5] "LLM Engineering (5): core techniques of inference optimization"
   (chenk.top), sections "Two phases with very different characteristics",
   "Paged attention", "Block manager: how paging works",
-  "INT8 weight-only quantization", "KV-cache quantization" (int8 and FP8
-  caches with per-token scales), "SGLang and RadixAttention", "Orca's
+  "INT8 weight-only quantization", "KV-cache quantization" (int8, FP8 and
+  INT4 caches with per-token(-per-head) scales), "SGLang and RadixAttention", "Orca's
   iteration-level scheduling" (chunked prefill) and "Speculative decoding"
   (k + 1 positions scored in one pass).
 * [LAYERS] the four-layer inference-optimization article (gsyq.cn/news/366077),
@@ -49,6 +49,7 @@ from .attention import (
 )
 from .cache import cache_write, quantize_int8, cache_write_int8
 from .fp8 import e4m3_decode, e4m3_encode, quantize_fp8, cache_write_fp8
+from .int4 import pack_int4, unpack_int4, quantize_int4, cache_write_int4
 from .closed_forms import kv_cache_bytes, decode_kv_bytes
 
 __all__ = [
@@ -68,6 +69,10 @@ __all__ = [
     "e4m3_encode",
     "quantize_fp8",
     "cache_write_fp8",
+    "pack_int4",
+    "unpack_int4",
+    "quantize_int4",
+    "cache_write_int4",
     "kv_cache_bytes",
     "decode_kv_bytes",
 ]

@@ -27,6 +27,8 @@ Readings taken where the pages are silent (each is listed in the design doc):
 * int8 cache: the value of a stored code ``c`` with scale ``s`` is ``c * s``
   ([LAYERS] 2.3, per-token scales; [ENG5] "KV-cache quantization",
   per-token-per-head scales), evaluated exactly in fp64.
+* INT4 cache: two codes per byte (layout and quantiser in ``int4.py``); the
+  value of code ``c`` with scale ``s`` is again ``c * s``, exactly.
 * bf16 elements are given as their 16-bit patterns (``uint16``); their value
   is the fp32 number whose upper half is that pattern.
 """
@@ -34,8 +36,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
 import numpy as np
 
 from . import fp8 as _fp8
+from . import int4 as _int4
 
-KV_DTYPES = ("f32", "bf16", "i8", "fp8")
+KV_DTYPES = ("f32", "bf16", "i8", "fp8", "i4")
+CODED = ("i8", "fp8", "i4")  # codes with one scale per (token, kv-head)
 
 
 def n_blocks(context_len, block_size):
@@ -104,20 +108,25 @@ def gather_kv(k_cache, v_cache, block_table, context_len, block_size, kv_head,
     Walks the sequence's logical blocks in order; logical block ``j`` lives in
     physical block ``block_table[j]`` and contributes its first
     ``rows_in_block(L, bs, j)`` rows.  Table entries past the last logical
-    block are never read.  For an int8 or FP8 cache each element's value is
-    its code's value times its token's scale.
+    block are never read.  For an int8, FP8 or INT4 cache each element's
+    value is its code's value times its token's scale; INT4 tiles hold two
+    dims per byte (``k_cache[..., D/2]``, ``v_cache[..., D/2, bs]``).
     """
     L = int(context_len)
     bs = int(block_size)
-    D = k_cache.shape[-1]
+    D = k_cache.shape[-1] * (2 if kv_dtype == "i4" else 1)
     K = np.zeros((L, D), dtype=np.float64)
     V = np.zeros((L, D), dtype=np.float64)
     for j in range(n_blocks(L, bs)):
         rows = rows_in_block(L, bs, j)
         blk = int(block_table[j])
-        k_rows = widen(k_cache[blk, kv_head, :rows, :], kv_dtype)        # [rows, D]
-        v_rows = widen(v_cache[blk, kv_head, :, :rows], kv_dtype).T      # [rows, D]
-        if kv_dtype in ("i8", "fp8"):
+        if kv_dtype == "i4":
+            k_rows = _int4.unpack_int4(k_cache[blk, kv_head, :rows, :], axis=-1).astype(np.float64)
+            v_rows = _int4.unpack_int4(v_cache[blk, kv_head, :, :rows], axis=0).astype(np.float64).T
+        else:
+            k_rows = widen(k_cache[blk, kv_head, :rows, :], kv_dtype)        # [rows, D]
+            v_rows = widen(v_cache[blk, kv_head, :, :rows], kv_dtype).T      # [rows, D]
+        if kv_dtype in CODED:
             ks = np.asarray(k_scale[blk, kv_head, :rows], dtype=np.float32).astype(np.float64)
             vs = np.asarray(v_scale[blk, kv_head, :rows], dtype=np.float32).astype(np.float64)
             k_rows = k_rows * ks[:, None]
@@ -150,8 +159,9 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
 
     Shapes: ``q[B, H, D]``; ``k_cache[NB, Hkv, bs, D]``;
     ``v_cache[NB, Hkv, D, bs]``; ``block_tables[B, MB]``; ``context_lens[B]``;
-    int8 scales ``[NB, Hkv, bs]``.  ``q_dtype`` / ``kv_dtype`` name the stored
-    element types ("f32", "bf16", "i8", "fp8").
+    scales ``[NB, Hkv, bs]`` (int8, FP8, INT4; INT4 tiles hold two dims per
+    byte).  ``q_dtype`` / ``kv_dtype`` name the stored element types ("f32",
+    "bf16", "i8", "fp8", "i4").
 
     Returns ``out[B, H, D]`` in fp64.  With ``samples`` (an iterable of
     ``(b, h)`` pairs) only those rows are computed and the others are NaN.

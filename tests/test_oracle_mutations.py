@@ -13,6 +13,7 @@ import oracle
 from oracle import attention as oatt
 from oracle import cache as ocache
 from oracle import fp8 as ofp8
+from oracle import int4 as oint4
 from oracle_pin_checks import ALL_CHECKS
 
 
@@ -177,6 +178,47 @@ def _mq_variant(shift=0, top_left=False, causal=True):
     return mq
 
 
+def _int4_unpack_swapped(packed, axis=-1):
+    # high nibble taken as the lower dim
+    b = np.moveaxis(np.asarray(packed, np.uint8).astype(np.int64), axis, -1)
+    lo, hi = b >> 4, b & 0xF
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int8)
+    out[..., 0::2] = np.where(lo >= 8, lo - 16, lo)
+    out[..., 1::2] = np.where(hi >= 8, hi - 16, hi)
+    return np.moveaxis(out, -1, axis)
+
+
+def _int4_unpack_unsigned(packed, axis=-1):
+    b = np.moveaxis(np.asarray(packed, np.uint8).astype(np.int64), axis, -1)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return np.moveaxis(out, -1, axis)
+
+
+def _int4_pack_swapped(codes, axis=-1):
+    c = np.moveaxis(np.asarray(codes).astype(np.int64), axis, -1) & 0xF
+    return np.moveaxis((c[..., 1::2] | (c[..., 0::2] << 4)).astype(np.uint8), -1, axis)
+
+
+def _int4_quant_over_8(x):
+    x = np.asarray(x, np.float32)
+    a = np.max(np.abs(x), axis=-1)
+    s = (a / np.float32(8)).astype(np.float32)
+    safe = np.where(a > 0, s, np.float32(1)).astype(np.float32)
+    c = np.clip(np.rint((x / safe[..., None]).astype(np.float32)), -8, 7)
+    c = np.where(a[..., None] > 0, c, 0).astype(np.int8)
+    return c, np.where(a > 0, s, 0).astype(np.float32)
+
+
+def _gather_int4_no_v_scale(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                            kv_dtype, k_scale=None, v_scale=None):
+    if kv_dtype == "i4":
+        v_scale = np.ones_like(v_scale)
+    return _orig_gather(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                        kv_dtype, k_scale, v_scale)
+
+
 _orig_e4m3_encode = ofp8.e4m3_encode
 _orig_e4m3_decode = ofp8.e4m3_decode
 _orig_gather = oatt.gather_kv
@@ -206,6 +248,11 @@ MUTATIONS = {
     "fp8_truncate": [(ofp8, "e4m3_encode", _fp8_encode_truncate)],
     "fp8_scale_over_240": [(ofp8, "quantize_fp8", _fp8_quant_over_240)],
     "fp8_v_scale_dropped": [(oatt, "gather_kv", _gather_fp8_no_v_scale)],
+    "int4_nibbles_swapped": [(oint4, "unpack_int4", _int4_unpack_swapped)],
+    "int4_no_sign_extension": [(oint4, "unpack_int4", _int4_unpack_unsigned)],
+    "int4_pack_high_first": [(oint4, "pack_int4", _int4_pack_swapped)],
+    "int4_scale_over_8": [(oint4, "quantize_int4", _int4_quant_over_8)],
+    "int4_v_scale_dropped": [(oatt, "gather_kv", _gather_int4_no_v_scale)],
     "mq_excludes_own_token": [(oatt, "multi_query_attention", _mq_variant(shift=-1))],
     "mq_top_left_causal": [(oatt, "multi_query_attention", _mq_variant(top_left=True))],
     "mq_not_causal": [(oatt, "multi_query_attention", _mq_variant(causal=False))],
