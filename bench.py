@@ -13,7 +13,7 @@ quantising write, then paged_attention_decode's two kernels), reported under
 Prints ONE JSON line.  ``value`` is the KV bytes a step must read divided by
 the measured step time (GB/s) on the 7B-shaped MHA workload (batch 32,
 2048-token contexts, 32 heads x 128 dims, bf16, 16-token blocks).  The
-70B-shaped GQA workloads (bf16, int8 KV and FP8 KV) and the shared-prefix
+70B-shaped GQA workloads (bf16, int8, FP8 and INT4 KV) and the shared-prefix
 workload (with its cascade-decode leg) are reported under
 ``secondary``.  Per-kernel times come from HIP events recorded on the
 stream the kernels run on: each kernel is also run alone, back to back, and
@@ -40,9 +40,11 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "paged decode-attn KV read GB/s (% of HBM peak) + µs/step, 7B & 70B shapes"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-KERNEL_SOURCES = ["decode_mfma.hip", "decode_append.hpp", "pkv_device.hpp", "pkv_kernels.hpp"]
+KERNEL_SOURCES = ["decode_mfma.hip", "decode_tile.hpp", "decode_append.hpp", "pkv_device.hpp",
+                  "pkv_kernels.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.txt")
-CODED = ("i8", "fp8")  # caches of byte codes with per-(token, kv-head) scales
+CODED = ("i8", "fp8", "i4")  # caches of codes with per-(token, kv-head) scales
+CODE_BYTES = {"i8": 1.0, "fp8": 1.0, "i4": 0.5, "bf16": 2.0, "f32": 4.0}  # per element
 
 DESCRIPTIONS = {
     1: "tiny_f32: B=4 L={47,200,16,1} H=Hkv=4 D=64 bs=16 fp32",
@@ -51,6 +53,7 @@ DESCRIPTIONS = {
     4: "prefix_bf16: B=256 shared 2000-token prefix + U{50..500} H=32 Hkv=8 D=128",
     5: "int8_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 int8 KV, bf16 q",
     6: "fp8_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 FP8 E4M3 KV, bf16 q",
+    7: "int4_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 INT4 KV, bf16 q",
 }
 
 
@@ -77,9 +80,9 @@ def read_traffic(workload_name):
 
 
 def kv_bytes(w):
-    elem = 1 if w.kv_dtype in CODED else (4 if w.kv_dtype == "f32" else 2)
+    elem = CODE_BYTES[w.kv_dtype]
     scale = 4 if w.kv_dtype in CODED else 0
-    return 2 * w.num_kv_heads * (w.head_dim * elem + scale) * w.attended_tokens
+    return int(2 * w.num_kv_heads * (w.head_dim * elem + scale) * w.attended_tokens)
 
 
 def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
@@ -99,12 +102,14 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
     slot = torch.from_numpy(w.slot_new).to(dev)
     k_new, v_new = up(w.k_new, store), up(w.v_new, store)
     ks = vs = None
-    write_codes = pkv.kv_cache_write_fp8 if w.kv_dtype == "fp8" else pkv.kv_cache_write_int8
+    write_codes = {"fp8": pkv.kv_cache_write_fp8, "i4": pkv.kv_cache_write_int4}.get(
+        w.kv_dtype, pkv.kv_cache_write_int8)
     if w.kv_dtype in CODED:
         NB, Hkv, bs, D = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
-        cd = torch.float8_e4m3fn if w.kv_dtype == "fp8" else torch.int8
-        kc = torch.zeros((NB, Hkv, bs, D), dtype=torch.uint8, device=dev).view(cd)
-        vc = torch.zeros((NB, Hkv, D, bs), dtype=torch.uint8, device=dev).view(cd)
+        cd = {"fp8": torch.float8_e4m3fn, "i4": torch.uint8}.get(w.kv_dtype, torch.int8)
+        Dw = D // 2 if w.kv_dtype == "i4" else D   # INT4: two dims per byte
+        kc = torch.zeros((NB, Hkv, bs, Dw), dtype=torch.uint8, device=dev).view(cd)
+        vc = torch.zeros((NB, Hkv, Dw, bs), dtype=torch.uint8, device=dev).view(cd)
         ks = torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=dev)
         vs = torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=dev)
         kf, vf, sf = up(w.k_fill, "f32"), up(w.v_fill, "f32"), torch.from_numpy(w.slot_fill).to(dev)
@@ -292,7 +297,7 @@ def unique_tile_bytes(w):
     for b, L in enumerate(w.context_lens):
         n = (int(L) + bs - 1) // bs
         ids.update(int(x) for x in w.block_tables[b, :n])
-    elem = 1 if w.kv_dtype in CODED else (4 if w.kv_dtype == "f32" else 2)
+    elem = CODE_BYTES[w.kv_dtype]
     scale = 4 if w.kv_dtype in CODED else 0
     return int(len(ids) * 2 * w.num_kv_heads * bs * (w.head_dim * elem + scale))
 
@@ -422,7 +427,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--configs", default="2,3,5,6,4", help="first is the headline workload")
+    ap.add_argument("--configs", default="2,3,5,6,7,4", help="first is the headline workload")
     ap.add_argument("--block-size", type=int, default=16, help="for config 4 (16 or 32)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -478,7 +483,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "i8": "i8", "fp8": "fp8_e4m3", "f32": "f32"}[w.kv_dtype],
+        "dtype": {"bf16": "bf16", "i8": "i8", "fp8": "fp8_e4m3", "i4": "i4", "f32": "f32"}[w.kv_dtype],
         "data": "synthetic (seeded N(0,1) K/V/q, shuffled block tables)",
         "config": {"workload": head["workload"], "num_seqs": w.num_seqs,
                    "context_len": int(w.context_lens.max()), "num_heads": w.num_heads,

@@ -35,7 +35,11 @@
  *   v_cache      [NB][Hkv][D][bs]   each (block, kv-head) tile dim-major:
  *                                   element (token row r, dim d) at d*bs + r
  *   k_scale,
- *   v_scale      [NB][Hkv][bs] fp32 (int8 and FP8 caches only)
+ *   v_scale      [NB][Hkv][bs] fp32 (int8, FP8 and INT4 caches only)
+ *   INT4 caches hold two codes per byte, two consecutive head dims of one
+ *   token (dim 2j in the low nibble, 2j + 1 in the high nibble, 4-bit two's
+ *   complement), so their tiles are k_cache [NB][Hkv][bs][D/2] and
+ *   v_cache [NB][Hkv][D/2][bs] (byte (j, r): dims 2j, 2j + 1 of token r).
  *   block_tables [B][MB] int32      logical block j of sequence b lives in
  *                                   physical block block_tables[b*MB + j];
  *                                   entries past the sequence's last block
@@ -74,8 +78,10 @@ typedef enum {
   PKV_F32 = 0,   /* IEEE binary32                         */
   PKV_BF16 = 1,  /* bfloat16, 16-bit patterns             */
   PKV_I8 = 2,    /* int8 codes with an fp32 per-row scale */
-  PKV_FP8 = 3    /* FP8 E4M3 codes (OCP: bias 7, largest finite 448, no
+  PKV_FP8 = 3,   /* FP8 E4M3 codes (OCP: bias 7, largest finite 448, no
                     infinities) with an fp32 per-row scale              */
+  PKV_I4 = 4     /* INT4 codes in [-7, 7], two per byte (layout above),
+                    with an fp32 per-row scale                          */
 } pkv_dtype;
 
 /*
@@ -132,6 +138,27 @@ pkv_status pkv_kv_cache_write_fp8(const float* k, const float* v, uint8_t* k_cac
                                   int64_t num_blocks, void* stream);
 
 /*
+ * Quantising cache write for an INT4 KV cache ([ENG5] "KV-cache
+ * quantization": INT4 KV caches calibrated per token, with per-token-per-
+ * head scales; [LAYERS] 2.3: K and V quantized separately).
+ *   Each (token, kv-head) row x of k (and, separately, of v), fp32, becomes
+ *     a = max_d |x_d|;  s = a / 7 (IEEE fp32 division);
+ *     code_d = clamp(rint(x_d / s), -7, 7)  (round half to even);
+ *     s == 0 (a == 0, or a / 7 underflows) gives all codes 0.
+ *   Codes are packed two per byte into the INT4 tiles (layout above): the
+ *   token's K row is k_cache[s_slot / bs][h][s_slot % bs][0 .. D/2-1], its
+ *   V codes v_cache[s_slot / bs][h][0 .. D/2-1][s_slot % bs]; scales as for
+ *   pkv_kv_cache_write_int8.  No byte is shared by two tokens, so any set of
+ *   distinct slots may be written in one call.  Inputs must be finite.
+ *   Bit-exact.  Errors as for pkv_kv_cache_write_int8.
+ */
+pkv_status pkv_kv_cache_write_int4(const float* k, const float* v, uint8_t* k_cache,
+                                   uint8_t* v_cache, float* k_scale, float* v_scale,
+                                   const int64_t* slot_mapping, int64_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, void* stream);
+
+/*
  * Bytes of device workspace pkv_paged_attention_decode needs for these
  * sizes (0 when every sequence fits one partition, in which case the
  * workspace pointer may be NULL).  partition_tokens as for decode.  Returns
@@ -157,13 +184,13 @@ int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_he
  *   For each sequence b with L = context_lens[b] and query head h (kv-head
  *   g = h / G), with K_b, V_b the L tokens gathered through the block table:
  *     out[b][h][:] = softmax(scale * K_b q[b][h]) V_b,  accumulated in fp32;
- *   L == 0 gives zeros.  For an int8 or FP8 cache each K/V element's value is its
- *   code times the token's scale.
+ *   L == 0 gives zeros.  For an int8, FP8 or INT4 cache each K/V element's
+ *   value is its code times the token's scale.
  * Supported: (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16), (BF16, I8),
- * (BF16, FP8)};
+ * (BF16, FP8), (BF16, I4)};
  * out has q's dtype; head_dim in {64, 128}; block_size in {16, 32};
- * G in {1, 2, 4, 8, 16}.  k_scale and v_scale are required for I8 and FP8 and must
- * be NULL otherwise.  num_seqs == 0 is a no-op.  scale must be finite.
+ * G in {1, 2, 4, 8, 16}.  k_scale and v_scale are required for I8, FP8 and
+ * I4 and must be NULL otherwise.  num_seqs == 0 is a no-op.  scale must be finite.
  * partition_tokens: 0 for the automatic choice, else a multiple of 32 in
  * [32, 128 * block_size]; long contexts are split into partitions of that
  * many tokens whose partial results a second kernel combines.
@@ -212,14 +239,14 @@ pkv_status pkv_paged_attention_decode_reduce(
  *   For every sequence b with L = context_lens[b] >= 1, the token at
  *   position L - 1 (its block is block_tables[b][(L-1) / bs], row
  *   (L-1) % bs) receives k_new[b][h][:] and v_new[b][h][:] for every
- *   kv-head h, exactly as pkv_kv_cache_write / pkv_kv_cache_write_int8 with
- *   that slot would write it; then out is computed as by
+ *   kv-head h, exactly as pkv_kv_cache_write or the quantising write of the
+ *   cache's kind (int8, FP8, INT4) with that slot would write it; then out is computed as by
  *   pkv_paged_attention_decode over the updated cache.  One launch does
  *   both (plus the reduce launch when a context spans several partitions):
  *   the workgroups of the partition holding position L - 1 write the token
  *   before attending, and nothing else reads it.
  *   k_new, v_new: [B][Hkv][D], the cache element type (fp32 or bf16), or
- *   fp32 for an int8 or FP8 cache (quantised in the kernel).  The block holding
+ *   fp32 for an int8, FP8 or INT4 cache (quantised in the kernel).  The block holding
  *   position L - 1 must belong to this sequence alone (copy it on write
  *   first if it is shared).  Other arguments, errors and the workspace as
  *   for pkv_paged_attention_decode; the caches (and int8 scales) are
@@ -271,7 +298,7 @@ pkv_status pkv_paged_attention_decode_step_partitions(
  *   the automatic choice, else a multiple of 32 in [32, 128 * block_size].
  *   partition_tokens as for decode (for the remaining tokens).
  * Supported: (BF16, BF16), (BF16, I8) and (BF16, FP8) with the sizes of decode; an fp32
- * cache returns PKV_ERR_UNSUPPORTED.  The workspace size comes from
+ * or INT4 cache returns PKV_ERR_UNSUPPORTED.  The workspace size comes from
  * pkv_paged_attention_cascade_workspace_size with the same sizes and is
  * needed whenever num_seqs > 0.  Three launches: prefix kernel (skipped when
  * max_shared_blocks is 0), partition kernel, reduce.
@@ -313,7 +340,8 @@ size_t pkv_paged_attention_cascade_workspace_size(
  * query_start: device int32 [num_seqs + 1], query_start[0] = 0,
  * non-decreasing, query_start[num_seqs] = num_query_tokens.
  * max_queries_per_seq: host bound on every n_b, in [1, num_query_tokens].
- * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8) with decode's sizes.
+ * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8) with decode's sizes (an
+ * fp32 or INT4 cache returns PKV_ERR_UNSUPPORTED).
  * partition_tokens: 0 for the automatic choice, else as for decode.
  * Workspace: pkv_paged_attention_multi_query_workspace_size(...) bytes,
  * 256-byte aligned, whenever num_query_tokens > 0.  Two launches (partials

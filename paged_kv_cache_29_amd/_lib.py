@@ -16,11 +16,19 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_NO_BLOCKS = range(6)
-PKV_F32, PKV_BF16, PKV_I8, PKV_FP8 = range(4)
+PKV_F32, PKV_BF16, PKV_I8, PKV_FP8, PKV_I4 = range(5)
 
+# INT4 caches are uint8 tensors holding two codes per byte
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_I8,
-           torch.float8_e4m3fn: PKV_FP8}
-_CODED = (PKV_I8, PKV_FP8)  # byte codes with per-(token, kv-head) scales
+           torch.float8_e4m3fn: PKV_FP8, torch.uint8: PKV_I4}
+_CODED = (PKV_I8, PKV_FP8, PKV_I4)  # codes with per-(token, kv-head) scales
+
+
+def _tile_shapes(kd, Hkv, bs, D):
+    """Per-block K and V tile shapes of a cache of kind kd: [Hkv, bs, D] and
+    [Hkv, D, bs], or [Hkv, bs, D/2] and [Hkv, D/2, bs] for INT4."""
+    w = D // 2 if kd == PKV_I4 else D
+    return (Hkv, bs, w), (Hkv, w, bs)
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -38,6 +46,8 @@ SIGNATURES = {
     "pkv_kv_cache_write_fp8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32,
                                        c_i32, c_i32, c_i64, c_vp]),
     "pkv_kv_cache_write_int8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32,
+                                        c_i32, c_i32, c_i64, c_vp]),
+    "pkv_kv_cache_write_int4": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32,
                                         c_i32, c_i32, c_i64, c_vp]),
     "pkv_paged_attention_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                                     c_i32]),
@@ -169,13 +179,26 @@ def kv_cache_write_fp8(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping):
                  "pkv_kv_cache_write_fp8")
 
 
+def kv_cache_write_int4(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping):
+    """Quantise fp32 K/V rows to INT4 codes in [-7, 7] + per-(token, kv-head)
+    scale and scatter; the caches are uint8 tensors ``[NB, Hkv, bs, D/2]``
+    (K) and ``[NB, Hkv, D/2, bs]`` (V), two consecutive dims per byte."""
+    _write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, torch.uint8,
+                 "pkv_kv_cache_write_int4")
+
+
 def _write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, cache_dtype, entry):
     dev = k_cache.device
     for n, t in (("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("k_scale", k_scale), ("v_scale", v_scale), ("slot_mapping", slot_mapping)):
         _dense_on(t, dev, n)
+    _need(k_cache.dim() == 4, "k_cache must be 4-d")
     NB, Hkv, bs, D = k_cache.shape
-    _need(tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB, Hkv, D, bs]")
+    kd = _DTYPES[cache_dtype]
+    if kd == PKV_I4:
+        D *= 2
+    kt, vt = _tile_shapes(kd, Hkv, bs, D)
+    _need(tuple(v_cache.shape) == (NB,) + vt, f"v_cache must be [NB, {', '.join(map(str, vt))}]")
     _need(k_cache.dtype == v_cache.dtype == cache_dtype, f"{cache_dtype} caches expected")
     _need(k.dtype == v.dtype == torch.float32, "k, v must be float32")
     _need(k.dim() == 3 and tuple(k.shape[1:]) == (Hkv, D) and k.shape == v.shape,
@@ -227,10 +250,11 @@ def _marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     _need(k_cache.dim() == 4, "k_cache must be [NB, Hkv, bs, D]")
     NB = k_cache.shape[0]
-    _need(tuple(k_cache.shape) == (NB, num_kv_heads, block_size, head_dim),
-          "k_cache must be [NB, Hkv, bs, D]")
-    _need(tuple(v_cache.shape) == (NB, num_kv_heads, head_dim, block_size),
-          "v_cache must be [NB, Hkv, D, bs]")
+    kt, vt = _tile_shapes(_DTYPES.get(k_cache.dtype), num_kv_heads, block_size, head_dim)
+    _need(tuple(k_cache.shape) == (NB,) + kt,
+          "k_cache must be [NB, Hkv, bs, D] ([NB, Hkv, bs, D/2] for INT4)")
+    _need(tuple(v_cache.shape) == (NB,) + vt,
+          "v_cache must be [NB, Hkv, D, bs] ([NB, Hkv, D/2, bs] for INT4)")
     _need(k_cache.dtype == v_cache.dtype, "k_cache and v_cache dtypes differ")
     B = q.shape[0]
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,
@@ -435,7 +459,7 @@ def probe_tile_read(pool, tile_ids, sink, grid, check_ids=True):
 def copy_blocks(dst, src, pairs):
     """Copy whole blocks from pool ``src`` to pool ``dst``: block ``pairs[i,
     0]`` of ``src`` to block ``pairs[i, 1]`` of ``dst`` (K tiles, V tiles and,
-    for int8 / FP8 pools, scale rows).  A pool is ``(k_cache, v_cache)`` or
+    for int8 / FP8 / INT4 pools, scale rows).  A pool is ``(k_cache, v_cache)`` or
     ``(k_cache, v_cache, k_scale, v_scale)``, on the device or in pinned host
     memory (swapping); ``pairs`` is an int32 ``[n, 2]`` tensor on the device.
     Runs on the current stream of the device pool's GPU."""
@@ -454,12 +478,15 @@ def copy_blocks(dst, src, pairs):
     _need(kd is not None and all(_DTYPES.get(t.dtype) == kd for t in (dst[1], src[0], src[1])),
           "pool dtypes must match")
     coded = kd in _CODED
-    _need(coded == (len(dst) == 4), "int8 / FP8 pools carry scales; fp32 / bf16 pools do not")
+    _need(coded == (len(dst) == 4), "int8 / FP8 / INT4 pools carry scales; fp32 / bf16 pools do not")
     k = dst[0]
     _need(k.dim() == 4, "k_cache must be [NB, Hkv, bs, D]")
     _, Hkv, bs, D = k.shape
+    if kd == PKV_I4:
+        D *= 2
+    kt, vt = _tile_shapes(kd, Hkv, bs, D)
     for pool in (dst, src):
-        _need(tuple(pool[0].shape[1:]) == (Hkv, bs, D) and tuple(pool[1].shape[1:]) == (Hkv, D, bs),
+        _need(tuple(pool[0].shape[1:]) == kt and tuple(pool[1].shape[1:]) == vt,
               "pools must share Hkv, bs and D")
     sc = (lambda pool: (_ptr(pool[2]), _ptr(pool[3]))) if coded else (lambda pool: (_ptr(None), _ptr(None)))
     st = load().pkv_copy_blocks(_ptr(dst[0]), _ptr(dst[1]), *sc(dst), _ptr(src[0]), _ptr(src[1]),

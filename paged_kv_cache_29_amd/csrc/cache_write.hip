@@ -13,7 +13,11 @@
 // ("LLM Engineering (5)", "KV-cache quantization" and "INT8 weight-only
 // quantization"; four-layer inference-optimization article, 2.3).
 // kv_cache_write_fp8 does the same with s = absmax / 448 and the nearest
-// OCP E4M3 code of x / s (the same section's FP8 KV caches).  This
+// OCP E4M3 code of x / s (the same section's FP8 KV caches).
+// kv_cache_write_int4 uses s = absmax / 7 and codes clamp(rint(x / s), -7, 7),
+// stored two per byte (two consecutive head dims of one token, the lower dim
+// in the low nibble, 4-bit two's complement); no byte holds two tokens, so
+// tokens are written independently.  This
 // translation unit is built without fast-math and with correctly rounded
 // fp32 division, so the codes and scales are bit-exact.
 
@@ -59,7 +63,8 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
 
 // One lane group of D/4 lanes per (token, kv-head, K-or-V) row, 4 values per
 // lane; rows alternate K, V.
-// KV: I8 (s = absmax / 127, quantize_code) or FP8 (s = absmax / 448, fp8_code).
+// KV: I8 (s = absmax / 127, quantize_code), FP8 (s = absmax / 448, fp8_code)
+// or I4 (s = absmax / 7, quantize_sym<7>, tiles of half the bytes).
 template <KvKind KV>
 __global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
   const int D = p.head_dim;
@@ -90,15 +95,31 @@ __global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
     float a = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
     for (int o = group / 2; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
     if (slot < 0) continue;
-    const float s = a / (KV == KvKind::FP8 ? 448.0f : 127.0f);
+    const float s = a / (KV == KvKind::FP8 ? 448.0f : (KV == KvKind::I4 ? 7.0f : 127.0f));
+    const int64_t blk = slot / BS;
+    const int row = static_cast<int>(slot - blk * BS);
+    const int d0 = 4 * sub;
+    if constexpr (KV == KvKind::I4) {
+      // dims d0 .. d0+3 -> bytes d0/2 and d0/2 + 1 of the token
+      const uint32_t b0 = pack_int4_pair(quantize_sym<7>(x[0], s), quantize_sym<7>(x[1], s));
+      const uint32_t b1 = pack_int4_pair(quantize_sym<7>(x[2], s), quantize_sym<7>(x[3], s));
+      const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * (D / 2);
+      const int j = d0 / 2;
+      if (!is_v) {
+        *reinterpret_cast<uint16_t*>(kc + tile + static_cast<int64_t>(row) * (D / 2) + j) =
+            static_cast<uint16_t>(b0 | (b1 << 8));
+      } else {
+        vc[tile + static_cast<int64_t>(j) * BS + row] = static_cast<uint8_t>(b0);
+        vc[tile + static_cast<int64_t>(j + 1) * BS + row] = static_cast<uint8_t>(b1);
+      }
+      if (sub == 0) (is_v ? p.v_scale : p.k_scale)[(blk * Hkv + h) * BS + row] = (s > 0.f) ? s : 0.f;
+      continue;
+    }
     uint32_t codes[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       codes[e] = KV == KvKind::FP8 ? fp8_code(x[e], s) : static_cast<uint32_t>(quantize_code(x[e], s));
-    const int64_t blk = slot / BS;
-    const int row = static_cast<int>(slot - blk * BS);
     const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * D;
-    const int d0 = 4 * sub;
     if (!is_v) {
       const uint32_t packed = (codes[0] & 0xffu) | ((codes[1] & 0xffu) << 8) |
                               ((codes[2] & 0xffu) << 16) | ((codes[3] & 0xffu) << 24);
@@ -139,6 +160,8 @@ hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream
   const unsigned grid = grid_for(p.num_tokens * p.num_kv_heads * 2, rows_per_block);
   if (kind == KvKind::FP8)
     hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::FP8>, dim3(grid), dim3(256), 0, s, p);
+  else if (kind == KvKind::I4)
+    hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::I4>, dim3(grid), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::I8>, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -18,8 +18,8 @@
 namespace pkv {
 
 // Called by all threads of a workgroup of at least 2 * D threads (and at
-// least two waves); pos = L - 1 >= 0.  KV: F32 or BF16 (bit copy), I8 or
-// FP8 (quantised from fp32 rows).
+// least two waves); pos = L - 1 >= 0.  KV: F32 or BF16 (bit copy), I8, FP8
+// or I4 (quantised from fp32 rows).
 template <KvKind KV, int D, int BS>
 __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, int kvh, int pos) {
   using KT = typename std::conditional<
@@ -33,7 +33,31 @@ __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, i
   KT* kc = static_cast<KT*>(const_cast<void*>(p.k_cache));
   KT* vc = static_cast<KT*>(const_cast<void*>(p.v_cache));
   const int t = threadIdx.x;
-  if constexpr (KV == KvKind::I8 || KV == KvKind::FP8) {
+  if constexpr (KV == KvKind::I4) {
+    // wave 0 quantises the K row, wave 1 the V row; lane < D/2 owns dims
+    // 2 lane and 2 lane + 1, which share one byte
+    const int wave = t / kWave;
+    const int lane = t % kWave;
+    if (wave < 2) {
+      const float* x = static_cast<const float*>(wave == 0 ? p.k_new : p.v_new) + src;
+      float2 v = {0.f, 0.f};
+      if (lane < D / 2) v = *reinterpret_cast<const float2*>(x + 2 * lane);
+      const float a = wave_max(fmaxf(fabsf(v.x), fabsf(v.y)));
+      const float s = a / 7.0f;
+      const size_t tile4 = (static_cast<size_t>(blk) * Hkv + kvh) * (static_cast<size_t>(BS) * D / 2);
+      if (lane < D / 2) {
+        const uint8_t byte = static_cast<uint8_t>(pack_int4_pair(quantize_sym<7>(v.x, s), quantize_sym<7>(v.y, s)));
+        if (wave == 0)
+          kc[tile4 + static_cast<size_t>(row) * (D / 2) + lane] = byte;
+        else
+          vc[tile4 + static_cast<size_t>(lane) * BS + row] = byte;
+      }
+      if (lane == 0) {
+        float* sc = const_cast<float*>(wave == 0 ? p.k_scale : p.v_scale);
+        sc[(static_cast<size_t>(blk) * Hkv + kvh) * BS + row] = (s > 0.f) ? s : 0.f;
+      }
+    }
+  } else if constexpr (KV == KvKind::I8 || KV == KvKind::FP8) {
     // wave 0 quantises the K row, wave 1 the V row; lane owns dims lane + 64i
     constexpr int ND = D / kWave;
     const int wave = t / kWave;

@@ -1,12 +1,12 @@
-// Paged decode attention, bf16 query over a bf16 or int8 paged KV cache,
-// on gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
+// Paged decode attention, bf16 query over a bf16, int8, FP8 or INT4 paged KV
+// cache, on gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
 //
 // What is computed: for each sequence b and query head h, softmax(scale *
 // K_b q) V_b over the L = context_lens[b] cached tokens, gathered through the
 // block table ("LLM Engineering (5)" [ENG5], "Paged attention"; every decode
 // step reads the whole KV cache: [ENG5] "Two phases with very different
-// characteristics").  int8 caches hold codes with one fp32 scale per
-// (token, kv-head) ([ENG5] "KV-cache quantization").
+// characteristics").  int8, FP8 and INT4 caches hold codes with one fp32
+// scale per (token, kv-head) ([ENG5] "KV-cache quantization").
 //
 // Work decomposition.  One workgroup of kDecodeWaves waves owns one
 // (sequence, kv-head, context partition of part_tokens tokens).  The G query
@@ -40,6 +40,14 @@
 // The contraction index of each MFMA is a free pairing of (lane group,
 // element) to (dim or token); A and B use the same pairing, so only the row
 // / column / accumulator layouts of the instruction matter here.
+//
+// INT4 caches: codes enter the contractions as c + 136 (see decode_tile.hpp).
+// The score accumulator starts at -136 * sum_d q_d, which cancels the offset
+// in K; the offset in V adds 136 * sum_t p_t v_scale_t to every output dim
+// of a head, which each wave subtracts from its accumulator before the
+// waves are merged.  Output tile 2m takes dims 32m + 2r and tile 2m + 1
+// dims 32m + 2r + 1 (r = tile row), so a lane's two tiles hold 8
+// consecutive dims.
 
 #include <type_traits>
 
@@ -59,11 +67,22 @@ namespace {
 template <KvKind KV>
 constexpr int kBatch = 2;
 
-// KV: BF16, or byte codes with per-token scales (I8, FP8).
+// Waves per SIMD.  Two chunks in flight per wave at two waves saturate
+// the bf16, int8 and FP8 streams; an INT4 chunk carries half the bytes for
+// the same arithmetic, and a third wave (162 VGPRs fit) hides more of the
+// load latency (measured 8% faster; int8 and FP8 gain nothing).
+template <KvKind KV>
+constexpr int kWavesPerSimd = KV == KvKind::I4 ? 3 : 2;
+
+// KV: BF16, or codes with per-token scales (I8, FP8: bytes; I4: nibbles).
 template <KvKind KV, int D, int BS, int W>
-__global__ __launch_bounds__(W * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(W * kWave)
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV>, kWavesPerSimd<KV>)))
 void decode_mfma_kernel(DecodeParams p) {
-  constexpr bool kInt8 = KV != KvKind::BF16;  // byte codes (int8 or FP8) with scales
+  constexpr bool kInt8 = KV != KvKind::BF16;  // codes (int8, FP8, INT4) with scales
+  constexpr bool kI4 = KV == KvKind::I4;
+  using ChunkT = typename std::conditional<kI4, ChunkI4<D>, Chunk<kInt8, D>>::type;
+  using LoaderT = typename std::conditional<kI4, ChunkLoaderI4<D, BS>, ChunkLoader<kInt8, D, BS>>::type;
   constexpr int NB = kBatch<KV>;
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
@@ -114,16 +133,26 @@ void decode_mfma_kernel(DecodeParams p) {
 
   // Q^T operand (B of the score MFMA): lane (c, g), MFMA j, 8 dims.
   bf16x8 qf[NJ];
+  float k_off = 0.f;  // INT4: 136 * sum_d q_d of head c
   {
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
                            (static_cast<size_t>(b) * H + h0 + c) * D;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int d0 = kInt8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g);
+      const int d0 = kI4 ? ((D / 4) * g + 8 * j)
+                         : (kInt8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g));
       u32x4 v = {0u, 0u, 0u, 0u};
       if (c < G) v = load_u32x4(qrow + d0);
+      if constexpr (kI4) {
+        // element order of the INT4 K operand: dims +0, 2, 4, 6, 1, 3, 5, 7
+        v = u32x4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                  __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k_off += bf16_lo(v[i]) + bf16_hi(v[i]);
+      }
       qf[j] = as_bf16x8(v);
     }
+    if constexpr (kI4) k_off = kInt4Offset * groups_sum(k_off);
   }
 
   // Physical block ids of the partition, staged in this wave's LDS slice so
@@ -137,7 +166,7 @@ void decode_mfma_kernel(DecodeParams p) {
   __builtin_amdgcn_s_waitcnt(0);  // wave-private slice: own stores only
   const int* my_ids = blk_ids[wave];
 
-  const ChunkLoader<kInt8, D, BS> ld(p, kvh, c, g);
+  const LoaderT ld(p, kvh, c, g);
 
   // Block ids of chunk `ch` (uniform).  Past the end of the context the
   // second half reuses the first block: valid memory whose rows are masked.
@@ -158,18 +187,28 @@ void decode_mfma_kernel(DecodeParams p) {
 
   float m_run = -INFINITY;
   float l_run = 0.f;
+  float pv_run = 0.f;  // INT4: sum_t p_t v_scale_t (this lane's tokens)
   f32x4 acc[NN];
 #pragma unroll
   for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto consume = [&](const Chunk<kInt8, D>& cw, int ch) {
+  auto consume = [&](const ChunkT& cw, int ch) {
     const int t0 = t_begin + ch * 32;
     // ---- scores: S^T of sub-tiles h = 0, 1
     f32x4 s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (kInt8) {
+      if constexpr (kI4) {
+        s[h] = f32x4{-k_off, -k_off, -k_off, -k_off};
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          uint32_t lo, hi;
+          int4_nibbles(cw.k[h][j], lo, hi);
+          const u32x2 a = nib4_to_bf16(lo), bq = nib4_to_bf16(hi);
+          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{a.x, a.y, bq.x, bq.y}), qf[j], s[h], 0, 0, 0);
+        }
+      } else if constexpr (kInt8) {
 #pragma unroll
         for (int jj = 0; jj < NJ / 2; ++jj) {
           const u32x4 w = cw.k[h][jj];
@@ -216,6 +255,7 @@ void decode_mfma_kernel(DecodeParams p) {
     if (__any(m_new > m_run)) {
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
+      if constexpr (kI4) pv_run *= alpha;
 #pragma unroll
       for (int n = 0; n < NN; ++n) acc[n] *= alpha;
       m_run = m_new;
@@ -233,6 +273,10 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[e] *= vs[e >> 2][e & 3];
       }
+      if constexpr (kI4) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv_run += pr[e];
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         ph[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
@@ -242,6 +286,34 @@ void decode_mfma_kernel(DecodeParams p) {
     const bf16x8 pfh = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
     const bf16x8 pfl = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
     // ---- O^T += V^T . P^T
+    if constexpr (kI4) {
+#pragma unroll
+      for (int m = 0; m < NN / 2; ++m) {
+        uint32_t lo0, hi0, lo1, hi1;
+        int4_nibbles(cw.v[0][m], lo0, hi0);
+        int4_nibbles(cw.v[1][m], lo1, hi1);
+        const u32x2 a0 = nib4_to_bf16(lo0), a1 = nib4_to_bf16(lo1);
+        const u32x2 b0 = nib4_to_bf16(hi0), b1 = nib4_to_bf16(hi1);
+        u32x4 ve = {a0.x, a0.y, a1.x, a1.y};  // dim 32m + 2c, tokens e = 4h + i
+        u32x4 vo = {b0.x, b0.y, b1.x, b1.y};  // dim 32m + 2c + 1
+        if (tail) {  // masked tokens contribute exact zeros
+          const int ta = t0 + 4 * g;
+          ve.x = mask_pair(ve.x, ta, t_end);
+          ve.y = mask_pair(ve.y, ta + 2, t_end);
+          ve.z = mask_pair(ve.z, ta + 16, t_end);
+          ve.w = mask_pair(ve.w, ta + 18, t_end);
+          vo.x = mask_pair(vo.x, ta, t_end);
+          vo.y = mask_pair(vo.y, ta + 2, t_end);
+          vo.z = mask_pair(vo.z, ta + 16, t_end);
+          vo.w = mask_pair(vo.w, ta + 18, t_end);
+        }
+        acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfh, acc[2 * m], 0, 0, 0);
+        acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfl, acc[2 * m], 0, 0, 0);
+        acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfh, acc[2 * m + 1], 0, 0, 0);
+        acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfl, acc[2 * m + 1], 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
       u32x4 vw;
@@ -272,7 +344,7 @@ void decode_mfma_kernel(DecodeParams p) {
   // hoist, together with its waits, above the batch's other loads.
   const int nchunks = (t_end - t_begin + 31) / 32;
   {
-    Chunk<kInt8, D> cb[NB];
+    ChunkT cb[NB];
     int blk[2], row0[2];
     for (int ch = wave; ch < nchunks; ch += NB * W) {
       if (ch + (NB - 1) * W < nchunks) {
@@ -296,6 +368,11 @@ void decode_mfma_kernel(DecodeParams p) {
 
   // per-head sum over the 4 lane groups (each holds different tokens)
   l_run = groups_sum(l_run);
+  if constexpr (kI4) {  // remove the V offset of this wave's tokens
+    const float v_off = kInt4Offset * groups_sum(pv_run);
+#pragma unroll
+    for (int n = 0; n < NN; ++n) acc[n] -= v_off;
+  }
 
   float M = m_run, Lsum = l_run;
   if constexpr (W > 1) {
@@ -329,6 +406,31 @@ void decode_mfma_kernel(DecodeParams p) {
   if (c >= G) return;
   const int h = h0 + c;
   const size_t bh = static_cast<size_t>(b) * H + h;
+  if constexpr (kI4) {  // lane holds dims 32m + 8g .. + 7: tiles 2m (even), 2m + 1 (odd)
+    if (single) {
+      uint16_t* orow = out + bh * D;
+#pragma unroll
+      for (int m = 0; m < NN / 2; ++m) {
+        const f32x4 e = acc[2 * m] / Lsum, o = acc[2 * m + 1] / Lsum;
+        *reinterpret_cast<u32x4*>(orow + 32 * m + 8 * g) =
+            u32x4{pack_bf16x2(e[0], o[0]), pack_bf16x2(e[1], o[1]), pack_bf16x2(e[2], o[2]), pack_bf16x2(e[3], o[3])};
+      }
+    } else {
+      const size_t slot = bh * p.num_parts + (cascade ? p.prefix_parts : 0) + part;
+      float* arow = p.ws_acc + slot * D;
+#pragma unroll
+      for (int m = 0; m < NN / 2; ++m) {
+        const f32x4 e = acc[2 * m], o = acc[2 * m + 1];
+        *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
+        *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
+      }
+      if (g == 0) {
+        p.ws_m[slot] = M;
+        p.ws_l[slot] = Lsum;
+      }
+    }
+    return;
+  }
   if (single) {
     uint16_t* orow = out + bh * D;
 #pragma unroll
@@ -371,6 +473,7 @@ hipError_t launch_kv(const DecodeParams& p, hipStream_t s) {
 
 hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s) {
   if (kv == KvKind::I8) return launch_kv<KvKind::I8>(p, s);
+  if (kv == KvKind::I4) return launch_kv<KvKind::I4>(p, s);
   if (kv == KvKind::FP8) return launch_kv<KvKind::FP8>(p, s);
   return launch_kv<KvKind::BF16>(p, s);
 }

@@ -67,6 +67,33 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t w0, uint32_t w1) {
                          codes_to_bf16x2<KV, 0>(w1), codes_to_bf16x2<KV, 1>(w1)});
 }
 
+// INT4 codes (two per byte, 4-bit two's complement) -> bf16 operands.
+// Flipping each nibble's top bit turns code c into the unsigned u = c + 8,
+// and the bf16 bit pattern 0x4300 | u is the integer 128 + u exactly, so a
+// byte permute builds two operands per instruction: every element carries
+// the value c + 136, and the kernels subtract the offset's contribution
+// (136 times the sum of the other operand) once per contraction.
+constexpr float kInt4Offset = 136.0f;
+
+// Nibbles of w, offset: lo = low nibble of each byte, hi = high nibble.
+__device__ __forceinline__ void int4_nibbles(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x88888888u;
+  lo = u & 0x0f0f0f0fu;
+  hi = (u >> 4) & 0x0f0f0f0fu;
+}
+
+// Bytes 0, 1 (HALF 0) or 2, 3 (HALF 1) of n (nibble values) -> bf16 pair.
+template <int HALF>
+__device__ __forceinline__ uint32_t nib_pair_to_bf16x2(uint32_t n) {
+  // result bytes: n[2 HALF], 0x43, n[2 HALF + 1], 0x43 (0x43 from the high word)
+  return __builtin_amdgcn_perm(0x43434343u, n, HALF ? 0x04030402u : 0x04010400u);
+}
+
+// The four bytes of n -> one half (4 elements) of a bf16x8 operand.
+__device__ __forceinline__ u32x2 nib4_to_bf16(uint32_t n) {
+  return u32x2{nib_pair_to_bf16x2<0>(n), nib_pair_to_bf16x2<1>(n)};
+}
+
 // Zero the bf16 elements (pairs packed in w) whose token is >= t_end.
 __device__ __forceinline__ uint32_t mask_pair(uint32_t w, int tok, int t_end) {
   const uint32_t lo = (tok < t_end) ? (w & 0xffffu) : 0u;
@@ -158,6 +185,61 @@ struct ChunkLoader {
         for (int n = 0; n < NN; ++n)
           ch.v[h][n] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, vs_row + 32 * n * BS, 0));
       }
+    }
+  }
+};
+
+// INT4 chunk.  K: per sub-tile, lane l = 16 g + c holds row c, dims
+// (D/4) g .. (D/4) g + D/4 - 1 (D/8 bytes, one load); operand j is the word
+// of dims (D/4) g + 8 j .. + 7, its elements in the order of that word's
+// low nibbles, then its high nibbles (dims +0, 2, 4, 6, 1, 3, 5, 7).
+// V: the tile is [D/2][bs] bytes; per sub-tile and dim-pair block m, the
+// lane holds tokens 4g .. 4g+3 of byte row 16 m + c (dims 32 m + 2 c and
+// 32 m + 2 c + 1): its low nibbles feed the rows of output tile 2 m, its
+// high nibbles those of tile 2 m + 1.
+template <int D>
+struct ChunkI4 {
+  typename std::conditional<D == 128, u32x4, u32x2>::type k[2];
+  uint32_t v[2][D / 32];
+  f32x4 ks[2], vs[2];
+};
+
+template <int D, int BS>
+struct ChunkLoaderI4 {
+  static constexpr uint32_t kTileBytes = BS * D / 2;
+  const char* kc;
+  const char* vc;
+  const char* ksc;
+  const char* vsc;
+  int Hkv, kvh;
+  uint32_t koff, voff, soff;
+
+  __device__ __forceinline__ ChunkLoaderI4(const DecodeParams& p, int kvh_, int c, int g)
+      : kc(static_cast<const char*>(p.k_cache)), vc(static_cast<const char*>(p.v_cache)),
+        ksc(reinterpret_cast<const char*>(p.k_scale)), vsc(reinterpret_cast<const char*>(p.v_scale)),
+        Hkv(p.num_kv_heads), kvh(kvh_) {
+    koff = static_cast<uint32_t>(c) * (D / 2) + (D / 8) * g;
+    voff = static_cast<uint32_t>(c) * BS + 4u * g;
+    soff = 4u * g * 4u;
+  }
+
+  __device__ __forceinline__ void load(ChunkI4<D>& ch, const int blk[2], const int row0[2]) const {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const size_t t = static_cast<size_t>(blk[h]) * Hkv + kvh;
+      const __amdgpu_buffer_rsrc_t rk = ChunkLoader<true, D, BS>::tile(kc, t * kTileBytes, kTileBytes);
+      const __amdgpu_buffer_rsrc_t rv = ChunkLoader<true, D, BS>::tile(vc, t * kTileBytes, kTileBytes);
+      if constexpr (D == 128)
+        ch.k[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, row0[h] * (D / 2), 0));
+      else
+        ch.k[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, koff, row0[h] * (D / 2), 0));
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m)
+        ch.v[h][m] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, row0[h] + 16 * m * BS, 0);
+      const __amdgpu_buffer_rsrc_t rks = ChunkLoader<true, D, BS>::tile(ksc, t * BS * 4, BS * 4);
+      const __amdgpu_buffer_rsrc_t rvs = ChunkLoader<true, D, BS>::tile(vsc, t * BS * 4, BS * 4);
+      ch.ks[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, soff, row0[h] * 4, 0));
+      ch.vs[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, soff, row0[h] * 4, 0));
     }
   }
 };

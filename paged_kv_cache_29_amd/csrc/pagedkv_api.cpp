@@ -136,6 +136,8 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
     kv = pkv::KvKind::I8;
   } else if (q_dtype == PKV_BF16 && kv_dtype == PKV_FP8) {
     kv = pkv::KvKind::FP8;
+  } else if (q_dtype == PKV_BF16 && kv_dtype == PKV_I4) {
+    kv = pkv::KvKind::I4;
   } else {
     return fail(PKV_ERR_UNSUPPORTED, "(q_dtype, kv_dtype) = (%d, %d) is not supported",
                 static_cast<int>(q_dtype), static_cast<int>(kv_dtype));
@@ -156,11 +158,11 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   }
   if (step && num_seqs > 0 && (!k_new || !v_new))
     return fail(PKV_ERR_INVALID, "decode step needs k_new and v_new");
-  if (kv == pkv::KvKind::I8 || kv == pkv::KvKind::FP8) {
+  if (kv == pkv::KvKind::I8 || kv == pkv::KvKind::FP8 || kv == pkv::KvKind::I4) {
     if (num_seqs > 0 && (!k_scale || !v_scale))
-      return fail(PKV_ERR_INVALID, "int8 cache needs k_scale and v_scale");
+      return fail(PKV_ERR_INVALID, "int8 / FP8 / INT4 cache needs k_scale and v_scale");
   } else if (k_scale || v_scale) {
-    return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL unless kv_dtype is PKV_I8 or PKV_FP8");
+    return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL unless kv_dtype is PKV_I8, PKV_FP8 or PKV_I4");
   }
   const size_t need = check_workspace ? workspace_bytes_for(num_seqs, num_heads, head_dim, nparts) : 0;
   if (need > 0 && num_seqs > 0) {
@@ -434,6 +436,16 @@ pkv_status pkv_kv_cache_write_fp8(const float* k, const float* v, uint8_t* k_cac
                      "kv_cache_write_fp8");
 }
 
+pkv_status pkv_kv_cache_write_int4(const float* k, const float* v, uint8_t* k_cache,
+                                   uint8_t* v_cache, float* k_scale, float* v_scale,
+                                   const int64_t* slot_mapping, int64_t num_tokens,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, void* stream) {
+  return write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens,
+                     num_kv_heads, head_dim, block_size, num_blocks, pkv::KvKind::I4, stream,
+                     "kv_cache_write_int4");
+}
+
 int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                              int32_t block_size, int32_t max_blocks_per_seq,
                                              int32_t partition_tokens) {
@@ -565,8 +577,8 @@ pkv_status pkv_paged_attention_decode_cascade(
                                  partition_tokens, nullptr, 0, nullptr, nullptr, false, &st,
                                  /*check_workspace=*/false);
   if (s != PKV_OK) return s;
-  if (st.kv == pkv::KvKind::F32)
-    return fail(PKV_ERR_UNSUPPORTED, "cascade decode supports bf16 and int8 caches only");
+  if (st.kv == pkv::KvKind::F32 || st.kv == pkv::KvKind::I4)
+    return fail(PKV_ERR_UNSUPPORTED, "cascade decode supports bf16, int8 and FP8 caches only");
   CascadeSizes cs;
   s = cascade_sizes(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq, num_groups,
                     max_group_size, max_shared_blocks, partition_tokens, prefix_partition_tokens, &cs);
@@ -620,18 +632,18 @@ pkv_status pkv_copy_blocks(void* dst_k, void* dst_v, float* dst_k_scale, float* 
   if (!head_dim_ok(head_dim)) return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: head_dim %d not in {64, 128}", head_dim);
   if (!block_size_ok(block_size))
     return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block_size %d not in {16, 32}", block_size);
-  int64_t elem;
-  const bool coded = dtype == PKV_I8 || dtype == PKV_FP8;
-  if (dtype == PKV_F32) elem = 4;
-  else if (dtype == PKV_BF16) elem = 2;
-  else if (coded) elem = 1;
-  else return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: unknown dtype %d", static_cast<int>(dtype));
+  int64_t tile_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim;  // per element byte
+  const bool coded = dtype == PKV_I8 || dtype == PKV_FP8 || dtype == PKV_I4;
+  if (dtype == PKV_F32) tile_bytes *= 4;
+  else if (dtype == PKV_BF16) tile_bytes *= 2;
+  else if (dtype == PKV_I4) tile_bytes /= 2;  // two codes per byte
+  else if (!coded) return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: unknown dtype %d", static_cast<int>(dtype));
   if (n > 65535) return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: at most 65535 pairs per call");
   if (n == 0) return ok();
   if (!dst_k || !dst_v || !src_k || !src_v || !pairs)
     return fail(PKV_ERR_INVALID, "copy_blocks: null pointer among the pools and pairs");
   if (coded && (!dst_k_scale || !dst_v_scale || !src_k_scale || !src_v_scale))
-    return fail(PKV_ERR_INVALID, "copy_blocks: int8 / FP8 pools need all four scale pointers");
+    return fail(PKV_ERR_INVALID, "copy_blocks: int8 / FP8 / INT4 pools need all four scale pointers");
   if (!coded && (dst_k_scale || dst_v_scale || src_k_scale || src_v_scale))
     return fail(PKV_ERR_INVALID, "copy_blocks: scale pointers must be NULL for fp32 / bf16 pools");
   // every pool must be device memory or host memory the device can address
@@ -665,7 +677,7 @@ pkv_status pkv_copy_blocks(void* dst_k, void* dst_v, float* dst_k_scale, float* 
   }
   p.pairs = pairs;
   p.num_pairs = n;
-  p.tile_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem;
+  p.tile_bytes = tile_bytes;
   p.scale_bytes = coded ? static_cast<int64_t>(num_kv_heads) * block_size * 4 : 0;
   const hipError_t e = pkv::launch_copy_blocks(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "copy_blocks launch failed: %s", hipGetErrorString(e));
@@ -702,7 +714,7 @@ pkv_status pkv_paged_attention_multi_query(
                                  block_size, max_blocks_per_seq, num_blocks, q_dtype, kv_dtype, 0,
                                  nullptr, 0, nullptr, nullptr, false, &st, /*check_workspace=*/false);
   if (s != PKV_OK) return s;
-  if (st.kv == pkv::KvKind::F32)
+  if (st.kv == pkv::KvKind::F32 || st.kv == pkv::KvKind::I4)
     return fail(PKV_ERR_UNSUPPORTED, "multi-query attention supports bf16, int8 and FP8 caches only");
   MqSizes ms;
   s = mq_sizes(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq, num_query_tokens,

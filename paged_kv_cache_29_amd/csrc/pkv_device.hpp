@@ -43,12 +43,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// int8 code of x for a row scale s = absmax / 127 (IEEE fp32 division, round
-// half to even, clamp to +-127); s == 0 means an all-zero (or underflowed)
-// row and gives 0.  Used by every int8 writer so their codes agree bit for bit.
-__device__ __forceinline__ int quantize_code(float x, float s) {
+// Symmetric integer code of x for a row scale s = absmax / MAXC (IEEE fp32
+// division, round half to even, clamp to +-MAXC); s == 0 means an all-zero
+// (or underflowed) row and gives 0.  MAXC is 127 for int8 and 7 for INT4.
+// Used by every writer of those caches so their codes agree bit for bit.
+template <int MAXC>
+__device__ __forceinline__ int quantize_sym(float x, float s) {
   if (!(s > 0.f)) return 0;
-  return static_cast<int>(fminf(fmaxf(rintf(x / s), -127.f), 127.f));
+  return static_cast<int>(fminf(fmaxf(rintf(x / s), -static_cast<float>(MAXC)), static_cast<float>(MAXC)));
+}
+__device__ __forceinline__ int quantize_code(float x, float s) { return quantize_sym<127>(x, s); }
+
+// Byte of two INT4 codes: lo in bits 0..3, hi in bits 4..7, two's complement.
+__device__ __forceinline__ uint32_t pack_int4_pair(int lo, int hi) {
+  return (static_cast<uint32_t>(lo) & 0xfu) | ((static_cast<uint32_t>(hi) & 0xfu) << 4);
 }
 
 // FP8 code of x for scale s: x / s (IEEE fp32 division) rounded to the

@@ -74,7 +74,9 @@ struct WriteParams {
   int32_t block_size;
 };
 
-enum class KvKind { F32 = 0, BF16 = 1, I8 = 2, FP8 = 3 };
+// I4: two 4-bit codes per byte, two consecutive head dims of one token
+// (K tiles [bs][D/2], V tiles [D/2][bs]).
+enum class KvKind { F32 = 0, BF16 = 1, I8 = 2, FP8 = 3, I4 = 4 };
 
 // Whole-block copies between two pools: parts 0..3 are the K tiles, the V
 // tiles, the K scale rows and the V scale rows of a block (tile_bytes,
@@ -130,7 +132,7 @@ hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group
 // sequence's context for up to max_queries new tokens per sequence.
 hipError_t launch_multi_query(const DecodeParams& p, KvKind kv, int max_queries, hipStream_t s);
 hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
-// Quantising write of fp32 rows into an int8 or FP8 cache (kind I8 or FP8).
+// Quantising write of fp32 rows into an int8, FP8 or INT4 cache.
 hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t s);
 hipError_t launch_tile_read(const void* pool, const int32_t* ids, int64_t ntiles, int grid,

@@ -24,6 +24,7 @@ id     name                   shape
                               fp32 N(0,1) K/V to be quantised to int8
 6      fp8_gqa70b             the same shape and draws, quantised to FP8
                               (E4M3) instead
+7      int4_gqa70b            the same shape and draws, quantised to INT4
 =====  =====================  =============================================
 
 Draw order with ``numpy.random.default_rng(seed)`` (PCG64): lengths, the
@@ -37,9 +38,9 @@ Layouts: ``k_cache[NB, Hkv, bs, D]``, ``v_cache[NB, Hkv, D, bs]``,
 ``q[B, H, D]``, ``block_tables[B, MB]`` int32 (-1 past the last block),
 ``context_lens[B]`` int32, slots int64.  bf16 arrays hold uint16 bit
 patterns.  Unused blocks, unused rows and the new-token slots hold NaN.
-For the int8 and FP8 workloads the pool is not materialised: ``k_fill`` / ``v_fill``
-``[T, Hkv, D]`` fp32 with ``slot_fill`` list every cached token but the new
-ones, for the consumer to quantise into its own int8 / FP8 cache (per sequence in
+For the int8, FP8 and INT4 workloads the pool is not materialised: ``k_fill`` /
+``v_fill`` ``[T, Hkv, D]`` fp32 with ``slot_fill`` list every cached token but the
+new ones, for the consumer to quantise into its own coded cache (per sequence in
 order; with a shared prefix, once per distinct slot instead).
 
 A shared prefix (``prefix`` tokens) is held by every sequence, or by each
@@ -55,6 +56,7 @@ import numpy as np
 from .blocks import BlockAllocator
 
 BF16_NAN = np.uint16(0x7FC0)
+CODED_KINDS = ("i8", "fp8", "i4")  # caches of codes with per-(token, kv-head) scales
 _CHUNK = 1 << 24  # elements drawn per RNG call when filling large pools
 
 
@@ -71,7 +73,7 @@ def bf16_bits(x):
 class Workload:
     name: str
     seed: int
-    kv_dtype: str            # "f32" | "bf16" | "i8" | "fp8"
+    kv_dtype: str            # "f32" | "bf16" | "i8" | "fp8" | "i4"
     q_dtype: str             # "f32" | "bf16"
     num_heads: int
     num_kv_heads: int
@@ -88,7 +90,7 @@ class Workload:
     slot_new: np.ndarray
     k_cache: np.ndarray = None   # f32 / bf16 pools
     v_cache: np.ndarray = None
-    k_fill: np.ndarray = None    # i8 / fp8 workload: fp32 rows of every cached token
+    k_fill: np.ndarray = None    # i8 / fp8 / i4 workload: fp32 rows of every cached token
     v_fill: np.ndarray = None
     slot_fill: np.ndarray = None
     meta: dict = field(default_factory=dict)
@@ -197,7 +199,7 @@ def build(name, seed, lens, num_heads, num_kv_heads, head_dim, block_size,
         context_lens=lens.astype(np.int32), block_tables=tables, q=q,
         k_new=None, v_new=None, slot_new=new_slots, meta=dict(meta or {}))
     w.meta.update(prefix=prefix, copies=list(alloc.copies), prefix_group_size=prefix_group_size)
-    if kv_dtype in ("i8", "fp8") and prefix:
+    if kv_dtype in CODED_KINDS and prefix:
         # shared blocks: fp32 pools as for bf16 (copy-on-write duplicates
         # included), then one fill row per distinct used slot
         k_pool = _draw(rng, (num_blocks, Hkv, bs, D), "f32")
@@ -220,7 +222,7 @@ def build(name, seed, lens, num_heads, num_kv_heads, head_dim, block_size,
             v_cache[dst, :, :, :rows] = v_cache[src, :, :, :rows]
         _poison(alloc, k_cache, v_cache, new_slots[new_slots >= 0], store)
         w.k_cache, w.v_cache = k_cache, v_cache
-    elif kv_dtype in ("i8", "fp8"):
+    elif kv_dtype in CODED_KINDS:
         w.meta["fill_per_sequence"] = True
         slot_fill = np.concatenate(fill_slots) if fill_slots else np.empty(0, np.int64)
         T = len(slot_fill)
@@ -241,11 +243,12 @@ CONFIG_NAMES = {
     4: "prefix_bf16",
     5: "int8_gqa70b",
     6: "fp8_gqa70b",
+    7: "int4_gqa70b",
 }
 
 
 def make_config(config, seed=0, block_size=None):
-    """The five workloads listed in the module docstring."""
+    """The workloads listed in the module docstring."""
     rng = np.random.default_rng(seed)
     if config == 1:
         return build("tiny_f32", seed, [47, 200, 16, 1], 4, 4, 64, 16, "f32", "f32",
@@ -269,6 +272,9 @@ def make_config(config, seed=0, block_size=None):
                      num_blocks=32768 + 4096, rng=rng)
     if config == 6:
         return build("fp8_gqa70b", seed, [8192] * 64, 64, 8, 128, 16, "fp8", "bf16",
+                     num_blocks=32768 + 4096, rng=rng)
+    if config == 7:
+        return build("int4_gqa70b", seed, [8192] * 64, 64, 8, 128, 16, "i4", "bf16",
                      num_blocks=32768 + 4096, rng=rng)
     raise ValueError(f"unknown config {config}")
 

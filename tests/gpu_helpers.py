@@ -12,11 +12,21 @@ import torch
 import oracle
 from oracle import cache as ocache
 from oracle import fp8 as ofp8
+from oracle import int4 as oint4
 import paged_kv_cache_29_amd as pkv
 from paged_kv_cache_29_amd import blocks, workloads
 
 DEV = torch.device("cuda:0")
-CODED = ("i8", "fp8")  # caches of byte codes with per-(token, kv-head) scales
+CODED = ("i8", "fp8", "i4")  # caches of codes with per-(token, kv-head) scales
+# torch element type of a coded cache, and its quantising write
+CODE_DTYPE = {"i8": torch.int8, "fp8": torch.float8_e4m3fn, "i4": torch.uint8}
+CODE_WRITE = {"i8": "kv_cache_write_int8", "fp8": "kv_cache_write_fp8", "i4": "kv_cache_write_int4"}
+
+
+def code_tile_shapes(kind, NB, Hkv, bs, D):
+    """Shapes of a coded cache's K and V pools (INT4 packs two dims per byte)."""
+    w = D // 2 if kind == "i4" else D
+    return (NB, Hkv, bs, w), (NB, Hkv, w, bs)
 
 
 def to_torch(arr, kind):
@@ -55,9 +65,10 @@ class DeviceWorkload:
         self.k_scale = self.v_scale = None
         if w.kv_dtype in CODED:
             NB, Hkv, bs, D = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
-            cd = torch.int8 if w.kv_dtype == "i8" else torch.float8_e4m3fn
-            self.k_cache = torch.zeros((NB, Hkv, bs, D), dtype=torch.uint8, device=DEV).view(cd)
-            self.v_cache = torch.zeros((NB, Hkv, D, bs), dtype=torch.uint8, device=DEV).view(cd)
+            cd = CODE_DTYPE[w.kv_dtype]
+            ks_, vs_ = code_tile_shapes(w.kv_dtype, NB, Hkv, bs, D)
+            self.k_cache = torch.zeros(ks_, dtype=torch.uint8, device=DEV).view(cd)
+            self.v_cache = torch.zeros(vs_, dtype=torch.uint8, device=DEV).view(cd)
             fill = float("nan") if poison_int8 else 0.0
             self.k_scale = torch.full((NB, Hkv, bs), fill, dtype=torch.float32, device=DEV)
             self.v_scale = torch.full((NB, Hkv, bs), fill, dtype=torch.float32, device=DEV)
@@ -70,11 +81,11 @@ class DeviceWorkload:
         self.out = torch.empty_like(self.q)
 
     def _write_codes(self, k, v, slots):
-        fn = pkv.kv_cache_write_int8 if self.w.kv_dtype == "i8" else pkv.kv_cache_write_fp8
+        fn = getattr(pkv, CODE_WRITE[self.w.kv_dtype])
         fn(k, v, self.k_cache, self.v_cache, self.k_scale, self.v_scale, slots)
 
     def fill_int8(self):
-        """Quantise and write every cached (non-new) token of an int8 / FP8 workload."""
+        """Quantise and write every cached (non-new) token of a coded workload."""
         self._write_codes(self.k_fill, self.v_fill, self.slot_fill)
 
     def write_new(self):
@@ -145,7 +156,7 @@ class DeviceWorkload:
 
 
 def oracle_caches(w, seqs=None):
-    """The oracle's cache after the step's writes (int8 / FP8: fill + new tokens).
+    """The oracle's cache after the step's writes (coded: fill + new tokens).
 
     ``seqs`` restricts an int8 fill to those sequences' tokens (enough for
     sampled checks of their outputs).
@@ -155,9 +166,11 @@ def oracle_caches(w, seqs=None):
                                   w.block_size) + (None, None)
     NB, Hkv, bs, D = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
     code_t = np.int8 if w.kv_dtype == "i8" else np.uint8
-    write = ocache.cache_write_int8 if w.kv_dtype == "i8" else ofp8.cache_write_fp8
-    kc = np.zeros((NB, Hkv, bs, D), code_t)
-    vc = np.zeros((NB, Hkv, D, bs), code_t)
+    write = {"i8": ocache.cache_write_int8, "fp8": ofp8.cache_write_fp8,
+             "i4": oint4.cache_write_int4}[w.kv_dtype]
+    kshape, vshape = code_tile_shapes(w.kv_dtype, NB, Hkv, bs, D)
+    kc = np.zeros(kshape, code_t)
+    vc = np.zeros(vshape, code_t)
     ks = np.full((NB, Hkv, bs), np.nan, np.float32)
     vs = np.full((NB, Hkv, bs), np.nan, np.float32)
     if not w.meta.get("fill_per_sequence", True):  # one row per distinct slot

@@ -18,7 +18,7 @@ HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.j
            if f.endswith(".h")]
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
-F32, BF16, I8 = range(3)
+F32, BF16, I8, FP8, I4 = range(5)
 
 
 def declared_functions():
@@ -84,6 +84,8 @@ def _decode(lib, **over):
     (dict(q_dtype=BF16, kv_dtype=F32), UNSUPPORTED, "not supported"),
     (dict(q_dtype=F32, kv_dtype=I8), UNSUPPORTED, "not supported"),
     (dict(kv_dtype=I8), INVALID, "k_scale"),
+    (dict(kv_dtype=I4), INVALID, "k_scale"),
+    (dict(q_dtype=F32, kv_dtype=I4), UNSUPPORTED, "not supported"),
     (dict(k_scale=_fake(7)), INVALID, "must be NULL"),
     (dict(partition_tokens=48), INVALID, "partition_tokens"),
     (dict(partition_tokens=16), INVALID, "partition_tokens"),
@@ -171,6 +173,18 @@ def test_write_int8_rejects(lib):
     assert st == OK
 
 
+def test_write_int4_rejects(lib):
+    f = lib.pkv_kv_cache_write_int4
+    st = f(_fake(1), _fake(2), _fake(3), _fake(4), None, _fake(6), _fake(7), 4, 8, 128, 16, 8, None)
+    assert st == INVALID and b"scale" in lib.pkv_last_error()
+    st = f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), 4, 8, 96, 16, 8, None)
+    assert st == UNSUPPORTED
+    st = f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), 4, 8, 128, 8, 8, None)
+    assert st == UNSUPPORTED
+    st = f(None, None, None, None, None, None, None, 0, 8, 128, 16, 8, None)
+    assert st == OK
+
+
 def test_python_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load(str(tmp_path / "missing.so"))
@@ -204,7 +218,8 @@ def _cascade(lib, **over):
 
 
 @pytest.mark.parametrize("over,code,frag", [
-    (dict(q_dtype=F32, kv_dtype=F32), UNSUPPORTED, "bf16 and int8"),
+    (dict(q_dtype=F32, kv_dtype=F32), UNSUPPORTED, "bf16, int8 and FP8"),
+    (dict(kv_dtype=I4, k_scale=_fake(9), v_scale=_fake(10)), UNSUPPORTED, "bf16, int8 and FP8"),
     (dict(num_groups=0), INVALID, "num_groups"),
     (dict(num_groups=5), INVALID, "num_groups"),
     (dict(max_group_size=0), INVALID, "max_group_size"),
@@ -267,6 +282,7 @@ def _copy(lib, **over):
     (dict(pairs=None), INVALID, "null pointer"),
     (dict(src_v=None), INVALID, "null pointer"),
     (dict(dtype=I8), INVALID, "scale"),
+    (dict(dtype=I4), INVALID, "scale"),
     (dict(dst_ks=_fake(6)), INVALID, "NULL"),
     (dict(n=70000), UNSUPPORTED, "65535"),
 ])
@@ -294,6 +310,7 @@ def _mq(lib, **over):
 
 @pytest.mark.parametrize("over,code,frag", [
     (dict(q_dtype=F32, kv_dtype=F32), UNSUPPORTED, "bf16, int8 and FP8"),
+    (dict(kv_dtype=I4, k_scale=_fake(9), v_scale=_fake(10)), UNSUPPORTED, "bf16, int8 and FP8"),
     (dict(num_query_tokens=-1), INVALID, "num_query_tokens"),
     (dict(max_queries_per_seq=0), INVALID, "max_queries_per_seq"),
     (dict(max_queries_per_seq=21), INVALID, "max_queries_per_seq"),

@@ -1,0 +1,165 @@
+"""GPU: the INT4 cache write is bit-exact against the oracle, and the
+attention kernels read every 4-bit code (both nibbles, every value including
+-8, which the writer never produces) as its value.
+
+The INT4 attention paths also run through the generic parity tests (decode
+variants, fused step, block permutation, full-size workload)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import int4 as oint4
+import paged_kv_cache_29_amd as pkv
+from paged_kv_cache_29_amd import workloads
+
+from gpu_helpers import DEV, assert_parity, bf16_bits_of, out_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(rng, T, Hkv, D):
+    x = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    x *= np.exp(rng.uniform(-20, 20, size=(T, Hkv, 1))).astype(np.float32)
+    x[0, 0] = 0.0                                      # zero row
+    # absmax 7: the scale is exactly 1, so x / s are the values themselves:
+    # every midpoint between neighbouring codes (ties to even) and the ends
+    x[1, 0] = 0.0
+    x[1, 0, 0] = 7.0
+    mids = np.arange(-6.5, 7.0, 1.0, dtype=np.float32)
+    x[1, 0, 1:D] = np.resize(np.concatenate([mids, -mids, [-7.0, 6.9, -0.49, 0.51]]), D - 1)
+    x[2, 0] = np.float32(1e-44)                        # absmax / 7 underflows to 0
+    x[3, 0] = rng.standard_normal(D).astype(np.float32) * np.float32(1e-38)   # subnormal scale
+    return x
+
+
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 32), (128, 32), (64, 16)])
+def test_write_int4_bitexact(D, bs):
+    rng = np.random.default_rng(D * 5 + bs)
+    NB, Hkv, T = 24, 2, 300
+    k = _rows(rng, T, Hkv, D)
+    v = _rows(rng, T, Hkv, D)[::-1].copy()
+    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
+    slots[10:20] = -1
+    kc = np.full((NB, Hkv, bs, D // 2), 0xAB, np.uint8)   # untouched bytes must stay
+    vc = np.full((NB, Hkv, D // 2, bs), 0xAB, np.uint8)
+    ks = np.full((NB, Hkv, bs), np.nan, np.float32)
+    vs = np.full((NB, Hkv, bs), np.nan, np.float32)
+    rk, rv, rks, rvs = oint4.cache_write_int4(k, v, kc, vc, ks, vs, slots, bs)
+    dk, dv = torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV)
+    dks, dvs = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+    pkv.kv_cache_write_int4(to_dev(k, "f32"), to_dev(v, "f32"), dk, dv, dks, dvs,
+                            torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.cpu().numpy(), rk)
+    assert np.array_equal(dv.cpu().numpy(), rv)
+    assert np.array_equal(dks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
+    assert np.array_equal(dvs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
+    # the crafted row really hits ties of both parities and both ends
+    s1 = int(slots[1])
+    codes = oint4.unpack_int4(rk[s1 // bs, 0, s1 % bs])
+    assert {-7, 7, 6, -6}.issubset(set(codes.tolist()))
+
+
+def test_every_code_is_read_as_its_value():
+    """V tiles of random bytes (every nibble value in both positions), scale
+    1, q = 0: the softmax is exactly uniform over 16 tokens, so each output is
+    the mean of 16 codes, exact in fp32 and in bf16; the kernel's output must
+    equal it bit for bit.  A nibble read from the wrong position, with the
+    wrong sign or for the wrong dim changes some dimension's mean."""
+    bs, D, Hkv, H, L = 16, 128, 2, 8, 16
+    rng = np.random.default_rng(3)
+    NB = 4
+    vc = rng.integers(0, 256, size=(NB, Hkv, D // 2, bs)).astype(np.uint8)
+    kc = rng.integers(0, 256, size=(NB, Hkv, bs, D // 2)).astype(np.uint8)
+    ks = np.ones((NB, Hkv, bs), np.float32)
+    vs = np.ones((NB, Hkv, bs), np.float32)
+    tables = np.array([[2], [0], [3]], np.int32)
+    lens = np.array([L, L, L], np.int32)
+    q = np.zeros((3, H, D), np.uint16)                   # bf16 zeros
+    out = torch.empty((3, H, D), dtype=torch.bfloat16, device=DEV)
+    pkv.paged_attention_decode(out, to_dev(q, "bf16"), to_dev(kc, "u8"), to_dev(vc, "u8"),
+                               to_dev(tables, "i32"), to_dev(lens, "i32"), 0.1, H, Hkv, D, bs,
+                               k_scale=to_dev(ks, "f32"), v_scale=to_dev(vs, "f32"))
+    torch.cuda.synchronize()
+    got = bf16_bits_of(out)
+    codes = oint4.unpack_int4(vc, axis=2)               # [NB, Hkv, D, bs]
+    for b in range(3):
+        for h in range(H):
+            mean = codes[tables[b, 0], h // (H // Hkv)].astype(np.float64).sum(axis=1) / L
+            want = workloads.bf16_bits(mean.astype(np.float32))
+            assert np.array_equal(got[b, h], want), (b, h)
+
+
+@pytest.mark.parametrize("G,D,bs", [(1, 128, 16), (8, 128, 16), (4, 64, 32), (16, 128, 32), (2, 64, 16)])
+def test_random_bytes_every_code(G, D, bs):
+    """Caches of random bytes (codes -8 .. 7 in both nibbles, K and V) with
+    random scales, ragged lengths and split partitions, against the oracle."""
+    rng = np.random.default_rng(G * 7 + D + bs)
+    Hkv, H = 2, 2 * G
+    lens = [1, 17, 33, 100, 257, 700]
+    w = workloads.make_custom(40 + G, lens, H, Hkv, D, bs, kv_dtype="i4")
+    NB = w.num_blocks
+    kc = rng.integers(0, 256, size=(NB, Hkv, bs, D // 2)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(NB, Hkv, D // 2, bs)).astype(np.uint8)
+    ks = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
+    ref = oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, H, Hkv, D,
+                                  bs, "i4", "bf16", k_scale=ks, v_scale=vs)
+    for pt in (0, 64):
+        out = torch.empty((len(lens), H, D), dtype=torch.bfloat16, device=DEV)
+        pkv.paged_attention_decode(out, to_dev(w.q, "bf16"), to_dev(kc, "u8"), to_dev(vc, "u8"),
+                                   to_dev(w.block_tables, "i32"), to_dev(w.context_lens, "i32"),
+                                   w.scale, H, Hkv, D, bs, k_scale=to_dev(ks, "f32"),
+                                   v_scale=to_dev(vs, "f32"), partition_tokens=pt)
+        torch.cuda.synchronize()
+        assert_parity(out_f64(out), ref, "i4", f"random bytes G={G} D={D} bs={bs} pt={pt}")
+
+
+def test_offsets_cancel_with_one_signed_query():
+    """All-positive queries of large magnitude make the K offset term
+    (136 * sum q) large against the scores, and all-positive V codes make
+    the V offset large against the output: both must still cancel to the
+    oracle's tolerance."""
+    rng = np.random.default_rng(9)
+    G, Hkv, D, bs = 8, 2, 128, 16
+    H = G * Hkv
+    lens = [3000, 64, 1025]
+    w = workloads.make_custom(77, lens, H, Hkv, D, bs, kv_dtype="i4")
+    w.q = workloads.bf16_bits((np.abs(rng.standard_normal(w.q.shape)) * 3 + 1).astype(np.float32))
+    NB = w.num_blocks
+    kc = rng.integers(0, 256, size=(NB, Hkv, bs, D // 2)).astype(np.uint8)
+    # V nibbles 0 .. 7 only (codes >= 0)
+    vc = (rng.integers(0, 8, size=(NB, Hkv, D // 2, bs)) |
+          (rng.integers(0, 8, size=(NB, Hkv, D // 2, bs)) << 4)).astype(np.uint8)
+    ks = rng.uniform(0.002, 0.01, size=(NB, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0.5, 2.0, size=(NB, Hkv, bs)).astype(np.float32)
+    ref = oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, H, Hkv, D,
+                                  bs, "i4", "bf16", k_scale=ks, v_scale=vs)
+    out = torch.empty((len(lens), H, D), dtype=torch.bfloat16, device=DEV)
+    pkv.paged_attention_decode(out, to_dev(w.q, "bf16"), to_dev(kc, "u8"), to_dev(vc, "u8"),
+                               to_dev(w.block_tables, "i32"), to_dev(w.context_lens, "i32"),
+                               w.scale, H, Hkv, D, bs, k_scale=to_dev(ks, "f32"),
+                               v_scale=to_dev(vs, "f32"))
+    torch.cuda.synchronize()
+    assert_parity(out_f64(out), ref, "i4", "one-signed q and V")
+
+
+def test_cascade_and_multi_query_reject_int4():
+    w = workloads.make_custom(5, [40, 50], 8, 2, 128, 16, kv_dtype="i4")
+    NB = w.num_blocks
+    kc = torch.zeros((NB, 2, 16, 64), dtype=torch.uint8, device=DEV)
+    vc = torch.zeros((NB, 2, 64, 16), dtype=torch.uint8, device=DEV)
+    sc = torch.ones((NB, 2, 16), dtype=torch.float32, device=DEV)
+    q = to_dev(w.q, "bf16")
+    bt, cl = to_dev(w.block_tables, "i32"), to_dev(w.context_lens, "i32")
+    with pytest.raises(NotImplementedError):
+        pkv.paged_attention_multi_query(torch.empty_like(q), q, kc, vc, bt, cl,
+                                        torch.tensor([0, 1, 2], dtype=torch.int32, device=DEV),
+                                        w.scale, 8, 2, 128, 16, 1, k_scale=sc, v_scale=sc)
+    with pytest.raises(NotImplementedError):
+        pkv.paged_attention_decode_cascade(torch.empty_like(q), q, kc, vc, bt, cl,
+                                           torch.tensor([0, 2], dtype=torch.int32, device=DEV),
+                                           torch.tensor([1], dtype=torch.int32, device=DEV),
+                                           w.scale, 8, 2, 128, 16, 2, 1, k_scale=sc, v_scale=sc)
