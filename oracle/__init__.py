@@ -48,7 +48,8 @@ from .attention import (
     multi_query_attention,
 )
 from .cache import cache_write, quantize_int8, cache_write_int8
-from .fp8 import e4m3_decode, e4m3_encode, quantize_fp8, cache_write_fp8
+from .fp8 import (e4m3_decode, e4m3_encode, quantize_fp8, cache_write_fp8, e5m2_decode,
+                  e5m2_encode, quantize_fp8_e5m2, cache_write_fp8_e5m2)
 from .int4 import pack_int4, unpack_int4, quantize_int4, cache_write_int4
 from .closed_forms import kv_cache_bytes, decode_kv_bytes
 
@@ -69,6 +70,10 @@ __all__ = [
     "e4m3_encode",
     "quantize_fp8",
     "cache_write_fp8",
+    "e5m2_decode",
+    "e5m2_encode",
+    "quantize_fp8_e5m2",
+    "cache_write_fp8_e5m2",
     "pack_int4",
     "unpack_int4",
     "quantize_int4",

@@ -38,8 +38,8 @@ import numpy as np
 from . import fp8 as _fp8
 from . import int4 as _int4
 
-KV_DTYPES = ("f32", "bf16", "i8", "fp8", "i4")
-CODED = ("i8", "fp8", "i4")  # codes with one scale per (token, kv-head)
+KV_DTYPES = ("f32", "bf16", "i8", "fp8", "e5m2", "i4")
+CODED = ("i8", "fp8", "e5m2", "i4")  # codes with one scale per (token, kv-head)
 
 
 def n_blocks(context_len, block_size):
@@ -98,6 +98,8 @@ def widen(x, kind):
         return x.astype(np.int8).astype(np.float64)
     if kind == "fp8":
         return _fp8.e4m3_decode(x.astype(np.uint8))
+    if kind == "e5m2":
+        return _fp8.e5m2_decode(x.astype(np.uint8))
     raise ValueError(f"unknown element type {kind!r}")
 
 
@@ -161,7 +163,7 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
     ``v_cache[NB, Hkv, D, bs]``; ``block_tables[B, MB]``; ``context_lens[B]``;
     scales ``[NB, Hkv, bs]`` (int8, FP8, INT4; INT4 tiles hold two dims per
     byte).  ``q_dtype`` / ``kv_dtype`` name the stored element types ("f32",
-    "bf16", "i8", "fp8", "i4").
+    "bf16", "i8", "fp8" (E4M3), "e5m2", "i4").
 
     Returns ``out[B, H, D]`` in fp64.  With ``samples`` (an iterable of
     ``(b, h)`` pairs) only those rows are computed and the others are NaN.

@@ -597,6 +597,141 @@ def check_brute_force_fp8():
             np.testing.assert_allclose(out[b, h], ref, rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------- FP8 (E5M2) codes
+def check_e5m2_decode_closed_forms():
+    # 1.0 = 2^0: exponent field 15 -> 0x3C; largest finite 1.75 * 2^15;
+    # smallest normal 2^-14; smallest subnormal 2^-16; infinities; NaNs
+    want = {0x00: 0.0, 0x3C: 1.0, 0xBC: -1.0, 0x7B: 57344.0, 0xFB: -57344.0, 0x04: 2.0 ** -14,
+            0x01: 2.0 ** -16, 0x03: 3 * 2.0 ** -16, 0x3E: 1.5, 0x40: 2.0, 0x38: 0.5, 0x3D: 1.25,
+            0x7C: math.inf, 0xFC: -math.inf}
+    got = ofp8.e5m2_decode(np.array(list(want), np.uint8))
+    assert got.tolist() == list(want.values())
+    assert np.isnan(ofp8.e5m2_decode(np.array([0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF], np.uint8))).all()
+    pos = ofp8.e5m2_decode(np.arange(0x7C, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(ofp8.e5m2_decode(np.arange(0x80, 0xFC, dtype=np.uint8)), -pos)
+
+
+def check_e5m2_decode_torch():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    got = ofp8.e5m2_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got)) and np.array_equal(ref[~nan], got[~nan])
+
+
+def check_e5m2_encode_torch():
+    import torch
+    rng = np.random.default_rng(51)
+    v = np.concatenate([rng.standard_normal(100000).astype(np.float32) * np.float32(3000),
+                        rng.uniform(-57344, 57344, 100000).astype(np.float32),
+                        rng.standard_normal(50000).astype(np.float32) * np.float32(1e-4)])
+    ref = torch.from_numpy(v).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(ofp8.e5m2_encode(v), ref)
+
+
+def check_e5m2_encode_ties_and_saturation():
+    pos = ofp8.e5m2_decode(np.arange(0x7C, dtype=np.uint8))
+    for c in range(0x7B):
+        mid = np.float32((pos[c] + pos[c + 1]) / 2)
+        assert float(mid) == (pos[c] + pos[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert int(ofp8.e5m2_encode(mid)) == even, c
+        assert int(ofp8.e5m2_encode(-mid)) == 0x80 | even, c
+        assert int(ofp8.e5m2_encode(np.nextafter(mid, np.float32(0)))) == c
+        assert int(ofp8.e5m2_encode(np.nextafter(mid, np.float32(1e9)))) == c + 1
+    assert np.array_equal(ofp8.e5m2_encode(pos.astype(np.float32)), np.arange(0x7C, dtype=np.uint8))
+    # beyond the largest finite value: saturate, never the infinity code
+    assert ofp8.e5m2_encode(np.float32(61440.0)) == 0x7B
+    assert ofp8.e5m2_encode(np.float32(1e30)) == 0x7B and ofp8.e5m2_encode(np.float32(-1e30)) == 0xFB
+    assert ofp8.e5m2_encode(np.float32(-0.0)) == 0x80 and ofp8.e5m2_encode(np.float32(1e-30)) == 0
+
+
+def check_e5m2_quantizer_closed_forms():
+    rng = np.random.default_rng(52)
+    x = rng.standard_normal((400, 128)).astype(np.float32) * rng.uniform(1e-3, 1e3, (400, 1)).astype(np.float32)
+    q, s = ofp8.quantize_fp8_e5m2(x)
+    a = np.max(np.abs(x), axis=1)
+    i = np.argmax(np.abs(x), axis=1)
+    top = q[np.arange(400), i]
+    assert np.all((top == 0x7B) | (top == 0xFB))
+    assert np.all(np.abs(np.float32(57344) * s - a) <= 2 * np.spacing(a))
+    # reconstruction: half a mantissa step (2^-3 relative) for normal codes,
+    # half of 2^-16 * s for subnormal ones
+    val = ofp8.e5m2_decode(q) * s[:, None].astype(np.float64)
+    err = np.abs(x.astype(np.float64) - val)
+    bound = np.maximum(np.abs(x) * 2.0 ** -3, 2.0 ** -17 * s[:, None]) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    q0, s0 = ofp8.quantize_fp8_e5m2(np.zeros((1, 16), np.float32))
+    assert s0[0] == 0 and np.all(q0 == 0)
+
+
+def check_e5m2_write_brute():
+    rng = np.random.default_rng(53)
+    NB, Hkv, bs, D, T = 4, 2, 16, 16, 9
+    k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
+    v = (rng.standard_normal((T, Hkv, D)) * 1e-3).astype(np.float32)
+    k[2, 1] = 0.0
+    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
+    slots[4] = -1
+    kc = np.zeros((NB, Hkv, bs, D), np.uint8)
+    vc = np.zeros((NB, Hkv, D, bs), np.uint8)
+    ksc = np.full((NB, Hkv, bs), np.nan, np.float32)
+    vsc = np.full((NB, Hkv, bs), np.nan, np.float32)
+    k2, v2, ks2, vs2 = ofp8.cache_write_fp8_e5m2(k, v, kc, vc, ksc, vsc, slots, bs)
+    values = [ofp8.e5m2_value(c) for c in range(0x7C)]
+    for t, sl in enumerate(slots.tolist()):
+        if sl < 0:
+            continue
+        blk, r = sl // bs, sl % bs
+        for h in range(Hkv):
+            for src, codes, sc in ((k[t, h], k2[blk, h, r, :], ks2[blk, h, r]),
+                                   (v[t, h], v2[blk, h, :, r], vs2[blk, h, r])):
+                a = float(np.max(np.abs(src)))
+                sref = np.float32(np.float32(a) / np.float32(57344.0))
+                if a == 0:
+                    assert sc == 0 and np.all(codes == 0)
+                    continue
+                assert sc == sref
+                for d in range(D):
+                    ratio = float(np.float32(src[d] / sref))
+                    mag = min(abs(ratio), 57344.0)
+                    best = min(range(0x7C), key=lambda c: (abs(values[c] - mag), c % 2))
+                    want = best | (0x80 if ratio < 0 or (ratio == 0 and math.copysign(1, ratio) < 0) else 0)
+                    assert int(codes[d]) == want, (t, h, d, ratio)
+
+
+def check_brute_force_e5m2():
+    """E5M2 cache: value = E5M2 value of the code x per-token scale."""
+    rng = np.random.default_rng(54)
+    NB, Hkv, bs, D, H = 6, 2, 16, 8, 4
+    kc = (rng.integers(0, 0x7C, size=(NB, Hkv, bs, D)) |
+          (rng.integers(0, 2, size=(NB, Hkv, bs, D)) << 7)).astype(np.uint8)
+    vc = rng.integers(0, 0x7C, size=(NB, Hkv, D, bs)).astype(np.uint8)
+    ks = rng.uniform(1e-6, 2e-5, size=(NB, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(1e-6, 2e-5, size=(NB, Hkv, bs)).astype(np.float32)
+    tables = np.array([[4, 1, 0], [2, 5, -1]], dtype=np.int32)
+    lens = np.array([35, 20], dtype=np.int32)
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    out = oracle.decode_attention(q, kc, vc, tables, lens, 0.25, H, Hkv, D, bs, "e5m2", "f32",
+                                  k_scale=ks, v_scale=vs)
+    for b in range(2):
+        for h in range(H):
+            g = h // 2
+            sc, rows = [], []
+            for t in range(int(lens[b])):
+                blk, r = int(tables[b][t // bs]), t % bs
+                kr = [ofp8.e5m2_value(kc[blk, g, r, d]) * float(ks[blk, g, r]) for d in range(D)]
+                vr = [ofp8.e5m2_value(vc[blk, g, d, r]) * float(vs[blk, g, r]) for d in range(D)]
+                sc.append(0.25 * sum(float(q[b, h, d]) * kr[d] for d in range(D)))
+                rows.append(vr)
+            m = max(sc)
+            ps = [math.exp(x - m) for x in sc]
+            ref = [sum(p * vr[d] for p, vr in zip(ps, rows)) / sum(ps) for d in range(D)]
+            np.testing.assert_allclose(out[b, h], ref, rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------------- INT4 codes
 def check_int4_packing_worked_example():
     # two's complement nibbles, dim 2j in the low nibble, 2j + 1 in the high:
@@ -841,6 +976,13 @@ ALL_CHECKS = [
     check_fp8_quantizer_closed_forms,
     check_fp8_write_brute,
     check_brute_force_fp8,
+    check_e5m2_decode_closed_forms,
+    check_e5m2_decode_torch,
+    check_e5m2_encode_torch,
+    check_e5m2_encode_ties_and_saturation,
+    check_e5m2_quantizer_closed_forms,
+    check_e5m2_write_brute,
+    check_brute_force_e5m2,
     check_int4_packing_worked_example,
     check_int4_quantizer_ties_and_clamp,
     check_int4_quantizer_closed_forms,

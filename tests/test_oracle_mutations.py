@@ -219,6 +219,35 @@ def _gather_int4_no_v_scale(k_cache, v_cache, block_table, context_len, block_si
                         kv_dtype, k_scale, v_scale)
 
 
+_T5_BIAS16 = np.array([ofp8.e5m2_value(c) / 2.0 for c in range(256)])
+
+
+def _e5m2_encode_ties_away(v):
+    v = np.asarray(v, np.float32)
+    a = np.abs(v).astype(np.float64)
+    pos = ofp8.e5m2_decode(np.arange(0x7C, dtype=np.uint8))
+    hi = np.minimum(np.searchsorted(pos, a, side="left"), 0x7B)
+    lo = np.maximum(hi - 1, 0)
+    code = np.where(pos[hi] - a <= a - pos[lo], hi, lo)
+    code = np.where(a >= 57344.0, 0x7B, code)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def _e5m2_quant_over_448(x):
+    x = np.asarray(x, np.float32)
+    a = np.max(np.abs(x), axis=-1)
+    s = (a / np.float32(448)).astype(np.float32)
+    safe = np.where(a > 0, s, np.float32(1)).astype(np.float32)
+    c = np.where(a[..., None] > 0, ofp8.e5m2_encode((x / safe[..., None]).astype(np.float32)), 0)
+    return c.astype(np.uint8), np.where(a > 0, s, 0).astype(np.float32)
+
+
+def _widen_e5m2_as_e4m3(x, kind):
+    if kind == "e5m2":
+        return ofp8.e4m3_decode(np.asarray(x).astype(np.uint8))
+    return _orig_widen(x, kind)
+
+
 _orig_e4m3_encode = ofp8.e4m3_encode
 _orig_e4m3_decode = ofp8.e4m3_decode
 _orig_gather = oatt.gather_kv
@@ -248,6 +277,10 @@ MUTATIONS = {
     "fp8_truncate": [(ofp8, "e4m3_encode", _fp8_encode_truncate)],
     "fp8_scale_over_240": [(ofp8, "quantize_fp8", _fp8_quant_over_240)],
     "fp8_v_scale_dropped": [(oatt, "gather_kv", _gather_fp8_no_v_scale)],
+    "e5m2_exponent_bias_16": [(ofp8, "e5m2_decode", lambda c: _T5_BIAS16[np.asarray(c, np.uint8)])],
+    "e5m2_round_ties_away": [(ofp8, "e5m2_encode", _e5m2_encode_ties_away)],
+    "e5m2_scale_over_448": [(ofp8, "quantize_fp8_e5m2", _e5m2_quant_over_448)],
+    "e5m2_read_as_e4m3": [(oatt, "widen", _widen_e5m2_as_e4m3)],
     "int4_nibbles_swapped": [(oint4, "unpack_int4", _int4_unpack_swapped)],
     "int4_no_sign_extension": [(oint4, "unpack_int4", _int4_unpack_unsigned)],
     "int4_pack_high_first": [(oint4, "pack_int4", _int4_pack_swapped)],
