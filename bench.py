@@ -43,8 +43,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL_SOURCES = ["decode_mfma.hip", "decode_tile.hpp", "decode_append.hpp", "pkv_device.hpp",
                   "pkv_kernels.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.txt")
-CODED = ("i8", "fp8", "i4")  # caches of codes with per-(token, kv-head) scales
-CODE_BYTES = {"i8": 1.0, "fp8": 1.0, "i4": 0.5, "bf16": 2.0, "f32": 4.0}  # per element
+CODED = ("i8", "fp8", "e5m2", "i4")  # caches of codes with per-(token, kv-head) scales
+CODE_BYTES = {"i8": 1.0, "fp8": 1.0, "e5m2": 1.0, "i4": 0.5, "bf16": 2.0, "f32": 4.0}  # per element
 
 DESCRIPTIONS = {
     1: "tiny_f32: B=4 L={47,200,16,1} H=Hkv=4 D=64 bs=16 fp32",
@@ -54,6 +54,7 @@ DESCRIPTIONS = {
     5: "int8_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 int8 KV, bf16 q",
     6: "fp8_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 FP8 E4M3 KV, bf16 q",
     7: "int4_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 INT4 KV, bf16 q",
+    8: "e5m2_gqa70b: B=64 L=8192 H=64 Hkv=8 D=128 bs=16 FP8 E5M2 KV, bf16 q",
 }
 
 
@@ -102,11 +103,12 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
     slot = torch.from_numpy(w.slot_new).to(dev)
     k_new, v_new = up(w.k_new, store), up(w.v_new, store)
     ks = vs = None
-    write_codes = {"fp8": pkv.kv_cache_write_fp8, "i4": pkv.kv_cache_write_int4}.get(
-        w.kv_dtype, pkv.kv_cache_write_int8)
+    write_codes = {"fp8": pkv.kv_cache_write_fp8, "e5m2": pkv.kv_cache_write_fp8_e5m2,
+                   "i4": pkv.kv_cache_write_int4}.get(w.kv_dtype, pkv.kv_cache_write_int8)
     if w.kv_dtype in CODED:
         NB, Hkv, bs, D = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
-        cd = {"fp8": torch.float8_e4m3fn, "i4": torch.uint8}.get(w.kv_dtype, torch.int8)
+        cd = {"fp8": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2,
+              "i4": torch.uint8}.get(w.kv_dtype, torch.int8)
         Dw = D // 2 if w.kv_dtype == "i4" else D   # INT4: two dims per byte
         kc = torch.zeros((NB, Hkv, bs, Dw), dtype=torch.uint8, device=dev).view(cd)
         vc = torch.zeros((NB, Hkv, Dw, bs), dtype=torch.uint8, device=dev).view(cd)
@@ -483,7 +485,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "i8": "i8", "fp8": "fp8_e4m3", "i4": "i4", "f32": "f32"}[w.kv_dtype],
+        "dtype": {"bf16": "bf16", "i8": "i8", "fp8": "fp8_e4m3", "e5m2": "fp8_e5m2", "i4": "i4",
+                  "f32": "f32"}[w.kv_dtype],
         "data": "synthetic (seeded N(0,1) K/V/q, shuffled block tables)",
         "config": {"workload": head["workload"], "num_seqs": w.num_seqs,
                    "context_len": int(w.context_lens.max()), "num_heads": w.num_heads,

@@ -36,6 +36,7 @@
  *                                   element (token row r, dim d) at d*bs + r
  *   k_scale,
  *   v_scale      [NB][Hkv][bs] fp32 (int8, FP8 and INT4 caches only)
+ *   FP8 caches hold E4M3 codes (PKV_FP8) or E5M2 codes (PKV_FP8_E5M2).
  *   INT4 caches hold two codes per byte, two consecutive head dims of one
  *   token (dim 2j in the low nibble, 2j + 1 in the high nibble, 4-bit two's
  *   complement), so their tiles are k_cache [NB][Hkv][bs][D/2] and
@@ -80,8 +81,10 @@ typedef enum {
   PKV_I8 = 2,    /* int8 codes with an fp32 per-row scale */
   PKV_FP8 = 3,   /* FP8 E4M3 codes (OCP: bias 7, largest finite 448, no
                     infinities) with an fp32 per-row scale              */
-  PKV_I4 = 4     /* INT4 codes in [-7, 7], two per byte (layout above),
+  PKV_I4 = 4,    /* INT4 codes in [-7, 7], two per byte (layout above),
                     with an fp32 per-row scale                          */
+  PKV_FP8_E5M2 = 5 /* FP8 E5M2 codes (bias 15, largest finite 57344) with
+                      an fp32 per-row scale                             */
 } pkv_dtype;
 
 /*
@@ -138,6 +141,20 @@ pkv_status pkv_kv_cache_write_fp8(const float* k, const float* v, uint8_t* k_cac
                                   int64_t num_blocks, void* stream);
 
 /*
+ * Quantising cache write for an FP8 KV cache in the E5M2 format (the other
+ * common FP8 encoding; [ENG5] "KV-cache quantization").
+ *   As pkv_kv_cache_write_fp8 with s = a / 57344 (IEEE fp32 division) and
+ *   code_d = the finite E5M2 code nearest to x_d / s (ties to the even
+ *   code; +-57344 at most, never an infinity; the sign of a zero is kept).
+ *   Bit-exact.  Errors as for pkv_kv_cache_write_int8.
+ */
+pkv_status pkv_kv_cache_write_fp8_e5m2(const float* k, const float* v, uint8_t* k_cache,
+                                       uint8_t* v_cache, float* k_scale, float* v_scale,
+                                       const int64_t* slot_mapping, int64_t num_tokens,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int64_t num_blocks, void* stream);
+
+/*
  * Quantising cache write for an INT4 KV cache ([ENG5] "KV-cache
  * quantization": INT4 KV caches calibrated per token, with per-token-per-
  * head scales; [LAYERS] 2.3: K and V quantized separately).
@@ -184,13 +201,13 @@ int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_he
  *   For each sequence b with L = context_lens[b] and query head h (kv-head
  *   g = h / G), with K_b, V_b the L tokens gathered through the block table:
  *     out[b][h][:] = softmax(scale * K_b q[b][h]) V_b,  accumulated in fp32;
- *   L == 0 gives zeros.  For an int8, FP8 or INT4 cache each K/V element's
- *   value is its code times the token's scale.
+ *   L == 0 gives zeros.  For an int8, FP8 (E4M3 or E5M2) or INT4 cache each
+ *   K/V element's value is its code times the token's scale.
  * Supported: (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16), (BF16, I8),
- * (BF16, FP8), (BF16, I4)};
+ * (BF16, FP8), (BF16, FP8_E5M2), (BF16, I4)};
  * out has q's dtype; head_dim in {64, 128}; block_size in {16, 32};
- * G in {1, 2, 4, 8, 16}.  k_scale and v_scale are required for I8, FP8 and
- * I4 and must be NULL otherwise.  num_seqs == 0 is a no-op.  scale must be finite.
+ * G in {1, 2, 4, 8, 16}.  k_scale and v_scale are required for the coded
+ * caches (I8, FP8, FP8_E5M2, I4) and must be NULL otherwise.  num_seqs == 0 is a no-op.  scale must be finite.
  * partition_tokens: 0 for the automatic choice, else a multiple of 32 in
  * [32, 128 * block_size]; long contexts are split into partitions of that
  * many tokens whose partial results a second kernel combines.
@@ -246,7 +263,7 @@ pkv_status pkv_paged_attention_decode_reduce(
  *   the workgroups of the partition holding position L - 1 write the token
  *   before attending, and nothing else reads it.
  *   k_new, v_new: [B][Hkv][D], the cache element type (fp32 or bf16), or
- *   fp32 for an int8, FP8 or INT4 cache (quantised in the kernel).  The block holding
+ *   fp32 for a coded cache (quantised in the kernel).  The block holding
  *   position L - 1 must belong to this sequence alone (copy it on write
  *   first if it is shared).  Other arguments, errors and the workspace as
  *   for pkv_paged_attention_decode; the caches (and int8 scales) are
@@ -297,8 +314,8 @@ pkv_status pkv_paged_attention_decode_step_partitions(
  *   prefix_partition_tokens: tokens of the shared span per workgroup; 0 for
  *   the automatic choice, else a multiple of 32 in [32, 128 * block_size].
  *   partition_tokens as for decode (for the remaining tokens).
- * Supported: (BF16, BF16), (BF16, I8) and (BF16, FP8) with the sizes of decode; an fp32
- * or INT4 cache returns PKV_ERR_UNSUPPORTED.  The workspace size comes from
+ * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8) and (BF16, FP8_E5M2) with the
+ * sizes of decode; an fp32 or INT4 cache returns PKV_ERR_UNSUPPORTED.  The workspace size comes from
  * pkv_paged_attention_cascade_workspace_size with the same sizes and is
  * needed whenever num_seqs > 0.  Three launches: prefix kernel (skipped when
  * max_shared_blocks is 0), partition kernel, reduce.
@@ -340,8 +357,8 @@ size_t pkv_paged_attention_cascade_workspace_size(
  * query_start: device int32 [num_seqs + 1], query_start[0] = 0,
  * non-decreasing, query_start[num_seqs] = num_query_tokens.
  * max_queries_per_seq: host bound on every n_b, in [1, num_query_tokens].
- * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8) with decode's sizes (an
- * fp32 or INT4 cache returns PKV_ERR_UNSUPPORTED).
+ * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8), (BF16, FP8_E5M2) with
+ * decode's sizes (an fp32 or INT4 cache returns PKV_ERR_UNSUPPORTED).
  * partition_tokens: 0 for the automatic choice, else as for decode.
  * Workspace: pkv_paged_attention_multi_query_workspace_size(...) bytes,
  * 256-byte aligned, whenever num_query_tokens > 0.  Two launches (partials

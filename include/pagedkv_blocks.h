@@ -122,8 +122,8 @@ pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq, int32_t* pairs, in
  * Pools may be the same (copy-on-write) or one of them pinned host memory
  * the device can address (swapping; e.g. hipHostMalloc'd, the kernel reads
  * or writes it over the host link).  pairs: device int32 [n][2].
- *   dtype: PKV_F32, PKV_BF16, PKV_I8, PKV_FP8 or PKV_I4; scale pointers
- *   required for I8 / FP8 / I4 and NULL otherwise.  n >= 0 (0: no launch).
+ *   dtype: PKV_F32, PKV_BF16, PKV_I8, PKV_FP8, PKV_FP8_E5M2 or PKV_I4;
+ *   scale pointers required for the coded kinds and NULL otherwise.  n >= 0 (0: no launch).
  * Not checked (device data): block ids inside their pools; no destination
  * block written twice, none both read and written by one call.
  */

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     kv_cache_write,
     kv_cache_write_int8,
     kv_cache_write_fp8,
+    kv_cache_write_fp8_e5m2,
     kv_cache_write_int4,
     cascade_workspace_size,
     paged_attention_decode,

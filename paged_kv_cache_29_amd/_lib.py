@@ -16,12 +16,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP, PKV_ERR_NO_BLOCKS = range(6)
-PKV_F32, PKV_BF16, PKV_I8, PKV_FP8, PKV_I4 = range(5)
+PKV_F32, PKV_BF16, PKV_I8, PKV_FP8, PKV_I4, PKV_FP8_E5M2 = range(6)
 
 # INT4 caches are uint8 tensors holding two codes per byte
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.int8: PKV_I8,
-           torch.float8_e4m3fn: PKV_FP8, torch.uint8: PKV_I4}
-_CODED = (PKV_I8, PKV_FP8, PKV_I4)  # codes with per-(token, kv-head) scales
+           torch.float8_e4m3fn: PKV_FP8, torch.float8_e5m2: PKV_FP8_E5M2, torch.uint8: PKV_I4}
+_CODED = (PKV_I8, PKV_FP8, PKV_FP8_E5M2, PKV_I4)  # codes with per-(token, kv-head) scales
 
 
 def _tile_shapes(kd, Hkv, bs, D):
@@ -47,6 +47,8 @@ SIGNATURES = {
                                        c_i32, c_i32, c_i64, c_vp]),
     "pkv_kv_cache_write_int8": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32,
                                         c_i32, c_i32, c_i64, c_vp]),
+    "pkv_kv_cache_write_fp8_e5m2": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32,
+                                            c_i32, c_i32, c_i64, c_vp]),
     "pkv_kv_cache_write_int4": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i32,
                                         c_i32, c_i32, c_i64, c_vp]),
     "pkv_paged_attention_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
@@ -177,6 +179,13 @@ def kv_cache_write_fp8(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping):
     scatter; the caches are ``torch.float8_e4m3fn`` tensors."""
     _write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, torch.float8_e4m3fn,
                  "pkv_kv_cache_write_fp8")
+
+
+def kv_cache_write_fp8_e5m2(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping):
+    """Quantise fp32 K/V rows to FP8 in the E5M2 format + per-(token,
+    kv-head) scale and scatter; the caches are ``torch.float8_e5m2``."""
+    _write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, torch.float8_e5m2,
+                 "pkv_kv_cache_write_fp8_e5m2")
 
 
 def kv_cache_write_int4(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping):

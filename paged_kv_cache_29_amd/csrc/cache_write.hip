@@ -14,7 +14,8 @@
 // quantization"; four-layer inference-optimization article, 2.3).
 // kv_cache_write_fp8 does the same with s = absmax / 448 and the nearest
 // OCP E4M3 code of x / s (the same section's FP8 KV caches).
-// kv_cache_write_int4 uses s = absmax / 7 and codes clamp(rint(x / s), -7, 7),
+// kv_cache_write_fp8_e5m2 does the same with the E5M2 format (s = absmax /
+// 57344).  kv_cache_write_int4 uses s = absmax / 7 and codes clamp(rint(x / s), -7, 7),
 // stored two per byte (two consecutive head dims of one token, the lower dim
 // in the low nibble, 4-bit two's complement); no byte holds two tokens, so
 // tokens are written independently.  This
@@ -63,8 +64,9 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
 
 // One lane group of D/4 lanes per (token, kv-head, K-or-V) row, 4 values per
 // lane; rows alternate K, V.
-// KV: I8 (s = absmax / 127, quantize_code), FP8 (s = absmax / 448, fp8_code)
-// or I4 (s = absmax / 7, quantize_sym<7>, tiles of half the bytes).
+// KV: I8 (s = absmax / 127, quantize_code), FP8 (s = absmax / 448, fp8_code),
+// E5M2 (s = absmax / 57344, e5m2_code) or I4 (s = absmax / 7,
+// quantize_sym<7>, tiles of half the bytes).
 template <KvKind KV>
 __global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
   const int D = p.head_dim;
@@ -95,7 +97,10 @@ __global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
     float a = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
     for (int o = group / 2; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
     if (slot < 0) continue;
-    const float s = a / (KV == KvKind::FP8 ? 448.0f : (KV == KvKind::I4 ? 7.0f : 127.0f));
+    const float s = a / (KV == KvKind::FP8    ? 448.0f
+                         : KV == KvKind::E5M2 ? 57344.0f
+                         : KV == KvKind::I4   ? 7.0f
+                                              : 127.0f);
     const int64_t blk = slot / BS;
     const int row = static_cast<int>(slot - blk * BS);
     const int d0 = 4 * sub;
@@ -118,7 +123,9 @@ __global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
     uint32_t codes[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      codes[e] = KV == KvKind::FP8 ? fp8_code(x[e], s) : static_cast<uint32_t>(quantize_code(x[e], s));
+      codes[e] = KV == KvKind::FP8    ? fp8_code(x[e], s)
+                 : KV == KvKind::E5M2 ? e5m2_code(x[e], s)
+                                      : static_cast<uint32_t>(quantize_code(x[e], s));
     const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * D;
     if (!is_v) {
       const uint32_t packed = (codes[0] & 0xffu) | ((codes[1] & 0xffu) << 8) |
@@ -162,6 +169,8 @@ hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream
     hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::FP8>, dim3(grid), dim3(256), 0, s, p);
   else if (kind == KvKind::I4)
     hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::I4>, dim3(grid), dim3(256), 0, s, p);
+  else if (kind == KvKind::E5M2)
+    hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::E5M2>, dim3(grid), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::I8>, dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -420,6 +420,7 @@ template <bool kMQ>
 hipError_t launch_mode(const DecodeParams& p, KvKind kv, int units, int max_rows, int parts, hipStream_t s) {
   if (kv == KvKind::I8) return launch_kv<KvKind::I8, kMQ>(p, units, max_rows, parts, s);
   if (kv == KvKind::FP8) return launch_kv<KvKind::FP8, kMQ>(p, units, max_rows, parts, s);
+  if (kv == KvKind::E5M2) return launch_kv<KvKind::E5M2, kMQ>(p, units, max_rows, parts, s);
   return launch_kv<KvKind::BF16, kMQ>(p, units, max_rows, parts, s);
 }
 

@@ -18,8 +18,8 @@
 namespace pkv {
 
 // Called by all threads of a workgroup of at least 2 * D threads (and at
-// least two waves); pos = L - 1 >= 0.  KV: F32 or BF16 (bit copy), I8, FP8
-// or I4 (quantised from fp32 rows).
+// least two waves); pos = L - 1 >= 0.  KV: F32 or BF16 (bit copy), I8, FP8,
+// E5M2 or I4 (quantised from fp32 rows).
 template <KvKind KV, int D, int BS>
 __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, int kvh, int pos) {
   using KT = typename std::conditional<
@@ -57,7 +57,7 @@ __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, i
         sc[(static_cast<size_t>(blk) * Hkv + kvh) * BS + row] = (s > 0.f) ? s : 0.f;
       }
     }
-  } else if constexpr (KV == KvKind::I8 || KV == KvKind::FP8) {
+  } else if constexpr (KV == KvKind::I8 || KV == KvKind::FP8 || KV == KvKind::E5M2) {
     // wave 0 quantises the K row, wave 1 the V row; lane owns dims lane + 64i
     constexpr int ND = D / kWave;
     const int wave = t / kWave;
@@ -72,12 +72,13 @@ __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, i
         a = fmaxf(a, fabsf(v[i]));
       }
       a = wave_max(a);
-      const float s = a / (KV == KvKind::FP8 ? 448.0f : 127.0f);
+      const float s = a / (KV == KvKind::FP8 ? 448.0f : (KV == KvKind::E5M2 ? 57344.0f : 127.0f));
 #pragma unroll
       for (int i = 0; i < ND; ++i) {
         const int d = lane + kWave * i;
-        const KT code = KV == KvKind::FP8 ? static_cast<KT>(fp8_code(v[i], s))
-                                          : static_cast<KT>(quantize_code(v[i], s));
+        const KT code = KV == KvKind::FP8    ? static_cast<KT>(fp8_code(v[i], s))
+                        : KV == KvKind::E5M2 ? static_cast<KT>(e5m2_code(v[i], s))
+                                             : static_cast<KT>(quantize_code(v[i], s));
         if (wave == 0)
           kc[tile + static_cast<size_t>(row) * D + d] = code;
         else

@@ -51,11 +51,20 @@ __device__ __forceinline__ uint32_t fp8pair_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HALF != 0));
 }
 
-// Byte codes of a cache of kind KV (I8 or FP8) -> exact bf16 values.
+// Two E5M2 codes -> packed bf16 pair (exact: every E5M2 value is a bf16
+// value, and no cached code is an infinity or NaN by construction).
+template <int HALF>
+__device__ __forceinline__ uint32_t e5m2pair_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HALF != 0));
+}
+
+// Byte codes of a cache of kind KV (I8, FP8 or E5M2) -> exact bf16 values.
 template <KvKind KV, int HALF>
 __device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t w) {
   if constexpr (KV == KvKind::FP8)
     return fp8pair_to_bf16x2<HALF>(w);
+  else if constexpr (KV == KvKind::E5M2)
+    return e5m2pair_to_bf16x2<HALF>(w);
   else
     return i8pair_to_bf16x2(w, HALF);
 }

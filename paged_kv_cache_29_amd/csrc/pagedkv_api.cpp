@@ -138,6 +138,8 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
     kv = pkv::KvKind::FP8;
   } else if (q_dtype == PKV_BF16 && kv_dtype == PKV_I4) {
     kv = pkv::KvKind::I4;
+  } else if (q_dtype == PKV_BF16 && kv_dtype == PKV_FP8_E5M2) {
+    kv = pkv::KvKind::E5M2;
   } else {
     return fail(PKV_ERR_UNSUPPORTED, "(q_dtype, kv_dtype) = (%d, %d) is not supported",
                 static_cast<int>(q_dtype), static_cast<int>(kv_dtype));
@@ -158,11 +160,11 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   }
   if (step && num_seqs > 0 && (!k_new || !v_new))
     return fail(PKV_ERR_INVALID, "decode step needs k_new and v_new");
-  if (kv == pkv::KvKind::I8 || kv == pkv::KvKind::FP8 || kv == pkv::KvKind::I4) {
+  if (kv != pkv::KvKind::F32 && kv != pkv::KvKind::BF16) {
     if (num_seqs > 0 && (!k_scale || !v_scale))
       return fail(PKV_ERR_INVALID, "int8 / FP8 / INT4 cache needs k_scale and v_scale");
   } else if (k_scale || v_scale) {
-    return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL unless kv_dtype is PKV_I8, PKV_FP8 or PKV_I4");
+    return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL for fp32 and bf16 caches");
   }
   const size_t need = check_workspace ? workspace_bytes_for(num_seqs, num_heads, head_dim, nparts) : 0;
   if (need > 0 && num_seqs > 0) {
@@ -436,6 +438,16 @@ pkv_status pkv_kv_cache_write_fp8(const float* k, const float* v, uint8_t* k_cac
                      "kv_cache_write_fp8");
 }
 
+pkv_status pkv_kv_cache_write_fp8_e5m2(const float* k, const float* v, uint8_t* k_cache,
+                                       uint8_t* v_cache, float* k_scale, float* v_scale,
+                                       const int64_t* slot_mapping, int64_t num_tokens,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                       int64_t num_blocks, void* stream) {
+  return write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens,
+                     num_kv_heads, head_dim, block_size, num_blocks, pkv::KvKind::E5M2, stream,
+                     "kv_cache_write_fp8_e5m2");
+}
+
 pkv_status pkv_kv_cache_write_int4(const float* k, const float* v, uint8_t* k_cache,
                                    uint8_t* v_cache, float* k_scale, float* v_scale,
                                    const int64_t* slot_mapping, int64_t num_tokens,
@@ -633,7 +645,7 @@ pkv_status pkv_copy_blocks(void* dst_k, void* dst_v, float* dst_k_scale, float* 
   if (!block_size_ok(block_size))
     return fail(PKV_ERR_UNSUPPORTED, "copy_blocks: block_size %d not in {16, 32}", block_size);
   int64_t tile_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim;  // per element byte
-  const bool coded = dtype == PKV_I8 || dtype == PKV_FP8 || dtype == PKV_I4;
+  const bool coded = dtype == PKV_I8 || dtype == PKV_FP8 || dtype == PKV_I4 || dtype == PKV_FP8_E5M2;
   if (dtype == PKV_F32) tile_bytes *= 4;
   else if (dtype == PKV_BF16) tile_bytes *= 2;
   else if (dtype == PKV_I4) tile_bytes /= 2;  // two codes per byte

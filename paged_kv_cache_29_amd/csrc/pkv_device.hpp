@@ -71,6 +71,16 @@ __device__ __forceinline__ uint32_t fp8_code(float x, float s) {
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(r, 0.f, 0, false)) & 0xffu;
 }
 
+// E5M2 code of x for scale s = absmax / 57344: x / s rounded to the nearest
+// E5M2 value (bias 15, largest finite 57344, ties to the even code) by the
+// hardware conversion, after clamping to +-57344 so that it never yields an
+// infinity; s == 0 gives code 0.
+__device__ __forceinline__ uint32_t e5m2_code(float x, float s) {
+  if (!(s > 0.f)) return 0u;
+  const float r = fminf(fmaxf(x / s, -57344.f), 57344.f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_bf8_f32(r, 0.f, 0, false)) & 0xffu;
+}
+
 // Combine a value across the four 16-lane groups of a wave (lanes l, l^16,
 // l^32, l^48), without lane-index registers: ds_swizzle swaps 16-lane
 // halves of each 32-lane group, v_permlane32_swap exchanges the two 32-lane

@@ -74,9 +74,10 @@ struct WriteParams {
   int32_t block_size;
 };
 
-// I4: two 4-bit codes per byte, two consecutive head dims of one token
-// (K tiles [bs][D/2], V tiles [D/2][bs]).
-enum class KvKind { F32 = 0, BF16 = 1, I8 = 2, FP8 = 3, I4 = 4 };
+// FP8: E4M3 codes; E5M2: the other FP8 format.  I4: two 4-bit codes per
+// byte, two consecutive head dims of one token (K tiles [bs][D/2], V tiles
+// [D/2][bs]).
+enum class KvKind { F32 = 0, BF16 = 1, I8 = 2, FP8 = 3, I4 = 4, E5M2 = 5 };
 
 // Whole-block copies between two pools: parts 0..3 are the K tiles, the V
 // tiles, the K scale rows and the V scale rows of a block (tile_bytes,

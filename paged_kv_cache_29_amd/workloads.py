@@ -25,6 +25,8 @@ id     name                   shape
 6      fp8_gqa70b             the same shape and draws, quantised to FP8
                               (E4M3) instead
 7      int4_gqa70b            the same shape and draws, quantised to INT4
+8      e5m2_gqa70b            the same shape and draws, quantised to FP8
+                              in the E5M2 format
 =====  =====================  =============================================
 
 Draw order with ``numpy.random.default_rng(seed)`` (PCG64): lengths, the
@@ -56,7 +58,7 @@ import numpy as np
 from .blocks import BlockAllocator
 
 BF16_NAN = np.uint16(0x7FC0)
-CODED_KINDS = ("i8", "fp8", "i4")  # caches of codes with per-(token, kv-head) scales
+CODED_KINDS = ("i8", "fp8", "e5m2", "i4")  # caches of codes with per-(token, kv-head) scales
 _CHUNK = 1 << 24  # elements drawn per RNG call when filling large pools
 
 
@@ -73,7 +75,7 @@ def bf16_bits(x):
 class Workload:
     name: str
     seed: int
-    kv_dtype: str            # "f32" | "bf16" | "i8" | "fp8" | "i4"
+    kv_dtype: str            # "f32" | "bf16" | "i8" | "fp8" | "e5m2" | "i4"
     q_dtype: str             # "f32" | "bf16"
     num_heads: int
     num_kv_heads: int
@@ -244,6 +246,7 @@ CONFIG_NAMES = {
     5: "int8_gqa70b",
     6: "fp8_gqa70b",
     7: "int4_gqa70b",
+    8: "e5m2_gqa70b",
 }
 
 
@@ -275,6 +278,9 @@ def make_config(config, seed=0, block_size=None):
                      num_blocks=32768 + 4096, rng=rng)
     if config == 7:
         return build("int4_gqa70b", seed, [8192] * 64, 64, 8, 128, 16, "i4", "bf16",
+                     num_blocks=32768 + 4096, rng=rng)
+    if config == 8:
+        return build("e5m2_gqa70b", seed, [8192] * 64, 64, 8, 128, 16, "e5m2", "bf16",
                      num_blocks=32768 + 4096, rng=rng)
     raise ValueError(f"unknown config {config}")
 

@@ -17,10 +17,12 @@ import paged_kv_cache_29_amd as pkv
 from paged_kv_cache_29_amd import blocks, workloads
 
 DEV = torch.device("cuda:0")
-CODED = ("i8", "fp8", "i4")  # caches of codes with per-(token, kv-head) scales
+CODED = ("i8", "fp8", "e5m2", "i4")  # caches of codes with per-(token, kv-head) scales
 # torch element type of a coded cache, and its quantising write
-CODE_DTYPE = {"i8": torch.int8, "fp8": torch.float8_e4m3fn, "i4": torch.uint8}
-CODE_WRITE = {"i8": "kv_cache_write_int8", "fp8": "kv_cache_write_fp8", "i4": "kv_cache_write_int4"}
+CODE_DTYPE = {"i8": torch.int8, "fp8": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2,
+              "i4": torch.uint8}
+CODE_WRITE = {"i8": "kv_cache_write_int8", "fp8": "kv_cache_write_fp8",
+              "e5m2": "kv_cache_write_fp8_e5m2", "i4": "kv_cache_write_int4"}
 
 
 def code_tile_shapes(kind, NB, Hkv, bs, D):
@@ -167,7 +169,7 @@ def oracle_caches(w, seqs=None):
     NB, Hkv, bs, D = w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim
     code_t = np.int8 if w.kv_dtype == "i8" else np.uint8
     write = {"i8": ocache.cache_write_int8, "fp8": ofp8.cache_write_fp8,
-             "i4": oint4.cache_write_int4}[w.kv_dtype]
+             "e5m2": ofp8.cache_write_fp8_e5m2, "i4": oint4.cache_write_int4}[w.kv_dtype]
     kshape, vshape = code_tile_shapes(w.kv_dtype, NB, Hkv, bs, D)
     kc = np.zeros(kshape, code_t)
     vc = np.zeros(vshape, code_t)

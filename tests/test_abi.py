@@ -18,7 +18,7 @@ HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.j
            if f.endswith(".h")]
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
-F32, BF16, I8, FP8, I4 = range(5)
+F32, BF16, I8, FP8, I4, E5M2 = range(6)
 
 
 def declared_functions():
@@ -85,6 +85,8 @@ def _decode(lib, **over):
     (dict(q_dtype=F32, kv_dtype=I8), UNSUPPORTED, "not supported"),
     (dict(kv_dtype=I8), INVALID, "k_scale"),
     (dict(kv_dtype=I4), INVALID, "k_scale"),
+    (dict(kv_dtype=E5M2), INVALID, "k_scale"),
+    (dict(kv_dtype=6, k_scale=_fake(9), v_scale=_fake(10)), UNSUPPORTED, "not supported"),
     (dict(q_dtype=F32, kv_dtype=I4), UNSUPPORTED, "not supported"),
     (dict(k_scale=_fake(7)), INVALID, "must be NULL"),
     (dict(partition_tokens=48), INVALID, "partition_tokens"),
@@ -168,6 +170,16 @@ def test_write_int8_rejects(lib):
     st = f(_fake(1), _fake(2), _fake(3), _fake(4), None, _fake(6), _fake(7), 4, 8, 128, 16, 8, None)
     assert st == INVALID and b"scale" in lib.pkv_last_error()
     st = f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), 4, 8, 48, 16, 8, None)
+    assert st == UNSUPPORTED
+    st = f(None, None, None, None, None, None, None, 0, 8, 128, 16, 8, None)
+    assert st == OK
+
+
+def test_write_fp8_e5m2_rejects(lib):
+    f = lib.pkv_kv_cache_write_fp8_e5m2
+    st = f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), None, _fake(7), 4, 8, 128, 16, 8, None)
+    assert st == INVALID and b"scale" in lib.pkv_last_error()
+    st = f(_fake(1), _fake(2), _fake(3), _fake(4), _fake(5), _fake(6), _fake(7), 4, 8, 128, 64, 8, None)
     assert st == UNSUPPORTED
     st = f(None, None, None, None, None, None, None, 0, 8, 128, 16, 8, None)
     assert st == OK

@@ -16,8 +16,8 @@ from gpu_helpers import DEV, assert_parity, out_f64, to_dev
 pytestmark = pytest.mark.gpu
 
 TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn,
-       "i4": torch.uint8}
-ESZ = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1, "i4": 1}
+       "e5m2": torch.float8_e5m2, "i4": torch.uint8}
+ESZ = {"f32": 4, "bf16": 2, "i8": 1, "fp8": 1, "e5m2": 1, "i4": 1}
 
 
 def _pool(gen, NB, Hkv, bs, D, kind, device=DEV, pinned=False):
@@ -32,7 +32,7 @@ def _pool(gen, NB, Hkv, bs, D, kind, device=DEV, pinned=False):
     W = D // 2 if kind == "i4" else D   # INT4: two dims per byte
     k = raw((NB, Hkv, bs, W), ESZ[kind]).view(TDT[kind]).view(NB, Hkv, bs, W)
     v = raw((NB, Hkv, W, bs), ESZ[kind]).view(TDT[kind]).view(NB, Hkv, W, bs)
-    if kind in ("i8", "fp8", "i4"):
+    if kind in ("i8", "fp8", "e5m2", "i4"):
         ks = raw((NB, Hkv, bs), 4).view(torch.float32).view(NB, Hkv, bs)
         vs = raw((NB, Hkv, bs), 4).view(torch.float32).view(NB, Hkv, bs)
         return (k, v, ks, vs)
@@ -43,7 +43,7 @@ def _bytes(pool):
     return [t.contiguous().view(torch.uint8).cpu().numpy().reshape(t.shape[0], -1) for t in pool]
 
 
-@pytest.mark.parametrize("kind", ["f32", "bf16", "i8", "fp8", "i4"])
+@pytest.mark.parametrize("kind", ["f32", "bf16", "i8", "fp8", "e5m2", "i4"])
 @pytest.mark.parametrize("Hkv,D,bs", [(4, 128, 16), (2, 64, 32), (8, 128, 32)])
 def test_copy_blocks_on_device(kind, Hkv, D, bs):
     gen = torch.Generator().manual_seed(Hkv * 100 + D + bs)

@@ -38,7 +38,7 @@ def test_f32_variants(G, D, bs, pt):
     assert_parity(got, oracle_out(w), "f32", f"f32 G={G} D={D} bs={bs} pt={pt}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "i4"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2", "i4"])
 @pytest.mark.parametrize("G,D,bs", [
     (1, 128, 16), (1, 64, 32), (2, 128, 16), (4, 128, 32), (4, 64, 16),
     (8, 128, 16), (8, 64, 32), (16, 128, 16), (16, 64, 32)])
@@ -51,7 +51,7 @@ def test_mfma_variants(kv, G, D, bs, pt):
     assert_parity(got, oracle_out(w), kv, f"{kv} G={G} D={D} bs={bs} pt={pt}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "i4", "f32"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2", "i4", "f32"])
 def test_empty_and_single_token(kv):
     """L = 0 gives zeros; L = 1 gives that token's V (exactly, for stored values)."""
     w = workloads.make_custom(7, [1, 0, 1, 40, 0], 8, 2, 128, 16, kv_dtype=kv)
@@ -102,14 +102,14 @@ def test_needle_dominates():
 
 def test_nan_poison_never_leaks():
     """Unused blocks, tail rows and table entries past the end hold NaN / -1."""
-    for kv in ("bf16", "i8", "fp8", "i4", "f32"):
+    for kv in ("bf16", "i8", "fp8", "e5m2", "i4", "f32"):
         w = workloads.make_custom(11, RAGGED[:12], 8, 2, 128, 16, kv_dtype=kv, spare=1.0)
         assert (w.block_tables == -1).any()
         got = DeviceWorkload(w).step()
         assert np.all(np.isfinite(got)), kv
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "i4"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2", "i4"])
 def test_block_permutation_bitexact(kv):
     """Relabelling physical blocks changes nothing, bit for bit."""
     w = workloads.make_custom(12, RAGGED, 16, 2, 128, 16, kv_dtype=kv)
@@ -120,7 +120,7 @@ def test_block_permutation_bitexact(kv):
         t = getattr(dw, name)
         if t is None:
             continue
-        raw = t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+        raw = t.view(torch.uint8) if t.dtype in (torch.float8_e4m3fn, torch.float8_e5m2) else t
         moved = torch.empty_like(raw)
         moved[perm] = raw
         setattr(dw, name, moved.view(t.dtype))
@@ -200,7 +200,7 @@ def test_repeated_steps_are_deterministic():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "i4"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2", "i4"])
 @pytest.mark.parametrize("bs,pt", [(16, 2048), (32, 4096), (16, 1056)])
 def test_partitions_spanning_more_than_64_blocks(kv, bs, pt):
     """A partition of up to 128 blocks: every block id is staged, none read stale."""

@@ -101,3 +101,87 @@ def test_every_code_is_read_as_its_value():
     got = out.cpu().view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(got, want)
     assert np.abs(ref[0, 0, :16]).max() > 20  # the large codes are in play
+
+
+# ---------------------------------------------------------------- E5M2
+def _rows_e5m2(rng, T, Hkv, D):
+    x = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    x *= np.exp(rng.uniform(-20, 20, size=(T, Hkv, 1))).astype(np.float32)
+    x[0, 0] = 0.0
+    x[1, 0] = 0.0
+    x[1, 0, 0] = -0.0
+    # absmax 57344: the scale is exactly 1, so x / s are the values themselves:
+    # midpoints between neighbouring codes (ties to even), subnormal values,
+    # a negative zero in a live row, and the largest value
+    pos = ofp8.e5m2_decode(np.arange(0x7C, dtype=np.uint8))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    x[2, 0] = 0.0
+    x[2, 0, 0] = 57344.0
+    x[2, 0, 1:D] = np.resize(np.concatenate([mids, -mids]), D - 1)
+    x[3, 0] = 0.0
+    x[3, 0, 0] = 57344.0
+    x[3, 0, 1:12] = np.array([2 ** -16, 3 * 2 ** -17, -2 ** -15, 5 * 2 ** -18, 2 ** -14,
+                              -0.0, 3 * 2 ** -16, 1e-5, -3e-5, 2 ** -17, 7 * 2 ** -18], np.float32)
+    x[4, 0] = np.float32(1e-44)                        # absmax / 57344 underflows to 0
+    x[5, 0] = rng.standard_normal(D).astype(np.float32) * np.float32(1e-36)
+    return x
+
+
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 32), (128, 32), (64, 16)])
+def test_write_e5m2_bitexact(D, bs):
+    rng = np.random.default_rng(D * 7 + bs)
+    NB, Hkv, T = 24, 2, 300
+    k = _rows_e5m2(rng, T, Hkv, D)
+    v = _rows_e5m2(rng, T, Hkv, D)[::-1].copy()
+    slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
+    slots[10:20] = -2
+    kc = np.full((NB, Hkv, bs, D), 0x7F, np.uint8)     # NaN codes where nothing is written
+    vc = np.full((NB, Hkv, D, bs), 0x7F, np.uint8)
+    ks = np.full((NB, Hkv, bs), np.nan, np.float32)
+    vs = np.full((NB, Hkv, bs), np.nan, np.float32)
+    rk, rv, rks, rvs = ofp8.cache_write_fp8_e5m2(k, v, kc, vc, ks, vs, slots, bs)
+    dk = torch.from_numpy(kc).to(DEV).view(torch.float8_e5m2)
+    dv = torch.from_numpy(vc).to(DEV).view(torch.float8_e5m2)
+    dks, dvs = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+    pkv.kv_cache_write_fp8_e5m2(to_dev(k, "f32"), to_dev(v, "f32"), dk, dv, dks, dvs,
+                                torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.view(torch.uint8).cpu().numpy(), rk)
+    assert np.array_equal(dv.view(torch.uint8).cpu().numpy(), rv)
+    assert np.array_equal(dks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
+    assert np.array_equal(dvs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
+    s0 = int(slots[3]) if slots[3] >= 0 else None
+    if s0 is not None:                                 # subnormal codes and a signed zero
+        codes = rk[s0 // bs, 0, s0 % bs, :12]
+        assert (codes & 0x7C == 0).sum() >= 5 and 0x80 in codes.tolist()
+
+
+def test_every_e5m2_code_is_read_as_its_value():
+    """As for E4M3: V tiles holding every finite E5M2 code (16 consecutive
+    codes per dim, so each dim's mean is exact in fp32), scale 1, q = 0; the
+    bf16 output must equal the oracle's mean bit for bit."""
+    bs, D, Hkv, H, L = 16, 128, 1, 2, 16
+    codes = np.arange(256, dtype=np.uint8)
+    codes = np.where((codes & 0x7C) == 0x7C, 0, codes).astype(np.uint8)   # inf / NaN codes -> 0
+    kc = np.zeros((1, Hkv, bs, D), np.uint8)
+    vc = np.zeros((1, Hkv, D, bs), np.uint8)
+    kc.reshape(-1)[:256] = codes[::-1]
+    vc.reshape(-1)[:256] = codes
+    ks = np.ones((1, Hkv, bs), np.float32)
+    vs = np.ones((1, Hkv, bs), np.float32)
+    q = np.zeros((1, H, D), np.uint16)
+    from oracle import decode_attention
+    from paged_kv_cache_29_amd import workloads
+    ref = decode_attention(q, kc, vc, np.zeros((1, 1), np.int32), np.array([L], np.int32), 1.0, H,
+                           Hkv, D, bs, "e5m2", "bf16", k_scale=ks, v_scale=vs)
+    want = workloads.bf16_bits(ref.astype(np.float32))
+    out = torch.empty((1, H, D), dtype=torch.bfloat16, device=DEV)
+    as_e5 = lambda a: torch.from_numpy(a).to(DEV).view(torch.float8_e5m2)
+    pkv.paged_attention_decode(out, to_dev(q, "bf16"), as_e5(kc), as_e5(vc),
+                               torch.zeros((1, 1), dtype=torch.int32, device=DEV),
+                               torch.tensor([L], dtype=torch.int32, device=DEV), 1.0, H, Hkv, D, bs,
+                               k_scale=torch.from_numpy(ks).to(DEV), v_scale=torch.from_numpy(vs).to(DEV))
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    assert np.abs(ref[0, 0, :16]).max() > 1000  # the large codes are in play

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("cfg,bs", [(1, None), (2, None), (3, None), (4, 16), (4, 32), (5, None),
-                                    (6, None), (7, None)])
+                                    (6, None), (7, None), (8, None)])
 def test_full_size_sampled(cfg, bs):
     w = workloads.make_config(cfg, 0, block_size=bs)
     print(f"\n[full] config {cfg} bs={w.block_size} B={w.num_seqs} H={w.num_heads} "
@@ -38,7 +38,7 @@ def test_full_size_sampled(cfg, bs):
         if kind == "bf16":
             assert np.array_equal(bf16_bits_of(dw.k_cache[blk, :, r, :]), caches[0][blk, :, r, :])
             assert np.array_equal(bf16_bits_of(dw.v_cache[blk, :, :, r]), caches[1][blk, :, :, r])
-        elif kind in ("i8", "fp8", "i4"):
+        elif kind in ("i8", "fp8", "e5m2", "i4"):
             for j in range(int(np.ceil(w.context_lens[b] / bs_))):
                 pb = int(w.block_tables[b][j])
                 assert np.array_equal(dw.k_cache[pb].view(torch.uint8).cpu().numpy(),

@@ -18,7 +18,7 @@ RAGGED = [5, 6, 15, 16, 17, 31, 32, 33, 100, 255, 700]
 
 def _run(w, n_per, seed=0, partition_tokens=0, samples=None):
     dw = DeviceWorkload(w)
-    if w.kv_dtype in ("i8", "fp8"):
+    if w.kv_dtype in ("i8", "fp8", "e5m2"):
         dw.fill_int8()
     dw.write_new()                                    # every context token is now cached
     qs = np.concatenate([[0], np.cumsum(n_per)]).astype(np.int32)
@@ -38,7 +38,7 @@ def _run(w, n_per, seed=0, partition_tokens=0, samples=None):
     return out_f64(out), ref, q, qs, dw
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2"])
 @pytest.mark.parametrize("G,D,bs", [(4, 128, 16), (8, 128, 32), (1, 64, 16), (2, 64, 32), (16, 128, 16)])
 @pytest.mark.parametrize("pt", [0, 64])
 def test_speculative_verify_five_tokens(kv, G, D, bs, pt):

@@ -21,7 +21,7 @@ def _cache_bytes(dw):
     return parts
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "i4", "f32"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2", "i4", "f32"])
 @pytest.mark.parametrize("G,D,bs,pt", [(1, 128, 16, 0), (8, 128, 16, 64), (4, 64, 32, 0), (16, 128, 32, 512)])
 def test_fused_step_equals_write_then_decode(kv, G, D, bs, pt):
     Hkv = 2
