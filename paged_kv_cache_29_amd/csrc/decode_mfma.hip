@@ -75,7 +75,14 @@ template <KvKind KV>
 constexpr int kWavesPerSimd = KV == KvKind::I4 ? 3 : 2;
 
 // KV: BF16, or codes with per-token scales (I8, FP8: bytes; I4: nibbles).
-template <KvKind KV, int D, int BS, int W>
+// kMQ: multi-query attention (speculative verification of a few new tokens
+// per sequence).  The 16 columns are (new token, head) pairs of one
+// sequence's kv-head group instead of its heads, tile `tile` of p.mq_tiles;
+// column i of the sequence's n new tokens x G heads sits at position
+// L - n + i / G and sees tokens 0 .. L - n + i / G (causal); every
+// partition leaves partials (empty ones with max -inf, sum 0) and the
+// reduce always runs.
+template <KvKind KV, int D, int BS, int W, bool kMQ>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV>, kWavesPerSimd<KV>)))
 void decode_mfma_kernel(DecodeParams p) {
@@ -102,16 +109,37 @@ void decode_mfma_kernel(DecodeParams p) {
   const int Hkv = p.num_kv_heads;
   const int H = p.num_heads;
   const int G = H / Hkv;
-  const int b = blockIdx.x / Hkv;
-  const int kvh = blockIdx.x - b * Hkv;
+  int b, kvh, tile = 0;
+  if constexpr (kMQ) {
+    // blockIdx.x = ((u / 8) * mq_tiles + tile) * 8 + u % 8 for u = b * Hkv +
+    // kvh: the column tiles of one (sequence, kv-head) run on the same XCD
+    // (workgroups go to XCDs round-robin) and share its L2
+    const int rest = blockIdx.x >> 3;
+    tile = rest % p.mq_tiles;
+    const int u = (rest / p.mq_tiles) * 8 + (blockIdx.x & 7);
+    if (u >= p.num_seqs * Hkv) return;  // uniform across the workgroup
+    b = u / Hkv;
+    kvh = u - b * Hkv;
+  } else {
+    b = blockIdx.x / Hkv;
+    kvh = blockIdx.x - b * Hkv;
+  }
   const int part = blockIdx.y;
   const int PT = p.part_tokens;
 
   const int L = p.context_lens[b];
+  // multi-query: this sequence's n new tokens x G heads are its columns
+  int qrow0 = 0, nnew = 0, ncol = G;
+  if constexpr (kMQ) {
+    qrow0 = p.query_start[b];
+    nnew = p.query_start[b + 1] - qrow0;
+    ncol = nnew * G;
+    if (tile * 16 >= ncol) return;  // uniform; also every sequence with L == 0
+  }
   // cascade: the group's shared tokens are attended by the prefix kernel
-  const bool cascade = p.group_start != nullptr;
+  const bool cascade = !kMQ && p.group_start != nullptr;
   const int t_begin = (cascade ? group_shared_tokens(p, group_of(p, b)) : 0) + part * PT;
-  if ((cascade || part != 0) && t_begin >= L) return;  // uniform across the workgroup
+  if ((kMQ || cascade || part != 0) && t_begin >= L) return;  // uniform across the workgroup
   const int h0 = kvh * G;
   uint16_t* out = static_cast<uint16_t*>(p.out);
 
@@ -120,12 +148,18 @@ void decode_mfma_kernel(DecodeParams p) {
       out[(static_cast<size_t>(b) * H + h0) * D + i] = 0;
     return;
   }
-  const int t_end = min(L, t_begin + PT);
-  const bool single = !cascade && L <= PT;
+  // multi-query: column col = tile * 16 + c sees tokens 0 .. lim; the
+  // workgroup reads nothing past its last column's position
+  const int col = tile * 16 + c;
+  const int lim = kMQ ? L - nnew + col / G : 0;
+  const int lim_lo = kMQ ? L - nnew + (tile * 16) / G : 0;
+  const int t_end = kMQ ? max(t_begin, min(min(L, t_begin + PT), L - nnew + min(tile * 16 + 15, ncol - 1) / G + 1))
+                        : min(L, t_begin + PT);
+  const bool single = !kMQ && !cascade && L <= PT;
 
   // Fused step: the partition holding the newest token writes it first; the
   // fence and barrier make the stores visible to this workgroup's loads.
-  if (p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
+  if (!kMQ && p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
     append_new_token<KV, D, BS>(p, b, kvh, L - 1);
     __threadfence_block();
     __syncthreads();
@@ -135,14 +169,16 @@ void decode_mfma_kernel(DecodeParams p) {
   bf16x8 qf[NJ];
   float k_off = 0.f;  // INT4: 136 * sum_d q_d of head c
   {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                           (static_cast<size_t>(b) * H + h0 + c) * D;
+    const size_t qr = kMQ ? (static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G)
+                          : (static_cast<size_t>(b) * H + h0 + c);
+    const bool qvalid = kMQ ? (col < ncol) : (c < G);
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qr * D;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int d0 = kI4 ? ((D / 4) * g + 8 * j)
                          : (kInt8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g));
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (c < G) v = load_u32x4(qrow + d0);
+      if (qvalid) v = load_u32x4(qrow + d0);
       if constexpr (kI4) {
         // element order of the INT4 K operand: dims +0, 2, 4, 6, 1, 3, 5, 7
         v = u32x4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
@@ -223,7 +259,8 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     // ---- online softmax (log2 domain); lane = head c, tokens 4g + i of
     // sub-tile h (chunk token 16h + 4g + i), element e = 4h + i
-    const bool tail = (t0 + 32) > t_end;
+    // multi-query: also mask tokens past a column's position
+    const bool tail = (t0 + 32) > t_end || (kMQ && t0 + 31 > lim_lo);
     float sc[8];
     f32x4 vs[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
 #pragma unroll
@@ -241,7 +278,8 @@ void decode_mfma_kernel(DecodeParams p) {
     if (tail) {  // select, never multiply: masked rows may hold NaN
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if (t0 + 16 * (e >> 2) + 4 * g + (e & 3) >= t_end) {
+        const int tok = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
+        if (tok >= t_end || (kMQ && tok > lim)) {
           sc[e] = -INFINITY;
           vs[e >> 2][e & 3] = 0.f;
         }
@@ -253,7 +291,8 @@ void decode_mfma_kernel(DecodeParams p) {
     mx = groups_max(mx);
     const float m_new = fmaxf(m_run, mx);
     if (__any(m_new > m_run)) {
-      const float alpha = fast_exp2(m_run - m_new);
+      float alpha = fast_exp2(m_run - m_new);
+      if constexpr (kMQ) alpha = (m_new == -INFINITY) ? 1.f : alpha;  // a column that saw nothing yet
       l_run *= alpha;
       if constexpr (kI4) pv_run *= alpha;
 #pragma unroll
@@ -267,6 +306,10 @@ void decode_mfma_kernel(DecodeParams p) {
       float pr[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(sc[e] - m_run);
+      if constexpr (kMQ) {  // -inf - -inf: a column that saw nothing yet
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[e] = (sc[e] == -INFINITY) ? 0.f : pr[e];
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) l_run += pr[e];
       if constexpr (kInt8) {
@@ -388,13 +431,14 @@ void decode_mfma_kernel(DecodeParams p) {
     if (wave != 0) return;
 #pragma unroll
     for (int w = 1; w < W; ++w) M = fmaxf(M, red_m[w][lane]);
-    const float f0 = fast_exp2(m_run - M);  // wave 0 always saw a chunk: M finite
+    // M finite: wave 0 saw a chunk (multi-query: unless the column saw nothing)
+    const float f0 = (kMQ && M == -INFINITY) ? 0.f : fast_exp2(m_run - M);
     Lsum = l_run * f0;
 #pragma unroll
     for (int n = 0; n < NN; ++n) acc[n] *= f0;
 #pragma unroll
     for (int w = 1; w < W; ++w) {
-      const float fw = fast_exp2(red_m[w][lane] - M);  // -inf (idle wave) -> 0
+      const float fw = (kMQ && M == -INFINITY) ? 0.f : fast_exp2(red_m[w][lane] - M);  // idle wave -> 0
       Lsum += fw * red_l[w][lane];
 #pragma unroll
       for (int n = 0; n < NN; ++n)
@@ -403,9 +447,10 @@ void decode_mfma_kernel(DecodeParams p) {
     }
   }
 
-  if (c >= G) return;
-  const int h = h0 + c;
-  const size_t bh = static_cast<size_t>(b) * H + h;
+  if (kMQ ? col >= ncol : c >= G) return;
+  // output row: (sequence, head), or (query row, head) in multi-query mode
+  const size_t bh = kMQ ? static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G
+                        : static_cast<size_t>(b) * H + h0 + c;
   if constexpr (kI4) {  // lane holds dims 32m + 8g .. + 7: tiles 2m (even), 2m + 1 (odd)
     if (single) {
       uint16_t* orow = out + bh * D;
@@ -452,21 +497,24 @@ void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
-template <KvKind KV, int D, int BS>
+template <KvKind KV, int D, int BS, bool kMQ>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
+  unsigned units = static_cast<unsigned>(p.num_seqs * p.num_kv_heads);
+  if constexpr (kMQ)  // (sequence, kv-head) units padded to whole groups of 8, x column tiles
+    units = (units + 7u) / 8u * 8u * static_cast<unsigned>(p.mq_tiles);
   // cascade: slots [0, prefix_parts) belong to the shared-prefix kernel
   const int parts = p.group_start != nullptr ? p.num_parts - p.prefix_parts : p.num_parts;
-  const dim3 grid(static_cast<unsigned>(p.num_seqs * p.num_kv_heads), static_cast<unsigned>(parts));
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves>), grid,
+  const dim3 grid(units, static_cast<unsigned>(parts));
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, kMQ>), grid,
                      dim3(kDecodeWaves * kWave), 0, s, p);
   return hipGetLastError();
 }
 
-template <KvKind KV>
+template <KvKind KV, bool kMQ = false>
 hipError_t launch_kv(const DecodeParams& p, hipStream_t s) {
   if (p.head_dim == 128)
-    return p.block_size == 16 ? launch_t<KV, 128, 16>(p, s) : launch_t<KV, 128, 32>(p, s);
-  return p.block_size == 16 ? launch_t<KV, 64, 16>(p, s) : launch_t<KV, 64, 32>(p, s);
+    return p.block_size == 16 ? launch_t<KV, 128, 16, kMQ>(p, s) : launch_t<KV, 128, 32, kMQ>(p, s);
+  return p.block_size == 16 ? launch_t<KV, 64, 16, kMQ>(p, s) : launch_t<KV, 64, 32, kMQ>(p, s);
 }
 
 }  // namespace
@@ -477,6 +525,13 @@ hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s) {
   if (kv == KvKind::E5M2) return launch_kv<KvKind::E5M2>(p, s);
   if (kv == KvKind::FP8) return launch_kv<KvKind::FP8>(p, s);
   return launch_kv<KvKind::BF16>(p, s);
+}
+
+hipError_t launch_multi_query_decode(const DecodeParams& p, KvKind kv, hipStream_t s) {
+  if (kv == KvKind::I8) return launch_kv<KvKind::I8, true>(p, s);
+  if (kv == KvKind::FP8) return launch_kv<KvKind::FP8, true>(p, s);
+  if (kv == KvKind::E5M2) return launch_kv<KvKind::E5M2, true>(p, s);
+  return launch_kv<KvKind::BF16, true>(p, s);
 }
 
 }  // namespace pkv

@@ -200,6 +200,7 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   p.prefix_parts = 0;
   p.query_start = nullptr;  // plain decode; the multi-query entry point sets it
   p.num_query_rows = 0;
+  p.mq_tiles = 0;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
@@ -312,8 +313,14 @@ int32_t auto_mq_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t qtil
   return pt;
 }
 
+// Multi-query sizing.  Up to kMqDecodeMaxTiles column tiles of 16 (new
+// token, head) pairs per (sequence, kv-head), the partition kernel runs it
+// (its waves split a partition's chunks, each with all the columns);
+// beyond, the LDS-staged kernel (its waves split 128 columns and share each
+// chunk).  qtiles counts the chosen kernel's column tiles.
 struct MqSizes {
   int32_t pt, parts, qtiles;
+  bool decode_style;
 };
 
 pkv_status mq_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t block_size,
@@ -325,8 +332,9 @@ pkv_status mq_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, i
   if (static_cast<int64_t>(num_query_tokens) * num_heads > 0x7fffffff)
     return fail(PKV_ERR_UNSUPPORTED, "num_query_tokens * num_heads too large");
   const int32_t G = num_heads / num_kv_heads;
-  const int64_t qtiles = (static_cast<int64_t>(max_queries > 0 ? max_queries : 1) * G + kPrefixQueries - 1) /
-                         kPrefixQueries;
+  const int64_t cols = static_cast<int64_t>(max_queries > 0 ? max_queries : 1) * G;
+  const bool decode_style = cols <= 16 * pkv::kMqDecodeMaxTiles;
+  const int64_t qtiles = decode_style ? (cols + 15) / 16 : (cols + kPrefixQueries - 1) / kPrefixQueries;
   if (qtiles > 65535) return fail(PKV_ERR_UNSUPPORTED, "max_queries_per_seq * G too large");
   int32_t pt = partition_tokens;
   if (pt == 0) {
@@ -339,6 +347,7 @@ pkv_status mq_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, i
   ms->pt = pt;
   ms->parts = num_parts_for(block_size, max_blocks_per_seq, pt);
   ms->qtiles = static_cast<int32_t>(qtiles);
+  ms->decode_style = decode_style;
   if (ms->parts > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many context partitions (%d)", ms->parts);
   return PKV_OK;
 }
@@ -753,7 +762,13 @@ pkv_status pkv_paged_attention_multi_query(
   p.part_tokens = ms.pt;
   p.num_parts = ms.parts;
   const hipStream_t strm = static_cast<hipStream_t>(stream);
-  hipError_t e = pkv::launch_multi_query(p, st.kv, max_queries_per_seq, strm);
+  hipError_t e;
+  if (ms.decode_style) {
+    p.mq_tiles = ms.qtiles;
+    e = pkv::launch_multi_query_decode(p, st.kv, strm);
+  } else {
+    e = pkv::launch_multi_query(p, st.kv, max_queries_per_seq, strm);
+  }
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "multi-query kernel launch failed: %s", hipGetErrorString(e));
   e = pkv::launch_decode_reduce(p, st.out_bf16, strm);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));

@@ -49,6 +49,9 @@ struct DecodeParams {
   // workspace ([T][H][P]) and the reduce always runs.
   const int32_t* query_start;
   int32_t num_query_rows;  // T (multi-query)
+  // Multi-query in the partition kernel: column tiles of 16 (new token,
+  // head) pairs per (sequence, kv-head); 0 otherwise.
+  int32_t mq_tiles;
   float scale_log2;  // scale * log2(e)
   int32_t num_seqs;
   int32_t num_heads;
@@ -132,6 +135,14 @@ hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group
 // Multi-query attention partials (query_start set): every partition of every
 // sequence's context for up to max_queries new tokens per sequence.
 hipError_t launch_multi_query(const DecodeParams& p, KvKind kv, int max_queries, hipStream_t s);
+// The same partials from the partition kernel (few new tokens per sequence:
+// p.mq_tiles column tiles of 16 per (sequence, kv-head); waves split the
+// chunks of a partition instead of its columns).
+hipError_t launch_multi_query_decode(const DecodeParams& p, KvKind kv, hipStream_t s);
+// Column tiles up to which the partition kernel runs multi-query attention
+// (70B GQA shape, 50 sequences, measured per call: 1 tile 373 us vs 508 us
+// staged, 2 tiles 516 vs 668, 3 tiles 649 vs 673, 4 tiles 775 vs 699).
+constexpr int kMqDecodeMaxTiles = 3;
 hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
 // Quantising write of fp32 rows into an int8, FP8 or INT4 cache.
 hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s);

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 RAGGED = [5, 6, 15, 16, 17, 31, 32, 33, 100, 255, 700]
 
 
-def _run(w, n_per, seed=0, partition_tokens=0, samples=None):
+def _run(w, n_per, seed=0, partition_tokens=0, samples=None, max_queries=None):
     dw = DeviceWorkload(w)
     if w.kv_dtype in ("i8", "fp8", "e5m2"):
         dw.fill_int8()
@@ -27,7 +27,8 @@ def _run(w, n_per, seed=0, partition_tokens=0, samples=None):
     out = torch.empty((T, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=DEV)
     pkv.paged_attention_multi_query(out, to_dev(q, "bf16"), dw.k_cache, dw.v_cache, dw.block_tables,
                                     dw.context_lens, torch.from_numpy(qs).to(DEV), w.scale, w.num_heads,
-                                    w.num_kv_heads, w.head_dim, w.block_size, max(1, max(n_per)),
+                                    w.num_kv_heads, w.head_dim, w.block_size,
+                                    max_queries or max(1, max(n_per)),
                                     k_scale=dw.k_scale, v_scale=dw.v_scale,
                                     partition_tokens=partition_tokens)
     torch.cuda.synchronize()
@@ -82,3 +83,30 @@ def test_speculative_verify_70b_shape_sampled():
     got, ref, *_ = _run(w, n, seed=11, samples=samples)
     for r, h in samples:
         assert_parity(got[r, h], ref[r, h], "bf16", f"70B verify (row {r}, head {h})")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+@pytest.mark.parametrize("G", [8, 2])
+def test_verify_straddling_partitions(kv, G):
+    """The new tokens straddle a partition boundary, so the earliest queries
+    see nothing in the last partition (empty partials in the partition
+    kernel's multi-query mode); some sequences have fewer new tokens, one
+    none."""
+    w = workloads.make_custom(21 + G, [66, 130, 68, 258, 5, 193], 2 * G, 2, 128, 16, kv_dtype=kv)
+    got, ref, *_ = _run(w, [5, 4, 5, 3, 0, 2], seed=G, partition_tokens=64)
+    assert_parity(got, ref, kv, f"straddle {kv} G={G}")
+
+
+@pytest.mark.parametrize("G,n", [(8, 5), (4, 8), (1, 16), (16, 2)])
+def test_both_kernels_agree(G, n):
+    """The same call through the partition kernel's multi-query mode (few
+    columns) and, with a looser max_queries_per_seq bound, through the
+    LDS-staged kernel: both match the oracle and each other."""
+    w = workloads.make_custom(30 + G, [n, 40, 333, 1000, 64 + n - 1], 2 * G, 2, 128, 16)
+    a, ref, *_ = _run(w, [n] * 5, seed=n, partition_tokens=128)
+    loose = (16 * 3) // G + 1                             # beyond the partition kernel's columns
+    b, ref2, *_ = _run(w, [n] * 5, seed=n, partition_tokens=128, max_queries=max(loose, n))
+    assert np.array_equal(ref, ref2)
+    assert_parity(a, ref, "bf16", f"partition kernel G={G} n={n}")
+    assert_parity(b, ref, "bf16", f"staged kernel G={G} n={n}")
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-5)
