@@ -7,6 +7,8 @@
 //      v_mfma_f32_16x16x32_bf16: row l % 16, contraction 8 (l / 16) + e);
 //   V: tokens 4g .. 4g+3 of dim 16n + c of each sub-tile, 8 contiguous
 //      bytes (bf16) of the dim-major V tile (element (r, d) at d*bs + r);
+//      byte codes (and INT4 at D = 128) load whole 16-byte rows and hand
+//      each lane its 4 tokens by a transpose across lane groups;
 //   int8 scales of tokens 4g .. 4g+3.
 // Every load is a buffer descriptor over one tile (uniform: scalar
 // registers) plus a loop-invariant lane offset.
@@ -103,6 +105,18 @@ __device__ __forceinline__ u32x2 nib4_to_bf16(uint32_t n) {
   return u32x2{nib_pair_to_bf16x2<0>(n), nib_pair_to_bf16x2<1>(n)};
 }
 
+// 4 x 4 transpose of words across the four 16-lane groups: on return, word
+// j of a lane in group g holds what word g of the lane at the same position
+// in group j held.  Two cross-half swaps (groups 0, 1 <-> 2, 3), then two
+// cross-row swaps (0 <-> 1, 2 <-> 3); no LDS, no shuffle addresses.
+__device__ __forceinline__ u32x4 transpose_groups(u32x4 w) {
+  const auto a = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  return u32x4{c[0], c[1], d[0], d[1]};
+}
+
 // Zero the bf16 elements (pairs packed in w) whose token is >= t_end.
 __device__ __forceinline__ uint32_t mask_pair(uint32_t w, int tok, int t_end) {
   const uint32_t lo = (tok < t_end) ? (w & 0xffffu) : 0u;
@@ -142,6 +156,7 @@ struct ChunkLoader {
   int Hkv, kvh;
   // loop-invariant per-lane byte offsets inside a (block, kv-head) tile
   uint32_t koff, voff, soff;
+  uint32_t vrow;  // byte codes: V row (dim) 16 g + c of each group of 64 dims
 
   __device__ __forceinline__ ChunkLoader(const DecodeParams& p, int kvh_, int c, int g)
       : kc(static_cast<const char*>(p.k_cache)), vc(static_cast<const char*>(p.v_cache)),
@@ -152,6 +167,7 @@ struct ChunkLoader {
     // V^T: dim c (+16n per load), tokens 4g .. 4g+3
     voff = (static_cast<uint32_t>(c) * BS + 4u * g) * kElem;
     soff = 4u * g * 4u;
+    vrow = (16u * g + c) * BS;
   }
 
   // Buffer resource over one (block, kv-head) tile: the base is uniform, so
@@ -179,9 +195,17 @@ struct ChunkLoader {
 #pragma unroll
         for (int jj = 0; jj < NJ / 2; ++jj)
           ch.k[h][jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, ks_row + 64 * jj, 0));
+        // V: a lane loads all 16 tokens of dim 64k + 16g + c (16 bytes), and a
+        // transpose across lane groups hands each lane its tokens 4g .. 4g+3
+        // of dims 64k + 16j + c, j = 0..3 (operand n = 4k + j): a quarter of
+        // the load instructions of one 4-byte load per operand
 #pragma unroll
-        for (int n = 0; n < NN; ++n)
-          ch.v[h][n] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, vs_row + 16 * n * BS, 0);
+        for (int k = 0; k < D / 64; ++k) {
+          const u32x4 w = transpose_groups(__builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vrow, row0[h] + 64 * k * BS, 0)));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ch.v[h][4 * k + j] = w[j];
+        }
         const __amdgpu_buffer_rsrc_t rks = tile(ksc, t * BS * 4, BS * 4);
         const __amdgpu_buffer_rsrc_t rvs = tile(vsc, t * BS * 4, BS * 4);
         ch.ks[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, soff, row0[h] * 4, 0));
@@ -230,7 +254,9 @@ struct ChunkLoaderI4 {
     koff = static_cast<uint32_t>(c) * (D / 2) + (D / 8) * g;
     voff = static_cast<uint32_t>(c) * BS + 4u * g;
     soff = 4u * g * 4u;
+    vrow = (16u * g + c) * BS;
   }
+  uint32_t vrow;  // D = 128: V row (dim pair) 16 g + c
 
   __device__ __forceinline__ void load(ChunkI4<D>& ch, const int blk[2], const int row0[2]) const {
 #pragma unroll
@@ -242,9 +268,18 @@ struct ChunkLoaderI4 {
         ch.k[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, row0[h] * (D / 2), 0));
       else
         ch.k[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, koff, row0[h] * (D / 2), 0));
+      if constexpr (D == 128) {
+        // all 16 tokens of dim pair 16g + c, then the transpose across lane
+        // groups: word m = tokens 4g .. 4g+3 of dim pair 16m + c
+        const u32x4 w = transpose_groups(__builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vrow, row0[h], 0)));
 #pragma unroll
-      for (int m = 0; m < D / 32; ++m)
-        ch.v[h][m] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, row0[h] + 16 * m * BS, 0);
+        for (int m = 0; m < 4; ++m) ch.v[h][m] = w[m];
+      } else {
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m)
+          ch.v[h][m] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, row0[h] + 16 * m * BS, 0);
+      }
       const __amdgpu_buffer_rsrc_t rks = ChunkLoader<true, D, BS>::tile(ksc, t * BS * 4, BS * 4);
       const __amdgpu_buffer_rsrc_t rvs = ChunkLoader<true, D, BS>::tile(vsc, t * BS * 4, BS * 4);
       ch.ks[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, soff, row0[h] * 4, 0));
