@@ -529,6 +529,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s) {
 
 hipError_t launch_multi_query_decode(const DecodeParams& p, KvKind kv, hipStream_t s) {
   if (kv == KvKind::I8) return launch_kv<KvKind::I8, true>(p, s);
+  if (kv == KvKind::I4) return launch_kv<KvKind::I4, true>(p, s);
   if (kv == KvKind::FP8) return launch_kv<KvKind::FP8, true>(p, s);
   if (kv == KvKind::E5M2) return launch_kv<KvKind::E5M2, true>(p, s);
   return launch_kv<KvKind::BF16, true>(p, s);

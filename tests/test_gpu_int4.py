@@ -146,7 +146,9 @@ def test_offsets_cancel_with_one_signed_query():
     assert_parity(out_f64(out), ref, "i4", "one-signed q and V")
 
 
-def test_cascade_and_multi_query_reject_int4():
+def test_cascade_and_wide_multi_query_reject_int4():
+    """Shared-prefix decode has no INT4 kernel, nor has multi-query
+    attention beyond 48 (new token, head) pairs per (sequence, kv-head)."""
     w = workloads.make_custom(5, [40, 50], 8, 2, 128, 16, kv_dtype="i4")
     NB = w.num_blocks
     kc = torch.zeros((NB, 2, 16, 64), dtype=torch.uint8, device=DEV)
@@ -155,9 +157,10 @@ def test_cascade_and_multi_query_reject_int4():
     q = to_dev(w.q, "bf16")
     bt, cl = to_dev(w.block_tables, "i32"), to_dev(w.context_lens, "i32")
     with pytest.raises(NotImplementedError):
-        pkv.paged_attention_multi_query(torch.empty_like(q), q, kc, vc, bt, cl,
-                                        torch.tensor([0, 1, 2], dtype=torch.int32, device=DEV),
-                                        w.scale, 8, 2, 128, 16, 1, k_scale=sc, v_scale=sc)
+        q13 = torch.zeros((26, 8, 128), dtype=torch.bfloat16, device=DEV)   # 13 x G = 52 > 48
+        pkv.paged_attention_multi_query(torch.empty_like(q13), q13, kc, vc, bt, cl,
+                                        torch.tensor([0, 13, 26], dtype=torch.int32, device=DEV),
+                                        w.scale, 8, 2, 128, 16, 13, k_scale=sc, v_scale=sc)
     with pytest.raises(NotImplementedError):
         pkv.paged_attention_decode_cascade(torch.empty_like(q), q, kc, vc, bt, cl,
                                            torch.tensor([0, 2], dtype=torch.int32, device=DEV),

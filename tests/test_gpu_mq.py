@@ -18,7 +18,7 @@ RAGGED = [5, 6, 15, 16, 17, 31, 32, 33, 100, 255, 700]
 
 def _run(w, n_per, seed=0, partition_tokens=0, samples=None, max_queries=None):
     dw = DeviceWorkload(w)
-    if w.kv_dtype in ("i8", "fp8", "e5m2"):
+    if w.kv_dtype in ("i8", "fp8", "e5m2", "i4"):
         dw.fill_int8()
     dw.write_new()                                    # every context token is now cached
     qs = np.concatenate([[0], np.cumsum(n_per)]).astype(np.int32)
@@ -110,3 +110,13 @@ def test_both_kernels_agree(G, n):
     assert_parity(a, ref, "bf16", f"partition kernel G={G} n={n}")
     assert_parity(b, ref, "bf16", f"staged kernel G={G} n={n}")
     assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-5)
+
+
+@pytest.mark.parametrize("G,D,bs,pt", [(8, 128, 16, 0), (4, 64, 32, 64), (1, 128, 32, 64), (2, 64, 16, 0)])
+def test_int4_verify(G, D, bs, pt):
+    """INT4 caches: up to 48 (new token, head) pairs per (sequence, kv-head)
+    run in the partition kernel's multi-query mode (the INT4 offsets
+    cancel per column); new tokens straddle partition boundaries."""
+    w = workloads.make_custom(50 + G, [5, 66, 130, 333, 700], 2 * G, 2, D, bs, kv_dtype="i4")
+    got, ref, *_ = _run(w, [5, 5, 4, 5, 3], seed=G, partition_tokens=pt)
+    assert_parity(got, ref, "i4", f"int4 verify G={G} D={D} bs={bs} pt={pt}")
