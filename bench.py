@@ -117,9 +117,17 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
         kf, vf, sf = up(w.k_fill, "f32"), up(w.v_fill, "f32"), torch.from_numpy(w.slot_fill).to(dev)
         write_codes(kf, vf, kc, vc, ks, vs, sf)   # fill the cache once
         torch.cuda.synchronize()
+        # the same fill again, timed: the quantising write at bulk size
+        fill = time_fill(torch, lambda: write_codes(kf, vf, kc, vc, ks, vs, sf),
+                         read_bytes=2 * kf.numel() * 4,
+                         write_bytes=int(2 * kf.shape[0] * Hkv * (D * CODE_BYTES[w.kv_dtype] + 4)),
+                         tokens=kf.shape[0])
         del kf, vf, sf
     else:
         kc, vc = up(w.k_cache, store), up(w.v_cache, store)
+        fill = None
+        if w.name == "mha7b_bf16":
+            fill = bulk_fill_bf16(torch, pkv, w, kc, vc)
     out = torch.empty_like(q)
     pt = args.partition_tokens
     need = pkv.workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
@@ -229,7 +237,48 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
     if w.meta.get("prefix"):
         res["cascade"] = run_cascade(w, args, torch, pkv, loop_time, write, out, q, kc, vc, bt, cl,
                                      ks, vs, nbytes, uniq, ms_per_step)
+    res["bulk_fill"] = fill
     res["_w"] = w
+    return res
+
+
+def time_fill(torch, fn, read_bytes, write_bytes, tokens, iters=5):
+    """Average duration of a bulk cache write (HIP events on the launch
+    stream) and its rate over the bytes it must read and write."""
+    fn()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(iters):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / iters * 1e3
+    return {"tokens": int(tokens), "us": us, "read_bytes": int(read_bytes), "write_bytes": int(write_bytes),
+            "gbs_read_plus_write": (read_bytes + write_bytes) / (us * 1e-6) / 1e9}
+
+
+def bulk_fill_bf16(torch, pkv, w, kc, vc):
+    """kv_cache_write of every cached token of the workload at once (a
+    prefill: each sequence's tokens in order, so consecutive tokens fill
+    consecutive rows of a block), from random bf16 rows; the cache is
+    rewritten with the values it is re-read with only after the timing."""
+    import numpy as np
+    bs = w.block_size
+    slots = []
+    for b, L in enumerate(w.context_lens):
+        pos = np.arange(int(L), dtype=np.int64)
+        slots.append(w.block_tables[b][pos // bs].astype(np.int64) * bs + pos % bs)
+    slot = torch.from_numpy(np.concatenate(slots)).to("cuda:0")
+    T, Hkv, D = slot.numel(), w.num_kv_heads, w.head_dim
+    k = torch.randn((T, Hkv, D), dtype=torch.bfloat16, device="cuda:0")
+    v = torch.randn((T, Hkv, D), dtype=torch.bfloat16, device="cuda:0")
+    k0, v0 = kc.clone(), vc.clone()
+    res = time_fill(torch, lambda: pkv.kv_cache_write(k, v, kc, vc, slot),
+                    read_bytes=2 * k.numel() * 2, write_bytes=2 * k.numel() * 2, tokens=T)
+    kc.copy_(k0)
+    vc.copy_(v0)
+    torch.cuda.synchronize()
     return res
 
 
@@ -498,6 +547,7 @@ def main():
         "kv_bytes_per_step": head["kv_bytes_per_step"],
         "kernel_us": head["kernel_us"],
         "unfused": head["unfused"],
+        "bulk_fill": head.get("bulk_fill"),
         "roofline": head["roofline"],
         "us_per_step_events": head["us_per_step_events"],
         "cascade": head.get("cascade"),

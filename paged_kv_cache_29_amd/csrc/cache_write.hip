@@ -28,117 +28,139 @@
 namespace pkv {
 namespace {
 
+// Lane mapping of both writes: a wave takes 16 consecutive tokens of one
+// kv-head (and, for the quantising write, K or V); lane 16 q + i holds token
+// t0 + i and every fourth 16-byte piece q, q + 4, ... of its row.
+// Consecutive lanes hold consecutive tokens, so when their slots are
+// consecutive rows of one block (a prefill or bulk fill), each V store
+// instruction writes neighbouring elements of a dim row instead of
+// scattering one element per line; the four lanes of a token load and
+// store 64 contiguous bytes of its row at a time.
+constexpr int kTokensPerWave = 16;
+
 template <typename T>
 __global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
   constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
   const int D = p.head_dim;
   const int BS = p.block_size;
   const int Hkv = p.num_kv_heads;
-  const int vecs = D / EPV;
-  const int64_t total = p.num_tokens * Hkv * vecs;
+  const int VPL = D / EPV / 4;         // vectors per lane per row
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ti = lane & 15;
+  const int q = lane >> 4;
+  const int64_t units = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * Hkv;
   const T* k = static_cast<const T*>(p.k);
   const T* v = static_cast<const T*>(p.v);
   T* kc = static_cast<T*>(p.k_cache);
   T* vc = static_cast<T*>(p.v_cache);
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t th = i / vecs;  // token * Hkv + head
-    const int vi = static_cast<int>(i - th * vecs);
-    const int64_t t = th / Hkv;
-    const int h = static_cast<int>(th - t * Hkv);
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; u < units;
+       u += static_cast<int64_t>(gridDim.x) * 4) {
+    const int64_t tg = u / Hkv;
+    const int h = static_cast<int>(u - tg * Hkv);
+    const int64_t t = tg * kTokensPerWave + ti;
+    if (t >= p.num_tokens) continue;
     const int64_t slot = p.slot_mapping[t];
     if (slot < 0) continue;
     const int64_t blk = slot / BS;
     const int row = static_cast<int>(slot - blk * BS);
-    const int d0 = vi * EPV;
-    const int64_t src = th * D + d0;
     const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * D;
-    *reinterpret_cast<u32x4*>(kc + tile + static_cast<int64_t>(row) * D + d0) =
-        *reinterpret_cast<const u32x4*>(k + src);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(v + src);
-    const T* ve = reinterpret_cast<const T*>(&vv);
+    const int64_t src = (t * Hkv + h) * D;
+    for (int j = 0; j < VPL; ++j) {
+      const int d0 = (4 * j + q) * EPV;
+      *reinterpret_cast<u32x4*>(kc + tile + static_cast<int64_t>(row) * D + d0) =
+          *reinterpret_cast<const u32x4*>(k + src + d0);
+      const u32x4 vv = *reinterpret_cast<const u32x4*>(v + src + d0);
+      const T* ve = reinterpret_cast<const T*>(&vv);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) vc[tile + static_cast<int64_t>(d0 + e) * BS + row] = ve[e];
+      for (int e = 0; e < EPV; ++e) vc[tile + static_cast<int64_t>(d0 + e) * BS + row] = ve[e];
+    }
   }
 }
 
-// One lane group of D/4 lanes per (token, kv-head, K-or-V) row, 4 values per
-// lane; rows alternate K, V.
+// The quantising write: one wave per (16 tokens, kv-head, K or V); the
+// four lanes of a token each hold a quarter of its row (4 dims of every 16),
+// and the row's absmax is the max over them (two xor shuffles).
 // KV: I8 (s = absmax / 127, quantize_code), FP8 (s = absmax / 448, fp8_code),
 // E5M2 (s = absmax / 57344, e5m2_code) or I4 (s = absmax / 7,
 // quantize_sym<7>, tiles of half the bytes).
 template <KvKind KV>
 __global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
+  constexpr float kMax = KV == KvKind::FP8    ? 448.0f
+                         : KV == KvKind::E5M2 ? 57344.0f
+                         : KV == KvKind::I4   ? 7.0f
+                                              : 127.0f;
   const int D = p.head_dim;
   const int BS = p.block_size;
   const int Hkv = p.num_kv_heads;
-  const int group = D / 4;                    // lanes per row (16 or 32)
-  const int rows_per_block = blockDim.x / group;
-  const int sub = threadIdx.x % group;
-  const int64_t total_rows = p.num_tokens * Hkv * 2;
+  const int NJ = D / 16;               // 4-dim groups per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int ti = lane & 15;
+  const int q = lane >> 4;
+  const int64_t units = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * Hkv * 2;
   const float* k = static_cast<const float*>(p.k);
   const float* v = static_cast<const float*>(p.v);
   uint8_t* kc = static_cast<uint8_t*>(p.k_cache);
   uint8_t* vc = static_cast<uint8_t*>(p.v_cache);
-  for (int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block; r0 < total_rows;
-       r0 += static_cast<int64_t>(gridDim.x) * rows_per_block) {
-    const int64_t r = r0 + threadIdx.x / group;
-    // every lane of a row group takes the same branch; the shuffles below
-    // stay inside the group (xor offsets < group)
-    const bool live = r < total_rows;
-    const int64_t th = live ? (r >> 1) : 0;
-    const bool is_v = (r & 1) != 0;
-    const int64_t t = th / Hkv;
-    const int h = static_cast<int>(th - t * Hkv);
-    const int64_t slot = live ? p.slot_mapping[t] : -1;
-    const float* src = (is_v ? v : k) + th * D + 4 * sub;
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (slot >= 0) x = *reinterpret_cast<const f32x4*>(src);
-    float a = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-    for (int o = group / 2; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; u < units;
+       u += static_cast<int64_t>(gridDim.x) * 4) {
+    // u = ((token group) * Hkv + head) * 2 + (K or V): uniform across the wave
+    const bool is_v = (u & 1) != 0;
+    const int64_t th = u >> 1;
+    const int64_t tg = th / Hkv;
+    const int h = static_cast<int>(th - tg * Hkv);
+    const int64_t t = tg * kTokensPerWave + ti;
+    const int64_t slot = t < p.num_tokens ? p.slot_mapping[t] : -1;
+    const float* src = (is_v ? v : k) + (t * Hkv + h) * D;
+    f32x4 x[8];                        // NJ <= 8 groups of 4 dims: dims 4 (4 j + q) + e
+    float a = 0.f;
+    for (int j = 0; j < NJ; ++j) {
+      x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (slot >= 0) x[j] = *reinterpret_cast<const f32x4*>(src + 4 * (4 * j + q));
+      a = fmaxf(a, fmaxf(fmaxf(fabsf(x[j][0]), fabsf(x[j][1])), fmaxf(fabsf(x[j][2]), fabsf(x[j][3]))));
+    }
+    // every lane of the wave takes part in the shuffles; the four lanes of a
+    // token are i, i + 16, i + 32, i + 48
+    a = fmaxf(a, __shfl_xor(a, 16, kWave));
+    a = fmaxf(a, __shfl_xor(a, 32, kWave));
     if (slot < 0) continue;
-    const float s = a / (KV == KvKind::FP8    ? 448.0f
-                         : KV == KvKind::E5M2 ? 57344.0f
-                         : KV == KvKind::I4   ? 7.0f
-                                              : 127.0f);
+    const float s = a / kMax;
     const int64_t blk = slot / BS;
     const int row = static_cast<int>(slot - blk * BS);
-    const int d0 = 4 * sub;
+    if (q == 0) (is_v ? p.v_scale : p.k_scale)[(blk * Hkv + h) * BS + row] = (s > 0.f) ? s : 0.f;
     if constexpr (KV == KvKind::I4) {
-      // dims d0 .. d0+3 -> bytes d0/2 and d0/2 + 1 of the token
-      const uint32_t b0 = pack_int4_pair(quantize_sym<7>(x[0], s), quantize_sym<7>(x[1], s));
-      const uint32_t b1 = pack_int4_pair(quantize_sym<7>(x[2], s), quantize_sym<7>(x[3], s));
       const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * (D / 2);
-      const int j = d0 / 2;
-      if (!is_v) {
-        *reinterpret_cast<uint16_t*>(kc + tile + static_cast<int64_t>(row) * (D / 2) + j) =
-            static_cast<uint16_t>(b0 | (b1 << 8));
-      } else {
-        vc[tile + static_cast<int64_t>(j) * BS + row] = static_cast<uint8_t>(b0);
-        vc[tile + static_cast<int64_t>(j + 1) * BS + row] = static_cast<uint8_t>(b1);
+      for (int j = 0; j < NJ; ++j) {
+        const int d0 = 4 * (4 * j + q);
+        const uint32_t b0 = pack_int4_pair(quantize_sym<7>(x[j][0], s), quantize_sym<7>(x[j][1], s));
+        const uint32_t b1 = pack_int4_pair(quantize_sym<7>(x[j][2], s), quantize_sym<7>(x[j][3], s));
+        if (!is_v) {
+          *reinterpret_cast<uint16_t*>(kc + tile + static_cast<int64_t>(row) * (D / 2) + d0 / 2) =
+              static_cast<uint16_t>(b0 | (b1 << 8));
+        } else {
+          vc[tile + static_cast<int64_t>(d0 / 2) * BS + row] = static_cast<uint8_t>(b0);
+          vc[tile + static_cast<int64_t>(d0 / 2 + 1) * BS + row] = static_cast<uint8_t>(b1);
+        }
       }
-      if (sub == 0) (is_v ? p.v_scale : p.k_scale)[(blk * Hkv + h) * BS + row] = (s > 0.f) ? s : 0.f;
       continue;
     }
-    uint32_t codes[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      codes[e] = KV == KvKind::FP8    ? fp8_code(x[e], s)
-                 : KV == KvKind::E5M2 ? e5m2_code(x[e], s)
-                                      : static_cast<uint32_t>(quantize_code(x[e], s));
     const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * D;
-    if (!is_v) {
-      const uint32_t packed = (codes[0] & 0xffu) | ((codes[1] & 0xffu) << 8) |
-                              ((codes[2] & 0xffu) << 16) | ((codes[3] & 0xffu) << 24);
-      *reinterpret_cast<uint32_t*>(kc + tile + static_cast<int64_t>(row) * D + d0) = packed;
-    } else {
+    for (int j = 0; j < NJ; ++j) {
+      const int d0 = 4 * (4 * j + q);
+      uint32_t codes[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        vc[tile + static_cast<int64_t>(d0 + e) * BS + row] = static_cast<uint8_t>(codes[e] & 0xffu);
-    }
-    if (sub == 0) {
-      const float sc = (s > 0.f) ? s : 0.f;
-      (is_v ? p.v_scale : p.k_scale)[(blk * Hkv + h) * BS + row] = sc;
+        codes[e] = KV == KvKind::FP8    ? fp8_code(x[j][e], s)
+                   : KV == KvKind::E5M2 ? e5m2_code(x[j][e], s)
+                                        : static_cast<uint32_t>(quantize_code(x[j][e], s));
+      if (!is_v) {
+        const uint32_t packed = (codes[0] & 0xffu) | ((codes[1] & 0xffu) << 8) |
+                                ((codes[2] & 0xffu) << 16) | ((codes[3] & 0xffu) << 24);
+        *reinterpret_cast<uint32_t*>(kc + tile + static_cast<int64_t>(row) * D + d0) = packed;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          vc[tile + static_cast<int64_t>(d0 + e) * BS + row] = static_cast<uint8_t>(codes[e] & 0xffu);
+      }
     }
   }
 }
@@ -152,9 +174,9 @@ unsigned grid_for(int64_t work, int per_block) {
 }  // namespace
 
 hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s) {
-  const int epv = kind == KvKind::F32 ? 4 : 8;
-  const int64_t work = p.num_tokens * p.num_kv_heads * (p.head_dim / epv);
-  const unsigned grid = grid_for(work, 256);
+  // one wave per (16 tokens, kv-head), four waves per workgroup
+  const int64_t waves = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * p.num_kv_heads;
+  const unsigned grid = grid_for(waves, 4);
   if (kind == KvKind::F32)
     hipLaunchKernelGGL(cache_write_kernel<float>, dim3(grid), dim3(256), 0, s, p);
   else
@@ -163,8 +185,9 @@ hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s) 
 }
 
 hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s) {
-  const int rows_per_block = 256 / (p.head_dim / 4);
-  const unsigned grid = grid_for(p.num_tokens * p.num_kv_heads * 2, rows_per_block);
+  // one wave per (16 tokens, kv-head, K or V), four waves per workgroup
+  const int64_t waves = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * p.num_kv_heads * 2;
+  const unsigned grid = grid_for(waves, 4);
   if (kind == KvKind::FP8)
     hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::FP8>, dim3(grid), dim3(256), 0, s, p);
   else if (kind == KvKind::I4)

@@ -105,3 +105,72 @@ def test_write_zero_tokens_noop():
     pkv.kv_cache_write(e, e, dk, dv, torch.empty(0, dtype=torch.int64, device=DEV))
     torch.cuda.synchronize()
     assert int(dk.abs().sum()) == 0
+
+
+def _prefill_slots(rng, NB, bs, lens):
+    """Slots of whole sequences written in order through shuffled block
+    tables (consecutive tokens fill consecutive rows of a block), the
+    layout a prefill or bulk fill writes; a few tokens skipped."""
+    perm = rng.permutation(NB)
+    out, nb = [], 0
+    for L in lens:
+        blocks = perm[nb: nb + (L + bs - 1) // bs]
+        nb += len(blocks)
+        pos = np.arange(L)
+        out.append(blocks[pos // bs].astype(np.int64) * bs + pos % bs)
+    slots = np.concatenate(out)
+    slots[5::97] = -1
+    return slots
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 32)])
+def test_write_prefill_order_bitexact(kind, D, bs):
+    rng = np.random.default_rng(D + bs + 3)
+    NB, Hkv = 64, 2
+    slots = _prefill_slots(rng, NB, bs, [37, 200, 16, 1, 300])
+    T = len(slots)
+    kc, vc = _pool(rng, NB, Hkv, bs, D, kind)
+    k = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    if kind == "bf16":
+        k, v = workloads.bf16_bits(k), workloads.bf16_bits(v)
+    ref_k, ref_v = ocache.cache_write(k, v, kc, vc, slots, bs)
+    dk, dv = to_dev(kc, kind), to_dev(vc, kind)
+    pkv.kv_cache_write(to_dev(k, kind), to_dev(v, kind), dk, dv, torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(dk, kind).view(np.uint8), ref_k.view(np.uint8))
+    assert np.array_equal(_host(dv, kind).view(np.uint8), ref_v.view(np.uint8))
+
+
+@pytest.mark.parametrize("kv", ["i8", "fp8", "e5m2", "i4"])
+@pytest.mark.parametrize("D,bs", [(128, 16), (64, 32)])
+def test_write_codes_prefill_order_bitexact(kv, D, bs):
+    from oracle import fp8 as ofp8, int4 as oint4
+    rng = np.random.default_rng(D + bs + 11)
+    NB, Hkv = 64, 3
+    slots = _prefill_slots(rng, NB, bs, [37, 200, 16, 1, 300])
+    T = len(slots)
+    k = (rng.standard_normal((T, Hkv, D)) * np.exp(rng.uniform(-5, 5, (T, Hkv, 1)))).astype(np.float32)
+    v = (rng.standard_normal((T, Hkv, D)) * np.exp(rng.uniform(-5, 5, (T, Hkv, 1)))).astype(np.float32)
+    W = D // 2 if kv == "i4" else D
+    kc = np.full((NB, Hkv, bs, W), 0x5A, np.uint8)
+    vc = np.full((NB, Hkv, W, bs), 0x5A, np.uint8)
+    ks = np.full((NB, Hkv, bs), np.nan, np.float32)
+    vs = np.full((NB, Hkv, bs), np.nan, np.float32)
+    write = {"i8": ocache.cache_write_int8, "fp8": ofp8.cache_write_fp8,
+             "e5m2": ofp8.cache_write_fp8_e5m2, "i4": oint4.cache_write_int4}[kv]
+    rk, rv, rks, rvs = write(k, v, kc.view(np.int8) if kv == "i8" else kc,
+                             vc.view(np.int8) if kv == "i8" else vc, ks, vs, slots, bs)
+    tdt = {"i8": torch.int8, "fp8": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2, "i4": torch.uint8}[kv]
+    dk = torch.from_numpy(kc).to(DEV).view(tdt)
+    dv = torch.from_numpy(vc).to(DEV).view(tdt)
+    dks, dvs = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+    fn = {"i8": pkv.kv_cache_write_int8, "fp8": pkv.kv_cache_write_fp8,
+          "e5m2": pkv.kv_cache_write_fp8_e5m2, "i4": pkv.kv_cache_write_int4}[kv]
+    fn(to_dev(k, "f32"), to_dev(v, "f32"), dk, dv, dks, dvs, torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(dk.view(torch.uint8).cpu().numpy(), np.asarray(rk).view(np.uint8))
+    assert np.array_equal(dv.view(torch.uint8).cpu().numpy(), np.asarray(rv).view(np.uint8))
+    assert np.array_equal(dks.cpu().numpy().view(np.uint32), rks.view(np.uint32))
+    assert np.array_equal(dvs.cpu().numpy().view(np.uint32), rvs.view(np.uint32))
