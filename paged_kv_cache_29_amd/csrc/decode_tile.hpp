@@ -288,7 +288,4 @@ struct ChunkLoaderI4 {
   }
 };
 
-// Block ids one partition may span (its context / block_size).
-constexpr int kMaxPartBlocks = 128;
-
 }  // namespace pkv

@@ -45,8 +45,8 @@ bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32; }
 bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
 
-constexpr int kChunk = 32;           // tokens per wave iteration
-constexpr int kMaxPartBlocks = 128;  // block ids of one partition staged in LDS
+using pkv::kChunk;          // tokens per wave iteration
+using pkv::kMaxPartBlocks;  // block ids of one partition staged in LDS
 
 // Automatic partition length: the longest of 2048 / 1024 / 512 / 256 tokens
 // (at most kMaxPartBlocks blocks) that still gives the launch about two full

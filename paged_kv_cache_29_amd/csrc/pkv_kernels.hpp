@@ -96,6 +96,13 @@ struct CopyParams {
 
 // Waves per workgroup of the partition kernels.
 constexpr int kDecodeWaves = 4;
+// Tokens a wave takes per step (one matrix-core chunk); partition lengths
+// are multiples of it.
+constexpr int kChunk = 32;
+// Block ids one partition may span (its length / block_size): the kernels
+// stage them in LDS arrays of this size, and the host rejects longer
+// partitions.
+constexpr int kMaxPartBlocks = 128;
 // Query-column tiles (16 queries each) per wave of the shared-prefix kernel,
 // and queries per workgroup.
 constexpr int kPrefixTiles = 2;
