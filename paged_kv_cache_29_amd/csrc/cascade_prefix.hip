@@ -61,7 +61,7 @@ struct PrefixLds {
 template <KvKind KV, int D, int BS, int NT, bool kMQ>
 __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void cascade_prefix_kernel(DecodeParams p) {
-  constexpr bool kInt8 = KV != KvKind::BF16;  // byte codes (int8 or FP8) with scales
+  constexpr bool kInt8 = KV != KvKind::BF16;  // byte codes (int8, FP8 E4M3 / E5M2) with scales
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
   static_assert(kDecodeWaves == 4, "one chunk piece per wave");

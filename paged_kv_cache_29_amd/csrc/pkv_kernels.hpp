@@ -25,7 +25,7 @@ struct DecodeParams {
   float* ws_m;
   float* ws_l;
   // Optional new token per sequence, [B][Hkv][D] (cache element type; fp32
-  // for an int8 cache): when non-null, the partition holding position L-1
+  // for a coded cache): when non-null, the partition holding position L-1
   // writes it there through the block table before attending.
   const void* k_new;
   const void* v_new;
