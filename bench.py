@@ -457,8 +457,41 @@ def cpu_baseline(w, seconds):
     nbytes = 2 * w.num_kv_heads * w.head_dim * elem * done_tokens
     return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done_seqs} of {w.num_seqs} sequences x all {w.num_heads} heads "
-                      f"({done_tokens} context tokens) of {w.name}, {el:.1f} s; "
-                      f"cpu_count={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"}
+                    f"({done_tokens} context tokens) of {w.name}, {el:.1f} s; "
+                    f"cpu_count={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}",
+            "cache_writes": cpu_cache_writes(w)}
+
+
+def cpu_cache_writes(w, tokens=4096, blocks=512):
+    """The cache-write oracles (slot scatter, int8 quantiser) on a bulk write
+    of `tokens` rows of the workload's kv-head shape into a pool of `blocks`
+    blocks (prefill order): rate over the bytes read and written, as the
+    GPU's bulk_fill reports it."""
+    import numpy as np
+    from oracle import cache as ocache
+    rng = np.random.default_rng(0)
+    Hkv, D, bs = w.num_kv_heads, w.head_dim, w.block_size
+    slots = rng.permutation(blocks)[:tokens // bs].repeat(bs) * bs + np.tile(np.arange(bs), tokens // bs)
+    k = rng.standard_normal((tokens, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((tokens, Hkv, D)).astype(np.float32)
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)   # bf16 bit patterns (truncated: any
+    vb = (v.view(np.uint32) >> 16).astype(np.uint16)   # pattern times the same)
+    kc = np.zeros((blocks, Hkv, bs, D), np.uint16)
+    vc = np.zeros((blocks, Hkv, D, bs), np.uint16)
+    t0 = time.perf_counter()
+    ocache.cache_write(kb, vb, kc, vc, slots, bs)
+    t_bf16 = time.perf_counter() - t0
+    kc8 = np.zeros((blocks, Hkv, bs, D), np.int8)
+    vc8 = np.zeros((blocks, Hkv, D, bs), np.int8)
+    sc = np.zeros((blocks, Hkv, bs), np.float32)
+    t0 = time.perf_counter()
+    ocache.cache_write_int8(k, v, kc8, vc8, sc, sc.copy(), slots, bs)
+    t_i8 = time.perf_counter() - t0
+    n = tokens * Hkv * D
+    return {"sample": f"{tokens} tokens x {Hkv} kv-heads x {D} dims into a {blocks}-block pool",
+            "kv_cache_write_bf16_gbs": 2 * (2 * n * 2) / t_bf16 / 1e9,
+            "kv_cache_write_int8_gbs": (2 * n * 4 + 2 * (n + tokens * Hkv * 4)) / t_i8 / 1e9,
+            "seconds": t_bf16 + t_i8}
 
 
 def copy_calibration(torch):
