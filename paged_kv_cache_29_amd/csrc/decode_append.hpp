@@ -17,11 +17,12 @@
 
 namespace pkv {
 
-// Called by all threads of a workgroup of at least 2 * D threads (and at
-// least two waves); pos = L - 1 >= 0.  KV: F32 or BF16 (bit copy), I8, FP8,
+// Called by all NT threads of a workgroup of at least two waves; pos =
+// L - 1 >= 0.  KV: F32 or BF16 (bit copy), I8, FP8,
 // E5M2 or I4 (quantised from fp32 rows).
-template <KvKind KV, int D, int BS>
+template <KvKind KV, int D, int BS, int NT>
 __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, int kvh, int pos) {
+  static_assert(NT >= 2 * kWave, "the coded appends use two waves");
   using KT = typename std::conditional<
       KV == KvKind::F32, float,
       typename std::conditional<KV == KvKind::BF16, uint16_t, uint8_t>::type>::type;
@@ -92,10 +93,12 @@ __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, i
   } else {
     const KT* kn = static_cast<const KT*>(p.k_new) + src;
     const KT* vn = static_cast<const KT*>(p.v_new) + src;
-    if (t < D)
-      kc[tile + static_cast<size_t>(row) * D + t] = kn[t];
-    else if (t < 2 * D)
-      vc[tile + static_cast<size_t>(t - D) * BS + row] = vn[t - D];
+    for (int i = t; i < 2 * D; i += NT) {
+      if (i < D)
+        kc[tile + static_cast<size_t>(row) * D + i] = kn[i];
+      else
+        vc[tile + static_cast<size_t>(i - D) * BS + row] = vn[i - D];
+    }
   }
 }
 

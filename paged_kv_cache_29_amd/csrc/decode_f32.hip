@@ -49,7 +49,7 @@ __global__ __launch_bounds__(W * kWave) void decode_f32_kernel(DecodeParams p) {
 
   // Fused step: the partition holding the newest token writes it first.
   if (p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
-    append_new_token<KvKind::F32, D, BS>(p, b, kvh, L - 1);
+    append_new_token<KvKind::F32, D, BS, W * kWave>(p, b, kvh, L - 1);
     __threadfence_block();
     __syncthreads();
   }

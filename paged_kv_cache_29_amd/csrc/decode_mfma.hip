@@ -160,7 +160,7 @@ void decode_mfma_kernel(DecodeParams p) {
   // Fused step: the partition holding the newest token writes it first; the
   // fence and barrier make the stores visible to this workgroup's loads.
   if (!kMQ && p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
-    append_new_token<KV, D, BS>(p, b, kvh, L - 1);
+    append_new_token<KV, D, BS, W * kWave>(p, b, kvh, L - 1);
     __threadfence_block();
     __syncthreads();
   }
