@@ -70,27 +70,32 @@ constexpr int kBatch = 2;
 // Waves per SIMD.  Two chunks in flight per wave at two waves saturate
 // the bf16, int8 and FP8 streams; an INT4 chunk carries half the bytes for
 // the same arithmetic, and a third wave (162 VGPRs fit) hides more of the
-// load latency (measured 8% faster; int8 and FP8 gain nothing).
-template <KvKind KV>
-constexpr int kWavesPerSimd = KV == KvKind::I4 ? 3 : 2;
+// load latency (measured 8% faster; int8 and FP8 gain nothing).  Several
+// column tiles (multi-query) need the registers of two waves per SIMD.
+template <KvKind KV, int NT>
+constexpr int kWavesPerSimd = KV == KvKind::I4 && NT == 1 ? 3 : 2;
 
 // KV: BF16, or codes with per-token scales (I8, FP8: bytes; I4: nibbles).
 // kMQ: multi-query attention (speculative verification of a few new tokens
-// per sequence).  The 16 columns are (new token, head) pairs of one
-// sequence's kv-head group instead of its heads, tile `tile` of p.mq_tiles;
-// column i of the sequence's n new tokens x G heads sits at position
-// L - n + i / G and sees tokens 0 .. L - n + i / G (causal); every
-// partition leaves partials (empty ones with max -inf, sum 0) and the
-// reduce always runs.
-template <KvKind KV, int D, int BS, int W, bool kMQ>
+// per sequence).  The columns are (new token, head) pairs of one sequence's
+// kv-head group instead of its heads: its n new tokens x G heads make
+// p.mq_tiles tiles of 16, and a workgroup takes NT consecutive ones (all of
+// them, or one per workgroup); column i sits at position L - n + i / G and
+// sees tokens 0 .. L - n + i / G (causal); every partition leaves partials
+// (empty ones with max -inf, sum 0) and the reduce always runs.  With
+// NT > 1 tiles every wave carries the tiles' states over one chunk in
+// flight: each K and V operand is loaded and widened once for all of them.
+template <KvKind KV, int D, int BS, int W, bool kMQ, int NT>
 __global__ __launch_bounds__(W * kWave)
-__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV>, kWavesPerSimd<KV>)))
+__attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, NT>, kWavesPerSimd<KV, NT>)))
 void decode_mfma_kernel(DecodeParams p) {
   constexpr bool kInt8 = KV != KvKind::BF16;  // codes (int8, FP8, INT4) with scales
   constexpr bool kI4 = KV == KvKind::I4;
   using ChunkT = typename std::conditional<kI4, ChunkI4<D>, Chunk<kInt8, D>>::type;
   using LoaderT = typename std::conditional<kI4, ChunkLoaderI4<D, BS>, ChunkLoader<kInt8, D, BS>>::type;
-  constexpr int NB = kBatch<KV>;
+  static_assert(NT >= 1 && NT <= kMqDecodeMaxTiles && (kMQ || NT == 1), "column tiles");
+  // the registers of the extra tiles' states replace the second chunk
+  constexpr int NB = NT > 1 ? 1 : kBatch<KV>;
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
   constexpr int NJ = D / 32;  // QK MFMAs per score tile
@@ -109,14 +114,16 @@ void decode_mfma_kernel(DecodeParams p) {
   const int Hkv = p.num_kv_heads;
   const int H = p.num_heads;
   const int G = H / Hkv;
-  int b, kvh, tile = 0;
+  int b, kvh, tile0 = 0;
   if constexpr (kMQ) {
-    // blockIdx.x = ((u / 8) * mq_tiles + tile) * 8 + u % 8 for u = b * Hkv +
-    // kvh: the column tiles of one (sequence, kv-head) run on the same XCD
-    // (workgroups go to XCDs round-robin) and share its L2
+    // blockIdx.x = ((u / 8) * groups + tg) * 8 + u % 8 for u = b * Hkv + kvh
+    // and tile group tg (tiles tg * NT ..): the tile groups of one (sequence,
+    // kv-head) run on the same XCD (workgroups go to XCDs round-robin) and
+    // share its L2
+    const int groups = (p.mq_tiles + NT - 1) / NT;
     const int rest = blockIdx.x >> 3;
-    tile = rest % p.mq_tiles;
-    const int u = (rest / p.mq_tiles) * 8 + (blockIdx.x & 7);
+    tile0 = (rest % groups) * NT;
+    const int u = (rest / groups) * 8 + (blockIdx.x & 7);
     if (u >= p.num_seqs * Hkv) return;  // uniform across the workgroup
     b = u / Hkv;
     kvh = u - b * Hkv;
@@ -134,7 +141,7 @@ void decode_mfma_kernel(DecodeParams p) {
     qrow0 = p.query_start[b];
     nnew = p.query_start[b + 1] - qrow0;
     ncol = nnew * G;
-    if (tile * 16 >= ncol) return;  // uniform; also every sequence with L == 0
+    if (16 * tile0 >= ncol) return;  // uniform; also every sequence with L == 0
   }
   // cascade: the group's shared tokens are attended by the prefix kernel
   const bool cascade = !kMQ && p.group_start != nullptr;
@@ -148,12 +155,14 @@ void decode_mfma_kernel(DecodeParams p) {
       out[(static_cast<size_t>(b) * H + h0) * D + i] = 0;
     return;
   }
-  // multi-query: column col = tile * 16 + c sees tokens 0 .. lim; the
+  // multi-query: column 16 t + c of tile t sees tokens 0 .. lim[t]; the
   // workgroup reads nothing past its last column's position
-  const int col = tile * 16 + c;
-  const int lim = kMQ ? L - nnew + col / G : 0;
-  const int lim_lo = kMQ ? L - nnew + (tile * 16) / G : 0;
-  const int t_end = kMQ ? max(t_begin, min(min(L, t_begin + PT), L - nnew + min(tile * 16 + 15, ncol - 1) / G + 1))
+  int lim[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) lim[t] = kMQ ? L - nnew + (16 * (tile0 + t) + c) / G : 0;
+  const int lim_lo = kMQ ? L - nnew + (16 * tile0) / G : 0;  // the first column's
+  const int t_end = kMQ ? max(t_begin, min(min(L, t_begin + PT),
+                                           L - nnew + min(16 * (tile0 + NT) - 1, ncol - 1) / G + 1))
                         : min(L, t_begin + PT);
   const bool single = !kMQ && !cascade && L <= PT;
 
@@ -165,14 +174,17 @@ void decode_mfma_kernel(DecodeParams p) {
     __syncthreads();
   }
 
-  // Q^T operand (B of the score MFMA): lane (c, g), MFMA j, 8 dims.
-  bf16x8 qf[NJ];
-  float k_off = 0.f;  // INT4: 136 * sum_d q_d of head c
-  {
+  // Q^T operand (B of the score MFMA): lane (c, g), tile t, MFMA j, 8 dims.
+  bf16x8 qf[NT][NJ];
+  float k_off[NT];  // INT4: 136 * sum_d q_d of column c
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = 16 * (tile0 + t) + c;
     const size_t qr = kMQ ? (static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G)
                           : (static_cast<size_t>(b) * H + h0 + c);
     const bool qvalid = kMQ ? (col < ncol) : (c < G);
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qr * D;
+    k_off[t] = 0.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int d0 = kI4 ? ((D / 4) * g + 8 * j)
@@ -184,11 +196,11 @@ void decode_mfma_kernel(DecodeParams p) {
         v = u32x4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
                   __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) k_off += bf16_lo(v[i]) + bf16_hi(v[i]);
+        for (int i = 0; i < 4; ++i) k_off[t] += bf16_lo(v[i]) + bf16_hi(v[i]);
       }
-      qf[j] = as_bf16x8(v);
+      qf[t][j] = as_bf16x8(v);
     }
-    if constexpr (kI4) k_off = kInt4Offset * groups_sum(k_off);
+    if constexpr (kI4) k_off[t] = kInt4Offset * groups_sum(k_off[t]);
   }
 
   // Physical block ids of the partition, staged in this wave's LDS slice so
@@ -221,114 +233,134 @@ void decode_mfma_kernel(DecodeParams p) {
     }
   };
 
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  float pv_run = 0.f;  // INT4: sum_t p_t v_scale_t (this lane's tokens)
-  f32x4 acc[NN];
+  float m_run[NT], l_run[NT];
+  float pv_run[NT];  // INT4: sum_t p_t v_scale_t (this lane's tokens)
+  f32x4 acc[NT][NN];
 #pragma unroll
-  for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) {
+    m_run[t] = -INFINITY;
+    l_run[t] = 0.f;
+    pv_run[t] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NN; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto consume = [&](const ChunkT& cw, int ch) {
     const int t0 = t_begin + ch * 32;
-    // ---- scores: S^T of sub-tiles h = 0, 1
-    f32x4 s[2];
+    // ---- scores: S^T of sub-tiles h = 0, 1 for every column tile; each K
+    // operand is widened once and feeds the tiles' contractions
+    f32x4 s[NT][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        s[t][h] = kI4 ? f32x4{-k_off[t], -k_off[t], -k_off[t], -k_off[t]} : f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (kI4) {
-        s[h] = f32x4{-k_off, -k_off, -k_off, -k_off};
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           uint32_t lo, hi;
           int4_nibbles(cw.k[h][j], lo, hi);
           const u32x2 a = nib4_to_bf16(lo), bq = nib4_to_bf16(hi);
-          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{a.x, a.y, bq.x, bq.y}), qf[j], s[h], 0, 0, 0);
+          const bf16x8 ka = as_bf16x8(u32x4{a.x, a.y, bq.x, bq.y});
+#pragma unroll
+          for (int t = 0; t < NT; ++t) s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[t][j], s[t][h], 0, 0, 0);
         }
       } else if constexpr (kInt8) {
 #pragma unroll
         for (int jj = 0; jj < NJ / 2; ++jj) {
           const u32x4 w = cw.k[h][jj];
-          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes8_to_bf16<KV>(w.x, w.y), qf[2 * jj], s[h], 0, 0, 0);
-          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes8_to_bf16<KV>(w.z, w.w), qf[2 * jj + 1], s[h], 0, 0, 0);
+          const bf16x8 k0 = codes8_to_bf16<KV>(w.x, w.y), k1 = codes8_to_bf16<KV>(w.z, w.w);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[t][2 * jj], s[t][h], 0, 0, 0);
+            s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[t][2 * jj + 1], s[t][h], 0, 0, 0);
+          }
         }
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw.k[h][j]), qf[j], s[h], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw.k[h][j]), qf[t][j], s[t][h], 0, 0, 0);
       }
     }
-    // ---- online softmax (log2 domain); lane = head c, tokens 4g + i of
+    // ---- online softmax (log2 domain); lane = column c, tokens 4g + i of
     // sub-tile h (chunk token 16h + 4g + i), element e = 4h + i
     // multi-query: also mask tokens past a column's position
-    const bool tail = (t0 + 32) > t_end || (kMQ && t0 + 31 > lim_lo);
-    float sc[8];
+    const bool past_end = (t0 + 32) > t_end;
+    const bool tail = past_end || (kMQ && t0 + 31 > lim_lo);
+    // V scales of the lane's tokens; zero past the end of the partition,
+    // where rows may hold NaN (select, never multiply)
     f32x4 vs[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x = s[h][i];
-        if constexpr (kInt8) {
-          x *= cw.ks[h][i];
-          vs[h][i] = cw.vs[h][i];
-        }
-        sc[4 * h + i] = x * p.scale_log2;
-      }
+    if constexpr (kInt8) {
+      vs[0] = cw.vs[0];
+      vs[1] = cw.vs[1];
     }
-    if (tail) {  // select, never multiply: masked rows may hold NaN
+    if (past_end) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tok = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
-        if (tok >= t_end || (kMQ && tok > lim)) {
-          sc[e] = -INFINITY;
-          vs[e >> 2][e & 3] = 0.f;
-        }
-      }
+      for (int e = 0; e < 8; ++e)
+        if (t0 + 16 * (e >> 2) + 4 * g + (e & 3) >= t_end) vs[e >> 2][e & 3] = 0.f;
     }
-    float mx = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-    mx = groups_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (__any(m_new > m_run)) {
-      float alpha = fast_exp2(m_run - m_new);
-      if constexpr (kMQ) alpha = (m_new == -INFINITY) ? 1.f : alpha;  // a column that saw nothing yet
-      l_run *= alpha;
-      if constexpr (kI4) pv_run *= alpha;
-#pragma unroll
-      for (int n = 0; n < NN; ++n) acc[n] *= alpha;
-      m_run = m_new;
-    }
-    // P^T operand as a bf16 pair hi + lo (hi = bf16(p), lo = bf16(p - hi)):
+    // P^T operands as bf16 pairs hi + lo (hi = bf16(p), lo = bf16(p - hi)):
     // two contractions give the weights to ~2^-16 relative instead of 2^-9.
-    uint32_t ph[4], pl[4];
-    {
+    uint32_t ph[NT][4], pl[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float sc[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[t][h][i];
+          if constexpr (kInt8) x *= cw.ks[h][i];
+          sc[4 * h + i] = x * p.scale_log2;
+        }
+      }
+      if (tail) {  // select, never multiply: masked rows may hold NaN
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tok = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
+          if (tok >= t_end || (kMQ && tok > lim[t])) sc[e] = -INFINITY;
+        }
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+      mx = groups_max(mx);
+      const float m_new = fmaxf(m_run[t], mx);
+      if (__any(m_new > m_run[t])) {
+        float alpha = fast_exp2(m_run[t] - m_new);
+        if constexpr (kMQ) alpha = (m_new == -INFINITY) ? 1.f : alpha;  // a column that saw nothing yet
+        l_run[t] *= alpha;
+        if constexpr (kI4) pv_run[t] *= alpha;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) acc[t][n] *= alpha;
+        m_run[t] = m_new;
+      }
       float pr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(sc[e] - m_run);
+      for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(sc[e] - m_run[t]);
       if constexpr (kMQ) {  // -inf - -inf: a column that saw nothing yet
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[e] = (sc[e] == -INFINITY) ? 0.f : pr[e];
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) l_run += pr[e];
+      for (int e = 0; e < 8; ++e) l_run[t] += pr[e];
       if constexpr (kInt8) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pr[e] *= vs[e >> 2][e & 3];
       }
       if constexpr (kI4) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv_run += pr[e];
+        for (int e = 0; e < 8; ++e) pv_run[t] += pr[e];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ph[i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
-        pl[i] = pack_bf16x2(pr[2 * i] - bf16_lo(ph[i]), pr[2 * i + 1] - bf16_hi(ph[i]));
+        ph[t][i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+        pl[t][i] = pack_bf16x2(pr[2 * i] - bf16_lo(ph[t][i]), pr[2 * i + 1] - bf16_hi(ph[t][i]));
       }
     }
-    const bf16x8 pfh = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
-    const bf16x8 pfl = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
-    // ---- O^T += V^T . P^T
+    // ---- O^T += V^T . P^T; each V operand is widened once for the tiles
     if constexpr (kI4) {
 #pragma unroll
       for (int m = 0; m < NN / 2; ++m) {
@@ -339,7 +371,7 @@ void decode_mfma_kernel(DecodeParams p) {
         const u32x2 b0 = nib4_to_bf16(hi0), b1 = nib4_to_bf16(hi1);
         u32x4 ve = {a0.x, a0.y, a1.x, a1.y};  // dim 32m + 2c, tokens e = 4h + i
         u32x4 vo = {b0.x, b0.y, b1.x, b1.y};  // dim 32m + 2c + 1
-        if (tail) {  // masked tokens contribute exact zeros
+        if (past_end) {  // masked tokens contribute exact zeros
           const int ta = t0 + 4 * g;
           ve.x = mask_pair(ve.x, ta, t_end);
           ve.y = mask_pair(ve.y, ta + 2, t_end);
@@ -350,10 +382,15 @@ void decode_mfma_kernel(DecodeParams p) {
           vo.z = mask_pair(vo.z, ta + 16, t_end);
           vo.w = mask_pair(vo.w, ta + 18, t_end);
         }
-        acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfh, acc[2 * m], 0, 0, 0);
-        acc[2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfl, acc[2 * m], 0, 0, 0);
-        acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfh, acc[2 * m + 1], 0, 0, 0);
-        acc[2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfl, acc[2 * m + 1], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const bf16x8 pfh = as_bf16x8(u32x4{ph[t][0], ph[t][1], ph[t][2], ph[t][3]});
+          const bf16x8 pfl = as_bf16x8(u32x4{pl[t][0], pl[t][1], pl[t][2], pl[t][3]});
+          acc[t][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfh, acc[t][2 * m], 0, 0, 0);
+          acc[t][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfl, acc[t][2 * m], 0, 0, 0);
+          acc[t][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfh, acc[t][2 * m + 1], 0, 0, 0);
+          acc[t][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfl, acc[t][2 * m + 1], 0, 0, 0);
+        }
       }
       return;
     }
@@ -366,7 +403,7 @@ void decode_mfma_kernel(DecodeParams p) {
       } else {
         vw = u32x4{cw.v[0][n].x, cw.v[0][n].y, cw.v[1][n].x, cw.v[1][n].y};
       }
-      if (tail) {  // masked tokens contribute exact zeros, even over NaN
+      if (past_end) {  // masked tokens contribute exact zeros, even over NaN
         const int ta = t0 + 4 * g;
         vw.x = mask_pair(vw.x, ta, t_end);
         vw.y = mask_pair(vw.y, ta + 2, t_end);
@@ -374,8 +411,13 @@ void decode_mfma_kernel(DecodeParams p) {
         vw.w = mask_pair(vw.w, ta + 18, t_end);
       }
       const bf16x8 va = as_bf16x8(vw);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc[n], 0, 0, 0);
-      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc[n], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 pfh = as_bf16x8(u32x4{ph[t][0], ph[t][1], ph[t][2], ph[t][3]});
+        const bf16x8 pfl = as_bf16x8(u32x4{pl[t][0], pl[t][1], pl[t][2], pl[t][3]});
+        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc[t][n], 0, 0, 0);
+        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc[t][n], 0, 0, 0);
+      }
     }
   };
 
@@ -409,104 +451,137 @@ void decode_mfma_kernel(DecodeParams p) {
     }
   }
 
-  // per-head sum over the 4 lane groups (each holds different tokens)
-  l_run = groups_sum(l_run);
-  if constexpr (kI4) {  // remove the V offset of this wave's tokens
-    const float v_off = kInt4Offset * groups_sum(pv_run);
+  // per-column sums over the 4 lane groups (each holds different tokens)
+  float M[NT], Lsum[NT];
 #pragma unroll
-    for (int n = 0; n < NN; ++n) acc[n] -= v_off;
+  for (int t = 0; t < NT; ++t) {
+    l_run[t] = groups_sum(l_run[t]);
+    if constexpr (kI4) {  // remove the V offset of this wave's tokens
+      const float v_off = kInt4Offset * groups_sum(pv_run[t]);
+#pragma unroll
+      for (int n = 0; n < NN; ++n) acc[t][n] -= v_off;
+    }
+    M[t] = m_run[t];
+    Lsum[t] = l_run[t];
   }
 
-  float M = m_run, Lsum = l_run;
   if constexpr (W > 1) {
-    red_m[wave][lane] = m_run;
-    red_l[wave][lane] = l_run;
-    if (wave > 0) {
+    // the waves' states merge into wave 0 through LDS, one column tile at a
+    // time (the buffers hold one tile)
 #pragma unroll
-      for (int n = 0; n < NN; ++n)
+    for (int t = 0; t < NT; ++t) {
+      if (t > 0) __syncthreads();  // wave 0 has read the previous tile
+      red_m[wave][lane] = m_run[t];
+      red_l[wave][lane] = l_run[t];
+      if (wave > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red_acc[wave - 1][4 * n + i][lane] = acc[n][i];
+        for (int n = 0; n < NN; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red_acc[wave - 1][4 * n + i][lane] = acc[t][n][i];
+      }
+      __syncthreads();
+      if (wave == 0) {
+        float Mt = m_run[t];
+#pragma unroll
+        for (int w = 1; w < W; ++w) Mt = fmaxf(Mt, red_m[w][lane]);
+        // Mt finite: wave 0 saw a chunk (multi-query: unless the column saw nothing)
+        const float f0 = (kMQ && Mt == -INFINITY) ? 0.f : fast_exp2(m_run[t] - Mt);
+        float Ls = l_run[t] * f0;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) acc[t][n] *= f0;
+#pragma unroll
+        for (int w = 1; w < W; ++w) {
+          const float fw = (kMQ && Mt == -INFINITY) ? 0.f : fast_exp2(red_m[w][lane] - Mt);  // idle wave -> 0
+          Ls += fw * red_l[w][lane];
+#pragma unroll
+          for (int n = 0; n < NN; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][n][i] += fw * red_acc[w - 1][4 * n + i][lane];
+        }
+        M[t] = Mt;
+        Lsum[t] = Ls;
+      }
     }
-    __syncthreads();
     if (wave != 0) return;
-#pragma unroll
-    for (int w = 1; w < W; ++w) M = fmaxf(M, red_m[w][lane]);
-    // M finite: wave 0 saw a chunk (multi-query: unless the column saw nothing)
-    const float f0 = (kMQ && M == -INFINITY) ? 0.f : fast_exp2(m_run - M);
-    Lsum = l_run * f0;
-#pragma unroll
-    for (int n = 0; n < NN; ++n) acc[n] *= f0;
-#pragma unroll
-    for (int w = 1; w < W; ++w) {
-      const float fw = (kMQ && M == -INFINITY) ? 0.f : fast_exp2(red_m[w][lane] - M);  // idle wave -> 0
-      Lsum += fw * red_l[w][lane];
-#pragma unroll
-      for (int n = 0; n < NN; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[n][i] += fw * red_acc[w - 1][4 * n + i][lane];
-    }
   }
 
-  if (kMQ ? col >= ncol : c >= G) return;
-  // output row: (sequence, head), or (query row, head) in multi-query mode
-  const size_t bh = kMQ ? static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G
-                        : static_cast<size_t>(b) * H + h0 + c;
-  if constexpr (kI4) {  // lane holds dims 32m + 8g .. + 7: tiles 2m (even), 2m + 1 (odd)
-    if (single) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int col = 16 * (tile0 + t) + c;
+    if (kMQ ? col >= ncol : c >= G) continue;
+    // output row: (sequence, head), or (query row, head) in multi-query mode
+    const size_t bh = kMQ ? static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G
+                          : static_cast<size_t>(b) * H + h0 + c;
+    const size_t slot = bh * p.num_parts + (cascade ? p.prefix_parts : 0) + part;
+    if constexpr (kI4) {  // lane holds dims 32m + 8g .. + 7: tiles 2m (even), 2m + 1 (odd)
+      if (single) {
+        uint16_t* orow = out + bh * D;
+#pragma unroll
+        for (int m = 0; m < NN / 2; ++m) {
+          const f32x4 e = acc[t][2 * m] / Lsum[t], o = acc[t][2 * m + 1] / Lsum[t];
+          *reinterpret_cast<u32x4*>(orow + 32 * m + 8 * g) =
+              u32x4{pack_bf16x2(e[0], o[0]), pack_bf16x2(e[1], o[1]), pack_bf16x2(e[2], o[2]), pack_bf16x2(e[3], o[3])};
+        }
+      } else {
+        float* arow = p.ws_acc + slot * D;
+#pragma unroll
+        for (int m = 0; m < NN / 2; ++m) {
+          const f32x4 e = acc[t][2 * m], o = acc[t][2 * m + 1];
+          *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
+          *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
+        }
+      }
+    } else if (single) {
       uint16_t* orow = out + bh * D;
 #pragma unroll
-      for (int m = 0; m < NN / 2; ++m) {
-        const f32x4 e = acc[2 * m] / Lsum, o = acc[2 * m + 1] / Lsum;
-        *reinterpret_cast<u32x4*>(orow + 32 * m + 8 * g) =
-            u32x4{pack_bf16x2(e[0], o[0]), pack_bf16x2(e[1], o[1]), pack_bf16x2(e[2], o[2]), pack_bf16x2(e[3], o[3])};
+      for (int n = 0; n < NN; ++n) {
+        u32x2 w;
+        w.x = pack_bf16x2(acc[t][n][0] / Lsum[t], acc[t][n][1] / Lsum[t]);
+        w.y = pack_bf16x2(acc[t][n][2] / Lsum[t], acc[t][n][3] / Lsum[t]);
+        *reinterpret_cast<u32x2*>(orow + 16 * n + 4 * g) = w;
       }
     } else {
-      const size_t slot = bh * p.num_parts + (cascade ? p.prefix_parts : 0) + part;
       float* arow = p.ws_acc + slot * D;
 #pragma unroll
-      for (int m = 0; m < NN / 2; ++m) {
-        const f32x4 e = acc[2 * m], o = acc[2 * m + 1];
-        *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
-        *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
-      }
-      if (g == 0) {
-        p.ws_m[slot] = M;
-        p.ws_l[slot] = Lsum;
-      }
+      for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[t][n];
     }
-    return;
-  }
-  if (single) {
-    uint16_t* orow = out + bh * D;
-#pragma unroll
-    for (int n = 0; n < NN; ++n) {
-      u32x2 w;
-      w.x = pack_bf16x2(acc[n][0] / Lsum, acc[n][1] / Lsum);
-      w.y = pack_bf16x2(acc[n][2] / Lsum, acc[n][3] / Lsum);
-      *reinterpret_cast<u32x2*>(orow + 16 * n + 4 * g) = w;
-    }
-  } else {
-    const size_t slot = bh * p.num_parts + (cascade ? p.prefix_parts : 0) + part;
-    float* arow = p.ws_acc + slot * D;
-#pragma unroll
-    for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[n];
-    if (g == 0) {
-      p.ws_m[slot] = M;
-      p.ws_l[slot] = Lsum;
+    if (!single && g == 0) {
+      p.ws_m[slot] = M[t];
+      p.ws_l[slot] = Lsum[t];
     }
   }
 }
 
 template <KvKind KV, int D, int BS, bool kMQ>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
-  unsigned units = static_cast<unsigned>(p.num_seqs * p.num_kv_heads);
-  if constexpr (kMQ)  // (sequence, kv-head) units padded to whole groups of 8, x column tiles
-    units = (units + 7u) / 8u * 8u * static_cast<unsigned>(p.mq_tiles);
   // cascade: slots [0, prefix_parts) belong to the shared-prefix kernel
   const int parts = p.group_start != nullptr ? p.num_parts - p.prefix_parts : p.num_parts;
-  const dim3 grid(units, static_cast<unsigned>(parts));
-  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, kMQ>), grid,
-                     dim3(kDecodeWaves * kWave), 0, s, p);
+  const unsigned units = static_cast<unsigned>(p.num_seqs * p.num_kv_heads);
+  const dim3 block(kDecodeWaves * kWave);
+  if constexpr (kMQ) {
+    if (p.mq_tiles < 1 || p.mq_tiles > kMqDecodeMaxTiles) return hipErrorInvalidValue;
+    // (sequence, kv-head) units padded to whole groups of 8, x tile groups
+    const unsigned padded = (units + 7u) / 8u * 8u;
+    if (KV == KvKind::I4 || p.mq_tiles == 1) {
+      // INT4: one tile per workgroup (more tiles' states do not fit beside
+      // its conversion registers at two waves per SIMD)
+      const dim3 grid(padded * static_cast<unsigned>(p.mq_tiles), static_cast<unsigned>(parts));
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, true, 1>), grid, block, 0, s, p);
+    } else {
+      // every column tile of a (sequence, kv-head) in one workgroup
+      static_assert(kMqDecodeMaxTiles == 3, "one instance per tile count");
+      const dim3 grid(padded, static_cast<unsigned>(parts));
+      if constexpr (KV != KvKind::I4) {
+        if (p.mq_tiles == 2)
+          hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, true, 2>), grid, block, 0, s, p);
+        else
+          hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, true, 3>), grid, block, 0, s, p);
+      }
+    }
+  } else {
+    const dim3 grid(units, static_cast<unsigned>(parts));
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

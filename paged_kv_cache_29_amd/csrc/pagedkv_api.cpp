@@ -315,7 +315,8 @@ int32_t auto_mq_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t qtil
 
 // Multi-query sizing.  Up to kMqDecodeMaxTiles column tiles of 16 (new
 // token, head) pairs per (sequence, kv-head), the partition kernel runs it
-// (its waves split a partition's chunks, each with all the columns);
+// (its waves split a partition's chunks, each carrying all the columns of
+// its workgroup);
 // beyond, the LDS-staged kernel (its waves split 128 columns and share each
 // chunk).  qtiles counts the chosen kernel's column tiles.
 struct MqSizes {

@@ -144,11 +144,13 @@ hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group
 hipError_t launch_multi_query(const DecodeParams& p, KvKind kv, int max_queries, hipStream_t s);
 // The same partials from the partition kernel (few new tokens per sequence:
 // p.mq_tiles column tiles of 16 per (sequence, kv-head); waves split the
-// chunks of a partition instead of its columns).
+// chunks of a partition instead of its columns, each wave carrying every
+// tile of its workgroup: all of them, or one for INT4).
 hipError_t launch_multi_query_decode(const DecodeParams& p, KvKind kv, hipStream_t s);
 // Column tiles up to which the partition kernel runs multi-query attention
-// (70B GQA shape, 50 sequences, measured per call: 1 tile 373 us vs 508 us
-// staged, 2 tiles 516 vs 668, 3 tiles 649 vs 673, 4 tiles 775 vs 699).
+// (70B GQA shape, 50 sequences, bf16, measured per call against the
+// LDS-staged kernel: 1 tile 373 us vs 508, 2 tiles 415 vs 668, 3 tiles 446
+// vs 673; four tiles' states do not fit two waves' registers per SIMD).
 constexpr int kMqDecodeMaxTiles = 3;
 hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
 // Quantising write of fp32 rows into an int8, FP8 or INT4 cache.

@@ -40,7 +40,8 @@ def _run(w, n_per, seed=0, partition_tokens=0, samples=None, max_queries=None):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2"])
-@pytest.mark.parametrize("G,D,bs", [(4, 128, 16), (8, 128, 32), (1, 64, 16), (2, 64, 32), (16, 128, 16)])
+@pytest.mark.parametrize("G,D,bs", [(4, 128, 16), (8, 128, 32), (1, 64, 16), (2, 64, 32), (16, 128, 16),
+                                    (8, 64, 16), (4, 64, 32)])
 @pytest.mark.parametrize("pt", [0, 64])
 def test_speculative_verify_five_tokens(kv, G, D, bs, pt):
     w = workloads.make_custom(400 + G + bs, RAGGED, G * 2, 2, D, bs, kv_dtype=kv)
