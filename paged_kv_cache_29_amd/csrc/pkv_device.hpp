@@ -82,23 +82,22 @@ __device__ __forceinline__ uint32_t e5m2_code(float x, float s) {
 }
 
 // Combine a value across the four 16-lane groups of a wave (lanes l, l^16,
-// l^32, l^48), without lane-index registers: ds_swizzle swaps 16-lane
-// halves of each 32-lane group, v_permlane32_swap exchanges the two 32-lane
-// halves (each lane gets back its own value and its partner's).
-__device__ __forceinline__ float swap16(float v) {
-  return __uint_as_float(__builtin_amdgcn_ds_swizzle(__float_as_uint(v), 0x401F));
-}
-
+// l^32, l^48) with two VALU lane swaps, no LDS traffic: v_permlane16_swap
+// of a register with itself hands every lane its value and that of the lane
+// 16 away (rows 0 <-> 1, 2 <-> 3), v_permlane32_swap that of the lane 32
+// away.  Every lane ends with the same bits ((v0 op v1) op (v2 op v3)).
 __device__ __forceinline__ float groups_max(float v) {
-  v = fmaxf(v, swap16(v));
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 __device__ __forceinline__ float groups_sum(float v) {
-  v = v + swap16(v);
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 }  // namespace pkv
