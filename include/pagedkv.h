@@ -314,8 +314,9 @@ pkv_status pkv_paged_attention_decode_step_partitions(
  *   prefix_partition_tokens: tokens of the shared span per workgroup; 0 for
  *   the automatic choice, else a multiple of 32 in [32, 128 * block_size].
  *   partition_tokens as for decode (for the remaining tokens).
- * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8) and (BF16, FP8_E5M2) with the
- * sizes of decode; an fp32 or INT4 cache returns PKV_ERR_UNSUPPORTED.  The workspace size comes from
+ * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8), (BF16, FP8_E5M2) and
+ * (BF16, I4) with the sizes of decode; an fp32 cache returns
+ * PKV_ERR_UNSUPPORTED.  The workspace size comes from
  * pkv_paged_attention_cascade_workspace_size with the same sizes and is
  * needed whenever num_seqs > 0.  Three launches: prefix kernel (skipped when
  * max_shared_blocks is 0), partition kernel, reduce.
@@ -357,12 +358,12 @@ size_t pkv_paged_attention_cascade_workspace_size(
  * query_start: device int32 [num_seqs + 1], query_start[0] = 0,
  * non-decreasing, query_start[num_seqs] = num_query_tokens.
  * max_queries_per_seq: host bound on every n_b, in [1, num_query_tokens].
- * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8), (BF16, FP8_E5M2) with
- * decode's sizes; (BF16, I4) when max_queries_per_seq * G <= 48 (else
- * PKV_ERR_UNSUPPORTED); an fp32 cache returns PKV_ERR_UNSUPPORTED.  Up to 48
- * (new token, head) pairs per sequence and kv-head the partition kernel
- * computes the partials (its waves split a partition's chunks), beyond that
- * an LDS-staged kernel (its waves split 128 columns and share each chunk).
+ * Supported: (BF16, BF16), (BF16, I8), (BF16, FP8), (BF16, FP8_E5M2) and
+ * (BF16, I4) with decode's sizes; an fp32 cache returns
+ * PKV_ERR_UNSUPPORTED.  Up to 48 (new token, head) pairs per sequence and
+ * kv-head (max_queries_per_seq * G <= 48) the partition kernel computes the
+ * partials (its waves split a partition's chunks), beyond that an
+ * LDS-staged kernel (its waves split 128 columns and share each chunk).
  * partition_tokens: 0 for the automatic choice, else as for decode.
  * Workspace: pkv_paged_attention_multi_query_workspace_size(...) bytes,
  * 256-byte aligned, whenever num_query_tokens > 0.  Two launches (partials

@@ -42,26 +42,35 @@
 namespace pkv {
 namespace {
 
-template <bool kInt8, int D, int BS, int NT>
+// LDS stage of one 32-token chunk.  A token's K row is RB bytes (bf16: 2D,
+// byte codes: D, INT4: D/2); V is stored as VR rows (dims, INT4: dim pairs)
+// of one sub-tile's 16 tokens.
+template <KvKind KV, int D, int BS, int NT>
 struct PrefixLds {
-  static constexpr int kElem = kInt8 ? 1 : 2;
-  static constexpr int KROW = D * kElem + 16;         // padded K token row
+  static constexpr int kElem = KV == KvKind::BF16 ? 2 : 1;
+  static constexpr int RB = KV == KvKind::I4 ? D / 2 : D * kElem;
+  static constexpr int VR = KV == KvKind::I4 ? D / 2 : D;
+  static constexpr int KROW = RB + 16;                // padded K token row
   static constexpr int KSUB = 16 * KROW;              // one 16-token K sub-tile
-  static constexpr int VROW = 16 * kElem;             // one dim's 16 tokens
-  static constexpr int VSUB = D * VROW;               // one 16-token V sub-tile
-  static constexpr int SC = kInt8 ? 4 * 64 : 0;       // k/v scales of both sub-tiles
+  static constexpr int VROW = 16 * kElem;             // one V row's 16 tokens
+  static constexpr int VSUB = VR * VROW;              // one 16-token V sub-tile
+  static constexpr int SC = KV != KvKind::BF16 ? 4 * 64 : 0;  // k/v scales of both sub-tiles
   static constexpr int STAGE = 2 * KSUB + 2 * VSUB + SC;
-  static constexpr int PIECE = 16 * D * kElem;        // bytes of one K or V sub-tile
-  static constexpr int UNITS = PIECE / (16 * kWave);  // 16-byte loads per lane per piece
+  static constexpr int PIECE = 16 * RB;               // bytes of one K or V sub-tile
+  // 16-byte loads per lane per piece (INT4 at D = 64: half the lanes load)
+  static constexpr int UNITS = (PIECE + 16 * kWave - 1) / (16 * kWave);
 };
 
-// KV: BF16, or byte codes with per-token scales (I8, FP8).  kMQ: the
+// KV: BF16, or codes with per-token scales (I8, FP8: bytes; I4: nibbles,
+// with the partition kernel's INT4 operands and offsets).  kMQ: the
 // multi-query form (one sequence's new tokens x heads as the columns, its
 // whole context partitioned, each column masked causally at its position).
 template <KvKind KV, int D, int BS, int NT, bool kMQ>
 __global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void cascade_prefix_kernel(DecodeParams p) {
-  constexpr bool kInt8 = KV != KvKind::BF16;  // byte codes (int8, FP8 E4M3 / E5M2) with scales
+  constexpr bool kInt8 = KV != KvKind::BF16;  // codes (int8, FP8 E4M3 / E5M2, INT4) with scales
+  constexpr bool kI4 = KV == KvKind::I4;
+  using ChunkT = typename std::conditional<kI4, ChunkI4<D>, Chunk<kInt8, D>>::type;
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
   static_assert(kDecodeWaves == 4, "one chunk piece per wave");
@@ -69,8 +78,7 @@ void cascade_prefix_kernel(DecodeParams p) {
   constexpr int NJ = D / 32;
   constexpr int NN = D / 16;
   constexpr int QW = 16 * NT;  // queries per wave
-  using L = PrefixLds<kInt8, D, BS, NT>;
-  constexpr int kElem = L::kElem;
+  using L = PrefixLds<KV, D, BS, NT>;
 
   __shared__ __attribute__((aligned(16))) char lds[2][L::STAGE];
   __shared__ int blk_ids[kMaxPartBlocks];
@@ -107,19 +115,31 @@ void cascade_prefix_kernel(DecodeParams p) {
   for (int t = 0; t < NT; ++t) lim[t] = S - nnew + (q0 + 16 * t + c) / G;
 
   // Q^T operands: tile t, lane (c, g), MFMA j: 8 dims from q_dim(j)
-  auto q_dim = [&](int j) { return kInt8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g); };
+  auto q_dim = [&](int j) {
+    return kI4 ? ((D / 4) * g + 8 * j) : (kInt8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g));
+  };
   bf16x8 qf[NT][NJ];
+  float k_off[NT];  // INT4: 136 * sum_d q_d of column c
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int r = q0 + 16 * t + c;
     const size_t qr = kMQ ? static_cast<size_t>(qrow0 + r / G) : static_cast<size_t>(gs + r / G);
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (qr * H + kvh * G + r % G) * D;
+    k_off[t] = 0.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (r < nq) v = load_u32x4(qrow + q_dim(j));
+      if constexpr (kI4) {
+        // element order of the INT4 K operand: dims +0, 2, 4, 6, 1, 3, 5, 7
+        v = u32x4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                  __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k_off[t] += bf16_lo(v[i]) + bf16_hi(v[i]);
+      }
       qf[t][j] = as_bf16x8(v);
     }
+    if constexpr (kI4) k_off[t] = kInt4Offset * groups_sum(k_off[t]);
   }
 
   // block ids of the span (the group's first sequence's table, or the
@@ -158,16 +178,17 @@ void cascade_prefix_kernel(DecodeParams p) {
     int blk[2], row0[2];
     chunk_blocks(ch, blk, row0);
     const size_t tile = static_cast<size_t>(blk[ph]) * Hkv + kvh;
-    const char* base = static_cast<const char*>(pv ? p.v_cache : p.k_cache) + tile * (BS * D * kElem);
+    const char* base = static_cast<const char*>(pv ? p.v_cache : p.k_cache) + tile * (BS * L::RB);
 #pragma unroll
     for (int i = 0; i < L::UNITS; ++i) {
       const int u = i * kWave + lane;  // 16-byte unit of the piece
+      if (u * 16 >= L::PIECE) break;   // INT4 at D = 64: half the lanes
       size_t off;
       if (!pv) {
-        off = static_cast<size_t>(row0[ph]) * D * kElem + u * 16;
+        off = static_cast<size_t>(row0[ph]) * L::RB + u * 16;
       } else if (BS == 16) {
         off = u * 16;
-      } else if (kInt8) {  // dim u: 16 tokens of a 32-token row
+      } else if (kInt8) {  // V row u (dim, INT4: dim pair): 16 tokens of a 32-token row
         off = u * 32 + 16 * ph;
       } else {  // dim u / 2, half u % 2 of the sub-tile's 32 bytes
         off = (u >> 1) * 64 + 32 * ph + 16 * (u & 1);
@@ -184,9 +205,10 @@ void cascade_prefix_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < L::UNITS; ++i) {
       const int u = i * kWave + lane;
+      if (u * 16 >= L::PIECE) break;
       if (!pv) {
-        const int row = (u * 16) / (D * kElem);
-        const int col = (u * 16) % (D * kElem);
+        const int row = (u * 16) / L::RB;
+        const int col = (u * 16) % L::RB;
         *reinterpret_cast<u32x4*>(dst + ph * L::KSUB + row * L::KROW + col) = pu[i];
       } else {
         u32x4 w = pu[i];
@@ -198,54 +220,82 @@ void cascade_prefix_kernel(DecodeParams p) {
       *reinterpret_cast<u32x4*>(dst + 2 * L::KSUB + 2 * L::VSUB + wave * 64 + lane * 16) = psc;
   };
   // this lane's operands of a staged chunk, in the partition kernel's layouts
-  auto lds_chunk = [&](int st, Chunk<kInt8, D>& cw) {
+  auto lds_chunk = [&](int st, ChunkT& cw) {
     const char* src = lds[st];
+    if constexpr (kI4) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const char* kr = src + h * L::KSUB + c * L::KROW;
-      if constexpr (kInt8) {
+      for (int h = 0; h < 2; ++h) {
+        // K: this lane's D/4 dims of row c; V: word m = tokens 4g .. 4g+3 of
+        // dim pair 16m + c
+        const char* kr = src + h * L::KSUB + c * L::KROW;
+        if constexpr (D == 128)
+          cw.k[h] = *reinterpret_cast<const u32x4*>(kr + 16 * g);
+        else
+          cw.k[h] = *reinterpret_cast<const u32x2*>(kr + 8 * g);
+        const char* vr = src + 2 * L::KSUB + h * L::VSUB;
 #pragma unroll
-        for (int jj = 0; jj < NJ / 2; ++jj) cw.k[h][jj] = *reinterpret_cast<const u32x4*>(kr + 16 * g + 64 * jj);
-      } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) cw.k[h][j] = *reinterpret_cast<const u32x4*>(kr + (32 * j + 8 * g) * 2);
-      }
-      const char* vr = src + 2 * L::KSUB + h * L::VSUB;
-#pragma unroll
-      for (int n = 0; n < NN; ++n) {
-        if constexpr (kInt8) {
-          cw.v[h][n] = *reinterpret_cast<const uint32_t*>(vr + (16 * n + c) * L::VROW + 4 * g);
-        } else {
-          const int gg = g ^ ((c >> 3) & 1);
-          cw.v[h][n] = *reinterpret_cast<const u32x2*>(vr + (16 * n + c) * L::VROW + 8 * gg);
-        }
-      }
-      if constexpr (kInt8) {
+        for (int m = 0; m < D / 32; ++m) cw.v[h][m] = *reinterpret_cast<const uint32_t*>(vr + (16 * m + c) * L::VROW + 4 * g);
         const char* sc = src + 2 * L::KSUB + 2 * L::VSUB;
         cw.ks[h] = *reinterpret_cast<const f32x4*>(sc + h * 64 + 16 * g);
         cw.vs[h] = *reinterpret_cast<const f32x4*>(sc + (2 + h) * 64 + 16 * g);
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const char* kr = src + h * L::KSUB + c * L::KROW;
+        if constexpr (kInt8) {
+#pragma unroll
+          for (int jj = 0; jj < NJ / 2; ++jj) cw.k[h][jj] = *reinterpret_cast<const u32x4*>(kr + 16 * g + 64 * jj);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) cw.k[h][j] = *reinterpret_cast<const u32x4*>(kr + (32 * j + 8 * g) * 2);
+        }
+        const char* vr = src + 2 * L::KSUB + h * L::VSUB;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) {
+          if constexpr (kInt8) {
+            cw.v[h][n] = *reinterpret_cast<const uint32_t*>(vr + (16 * n + c) * L::VROW + 4 * g);
+          } else {
+            const int gg = g ^ ((c >> 3) & 1);
+            cw.v[h][n] = *reinterpret_cast<const u32x2*>(vr + (16 * n + c) * L::VROW + 8 * gg);
+          }
+        }
+        if constexpr (kInt8) {
+          const char* sc = src + 2 * L::KSUB + 2 * L::VSUB;
+          cw.ks[h] = *reinterpret_cast<const f32x4*>(sc + h * 64 + 16 * g);
+          cw.vs[h] = *reinterpret_cast<const f32x4*>(sc + (2 + h) * 64 + 16 * g);
+        }
       }
     }
   };
 
   float m_run[NT], l_run[NT];
+  float pv_run[NT];  // INT4: sum_t p_t v_scale_t (this lane's tokens)
   f32x4 acc[NT][NN];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     m_run[t] = -INFINITY;
     l_run[t] = 0.f;
+    pv_run[t] = 0.f;
 #pragma unroll
     for (int n = 0; n < NN; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto consume = [&](const Chunk<kInt8, D>& cw, int ch) {
+  auto consume = [&](const ChunkT& cw, int ch) {
     const int t0 = t_begin + ch * 32;
     const bool tail = (t0 + 32) > t_end;  // only a lone last block at bs = 16
-    // V^T operands of the chunk, shared by the query tiles
+    // V^T operands of the chunk, shared by the query tiles (INT4: operand
+    // 2m holds the even dims of dim pairs 16m + c, 2m + 1 the odd ones)
     u32x4 vw[NN];
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
-      if constexpr (kInt8) {
+      if constexpr (kI4) {
+        uint32_t lo0, hi0, lo1, hi1;
+        int4_nibbles(cw.v[0][n / 2], lo0, hi0);
+        int4_nibbles(cw.v[1][n / 2], lo1, hi1);
+        const u32x2 a0 = nib4_to_bf16((n & 1) ? hi0 : lo0), a1 = nib4_to_bf16((n & 1) ? hi1 : lo1);
+        vw[n] = u32x4{a0.x, a0.y, a1.x, a1.y};
+      } else if constexpr (kInt8) {
         vw[n] = u32x4{codes_to_bf16x2<KV, 0>(cw.v[0][n]), codes_to_bf16x2<KV, 1>(cw.v[0][n]),
                       codes_to_bf16x2<KV, 0>(cw.v[1][n]), codes_to_bf16x2<KV, 1>(cw.v[1][n])};
       } else {
@@ -268,7 +318,16 @@ void cascade_prefix_kernel(DecodeParams p) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         s[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (kInt8) {
+        if constexpr (kI4) {
+          s[h] = f32x4{-k_off[t], -k_off[t], -k_off[t], -k_off[t]};
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            uint32_t lo, hi;
+            int4_nibbles(cw.k[h][j], lo, hi);
+            const u32x2 a = nib4_to_bf16(lo), bq = nib4_to_bf16(hi);
+            s[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(u32x4{a.x, a.y, bq.x, bq.y}), qf[t][j], s[h], 0, 0, 0);
+          }
+        } else if constexpr (kInt8) {
 #pragma unroll
           for (int jj = 0; jj < NJ / 2; ++jj) {
             const u32x4 w = cw.k[h][jj];
@@ -318,8 +377,11 @@ void cascade_prefix_kernel(DecodeParams p) {
       mx = groups_max(mx);
       const float m_new = fmaxf(m_run[t], mx);
       if (__any(m_new > m_run[t])) {
-        const float alpha = fast_exp2(m_run[t] - m_new);
+        float alpha = fast_exp2(m_run[t] - m_new);
+        // multi-query: a column that has seen nothing yet (-inf - -inf)
+        if constexpr (kMQ) alpha = (m_new == -INFINITY) ? 1.f : alpha;
         l_run[t] *= alpha;
+        if constexpr (kI4) pv_run[t] *= alpha;
 #pragma unroll
         for (int n = 0; n < NN; ++n) acc[t][n] *= alpha;
         m_run[t] = m_new;
@@ -338,6 +400,10 @@ void cascade_prefix_kernel(DecodeParams p) {
         if constexpr (kInt8) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) pr[e] *= vs[e >> 2][e & 3];
+        }
+        if constexpr (kI4) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pv_run[t] += pr[e];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -367,7 +433,7 @@ void cascade_prefix_kernel(DecodeParams p) {
     const bool more = ch + 1 < nchunks;
     if (more) piece_load(ch + 1);
     {
-      Chunk<kInt8, D> cw;
+      ChunkT cw;
       lds_chunk(ch & 1, cw);
       consume(cw, ch);
     }
@@ -379,14 +445,28 @@ void cascade_prefix_kernel(DecodeParams p) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const float Lsum = groups_sum(l_run[t]);
+    if constexpr (kI4) {  // remove the V offset of this wave's tokens
+      const float v_off = kInt4Offset * groups_sum(pv_run[t]);
+#pragma unroll
+      for (int n = 0; n < NN; ++n) acc[t][n] -= v_off;
+    }
     const int r = q0 + 16 * t + c;
     if (r >= nq) continue;
     const size_t qr = kMQ ? static_cast<size_t>(qrow0 + r / G) : static_cast<size_t>(gs + r / G);
     const size_t bh = qr * H + kvh * G + r % G;
     const size_t slot = bh * p.num_parts + part;
     float* arow = p.ws_acc + slot * D;
+    if constexpr (kI4) {  // lane holds dims 32m + 8g .. + 7: tiles 2m (even), 2m + 1 (odd)
 #pragma unroll
-    for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[t][n];
+      for (int m = 0; m < NN / 2; ++m) {
+        const f32x4 e = acc[t][2 * m], o = acc[t][2 * m + 1];
+        *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
+        *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[t][n];
+    }
     if (g == 0) {
       p.ws_m[slot] = m_run[t];
       p.ws_l[slot] = Lsum;
@@ -419,6 +499,7 @@ hipError_t launch_kv(const DecodeParams& p, int units, int max_rows, int parts, 
 template <bool kMQ>
 hipError_t launch_mode(const DecodeParams& p, KvKind kv, int units, int max_rows, int parts, hipStream_t s) {
   if (kv == KvKind::I8) return launch_kv<KvKind::I8, kMQ>(p, units, max_rows, parts, s);
+  if (kv == KvKind::I4) return launch_kv<KvKind::I4, kMQ>(p, units, max_rows, parts, s);
   if (kv == KvKind::FP8) return launch_kv<KvKind::FP8, kMQ>(p, units, max_rows, parts, s);
   if (kv == KvKind::E5M2) return launch_kv<KvKind::E5M2, kMQ>(p, units, max_rows, parts, s);
   return launch_kv<KvKind::BF16, kMQ>(p, units, max_rows, parts, s);

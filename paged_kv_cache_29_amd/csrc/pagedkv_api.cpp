@@ -599,8 +599,8 @@ pkv_status pkv_paged_attention_decode_cascade(
                                  partition_tokens, nullptr, 0, nullptr, nullptr, false, &st,
                                  /*check_workspace=*/false);
   if (s != PKV_OK) return s;
-  if (st.kv == pkv::KvKind::F32 || st.kv == pkv::KvKind::I4)
-    return fail(PKV_ERR_UNSUPPORTED, "cascade decode supports bf16, int8 and FP8 caches only");
+  if (st.kv == pkv::KvKind::F32)
+    return fail(PKV_ERR_UNSUPPORTED, "cascade decode supports bf16, int8, FP8 and INT4 caches only");
   CascadeSizes cs;
   s = cascade_sizes(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq, num_groups,
                     max_group_size, max_shared_blocks, partition_tokens, prefix_partition_tokens, &cs);
@@ -742,11 +742,6 @@ pkv_status pkv_paged_attention_multi_query(
   s = mq_sizes(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq, num_query_tokens,
                max_queries_per_seq, partition_tokens, &ms);
   if (s != PKV_OK) return s;
-  if (st.kv == pkv::KvKind::I4 && !ms.decode_style)
-    return fail(PKV_ERR_UNSUPPORTED,
-                "multi-query attention over an INT4 cache supports at most %d (new token, head) pairs "
-                "per sequence and kv-head (max_queries_per_seq * G = %d)",
-                16 * pkv::kMqDecodeMaxTiles, max_queries_per_seq * (num_heads / num_kv_heads));
   if (num_seqs == 0 || num_query_tokens == 0) return ok();
   if (!query_start) return fail(PKV_ERR_INVALID, "multi-query attention needs query_start");
   const size_t need = mq_workspace_bytes(num_query_tokens, num_heads, head_dim, ms.parts);

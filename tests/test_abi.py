@@ -230,8 +230,7 @@ def _cascade(lib, **over):
 
 
 @pytest.mark.parametrize("over,code,frag", [
-    (dict(q_dtype=F32, kv_dtype=F32), UNSUPPORTED, "bf16, int8 and FP8"),
-    (dict(kv_dtype=I4, k_scale=_fake(9), v_scale=_fake(10)), UNSUPPORTED, "bf16, int8 and FP8"),
+    (dict(q_dtype=F32, kv_dtype=F32), UNSUPPORTED, "bf16, int8, FP8 and INT4"),
     (dict(num_groups=0), INVALID, "num_groups"),
     (dict(num_groups=5), INVALID, "num_groups"),
     (dict(max_group_size=0), INVALID, "max_group_size"),
@@ -322,8 +321,6 @@ def _mq(lib, **over):
 
 @pytest.mark.parametrize("over,code,frag", [
     (dict(q_dtype=F32, kv_dtype=F32), UNSUPPORTED, "bf16, int8, FP8 and INT4"),
-    (dict(kv_dtype=I4, k_scale=_fake(9), v_scale=_fake(10), max_queries_per_seq=13), UNSUPPORTED,
-     "at most 48"),
     (dict(num_query_tokens=-1), INVALID, "num_query_tokens"),
     (dict(max_queries_per_seq=0), INVALID, "max_queries_per_seq"),
     (dict(max_queries_per_seq=21), INVALID, "max_queries_per_seq"),

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 100, 255, 700]
 
 
-@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2"])
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2", "i4"])
 @pytest.mark.parametrize("G,D,bs", [(4, 128, 16), (8, 128, 32), (1, 64, 16), (2, 64, 32), (16, 128, 16)])
 @pytest.mark.parametrize("prefix,group", [(33, 3), (200, None), (64, 4)])
 def test_cascade_matches_oracle(kv, G, D, bs, prefix, group):

@@ -3,7 +3,8 @@ attention kernels read every 4-bit code (both nibbles, every value including
 -8, which the writer never produces) as its value.
 
 The INT4 attention paths also run through the generic parity tests (decode
-variants, fused step, block permutation, full-size workload)."""
+variants, fused step, block permutation, shared-prefix decode, multi-query
+attention, full-size workload)."""
 
 import numpy as np
 import pytest
@@ -12,7 +13,7 @@ import torch
 import oracle
 from oracle import int4 as oint4
 import paged_kv_cache_29_amd as pkv
-from paged_kv_cache_29_amd import workloads
+from paged_kv_cache_29_amd import blocks, workloads
 
 from gpu_helpers import DEV, assert_parity, bf16_bits_of, out_f64, to_dev
 
@@ -146,23 +147,61 @@ def test_offsets_cancel_with_one_signed_query():
     assert_parity(out_f64(out), ref, "i4", "one-signed q and V")
 
 
-def test_cascade_and_wide_multi_query_reject_int4():
-    """Shared-prefix decode has no INT4 kernel, nor has multi-query
-    attention beyond 48 (new token, head) pairs per (sequence, kv-head)."""
-    w = workloads.make_custom(5, [40, 50], 8, 2, 128, 16, kv_dtype="i4")
-    NB = w.num_blocks
-    kc = torch.zeros((NB, 2, 16, 64), dtype=torch.uint8, device=DEV)
-    vc = torch.zeros((NB, 2, 64, 16), dtype=torch.uint8, device=DEV)
-    sc = torch.ones((NB, 2, 16), dtype=torch.float32, device=DEV)
-    q = to_dev(w.q, "bf16")
-    bt, cl = to_dev(w.block_tables, "i32"), to_dev(w.context_lens, "i32")
-    with pytest.raises(NotImplementedError):
-        q13 = torch.zeros((26, 8, 128), dtype=torch.bfloat16, device=DEV)   # 13 x G = 52 > 48
-        pkv.paged_attention_multi_query(torch.empty_like(q13), q13, kc, vc, bt, cl,
-                                        torch.tensor([0, 13, 26], dtype=torch.int32, device=DEV),
-                                        w.scale, 8, 2, 128, 16, 13, k_scale=sc, v_scale=sc)
-    with pytest.raises(NotImplementedError):
-        pkv.paged_attention_decode_cascade(torch.empty_like(q), q, kc, vc, bt, cl,
-                                           torch.tensor([0, 2], dtype=torch.int32, device=DEV),
-                                           torch.tensor([1], dtype=torch.int32, device=DEV),
-                                           w.scale, 8, 2, 128, 16, 2, 1, k_scale=sc, v_scale=sc)
+def _random_int4_caches(rng, NB, Hkv, D, bs):
+    kc = rng.integers(0, 256, size=(NB, Hkv, bs, D // 2)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(NB, Hkv, D // 2, bs)).astype(np.uint8)
+    ks = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
+    vs = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
+    return kc, vc, ks, vs
+
+
+@pytest.mark.parametrize("G,D,bs", [(4, 128, 16), (8, 64, 32), (1, 128, 32)])
+def test_cascade_random_bytes(G, D, bs):
+    """Shared-prefix decode over INT4 caches of random bytes (every code,
+    -8 included, in K and V): the LDS-staged kernel reads the shared blocks
+    once per group, with the partition kernel's INT4 operands and offsets."""
+    rng = np.random.default_rng(60 + G + D + bs)
+    Hkv, H = 2, 2 * G
+    prefix = 96
+    lens = [prefix + x for x in (1, 17, 40, 200, 333)]
+    w = workloads.make_custom(61 + G, lens, H, Hkv, D, bs, kv_dtype="i4", prefix=prefix)
+    kc, vc, ks, vs = _random_int4_caches(rng, w.num_blocks, Hkv, D, bs)
+    gs, gsb, mg, msb = blocks.cascade_groups(w.block_tables, w.context_lens, bs)
+    assert msb >= prefix // bs - 1 and mg >= 3         # the sharing is really used
+    ref = oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, H, Hkv, D,
+                                  bs, "i4", "bf16", k_scale=ks, v_scale=vs)
+    for ppt in (0, 32):
+        out = torch.empty((len(lens), H, D), dtype=torch.bfloat16, device=DEV)
+        pkv.paged_attention_decode_cascade(
+            out, to_dev(w.q, "bf16"), to_dev(kc, "u8"), to_dev(vc, "u8"),
+            to_dev(w.block_tables, "i32"), to_dev(w.context_lens, "i32"),
+            torch.from_numpy(gs).to(DEV), torch.from_numpy(gsb).to(DEV), w.scale, H, Hkv, D, bs,
+            mg, msb, k_scale=to_dev(ks, "f32"), v_scale=to_dev(vs, "f32"), prefix_partition_tokens=ppt)
+        torch.cuda.synchronize()
+        assert_parity(out_f64(out), ref, "i4", f"cascade random bytes G={G} D={D} bs={bs} ppt={ppt}")
+
+
+@pytest.mark.parametrize("G,D,bs", [(4, 128, 16), (2, 64, 32), (16, 128, 32)])
+def test_wide_multi_query_random_bytes(G, D, bs):
+    """More than 48 (new token, head) pairs per (sequence, kv-head): the
+    LDS-staged kernel's multi-query mode over INT4 caches of random bytes."""
+    rng = np.random.default_rng(70 + G + D + bs)
+    Hkv, H = 2, 2 * G
+    lens = [30, 70, 129, 400]
+    n = [30, 13, 40, 26]
+    w = workloads.make_custom(71 + G, lens, H, Hkv, D, bs, kv_dtype="i4")
+    kc, vc, ks, vs = _random_int4_caches(rng, w.num_blocks, Hkv, D, bs)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = workloads.bf16_bits(rng.standard_normal((int(qs[-1]), H, D)).astype(np.float32))
+    ref = oracle.multi_query_attention(q, kc, vc, w.block_tables, w.context_lens, qs, w.scale, H, Hkv,
+                                       D, bs, "i4", "bf16", k_scale=ks, v_scale=vs)
+    assert max(n) * G > 48                              # the staged kernel runs
+    for pt in (0, 64):
+        out = torch.empty((int(qs[-1]), H, D), dtype=torch.bfloat16, device=DEV)
+        pkv.paged_attention_multi_query(out, to_dev(q, "bf16"), to_dev(kc, "u8"), to_dev(vc, "u8"),
+                                        to_dev(w.block_tables, "i32"), to_dev(w.context_lens, "i32"),
+                                        torch.from_numpy(qs).to(DEV), w.scale, H, Hkv, D, bs, max(n),
+                                        k_scale=to_dev(ks, "f32"), v_scale=to_dev(vs, "f32"),
+                                        partition_tokens=pt)
+        torch.cuda.synchronize()
+        assert_parity(out_f64(out), ref, "i4", f"wide multi-query G={G} D={D} bs={bs} pt={pt}")

@@ -98,19 +98,46 @@ def test_verify_straddling_partitions(kv, G):
     assert_parity(got, ref, kv, f"straddle {kv} G={G}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8", "i4"])
 @pytest.mark.parametrize("G,n", [(8, 5), (4, 8), (1, 16), (16, 2)])
-def test_both_kernels_agree(G, n):
+def test_both_kernels_agree(kv, G, n):
     """The same call through the partition kernel's multi-query mode (few
     columns) and, with a looser max_queries_per_seq bound, through the
     LDS-staged kernel: both match the oracle and each other."""
-    w = workloads.make_custom(30 + G, [n, 40, 333, 1000, 64 + n - 1], 2 * G, 2, 128, 16)
+    w = workloads.make_custom(30 + G, [n, 40, 333, 1000, 64 + n - 1], 2 * G, 2, 128, 16, kv_dtype=kv)
     a, ref, *_ = _run(w, [n] * 5, seed=n, partition_tokens=128)
     loose = (16 * 3) // G + 1                             # beyond the partition kernel's columns
-    b, ref2, *_ = _run(w, [n] * 5, seed=n, partition_tokens=128, max_queries=max(loose, n))
+    b, ref2, _, _, dw = _run(w, [n] * 5, seed=n, partition_tokens=128, max_queries=max(loose, n))
     assert np.array_equal(ref, ref2)
-    assert_parity(a, ref, "bf16", f"partition kernel G={G} n={n}")
-    assert_parity(b, ref, "bf16", f"staged kernel G={G} n={n}")
-    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-5)
+    assert_parity(a, ref, kv, f"partition kernel {kv} G={G} n={n}")
+    assert_parity(b, ref, kv, f"staged kernel {kv} G={G} n={n}")
+    # the same sums in different orders: within a bf16 unit plus fp32 noise.
+    # INT4 values enter the contractions as c + 136 (c in [-8, 7]), so the
+    # ~2^-17 relative error of each kernel's hi/lo weights acts on values up
+    # to 144 v_scale, and the offset removed afterwards (136 v_scale per unit
+    # of weight) is summed from the unrounded weights: up to (144 + 136)
+    # 2^-17 max(v_scale) per kernel, twice that between two kernels
+    slack = 1e-5
+    if kv == "i4":
+        slack += 2 * (144 + 136) * 2.0 ** -17 * float(np.nanmax(dw.v_scale.cpu().numpy()))
+    d = np.abs(a - b) - 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b))
+    assert np.all(d <= slack), f"kernels differ by {d.max():.3e} beyond a bf16 unit (slack {slack:.3e})"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8", "i4"])
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_partition_start_inside_a_column_tile(kv, G):
+    """Partitions that start between the positions of one column tile's new
+    tokens (context minus new tokens odd, partitions of 64): within a tile,
+    columns that see nothing yet in the partition sit beside columns that
+    do, and must keep their empty state (no exp(-inf + inf)) until they see
+    a token.  Enough columns for the LDS-staged kernel."""
+    lens = [201, 150, 97, 300]
+    n = [100, 60, 33, 77]                                 # 201 - 100 = 101: token 128 is in query 27's view
+    w = workloads.make_custom(90 + G, lens, 2 * G, 2, 128, 16, kv_dtype=kv)
+    got, ref, *_ = _run(w, n, seed=G, partition_tokens=64)
+    assert max(n) * G > 48
+    assert_parity(got, ref, kv, f"partition inside a tile {kv} G={G}")
 
 
 @pytest.mark.parametrize("G,D,bs,pt", [(8, 128, 16, 0), (4, 64, 32, 64), (1, 128, 32, 64), (2, 64, 16, 0)])
