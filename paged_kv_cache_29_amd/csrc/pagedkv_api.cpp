@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/pagedkv.h"
@@ -44,6 +45,47 @@ using pkv::ok;
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 bool block_size_ok(int32_t bs) { return bs == 16 || bs == 32; }
 bool group_ok(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+// A second stream per device for the shared-prefix kernel of cascade
+// decode: that kernel is bound by its contractions and softmax, the
+// partition kernel over each sequence's own tokens by HBM, and they write
+// disjoint workspace slots, so they run side by side; the caller's stream
+// waits for it (an event) before the reduce.  Created on first use with the
+// default priority and kept until the process ends.  The fork / join
+// sequence is enqueued under g_side_mutex so that concurrent callers never
+// re-record each other's events in between.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mutex;
+SideStream g_side[kMaxDevices];
+
+// The current device's side stream (caller holds g_side_mutex).
+hipError_t side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& ss = g_side[dev];
+  if (ss.stream == nullptr) {
+    SideStream n;
+    e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (n.join) hipEventDestroy(n.join);
+      if (n.fork) hipEventDestroy(n.fork);
+      if (n.stream) hipStreamDestroy(n.stream);
+      return e;
+    }
+    ss = n;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
 
 using pkv::kChunk;          // tokens per wave iteration
 using pkv::kMaxPartBlocks;  // block ids of one partition staged in LDS
@@ -230,15 +272,17 @@ pkv_status launch_reduce(const DecodeSetup& st, hipStream_t stream) {
 }
 
 // Shared-prefix partition length: the longest of 2048 ... 32 tokens that
-// still gives the prefix kernel one full round of workgroups (two per CU on
-// 256 CUs; at most kMaxPartBlocks blocks; a multiple of 32, hence of the
-// block size).
+// still gives the prefix kernel one workgroup per CU (256 CUs; at most
+// kMaxPartBlocks blocks; a multiple of 32, hence of the block size).  The
+// other half of each CU's workgroup slots is left to the partition kernel,
+// which runs beside it on the caller's stream (shared-prefix workload, bs
+// 16: 109-111 us per step against 118-121 us with one full round of 512).
 int32_t auto_prefix_part_tokens(int64_t prefix_units, int32_t block_size, int32_t max_shared_blocks) {
   const int64_t span = static_cast<int64_t>(max_shared_blocks) * block_size;
   int32_t pt = 32;
   for (int32_t cand : {2048, 1024, 512, 256, 128, 64}) {
     if (cand > kMaxPartBlocks * block_size) continue;
-    if (prefix_units * ((span + cand - 1) / cand) >= 512) {
+    if (prefix_units * ((span + cand - 1) / cand) >= 256) {
       pt = cand;
       break;
     }
@@ -632,12 +676,29 @@ pkv_status pkv_paged_attention_decode_cascade(
   p.num_parts = cs.pparts + cs.sparts;
   const hipStream_t strm = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (cs.pparts > 0) {
-    e = pkv::launch_cascade_prefix(p, st.kv, max_group_size, strm);
-    if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefix kernel launch failed: %s", hipGetErrorString(e));
+  {
+    // prefix kernel on the side stream, partition kernel on the caller's,
+    // joined before the reduce
+    std::unique_lock<std::mutex> lock(g_side_mutex, std::defer_lock);
+    SideStream* ss = nullptr;
+    if (cs.pparts > 0) {
+      lock.lock();
+      e = side_stream(&ss);
+      if (e == hipSuccess) e = hipEventRecord(ss->fork, strm);
+      if (e == hipSuccess) e = hipStreamWaitEvent(ss->stream, ss->fork, 0);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefix stream fork failed: %s", hipGetErrorString(e));
+      e = pkv::launch_cascade_prefix(p, st.kv, max_group_size, ss->stream);
+      if (e == hipSuccess) e = hipEventRecord(ss->join, ss->stream);
+      if (e != hipSuccess) return fail(PKV_ERR_HIP, "prefix kernel launch failed: %s", hipGetErrorString(e));
+    }
+    e = pkv::launch_decode_mfma(p, st.kv, strm);
+    if (ss != nullptr) {  // join even after a failed launch: the prefix kernel writes the workspace
+      const hipError_t ej = hipStreamWaitEvent(strm, ss->join, 0);
+      if (e == hipSuccess && ej != hipSuccess)
+        return fail(PKV_ERR_HIP, "prefix stream join failed: %s", hipGetErrorString(ej));
+    }
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "partition kernel launch failed: %s", hipGetErrorString(e));
   }
-  e = pkv::launch_decode_mfma(p, st.kv, strm);
-  if (e != hipSuccess) return fail(PKV_ERR_HIP, "partition kernel launch failed: %s", hipGetErrorString(e));
   e = pkv::launch_decode_reduce(p, st.out_bf16, strm);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -84,3 +84,48 @@ def test_cascade_shared_prefix_workload_full_size(bs):
     ref = oracle_out(w, samples=samples)
     for b, h in samples:
         assert_parity(got[b, h], ref[b, h], "bf16", f"prefix bs={bs} (b={b}, h={h})")
+
+
+def test_cascade_graph_replays_match_eager():
+    """The cascade call forks its prefix kernel onto the library's second
+    stream and joins it back by events; captured in a graph, every replay
+    (new queries copied in eagerly, synchronised between replays) equals an
+    eager call on the same inputs bit for bit."""
+    import torch
+    from gpu_helpers import DEV, out_f64
+    import paged_kv_cache_29_amd as pkv
+    from paged_kv_cache_29_amd import blocks
+
+    w = workloads.make_custom(77, [300 + x for x in RAGGED], 16, 2, 128, 16, prefix=300)
+    dw = DeviceWorkload(w)
+    dw.step_cascade()                                   # cache written; side stream created
+    gs, gsb, mg, ms = blocks.cascade_groups(w.block_tables, w.context_lens, w.block_size)
+    gs_d, gsb_d = torch.from_numpy(gs).to(DEV), torch.from_numpy(gsb).to(DEV)
+    need = pkv.cascade_workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                      w.block_size, w.block_tables.shape[1], len(gsb), mg, ms)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=DEV)
+    q = dw.q.clone()
+    out = torch.empty_like(q)
+
+    def call(o):
+        pkv.paged_attention_decode_cascade(o, q, dw.k_cache, dw.v_cache, dw.block_tables,
+                                           dw.context_lens, gs_d, gsb_d, w.scale, w.num_heads,
+                                           w.num_kv_heads, w.head_dim, w.block_size, mg, ms,
+                                           workspace=ws)
+
+    call(out)                                           # warm, outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    for i in range(3):
+        q.copy_(torch.randn(q.shape, generator=gen).to(torch.bfloat16).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_f64(out)
+        ref = torch.empty_like(q)
+        call(ref)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, out_f64(ref)), f"replay {i} differs from the eager call"
