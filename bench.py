@@ -458,7 +458,8 @@ def cpu_baseline(w, seconds):
     return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done_seqs} of {w.num_seqs} sequences x all {w.num_heads} heads "
                     f"({done_tokens} context tokens) of {w.name}, {el:.1f} s; "
-                    f"cpu_count={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}",
+                    f"cpu_count={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}, "
+                    f"blas_threads={threads}",
             "cache_writes": cpu_cache_writes(w)}
 
 
