@@ -11,7 +11,7 @@
 // sequences at once: the matrix-core N dimension holds (sequence, head)
 // pairs of the group instead of one sequence's heads.
 //
-// Each workgroup owns (group, kv-head, kPrefixQueries queries, partition of
+// Each workgroup owns (group, kv-head, 64 NT queries, partition of
 // prefix_part_tokens shared tokens) and leaves, per query, the partial (max,
 // sum, unnormalised output) of its partition in workspace slot `partition`;
 // the reduce kernel merges them with the partials of each sequence's own
@@ -20,7 +20,8 @@
 // The kv-head index varies fastest in the grid, so with 8 kv-heads each
 // XCD's L2 serves one kv-head's shared blocks.
 //
-// Work split: every wave owns 16 * kPrefixTiles queries and walks every
+// Work split: every wave owns 16 NT queries (NT = 2, or 1 when the unit's
+// columns fit 64: prefix_tiles_for) and walks every
 // 32-token chunk of the partition.  A chunk is staged once in LDS: its four
 // pieces (K and V of the two 16-token sub-tiles, plus int8 scales) are
 // loaded by the four waves, one piece each, while the previous chunk is
@@ -61,12 +62,20 @@ struct PrefixLds {
   static constexpr int UNITS = (PIECE + 16 * kWave - 1) / (16 * kWave);
 };
 
+// Waves per SIMD: two tiles' states per wave take two waves' registers;
+// one tile's (at most 173 VGPRs) fit three, which hide more of the chunk
+// loop's LDS and barrier latency (70B GQA, 8-token verification per call:
+// 545 us at two waves, 470 us at three; 667 us with two tiles per wave).
+template <int NT>
+constexpr int kPrefixWavesPerSimd = NT == 1 ? 3 : 2;
+
 // KV: BF16, or codes with per-token scales (I8, FP8: bytes; I4: nibbles,
 // with the partition kernel's INT4 operands and offsets).  kMQ: the
 // multi-query form (one sequence's new tokens x heads as the columns, its
 // whole context partitioned, each column masked causally at its position).
 template <KvKind KV, int D, int BS, int NT, bool kMQ>
-__global__ __launch_bounds__(kDecodeWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kDecodeWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(kPrefixWavesPerSimd<NT>, kPrefixWavesPerSimd<NT>)))
 void cascade_prefix_kernel(DecodeParams p) {
   constexpr bool kInt8 = KV != KvKind::BF16;  // codes (int8, FP8 E4M3 / E5M2, INT4) with scales
   constexpr bool kI4 = KV == KvKind::I4;
@@ -312,8 +321,9 @@ void cascade_prefix_kernel(DecodeParams p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       // every column of the tile is padding (uniform): skip its arithmetic
-      // (not for int8 at D = 128, whose registers are too tight for the branch)
-      if (!(KV == KvKind::I8 && D == 128) && q0 + 16 * t >= nq) continue;
+      // (not for int8 at D = 128 with two tiles per wave, whose registers
+      // are too tight for the branch)
+      if (!(KV == KvKind::I8 && D == 128 && NT == 2) && q0 + 16 * t >= nq) continue;
       f32x4 s[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -479,11 +489,15 @@ void cascade_prefix_kernel(DecodeParams p) {
 template <KvKind KV, int D, int BS, bool kMQ>
 hipError_t launch_t(const DecodeParams& p, int units, int max_rows, int parts, hipStream_t s) {
   const int G = p.num_heads / p.num_kv_heads;
-  const int qtiles = (max_rows * G + kPrefixQueries - 1) / kPrefixQueries;
+  const int64_t cols = static_cast<int64_t>(max_rows) * G;
+  const int64_t qtiles = (cols + prefix_queries_for(cols) - 1) / prefix_queries_for(cols);
   const dim3 grid(static_cast<unsigned>(units * p.num_kv_heads), static_cast<unsigned>(qtiles),
                   static_cast<unsigned>(parts));
-  hipLaunchKernelGGL((cascade_prefix_kernel<KV, D, BS, kPrefixTiles, kMQ>), grid,
-                     dim3(kDecodeWaves * kWave), 0, s, p);
+  static_assert(kPrefixTiles == 2, "one instance per tile count");
+  if (prefix_tiles_for(cols) == 1)
+    hipLaunchKernelGGL((cascade_prefix_kernel<KV, D, BS, 1, kMQ>), grid, dim3(kDecodeWaves * kWave), 0, s, p);
+  else
+    hipLaunchKernelGGL((cascade_prefix_kernel<KV, D, BS, 2, kMQ>), grid, dim3(kDecodeWaves * kWave), 0, s, p);
   return hipGetLastError();
 }
 

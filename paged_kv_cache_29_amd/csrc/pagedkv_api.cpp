@@ -290,7 +290,7 @@ int32_t auto_prefix_part_tokens(int64_t prefix_units, int32_t block_size, int32_
   return pt;
 }
 
-using pkv::kPrefixQueries;  // queries per prefix workgroup
+using pkv::prefix_queries_for;  // queries per prefix workgroup
 
 struct CascadeSizes {
   int32_t ppt, pparts, spt, sparts, qtiles;
@@ -312,7 +312,8 @@ pkv_status cascade_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_hea
     return fail(PKV_ERR_INVALID, "max_shared_blocks must be in [0, max_blocks_per_seq] (got %d)",
                 max_shared_blocks);
   const int32_t G = num_heads / num_kv_heads;
-  const int64_t qtiles = (static_cast<int64_t>(max_group_size) * G + kPrefixQueries - 1) / kPrefixQueries;
+  const int64_t cols = static_cast<int64_t>(max_group_size) * G;
+  const int64_t qtiles = (cols + prefix_queries_for(cols) - 1) / prefix_queries_for(cols);
   if (qtiles > 65535) return fail(PKV_ERR_UNSUPPORTED, "max_group_size * G too large");
   if (static_cast<int64_t>(num_groups) * num_kv_heads > 0x7fffffff)
     return fail(PKV_ERR_UNSUPPORTED, "num_groups * num_kv_heads too large");
@@ -379,7 +380,7 @@ pkv_status mq_sizes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, i
   const int32_t G = num_heads / num_kv_heads;
   const int64_t cols = static_cast<int64_t>(max_queries > 0 ? max_queries : 1) * G;
   const bool decode_style = cols <= 16 * pkv::kMqDecodeMaxTiles;
-  const int64_t qtiles = decode_style ? (cols + 15) / 16 : (cols + kPrefixQueries - 1) / kPrefixQueries;
+  const int64_t qtiles = decode_style ? (cols + 15) / 16 : (cols + prefix_queries_for(cols) - 1) / prefix_queries_for(cols);
   if (qtiles > 65535) return fail(PKV_ERR_UNSUPPORTED, "max_queries_per_seq * G too large");
   int32_t pt = partition_tokens;
   if (pt == 0) {

@@ -103,10 +103,17 @@ constexpr int kChunk = 32;
 // stage them in LDS arrays of this size, and the host rejects longer
 // partitions.
 constexpr int kMaxPartBlocks = 128;
-// Query-column tiles (16 queries each) per wave of the shared-prefix kernel,
-// and queries per workgroup.
+// Query-column tiles (16 queries each) per wave of the shared-prefix
+// kernel: two (128 columns per workgroup), or one when a unit's columns fit
+// 64, so that no wave of the workgroup sits idle beside the others.
 constexpr int kPrefixTiles = 2;
-constexpr int kPrefixQueries = 16 * kPrefixTiles * kDecodeWaves;
+__host__ __device__ constexpr int prefix_tiles_for(int64_t columns) {
+  return columns <= 16 * kDecodeWaves ? 1 : kPrefixTiles;
+}
+// Queries per workgroup for a unit of `columns` query columns.
+__host__ __device__ constexpr int prefix_queries_for(int64_t columns) {
+  return 16 * prefix_tiles_for(columns) * kDecodeWaves;
+}
 
 // Tokens of group g attended by the shared-prefix kernel: its shared
 // blocks, capped at the whole blocks of its first sequence's context (so

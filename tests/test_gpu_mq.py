@@ -126,18 +126,23 @@ def test_both_kernels_agree(kv, G, n):
 
 @pytest.mark.parametrize("kv", ["bf16", "i8", "i4"])
 @pytest.mark.parametrize("G", [1, 2, 4])
-def test_partition_start_inside_a_column_tile(kv, G):
+@pytest.mark.parametrize("width", ["wide", "narrow"])
+def test_partition_start_inside_a_column_tile(kv, G, width):
     """Partitions that start between the positions of one column tile's new
     tokens (context minus new tokens odd, partitions of 64): within a tile,
     columns that see nothing yet in the partition sit beside columns that
     do, and must keep their empty state (no exp(-inf + inf)) until they see
-    a token.  Enough columns for the LDS-staged kernel."""
+    a token.  Wide: the LDS-staged kernel with two tiles per wave; narrow:
+    at most 64 columns (G = 4: the staged kernel with one tile per wave;
+    G = 1, 2: the partition kernel's multi-query mode)."""
     lens = [201, 150, 97, 300]
-    n = [100, 60, 33, 77]                                 # 201 - 100 = 101: token 128 is in query 27's view
+    # wide: 201 - 100 = 101, token 128 first seen by query 27; narrow:
+    # 201 - 16 = 185, token 192 first seen by query 7
+    n = [100, 60, 33, 77] if width == "wide" else [16, 13, 14, 15]
     w = workloads.make_custom(90 + G, lens, 2 * G, 2, 128, 16, kv_dtype=kv)
     got, ref, *_ = _run(w, n, seed=G, partition_tokens=64)
-    assert max(n) * G > 48
-    assert_parity(got, ref, kv, f"partition inside a tile {kv} G={G}")
+    assert (max(n) * G > 48) == (width == "wide" or G == 4)
+    assert_parity(got, ref, kv, f"partition inside a tile {kv} G={G} {width}")
 
 
 @pytest.mark.parametrize("G,D,bs,pt", [(8, 128, 16, 0), (4, 64, 32, 64), (1, 128, 32, 64), (2, 64, 16, 0)])
