@@ -38,26 +38,36 @@ namespace {
 // store 64 contiguous bytes of its row at a time.
 constexpr int kTokensPerWave = 16;
 
-template <typename T>
-__global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
+// The bit-copy write also has a small-batch form: a decode step writes one
+// token per sequence, each into a different block, so every V element is a
+// store to its own line, and scattered stores go through a CU's address
+// path about one line per clock.  There a wave takes 4 tokens (16 lanes per
+// token, one 16-byte piece each) and a workgroup is one wave, which spreads
+// the stores over up to 4x as many waves and 4x as many CUs as the 16-token
+// form (7B step, 32 tokens x 32 kv-heads: 16 CUs -> all 256).
+//
+// TPW tokens per wave; WPG waves per workgroup.
+template <typename T, int D, int TPW, int WPG>
+__global__ __launch_bounds__(WPG * kWave) void cache_write_kernel(WriteParams p) {
   constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
-  const int D = p.head_dim;
+  constexpr int LPT = kWave / TPW;     // lanes per token
+  constexpr int NV = D / EPV;          // 16-byte vectors per row
+  constexpr int VPL = (NV + LPT - 1) / LPT;  // vectors per lane per row
   const int BS = p.block_size;
   const int Hkv = p.num_kv_heads;
-  const int VPL = D / EPV / 4;         // vectors per lane per row
   const int lane = threadIdx.x & (kWave - 1);
-  const int ti = lane & 15;
-  const int q = lane >> 4;
-  const int64_t units = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * Hkv;
-  const T* k = static_cast<const T*>(p.k);
-  const T* v = static_cast<const T*>(p.v);
-  T* kc = static_cast<T*>(p.k_cache);
-  T* vc = static_cast<T*>(p.v_cache);
-  for (int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; u < units;
-       u += static_cast<int64_t>(gridDim.x) * 4) {
+  const int ti = lane % TPW;
+  const int q = lane / TPW;
+  const int64_t units = (p.num_tokens + TPW - 1) / TPW * Hkv;
+  const T* __restrict__ k = static_cast<const T*>(p.k);
+  const T* __restrict__ v = static_cast<const T*>(p.v);
+  T* __restrict__ kc = static_cast<T*>(p.k_cache);
+  T* __restrict__ vc = static_cast<T*>(p.v_cache);
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * WPG + threadIdx.x / kWave; u < units;
+       u += static_cast<int64_t>(gridDim.x) * WPG) {
     const int64_t tg = u / Hkv;
     const int h = static_cast<int>(u - tg * Hkv);
-    const int64_t t = tg * kTokensPerWave + ti;
+    const int64_t t = tg * TPW + ti;
     if (t >= p.num_tokens) continue;
     const int64_t slot = p.slot_mapping[t];
     if (slot < 0) continue;
@@ -65,12 +75,23 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
     const int row = static_cast<int>(slot - blk * BS);
     const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * D;
     const int64_t src = (t * Hkv + h) * D;
+    // every load of the lane's share of the row first, then the stores: the
+    // new rows and the cache are different buffers, and issuing the loads
+    // together costs one memory latency instead of one per piece
+    // (bf16 at D = 64 in the small-batch form: half the lanes of a token)
+    if (NV % LPT != 0 && q >= NV) continue;
+    u32x4 kk[VPL], vv[VPL];
+#pragma unroll
     for (int j = 0; j < VPL; ++j) {
-      const int d0 = (4 * j + q) * EPV;
-      *reinterpret_cast<u32x4*>(kc + tile + static_cast<int64_t>(row) * D + d0) =
-          *reinterpret_cast<const u32x4*>(k + src + d0);
-      const u32x4 vv = *reinterpret_cast<const u32x4*>(v + src + d0);
-      const T* ve = reinterpret_cast<const T*>(&vv);
+      const int d0 = (LPT * j + q) * EPV;
+      kk[j] = *reinterpret_cast<const u32x4*>(k + src + d0);
+      vv[j] = *reinterpret_cast<const u32x4*>(v + src + d0);
+    }
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+      const int d0 = (LPT * j + q) * EPV;
+      *reinterpret_cast<u32x4*>(kc + tile + static_cast<int64_t>(row) * D + d0) = kk[j];
+      const T* ve = reinterpret_cast<const T*>(&vv[j]);
 #pragma unroll
       for (int e = 0; e < EPV; ++e) vc[tile + static_cast<int64_t>(d0 + e) * BS + row] = ve[e];
     }
@@ -79,49 +100,60 @@ __global__ __launch_bounds__(256) void cache_write_kernel(WriteParams p) {
 
 // The quantising write: one wave per (16 tokens, kv-head, K or V); the
 // four lanes of a token each hold a quarter of its row (4 dims of every 16),
-// and the row's absmax is the max over them (two xor shuffles).
+// all loaded before any is used, and the row's absmax is the max over the
+// four lane groups.
 // KV: I8 (s = absmax / 127, quantize_code), FP8 (s = absmax / 448, fp8_code),
 // E5M2 (s = absmax / 57344, e5m2_code) or I4 (s = absmax / 7,
 // quantize_sym<7>, tiles of half the bytes).
-template <KvKind KV>
-__global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
+// Small-batch form as for the bit copy (TPW = 4, one wave per workgroup):
+// a token's 16 lanes are contiguous there, and its absmax is a butterfly
+// over them.
+template <KvKind KV, int D, int TPW, int WPG>
+__global__ __launch_bounds__(WPG * kWave) void cache_write_codes_kernel(WriteParams p) {
   constexpr float kMax = KV == KvKind::FP8    ? 448.0f
                          : KV == KvKind::E5M2 ? 57344.0f
                          : KV == KvKind::I4   ? 7.0f
                                               : 127.0f;
-  const int D = p.head_dim;
+  static_assert(TPW == kTokensPerWave || TPW == 4, "token mappings");
+  constexpr int LPT = kWave / TPW;     // lanes per token
+  constexpr int NJ = D / 4 / LPT;      // 4-dim groups per lane
   const int BS = p.block_size;
   const int Hkv = p.num_kv_heads;
-  const int NJ = D / 16;               // 4-dim groups per lane
   const int lane = threadIdx.x & (kWave - 1);
-  const int ti = lane & 15;
-  const int q = lane >> 4;
-  const int64_t units = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * Hkv * 2;
-  const float* k = static_cast<const float*>(p.k);
-  const float* v = static_cast<const float*>(p.v);
-  uint8_t* kc = static_cast<uint8_t*>(p.k_cache);
-  uint8_t* vc = static_cast<uint8_t*>(p.v_cache);
-  for (int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave; u < units;
-       u += static_cast<int64_t>(gridDim.x) * 4) {
+  const int ti = TPW == kTokensPerWave ? (lane & 15) : lane / LPT;
+  const int q = TPW == kTokensPerWave ? (lane >> 4) : lane % LPT;
+  const int64_t units = (p.num_tokens + TPW - 1) / TPW * Hkv * 2;
+  const float* __restrict__ k = static_cast<const float*>(p.k);
+  const float* __restrict__ v = static_cast<const float*>(p.v);
+  uint8_t* __restrict__ kc = static_cast<uint8_t*>(p.k_cache);
+  uint8_t* __restrict__ vc = static_cast<uint8_t*>(p.v_cache);
+  for (int64_t u = static_cast<int64_t>(blockIdx.x) * WPG + threadIdx.x / kWave; u < units;
+       u += static_cast<int64_t>(gridDim.x) * WPG) {
     // u = ((token group) * Hkv + head) * 2 + (K or V): uniform across the wave
     const bool is_v = (u & 1) != 0;
     const int64_t th = u >> 1;
     const int64_t tg = th / Hkv;
     const int h = static_cast<int>(th - tg * Hkv);
-    const int64_t t = tg * kTokensPerWave + ti;
+    const int64_t t = tg * TPW + ti;
     const int64_t slot = t < p.num_tokens ? p.slot_mapping[t] : -1;
     const float* src = (is_v ? v : k) + (t * Hkv + h) * D;
-    f32x4 x[8];                        // NJ <= 8 groups of 4 dims: dims 4 (4 j + q) + e
-    float a = 0.f;
+    f32x4 x[NJ];                       // groups of 4 dims: dims 4 (LPT j + q) + e
+#pragma unroll
     for (int j = 0; j < NJ; ++j) {
       x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (slot >= 0) x[j] = *reinterpret_cast<const f32x4*>(src + 4 * (4 * j + q));
-      a = fmaxf(a, fmaxf(fmaxf(fabsf(x[j][0]), fabsf(x[j][1])), fmaxf(fabsf(x[j][2]), fabsf(x[j][3]))));
+      if (slot >= 0) x[j] = *reinterpret_cast<const f32x4*>(src + 4 * (LPT * j + q));
     }
-    // every lane of the wave takes part in the shuffles; the four lanes of a
-    // token are i, i + 16, i + 32, i + 48
-    a = fmaxf(a, __shfl_xor(a, 16, kWave));
-    a = fmaxf(a, __shfl_xor(a, 32, kWave));
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      a = fmaxf(a, fmaxf(fmaxf(fabsf(x[j][0]), fabsf(x[j][1])), fmaxf(fabsf(x[j][2]), fabsf(x[j][3]))));
+    // every lane of the wave takes part
+    if constexpr (TPW == kTokensPerWave) {
+      a = groups_max(a);  // a token's lanes i, i + 16, i + 32, i + 48
+    } else {
+#pragma unroll
+      for (int o = LPT / 2; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, kWave));
+    }
     if (slot < 0) continue;
     const float s = a / kMax;
     const int64_t blk = slot / BS;
@@ -129,8 +161,9 @@ __global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
     if (q == 0) (is_v ? p.v_scale : p.k_scale)[(blk * Hkv + h) * BS + row] = (s > 0.f) ? s : 0.f;
     if constexpr (KV == KvKind::I4) {
       const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * (D / 2);
+#pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const int d0 = 4 * (4 * j + q);
+        const int d0 = 4 * (LPT * j + q);
         const uint32_t b0 = pack_int4_pair(quantize_sym<7>(x[j][0], s), quantize_sym<7>(x[j][1], s));
         const uint32_t b1 = pack_int4_pair(quantize_sym<7>(x[j][2], s), quantize_sym<7>(x[j][3], s));
         if (!is_v) {
@@ -144,8 +177,9 @@ __global__ __launch_bounds__(256) void cache_write_codes_kernel(WriteParams p) {
       continue;
     }
     const int64_t tile = (blk * Hkv + h) * static_cast<int64_t>(BS) * D;
+#pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int d0 = 4 * (4 * j + q);
+      const int d0 = 4 * (LPT * j + q);
       uint32_t codes[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -171,32 +205,54 @@ unsigned grid_for(int64_t work, int per_block) {
   return static_cast<unsigned>(blocks < 1 ? 1 : (blocks > cap ? cap : blocks));
 }
 
-}  // namespace
-
-hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s) {
-  // one wave per (16 tokens, kv-head), four waves per workgroup
-  const int64_t waves = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * p.num_kv_heads;
-  const unsigned grid = grid_for(waves, 4);
-  if (kind == KvKind::F32)
-    hipLaunchKernelGGL(cache_write_kernel<float>, dim3(grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(cache_write_kernel<uint16_t>, dim3(grid), dim3(256), 0, s, p);
+template <KvKind KV, int D>
+hipError_t launch_codes_t(const WriteParams& p, hipStream_t s) {
+  // as launch_write_t: 16-token waves, or 4-token waves for small batches
+  const int64_t waves16 = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * p.num_kv_heads * 2;
+  if (waves16 < 1024) {
+    const int64_t waves4 = (p.num_tokens + 3) / 4 * p.num_kv_heads * 2;
+    hipLaunchKernelGGL((cache_write_codes_kernel<KV, D, 4, 1>), dim3(grid_for(waves4, 1)), dim3(kWave), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((cache_write_codes_kernel<KV, D, kTokensPerWave, 4>), dim3(grid_for(waves16, 4)),
+                       dim3(4 * kWave), 0, s, p);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s) {
-  // one wave per (16 tokens, kv-head, K or V), four waves per workgroup
-  const int64_t waves = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * p.num_kv_heads * 2;
-  const unsigned grid = grid_for(waves, 4);
-  if (kind == KvKind::FP8)
-    hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::FP8>, dim3(grid), dim3(256), 0, s, p);
-  else if (kind == KvKind::I4)
-    hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::I4>, dim3(grid), dim3(256), 0, s, p);
-  else if (kind == KvKind::E5M2)
-    hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::E5M2>, dim3(grid), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(cache_write_codes_kernel<KvKind::I8>, dim3(grid), dim3(256), 0, s, p);
+template <KvKind KV>
+hipError_t launch_codes(const WriteParams& p, hipStream_t s) {
+  return p.head_dim == 128 ? launch_codes_t<KV, 128>(p, s) : launch_codes_t<KV, 64>(p, s);  // else 64
+}
+
+
+}  // namespace
+
+template <typename T, int D>
+hipError_t launch_write_t(const WriteParams& p, hipStream_t s) {
+  // 16-token waves, four per workgroup; fewer than 1024 such waves (four
+  // per CU) is a small batch: 4-token waves, one per workgroup
+  const int64_t waves16 = (p.num_tokens + kTokensPerWave - 1) / kTokensPerWave * p.num_kv_heads;
+  if (waves16 < 1024) {
+    const int64_t waves4 = (p.num_tokens + 3) / 4 * p.num_kv_heads;
+    hipLaunchKernelGGL((cache_write_kernel<T, D, 4, 1>), dim3(grid_for(waves4, 1)), dim3(kWave), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((cache_write_kernel<T, D, kTokensPerWave, 4>), dim3(grid_for(waves16, 4)),
+                       dim3(4 * kWave), 0, s, p);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s) {
+  const bool d128 = p.head_dim == 128;  // else 64 (validated by the caller)
+  if (kind == KvKind::F32) return d128 ? launch_write_t<float, 128>(p, s) : launch_write_t<float, 64>(p, s);
+  return d128 ? launch_write_t<uint16_t, 128>(p, s) : launch_write_t<uint16_t, 64>(p, s);
+}
+
+hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s) {
+  if (kind == KvKind::FP8) return launch_codes<KvKind::FP8>(p, s);
+  if (kind == KvKind::I4) return launch_codes<KvKind::I4>(p, s);
+  if (kind == KvKind::E5M2) return launch_codes<KvKind::E5M2>(p, s);
+  return launch_codes<KvKind::I8>(p, s);
 }
 
 }  // namespace pkv

@@ -45,6 +45,30 @@ def test_write_bitexact(kind, D, bs):
     assert np.array_equal(_host(dv, kind).view(np.uint8), ref_v.view(np.uint8))
 
 
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("D,bs", [(64, 16), (128, 32)])
+def test_write_bulk_form_bitexact(kind, D, bs):
+    """2048 tokens x 8 kv-heads = 1024 waves of 16 tokens: the bulk form of
+    the write (small batches take 4-token waves), in prefill order with
+    skipped slots."""
+    rng = np.random.default_rng(D + bs + 11)
+    NB, Hkv = 160, 8
+    slots = _prefill_slots(rng, NB, bs, [700, 1000, 348])
+    T = len(slots)
+    assert (T + 15) // 16 * Hkv >= 1024
+    kc, vc = _pool(rng, NB, Hkv, bs, D, kind)
+    k = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+    if kind == "bf16":
+        k, v = workloads.bf16_bits(k), workloads.bf16_bits(v)
+    ref_k, ref_v = ocache.cache_write(k, v, kc, vc, slots, bs)
+    dk, dv = to_dev(kc, kind), to_dev(vc, kind)
+    pkv.kv_cache_write(to_dev(k, kind), to_dev(v, kind), dk, dv, torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(_host(dk, kind).view(np.uint8), ref_k.view(np.uint8))
+    assert np.array_equal(_host(dv, kind).view(np.uint8), ref_v.view(np.uint8))
+
+
 def test_write_bulk_7b_fill():
     """A whole 7B-shaped layer fill: 65,536 tokens x 32 kv-heads x 128 dims, bf16."""
     rng = np.random.default_rng(1)
@@ -145,12 +169,17 @@ def test_write_prefill_order_bitexact(kind, D, bs):
 
 @pytest.mark.parametrize("kv", ["i8", "fp8", "e5m2", "i4"])
 @pytest.mark.parametrize("D,bs", [(128, 16), (64, 32)])
-def test_write_codes_prefill_order_bitexact(kv, D, bs):
+@pytest.mark.parametrize("bulk", [False, True])
+def test_write_codes_prefill_order_bitexact(kv, D, bs, bulk):
+    """Quantising writes in prefill order, as a small batch (4-token waves)
+    and, with 2048 tokens x 8 kv-heads x K and V = 2048 waves of 16 tokens,
+    in the bulk form."""
     from oracle import fp8 as ofp8, int4 as oint4
-    rng = np.random.default_rng(D + bs + 11)
-    NB, Hkv = 64, 3
-    slots = _prefill_slots(rng, NB, bs, [37, 200, 16, 1, 300])
+    rng = np.random.default_rng(D + bs + 11 + bulk)
+    NB, Hkv = (160, 8) if bulk else (64, 3)
+    slots = _prefill_slots(rng, NB, bs, [700, 1000, 348] if bulk else [37, 200, 16, 1, 300])
     T = len(slots)
+    assert ((T + 15) // 16 * Hkv * 2 >= 1024) == bulk
     k = (rng.standard_normal((T, Hkv, D)) * np.exp(rng.uniform(-5, 5, (T, Hkv, 1)))).astype(np.float32)
     v = (rng.standard_normal((T, Hkv, D)) * np.exp(rng.uniform(-5, 5, (T, Hkv, 1)))).astype(np.float32)
     W = D // 2 if kv == "i4" else D
