@@ -2,8 +2,11 @@
  * pagedkv — paged KV cache decode attention for AMD MI355X (gfx950).
  *
  * C ABI of libpagedkv.so.  Every pointer argument is device memory owned by
- * the caller unless stated otherwise; the library never allocates, frees or
- * retains a pointer after a call returns.  Every call is asynchronous on the
+ * the caller unless stated otherwise; the library never allocates or frees
+ * device memory and retains no pointer after a call returns (the only
+ * resources it creates are, on the first cascade decode on a device, one
+ * stream and two events for that device, kept until the process ends).
+ * Every call is asynchronous on the
  * given HIP stream (a hipStream_t passed as void*, NULL = the default stream)
  * and never synchronises it.  A non-OK return launches nothing and has no
  * side effects, except PKV_ERR_HIP, which reports a failed launch.  Errors
@@ -367,7 +370,8 @@ size_t pkv_paged_attention_cascade_workspace_size(
  * PKV_ERR_UNSUPPORTED.  Up to 48 (new token, head) pairs per sequence and
  * kv-head (max_queries_per_seq * G <= 48) the partition kernel computes the
  * partials (its waves split a partition's chunks), beyond that an
- * LDS-staged kernel (its waves split 128 columns and share each chunk).
+ * LDS-staged kernel (its waves split the columns, 64 or 128 per workgroup,
+ * and share each chunk).
  * partition_tokens: 0 for the automatic choice, else as for decode.
  * Workspace: pkv_paged_attention_multi_query_workspace_size(...) bytes,
  * 256-byte aligned, whenever num_query_tokens > 0.  Two launches (partials
