@@ -1,0 +1,106 @@
+"""GPU: a decode loop driven by the native block manager, step after step.
+
+Sequences grow one token per step across block boundaries; three of them
+are forks of a common prefix whose partial tail block is shared, so their
+first appends copy it on write (copy_blocks), and every later step appends
+into private blocks.  Even steps run the fused step (append at position
+L - 1 through the block table, then attend), odd steps write the new tokens
+through the manager's slots and run shared-prefix (cascade) decode with the
+groups found from the block tables.  Every step is checked against the
+oracle on a host mirror of the pool that follows the same writes and
+copies.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import cache as ocache
+import paged_kv_cache_29_amd as pkv
+from paged_kv_cache_29_amd import blocks, workloads
+
+from gpu_helpers import DEV, assert_parity, out_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("G,bs", [(4, 16), (8, 32)])
+def test_block_manager_decode_loop(G, bs):
+    rng = np.random.default_rng(G * 10 + bs)
+    NB, Hkv, D = 96, 2, 128
+    H = G * Hkv
+    scale = 1 / np.sqrt(D)
+    bm = pkv.BlockManager(NB, bs, order=rng.permutation(NB))
+    kc_np = np.full((NB, Hkv, bs, D), workloads.BF16_NAN, np.uint16)
+    vc_np = np.full((NB, Hkv, D, bs), workloads.BF16_NAN, np.uint16)
+    kc, vc = to_dev(kc_np, "bf16"), to_dev(vc_np, "bf16")
+
+    def rows(n):
+        return workloads.bf16_bits(rng.standard_normal((n, Hkv, D)).astype(np.float32))
+
+    def copy_on_write(copies):
+        nonlocal kc_np, vc_np
+        for src, dst, nrows in copies:
+            pkv.copy_blocks((kc, vc), (kc, vc), torch.tensor([[src, dst]], dtype=torch.int32, device=DEV))
+            kc_np[dst, :, :nrows] = kc_np[src, :, :nrows]
+            vc_np[dst, :, :, :nrows] = vc_np[src, :, :, :nrows]
+
+    def prefill(sid, n):
+        nonlocal kc_np, vc_np
+        slots, copies = bm.append(sid, n)
+        copy_on_write(copies)
+        k, v = rows(n), rows(n)
+        pkv.kv_cache_write(to_dev(k, "bf16"), to_dev(v, "bf16"), kc, vc, torch.from_numpy(slots).to(DEV))
+        kc_np, vc_np = ocache.cache_write(k, v, kc_np, vc_np, slots, bs)
+
+    root = bm.new_sequence()
+    prefill(root, 3 * bs + 5)                             # shared prefix ends inside a block
+    seqs = [root] + [bm.fork(root) for _ in range(3)]
+    for n in (bs - 3, 2 * bs + 7):                        # two independent sequences
+        s = bm.new_sequence()
+        prefill(s, n)
+        seqs.append(s)
+
+    copied = 0
+    for step in range(24):
+        B = len(seqs)
+        slots = np.empty(B, np.int64)
+        for i, s in enumerate(seqs):
+            sl, copies = bm.append(s, 1)
+            copied += len(copies)
+            copy_on_write(copies)
+            slots[i] = sl[0]
+        lens = np.array([bm.length(s) for s in seqs], np.int32)
+        MB = int(max((L + bs - 1) // bs for L in lens))
+        tables = bm.tables(seqs, MB)
+        # the manager's slot is the block-table position of token L - 1
+        assert np.array_equal(slots, tables[np.arange(B), (lens - 1) // bs].astype(np.int64) * bs + (lens - 1) % bs)
+        k_new, v_new = rows(B), rows(B)
+        q = workloads.bf16_bits(rng.standard_normal((B, H, D)).astype(np.float32))
+        out = torch.empty((B, H, D), dtype=torch.bfloat16, device=DEV)
+        bt, cl = torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV)
+        if step % 2 == 0:
+            pkv.paged_attention_decode_step(out, to_dev(q, "bf16"), to_dev(k_new, "bf16"), to_dev(v_new, "bf16"),
+                                            kc, vc, bt, cl, scale, H, Hkv, D, bs)
+        else:
+            pkv.kv_cache_write(to_dev(k_new, "bf16"), to_dev(v_new, "bf16"), kc, vc, torch.from_numpy(slots).to(DEV))
+            gs, gsb, mg, ms = blocks.cascade_groups(tables, lens, bs)
+            assert ms >= 3                                # the forks still share the prefix blocks
+            pkv.paged_attention_decode_cascade(out, to_dev(q, "bf16"), kc, vc, bt, cl,
+                                               torch.from_numpy(gs).to(DEV), torch.from_numpy(gsb).to(DEV),
+                                               scale, H, Hkv, D, bs, mg, ms)
+        torch.cuda.synchronize()
+        kc_np, vc_np = ocache.cache_write(k_new, v_new, kc_np, vc_np, slots, bs)
+        ref = oracle.decode_attention(q, kc_np, vc_np, tables, lens, scale, H, Hkv, D, bs, "bf16", "bf16")
+        assert_parity(out_f64(out), ref, "bf16", f"step {step} ({'fused' if step % 2 == 0 else 'cascade'})")
+    assert copied == 3                                    # each fork but the last writer copied the tail once
+    # the device pool equals the mirror wherever a sequence holds a token
+    dk = kc.cpu().view(torch.int16).numpy().view(np.uint16)
+    dv = vc.cpu().view(torch.int16).numpy().view(np.uint16)
+    for s in seqs:
+        L = bm.length(s)
+        for j, blk in enumerate(bm.block_table(s)):
+            n = min(bs, L - j * bs)
+            assert np.array_equal(dk[blk, :, :n], kc_np[blk, :, :n])
+            assert np.array_equal(dv[blk, :, :, :n], vc_np[blk, :, :, :n])
