@@ -439,25 +439,25 @@ def cpu_baseline(w, seconds):
     except Exception:
         threads = os.cpu_count() or 1
     kc, vc = ocache.cache_write(w.k_new, w.v_new, w.k_cache, w.v_cache, w.slot_new, w.block_size)
+    # whole sequences (all heads), in order, repeating the workload until
+    # `seconds` have passed
     done_tokens = 0
     done_seqs = 0
     t_start = time.perf_counter()
-    b = 0
-    while b < w.num_seqs:
+    while time.perf_counter() - t_start < seconds:
+        b = done_seqs % w.num_seqs
         oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.num_heads,
                                 w.num_kv_heads, w.head_dim, w.block_size, w.kv_dtype, w.q_dtype,
                                 samples=[(b, h) for h in range(w.num_heads)])
         done_tokens += int(w.context_lens[b])
         done_seqs += 1
-        b += 1
-        if time.perf_counter() - t_start >= seconds:
-            break
     el = time.perf_counter() - t_start
     elem = 4 if w.kv_dtype == "f32" else 2
     nbytes = 2 * w.num_kv_heads * w.head_dim * elem * done_tokens
     return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done_seqs} of {w.num_seqs} sequences x all {w.num_heads} heads "
-                    f"({done_tokens} context tokens) of {w.name}, {el:.1f} s; "
+            "sample": f"{done_seqs} sequence passes ({done_seqs / w.num_seqs:.1f} x all {w.num_seqs} "
+                    f"sequences) x all {w.num_heads} heads ({done_tokens} context tokens) of "
+                    f"{w.name}, {el:.1f} s; "
                     f"cpu_count={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}, "
                     f"blas_threads={threads}",
             "cache_writes": cpu_cache_writes(w)}
