@@ -245,7 +245,13 @@ void decode_mfma_kernel(DecodeParams p) {
     for (int n = 0; n < NN; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto consume = [&](const ChunkT& cw, int ch) {
+  // `masked` (a compile-time bool): the chunk may hold tokens past the end
+  // of the partition or past a column's position.  Clean chunks (all but
+  // the last of a partition) take the instantiation without any masking
+  // code: left to a runtime branch, the compiler turns the masking into
+  // selects that every chunk executes.
+  auto consume = [&](const ChunkT& cw, int ch, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     const int t0 = t_begin + ch * 32;
     // ---- scores: S^T of sub-tiles h = 0, 1 for every column tile; each K
     // operand is widened once and feeds the tiles' contractions
@@ -287,8 +293,8 @@ void decode_mfma_kernel(DecodeParams p) {
     // ---- online softmax (log2 domain); lane = column c, tokens 4g + i of
     // sub-tile h (chunk token 16h + 4g + i), element e = 4h + i
     // multi-query: also mask tokens past a column's position
-    const bool past_end = (t0 + 32) > t_end;
-    const bool tail = past_end || (kMQ && t0 + 31 > lim_lo);
+    const bool past_end = kMasked && (t0 + 32) > t_end;
+    const bool tail = kMasked && (past_end || (kMQ && t0 + 31 > lim_lo));
     // V scales of the lane's tokens; zero past the end of the partition,
     // where rows may hold NaN (select, never multiply)
     f32x4 vs[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
@@ -427,12 +433,22 @@ void decode_mfma_kernel(DecodeParams p) {
   // loads behind it.  A batch is loaded and consumed last chunk first, so the
   // full-batch and tail branches share no leading code the compiler could
   // hoist, together with its waits, above the batch's other loads.
+  // Full batches take only clean chunks (every token inside the partition
+  // and, multi-query, at or before every column's position); from the
+  // first batch that would reach an unclean chunk on, chunks go one at a
+  // time through the masked instantiation.
+  // (Batches of one chunk, several column tiles, keep the one masked body
+  // for every chunk, and so does INT4 at bs = 32: a second copy of their
+  // body spills.)
+  constexpr bool kCleanBatches = NB > 1 && !(kI4 && BS == 32);
+  using kBatchMasked = std::integral_constant<bool, !kCleanBatches>;
   const int nchunks = (t_end - t_begin + 31) / 32;
+  const int nclean = kCleanBatches ? max(0, ((kMQ ? min(t_end, lim_lo + 1) : t_end) - t_begin) / 32) : nchunks;
   {
     ChunkT cb[NB];
     int blk[2], row0[2];
     for (int ch = wave; ch < nchunks; ch += NB * W) {
-      if (ch + (NB - 1) * W < nchunks) {
+      if (ch + (NB - 1) * W < nclean) {
 #pragma unroll
         for (int k = NB - 1; k >= 0; --k) {
           chunk_blocks(ch + k * W, blk, row0);
@@ -440,12 +456,12 @@ void decode_mfma_kernel(DecodeParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of the math
 #pragma unroll
-        for (int k = NB - 1; k >= 0; --k) consume(cb[k], ch + k * W);
+        for (int k = NB - 1; k >= 0; --k) consume(cb[k], ch + k * W, kBatchMasked{});
       } else {
         for (int c2 = ch; c2 < nchunks; c2 += W) {
           chunk_blocks(c2, blk, row0);
           ld.load(cb[0], blk, row0);
-          consume(cb[0], c2);
+          consume(cb[0], c2, std::true_type{});
         }
       }
     }
