@@ -290,9 +290,14 @@ void cascade_prefix_kernel(DecodeParams p) {
     for (int n = 0; n < NN; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto consume = [&](const ChunkT& cw, int ch) {
+  // `masked` (compile time): the chunk may hold tokens past the end of the
+  // span or, multi-query, past a column's position; clean chunks take the
+  // instantiation without masking code (as a runtime branch the compiler
+  // turns the masking into selects that every chunk executes).
+  auto consume = [&](const ChunkT& cw, int ch, auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
     const int t0 = t_begin + ch * 32;
-    const bool tail = (t0 + 32) > t_end;  // only a lone last block at bs = 16
+    const bool tail = kMasked && (t0 + 32) > t_end;  // only a lone last block at bs = 16
     // V^T operands of the chunk, shared by the query tiles (INT4: operand
     // 2m holds the even dims of dim pairs 16m + c, 2m + 1 the odd ones)
     u32x4 vw[NN];
@@ -374,7 +379,7 @@ void cascade_prefix_kernel(DecodeParams p) {
           }
         }
       }
-      if constexpr (kMQ) {  // causal: column c sees tokens up to lim[t]
+      if constexpr (kMQ && kMasked) {  // causal: column c sees tokens up to lim[t]
         if (t0 + 31 > lim[t]) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -435,21 +440,31 @@ void cascade_prefix_kernel(DecodeParams p) {
 
   // ---- every chunk of the partition, two LDS stages: the next chunk's
   // pieces are in flight while the current one is consumed
+  // Clean chunks (inside the span and, multi-query, at or before the
+  // workgroup's first column's position, hence every column's) first, then
+  // the rest; the bound is uniform across the workgroup, so every wave runs
+  // the same iterations between the barriers.
   const int nchunks = (t_end - t_begin + 31) / 32;
+  const int clean_end = kMQ ? min(t_end, S - nnew + qwg / G + 1) : t_end;
+  const int nclean = min(nchunks, max(0, (clean_end - t_begin) / 32));
+  auto run = [&](int ch0, int ch1, auto masked) {
+    for (int ch = ch0; ch < ch1; ++ch) {
+      const bool more = ch + 1 < nchunks;
+      if (more) piece_load(ch + 1);
+      {
+        ChunkT cw;
+        lds_chunk(ch & 1, cw);
+        consume(cw, ch, masked);
+      }
+      if (more) piece_store((ch + 1) & 1);
+      __syncthreads();
+    }
+  };
   piece_load(0);
   piece_store(0);
   __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const bool more = ch + 1 < nchunks;
-    if (more) piece_load(ch + 1);
-    {
-      ChunkT cw;
-      lds_chunk(ch & 1, cw);
-      consume(cw, ch);
-    }
-    if (more) piece_store((ch + 1) & 1);
-    __syncthreads();
-  }
+  run(0, nclean, std::false_type{});
+  run(nclean, nchunks, std::true_type{});
 
   // ---- this wave's partials
 #pragma unroll
