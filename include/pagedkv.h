@@ -54,10 +54,14 @@
  *   new k, v     [T][Hkv][D]
  * All arrays are dense and row-major with exactly these shapes.
  *
- * Device-data preconditions that are NOT checked (a violation is undefined
- * behaviour, typically a memory fault): every block id a sequence uses is in
- * [0, NB); context_lens[b] <= MB * bs; every slot is < NB * bs; no two
- * tokens of one write call share a slot (they would race).
+ * Device-data preconditions that are NOT checked by default (a violation is
+ * undefined behaviour, typically a memory fault): every block id a sequence
+ * uses is in [0, NB); context_lens[b] <= MB * bs; every slot is < NB * bs;
+ * no two tokens of one write call share a slot (they would race).  With the
+ * environment variable PKV_DEBUG=1 every attention and cache-write call
+ * checks them, and the group and query arrays below, on host copies before
+ * launching (synchronising its stream); pagedkv_debug.h declares the same
+ * checks for callers to run on host arrays.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -327,9 +331,9 @@ pkv_status pkv_paged_attention_decode_step_partitions(
  * `stream` beside it, then the reduce on `stream` after both (the second
  * stream is forked from and joined back into `stream` by events, so the
  * call orders like three launches on `stream`, also under graph capture).
- * Not checked (device data): the group arrays as stated above; every
- * member's context_lens >= S_g; the shared entries really are equal (if not,
- * the first member's blocks are used for the whole group).
+ * Not checked unless PKV_DEBUG=1 (device data): the group arrays as stated
+ * above; every member's context_lens >= S_g; the shared entries really are
+ * equal (if not, the first member's blocks are used for the whole group).
  */
 pkv_status pkv_paged_attention_decode_cascade(
     void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
@@ -376,8 +380,8 @@ size_t pkv_paged_attention_cascade_workspace_size(
  * Workspace: pkv_paged_attention_multi_query_workspace_size(...) bytes,
  * 256-byte aligned, whenever num_query_tokens > 0.  Two launches (partials
  * of every context partition, then the combine).
- * Not checked (device data): query_start as stated; n_b <= context_lens[b];
- * n_b <= max_queries_per_seq.
+ * Not checked unless PKV_DEBUG=1 (device data): query_start as stated;
+ * n_b <= context_lens[b]; n_b <= max_queries_per_seq.
  */
 pkv_status pkv_paged_attention_multi_query(
     void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,

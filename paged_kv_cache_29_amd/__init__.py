@@ -7,6 +7,10 @@ block allocator (free list, refcounts, copy-on-write).
 """
 
 from ._lib import (  # noqa: F401
+    check_block_tables,
+    check_groups,
+    check_query_start,
+    check_slot_mapping,
     copy_blocks,
     kv_cache_write,
     kv_cache_write_int8,

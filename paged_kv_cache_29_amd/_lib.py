@@ -81,6 +81,10 @@ SIGNATURES = {
     "pkv_bm_swap_out": (c_i32, [c_vp, c_i64, c_vp, c_i32, ctypes.POINTER(c_i32)]),
     "pkv_bm_swap_in": (c_i32, [c_vp, c_i64, c_vp, c_i32, ctypes.POINTER(c_i32)]),
     "pkv_copy_blocks": (c_i32, [c_vp] * 9 + [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp]),
+    "pkv_check_block_tables": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i64]),
+    "pkv_check_slot_mapping": (c_i32, [c_vp, c_i64, c_i32, c_i64]),
+    "pkv_check_query_start": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32]),
+    "pkv_check_groups": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
@@ -501,3 +505,61 @@ def copy_blocks(dst, src, pairs):
     st = load().pkv_copy_blocks(_ptr(dst[0]), _ptr(dst[1]), *sc(dst), _ptr(src[0]), _ptr(src[1]),
                                 *sc(src), _ptr(pairs), pairs.shape[0], Hkv, D, bs, kd, _stream(dev))
     _check(st, "copy_blocks")
+
+
+# ---- host checks of the device-data preconditions (include/pagedkv_debug.h)
+
+def _host_i(a, dtype):
+    import numpy as np
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, ctypes.c_void_p(a.ctypes.data if a.size else 0)
+
+
+def check_block_tables(block_tables, context_lens, block_size, num_blocks):
+    """Raise ValueError unless every context fits its table row and every
+    block id it uses is in [0, num_blocks) (``pkv_check_block_tables``)."""
+    import numpy as np
+    bt, pbt = _host_i(block_tables, np.int32)
+    cl, pcl = _host_i(context_lens, np.int32)
+    _need(bt.ndim == 2 and cl.ndim == 1 and cl.shape[0] == bt.shape[0], "block_tables [B, MB], context_lens [B]")
+    _check(load().pkv_check_block_tables(pbt, pcl, bt.shape[0], bt.shape[1], block_size, num_blocks),
+           "check_block_tables")
+
+
+def check_slot_mapping(slot_mapping, block_size, num_blocks):
+    """Raise ValueError if a slot is past the pool or two tokens share one
+    (``pkv_check_slot_mapping``; negative slots are skipped)."""
+    import numpy as np
+    sm, psm = _host_i(slot_mapping, np.int64)
+    _need(sm.ndim == 1, "slot_mapping must be 1-D")
+    _check(load().pkv_check_slot_mapping(psm, sm.shape[0], block_size, num_blocks), "check_slot_mapping")
+
+
+def check_query_start(query_start, context_lens, num_query_tokens, max_queries_per_seq):
+    """Raise ValueError unless query_start is a valid prefix sum of the new
+    tokens per sequence (``pkv_check_query_start``)."""
+    import numpy as np
+    qs, pqs = _host_i(query_start, np.int32)
+    cl, pcl = _host_i(context_lens, np.int32)
+    _need(qs.ndim == 1 and cl.ndim == 1 and qs.shape[0] == cl.shape[0] + 1,
+          "query_start [B + 1], context_lens [B]")
+    _check(load().pkv_check_query_start(pqs, pcl, cl.shape[0], num_query_tokens, max_queries_per_seq),
+           "check_query_start")
+
+
+def check_groups(group_start, group_shared_blocks, block_tables, context_lens, block_size,
+                 max_group_size, max_shared_blocks):
+    """Raise ValueError unless the shared-prefix groups are valid for the
+    block tables (``pkv_check_groups``)."""
+    import numpy as np
+    gs, pgs = _host_i(group_start, np.int32)
+    gsb, pgsb = _host_i(group_shared_blocks, np.int32)
+    bt, pbt = _host_i(block_tables, np.int32)
+    cl, pcl = _host_i(context_lens, np.int32)
+    _need(gs.ndim == 1 and gsb.ndim == 1 and gs.shape[0] == gsb.shape[0] + 1,
+          "group_start [G + 1], group_shared_blocks [G]")
+    _need(bt.ndim == 2 and cl.ndim == 1 and cl.shape[0] == bt.shape[0], "block_tables [B, MB], context_lens [B]")
+    _check(load().pkv_check_groups(pgs, pgsb, pbt, pcl, bt.shape[0], bt.shape[1], block_size, gsb.shape[0],
+                                   max_group_size, max_shared_blocks), "check_groups")

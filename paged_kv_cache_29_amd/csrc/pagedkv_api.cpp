@@ -7,10 +7,12 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/pagedkv.h"
 #include "../../include/pagedkv_blocks.h"
 #include "../../include/pagedkv_probe.h"
+#include "pkv_debug.hpp"
 #include "pkv_host.hpp"
 #include "pkv_kernels.hpp"
 
@@ -76,9 +78,9 @@ hipError_t side_stream(SideStream** out) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
     if (e != hipSuccess) {
-      if (n.join) hipEventDestroy(n.join);
-      if (n.fork) hipEventDestroy(n.fork);
-      if (n.stream) hipStreamDestroy(n.stream);
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.stream) (void)hipStreamDestroy(n.stream);
       return e;
     }
     ss = n;
@@ -433,6 +435,25 @@ pkv_status validate_write(const void* k, const void* v, const void* k_cache, con
   return PKV_OK;
 }
 
+// PKV_DEBUG=1: the device-data preconditions of a write / of decode-style
+// calls, checked on host copies before anything is launched.
+pkv_status debug_write(const int64_t* slot_mapping, int64_t num_tokens, int32_t block_size,
+                       int64_t num_blocks, void* stream) {
+  if (!pkv::debug_checks_enabled() || num_tokens == 0) return PKV_OK;
+  return pkv::debug_check_slots(slot_mapping, num_tokens, block_size, num_blocks,
+                                static_cast<hipStream_t>(stream));
+}
+
+pkv_status debug_tables(const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t max_blocks_per_seq, int32_t block_size, int64_t num_blocks, void* stream,
+                        std::vector<int32_t>* tables = nullptr, std::vector<int32_t>* lens = nullptr) {
+  if (!pkv::debug_checks_enabled() || num_seqs == 0) return PKV_OK;
+  std::vector<int32_t> t, l;
+  return pkv::debug_check_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size,
+                                 num_blocks, static_cast<hipStream_t>(stream), tables ? tables : &t,
+                                 lens ? lens : &l);
+}
+
 pkv_status write_codes(const float* k, const float* v, void* k_cache, void* v_cache,
                        float* k_scale, float* v_scale, const int64_t* slot_mapping,
                        int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
@@ -444,6 +465,8 @@ pkv_status write_codes(const float* k, const float* v, void* k_cache, void* v_ca
   if (num_tokens > 0 && (!k_scale || !v_scale))
     return fail(PKV_ERR_INVALID, "null k_scale or v_scale");
   if (num_tokens == 0) return ok();
+  st = debug_write(slot_mapping, num_tokens, block_size, num_blocks, stream);
+  if (st != PKV_OK) return st;
   pkv::WriteParams p{k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, num_tokens,
                      num_kv_heads, head_dim, block_size};
   hipError_t e = pkv::launch_cache_write_codes(p, kind, static_cast<hipStream_t>(stream));
@@ -465,6 +488,8 @@ pkv_status pkv_kv_cache_write(const void* k, const void* v, void* k_cache, void*
   if (dtype != PKV_F32 && dtype != PKV_BF16)
     return fail(PKV_ERR_UNSUPPORTED, "kv_cache_write dtype must be PKV_F32 or PKV_BF16");
   if (num_tokens == 0) return ok();
+  st = debug_write(slot_mapping, num_tokens, block_size, num_blocks, stream);
+  if (st != PKV_OK) return st;
   pkv::WriteParams p{k, v, k_cache, v_cache, nullptr, nullptr, slot_mapping, num_tokens,
                      num_kv_heads, head_dim, block_size};
   hipError_t e = pkv::launch_cache_write(p, dtype == PKV_F32 ? pkv::KvKind::F32 : pkv::KvKind::BF16,
@@ -553,6 +578,8 @@ pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
   pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
+  s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
+  if (s != PKV_OK) return s;
   s = launch_partitions(st, static_cast<hipStream_t>(stream));
   if (s != PKV_OK) return s;
   s = launch_reduce(st, static_cast<hipStream_t>(stream));
@@ -565,6 +592,8 @@ pkv_status pkv_paged_attention_decode_partitions(PKV_DECODE_PARAMS) {
   pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
+  s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
+  if (s != PKV_OK) return s;
   s = launch_partitions(st, static_cast<hipStream_t>(stream));
   if (s != PKV_OK) return s;
   return ok();
@@ -575,6 +604,8 @@ pkv_status pkv_paged_attention_decode_reduce(PKV_DECODE_PARAMS) {
   pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
+  s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
+  if (s != PKV_OK) return s;
   s = launch_reduce(st, static_cast<hipStream_t>(stream));
   if (s != PKV_OK) return s;
   return ok();
@@ -593,6 +624,8 @@ pkv_status pkv_paged_attention_decode_step(PKV_STEP_PARAMS) {
   pkv_status s = validate_decode(PKV_DECODE_ARGS, k_new, v_new, true, &st);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
+  s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
+  if (s != PKV_OK) return s;
   s = launch_partitions(st, static_cast<hipStream_t>(stream));
   if (s != PKV_OK) return s;
   s = launch_reduce(st, static_cast<hipStream_t>(stream));
@@ -605,6 +638,8 @@ pkv_status pkv_paged_attention_decode_step_partitions(PKV_STEP_PARAMS) {
   pkv_status s = validate_decode(PKV_DECODE_ARGS, k_new, v_new, true, &st);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
+  s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
+  if (s != PKV_OK) return s;
   s = launch_partitions(st, static_cast<hipStream_t>(stream));
   if (s != PKV_OK) return s;
   return ok();
@@ -659,6 +694,16 @@ pkv_status pkv_paged_attention_decode_cascade(
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (pkv::debug_checks_enabled()) {
+    std::vector<int32_t> tables, lens;
+    s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream,
+                     &tables, &lens);
+    if (s == PKV_OK)
+      s = pkv::debug_check_groups(group_start, group_shared_blocks, tables, lens, num_seqs, max_blocks_per_seq,
+                                  block_size, num_groups, max_group_size, max_shared_blocks,
+                                  static_cast<hipStream_t>(stream));
+    if (s != PKV_OK) return s;
+  }
   pkv::DecodeParams& p = st.p;
   const size_t rows = static_cast<size_t>(num_seqs) * num_heads * (cs.pparts + cs.sparts);
   const size_t acc_bytes = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
@@ -812,6 +857,15 @@ pkv_status pkv_paged_attention_multi_query(
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(PKV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (pkv::debug_checks_enabled()) {
+    std::vector<int32_t> tables, lens;
+    s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream,
+                     &tables, &lens);
+    if (s == PKV_OK)
+      s = pkv::debug_check_query_start(query_start, lens, num_seqs, num_query_tokens, max_queries_per_seq,
+                                       static_cast<hipStream_t>(stream));
+    if (s != PKV_OK) return s;
+  }
   pkv::DecodeParams& p = st.p;
   const size_t rows = static_cast<size_t>(num_query_tokens) * num_heads * ms.parts;
   const size_t acc_bytes = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
