@@ -8,10 +8,13 @@
 // which equals softmax over the whole context exactly (up to rounding), so
 // the split never changes the definition.
 //
-// One wave per (sequence, query head); a lane owns dims lane and lane + 64.
-// The weights of up to 64 partitions are computed lane-parallel and read
-// back one by one with readlane, so the partial rows are independent loads
-// the unrolled loop keeps in flight together.
+// One wave per (sequence, query head), four per workgroup; a lane owns dims
+// lane and lane + 64.  The weights of up to 64 partitions are computed
+// lane-parallel and read back one by one with readlane, so the partial rows
+// are independent loads the unrolled loop keeps in flight together; the
+// first 8 rows are loaded with the partitions' maxima and sums, before the
+// wave knows the overall maximum (the kernel is bound by its chain of
+// dependent loads, not by its bytes).
 
 #include "pkv_device.hpp"
 #include "pkv_kernels.hpp"
@@ -19,12 +22,16 @@
 namespace pkv {
 namespace {
 
+constexpr int kReduceWaves = 4;
+
 template <int D, bool kOutBf16>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(DecodeParams p) {
   constexpr int ND = D / kWave;
-  const int lane = threadIdx.x;
-  const int bh = blockIdx.x;  // (sequence, head), or (query row, head) in multi-query mode
+  const int lane = threadIdx.x & (kWave - 1);
   const bool mq = p.query_start != nullptr;
+  // (sequence, head), or (query row, head) in multi-query mode
+  const int bh = __builtin_amdgcn_readfirstlane(blockIdx.x * kReduceWaves + (threadIdx.x >> 6));
+  if (bh >= (mq ? p.num_query_rows : p.num_seqs) * p.num_heads) return;  // the whole wave
   const int b = mq ? range_of(p.query_start, p.num_seqs, bh / p.num_heads) : bh / p.num_heads;
   const int L = p.context_lens[b];
   // Partials i = 0 .. nparts-1 live in workspace slots slot(i): partitions
@@ -59,39 +66,56 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
   const size_t base = static_cast<size_t>(bh) * p.num_parts;
   const float* m = p.ws_m + base;
   const float* l = p.ws_l + base;
-  const float* a = p.ws_acc + base * D;
-
-  float M = -INFINITY;
-  for (int i = lane; i < nparts; i += kWave) M = fmaxf(M, m[slot(i)]);
-  M = wave_max(M);
-
+  const float* row = p.ws_acc + base * D + lane;
+  // groups of 8 rows: 8 independent loads per lane in flight; rows past
+  // cnt re-read the last valid row and get weight 0 (wv is 0 there)
+  auto load8 = [&](float (&x)[8][ND], int first, int j0, int cnt) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = slot(first + min(j0 + u, max(cnt - 1, 0)));
+#pragma unroll
+      for (int k = 0; k < ND; ++k) x[u][k] = row[static_cast<size_t>(j) * D + kWave * k];
+    }
+  };
   float num[ND];
 #pragma unroll
   for (int k = 0; k < ND; ++k) num[k] = 0.f;
+  auto add8 = [&](const float (&x)[8][ND], int j0, int cnt, float wv) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), (j0 + u) & (kWave - 1)));
+      const float wu = (j0 + u < cnt) ? w : 0.f;
+#pragma unroll
+      for (int k = 0; k < ND; ++k) num[k] = fmaf(wu, x[u][k], num[k]);
+    }
+  };
+
+  // the first 8 rows go out with the maxima and sums
+  float x0[8][ND];
+  load8(x0, 0, 0, min(kWave, nparts));
+  const float m0 = lane < nparts ? m[slot(lane)] : -INFINITY;
+  const float l0 = lane < nparts ? l[slot(lane)] : 0.f;
+  float M = m0;
+  for (int i = lane + kWave; i < nparts; i += kWave) M = fmaxf(M, m[slot(i)]);
+  M = wave_max(M);
+
   float den = 0.f;
   for (int first = 0; first < nparts; first += kWave) {
     const int i = first + lane;
-    const float wv = (i < nparts) ? exp2f(m[slot(i)] - M) : 0.f;
-    if (i < nparts) den = fmaf(wv, l[slot(i)], den);
+    const float mi = first == 0 ? m0 : (i < nparts ? m[slot(i)] : -INFINITY);
+    const float li = first == 0 ? l0 : (i < nparts ? l[slot(i)] : 0.f);
+    const float wv = (i < nparts) ? exp2f(mi - M) : 0.f;
+    if (i < nparts) den = fmaf(wv, li, den);
     const int cnt = min(kWave, nparts - first);
-    const float* row = a + lane;
-    // groups of 8 rows: 8 independent loads per lane in flight; rows past
-    // cnt re-read the last valid row and get weight 0 (wv is 0 there)
-    for (int j0 = 0; j0 < cnt; j0 += 8) {
+    int j0 = 0;
+    if (first == 0) {
+      add8(x0, 0, cnt, wv);
+      j0 = 8;
+    }
+    for (; j0 < cnt; j0 += 8) {
       float x[8][ND];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = slot(first + min(j0 + u, cnt - 1));
-#pragma unroll
-        for (int k = 0; k < ND; ++k) x[u][k] = row[static_cast<size_t>(j) * D + kWave * k];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), (j0 + u) & (kWave - 1)));
-        const float wu = (j0 + u < cnt) ? w : 0.f;
-#pragma unroll
-        for (int k = 0; k < ND; ++k) num[k] = fmaf(wu, x[u][k], num[k]);
-      }
+      load8(x, first, j0, cnt);
+      add8(x, j0, cnt, wv);
     }
   }
   den = wave_sum(den);
@@ -109,11 +133,13 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeParams p) {
 template <int D>
 hipError_t launch_t(const DecodeParams& p, bool out_bf16, hipStream_t s) {
   const int rows = p.query_start != nullptr ? p.num_query_rows : p.num_seqs;
-  const dim3 grid(static_cast<unsigned>(rows * p.num_heads));
+  const int64_t waves = static_cast<int64_t>(rows) * p.num_heads;
+  const dim3 grid(static_cast<unsigned>((waves + kReduceWaves - 1) / kReduceWaves));
+  const dim3 block(kReduceWaves * kWave);
   if (out_bf16)
-    hipLaunchKernelGGL((decode_reduce_kernel<D, true>), grid, dim3(kWave), 0, s, p);
+    hipLaunchKernelGGL((decode_reduce_kernel<D, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((decode_reduce_kernel<D, false>), grid, dim3(kWave), 0, s, p);
+    hipLaunchKernelGGL((decode_reduce_kernel<D, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
