@@ -180,6 +180,19 @@ def test_partition_size_does_not_change_result():
         assert np.all(d <= np.abs(base) * 2 ** -7 + 1e-6), (pt, d.max())
 
 
+@pytest.mark.parametrize("kv", ["f32", "bf16"])
+def test_more_than_64_partitions_per_row(kv):
+    """The combine weighs a row's partials 64 at a time: 32-token partitions
+    give rows of 66, 128, 64 and 2 partials (a second, partial group of 64
+    and a full second group)."""
+    w = workloads.make_custom(15, [2100, 4095, 2048, 33], 8, 2, 128, 16, kv_dtype=kv)
+    dw = DeviceWorkload(w)
+    dw.write_new()
+    o = out_f64(dw.decode(partition_tokens=32))
+    torch.cuda.synchronize()
+    assert_parity(o, oracle_out(w), kv, f"{kv} 32-token partitions")
+
+
 def test_two_phase_calls_equal_one_call():
     w = workloads.make_custom(15, RAGGED, 16, 2, 128, 16, kv_dtype="bf16")
     dw = DeviceWorkload(w)
