@@ -8,7 +8,8 @@
  * stream and two events for that device, kept until the process ends).
  * Every call is asynchronous on the
  * given HIP stream (a hipStream_t passed as void*, NULL = the default stream)
- * and never synchronises it.  A non-OK return launches nothing and has no
+ * and never synchronises it (except in the PKV_DEBUG=1 checking mode of
+ * pagedkv_debug.h).  A non-OK return launches nothing and has no
  * side effects, except PKV_ERR_HIP, which reports a failed launch.  Errors
  * that happen while a kernel runs surface at the caller's next
  * synchronisation.  pkv_last_error() gives the text of the last failure on
