@@ -166,3 +166,30 @@ def test_groups_reject_member_shorter_than_the_span():
     lens[3] = S - 1
     with pytest.raises(ValueError, match=f"sequence 3 of group 0 has {S - 1} tokens, fewer than the {S} shared"):
         pkv.check_groups(gs, gsb, tables, lens, bs, mg, ms)
+
+
+# ---- the checkers' own argument checks, through the C ABI -------------------
+
+def test_checkers_reject_bad_arguments():
+    import ctypes
+    lib = pkv.load_library()
+    one = (ctypes.c_int32 * 4)(0, 0, 0, 0)
+    slots = (ctypes.c_int64 * 2)(0, 1)
+    INVALID = 1
+    cases = [
+        (lambda: lib.pkv_check_block_tables(one, one, -1, 1, 16, 8), "invalid sizes"),
+        (lambda: lib.pkv_check_block_tables(one, one, 1, 0, 16, 8), "invalid sizes"),
+        (lambda: lib.pkv_check_block_tables(None, one, 1, 1, 16, 8), "null array"),
+        (lambda: lib.pkv_check_slot_mapping(slots, 2, 0, 8), "invalid sizes"),
+        (lambda: lib.pkv_check_slot_mapping(None, 2, 16, 8), "null array"),
+        (lambda: lib.pkv_check_query_start(one, one, -1, 0, 1), "invalid sizes"),
+        (lambda: lib.pkv_check_query_start(None, one, 1, 0, 1), "null array"),
+        (lambda: lib.pkv_check_groups(one, one, one, one, 1, 1, 16, -1, 1, 0), "invalid sizes"),
+        (lambda: lib.pkv_check_groups(one, None, one, one, 1, 1, 16, 1, 1, 0), "null array"),
+    ]
+    for call, frag in cases:
+        assert call() == INVALID
+        assert frag in lib.pkv_last_error().decode()
+    # nothing to check is valid, and clears the last error
+    assert lib.pkv_check_slot_mapping(None, 0, 16, 8) == 0
+    assert lib.pkv_last_error() == b""
