@@ -186,8 +186,11 @@ pkv_status pkv_kv_cache_write_int4(const float* k, const float* v, uint8_t* k_ca
 /*
  * Bytes of device workspace pkv_paged_attention_decode needs for these
  * sizes (0 when every sequence fits one partition, in which case the
- * workspace pointer may be NULL).  partition_tokens as for decode.  Returns
- * 0 also for invalid sizes (decode then reports the error).
+ * workspace pointer may be NULL).  partition_tokens as for decode.  The
+ * cache kind is not an argument, so the size covers both ways decode may
+ * split contexts (fixed partitions for fp32 caches, balanced shares for the
+ * others).  Returns 0 also for invalid sizes (decode then reports the
+ * error).
  */
 size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads,
                                           int32_t num_kv_heads, int32_t head_dim,
@@ -197,10 +200,21 @@ size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads,
 /*
  * Token count per context partition the library would use for these sizes
  * when partition_tokens is 0 (the automatic choice); 0 for invalid sizes.
+ * With balanced shares (below) this is the fixed-partition length that
+ * decides between the two: contexts up to it are attended whole.
  */
 int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                              int32_t block_size, int32_t max_blocks_per_seq,
                                              int32_t partition_tokens);
+
+/*
+ * Number of balanced shares decode (and the fused step) use for these sizes
+ * and cache kind, or 0 when they use fixed partitions (see
+ * pkv_paged_attention_decode: partition_tokens); 0 also for invalid sizes.
+ */
+int32_t pkv_paged_attention_shares(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int32_t partition_tokens,
+                                   pkv_dtype kv_dtype);
 
 /*
  * Single-token decode attention over the paged cache ([ENG5] "Two phases
@@ -216,9 +230,18 @@ int32_t pkv_paged_attention_partition_tokens(int32_t num_seqs, int32_t num_kv_he
  * out has q's dtype; head_dim in {64, 128}; block_size in {16, 32};
  * G in {1, 2, 4, 8, 16}.  k_scale and v_scale are required for the coded
  * caches (I8, FP8, FP8_E5M2, I4) and must be NULL otherwise.  num_seqs == 0 is a no-op.  scale must be finite.
- * partition_tokens: 0 for the automatic choice, else a multiple of 32 in
- * [32, 128 * block_size]; long contexts are split into partitions of that
- * many tokens whose partial results a second kernel combines.
+ * partition_tokens: a multiple of 32 in [32, 128 * block_size]: long
+ * contexts are split into partitions of that many tokens, one workgroup
+ * each, whose partial results a second kernel combines.  0: the automatic
+ * choice.  If every context fits the automatic partition length (as
+ * max_blocks_per_seq * block_size bounds it), one workgroup per (sequence,
+ * kv-head) attends it whole and no second kernel runs.  Otherwise (and for
+ * every cache kind but fp32) the work is balanced: the 32-token chunks of
+ * all (sequence, kv-head) pairs, laid end to end, are cut into equal
+ * contiguous shares, one per workgroup of a grid sized to the GPU
+ * (pkv_paged_attention_shares), so that ragged context lengths leave no
+ * tail of idle CUs; pairs split between shares are combined by the second
+ * kernel.  The result is the same softmax in every case, up to rounding.
  * workspace / workspace_bytes: device scratch of at least
  * pkv_paged_attention_workspace_size(...) bytes, 256-byte aligned.
  */

@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     paged_attention_decode_step,
     paged_attention_decode_step_partitions,
     partition_tokens,
+    balanced_shares,
     probe_tile_read,
     workspace_size,
     load as load_library,

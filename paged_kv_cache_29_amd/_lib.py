@@ -54,6 +54,7 @@ SIGNATURES = {
     "pkv_paged_attention_workspace_size": (c_size, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                                     c_i32]),
     "pkv_paged_attention_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pkv_paged_attention_shares": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_attention_decode": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_partitions": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_reduce": (c_i32, _DECODE_ARGS),
@@ -230,6 +231,13 @@ def _write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, cache_d
 def partition_tokens(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, requested=0):
     return int(load().pkv_paged_attention_partition_tokens(num_seqs, num_kv_heads, block_size,
                                                            max_blocks_per_seq, requested))
+
+
+def balanced_shares(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, kv_dtype, requested=0):
+    """Balanced shares decode uses for a cache of torch dtype ``kv_dtype``
+    (0: fixed partitions)."""
+    return int(load().pkv_paged_attention_shares(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
+                                                 requested, _DTYPES[kv_dtype]))
 
 
 def workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,

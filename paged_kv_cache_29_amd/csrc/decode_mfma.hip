@@ -75,6 +75,29 @@ constexpr int kBatch = 2;
 template <KvKind KV, int NT>
 constexpr int kWavesPerSimd = KV == KvKind::I4 && NT == 1 ? 3 : 2;
 
+// Chunks of the smallest share of the balanced mode (below, 256 tokens):
+// fewer chunks would cost more in per-segment set-up than they gain in
+// spread.
+constexpr int kMinShareChunks = 8;
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int64_t wave_incl_scan(int64_t v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint64_t u = static_cast<uint64_t>(v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(u), l);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(u >> 32), l);
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // KV: BF16, or codes with per-token scales (I8, FP8: bytes; I4: nibbles).
 // kMQ: multi-query attention (speculative verification of a few new tokens
 // per sequence).  The columns are (new token, head) pairs of one sequence's
@@ -85,7 +108,16 @@ constexpr int kWavesPerSimd = KV == KvKind::I4 && NT == 1 ? 3 : 2;
 // (empty ones with max -inf, sum 0) and the reduce always runs.  With
 // NT > 1 tiles every wave carries the tiles' states over one chunk in
 // flight: each K and V operand is loaded and widened once for all of them.
-template <KvKind KV, int D, int BS, int W, bool kMQ, int NT>
+// kBal: balanced shares instead of fixed partitions.  The chunks of every
+// (sequence, kv-head) unit, laid end to end in unit order (u = b * Hkv +
+// kvh), are cut into equal contiguous shares, one per workgroup of a grid
+// sized to the GPU's workgroup slots; a workgroup attends the pieces of
+// the units its share covers one after the other (segments).  A unit that
+// lies inside one share is finished there; a split unit is the first or
+// the last segment of each share it touches, so its partials go to that
+// share's two slots (2s, 2s + 1), and the workgroup holding its first chunk
+// records where they are ({first slot, count} in ws_unit) for the reduce.
+template <KvKind KV, int D, int BS, int W, bool kMQ, int NT, bool kBal>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, NT>, kWavesPerSimd<KV, NT>)))
 void decode_mfma_kernel(DecodeParams p) {
@@ -94,12 +126,14 @@ void decode_mfma_kernel(DecodeParams p) {
   using ChunkT = typename std::conditional<kI4, ChunkI4<D>, Chunk<kInt8, D>>::type;
   using LoaderT = typename std::conditional<kI4, ChunkLoaderI4<D, BS>, ChunkLoader<kInt8, D, BS>>::type;
   static_assert(NT >= 1 && NT <= kMqDecodeMaxTiles && (kMQ || NT == 1), "column tiles");
+  static_assert(!(kBal && kMQ), "balanced shares are a one-query mode");
   // the registers of the extra tiles' states replace the second chunk
   constexpr int NB = NT > 1 ? 1 : kBatch<KV>;
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(BS == 16 || BS == 32, "block_size");
   constexpr int NJ = D / 32;  // QK MFMAs per score tile
   constexpr int NN = D / 16;  // PV MFMA pairs per chunk
+  constexpr int kPiece = kMaxPartBlocks * BS;  // tokens whose block ids one staging holds
 
   __shared__ float red_acc[W > 1 ? W - 1 : 1][NN * 4][kWave];
   __shared__ float red_m[W][kWave];
@@ -114,457 +148,560 @@ void decode_mfma_kernel(DecodeParams p) {
   const int Hkv = p.num_kv_heads;
   const int H = p.num_heads;
   const int G = H / Hkv;
-  int b, kvh, tile0 = 0;
-  if constexpr (kMQ) {
-    // blockIdx.x = ((u / 8) * groups + tg) * 8 + u % 8 for u = b * Hkv + kvh
-    // and tile group tg (tiles tg * NT ..): the tile groups of one (sequence,
-    // kv-head) run on the same XCD (workgroups go to XCDs round-robin) and
-    // share its L2
-    const int groups = (p.mq_tiles + NT - 1) / NT;
-    const int rest = blockIdx.x >> 3;
-    tile0 = (rest % groups) * NT;
-    const int u = (rest / groups) * 8 + (blockIdx.x & 7);
-    if (u >= p.num_seqs * Hkv) return;  // uniform across the workgroup
-    b = u / Hkv;
-    kvh = u - b * Hkv;
-  } else {
-    b = blockIdx.x / Hkv;
-    kvh = blockIdx.x - b * Hkv;
-  }
-  const int part = blockIdx.y;
-  const int PT = p.part_tokens;
-
-  const int L = p.context_lens[b];
-  // multi-query: this sequence's n new tokens x G heads are its columns
-  int qrow0 = 0, nnew = 0, ncol = G;
-  if constexpr (kMQ) {
-    qrow0 = p.query_start[b];
-    nnew = p.query_start[b + 1] - qrow0;
-    ncol = nnew * G;
-    if (16 * tile0 >= ncol) return;  // uniform; also every sequence with L == 0
-  }
-  // cascade: the group's shared tokens are attended by the prefix kernel
-  const bool cascade = !kMQ && p.group_start != nullptr;
-  const int t_begin = (cascade ? group_shared_tokens(p, group_of(p, b)) : 0) + part * PT;
-  if ((kMQ || cascade || part != 0) && t_begin >= L) return;  // uniform across the workgroup
-  const int h0 = kvh * G;
   uint16_t* out = static_cast<uint16_t*>(p.out);
 
-  if (L <= 0) {  // empty context: zero output
-    for (int i = threadIdx.x; i < G * D; i += W * kWave)
-      out[(static_cast<size_t>(b) * H + h0) * D + i] = 0;
-    return;
-  }
-  // multi-query: column 16 t + c of tile t sees tokens 0 .. lim[t]; the
-  // workgroup reads nothing past its last column's position
-  int lim[NT];
+  // Attends tokens [t_begin, t_end) of sequence b (context L >= 1) for
+  // kv-head kvh: the column tiles tile0 .. tile0 + NT - 1 (multi-query:
+  // query rows from qrow0, nnew new tokens, ncol columns; else the G heads).
+  // final_out: the range is the whole context, so the normalised output is
+  // written; otherwise the partial goes to slot pslot (fixed partitions:
+  // slot pslot of the (row, head)'s num_parts; balanced: share slot pslot,
+  // one row per head of the group).
+  auto run = [&](int b, int kvh, int L, int t_begin, int t_end, int tile0, int qrow0, int nnew,
+                 int ncol, bool final_out, int64_t pslot) {
+    const int h0 = kvh * G;
+    // multi-query: column 16 t + c of tile t sees tokens 0 .. lim[t]; the
+    // workgroup reads nothing past its last column's position
+    int lim[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) lim[t] = kMQ ? L - nnew + (16 * (tile0 + t) + c) / G : 0;
-  const int lim_lo = kMQ ? L - nnew + (16 * tile0) / G : 0;  // the first column's
-  const int t_end = kMQ ? max(t_begin, min(min(L, t_begin + PT),
-                                           L - nnew + min(16 * (tile0 + NT) - 1, ncol - 1) / G + 1))
-                        : min(L, t_begin + PT);
-  const bool single = !kMQ && !cascade && L <= PT;
+    for (int t = 0; t < NT; ++t) lim[t] = kMQ ? L - nnew + (16 * (tile0 + t) + c) / G : 0;
+    const int lim_lo = kMQ ? L - nnew + (16 * tile0) / G : 0;  // the first column's
 
-  // Fused step: the partition holding the newest token writes it first; the
-  // fence and barrier make the stores visible to this workgroup's loads.
-  if (!kMQ && p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
-    append_new_token<KV, D, BS, W * kWave>(p, b, kvh, L - 1);
-    __threadfence_block();
-    __syncthreads();
-  }
+    // Fused step: the range holding the newest token writes it first; the
+    // fence and barrier make the stores visible to this workgroup's loads.
+    if (!kMQ && p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
+      append_new_token<KV, D, BS, W * kWave>(p, b, kvh, L - 1);
+      __threadfence_block();
+      __syncthreads();
+    }
 
-  // Q^T operand (B of the score MFMA): lane (c, g), tile t, MFMA j, 8 dims.
-  bf16x8 qf[NT][NJ];
-  float k_off[NT];  // INT4: 136 * sum_d q_d of column c
+    // Q^T operand (B of the score MFMA): lane (c, g), tile t, MFMA j, 8 dims.
+    bf16x8 qf[NT][NJ];
+    float k_off[NT];  // INT4: 136 * sum_d q_d of column c
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int col = 16 * (tile0 + t) + c;
-    const size_t qr = kMQ ? (static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G)
-                          : (static_cast<size_t>(b) * H + h0 + c);
-    const bool qvalid = kMQ ? (col < ncol) : (c < G);
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qr * D;
-    k_off[t] = 0.f;
+    for (int t = 0; t < NT; ++t) {
+      const int col = 16 * (tile0 + t) + c;
+      const size_t qr = kMQ ? (static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G)
+                            : (static_cast<size_t>(b) * H + h0 + c);
+      const bool qvalid = kMQ ? (col < ncol) : (c < G);
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qr * D;
+      k_off[t] = 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int d0 = kI4 ? ((D / 4) * g + 8 * j)
-                         : (kInt8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g));
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qvalid) v = load_u32x4(qrow + d0);
-      if constexpr (kI4) {
-        // element order of the INT4 K operand: dims +0, 2, 4, 6, 1, 3, 5, 7
-        v = u32x4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
-                  __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
+      for (int j = 0; j < NJ; ++j) {
+        const int d0 = kI4 ? ((D / 4) * g + 8 * j)
+                           : (kInt8 ? (64 * (j >> 1) + 16 * g + 8 * (j & 1)) : (32 * j + 8 * g));
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (qvalid) v = load_u32x4(qrow + d0);
+        if constexpr (kI4) {
+          // element order of the INT4 K operand: dims +0, 2, 4, 6, 1, 3, 5, 7
+          v = u32x4{__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                    __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u)};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) k_off[t] += bf16_lo(v[i]) + bf16_hi(v[i]);
+          for (int i = 0; i < 4; ++i) k_off[t] += bf16_lo(v[i]) + bf16_hi(v[i]);
+        }
+        qf[t][j] = as_bf16x8(v);
       }
-      qf[t][j] = as_bf16x8(v);
+      if constexpr (kI4) k_off[t] = kInt4Offset * groups_sum(k_off[t]);
     }
-    if constexpr (kI4) k_off[t] = kInt4Offset * groups_sum(k_off[t]);
-  }
 
-  // Physical block ids of the partition, staged in this wave's LDS slice so
-  // that reading them later waits on LDS traffic only, never on the K/V loads
-  // in flight.
-  const int nblk = (t_end - t_begin + BS - 1) / BS;
-  {
-    const int32_t* bt = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq + t_begin / BS;
-    for (int i = lane; i < nblk; i += kWave) blk_ids[wave][i] = bt[i];  // nblk <= kMaxPartBlocks
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // wave-private slice: own stores only
-  const int* my_ids = blk_ids[wave];
+    const int32_t* bt_row = p.block_tables + static_cast<size_t>(b) * p.max_blocks_per_seq;
+    const int* my_ids = blk_ids[wave];
+    const LoaderT ld(p, kvh, c, g);
 
-  const LoaderT ld(p, kvh, c, g);
-
-  // Block ids of chunk `ch` (uniform).  Past the end of the context the
-  // second half reuses the first block: valid memory whose rows are masked.
-  auto chunk_blocks = [&](int ch, int blk[2], int row0[2]) {
-    const int t0 = t_begin + ch * 32;
-    if (BS == 16) {
-      const int lb = ch * 2;
-      blk[0] = __builtin_amdgcn_readfirstlane(my_ids[lb]);
-      blk[1] = (t0 + 16 < t_end) ? __builtin_amdgcn_readfirstlane(my_ids[lb + 1]) : blk[0];
-      row0[0] = 0;
-      row0[1] = 0;
-    } else {
-      blk[0] = blk[1] = __builtin_amdgcn_readfirstlane(my_ids[ch]);
-      row0[0] = 0;
-      row0[1] = 16;
+    float m_run[NT], l_run[NT];
+    float pv_run[NT];  // INT4: sum_t p_t v_scale_t (this lane's tokens)
+    f32x4 acc[NT][NN];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      m_run[t] = -INFINITY;
+      l_run[t] = 0.f;
+      pv_run[t] = 0.f;
+#pragma unroll
+      for (int n = 0; n < NN; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  };
 
-  float m_run[NT], l_run[NT];
-  float pv_run[NT];  // INT4: sum_t p_t v_scale_t (this lane's tokens)
-  f32x4 acc[NT][NN];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    m_run[t] = -INFINITY;
-    l_run[t] = 0.f;
-    pv_run[t] = 0.f;
-#pragma unroll
-    for (int n = 0; n < NN; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    // The range in pieces of at most kPiece tokens (one staging of block ids
+    // each; fixed partitions are one piece).  Pieces start on chunk
+    // boundaries, so only the last chunk of the last piece can be partial.
+    for (int pb = t_begin; pb < t_end; pb += kPiece) {
+      const int pe = min(t_end, pb + kPiece);
+      // Physical block ids of the piece, staged in this wave's LDS slice so
+      // that reading them later waits on LDS traffic only, never on the K/V
+      // loads in flight.
+      {
+        const int nblk = (pe - pb + BS - 1) / BS;  // <= kMaxPartBlocks
+        const int32_t* bt = bt_row + pb / BS;
+        for (int i = lane; i < nblk; i += kWave) blk_ids[wave][i] = bt[i];
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // wave-private slice: own stores only
 
-  // `masked` (a compile-time bool): the chunk may hold tokens past the end
-  // of the partition or past a column's position.  Clean chunks (all but
-  // the last of a partition) take the instantiation without any masking
-  // code: left to a runtime branch, the compiler turns the masking into
-  // selects that every chunk executes.
-  auto consume = [&](const ChunkT& cw, int ch, auto masked) {
-    constexpr bool kMasked = decltype(masked)::value;
-    const int t0 = t_begin + ch * 32;
-    // ---- scores: S^T of sub-tiles h = 0, 1 for every column tile; each K
-    // operand is widened once and feeds the tiles' contractions
-    f32x4 s[NT][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        s[t][h] = kI4 ? f32x4{-k_off[t], -k_off[t], -k_off[t], -k_off[t]} : f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (kI4) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          uint32_t lo, hi;
-          int4_nibbles(cw.k[h][j], lo, hi);
-          const u32x2 a = nib4_to_bf16(lo), bq = nib4_to_bf16(hi);
-          const bf16x8 ka = as_bf16x8(u32x4{a.x, a.y, bq.x, bq.y});
-#pragma unroll
-          for (int t = 0; t < NT; ++t) s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[t][j], s[t][h], 0, 0, 0);
+      // Block ids of chunk `ch` of the piece (uniform).  Past the end of the
+      // range the second half reuses the first block: valid memory whose rows
+      // are masked.
+      auto chunk_blocks = [&](int ch, int blk[2], int row0[2]) {
+        const int t0 = pb + ch * 32;
+        if (BS == 16) {
+          const int lb = ch * 2;
+          blk[0] = __builtin_amdgcn_readfirstlane(my_ids[lb]);
+          blk[1] = (t0 + 16 < t_end) ? __builtin_amdgcn_readfirstlane(my_ids[lb + 1]) : blk[0];
+          row0[0] = 0;
+          row0[1] = 0;
+        } else {
+          blk[0] = blk[1] = __builtin_amdgcn_readfirstlane(my_ids[ch]);
+          row0[0] = 0;
+          row0[1] = 16;
         }
-      } else if constexpr (kInt8) {
+      };
+
+      // `masked` (a compile-time bool): the chunk may hold tokens past the
+      // end of the range or past a column's position.  Clean chunks (all but
+      // the last of a range) take the instantiation without any masking
+      // code: left to a runtime branch, the compiler turns the masking into
+      // selects that every chunk executes.
+      auto consume = [&](const ChunkT& cw, int ch, auto masked) {
+        constexpr bool kMasked = decltype(masked)::value;
+        const int t0 = pb + ch * 32;
+        // ---- scores: S^T of sub-tiles h = 0, 1 for every column tile; each K
+        // operand is widened once and feeds the tiles' contractions
+        f32x4 s[NT][2];
 #pragma unroll
-        for (int jj = 0; jj < NJ / 2; ++jj) {
-          const u32x4 w = cw.k[h][jj];
-          const bf16x8 k0 = codes8_to_bf16<KV>(w.x, w.y), k1 = codes8_to_bf16<KV>(w.z, w.w);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[t][2 * jj], s[t][h], 0, 0, 0);
-            s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[t][2 * jj + 1], s[t][h], 0, 0, 0);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
           for (int t = 0; t < NT; ++t)
-            s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw.k[h][j]), qf[t][j], s[t][h], 0, 0, 0);
-      }
-    }
-    // ---- online softmax (log2 domain); lane = column c, tokens 4g + i of
-    // sub-tile h (chunk token 16h + 4g + i), element e = 4h + i
-    // multi-query: also mask tokens past a column's position
-    const bool past_end = kMasked && (t0 + 32) > t_end;
-    const bool tail = kMasked && (past_end || (kMQ && t0 + 31 > lim_lo));
-    // V scales of the lane's tokens; zero past the end of the partition,
-    // where rows may hold NaN (select, never multiply)
-    f32x4 vs[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
-    if constexpr (kInt8) {
-      vs[0] = cw.vs[0];
-      vs[1] = cw.vs[1];
-    }
-    if (past_end) {
+            s[t][h] = kI4 ? f32x4{-k_off[t], -k_off[t], -k_off[t], -k_off[t]} : f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (kI4) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (t0 + 16 * (e >> 2) + 4 * g + (e & 3) >= t_end) vs[e >> 2][e & 3] = 0.f;
-    }
-    // P^T operands as bf16 pairs hi + lo (hi = bf16(p), lo = bf16(p - hi)):
-    // two contractions give the weights to ~2^-16 relative instead of 2^-9.
-    uint32_t ph[NT][4], pl[NT][4];
+            for (int j = 0; j < NJ; ++j) {
+              uint32_t lo, hi;
+              int4_nibbles(cw.k[h][j], lo, hi);
+              const u32x2 a = nib4_to_bf16(lo), bq = nib4_to_bf16(hi);
+              const bf16x8 ka = as_bf16x8(u32x4{a.x, a.y, bq.x, bq.y});
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float sc[8];
+              for (int t = 0; t < NT; ++t) s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[t][j], s[t][h], 0, 0, 0);
+            }
+          } else if constexpr (kInt8) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+            for (int jj = 0; jj < NJ / 2; ++jj) {
+              const u32x4 w = cw.k[h][jj];
+              const bf16x8 k0 = codes8_to_bf16<KV>(w.x, w.y), k1 = codes8_to_bf16<KV>(w.z, w.w);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = s[t][h][i];
-          if constexpr (kInt8) x *= cw.ks[h][i];
-          sc[4 * h + i] = x * p.scale_log2;
+              for (int t = 0; t < NT; ++t) {
+                s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[t][2 * jj], s[t][h], 0, 0, 0);
+                s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[t][2 * jj + 1], s[t][h], 0, 0, 0);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+              for (int t = 0; t < NT; ++t)
+                s[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cw.k[h][j]), qf[t][j], s[t][h], 0, 0, 0);
+          }
         }
-      }
-      if (tail) {  // select, never multiply: masked rows may hold NaN
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tok = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
-          if (tok >= t_end || (kMQ && tok > lim[t])) sc[e] = -INFINITY;
+        // ---- online softmax (log2 domain); lane = column c, tokens 4g + i of
+        // sub-tile h (chunk token 16h + 4g + i), element e = 4h + i
+        // multi-query: also mask tokens past a column's position
+        const bool past_end = kMasked && (t0 + 32) > t_end;
+        const bool tail = kMasked && (past_end || (kMQ && t0 + 31 > lim_lo));
+        // V scales of the lane's tokens; zero past the end of the range,
+        // where rows may hold NaN (select, never multiply)
+        f32x4 vs[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};
+        if constexpr (kInt8) {
+          vs[0] = cw.vs[0];
+          vs[1] = cw.vs[1];
         }
-      }
-      float mx = sc[0];
+        if (past_end) {
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-      mx = groups_max(mx);
-      const float m_new = fmaxf(m_run[t], mx);
-      if (__any(m_new > m_run[t])) {
-        float alpha = fast_exp2(m_run[t] - m_new);
-        if constexpr (kMQ) alpha = (m_new == -INFINITY) ? 1.f : alpha;  // a column that saw nothing yet
-        l_run[t] *= alpha;
-        if constexpr (kI4) pv_run[t] *= alpha;
-#pragma unroll
-        for (int n = 0; n < NN; ++n) acc[t][n] *= alpha;
-        m_run[t] = m_new;
-      }
-      float pr[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(sc[e] - m_run[t]);
-      if constexpr (kMQ) {  // -inf - -inf: a column that saw nothing yet
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pr[e] = (sc[e] == -INFINITY) ? 0.f : pr[e];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) l_run[t] += pr[e];
-      if constexpr (kInt8) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pr[e] *= vs[e >> 2][e & 3];
-      }
-      if constexpr (kI4) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv_run[t] += pr[e];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ph[t][i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
-        pl[t][i] = pack_bf16x2(pr[2 * i] - bf16_lo(ph[t][i]), pr[2 * i + 1] - bf16_hi(ph[t][i]));
-      }
-    }
-    // ---- O^T += V^T . P^T; each V operand is widened once for the tiles
-    if constexpr (kI4) {
-#pragma unroll
-      for (int m = 0; m < NN / 2; ++m) {
-        uint32_t lo0, hi0, lo1, hi1;
-        int4_nibbles(cw.v[0][m], lo0, hi0);
-        int4_nibbles(cw.v[1][m], lo1, hi1);
-        const u32x2 a0 = nib4_to_bf16(lo0), a1 = nib4_to_bf16(lo1);
-        const u32x2 b0 = nib4_to_bf16(hi0), b1 = nib4_to_bf16(hi1);
-        u32x4 ve = {a0.x, a0.y, a1.x, a1.y};  // dim 32m + 2c, tokens e = 4h + i
-        u32x4 vo = {b0.x, b0.y, b1.x, b1.y};  // dim 32m + 2c + 1
-        if (past_end) {  // masked tokens contribute exact zeros
-          const int ta = t0 + 4 * g;
-          ve.x = mask_pair(ve.x, ta, t_end);
-          ve.y = mask_pair(ve.y, ta + 2, t_end);
-          ve.z = mask_pair(ve.z, ta + 16, t_end);
-          ve.w = mask_pair(ve.w, ta + 18, t_end);
-          vo.x = mask_pair(vo.x, ta, t_end);
-          vo.y = mask_pair(vo.y, ta + 2, t_end);
-          vo.z = mask_pair(vo.z, ta + 16, t_end);
-          vo.w = mask_pair(vo.w, ta + 18, t_end);
+          for (int e = 0; e < 8; ++e)
+            if (t0 + 16 * (e >> 2) + 4 * g + (e & 3) >= t_end) vs[e >> 2][e & 3] = 0.f;
         }
+        // P^T operands as bf16 pairs hi + lo (hi = bf16(p), lo = bf16(p - hi)):
+        // two contractions give the weights to ~2^-16 relative instead of 2^-9.
+        uint32_t ph[NT][4], pl[NT][4];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          const bf16x8 pfh = as_bf16x8(u32x4{ph[t][0], ph[t][1], ph[t][2], ph[t][3]});
-          const bf16x8 pfl = as_bf16x8(u32x4{pl[t][0], pl[t][1], pl[t][2], pl[t][3]});
-          acc[t][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfh, acc[t][2 * m], 0, 0, 0);
-          acc[t][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfl, acc[t][2 * m], 0, 0, 0);
-          acc[t][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfh, acc[t][2 * m + 1], 0, 0, 0);
-          acc[t][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfl, acc[t][2 * m + 1], 0, 0, 0);
+          float sc[8];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float x = s[t][h][i];
+              if constexpr (kInt8) x *= cw.ks[h][i];
+              sc[4 * h + i] = x * p.scale_log2;
+            }
+          }
+          if (tail) {  // select, never multiply: masked rows may hold NaN
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int tok = t0 + 16 * (e >> 2) + 4 * g + (e & 3);
+              if (tok >= t_end || (kMQ && tok > lim[t])) sc[e] = -INFINITY;
+            }
+          }
+          float mx = sc[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+          mx = groups_max(mx);
+          const float m_new = fmaxf(m_run[t], mx);
+          if (__any(m_new > m_run[t])) {
+            float alpha = fast_exp2(m_run[t] - m_new);
+            if constexpr (kMQ) alpha = (m_new == -INFINITY) ? 1.f : alpha;  // a column that saw nothing yet
+            l_run[t] *= alpha;
+            if constexpr (kI4) pv_run[t] *= alpha;
+#pragma unroll
+            for (int n = 0; n < NN; ++n) acc[t][n] *= alpha;
+            m_run[t] = m_new;
+          }
+          float pr[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(sc[e] - m_run[t]);
+          if constexpr (kMQ) {  // -inf - -inf: a column that saw nothing yet
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pr[e] = (sc[e] == -INFINITY) ? 0.f : pr[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) l_run[t] += pr[e];
+          if constexpr (kInt8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pr[e] *= vs[e >> 2][e & 3];
+          }
+          if constexpr (kI4) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv_run[t] += pr[e];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ph[t][i] = pack_bf16x2(pr[2 * i], pr[2 * i + 1]);
+            pl[t][i] = pack_bf16x2(pr[2 * i] - bf16_lo(ph[t][i]), pr[2 * i + 1] - bf16_hi(ph[t][i]));
+          }
+        }
+        // ---- O^T += V^T . P^T; each V operand is widened once for the tiles
+        if constexpr (kI4) {
+#pragma unroll
+          for (int m = 0; m < NN / 2; ++m) {
+            uint32_t lo0, hi0, lo1, hi1;
+            int4_nibbles(cw.v[0][m], lo0, hi0);
+            int4_nibbles(cw.v[1][m], lo1, hi1);
+            const u32x2 a0 = nib4_to_bf16(lo0), a1 = nib4_to_bf16(lo1);
+            const u32x2 b0 = nib4_to_bf16(hi0), b1 = nib4_to_bf16(hi1);
+            u32x4 ve = {a0.x, a0.y, a1.x, a1.y};  // dim 32m + 2c, tokens e = 4h + i
+            u32x4 vo = {b0.x, b0.y, b1.x, b1.y};  // dim 32m + 2c + 1
+            if (past_end) {  // masked tokens contribute exact zeros
+              const int ta = t0 + 4 * g;
+              ve.x = mask_pair(ve.x, ta, t_end);
+              ve.y = mask_pair(ve.y, ta + 2, t_end);
+              ve.z = mask_pair(ve.z, ta + 16, t_end);
+              ve.w = mask_pair(ve.w, ta + 18, t_end);
+              vo.x = mask_pair(vo.x, ta, t_end);
+              vo.y = mask_pair(vo.y, ta + 2, t_end);
+              vo.z = mask_pair(vo.z, ta + 16, t_end);
+              vo.w = mask_pair(vo.w, ta + 18, t_end);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const bf16x8 pfh = as_bf16x8(u32x4{ph[t][0], ph[t][1], ph[t][2], ph[t][3]});
+              const bf16x8 pfl = as_bf16x8(u32x4{pl[t][0], pl[t][1], pl[t][2], pl[t][3]});
+              acc[t][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfh, acc[t][2 * m], 0, 0, 0);
+              acc[t][2 * m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ve), pfl, acc[t][2 * m], 0, 0, 0);
+              acc[t][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfh, acc[t][2 * m + 1], 0, 0, 0);
+              acc[t][2 * m + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vo), pfl, acc[t][2 * m + 1], 0, 0, 0);
+            }
+          }
+          return;
+        }
+#pragma unroll
+        for (int n = 0; n < NN; ++n) {
+          u32x4 vw;
+          if constexpr (kInt8) {
+            vw = u32x4{codes_to_bf16x2<KV, 0>(cw.v[0][n]), codes_to_bf16x2<KV, 1>(cw.v[0][n]),
+                       codes_to_bf16x2<KV, 0>(cw.v[1][n]), codes_to_bf16x2<KV, 1>(cw.v[1][n])};
+          } else {
+            vw = u32x4{cw.v[0][n].x, cw.v[0][n].y, cw.v[1][n].x, cw.v[1][n].y};
+          }
+          if (past_end) {  // masked tokens contribute exact zeros, even over NaN
+            const int ta = t0 + 4 * g;
+            vw.x = mask_pair(vw.x, ta, t_end);
+            vw.y = mask_pair(vw.y, ta + 2, t_end);
+            vw.z = mask_pair(vw.z, ta + 16, t_end);
+            vw.w = mask_pair(vw.w, ta + 18, t_end);
+          }
+          const bf16x8 va = as_bf16x8(vw);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const bf16x8 pfh = as_bf16x8(u32x4{ph[t][0], ph[t][1], ph[t][2], ph[t][3]});
+            const bf16x8 pfl = as_bf16x8(u32x4{pl[t][0], pl[t][1], pl[t][2], pl[t][3]});
+            acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc[t][n], 0, 0, 0);
+            acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc[t][n], 0, 0, 0);
+          }
+        }
+      };
+
+      // ---- this wave's chunks ch = wave, wave + W, ... of the piece in
+      // batches of NB: the loads of the whole batch are issued before any
+      // chunk is consumed, and no load stays pending across iterations, so
+      // every wait counts exactly the loads behind it.  A batch is loaded and
+      // consumed last chunk first, so the full-batch and tail branches share
+      // no leading code the compiler could hoist, together with its waits,
+      // above the batch's other loads.
+      // Full batches take only clean chunks (every token inside the range
+      // and, multi-query, at or before every column's position); from the
+      // first batch that would reach an unclean chunk on, chunks go one at a
+      // time through the masked instantiation.
+      // (Batches of one chunk, several column tiles, keep the one masked body
+      // for every chunk, and so does INT4 at bs = 32: a second copy of their
+      // body spills.)
+      constexpr bool kCleanBatches = NB > 1 && !(kI4 && BS == 32);
+      using kBatchMasked = std::integral_constant<bool, !kCleanBatches>;
+      const int nchunks = (pe - pb + 31) / 32;
+      const int nclean = kCleanBatches ? max(0, ((kMQ ? min(pe, lim_lo + 1) : pe) - pb) / 32) : nchunks;
+      {
+        ChunkT cb[NB];
+        int blk[2], row0[2];
+        for (int ch = wave; ch < nchunks; ch += NB * W) {
+          if (ch + (NB - 1) * W < nclean) {
+#pragma unroll
+            for (int k = NB - 1; k >= 0; --k) {
+              chunk_blocks(ch + k * W, blk, row0);
+              ld.load(cb[k], blk, row0);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of the math
+#pragma unroll
+            for (int k = NB - 1; k >= 0; --k) consume(cb[k], ch + k * W, kBatchMasked{});
+          } else {
+            for (int c2 = ch; c2 < nchunks; c2 += W) {
+              chunk_blocks(c2, blk, row0);
+              ld.load(cb[0], blk, row0);
+              consume(cb[0], c2, std::true_type{});
+            }
+          }
         }
       }
-      return;
     }
-#pragma unroll
-    for (int n = 0; n < NN; ++n) {
-      u32x4 vw;
-      if constexpr (kInt8) {
-        vw = u32x4{codes_to_bf16x2<KV, 0>(cw.v[0][n]), codes_to_bf16x2<KV, 1>(cw.v[0][n]),
-                   codes_to_bf16x2<KV, 0>(cw.v[1][n]), codes_to_bf16x2<KV, 1>(cw.v[1][n])};
-      } else {
-        vw = u32x4{cw.v[0][n].x, cw.v[0][n].y, cw.v[1][n].x, cw.v[1][n].y};
-      }
-      if (past_end) {  // masked tokens contribute exact zeros, even over NaN
-        const int ta = t0 + 4 * g;
-        vw.x = mask_pair(vw.x, ta, t_end);
-        vw.y = mask_pair(vw.y, ta + 2, t_end);
-        vw.z = mask_pair(vw.z, ta + 16, t_end);
-        vw.w = mask_pair(vw.w, ta + 18, t_end);
-      }
-      const bf16x8 va = as_bf16x8(vw);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8 pfh = as_bf16x8(u32x4{ph[t][0], ph[t][1], ph[t][2], ph[t][3]});
-        const bf16x8 pfl = as_bf16x8(u32x4{pl[t][0], pl[t][1], pl[t][2], pl[t][3]});
-        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfh, acc[t][n], 0, 0, 0);
-        acc[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pfl, acc[t][n], 0, 0, 0);
-      }
-    }
-  };
 
-  // ---- this wave's chunks ch = wave, wave + W, ... in batches of NB: the
-  // loads of the whole batch are issued before any chunk is consumed, and no
-  // load stays pending across iterations, so every wait counts exactly the
-  // loads behind it.  A batch is loaded and consumed last chunk first, so the
-  // full-batch and tail branches share no leading code the compiler could
-  // hoist, together with its waits, above the batch's other loads.
-  // Full batches take only clean chunks (every token inside the partition
-  // and, multi-query, at or before every column's position); from the
-  // first batch that would reach an unclean chunk on, chunks go one at a
-  // time through the masked instantiation.
-  // (Batches of one chunk, several column tiles, keep the one masked body
-  // for every chunk, and so does INT4 at bs = 32: a second copy of their
-  // body spills.)
-  constexpr bool kCleanBatches = NB > 1 && !(kI4 && BS == 32);
-  using kBatchMasked = std::integral_constant<bool, !kCleanBatches>;
-  const int nchunks = (t_end - t_begin + 31) / 32;
-  const int nclean = kCleanBatches ? max(0, ((kMQ ? min(t_end, lim_lo + 1) : t_end) - t_begin) / 32) : nchunks;
-  {
-    ChunkT cb[NB];
-    int blk[2], row0[2];
-    for (int ch = wave; ch < nchunks; ch += NB * W) {
-      if (ch + (NB - 1) * W < nclean) {
-#pragma unroll
-        for (int k = NB - 1; k >= 0; --k) {
-          chunk_blocks(ch + k * W, blk, row0);
-          ld.load(cb[k], blk, row0);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of the math
-#pragma unroll
-        for (int k = NB - 1; k >= 0; --k) consume(cb[k], ch + k * W, kBatchMasked{});
-      } else {
-        for (int c2 = ch; c2 < nchunks; c2 += W) {
-          chunk_blocks(c2, blk, row0);
-          ld.load(cb[0], blk, row0);
-          consume(cb[0], c2, std::true_type{});
-        }
-      }
-    }
-  }
-
-  // per-column sums over the 4 lane groups (each holds different tokens)
-  float M[NT], Lsum[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    l_run[t] = groups_sum(l_run[t]);
-    if constexpr (kI4) {  // remove the V offset of this wave's tokens
-      const float v_off = kInt4Offset * groups_sum(pv_run[t]);
-#pragma unroll
-      for (int n = 0; n < NN; ++n) acc[t][n] -= v_off;
-    }
-    M[t] = m_run[t];
-    Lsum[t] = l_run[t];
-  }
-
-  if constexpr (W > 1) {
-    // the waves' states merge into wave 0 through LDS, one column tile at a
-    // time (the buffers hold one tile)
+    // per-column sums over the 4 lane groups (each holds different tokens)
+    float M[NT], Lsum[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (t > 0) __syncthreads();  // wave 0 has read the previous tile
-      red_m[wave][lane] = m_run[t];
-      red_l[wave][lane] = l_run[t];
-      if (wave > 0) {
+      l_run[t] = groups_sum(l_run[t]);
+      if constexpr (kI4) {  // remove the V offset of this wave's tokens
+        const float v_off = kInt4Offset * groups_sum(pv_run[t]);
 #pragma unroll
-        for (int n = 0; n < NN; ++n)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) red_acc[wave - 1][4 * n + i][lane] = acc[t][n][i];
+        for (int n = 0; n < NN; ++n) acc[t][n] -= v_off;
       }
-      __syncthreads();
-      if (wave == 0) {
-        float Mt = m_run[t];
+      M[t] = m_run[t];
+      Lsum[t] = l_run[t];
+    }
+
+    if constexpr (W > 1) {
+      // the waves' states merge into wave 0 through LDS, one column tile at a
+      // time (the buffers hold one tile)
 #pragma unroll
-        for (int w = 1; w < W; ++w) Mt = fmaxf(Mt, red_m[w][lane]);
-        // Mt finite: wave 0 saw a chunk (multi-query: unless the column saw nothing)
-        const float f0 = (kMQ && Mt == -INFINITY) ? 0.f : fast_exp2(m_run[t] - Mt);
-        float Ls = l_run[t] * f0;
-#pragma unroll
-        for (int n = 0; n < NN; ++n) acc[t][n] *= f0;
-#pragma unroll
-        for (int w = 1; w < W; ++w) {
-          const float fw = (kMQ && Mt == -INFINITY) ? 0.f : fast_exp2(red_m[w][lane] - Mt);  // idle wave -> 0
-          Ls += fw * red_l[w][lane];
+      for (int t = 0; t < NT; ++t) {
+        if (t > 0) __syncthreads();  // wave 0 has read the previous tile
+        red_m[wave][lane] = m_run[t];
+        red_l[wave][lane] = l_run[t];
+        if (wave > 0) {
 #pragma unroll
           for (int n = 0; n < NN; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][n][i] += fw * red_acc[w - 1][4 * n + i][lane];
+            for (int i = 0; i < 4; ++i) red_acc[wave - 1][4 * n + i][lane] = acc[t][n][i];
         }
-        M[t] = Mt;
-        Lsum[t] = Ls;
+        __syncthreads();
+        if (wave == 0) {
+          float Mt = m_run[t];
+#pragma unroll
+          for (int w = 1; w < W; ++w) Mt = fmaxf(Mt, red_m[w][lane]);
+          // Mt finite: wave 0 saw a chunk (multi-query: unless the column saw nothing)
+          const float f0 = (kMQ && Mt == -INFINITY) ? 0.f : fast_exp2(m_run[t] - Mt);
+          float Ls = l_run[t] * f0;
+#pragma unroll
+          for (int n = 0; n < NN; ++n) acc[t][n] *= f0;
+#pragma unroll
+          for (int w = 1; w < W; ++w) {
+            const float fw = (kMQ && Mt == -INFINITY) ? 0.f : fast_exp2(red_m[w][lane] - Mt);  // idle wave -> 0
+            Ls += fw * red_l[w][lane];
+#pragma unroll
+            for (int n = 0; n < NN; ++n)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[t][n][i] += fw * red_acc[w - 1][4 * n + i][lane];
+          }
+          M[t] = Mt;
+          Lsum[t] = Ls;
+        }
       }
+      if (wave != 0) return;
     }
-    if (wave != 0) return;
-  }
 
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int col = 16 * (tile0 + t) + c;
-    if (kMQ ? col >= ncol : c >= G) continue;
-    // output row: (sequence, head), or (query row, head) in multi-query mode
-    const size_t bh = kMQ ? static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G
-                          : static_cast<size_t>(b) * H + h0 + c;
-    const size_t slot = bh * p.num_parts + (cascade ? p.prefix_parts : 0) + part;
-    if constexpr (kI4) {  // lane holds dims 32m + 8g .. + 7: tiles 2m (even), 2m + 1 (odd)
-      if (single) {
+    for (int t = 0; t < NT; ++t) {
+      const int col = 16 * (tile0 + t) + c;
+      if (kMQ ? col >= ncol : c >= G) continue;
+      // output row: (sequence, head), or (query row, head) in multi-query mode
+      const size_t bh = kMQ ? static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G
+                            : static_cast<size_t>(b) * H + h0 + c;
+      const size_t slot = kBal ? static_cast<size_t>(pslot) * G + c : bh * p.num_parts + pslot;
+      if constexpr (kI4) {  // lane holds dims 32m + 8g .. + 7: tiles 2m (even), 2m + 1 (odd)
+        if (final_out) {
+          uint16_t* orow = out + bh * D;
+#pragma unroll
+          for (int m = 0; m < NN / 2; ++m) {
+            const f32x4 e = acc[t][2 * m] / Lsum[t], o = acc[t][2 * m + 1] / Lsum[t];
+            *reinterpret_cast<u32x4*>(orow + 32 * m + 8 * g) =
+                u32x4{pack_bf16x2(e[0], o[0]), pack_bf16x2(e[1], o[1]), pack_bf16x2(e[2], o[2]), pack_bf16x2(e[3], o[3])};
+          }
+        } else {
+          float* arow = p.ws_acc + slot * D;
+#pragma unroll
+          for (int m = 0; m < NN / 2; ++m) {
+            const f32x4 e = acc[t][2 * m], o = acc[t][2 * m + 1];
+            *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
+            *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
+          }
+        }
+      } else if (final_out) {
         uint16_t* orow = out + bh * D;
 #pragma unroll
-        for (int m = 0; m < NN / 2; ++m) {
-          const f32x4 e = acc[t][2 * m] / Lsum[t], o = acc[t][2 * m + 1] / Lsum[t];
-          *reinterpret_cast<u32x4*>(orow + 32 * m + 8 * g) =
-              u32x4{pack_bf16x2(e[0], o[0]), pack_bf16x2(e[1], o[1]), pack_bf16x2(e[2], o[2]), pack_bf16x2(e[3], o[3])};
+        for (int n = 0; n < NN; ++n) {
+          u32x2 w;
+          w.x = pack_bf16x2(acc[t][n][0] / Lsum[t], acc[t][n][1] / Lsum[t]);
+          w.y = pack_bf16x2(acc[t][n][2] / Lsum[t], acc[t][n][3] / Lsum[t]);
+          *reinterpret_cast<u32x2*>(orow + 16 * n + 4 * g) = w;
         }
       } else {
         float* arow = p.ws_acc + slot * D;
 #pragma unroll
-        for (int m = 0; m < NN / 2; ++m) {
-          const f32x4 e = acc[t][2 * m], o = acc[t][2 * m + 1];
-          *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
-          *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
-        }
+        for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[t][n];
       }
-    } else if (single) {
-      uint16_t* orow = out + bh * D;
-#pragma unroll
-      for (int n = 0; n < NN; ++n) {
-        u32x2 w;
-        w.x = pack_bf16x2(acc[t][n][0] / Lsum[t], acc[t][n][1] / Lsum[t]);
-        w.y = pack_bf16x2(acc[t][n][2] / Lsum[t], acc[t][n][3] / Lsum[t]);
-        *reinterpret_cast<u32x2*>(orow + 16 * n + 4 * g) = w;
+      if (!final_out && g == 0) {
+        p.ws_m[slot] = M[t];
+        p.ws_l[slot] = Lsum[t];
       }
+    }
+  };
+
+  if constexpr (kBal) {
+    // ---- the workgroup's share.  Unit u = b * Hkv + kvh holds n_b =
+    // ceil(L_b / 32) chunks; sequence b's units start at chunk Hkv * P_b,
+    // P_b = sum of n over the sequences before b.  Every wave computes the
+    // same (uniform) values.
+    const int B = p.num_seqs;
+    int64_t C = 0;  // all chunks
+    for (int base = 0; base < B; base += kWave) {
+      const int bb = base + lane;
+      const int Lb = bb < B ? max(p.context_lens[bb], 0) : 0;
+      C += readlane64(wave_incl_scan((Lb + 31) >> 5), kWave - 1);
+    }
+    C *= Hkv;
+    // shares: at least kMinShareChunks chunks each, at most one per
+    // workgroup, a multiple of 8 (the XCD count) once there are 8
+    int64_t se = min(static_cast<int64_t>(gridDim.x), C / kMinShareChunks);
+    se = max(se, int64_t(1));
+    if (se >= 8) se &= ~int64_t(7);
+    const int Se = static_cast<int>(se);
+    const int bid = blockIdx.x;
+    if (bid >= Se) return;
+    // workgroups go to the XCDs round-robin; share s = XCD-major, so each
+    // XCD takes a contiguous run of shares and the kv-heads whose scale rows
+    // share cache lines run on one XCD's L2
+    const int s = Se >= 8 ? (bid & 7) * (Se >> 3) + (bid >> 3) : bid;
+    const int64_t cq = C / Se, cr = C % Se;
+    const int64_t a = cq * s + (cr * s) / Se;            // floor(s C / Se)
+    const int64_t e = cq * (s + 1) + (cr * (s + 1)) / Se;
+    if (a >= e) return;  // no chunks at all
+    // share holding chunk x: the largest s' with floor(s' C / Se) <= x
+    auto share_of = [&](int64_t x) { return ((x + 1) * Se - 1) / C; };
+
+    // the sequence holding chunk a, and where its units start
+    int b = 0, L = 0;
+    int64_t pos = 0;
+    for (int base = 0; base < B; base += kWave) {
+      const int bb = base + lane;
+      const int Lb = bb < B ? max(p.context_lens[bb], 0) : 0;
+      const int64_t w = static_cast<int64_t>((Lb + 31) >> 5) * Hkv;
+      const int64_t incl = wave_incl_scan(w);
+      const int64_t tot = readlane64(incl, kWave - 1);
+      if (pos + tot > a) {
+        const int j = __builtin_ctzll(__ballot(pos + incl > a));
+        b = base + j;
+        L = __builtin_amdgcn_readlane(Lb, j);
+        pos += readlane64(incl - w, j);
+        break;
+      }
+      pos += tot;
+    }
+    int nb = (L + 31) >> 5;
+    int kvh = static_cast<int>((a - pos) / nb);
+    int64_t cu = pos + static_cast<int64_t>(kvh) * nb;  // first chunk of unit (b, kvh)
+    int64_t lo = a;
+    for (;;) {
+      const int64_t uend = cu + nb;
+      const int64_t hi = min(uend, e);
+      const bool whole = lo == cu && hi == uend;
+      const int64_t pslot = lo == a ? 2 * int64_t(s) : 2 * int64_t(s) + 1;
+      if (lo == cu && threadIdx.x == 0) {  // this share holds the unit's first chunk
+        const int nsplit = whole ? 1 : static_cast<int>(share_of(uend - 1) - s + 1);
+        *reinterpret_cast<int2*>(p.ws_unit + 2 * (static_cast<size_t>(b) * Hkv + kvh)) =
+            int2{static_cast<int>(pslot), nsplit};
+      }
+      run(b, kvh, L, static_cast<int>(lo - cu) * 32, min(L, static_cast<int>(hi - cu) * 32), 0, 0, 0, G,
+          whole, pslot);
+      if (uend >= e) break;
+      __syncthreads();  // the merge buffers are reused by the next segment
+      lo = cu = uend;
+      if (++kvh == Hkv) {
+        // the next sequence with tokens (one exists: chunks remain before e)
+        kvh = 0;
+        do {
+          ++b;
+          L = p.context_lens[b];
+        } while (L <= 0);
+        nb = (L + 31) >> 5;
+      }
+    }
+  } else {
+    int b, kvh, tile0 = 0;
+    if constexpr (kMQ) {
+      // blockIdx.x = ((u / 8) * groups + tg) * 8 + u % 8 for u = b * Hkv + kvh
+      // and tile group tg (tiles tg * NT ..): the tile groups of one (sequence,
+      // kv-head) run on the same XCD (workgroups go to XCDs round-robin) and
+      // share its L2
+      const int groups = (p.mq_tiles + NT - 1) / NT;
+      const int rest = blockIdx.x >> 3;
+      tile0 = (rest % groups) * NT;
+      const int u = (rest / groups) * 8 + (blockIdx.x & 7);
+      if (u >= p.num_seqs * Hkv) return;  // uniform across the workgroup
+      b = u / Hkv;
+      kvh = u - b * Hkv;
     } else {
-      float* arow = p.ws_acc + slot * D;
-#pragma unroll
-      for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[t][n];
+      b = blockIdx.x / Hkv;
+      kvh = blockIdx.x - b * Hkv;
     }
-    if (!single && g == 0) {
-      p.ws_m[slot] = M[t];
-      p.ws_l[slot] = Lsum[t];
+    const int part = blockIdx.y;
+    const int PT = p.part_tokens;
+
+    const int L = p.context_lens[b];
+    // multi-query: this sequence's n new tokens x G heads are its columns
+    int qrow0 = 0, nnew = 0, ncol = G;
+    if constexpr (kMQ) {
+      qrow0 = p.query_start[b];
+      nnew = p.query_start[b + 1] - qrow0;
+      ncol = nnew * G;
+      if (16 * tile0 >= ncol) return;  // uniform; also every sequence with L == 0
     }
+    // cascade: the group's shared tokens are attended by the prefix kernel
+    const bool cascade = !kMQ && p.group_start != nullptr;
+    const int t_begin = (cascade ? group_shared_tokens(p, group_of(p, b)) : 0) + part * PT;
+    if ((kMQ || cascade || part != 0) && t_begin >= L) return;  // uniform across the workgroup
+
+    if (L <= 0) {  // empty context: zero output
+      for (int i = threadIdx.x; i < G * D; i += W * kWave)
+        out[(static_cast<size_t>(b) * H + kvh * G) * D + i] = 0;
+      return;
+    }
+    const int t_end = kMQ ? max(t_begin, min(min(L, t_begin + PT),
+                                             L - nnew + min(16 * (tile0 + NT) - 1, ncol - 1) / G + 1))
+                          : min(L, t_begin + PT);
+    const bool single = !kMQ && !cascade && L <= PT;
+    run(b, kvh, L, t_begin, t_end, tile0, qrow0, nnew, ncol, single, (cascade ? p.prefix_parts : 0) + part);
   }
 }
 
@@ -582,21 +719,29 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
       // INT4: one tile per workgroup (more tiles' states do not fit beside
       // its conversion registers at two waves per SIMD)
       const dim3 grid(padded * static_cast<unsigned>(p.mq_tiles), static_cast<unsigned>(parts));
-      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, true, 1>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, true, 1, false>), grid, block, 0, s, p);
     } else {
       // every column tile of a (sequence, kv-head) in one workgroup
       static_assert(kMqDecodeMaxTiles == 3, "one instance per tile count");
       const dim3 grid(padded, static_cast<unsigned>(parts));
       if constexpr (KV != KvKind::I4) {
         if (p.mq_tiles == 2)
-          hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, true, 2>), grid, block, 0, s, p);
+          hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, true, 2, false>), grid, block, 0, s, p);
         else
-          hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, true, 3>), grid, block, 0, s, p);
+          hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, true, 3, false>), grid, block, 0, s, p);
       }
+    }
+  } else if (p.bal_shares > 0) {
+    // balanced shares: one workgroup per share, a 1-D grid (not INT4)
+    if constexpr (KV == KvKind::I4) {
+      return hipErrorInvalidValue;
+    } else {
+      const dim3 grid(static_cast<unsigned>(p.bal_shares));
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, true>), grid, block, 0, s, p);
     }
   } else {
     const dim3 grid(units, static_cast<unsigned>(parts));
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
@@ -609,6 +754,10 @@ hipError_t launch_kv(const DecodeParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int balanced_slots_per_cu(KvKind kv) {
+  return kv == KvKind::I4 ? kWavesPerSimd<KvKind::I4, 1> : kWavesPerSimd<KvKind::BF16, 1>;
+}
 
 hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s) {
   if (kv == KvKind::I8) return launch_kv<KvKind::I8>(p, s);

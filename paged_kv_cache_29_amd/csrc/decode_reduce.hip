@@ -34,12 +34,32 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
   if (bh >= (mq ? p.num_query_rows : p.num_seqs) * p.num_heads) return;  // the whole wave
   const int b = mq ? range_of(p.query_start, p.num_seqs, bh / p.num_heads) : bh / p.num_heads;
   const int L = p.context_lens[b];
-  // Partials i = 0 .. nparts-1 live in workspace slots slot(i): partitions
-  // of the context, or (cascade) npre shared-prefix partitions in slots
+  // Partials i = 0 .. nparts-1 live in workspace rows idx(i): partitions of
+  // the context, or (cascade) npre shared-prefix partitions in slots
   // 0 .. npre-1 followed by the partitions of the rest of the context from
-  // slot prefix_parts on.
+  // slot prefix_parts on, or (balanced shares) the share slots the unit's
+  // first workgroup recorded.
   int npre = 0, nparts, skip = 0;
-  if (p.group_start != nullptr) {
+  int slot0 = 0, gh = 0;  // balanced: first slot of the unit; head within its group
+  if (p.bal_shares > 0) {
+    if (L <= 0) {  // empty context: no share attended it
+      for (int k = lane; k < D; k += kWave) {
+        const size_t idx = static_cast<size_t>(bh) * D + k;
+        if constexpr (kOutBf16)
+          static_cast<uint16_t*>(p.out)[idx] = 0;
+        else
+          static_cast<float*>(p.out)[idx] = 0.f;
+      }
+      return;
+    }
+    const int G = p.num_heads / p.num_kv_heads;
+    const int h = bh - b * p.num_heads;
+    gh = h % G;
+    const int2 u = *reinterpret_cast<const int2*>(p.ws_unit + 2 * (static_cast<size_t>(b) * p.num_kv_heads + h / G));
+    slot0 = __builtin_amdgcn_readfirstlane(u.x);
+    nparts = __builtin_amdgcn_readfirstlane(u.y);
+    if (nparts <= 1) return;  // written whole by the partition kernel
+  } else if (p.group_start != nullptr) {
     const int S = group_shared_tokens(p, group_of(p, b));
     npre = (S + p.prefix_part_tokens - 1) / p.prefix_part_tokens;
     nparts = npre + (L > S ? (L - S + p.part_tokens - 1) / p.part_tokens : 0);
@@ -62,19 +82,25 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
     nparts = (L + p.part_tokens - 1) / p.part_tokens;
     if (nparts <= 1) return;  // written by the partition kernel
   }
-  auto slot = [&](int i) { return i < npre ? i : i + skip; };
+  const bool bal = p.bal_shares > 0;
+  const int G = p.num_heads / p.num_kv_heads;
   const size_t base = static_cast<size_t>(bh) * p.num_parts;
-  const float* m = p.ws_m + base;
-  const float* l = p.ws_l + base;
-  const float* row = p.ws_acc + base * D + lane;
+  // workspace row (of ws_m / ws_l, and of D floats in ws_acc) of partial i
+  auto slot = [&](int i) -> size_t {
+    if (bal) return static_cast<size_t>(i == 0 ? slot0 : 2 * ((slot0 >> 1) + i)) * G + gh;
+    return base + (i < npre ? i : i + skip);
+  };
+  const float* m = p.ws_m;
+  const float* l = p.ws_l;
+  const float* row = p.ws_acc + lane;
   // groups of 8 rows: 8 independent loads per lane in flight; rows past
   // cnt re-read the last valid row and get weight 0 (wv is 0 there)
   auto load8 = [&](float (&x)[8][ND], int first, int j0, int cnt) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int j = slot(first + min(j0 + u, max(cnt - 1, 0)));
+      const size_t j = slot(first + min(j0 + u, max(cnt - 1, 0)));
 #pragma unroll
-      for (int k = 0; k < ND; ++k) x[u][k] = row[static_cast<size_t>(j) * D + kWave * k];
+      for (int k = 0; k < ND; ++k) x[u][k] = row[j * D + kWave * k];
     }
   };
   float num[ND];

@@ -2,6 +2,7 @@
 // sizing and error reporting.  Every check here runs before any HIP call, so
 // an invalid call launches nothing and has no side effect.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -127,6 +128,57 @@ int32_t num_parts_for(int32_t block_size, int32_t max_blocks_per_seq, int32_t pt
   return static_cast<int32_t>((ctx + pt - 1) / pt);
 }
 
+// Balanced shares (DecodeParams::bal_shares).  The partition kernel's grid
+// is one workgroup per share, sized to the workgroups all CUs hold at once
+// (MI355X: 256 CUs) times kShareRounds.
+constexpr int32_t kNumCUs = 256;
+constexpr int32_t kShareRounds = 1;
+
+int32_t shares_for(pkv::KvKind kv) { return kShareRounds * kNumCUs * pkv::balanced_slots_per_cu(kv); }
+int32_t max_shares() {
+  int32_t s = 0;
+  for (pkv::KvKind kv : {pkv::KvKind::BF16, pkv::KvKind::I8, pkv::KvKind::FP8, pkv::KvKind::E5M2})
+    s = std::max(s, shares_for(kv));
+  return s;
+}
+
+// Does a call with these sizes run in balanced shares?  The automatic
+// choice, a bf16 or byte-code cache, and contexts that may span more than
+// one partition (otherwise one workgroup per (sequence, kv-head) attends
+// it whole and no reduce runs); chunk counts must stay far inside 64-bit
+// arithmetic.  fp32 caches have their own kernel.  INT4 keeps fixed
+// partitions: its kernel runs three workgroups per CU only within 168
+// VGPRs, which the share walk exceeds (spills); at two per CU, or with the
+// spills, its step measured 134-166 us against 131-133 us on fixed
+// partitions (70B-shaped INT4 workload, one box).
+bool balanced_for(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size, int32_t max_blocks_per_seq,
+                  int32_t partition_tokens, pkv::KvKind kv) {
+  if (partition_tokens != 0 || num_seqs <= 0) return false;
+  if (kv != pkv::KvKind::BF16 && kv != pkv::KvKind::I8 && kv != pkv::KvKind::FP8 && kv != pkv::KvKind::E5M2)
+    return false;
+  const int32_t pt = auto_part_tokens(num_seqs, num_kv_heads, block_size, max_blocks_per_seq);
+  const int64_t ctx = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  if (ctx <= pt) return false;
+  const int64_t chunks = static_cast<int64_t>(num_seqs) * num_kv_heads * ((ctx + kChunk - 1) / kChunk);
+  return chunks < (int64_t(1) << 40);
+}
+
+// Workspace of balanced shares: ws_acc [2S][G][D], ws_m and ws_l [2S][G],
+// ws_unit [B * Hkv][2] int32, each 256-byte aligned.
+struct BalancedLayout {
+  size_t acc, ml, unit;
+  size_t total() const { return acc + 2 * ml + unit; }
+};
+BalancedLayout balanced_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t shares) {
+  const size_t rows = static_cast<size_t>(2) * shares * (num_heads / num_kv_heads);
+  BalancedLayout l;
+  l.acc = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
+  l.ml = (rows * sizeof(float) + 255) & ~size_t(255);
+  l.unit = (static_cast<size_t>(num_seqs) * num_kv_heads * 2 * sizeof(int32_t) + 255) & ~size_t(255);
+  return l;
+}
+
 size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t nparts) {
   if (nparts <= 1) return 0;
   const size_t rows = static_cast<size_t>(num_seqs) * num_heads * nparts;
@@ -151,7 +203,7 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
                            int64_t num_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype,
                            int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                            const void* k_new, const void* v_new, bool step, DecodeSetup* st,
-                           bool check_workspace = true) {
+                           bool check_workspace = true, bool allow_balanced = false) {
   if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
   if (num_heads <= 0 || num_kv_heads <= 0)
     return fail(PKV_ERR_INVALID, "num_heads and num_kv_heads must be positive");
@@ -210,7 +262,13 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   } else if (k_scale || v_scale) {
     return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL for fp32 and bf16 caches");
   }
-  const size_t need = check_workspace ? workspace_bytes_for(num_seqs, num_heads, head_dim, nparts) : 0;
+  const bool bal = allow_balanced && balanced_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
+                                                  partition_tokens, kv);
+  const int32_t shares = bal ? shares_for(kv) : 0;
+  const BalancedLayout bl = balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim, shares);
+  const size_t need = !check_workspace ? 0
+                      : bal          ? bl.total()
+                                     : workspace_bytes_for(num_seqs, num_heads, head_dim, nparts);
   if (need > 0 && num_seqs > 0) {
     if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
     if (workspace_bytes < need)
@@ -234,6 +292,14 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   p.ws_acc = need ? reinterpret_cast<float*>(ws) : nullptr;
   p.ws_m = need ? reinterpret_cast<float*>(ws + acc_bytes) : nullptr;
   p.ws_l = need ? reinterpret_cast<float*>(ws + acc_bytes + ml_bytes) : nullptr;
+  p.bal_shares = shares;
+  p.ws_unit = nullptr;
+  if (bal && need) {
+    p.ws_acc = reinterpret_cast<float*>(ws);
+    p.ws_m = reinterpret_cast<float*>(ws + bl.acc);
+    p.ws_l = reinterpret_cast<float*>(ws + bl.acc + bl.ml);
+    p.ws_unit = reinterpret_cast<int32_t*>(ws + bl.acc + 2 * bl.ml);
+  }
   p.k_new = step ? k_new : nullptr;
   p.v_new = step ? v_new : nullptr;
   p.group_start = nullptr;  // plain decode; the cascade entry point sets these
@@ -267,7 +333,7 @@ pkv_status launch_partitions(const DecodeSetup& st, hipStream_t stream) {
 }
 
 pkv_status launch_reduce(const DecodeSetup& st, hipStream_t stream) {
-  if (st.p.num_parts <= 1) return PKV_OK;
+  if (st.p.num_parts <= 1 && st.p.bal_shares == 0) return PKV_OK;
   hipError_t e = pkv::launch_decode_reduce(st.p, st.out_bf16, stream);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));
   return PKV_OK;
@@ -556,8 +622,31 @@ size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads,
   const int32_t pt = part_tokens_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
                                      partition_tokens);
   if (pt == 0) return 0;
-  return workspace_bytes_for(num_seqs, num_heads, head_dim,
-                             num_parts_for(block_size, max_blocks_per_seq, pt));
+  const size_t fixed = workspace_bytes_for(num_seqs, num_heads, head_dim,
+                                           num_parts_for(block_size, max_blocks_per_seq, pt));
+  // the cache kind is not an argument: enough for fixed partitions (fp32
+  // caches) and for balanced shares (the other kinds)
+  if (!balanced_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, partition_tokens,
+                    pkv::KvKind::BF16))
+    return fixed;
+  return std::max(fixed, balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim, max_shares()).total());
+}
+
+int32_t pkv_paged_attention_shares(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int32_t partition_tokens, pkv_dtype kv_dtype) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || !block_size_ok(block_size) || max_blocks_per_seq <= 0)
+    return 0;
+  pkv::KvKind kv;
+  switch (kv_dtype) {
+    case PKV_BF16: kv = pkv::KvKind::BF16; break;
+    case PKV_I8: kv = pkv::KvKind::I8; break;
+    case PKV_FP8: kv = pkv::KvKind::FP8; break;
+    case PKV_FP8_E5M2: kv = pkv::KvKind::E5M2; break;
+    case PKV_I4: kv = pkv::KvKind::I4; break;
+    default: return 0;
+  }
+  return balanced_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, partition_tokens, kv) ? shares_for(kv)
+                                                                                                     : 0;
 }
 
 #define PKV_DECODE_ARGS                                                                       \
@@ -575,7 +664,7 @@ size_t pkv_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads,
 
 pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
   DecodeSetup st;
-  pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st);
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st, true, true);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
   s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
@@ -589,7 +678,7 @@ pkv_status pkv_paged_attention_decode(PKV_DECODE_PARAMS) {
 
 pkv_status pkv_paged_attention_decode_partitions(PKV_DECODE_PARAMS) {
   DecodeSetup st;
-  pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st);
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st, true, true);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
   s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
@@ -601,7 +690,7 @@ pkv_status pkv_paged_attention_decode_partitions(PKV_DECODE_PARAMS) {
 
 pkv_status pkv_paged_attention_decode_reduce(PKV_DECODE_PARAMS) {
   DecodeSetup st;
-  pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st);
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, nullptr, nullptr, false, &st, true, true);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
   s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
@@ -621,7 +710,7 @@ pkv_status pkv_paged_attention_decode_reduce(PKV_DECODE_PARAMS) {
 
 pkv_status pkv_paged_attention_decode_step(PKV_STEP_PARAMS) {
   DecodeSetup st;
-  pkv_status s = validate_decode(PKV_DECODE_ARGS, k_new, v_new, true, &st);
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, k_new, v_new, true, &st, true, true);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
   s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
@@ -635,7 +724,7 @@ pkv_status pkv_paged_attention_decode_step(PKV_STEP_PARAMS) {
 
 pkv_status pkv_paged_attention_decode_step_partitions(PKV_STEP_PARAMS) {
   DecodeSetup st;
-  pkv_status s = validate_decode(PKV_DECODE_ARGS, k_new, v_new, true, &st);
+  pkv_status s = validate_decode(PKV_DECODE_ARGS, k_new, v_new, true, &st, true, true);
   if (s != PKV_OK) return s;
   if (num_seqs == 0) return ok();
   s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);

@@ -61,6 +61,18 @@ struct DecodeParams {
   int32_t max_blocks_per_seq;
   int32_t part_tokens;
   int32_t num_parts;
+  // Balanced shares (plain decode and the fused step with the automatic
+  // choice, when contexts span several partitions), or 0.  The partition
+  // kernel's grid is bal_shares workgroups; each takes an equal contiguous
+  // share of all (sequence, kv-head) units' 32-token chunks.  Partials of
+  // split units go to share slots instead of per-partition slots:
+  //   ws_acc [2 * bal_shares][G][D], ws_m / ws_l [2 * bal_shares][G]
+  //   ws_unit [B * Hkv][2]: first slot of unit b * Hkv + kvh, and its
+  //                          number of splits (1: written whole)
+  // where split j >= 1 of a unit whose first slot is f lives in slot
+  // 2 * (f / 2 + j).
+  int32_t bal_shares;
+  int32_t* ws_unit;
 };
 
 struct WriteParams {
@@ -143,6 +155,9 @@ __device__ __forceinline__ int group_of(const DecodeParams& p, int b) {
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s);
+// Workgroups of the partition kernel one CU holds at once for cache kind kv
+// (its waves per SIMD: 4-wave workgroups on 4 SIMDs).
+int balanced_slots_per_cu(KvKind kv);
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, hipStream_t s);
 hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group_size, hipStream_t s);
