@@ -423,6 +423,35 @@ size_t pkv_paged_attention_multi_query_workspace_size(
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
     int32_t partition_tokens);
 
+/*
+ * pkv_paged_attention_decode without a workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It calls no allocating routine.
+ *   Arguments, result and errors as pkv_paged_attention_decode with
+ *   partition_tokens 0 (the automatic choice); the split-context partials
+ *   go to a scratch array inside the library instead of a workspace:
+ *   PKV_NOALLOC_SCRATCH_BYTES of device memory per GPU, held from the
+ *   library's loading until the process ends.  Sizes whose partials need
+ *   more (pkv_paged_attention_workspace_size bounds them; with balanced
+ *   shares they do not grow with context length) return PKV_ERR_WORKSPACE
+ *   and launch nothing.
+ *   Every call on one GPU uses that GPU's one scratch array, and it keeps
+ *   the last call's contents: calls that overlap on one GPU (on different
+ *   streams, or from several threads without ordering) race and give wrong
+ *   results; calls ordered on one stream are safe.  Nothing in the scratch
+ *   needs to start at zero.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache,
+                                              const void* v_cache, const float* k_scale,
+                                              const float* v_scale, const int32_t* block_tables,
+                                              const int32_t* context_lens, float scale,
+                                              int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              int32_t block_size, int32_t max_blocks_per_seq,
+                                              int64_t num_blocks, pkv_dtype q_dtype,
+                                              pkv_dtype kv_dtype, void* stream);
+
 /* Text of the last failure on this thread ("" after a successful call).
  * The pointer stays valid until the next call on the same thread. */
 const char* pkv_last_error(void);

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     kv_cache_write_int4,
     cascade_workspace_size,
     paged_attention_decode,
+    paged_attention_decode_noalloc,
     paged_attention_decode_cascade,
     paged_attention_multi_query,
     multi_query_workspace_size,

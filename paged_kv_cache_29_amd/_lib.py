@@ -57,6 +57,7 @@ SIGNATURES = {
     "pkv_paged_attention_shares": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_attention_decode": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_partitions": (c_i32, _DECODE_ARGS),
+    "pkv_paged_attention_decode_noalloc": (c_i32, _DECODE_ARGS[:18] + [c_vp]),
     "pkv_paged_attention_decode_reduce": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_step": (c_i32, _DECODE_ARGS[:2] + [c_vp, c_vp] + _DECODE_ARGS[2:]),
     "pkv_paged_attention_decode_step_partitions": (c_i32, _DECODE_ARGS[:2] + [c_vp, c_vp] + _DECODE_ARGS[2:]),
@@ -408,6 +409,19 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
                            num_heads, num_kv_heads, head_dim, block_size, k_scale, v_scale,
                            partition_tokens, workspace)
     _check(load().pkv_paged_attention_decode(*args), "paged_attention_decode")
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   num_heads, num_kv_heads, head_dim, block_size, k_scale=None,
+                                   v_scale=None):
+    """paged_attention_decode without a workspace: the split-context
+    partials go to the library's own per-GPU scratch (automatic partitions;
+    calls that overlap on one GPU race)."""
+    args = _marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, num_heads,
+                           num_kv_heads, head_dim, block_size, k_scale, v_scale, 0,
+                           workspace=_NO_WORKSPACE)
+    _check(load().pkv_paged_attention_decode_noalloc(*args[:18], args[21]),
+           "paged_attention_decode_noalloc")
 
 
 def paged_attention_decode_partitions(*args, **kwargs):

@@ -90,6 +90,35 @@ hipError_t side_stream(SideStream** out) {
   return hipSuccess;
 }
 
+// Scratch of pkv_paged_attention_decode_noalloc: the split-context
+// partials of a decode call, in device memory the library never allocates.
+// One copy per GPU, loaded with the library's code and held until the
+// process ends.  Host code reaches it only through the device address
+// hipGetSymbolAddress returns for the current device (the array's name on
+// the host is a stand-in, not a device address); the address is looked up
+// once per device, on that device's first call, and kept.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];
+
+// The current device's scratch address.
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
 using pkv::kChunk;          // tokens per wave iteration
 using pkv::kMaxPartBlocks;  // block ids of one partition staged in LDS
 
@@ -193,6 +222,7 @@ struct DecodeSetup {
   pkv::DecodeParams p;
   pkv::KvKind kv;
   bool out_bf16;
+  size_t need;  // workspace bytes this call uses (plain decode / step layout)
 };
 
 pkv_status validate_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -269,6 +299,7 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   const size_t need = !check_workspace ? 0
                       : bal          ? bl.total()
                                      : workspace_bytes_for(num_seqs, num_heads, head_dim, nparts);
+  st->need = bal ? bl.total() : workspace_bytes_for(num_seqs, num_heads, head_dim, nparts);
   if (need > 0 && num_seqs > 0) {
     if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
     if (workspace_bytes < need)
@@ -978,6 +1009,46 @@ pkv_status pkv_paged_attention_multi_query(
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "multi-query kernel launch failed: %s", hipGetErrorString(e));
   e = pkv::launch_decode_reduce(p, st.out_bf16, strm);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                              const float* k_scale, const float* v_scale,
+                                              const int32_t* block_tables, const int32_t* context_lens,
+                                              float scale, int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int32_t max_blocks_per_seq, int64_t num_blocks, pkv_dtype q_dtype,
+                                              pkv_dtype kv_dtype, void* stream) {
+  // the plain checks, then the partials' size against the scratch
+  DecodeSetup st;
+  pkv_status s = validate_decode(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale,
+                                 num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                 num_blocks, q_dtype, kv_dtype, 0, nullptr, 0, nullptr, nullptr, false, &st,
+                                 /*check_workspace=*/false, /*allow_balanced=*/true);
+  if (s != PKV_OK) return s;
+  if (num_seqs == 0) return ok();
+  if (st.need > PKV_NOALLOC_SCRATCH_BYTES)
+    return fail(PKV_ERR_WORKSPACE,
+                "decode_noalloc: these sizes need %zu bytes of partials, more than its %zu-byte scratch "
+                "(use pkv_paged_attention_decode with a workspace)",
+                st.need, static_cast<size_t>(PKV_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (st.need > 0) {
+    const hipError_t e = noalloc_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(PKV_ERR_HIP, "decode_noalloc: scratch address lookup failed: %s", hipGetErrorString(e));
+  }
+  s = validate_decode(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale, num_seqs,
+                      num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, q_dtype,
+                      kv_dtype, 0, ws, ws ? PKV_NOALLOC_SCRATCH_BYTES : 0, nullptr, nullptr, false, &st,
+                      /*check_workspace=*/true, /*allow_balanced=*/true);
+  if (s != PKV_OK) return s;
+  s = debug_tables(block_tables, context_lens, num_seqs, max_blocks_per_seq, block_size, num_blocks, stream);
+  if (s != PKV_OK) return s;
+  s = launch_partitions(st, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
+  s = launch_reduce(st, static_cast<hipStream_t>(stream));
+  if (s != PKV_OK) return s;
   return ok();
 }
 
