@@ -12,21 +12,26 @@ quantising write, then paged_attention_decode's two kernels), reported under
 
 Prints ONE JSON line.  ``value`` is the KV bytes a step must read divided by
 the measured step time (GB/s) on the 7B-shaped MHA workload (batch 32,
-2048-token contexts, 32 heads x 128 dims, bf16, 16-token blocks).  The
-70B-shaped GQA workloads (bf16, int8, FP8 and INT4 KV) and the shared-prefix
-workload (with its cascade-decode leg) are reported under
-``secondary``.  Per-kernel times come from HIP events recorded on the
-stream the kernels run on: each kernel is also run alone, back to back, and
-its average duration is the roofline's time.
+2048-token contexts, 32 heads x 128 dims, bf16, 16-token blocks).  Every
+other workload is reported under ``secondary``, one entry each: the
+70B-shaped GQA workloads (bf16; int8, FP8 E4M3, FP8 E5M2 and INT4 KV), the
+shared-prefix workload at block size 16 and at 32 (with its cascade-decode
+leg), and the tiny fp32 workload (microseconds only).  Per-kernel times come
+from HIP events recorded on the stream the kernels run on: each kernel is
+also run alone, back to back, and its average duration is the roofline's
+time.  Every workload carries ``cpu_baseline``: the oracle on the host's
+cores over a bounded sample of the same workload.
 
 Before each workload's warm-up steps the step also runs, untimed, for
 --settle-seconds (0.3 s): the GPU's clocks drop while the host builds a
 workload, and the first timed loop would otherwise measure their ramp.
 
 Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1),
---configs (which workloads), --partition-tokens, --cpu-seconds (bound of the
-CPU oracle baseline; 0 disables it), --copy-calibration (only run a 1 GiB
-device copy, for scaling rocprofv3 byte counters).
+--configs (which workloads: ids, with @bs for the shared-prefix workload's
+block size), --partition-tokens, --cpu-seconds / --cpu-seconds-secondary
+(bound of the CPU oracle baseline of the headline / of each other workload;
+0 disables it), --copy-calibration (only run a 1 GiB device copy, for
+scaling rocprofv3 byte counters).
 """
 
 import argparse
@@ -45,6 +50,7 @@ KERNEL_SOURCES = ["decode_mfma.hip", "decode_tile.hpp", "decode_append.hpp", "pk
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.txt")
 CODED = ("i8", "fp8", "e5m2", "i4")  # caches of codes with per-(token, kv-head) scales
 CODE_BYTES = {"i8": 1.0, "fp8": 1.0, "e5m2": 1.0, "i4": 0.5, "bf16": 2.0, "f32": 4.0}  # per element
+DEFAULT_CONFIGS = "2,3,5,6,7,8,4@16,4@32,1"
 
 DESCRIPTIONS = {
     1: "tiny_f32: B=4 L={47,200,16,1} H=Hkv=4 D=64 bs=16 fp32",
@@ -84,6 +90,12 @@ def kv_bytes(w):
     elem = CODE_BYTES[w.kv_dtype]
     scale = 4 if w.kv_dtype in CODED else 0
     return int(2 * w.num_kv_heads * (w.head_dim * elem + scale) * w.attended_tokens)
+
+
+def torch_kv_dtype(torch, kind):
+    """The torch element type of a cache of kind ``kind``."""
+    return {"bf16": torch.bfloat16, "i8": torch.int8, "fp8": torch.float8_e4m3fn,
+            "e5m2": torch.float8_e5m2, "i4": torch.uint8, "f32": torch.float32}[kind]
 
 
 def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
@@ -226,11 +238,32 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
         "partition_tokens": pkv.partition_tokens(w.num_seqs, w.num_kv_heads, w.block_size,
                                                  w.block_tables.shape[1], pt),
     }
-    achieved = nbytes / (part_avg * 1e-6) / 1e9
-    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+    # Roofline of the step's dominant kernel, the partition kernel of the
+    # fused step, timed alone (back-to-back launches).  Its algorithmic
+    # bytes are the KV bytes a step must read; with shared blocks (the
+    # prefix workload) those are the distinct tiles, which is all HBM has
+    # to deliver; the logical bytes are reported beside it.
+    shared = bool(w.meta.get("prefix"))
+    alg = uniq if shared else nbytes
+    achieved = alg / (part_avg * 1e-6) / 1e9
+    res["roofline"] = {"bound": "latency" if w.kv_dtype == "f32" else "hbm",
+                       "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": achieved / HBM_PEAK_GBS, "traffic": read_traffic(w.name),
                        "kernel": "decode_mfma_kernel (fused step: append + attend)"
-                       if w.kv_dtype != "f32" else "decode_f32_kernel (fused step)"}
+                       if w.kv_dtype != "f32" else "decode_f32_kernel (fused step)",
+                       "basis": ("unique tile bytes" if shared else "KV bytes")
+                       + " / partition-kernel time (the kernel alone, back-to-back launches)",
+                       "step_frac": alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if shared:
+        res["roofline"]["logical_gbs"] = nbytes / (part_avg * 1e-6) / 1e9
+        res["pct_hbm_peak"] = 100.0 * uniq / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+        res["pct_hbm_peak_basis"] = "unique tile bytes"
+    if w.kv_dtype == "f32":
+        res["roofline"]["note"] = ("the whole workload (540 KB of KV) stays in the caches: the step "
+                                   "is bound by launch and dependent-load latency, so only us/step counts")
+    res["shares"] = pkv.balanced_shares(w.num_seqs, w.num_kv_heads, w.block_size,
+                                        w.block_tables.shape[1], torch_kv_dtype(torch, w.kv_dtype), pt) \
+        if w.kv_dtype != "f32" else 0
     if w.name == "gqa70b_bf16":
         res["speculative_verify"] = run_multi_query(w, args, torch, pkv, loop_time, q, kc, vc, bt, cl,
                                                     nbytes, ms_per_step)
@@ -333,8 +366,10 @@ def run_cascade(w, args, torch, pkv, loop_time, write, out, q, kc, vc, bt, cl, k
 
     us = loop_time(step)
     us_attn = loop_time(cascade)
-    return {"us_per_step": us, "kv_gbs": nbytes / (us * 1e-6) / 1e9,
-            "unique_gbs": uniq / (us * 1e-6) / 1e9, "attention_us": us_attn,
+    return {"us_per_step": us, "logical_kv_gbs": nbytes / (us * 1e-6) / 1e9,
+            "unique_gbs": uniq / (us * 1e-6) / 1e9,
+            "frac_hbm_unique": uniq / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "attention_us": us_attn,
             "speedup_vs_fused_step": ms_fused * 1e3 / us,
             "groups": int(len(gsb)), "max_group_size": int(mg), "shared_blocks": int(msb)}
 
@@ -427,40 +462,74 @@ def block_moves(torch, pkv, steps=10):
     return res
 
 
-def cpu_baseline(w, seconds):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(w, seconds, with_writes=False):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole sequences (all heads), in order, repeated until `seconds` of
+    oracle decode time have passed.  For a coded cache the oracle first
+    quantises each sampled sequence's tokens into its own cache (untimed:
+    that is the cache write's oracle, not decode's)."""
     import numpy as np
     sys.path.insert(0, ROOT)
     import oracle
     from oracle import cache as ocache
+    from oracle import fp8 as ofp8
+    from oracle import int4 as oint4
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    kc, vc = ocache.cache_write(w.k_new, w.v_new, w.k_cache, w.v_cache, w.slot_new, w.block_size)
-    # whole sequences (all heads), in order, repeating the workload until
-    # `seconds` have passed
+    bs = w.block_size
+    ks = vs = None
+    if w.kv_dtype in CODED:
+        NB, Hkv, D = w.num_blocks, w.num_kv_heads, w.head_dim
+        Dw = D // 2 if w.kv_dtype == "i4" else D
+        code_t = np.int8 if w.kv_dtype == "i8" else np.uint8
+        kc = np.zeros((NB, Hkv, bs, Dw), code_t)   # untouched pages stay unallocated
+        vc = np.zeros((NB, Hkv, Dw, bs), code_t)
+        ks = np.full((NB, Hkv, bs), np.nan, np.float32)
+        vs = np.full((NB, Hkv, bs), np.nan, np.float32)
+        write = {"i8": ocache.cache_write_int8, "fp8": ofp8.cache_write_fp8,
+                 "e5m2": ofp8.cache_write_fp8_e5m2, "i4": oint4.cache_write_int4}[w.kv_dtype]
+        per_seq = w.meta.get("fill_per_sequence", True)
+        starts = np.concatenate([[0], np.cumsum(np.maximum(w.context_lens.astype(np.int64) - 1, 0))])
+        ready = set()
+    else:
+        kc, vc = ocache.cache_write(w.k_new, w.v_new, w.k_cache, w.v_cache, w.slot_new, bs)
     done_tokens = 0
     done_seqs = 0
-    t_start = time.perf_counter()
-    while time.perf_counter() - t_start < seconds:
+    timed = 0.0
+    t_wall = time.perf_counter()
+    while timed < seconds and time.perf_counter() - t_wall < 4 * seconds + 30:
         b = done_seqs % w.num_seqs
+        if w.kv_dtype in CODED and b not in ready:
+            if per_seq:
+                a, e = int(starts[b]), int(starts[b + 1])
+                kc, vc, ks, vs = write(w.k_fill[a:e], w.v_fill[a:e], kc, vc, ks, vs, w.slot_fill[a:e], bs)
+            elif not ready:
+                kc, vc, ks, vs = write(w.k_fill, w.v_fill, kc, vc, ks, vs, w.slot_fill, bs)
+            kc, vc, ks, vs = write(w.k_new[b:b + 1], w.v_new[b:b + 1], kc, vc, ks, vs, w.slot_new[b:b + 1], bs)
+            ready.add(b)
+        t0 = time.perf_counter()
         oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, w.num_heads,
                                 w.num_kv_heads, w.head_dim, w.block_size, w.kv_dtype, w.q_dtype,
-                                samples=[(b, h) for h in range(w.num_heads)])
+                                k_scale=ks, v_scale=vs, samples=[(b, h) for h in range(w.num_heads)])
+        timed += time.perf_counter() - t0
         done_tokens += int(w.context_lens[b])
         done_seqs += 1
-    el = time.perf_counter() - t_start
-    elem = 4 if w.kv_dtype == "f32" else 2
-    nbytes = 2 * w.num_kv_heads * w.head_dim * elem * done_tokens
-    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done_seqs} sequence passes ({done_seqs / w.num_seqs:.1f} x all {w.num_seqs} "
-                    f"sequences) x all {w.num_heads} heads ({done_tokens} context tokens) of "
-                    f"{w.name}, {el:.1f} s; "
-                    f"cpu_count={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}, "
-                    f"blas_threads={threads}",
-            "cache_writes": cpu_cache_writes(w)}
+    per_tok = 2 * w.num_kv_heads * (w.head_dim * CODE_BYTES[w.kv_dtype] + (4 if w.kv_dtype in CODED else 0))
+    nbytes = per_tok * done_tokens
+    res = {"value": nbytes / timed / 1e9 if timed > 0 else None, "unit": "GB/s", "cores": int(threads),
+           "kind": "oracle",
+           "us_per_step_equiv": timed / max(done_tokens, 1) * w.attended_tokens * 1e6,
+           "sample": f"{done_seqs} sequence passes ({done_seqs / w.num_seqs:.2f} x all {w.num_seqs} "
+                     f"sequences) x all {w.num_heads} heads ({done_tokens} context tokens) of "
+                     f"{w.name}, {timed:.1f} s of oracle decode; "
+                     f"cpu_count={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}, "
+                     f"blas_threads={threads}"}
+    if with_writes:
+        res["cache_writes"] = cpu_cache_writes(w)
+    return res
 
 
 def cpu_cache_writes(w, tokens=4096, blocks=512):
@@ -507,15 +576,30 @@ def copy_calibration(torch):
                       "copy_calibration_bytes_written_per_dispatch": n}))
 
 
+def parse_configs(spec):
+    """'2,3,4@32' -> [(2, None), (3, None), (4, 32)]: workload ids, with the
+    shared-prefix workload's block size after '@'."""
+    out = []
+    for item in spec.split(","):
+        item = item.strip()
+        if not item:
+            continue
+        cfg, _, bs = item.partition("@")
+        out.append((int(cfg), int(bs) if bs else (16 if int(cfg) == 4 else None)))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--configs", default="2,3,5,6,7,4", help="first is the headline workload")
-    ap.add_argument("--block-size", type=int, default=16, help="for config 4 (16 or 32)")
+    ap.add_argument("--configs", default=DEFAULT_CONFIGS,
+                    help="workload ids, the first is the headline; 4@32 = the shared-prefix workload at bs 32")
     ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time on the headline workload")
+    ap.add_argument("--cpu-seconds-secondary", type=float, default=4.0,
+                    help="oracle time on each other workload")
     ap.add_argument("--settle-seconds", type=float, default=0.3,
                     help="untimed steps before each workload's first warm-up, so clocks have settled")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -538,15 +622,27 @@ def main():
     import paged_kv_cache_29_amd as pkv
     from paged_kv_cache_29_amd import workloads
     pkv.load_library()
-    cfgs = [int(c) for c in args.configs.split(",") if c]
     results = []
-    for c in cfgs:
-        print(f"[bench] config {c} ...", file=sys.stderr, flush=True)
-        r = run_workload(c, args, torch, pkv, workloads, args.block_size if c == 4 else None)
-        print(f"[bench] config {c}: {r['us_per_step']:.1f} us/step, {r['kv_gbs']:.0f} GB/s",
+    for i, (c, bs) in enumerate(parse_configs(args.configs)):
+        tag = f"{c}" + (f"@{bs}" if c == 4 else "")
+        print(f"[bench] config {tag} ...", file=sys.stderr, flush=True)
+        r = run_workload(c, args, torch, pkv, workloads, bs if c == 4 else None)
+        r["config_id"] = tag
+        print(f"[bench] config {tag}: {r['us_per_step']:.1f} us/step, {r['kv_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
-        results.append(r)
         torch.cuda.empty_cache()
+        secs = args.cpu_seconds if i == 0 else args.cpu_seconds_secondary
+        w = r.pop("_w")
+        if secs > 0:
+            print(f"[bench] config {tag}: cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+            r["cpu_baseline"] = cpu_baseline(w, secs, with_writes=(i == 0))
+        else:
+            r["cpu_baseline"] = None
+        r["_shape"] = {"num_seqs": w.num_seqs, "context_len": int(w.context_lens.max()),
+                       "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                       "block_size": w.block_size, "kv_dtype": w.kv_dtype}
+        del w
+        results.append(r)
     print("[bench] read ceiling probe ...", file=sys.stderr, flush=True)
     ceiling = read_ceiling(torch, pkv)
     print("[bench] block moves ...", file=sys.stderr, flush=True)
@@ -554,9 +650,9 @@ def main():
     for r in results:
         r["roofline"]["frac_of_read_ceiling"] = r["roofline"]["achieved"] / ceiling["gbs"]
     head = results[0]
-    w = head.pop("_w")
+    shp = head.pop("_shape")
     for r in results[1:]:
-        r.pop("_w")
+        r.pop("_shape")
     line = {
         "metric": METRIC,
         "value": round(head["kv_gbs"], 2),
@@ -569,12 +665,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"bf16": "bf16", "i8": "i8", "fp8": "fp8_e4m3", "e5m2": "fp8_e5m2", "i4": "i4",
-                  "f32": "f32"}[w.kv_dtype],
+                  "f32": "f32"}[shp["kv_dtype"]],
         "data": "synthetic (seeded N(0,1) K/V/q, shuffled block tables)",
-        "config": {"workload": head["workload"], "num_seqs": w.num_seqs,
-                   "context_len": int(w.context_lens.max()), "num_heads": w.num_heads,
-                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-                   "block_size": w.block_size, "partition_tokens": head["partition_tokens"]},
+        "config": {"workload": head["workload"], "num_seqs": shp["num_seqs"],
+                   "context_len": shp["context_len"], "num_heads": shp["num_heads"],
+                   "num_kv_heads": shp["num_kv_heads"], "head_dim": shp["head_dim"],
+                   "block_size": shp["block_size"], "partition_tokens": head["partition_tokens"]},
         "us_per_step": head["us_per_step"],
         "pct_hbm_peak": head["pct_hbm_peak"],
         "tokens_per_s": head["tokens_per_s"],
@@ -584,18 +680,12 @@ def main():
         "bulk_fill": head.get("bulk_fill"),
         "roofline": head["roofline"],
         "us_per_step_events": head["us_per_step_events"],
-        "cascade": head.get("cascade"),
-        "speculative_verify": head.get("speculative_verify"),
         "read_ceiling": ceiling,
         "block_moves": moves,
         "kernel_source_sha": kernel_source_sha(),
-        "secondary": [{k: v for k, v in r.items()} for r in results[1:]],
+        "cpu_baseline": head["cpu_baseline"],
+        "secondary": results[1:],
     }
-    if args.cpu_seconds > 0 and w.kv_dtype not in CODED:
-        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    else:
-        line["cpu_baseline"] = None
     print(json.dumps(line))
     return 0
 
