@@ -123,7 +123,7 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
               "i4": torch.uint8}.get(w.kv_dtype, torch.int8)
         Dw = D // 2 if w.kv_dtype == "i4" else D   # INT4: two dims per byte
         kc = torch.zeros((NB, Hkv, bs, Dw), dtype=torch.uint8, device=dev).view(cd)
-        vc = torch.zeros((NB, Hkv, Dw, bs), dtype=torch.uint8, device=dev).view(cd)
+        vc = torch.zeros((NB, Hkv, bs // 4, Dw, 4), dtype=torch.uint8, device=dev).view(cd)
         ks = torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=dev)
         vs = torch.zeros((NB, Hkv, bs), dtype=torch.float32, device=dev)
         kf, vf, sf = up(w.k_fill, "f32"), up(w.v_fill, "f32"), torch.from_numpy(w.slot_fill).to(dev)
@@ -426,9 +426,9 @@ def block_moves(torch, pkv, steps=10):
     dev = torch.device("cuda:0")
     Hkv, bs, D, NB, NH, n = 8, 16, 128, 12288, 4096, 4096
     kc = torch.empty((NB, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
-    vc = torch.empty((NB, Hkv, D, bs), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty((NB, Hkv, bs // 4, D, 4), dtype=torch.bfloat16, device=dev)
     hk = torch.empty((NH, Hkv, bs, D), dtype=torch.bfloat16).pin_memory()
-    hv = torch.empty((NH, Hkv, D, bs), dtype=torch.bfloat16).pin_memory()
+    hv = torch.empty((NH, Hkv, bs // 4, D, 4), dtype=torch.bfloat16).pin_memory()
     rng = np.random.default_rng(0)
     perm = rng.permutation(NB)
     cow = torch.from_numpy(np.stack([perm[:n], perm[n:2 * n]], 1).astype(np.int32)).to(dev)
@@ -486,7 +486,7 @@ def cpu_baseline(w, seconds, with_writes=False):
         Dw = D // 2 if w.kv_dtype == "i4" else D
         code_t = np.int8 if w.kv_dtype == "i8" else np.uint8
         kc = np.zeros((NB, Hkv, bs, Dw), code_t)   # untouched pages stay unallocated
-        vc = np.zeros((NB, Hkv, Dw, bs), code_t)
+        vc = np.zeros((NB, Hkv, bs // 4, Dw, 4), code_t)
         ks = np.full((NB, Hkv, bs), np.nan, np.float32)
         vs = np.full((NB, Hkv, bs), np.nan, np.float32)
         write = {"i8": ocache.cache_write_int8, "fp8": ofp8.cache_write_fp8,
@@ -547,12 +547,12 @@ def cpu_cache_writes(w, tokens=4096, blocks=512):
     kb = (k.view(np.uint32) >> 16).astype(np.uint16)   # bf16 bit patterns (truncated: any
     vb = (v.view(np.uint32) >> 16).astype(np.uint16)   # pattern times the same)
     kc = np.zeros((blocks, Hkv, bs, D), np.uint16)
-    vc = np.zeros((blocks, Hkv, D, bs), np.uint16)
+    vc = np.zeros((blocks, Hkv, bs // 4, D, 4), np.uint16)
     t0 = time.perf_counter()
     ocache.cache_write(kb, vb, kc, vc, slots, bs)
     t_bf16 = time.perf_counter() - t0
     kc8 = np.zeros((blocks, Hkv, bs, D), np.int8)
-    vc8 = np.zeros((blocks, Hkv, D, bs), np.int8)
+    vc8 = np.zeros((blocks, Hkv, bs // 4, D, 4), np.int8)
     sc = np.zeros((blocks, Hkv, bs), np.float32)
     t0 = time.perf_counter()
     ocache.cache_write_int8(k, v, kc8, vc8, sc, sc.copy(), slots, bs)

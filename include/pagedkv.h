@@ -36,15 +36,18 @@
  * Hkv = num_kv_heads, bs = block_size, D = head_dim, H = num_heads,
  * G = H / Hkv, B = num_seqs, MB = max_blocks_per_seq, T = num_tokens.
  *   k_cache      [NB][Hkv][bs][D]   one row of D elements per token
- *   v_cache      [NB][Hkv][D][bs]   each (block, kv-head) tile dim-major:
- *                                   element (token row r, dim d) at d*bs + r
+ *   v_cache      [NB][Hkv][bs/4][D][4]  each (block, kv-head) tile in groups
+ *                                   of 4 consecutive tokens, dim-major inside
+ *                                   a group: element (token row r, dim d) at
+ *                                   ((r / 4) * D + d) * 4 + r % 4
  *   k_scale,
  *   v_scale      [NB][Hkv][bs] fp32 (int8, FP8 and INT4 caches only)
  *   FP8 caches hold E4M3 codes (PKV_FP8) or E5M2 codes (PKV_FP8_E5M2).
  *   INT4 caches hold two codes per byte, two consecutive head dims of one
  *   token (dim 2j in the low nibble, 2j + 1 in the high nibble, 4-bit two's
  *   complement), so their tiles are k_cache [NB][Hkv][bs][D/2] and
- *   v_cache [NB][Hkv][D/2][bs] (byte (j, r): dims 2j, 2j + 1 of token r).
+ *   v_cache [NB][Hkv][bs/4][D/2][4] (byte ((r / 4) * D/2 + j) * 4 + r % 4:
+ *   dims 2j, 2j + 1 of token r).
  *   block_tables [B][MB] int32      logical block j of sequence b lives in
  *                                   physical block block_tables[b*MB + j];
  *                                   entries past the sequence's last block
@@ -98,9 +101,10 @@ typedef enum {
 /*
  * Slot-scatter cache write ([ENG5] "Block manager: how paging works": a new
  * token goes to the next slot of its sequence's tail block).
- *   For every token t with s = slot_mapping[t] >= 0 and every kv-head h:
- *     k_cache[s / bs][h][s % bs][:] = k[t][h][:]
- *     v_cache[s / bs][h][:][s % bs] = v[t][h][:]
+ *   For every token t with s = slot_mapping[t] >= 0, row r = s % bs and
+ *   every kv-head h:
+ *     k_cache[s / bs][h][r][:] = k[t][h][:]
+ *     v_cache[s / bs][h][r / 4][:][r % 4] = v[t][h][:]
  *   The copy is bit-exact.  dtype is PKV_F32 or PKV_BF16 (the element type of
  *   k, v and both caches).  head_dim in {64, 128}; block_size in {16, 32};
  *   num_tokens >= 0 (0: no-op).  Errors: PKV_ERR_INVALID for null pointers
@@ -171,8 +175,9 @@ pkv_status pkv_kv_cache_write_fp8_e5m2(const float* k, const float* v, uint8_t* 
  *     code_d = clamp(rint(x_d / s), -7, 7)  (round half to even);
  *     s == 0 (a == 0, or a / 7 underflows) gives all codes 0.
  *   Codes are packed two per byte into the INT4 tiles (layout above): the
- *   token's K row is k_cache[s_slot / bs][h][s_slot % bs][0 .. D/2-1], its
- *   V codes v_cache[s_slot / bs][h][0 .. D/2-1][s_slot % bs]; scales as for
+ *   token's K row is k_cache[s_slot / bs][h][r][0 .. D/2-1], its V codes
+ *   v_cache[s_slot / bs][h][r / 4][0 .. D/2-1][r % 4] (r = s_slot % bs);
+ *   scales as for
  *   pkv_kv_cache_write_int8.  No byte is shared by two tokens, so any set of
  *   distinct slots may be written in one call.  Inputs must be finite.
  *   Bit-exact.  Errors as for pkv_kv_cache_write_int8.

@@ -19,9 +19,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
 
 * Cache layout (the pages print sizes, not an order): ``k_cache`` is
   ``[num_blocks, num_kv_heads, block_size, head_dim]`` (each token a row) and
-  ``v_cache`` is ``[num_blocks, num_kv_heads, head_dim, block_size]`` (each
-  tile stored dim-major).  The oracle reads both by index, token by token
-  within a block, so its arithmetic does not depend on the layout.
+  ``v_cache`` is ``[num_blocks, num_kv_heads, block_size / 4, head_dim, 4]``
+  (each tile in groups of 4 consecutive tokens, dim-major inside a group:
+  token ``r``, dim ``d`` at ``[r // 4, d, r % 4]``).  The oracle reads both
+  by index, token by token within a block, so its arithmetic does not
+  depend on the layout.
 * GQA grouping: query head ``h`` reads kv-head ``h // (H / Hkv)``.
 * ``context_len == 0`` gives an all-zero output row.
 * int8 cache: the value of a stored code ``c`` with scale ``s`` is ``c * s``
@@ -112,7 +114,7 @@ def gather_kv(k_cache, v_cache, block_table, context_len, block_size, kv_head,
     ``rows_in_block(L, bs, j)`` rows.  Table entries past the last logical
     block are never read.  For an int8, FP8 or INT4 cache each element's
     value is its code's value times its token's scale; INT4 tiles hold two
-    dims per byte (``k_cache[..., D/2]``, ``v_cache[..., D/2, bs]``).
+    dims per byte (``k_cache[..., D/2]``, ``v_cache[..., D/2, 4]``).
     """
     L = int(context_len)
     bs = int(block_size)
@@ -122,12 +124,16 @@ def gather_kv(k_cache, v_cache, block_table, context_len, block_size, kv_head,
     for j in range(n_blocks(L, bs)):
         rows = rows_in_block(L, bs, j)
         blk = int(block_table[j])
+        # V token rows: token r of the tile is [r // 4, :, r % 4]; swapping
+        # the last two axes and merging the first two lists them in order
+        v_tile = np.asarray(v_cache[blk, kv_head])                          # [bs/4, D(/2), 4]
+        v_tok = np.swapaxes(v_tile, 1, 2).reshape(bs, v_tile.shape[1])[:rows]
         if kv_dtype == "i4":
             k_rows = _int4.unpack_int4(k_cache[blk, kv_head, :rows, :], axis=-1).astype(np.float64)
-            v_rows = _int4.unpack_int4(v_cache[blk, kv_head, :, :rows], axis=0).astype(np.float64).T
+            v_rows = _int4.unpack_int4(v_tok, axis=-1).astype(np.float64)
         else:
             k_rows = widen(k_cache[blk, kv_head, :rows, :], kv_dtype)        # [rows, D]
-            v_rows = widen(v_cache[blk, kv_head, :, :rows], kv_dtype).T      # [rows, D]
+            v_rows = widen(v_tok, kv_dtype)                                  # [rows, D]
         if kv_dtype in CODED:
             ks = np.asarray(k_scale[blk, kv_head, :rows], dtype=np.float32).astype(np.float64)
             vs = np.asarray(v_scale[blk, kv_head, :rows], dtype=np.float32).astype(np.float64)
@@ -160,7 +166,7 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
     """fp64 decode attention for a batch of sequences (one query token each).
 
     Shapes: ``q[B, H, D]``; ``k_cache[NB, Hkv, bs, D]``;
-    ``v_cache[NB, Hkv, D, bs]``; ``block_tables[B, MB]``; ``context_lens[B]``;
+    ``v_cache[NB, Hkv, bs/4, D, 4]``; ``block_tables[B, MB]``; ``context_lens[B]``;
     scales ``[NB, Hkv, bs]`` (int8, FP8, INT4; INT4 tiles hold two dims per
     byte).  ``q_dtype`` / ``kv_dtype`` name the stored element types ("f32",
     "bf16", "i8", "fp8" (E4M3), "e5m2", "i4").

@@ -9,7 +9,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   (the block/row model of [ENG5] "Paged attention").  Reading taken: a
   negative slot means "no write" for that token.  Layout as in
   ``attention.py``: K rows at ``k_cache[blk, h, row, :]``, V at
-  ``v_cache[blk, h, :, row]``.  The write is a bit copy.
+  ``v_cache[blk, h, row // 4, :, row % 4]``.  The write is a bit copy.
 
 * int8 quantiser.  Symmetric int8 with one scale per (token, kv-head)
   ([ENG5] "KV-cache quantization": per-token-per-head scales computed online;
@@ -39,7 +39,7 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, block_size):
             continue
         blk, row = s // bs, s % bs
         k_out[blk, :, row, :] = k[t]
-        v_out[blk, :, :, row] = v[t]
+        v_out[blk, :, row // 4, :, row % 4] = v[t]
     return k_out, v_out
 
 
@@ -80,7 +80,7 @@ def cache_write_int8(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping,
             continue
         blk, row = s // bs, s % bs
         k_out[blk, :, row, :] = kq[t]
-        v_out[blk, :, :, row] = vq[t]
+        v_out[blk, :, row // 4, :, row % 4] = vq[t]
         ks_out[blk, :, row] = ks[t]
         vs_out[blk, :, row] = vs[t]
     return k_out, v_out, ks_out, vs_out

@@ -169,7 +169,7 @@ def cache_write_fp8(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, bloc
             continue
         blk, row = s // bs, s % bs
         k_out[blk, :, row, :] = kq[t]
-        v_out[blk, :, :, row] = vq[t]
+        v_out[blk, :, row // 4, :, row % 4] = vq[t]
         ks_out[blk, :, row] = ks[t]
         vs_out[blk, :, row] = vs[t]
     return k_out, v_out, ks_out, vs_out

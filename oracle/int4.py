@@ -19,8 +19,9 @@ Readings taken where the pages are silent:
   consecutive head dims of one token, dim ``2j`` in the low nibble and dim
   ``2j + 1`` in the high nibble.  K tiles are ``[num_blocks, num_kv_heads,
   block_size, head_dim / 2]`` (byte ``j`` of a token's row) and V tiles
-  ``[num_blocks, num_kv_heads, head_dim / 2, block_size]`` (byte ``(j, r)``
-  holds dims ``2j, 2j + 1`` of token ``r``), so no byte mixes two tokens.
+  ``[num_blocks, num_kv_heads, block_size / 4, head_dim / 2, 4]`` (byte
+  ``[r // 4, j, r % 4]`` holds dims ``2j, 2j + 1`` of token ``r``), so no
+  byte mixes two tokens.
 * The outlier retention the pages pair with per-token-per-head scales
   (about 1% of channels kept in high precision) is not part of this format:
   the pages say neither how those channels are chosen nor how they are
@@ -96,7 +97,7 @@ def cache_write_int4(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, blo
             continue
         blk, row = s // bs, s % bs
         k_out[blk, :, row, :] = kp[t]
-        v_out[blk, :, :, row] = vp[t]
+        v_out[blk, :, row // 4, :, row % 4] = vp[t]
         ks_out[blk, :, row] = ks[t]
         vs_out[blk, :, row] = vs[t]
     return k_out, v_out, ks_out, vs_out

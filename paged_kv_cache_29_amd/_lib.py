@@ -26,9 +26,10 @@ _CODED = (PKV_I8, PKV_FP8, PKV_FP8_E5M2, PKV_I4)  # codes with per-(token, kv-he
 
 def _tile_shapes(kd, Hkv, bs, D):
     """Per-block K and V tile shapes of a cache of kind kd: [Hkv, bs, D] and
-    [Hkv, D, bs], or [Hkv, bs, D/2] and [Hkv, D/2, bs] for INT4."""
+    [Hkv, bs/4, D, 4] (V in groups of 4 tokens: token r, dim d at
+    [r // 4, d, r % 4]), or [Hkv, bs, D/2] and [Hkv, bs/4, D/2, 4] for INT4."""
     w = D // 2 if kd == PKV_I4 else D
-    return (Hkv, bs, w), (Hkv, w, bs)
+    return (Hkv, bs, w), (Hkv, bs // 4, w, 4)
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -158,9 +159,9 @@ def kv_cache_write(k, v, k_cache, v_cache, slot_mapping):
     for n, t in (("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache),
                  ("slot_mapping", slot_mapping)):
         _dense_on(t, dev, n)
-    _need(k_cache.dim() == 4 and v_cache.dim() == 4, "caches must be 4-D")
+    _need(k_cache.dim() == 4 and v_cache.dim() == 5, "k_cache must be 4-D and v_cache 5-D")
     NB, Hkv, bs, D = k_cache.shape
-    _need(tuple(v_cache.shape) == (NB, Hkv, D, bs), "v_cache must be [NB, Hkv, D, bs]")
+    _need(tuple(v_cache.shape) == (NB, Hkv, bs // 4, D, 4), "v_cache must be [NB, Hkv, bs/4, D, 4]")
     _need(k.dim() == 3 and tuple(k.shape[1:]) == (Hkv, D) and k.shape == v.shape,
           "k, v must be [T, Hkv, D]")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (k.shape[0],),
@@ -276,7 +277,7 @@ def _marshal_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
     _need(tuple(k_cache.shape) == (NB,) + kt,
           "k_cache must be [NB, Hkv, bs, D] ([NB, Hkv, bs, D/2] for INT4)")
     _need(tuple(v_cache.shape) == (NB,) + vt,
-          "v_cache must be [NB, Hkv, D, bs] ([NB, Hkv, D/2, bs] for INT4)")
+          "v_cache must be [NB, Hkv, bs/4, D, 4] ([NB, Hkv, bs/4, D/2, 4] for INT4)")
     _need(k_cache.dtype == v_cache.dtype, "k_cache and v_cache dtypes differ")
     B = q.shape[0]
     _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and block_tables.shape[0] == B,

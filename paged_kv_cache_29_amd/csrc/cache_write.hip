@@ -3,8 +3,10 @@
 // A new token's K and V go to the slot the block manager assigned it in its
 // sequence's tail block ("LLM Engineering (5)", "Block manager: how paging
 // works"); a slot is physical_block * block_size + row.  K rows are
-// contiguous in the cache; V tiles are dim-major, so a token's V is a column
-// of its tile (stride block_size).  Negative slots are skipped.
+// contiguous in the cache; V tiles hold groups of 4 tokens, dim-major
+// inside a group (element (r, d) at ((r / 4) D + d) 4 + r % 4), so a
+// token's V is every fourth element of its group (D / 16 lines of 128
+// bytes at bf16).  Negative slots are skipped.
 //
 // kv_cache_write copies bits.  kv_cache_write_int8 first quantises each
 // (token, kv-head) row on its own: s = absmax / 127 in IEEE fp32,
@@ -33,9 +35,9 @@ namespace {
 // t0 + i and every fourth 16-byte piece q, q + 4, ... of its row.
 // Consecutive lanes hold consecutive tokens, so when their slots are
 // consecutive rows of one block (a prefill or bulk fill), each V store
-// instruction writes neighbouring elements of a dim row instead of
-// scattering one element per line; the four lanes of a token load and
-// store 64 contiguous bytes of its row at a time.
+// instruction writes the 4 contiguous elements of a token group's dim for
+// every 4 lanes instead of scattering one element per line; the four lanes
+// of a token load and store 64 contiguous bytes of its row at a time.
 constexpr int kTokensPerWave = 16;
 
 // The bit-copy write also has a small-batch form: a decode step writes one
@@ -92,8 +94,9 @@ __global__ __launch_bounds__(WPG * kWave) void cache_write_kernel(WriteParams p)
       const int d0 = (LPT * j + q) * EPV;
       *reinterpret_cast<u32x4*>(kc + tile + static_cast<int64_t>(row) * D + d0) = kk[j];
       const T* ve = reinterpret_cast<const T*>(&vv[j]);
+      T* vg = vc + tile + static_cast<int64_t>(row >> 2) * D * 4 + (row & 3);  // the token's group
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) vc[tile + static_cast<int64_t>(d0 + e) * BS + row] = ve[e];
+      for (int e = 0; e < EPV; ++e) vg[static_cast<int64_t>(d0 + e) * 4] = ve[e];
     }
   }
 }
@@ -170,8 +173,9 @@ __global__ __launch_bounds__(WPG * kWave) void cache_write_codes_kernel(WritePar
           *reinterpret_cast<uint16_t*>(kc + tile + static_cast<int64_t>(row) * (D / 2) + d0 / 2) =
               static_cast<uint16_t>(b0 | (b1 << 8));
         } else {
-          vc[tile + static_cast<int64_t>(d0 / 2) * BS + row] = static_cast<uint8_t>(b0);
-          vc[tile + static_cast<int64_t>(d0 / 2 + 1) * BS + row] = static_cast<uint8_t>(b1);
+          uint8_t* vg = vc + tile + static_cast<int64_t>(row >> 2) * (D / 2) * 4 + (row & 3);
+          vg[static_cast<int64_t>(d0 / 2) * 4] = static_cast<uint8_t>(b0);
+          vg[static_cast<int64_t>(d0 / 2 + 1) * 4] = static_cast<uint8_t>(b1);
         }
       }
       continue;
@@ -191,9 +195,9 @@ __global__ __launch_bounds__(WPG * kWave) void cache_write_codes_kernel(WritePar
                                 ((codes[2] & 0xffu) << 16) | ((codes[3] & 0xffu) << 24);
         *reinterpret_cast<uint32_t*>(kc + tile + static_cast<int64_t>(row) * D + d0) = packed;
       } else {
+        uint8_t* vg = vc + tile + static_cast<int64_t>(row >> 2) * D * 4 + (row & 3);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          vc[tile + static_cast<int64_t>(d0 + e) * BS + row] = static_cast<uint8_t>(codes[e] & 0xffu);
+        for (int e = 0; e < 4; ++e) vg[static_cast<int64_t>(d0 + e) * 4] = static_cast<uint8_t>(codes[e] & 0xffu);
       }
     }
   }

@@ -33,8 +33,10 @@
 // sharing the chunk's K and V operands (and int8 widening) between tiles.
 // LDS layout per stage: K sub-tiles as token rows padded by 16 bytes (the
 // 16 rows a wave reads together fall in distinct banks); V sub-tiles
-// dim-major as in the cache, bf16 rows with their two 8-byte halves of each
-// 16-byte unit swapped on every other group of 8 dims (same purpose).
+// dim-major, one row of 16 tokens per dim (INT4: per dim pair), gathered
+// from the cache's groups of 4 tokens while staging; bf16 rows with their
+// 8-byte token quads 2k and 2k + 1 swapped on every other group of 8 dims
+// (same purpose).
 
 #include "decode_tile.hpp"
 #include "pkv_device.hpp"
@@ -192,16 +194,9 @@ void cascade_prefix_kernel(DecodeParams p) {
     for (int i = 0; i < L::UNITS; ++i) {
       const int u = i * kWave + lane;  // 16-byte unit of the piece
       if (u * 16 >= L::PIECE) break;   // INT4 at D = 64: half the lanes
-      size_t off;
-      if (!pv) {
-        off = static_cast<size_t>(row0[ph]) * L::RB + u * 16;
-      } else if (BS == 16) {
-        off = u * 16;
-      } else if (kInt8) {  // V row u (dim, INT4: dim pair): 16 tokens of a 32-token row
-        off = u * 32 + 16 * ph;
-      } else {  // dim u / 2, half u % 2 of the sub-tile's 32 bytes
-        off = (u >> 1) * 64 + 32 * ph + 16 * (u & 1);
-      }
+      // K: 16 token rows; V: the sub-tile's 4 token groups (row0 is a
+      // multiple of 4): both 16 * RB contiguous bytes from row0 * RB
+      const size_t off = static_cast<size_t>(row0[ph]) * L::RB + u * 16;
       pu[i] = load_u32x4(base + off);
     }
     if (kInt8 && lane < 4) {
@@ -220,9 +215,24 @@ void cascade_prefix_kernel(DecodeParams p) {
         const int col = (u * 16) % L::RB;
         *reinterpret_cast<u32x4*>(dst + ph * L::KSUB + row * L::KROW + col) = pu[i];
       } else {
-        u32x4 w = pu[i];
-        if (!kInt8 && (((u >> 1) >> 3) & 1)) w = u32x4{w.z, w.w, w.x, w.y};
-        *reinterpret_cast<u32x4*>(dst + 2 * L::KSUB + ph * L::VSUB + u * 16) = w;
+        // unit u of the cache's V sub-tile: token group u / (VR / 4) (4 tokens)
+        // of rows 4 (u % (VR / 4)) .. + 3 (byte codes, INT4), or of dims
+        // 2 (u % (D / 2)) and + 1 (bf16); each row's 4 tokens go to that
+        // row of the dim-major stage
+        const u32x4 w = pu[i];
+        char* vt = dst + 2 * L::KSUB + ph * L::VSUB;
+        if constexpr (kInt8) {
+          const int gq = u / (L::VR / 4);
+          const int r = 4 * (u % (L::VR / 4));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(vt + (r + j) * L::VROW + 4 * gq) = w[j];
+        } else {
+          const int gq = u / (D / 2);
+          const int d = 2 * (u % (D / 2));
+          const int slot = 8 * (gq ^ ((d >> 3) & 1));  // d and d + 1 share the 8-dim group
+          *reinterpret_cast<u32x2*>(vt + d * L::VROW + slot) = u32x2{w.x, w.y};
+          *reinterpret_cast<u32x2*>(vt + (d + 1) * L::VROW + slot) = u32x2{w.z, w.w};
+        }
       }
     }
     if (kInt8 && lane < 4)

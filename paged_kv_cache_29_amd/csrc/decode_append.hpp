@@ -50,8 +50,8 @@ __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, i
         const uint8_t byte = static_cast<uint8_t>(pack_int4_pair(quantize_sym<7>(v.x, s), quantize_sym<7>(v.y, s)));
         if (wave == 0)
           kc[tile4 + static_cast<size_t>(row) * (D / 2) + lane] = byte;
-        else
-          vc[tile4 + static_cast<size_t>(lane) * BS + row] = byte;
+        else  // token group row / 4, dim pair lane, token row % 4
+          vc[tile4 + (static_cast<size_t>(row >> 2) * (D / 2) + lane) * 4 + (row & 3)] = byte;
       }
       if (lane == 0) {
         float* sc = const_cast<float*>(wave == 0 ? p.k_scale : p.v_scale);
@@ -83,7 +83,7 @@ __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, i
         if (wave == 0)
           kc[tile + static_cast<size_t>(row) * D + d] = code;
         else
-          vc[tile + static_cast<size_t>(d) * BS + row] = code;
+          vc[tile + (static_cast<size_t>(row >> 2) * D + d) * 4 + (row & 3)] = code;
       }
       if (lane == 0) {
         float* sc = const_cast<float*>(wave == 0 ? p.k_scale : p.v_scale);
@@ -96,8 +96,8 @@ __device__ __forceinline__ void append_new_token(const DecodeParams& p, int b, i
     for (int i = t; i < 2 * D; i += NT) {
       if (i < D)
         kc[tile + static_cast<size_t>(row) * D + i] = kn[i];
-      else
-        vc[tile + static_cast<size_t>(i - D) * BS + row] = vn[i - D];
+      else  // token group row / 4, dim i - D, token row % 4
+        vc[tile + (static_cast<size_t>(row >> 2) * D + (i - D)) * 4 + (row & 3)] = vn[i - D];
     }
   }
 }

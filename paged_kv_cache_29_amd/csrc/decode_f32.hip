@@ -80,7 +80,7 @@ __global__ __launch_bounds__(W * kWave) void decode_f32_kernel(DecodeParams p) {
     for (int k = 0; k < ND; ++k) {
       const int d = lane + kWave * k;
       kk[k] = kc[tile + static_cast<size_t>(r) * D + d];
-      vv[k] = vc[tile + static_cast<size_t>(d) * BS + r];
+      vv[k] = vc[tile + (static_cast<size_t>(r >> 2) * D + d) * 4 + (r & 3)];
     }
 #pragma unroll
     for (int cc = 0; cc < kMaxGroup; ++cc) {

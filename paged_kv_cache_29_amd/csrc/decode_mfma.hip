@@ -29,8 +29,10 @@
 //   online softmax on the 8 scores a lane holds, max across the 4 lane
 //     groups by shuffles.
 //   O^T[D x 16 heads] += V^T[D x 32 tok] . P^T[32 tok x 16 heads]   2 * D/16 MFMAs
-//     A operand: V tiles are stored dim-major (element (r, d) at d*bs + r),
-//     so the 4 tokens a lane needs from each sub-tile are 8 contiguous bytes.
+//     A operand: V tiles are stored in groups of 4 tokens, dim-major inside
+//     a group (element (r, d) at ((r / 4) D + d) 4 + r % 4), so the 4 tokens
+//     a lane needs from each sub-tile are contiguous for every dim, and one
+//     16-byte load gives them for several dims (decode_tile.hpp).
 //     B operand: the lane's own 8 probabilities, split into a bf16 hi/lo
 //     pair (two MFMAs) so the weights keep ~16 bits; no shuffle is needed
 //     because the score layout already matches.
@@ -45,9 +47,8 @@
 // The score accumulator starts at -136 * sum_d q_d, which cancels the offset
 // in K; the offset in V adds 136 * sum_t p_t v_scale_t to every output dim
 // of a head, which each wave subtracts from its accumulator before the
-// waves are merged.  Output tile 2m takes dims 32m + 2r and tile 2m + 1
-// dims 32m + 2r + 1 (r = tile row), so a lane's two tiles hold 8
-// consecutive dims.
+// waves are merged.  Output tile 2m takes the even dims of the dim pairs a
+// lane loaded, tile 2m + 1 the odd ones.
 
 #include <type_traits>
 
@@ -539,37 +540,72 @@ void decode_mfma_kernel(DecodeParams p) {
       const size_t bh = kMQ ? static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G
                             : static_cast<size_t>(b) * H + h0 + c;
       const size_t slot = kBal ? static_cast<size_t>(pslot) * G + c : bh * p.num_parts + pslot;
-      if constexpr (kI4) {  // lane holds dims 32m + 8g .. + 7: tiles 2m (even), 2m + 1 (odd)
-        if (final_out) {
-          uint16_t* orow = out + bh * D;
+      // Output maps: accumulator element i of tile n in lane (c, g) is row
+      // 4g + i of that tile, and the row's dim follows the V operand loads
+      // (decode_tile.hpp); each lane ends up with runs of consecutive dims.
+      uint16_t* orow = out + bh * D;
+      float* arow = p.ws_acc + slot * D;
+      const float ls = Lsum[t];  // final outputs are acc / ls
+      if constexpr (kI4) {
+        // tile 2m + o: dim 2 (P r + m) + o, P = D/32 pairs per lane: the
+        // lane holds dims 8P g + 2P i + n for tile n, i = 0..3
+        constexpr int P = D / 32;
 #pragma unroll
-          for (int m = 0; m < NN / 2; ++m) {
-            const f32x4 e = acc[t][2 * m] / Lsum[t], o = acc[t][2 * m + 1] / Lsum[t];
-            *reinterpret_cast<u32x4*>(orow + 32 * m + 8 * g) =
-                u32x4{pack_bf16x2(e[0], o[0]), pack_bf16x2(e[1], o[1]), pack_bf16x2(e[2], o[2]), pack_bf16x2(e[3], o[3])};
-          }
-        } else {
-          float* arow = p.ws_acc + slot * D;
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = 8 * P * g + 2 * P * i;
+          if (final_out) {
+            uint32_t wv[P];
 #pragma unroll
-          for (int m = 0; m < NN / 2; ++m) {
-            const f32x4 e = acc[t][2 * m], o = acc[t][2 * m + 1];
-            *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
-            *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
+            for (int m = 0; m < P; ++m) wv[m] = pack_bf16x2(acc[t][2 * m][i] / ls, acc[t][2 * m + 1][i] / ls);
+            if constexpr (P == 4)
+              *reinterpret_cast<u32x4*>(orow + d0) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            else
+              *reinterpret_cast<u32x2*>(orow + d0) = u32x2{wv[0], wv[1]};
+          } else {
+#pragma unroll
+            for (int n = 0; n < NN; n += 4)
+              *reinterpret_cast<f32x4*>(arow + d0 + n) =
+                  f32x4{acc[t][n][i], acc[t][n + 1][i], acc[t][n + 2][i], acc[t][n + 3][i]};
           }
         }
-      } else if (final_out) {
-        uint16_t* orow = out + bh * D;
+      } else if constexpr (kInt8) {
+        // operand 4k + j: dim 64k + 4 r + j: the lane holds dims
+        // 64k + 16g + 4i + j
 #pragma unroll
-        for (int n = 0; n < NN; ++n) {
-          u32x2 w;
-          w.x = pack_bf16x2(acc[t][n][0] / Lsum[t], acc[t][n][1] / Lsum[t]);
-          w.y = pack_bf16x2(acc[t][n][2] / Lsum[t], acc[t][n][3] / Lsum[t]);
-          *reinterpret_cast<u32x2*>(orow + 16 * n + 4 * g) = w;
+        for (int k = 0; k < D / 64; ++k) {
+          const int d0 = 64 * k + 16 * g;
+          if (final_out) {
+            uint32_t wv[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              wv[2 * i] = pack_bf16x2(acc[t][4 * k][i] / ls, acc[t][4 * k + 1][i] / ls);
+              wv[2 * i + 1] = pack_bf16x2(acc[t][4 * k + 2][i] / ls, acc[t][4 * k + 3][i] / ls);
+            }
+            *reinterpret_cast<u32x4*>(orow + d0) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            *reinterpret_cast<u32x4*>(orow + d0 + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              *reinterpret_cast<f32x4*>(arow + d0 + 4 * i) =
+                  f32x4{acc[t][4 * k][i], acc[t][4 * k + 1][i], acc[t][4 * k + 2][i], acc[t][4 * k + 3][i]};
+          }
         }
       } else {
-        float* arow = p.ws_acc + slot * D;
+        // bf16, operand 2k + o: dim 32k + 2 r + o: the lane holds dims
+        // 32k + 8g + 2i + o
 #pragma unroll
-        for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[t][n];
+        for (int k = 0; k < NN / 2; ++k) {
+          const int d0 = 32 * k + 8 * g;
+          const f32x4 e = acc[t][2 * k], o = acc[t][2 * k + 1];
+          if (final_out) {
+            *reinterpret_cast<u32x4*>(orow + d0) =
+                u32x4{pack_bf16x2(e[0] / ls, o[0] / ls), pack_bf16x2(e[1] / ls, o[1] / ls),
+                      pack_bf16x2(e[2] / ls, o[2] / ls), pack_bf16x2(e[3] / ls, o[3] / ls)};
+          } else {
+            *reinterpret_cast<f32x4*>(arow + d0) = f32x4{e[0], o[0], e[1], o[1]};
+            *reinterpret_cast<f32x4*>(arow + d0 + 4) = f32x4{e[2], o[2], e[3], o[3]};
+          }
+        }
       }
       if (!final_out && g == 0) {
         p.ws_m[slot] = M[t];

@@ -5,10 +5,16 @@
 // bs = 16, the two halves of one block at bs = 32).  Lane l = 16 g + c loads
 //   K: row c of each sub-tile, 8 dims per operand (the A operand of
 //      v_mfma_f32_16x16x32_bf16: row l % 16, contraction 8 (l / 16) + e);
-//   V: tokens 4g .. 4g+3 of dim 16n + c of each sub-tile, 8 contiguous
-//      bytes (bf16) of the dim-major V tile (element (r, d) at d*bs + r);
-//      byte codes (and INT4 at D = 128) load whole 16-byte rows and hand
-//      each lane its 4 tokens by a transpose across lane groups;
+//   V: tokens 4g .. 4g+3 of the sub-tile (its token group g) for several
+//      dims at once.  V tiles are stored in groups of 4 tokens, dim-major
+//      inside a group (element (r, d) at ((r / 4) D + d) 4 + r % 4), so the
+//      4 tokens of one dim are contiguous and one 16-byte load holds them
+//      for 2 dims (bf16), 4 dims (byte codes) or 4 dim pairs (INT4): the
+//      dims 2c, 2c + 1 (4c .. 4c + 3, pairs 4c .. 4c + 3) of a 32-dim
+//      (64-dim, 64-pair) block.  Operand n of the PV contraction is one of
+//      those dims; which dim a tile row holds does not matter to the
+//      contraction, only to where the outputs are written (the kernels'
+//      output maps);
 //   int8 scales of tokens 4g .. 4g+3.
 // Every load is a buffer descriptor over one tile (uniform: scalar
 // registers) plus a loop-invariant lane offset.
@@ -105,18 +111,6 @@ __device__ __forceinline__ u32x2 nib4_to_bf16(uint32_t n) {
   return u32x2{nib_pair_to_bf16x2<0>(n), nib_pair_to_bf16x2<1>(n)};
 }
 
-// 4 x 4 transpose of words across the four 16-lane groups: on return, word
-// j of a lane in group g holds what word g of the lane at the same position
-// in group j held.  Two cross-half swaps (groups 0, 1 <-> 2, 3), then two
-// cross-row swaps (0 <-> 1, 2 <-> 3); no LDS, no shuffle addresses.
-__device__ __forceinline__ u32x4 transpose_groups(u32x4 w) {
-  const auto a = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
-  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  return u32x4{c[0], c[1], d[0], d[1]};
-}
-
 // Zero the bf16 elements (pairs packed in w) whose token is >= t_end.
 __device__ __forceinline__ uint32_t mask_pair(uint32_t w, int tok, int t_end) {
   const uint32_t lo = (tok < t_end) ? (w & 0xffffu) : 0u;
@@ -134,8 +128,9 @@ struct Chunk {
   // K rows: per sub-tile h, NJ operands of 8 dims (bf16: 16 B each; int8:
   // one 16-byte load feeds two operands, so NJ/2 loads)
   u32x4 k[2][kInt8 ? NJ / 2 : NJ];
-  // V^T: per sub-tile h and dim block n, tokens 4g .. 4g+3 of dim 16n + c
-  // (bf16: 8 B; int8: 4 B)
+  // V^T: per sub-tile h and operand n, tokens 4g .. 4g+3 of one dim (bf16:
+  // 8 B, dim 32 (n / 2) + 2c + n % 2; byte codes: 4 B, dim
+  // 64 (n / 4) + 4c + n % 4)
   typename std::conditional<kInt8, uint32_t, u32x2>::type v[2][NN];
   f32x4 ks[2], vs[2];  // int8 scales of sub-tile tokens 4g .. 4g+3
 };
@@ -156,7 +151,6 @@ struct ChunkLoader {
   int Hkv, kvh;
   // loop-invariant per-lane byte offsets inside a (block, kv-head) tile
   uint32_t koff, voff, soff;
-  uint32_t vrow;  // byte codes: V row (dim) 16 g + c of each group of 64 dims
 
   __device__ __forceinline__ ChunkLoader(const DecodeParams& p, int kvh_, int c, int g)
       : kc(static_cast<const char*>(p.k_cache)), vc(static_cast<const char*>(p.v_cache)),
@@ -164,10 +158,10 @@ struct ChunkLoader {
         Hkv(p.num_kv_heads), kvh(kvh_) {
     // K: row c of the sub-tile; dims 32j + 8g (bf16) or 64jj + 16g (int8)
     koff = (static_cast<uint32_t>(c) * D + (kInt8 ? 16u : 8u) * g) * kElem;
-    // V^T: dim c (+16n per load), tokens 4g .. 4g+3
-    voff = (static_cast<uint32_t>(c) * BS + 4u * g) * kElem;
+    // V: token group g of the sub-tile, dims 2c, 2c + 1 (bf16) or
+    // 4c .. 4c + 3 (byte codes) of each 32- (64-) dim block
+    voff = (static_cast<uint32_t>(g) * D + (kInt8 ? 4u : 2u) * c) * 4u * kElem;
     soff = 4u * g * 4u;
-    vrow = (16u * g + c) * BS;
   }
 
   // Buffer resource over one (block, kv-head) tile: the base is uniform, so
@@ -188,21 +182,21 @@ struct ChunkLoader {
       const __amdgpu_buffer_rsrc_t rk = tile(kc, t * kTileBytes, kTileBytes);
       const __amdgpu_buffer_rsrc_t rv = tile(vc, t * kTileBytes, kTileBytes);
       // uniform offsets (row of the sub-tile, per-load constants) go in the
-      // scalar offset operand, so the lane offset is the only vector input
+      // scalar offset operand, so the lane offset is the only vector input;
+      // the sub-tile's first row is a multiple of 4, so its token groups
+      // start at row0 * D elements
       const int ks_row = row0[h] * D * kElem;
-      const int vs_row = row0[h] * kElem;
+      const int vs_row = row0[h] * D * kElem;
       if constexpr (kInt8) {
 #pragma unroll
         for (int jj = 0; jj < NJ / 2; ++jj)
           ch.k[h][jj] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, ks_row + 64 * jj, 0));
-        // V: a lane loads all 16 tokens of dim 64k + 16g + c (16 bytes), and a
-        // transpose across lane groups hands each lane its tokens 4g .. 4g+3
-        // of dims 64k + 16j + c, j = 0..3 (operand n = 4k + j): a quarter of
-        // the load instructions of one 4-byte load per operand
+        // V: tokens 4g .. 4g+3 of dims 64k + 4c + j, j = 0..3 (operand
+        // n = 4k + j), one 16-byte load per 64 dims
 #pragma unroll
         for (int k = 0; k < D / 64; ++k) {
-          const u32x4 w = transpose_groups(__builtin_bit_cast(
-              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vrow, row0[h] + 64 * k * BS, 0)));
+          const u32x4 w = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, vs_row + 256 * k, 0));
 #pragma unroll
           for (int j = 0; j < 4; ++j) ch.v[h][4 * k + j] = w[j];
         }
@@ -214,9 +208,15 @@ struct ChunkLoader {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           ch.k[h][j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, ks_row + 64 * j, 0));
+        // V: tokens 4g .. 4g+3 of dims 32k + 2c and 32k + 2c + 1 (operands
+        // 2k, 2k + 1), one 16-byte load per 32 dims
 #pragma unroll
-        for (int n = 0; n < NN; ++n)
-          ch.v[h][n] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, vs_row + 32 * n * BS, 0));
+        for (int k = 0; k < NN / 2; ++k) {
+          const u32x4 w = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, vs_row + 256 * k, 0));
+          ch.v[h][2 * k] = u32x2{w.x, w.y};
+          ch.v[h][2 * k + 1] = u32x2{w.z, w.w};
+        }
       }
     }
   }
@@ -226,10 +226,11 @@ struct ChunkLoader {
 // (D/4) g .. (D/4) g + D/4 - 1 (D/8 bytes, one load); operand j is the word
 // of dims (D/4) g + 8 j .. + 7, its elements in the order of that word's
 // low nibbles, then its high nibbles (dims +0, 2, 4, 6, 1, 3, 5, 7).
-// V: the tile is [D/2][bs] bytes; per sub-tile and dim-pair block m, the
-// lane holds tokens 4g .. 4g+3 of byte row 16 m + c (dims 32 m + 2 c and
-// 32 m + 2 c + 1): its low nibbles feed the rows of output tile 2 m, its
-// high nibbles those of tile 2 m + 1.
+// V: the tile is [bs/4][D/2][4] bytes (token groups, dim pairs, tokens);
+// per sub-tile the lane holds words m = 0 .. D/32 - 1: tokens 4g .. 4g+3 of
+// dim pair (D/32) c + m (dims 2 ((D/32) c + m) and that + 1), one load;
+// word m's low nibbles feed the rows of output tile 2 m, its high nibbles
+// those of tile 2 m + 1.
 template <int D>
 struct ChunkI4 {
   typename std::conditional<D == 128, u32x4, u32x2>::type k[2];
@@ -252,11 +253,10 @@ struct ChunkLoaderI4 {
         ksc(reinterpret_cast<const char*>(p.k_scale)), vsc(reinterpret_cast<const char*>(p.v_scale)),
         Hkv(p.num_kv_heads), kvh(kvh_) {
     koff = static_cast<uint32_t>(c) * (D / 2) + (D / 8) * g;
-    voff = static_cast<uint32_t>(c) * BS + 4u * g;
+    // V: token group g, dim pairs (D/32) c .. (D/32) c + D/32 - 1
+    voff = (static_cast<uint32_t>(g) * (D / 2) + (D / 32) * c) * 4u;
     soff = 4u * g * 4u;
-    vrow = (16u * g + c) * BS;
   }
-  uint32_t vrow;  // D = 128: V row (dim pair) 16 g + c
 
   __device__ __forceinline__ void load(ChunkI4<D>& ch, const int blk[2], const int row0[2]) const {
 #pragma unroll
@@ -268,17 +268,17 @@ struct ChunkLoaderI4 {
         ch.k[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, row0[h] * (D / 2), 0));
       else
         ch.k[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, koff, row0[h] * (D / 2), 0));
+      // the sub-tile's token groups start at row0 * D/2 bytes
       if constexpr (D == 128) {
-        // all 16 tokens of dim pair 16g + c, then the transpose across lane
-        // groups: word m = tokens 4g .. 4g+3 of dim pair 16m + c
-        const u32x4 w = transpose_groups(__builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, vrow, row0[h], 0)));
+        const u32x4 w = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff, row0[h] * (D / 2), 0));
 #pragma unroll
         for (int m = 0; m < 4; ++m) ch.v[h][m] = w[m];
       } else {
-#pragma unroll
-        for (int m = 0; m < D / 32; ++m)
-          ch.v[h][m] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, row0[h] + 16 * m * BS, 0);
+        const u32x2 w = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, row0[h] * (D / 2), 0));
+        ch.v[h][0] = w.x;
+        ch.v[h][1] = w.y;
       }
       const __amdgpu_buffer_rsrc_t rks = ChunkLoader<true, D, BS>::tile(ksc, t * BS * 4, BS * 4);
       const __amdgpu_buffer_rsrc_t rvs = ChunkLoader<true, D, BS>::tile(vsc, t * BS * 4, BS * 4);

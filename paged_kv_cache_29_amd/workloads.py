@@ -36,7 +36,8 @@ nearest-even.  The last token of every sequence is the step's new token: its
 slot is poisoned in the pool and its K/V come in ``k_new`` / ``v_new`` with
 ``slot_new``, to be written by the cache write before attention reads it.
 
-Layouts: ``k_cache[NB, Hkv, bs, D]``, ``v_cache[NB, Hkv, D, bs]``,
+Layouts: ``k_cache[NB, Hkv, bs, D]``, ``v_cache[NB, Hkv, bs/4, D, 4]``
+(token ``r``, dim ``d`` of a V tile at ``[r // 4, d, r % 4]``),
 ``q[B, H, D]``, ``block_tables[B, MB]`` int32 (-1 past the last block),
 ``context_lens[B]`` int32, slots int64.  bf16 arrays hold uint16 bit
 patterns.  Unused blocks, unused rows and the new-token slots hold NaN.
@@ -126,10 +127,18 @@ def _poison(alloc, k_cache, v_cache, slots_new, kind):
     for blk in np.nonzero((alloc.refcount > 0) & (alloc.fill < bs))[0]:
         f = int(alloc.fill[blk])
         k_cache[blk, :, f:, :] = nan
-        v_cache[blk, :, :, f:] = nan
+        for r in range(f, bs):
+            v_cache[blk, :, r // 4, :, r % 4] = nan
     for s in np.asarray(slots_new).tolist():
         k_cache[s // bs, :, s % bs, :] = nan
-        v_cache[s // bs, :, :, s % bs] = nan
+        v_cache[s // bs, :, (s % bs) // 4, :, s % 4] = nan
+
+
+def _copy_rows(pool_k, pool_v, src, dst, rows):
+    """Copy-on-write duplicate: the first ``rows`` tokens of block ``src``."""
+    pool_k[dst, :, :rows, :] = pool_k[src, :, :rows, :]
+    for r in range(rows):
+        pool_v[dst, :, r // 4, :, r % 4] = pool_v[src, :, r // 4, :, r % 4]
 
 
 def _allocate(lens, bs, num_blocks, order, prefix=0, prefix_group_size=None):
@@ -205,23 +214,21 @@ def build(name, seed, lens, num_heads, num_kv_heads, head_dim, block_size,
         # shared blocks: fp32 pools as for bf16 (copy-on-write duplicates
         # included), then one fill row per distinct used slot
         k_pool = _draw(rng, (num_blocks, Hkv, bs, D), "f32")
-        v_pool = _draw(rng, (num_blocks, Hkv, D, bs), "f32")
+        v_pool = _draw(rng, (num_blocks, Hkv, bs // 4, D, 4), "f32")
         for src, dst, rows in alloc.copies:
-            k_pool[dst, :, :rows, :] = k_pool[src, :, :rows, :]
-            v_pool[dst, :, :, :rows] = v_pool[src, :, :, :rows]
+            _copy_rows(k_pool, v_pool, src, dst, rows)
         used = [np.asarray(f, np.int64) for f in fill_slots]
         used += [np.arange(dst * bs, dst * bs + rows, dtype=np.int64) for _, dst, rows in alloc.copies]
         slot_fill = np.unique(np.concatenate(used)) if used else np.empty(0, np.int64)
         w.k_fill = np.ascontiguousarray(k_pool[slot_fill // bs, :, slot_fill % bs, :])
-        w.v_fill = np.ascontiguousarray(v_pool[slot_fill // bs, :, :, slot_fill % bs])
+        w.v_fill = np.ascontiguousarray(v_pool[slot_fill // bs, :, (slot_fill % bs) // 4, :, slot_fill % 4])
         w.slot_fill = slot_fill
         w.meta["fill_per_sequence"] = False
     elif kv_dtype in ("f32", "bf16"):
         k_cache = _draw(rng, (num_blocks, Hkv, bs, D), store)
-        v_cache = _draw(rng, (num_blocks, Hkv, D, bs), store)
+        v_cache = _draw(rng, (num_blocks, Hkv, bs // 4, D, 4), store)
         for src, dst, rows in alloc.copies:        # copy-on-write duplicates
-            k_cache[dst, :, :rows, :] = k_cache[src, :, :rows, :]
-            v_cache[dst, :, :, :rows] = v_cache[src, :, :, :rows]
+            _copy_rows(k_cache, v_cache, src, dst, rows)
         _poison(alloc, k_cache, v_cache, new_slots[new_slots >= 0], store)
         w.k_cache, w.v_cache = k_cache, v_cache
     elif kv_dtype in CODED_KINDS:

@@ -28,7 +28,7 @@ CODE_WRITE = {"i8": "kv_cache_write_int8", "fp8": "kv_cache_write_fp8",
 def code_tile_shapes(kind, NB, Hkv, bs, D):
     """Shapes of a coded cache's K and V pools (INT4 packs two dims per byte)."""
     w = D // 2 if kind == "i4" else D
-    return (NB, Hkv, bs, w), (NB, Hkv, w, bs)
+    return (NB, Hkv, bs, w), (NB, Hkv, bs // 4, w, 4)
 
 
 def to_torch(arr, kind):

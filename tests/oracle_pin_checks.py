@@ -52,7 +52,7 @@ def brute_force_decode(w, b, h, k_cache=None, v_cache=None):
         blk = int(w.block_tables[b][t // bs])
         r = t % bs
         krow = [float(x) for x in oatt.widen(k_cache[blk, g, r, :], kind)]
-        vrow = [float(x) for x in oatt.widen(v_cache[blk, g, :, r], kind)]
+        vrow = [float(x) for x in oatt.widen(v_cache[blk, g, r // 4, :, r % 4], kind)]
         dot = 0.0
         for d in range(D):
             dot += qv[d] * krow[d]
@@ -113,11 +113,11 @@ def check_worked_example_gather():
     assert table == [71, 18, 58]
     NB, D = 72, 4
     k = np.zeros((NB, 1, bs, D), dtype=np.float32)
-    v = np.zeros((NB, 1, D, bs), dtype=np.float32)
+    v = np.zeros((NB, 1, bs // 4, D, 4), dtype=np.float32)
     for blk in range(NB):
         for r in range(bs):
             k[blk, 0, r, :] = blk * 1000 + r
-            v[blk, 0, :, r] = -(blk * 1000 + r)
+            v[blk, 0, r // 4, :, r % 4] = -(blk * 1000 + r)
     K, V = oracle.gather_kv(k, v, np.array(table), 47, bs, 0, "f32")
     expect = [71000 + r for r in range(16)] + [18000 + r for r in range(16)] \
         + [58000 + r for r in range(15)]
@@ -183,7 +183,7 @@ def check_unpaged_sdpa():
         Vc = rng.standard_normal((Hkv, n * bs, D)).astype(np.float32)
         q = rng.standard_normal((1, H, D)).astype(np.float32)
         k_cache = Kc.reshape(Hkv, n, bs, D).transpose(1, 0, 2, 3).copy()
-        v_cache = Vc.reshape(Hkv, n, bs, D).transpose(1, 0, 3, 2).copy()
+        v_cache = Vc.reshape(Hkv, n, bs // 4, 4, D).transpose(1, 0, 2, 4, 3).copy()
         tables = np.arange(n, dtype=np.int32)[None, :]
         scale = 1.0 / math.sqrt(D)
         out = oracle.decode_attention(q, k_cache, v_cache, tables, np.array([L], np.int32),
@@ -221,7 +221,7 @@ def check_brute_force_int8():
     rng = np.random.default_rng(11)
     NB, Hkv, bs, D, H = 6, 2, 16, 8, 4
     kc = rng.integers(-127, 128, size=(NB, Hkv, bs, D)).astype(np.int8)
-    vc = rng.integers(-127, 128, size=(NB, Hkv, D, bs)).astype(np.int8)
+    vc = rng.integers(-127, 128, size=(NB, Hkv, bs // 4, D, 4)).astype(np.int8)
     ks = rng.uniform(0.001, 0.03, size=(NB, Hkv, bs)).astype(np.float32)
     vs = rng.uniform(0.001, 0.03, size=(NB, Hkv, bs)).astype(np.float32)
     tables = np.array([[4, 1, 3], [0, 5, -1]], dtype=np.int32)
@@ -236,7 +236,7 @@ def check_brute_force_int8():
             for t in range(int(lens[b])):
                 blk, r = int(tables[b][t // bs]), t % bs
                 kr = [float(kc[blk, g, r, d]) * float(ks[blk, g, r]) for d in range(D)]
-                vr = [float(vc[blk, g, d, r]) * float(vs[blk, g, r]) for d in range(D)]
+                vr = [float(vc[blk, g, r // 4, d, r % 4]) * float(vs[blk, g, r]) for d in range(D)]
                 sc.append(0.3 * sum(float(q[b, h, d]) * kr[d] for d in range(D)))
                 rows.append(vr)
             m = max(sc)
@@ -252,7 +252,7 @@ def check_single_token():
     b = int(np.nonzero(w.context_lens == 1)[0][0])
     blk = int(w.block_tables[b][0])
     for h in range(w.num_heads):
-        v0 = w.v_cache[blk, h, :, 0].astype(np.float64)
+        v0 = w.v_cache[blk, h, 0, :, 0].astype(np.float64)
         assert np.array_equal(out[b, h], v0)
 
 
@@ -275,7 +275,7 @@ def check_equal_keys_mean():
     for b in range(w.num_seqs):
         L, bs = int(w.context_lens[b]), w.block_size
         for h in range(w.num_heads):
-            vals = [w.v_cache[w.block_tables[b][t // bs], h, :, t % bs] for t in range(L)]
+            vals = [w.v_cache[w.block_tables[b][t // bs], h, (t % bs) // 4, :, t % 4] for t in range(L)]
             np.testing.assert_allclose(out[b, h], np.mean(np.array(vals, np.float64), axis=0),
                                        rtol=1e-12, atol=1e-13)
 
@@ -293,7 +293,7 @@ def check_needle():
         qv = w.q[b, h].astype(np.float64)
         k[blk, h, r, :] = (50.0 * qv / np.linalg.norm(qv) * math.sqrt(w.head_dim)).astype(np.float32)
         out = oracle_decode(w, k_cache=k, samples=[(b, h)])
-        np.testing.assert_allclose(out[b, h], w.v_cache[blk, h, :, r].astype(np.float64), atol=1e-9)
+        np.testing.assert_allclose(out[b, h], w.v_cache[blk, h, r // 4, :, r % 4].astype(np.float64), atol=1e-9)
 
 
 # ---------------------------------------------------------------- P11, P13
@@ -354,15 +354,15 @@ def _slot_view_k(k_cache):
 
 
 def _slot_view_v(v_cache):
-    NB, Hkv, D, bs = v_cache.shape
-    return v_cache.transpose(0, 3, 1, 2).reshape(NB * bs, Hkv, D)
+    NB, Hkv, G4, D, four = v_cache.shape   # token r of a tile at [r // 4, :, r % 4]
+    return v_cache.transpose(0, 2, 4, 1, 3).reshape(NB * G4 * four, Hkv, D)
 
 
 def check_cache_write_slots():
     rng = np.random.default_rng(4)
     NB, Hkv, bs, D, T = 9, 3, 16, 8, 20
     k_cache = rng.standard_normal((NB, Hkv, bs, D)).astype(np.float32)
-    v_cache = rng.standard_normal((NB, Hkv, D, bs)).astype(np.float32)
+    v_cache = rng.standard_normal((NB, Hkv, bs // 4, D, 4)).astype(np.float32)
     k = rng.standard_normal((T, Hkv, D)).astype(np.float32)
     v = rng.standard_normal((T, Hkv, D)).astype(np.float32)
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
@@ -425,7 +425,7 @@ def check_int8_write_brute():
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
     slots[2] = -1
     kc = np.zeros((NB, Hkv, bs, D), np.int8)
-    vc = np.zeros((NB, Hkv, D, bs), np.int8)
+    vc = np.zeros((NB, Hkv, bs // 4, D, 4), np.int8)
     ksc = np.full((NB, Hkv, bs), np.nan, np.float32)
     vsc = np.full((NB, Hkv, bs), np.nan, np.float32)
     k2, v2, ks2, vs2 = ocache.cache_write_int8(k, v, kc, vc, ksc, vsc, slots, bs)
@@ -435,7 +435,7 @@ def check_int8_write_brute():
         blk, r = s // bs, s % bs
         for h in range(Hkv):
             for src, codes, sc in ((k[t, h], k2[blk, h, r, :], ks2[blk, h, r]),
-                                   (v[t, h], v2[blk, h, :, r], vs2[blk, h, r])):
+                                   (v[t, h], v2[blk, h, r // 4, :, r % 4], vs2[blk, h, r])):
                 a = float(np.max(np.abs(src)))
                 sref = np.float32(np.float32(a) / np.float32(127.0))
                 if a == 0:
@@ -539,7 +539,7 @@ def check_fp8_write_brute():
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
     slots[5] = -1
     kc = np.zeros((NB, Hkv, bs, D), np.uint8)
-    vc = np.zeros((NB, Hkv, D, bs), np.uint8)
+    vc = np.zeros((NB, Hkv, bs // 4, D, 4), np.uint8)
     ksc = np.full((NB, Hkv, bs), np.nan, np.float32)
     vsc = np.full((NB, Hkv, bs), np.nan, np.float32)
     k2, v2, ks2, vs2 = ofp8.cache_write_fp8(k, v, kc, vc, ksc, vsc, slots, bs)
@@ -550,7 +550,7 @@ def check_fp8_write_brute():
         blk, r = sl // bs, sl % bs
         for h in range(Hkv):
             for src, codes, sc in ((k[t, h], k2[blk, h, r, :], ks2[blk, h, r]),
-                                   (v[t, h], v2[blk, h, :, r], vs2[blk, h, r])):
+                                   (v[t, h], v2[blk, h, r // 4, :, r % 4], vs2[blk, h, r])):
                 a = float(np.max(np.abs(src)))
                 sref = np.float32(np.float32(a) / np.float32(448.0))
                 if a == 0:
@@ -573,7 +573,7 @@ def check_brute_force_fp8():
     NB, Hkv, bs, D, H = 6, 2, 16, 8, 4
     kc = rng.integers(0, 0x7F, size=(NB, Hkv, bs, D)).astype(np.uint8) | \
         (rng.integers(0, 2, size=(NB, Hkv, bs, D)).astype(np.uint8) << 7)
-    vc = rng.integers(0, 0x7F, size=(NB, Hkv, D, bs)).astype(np.uint8)
+    vc = rng.integers(0, 0x7F, size=(NB, Hkv, bs // 4, D, 4)).astype(np.uint8)
     ks = rng.uniform(1e-4, 3e-3, size=(NB, Hkv, bs)).astype(np.float32)
     vs = rng.uniform(1e-4, 3e-3, size=(NB, Hkv, bs)).astype(np.float32)
     tables = np.array([[2, 5, 0], [1, 4, -1]], dtype=np.int32)
@@ -588,7 +588,7 @@ def check_brute_force_fp8():
             for t in range(int(lens[b])):
                 blk, r = int(tables[b][t // bs]), t % bs
                 kr = [ofp8.e4m3_value(kc[blk, g, r, d]) * float(ks[blk, g, r]) for d in range(D)]
-                vr = [ofp8.e4m3_value(vc[blk, g, d, r]) * float(vs[blk, g, r]) for d in range(D)]
+                vr = [ofp8.e4m3_value(vc[blk, g, r // 4, d, r % 4]) * float(vs[blk, g, r]) for d in range(D)]
                 sc.append(0.2 * sum(float(q[b, h, d]) * kr[d] for d in range(D)))
                 rows.append(vr)
             m = max(sc)
@@ -676,7 +676,7 @@ def check_e5m2_write_brute():
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
     slots[4] = -1
     kc = np.zeros((NB, Hkv, bs, D), np.uint8)
-    vc = np.zeros((NB, Hkv, D, bs), np.uint8)
+    vc = np.zeros((NB, Hkv, bs // 4, D, 4), np.uint8)
     ksc = np.full((NB, Hkv, bs), np.nan, np.float32)
     vsc = np.full((NB, Hkv, bs), np.nan, np.float32)
     k2, v2, ks2, vs2 = ofp8.cache_write_fp8_e5m2(k, v, kc, vc, ksc, vsc, slots, bs)
@@ -687,7 +687,7 @@ def check_e5m2_write_brute():
         blk, r = sl // bs, sl % bs
         for h in range(Hkv):
             for src, codes, sc in ((k[t, h], k2[blk, h, r, :], ks2[blk, h, r]),
-                                   (v[t, h], v2[blk, h, :, r], vs2[blk, h, r])):
+                                   (v[t, h], v2[blk, h, r // 4, :, r % 4], vs2[blk, h, r])):
                 a = float(np.max(np.abs(src)))
                 sref = np.float32(np.float32(a) / np.float32(57344.0))
                 if a == 0:
@@ -708,7 +708,7 @@ def check_brute_force_e5m2():
     NB, Hkv, bs, D, H = 6, 2, 16, 8, 4
     kc = (rng.integers(0, 0x7C, size=(NB, Hkv, bs, D)) |
           (rng.integers(0, 2, size=(NB, Hkv, bs, D)) << 7)).astype(np.uint8)
-    vc = rng.integers(0, 0x7C, size=(NB, Hkv, D, bs)).astype(np.uint8)
+    vc = rng.integers(0, 0x7C, size=(NB, Hkv, bs // 4, D, 4)).astype(np.uint8)
     ks = rng.uniform(1e-6, 2e-5, size=(NB, Hkv, bs)).astype(np.float32)
     vs = rng.uniform(1e-6, 2e-5, size=(NB, Hkv, bs)).astype(np.float32)
     tables = np.array([[4, 1, 0], [2, 5, -1]], dtype=np.int32)
@@ -723,7 +723,7 @@ def check_brute_force_e5m2():
             for t in range(int(lens[b])):
                 blk, r = int(tables[b][t // bs]), t % bs
                 kr = [ofp8.e5m2_value(kc[blk, g, r, d]) * float(ks[blk, g, r]) for d in range(D)]
-                vr = [ofp8.e5m2_value(vc[blk, g, d, r]) * float(vs[blk, g, r]) for d in range(D)]
+                vr = [ofp8.e5m2_value(vc[blk, g, r // 4, d, r % 4]) * float(vs[blk, g, r]) for d in range(D)]
                 sc.append(0.25 * sum(float(q[b, h, d]) * kr[d] for d in range(D)))
                 rows.append(vr)
             m = max(sc)
@@ -790,7 +790,7 @@ def check_int4_write_brute():
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
     slots[1] = -1
     kc = np.full((NB, Hkv, bs, D // 2), 0xAB, np.uint8)
-    vc = np.full((NB, Hkv, D // 2, bs), 0xAB, np.uint8)
+    vc = np.full((NB, Hkv, bs // 4, D // 2, 4), 0xAB, np.uint8)
     ksc = np.full((NB, Hkv, bs), np.nan, np.float32)
     vsc = np.full((NB, Hkv, bs), np.nan, np.float32)
     k2, v2, ks2, vs2 = oint4.cache_write_int4(k, v, kc, vc, ksc, vsc, slots, bs)
@@ -800,7 +800,7 @@ def check_int4_write_brute():
         blk, r = sl // bs, sl % bs
         for h in range(Hkv):
             for src, packed, sc in ((k[t, h], k2[blk, h, r, :], ks2[blk, h, r]),
-                                    (v[t, h], v2[blk, h, :, r], vs2[blk, h, r])):
+                                    (v[t, h], v2[blk, h, r // 4, :, r % 4], vs2[blk, h, r])):
                 a = float(np.max(np.abs(src)))
                 sref = np.float32(np.float32(a) / np.float32(7.0))
                 if a == 0:
@@ -819,7 +819,7 @@ def check_int4_write_brute():
     written = {sl for sl in slots.tolist() if sl >= 0}
     for sl in set(range(NB * bs)) - written:
         blk, r = sl // bs, sl % bs
-        assert np.all(k2[blk, :, r, :] == 0xAB) and np.all(v2[blk, :, :, r] == 0xAB)
+        assert np.all(k2[blk, :, r, :] == 0xAB) and np.all(v2[blk, :, r // 4, :, r % 4] == 0xAB)
         assert np.isnan(ks2[blk, 0, r])
 
 
@@ -834,7 +834,7 @@ def check_brute_force_int4():
     rng = np.random.default_rng(43)
     NB, Hkv, bs, D, H = 6, 2, 16, 8, 4
     kc = rng.integers(0, 256, size=(NB, Hkv, bs, D // 2)).astype(np.uint8)
-    vc = rng.integers(0, 256, size=(NB, Hkv, D // 2, bs)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(NB, Hkv, bs // 4, D // 2, 4)).astype(np.uint8)
     ks = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
     vs = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
     tables = np.array([[3, 0, 5], [4, 1, -1]], dtype=np.int32)
@@ -849,7 +849,7 @@ def check_brute_force_int4():
             for t in range(int(lens[b])):
                 blk, r = int(tables[b][t // bs]), t % bs
                 kr = [_int4_value(kc[blk, g, r, d // 2], d % 2) * float(ks[blk, g, r]) for d in range(D)]
-                vr = [_int4_value(vc[blk, g, d // 2, r], d % 2) * float(vs[blk, g, r]) for d in range(D)]
+                vr = [_int4_value(vc[blk, g, r // 4, d // 2, r % 4], d % 2) * float(vs[blk, g, r]) for d in range(D)]
                 sc.append(0.3 * sum(float(q[b, h, d]) * kr[d] for d in range(D)))
                 rows.append(vr)
             m = max(sc)
@@ -907,12 +907,12 @@ def check_mq_sdpa_bottom_right_causal():
     L, n, H, D, bs = 45, 7, 2, 16, 16
     nb = (L + bs - 1) // bs
     kc = rng.standard_normal((nb, 1, bs, D)).astype(np.float32)
-    vc = rng.standard_normal((nb, 1, D, bs)).astype(np.float32)
+    vc = rng.standard_normal((nb, 1, bs // 4, D, 4)).astype(np.float32)
     q = rng.standard_normal((n, H, D)).astype(np.float32)
     out = oracle.multi_query_attention(q, kc, vc, np.arange(nb, dtype=np.int32)[None], np.array([L], np.int32),
                                        np.array([0, n], np.int32), 0.3, H, 1, D, bs, "f32", "f32")
     K = torch.from_numpy(kc[:, 0].reshape(-1, D)[:L].astype(np.float64))
-    V = torch.from_numpy(np.transpose(vc[:, 0], (0, 2, 1)).reshape(-1, D)[:L].astype(np.float64))
+    V = torch.from_numpy(np.transpose(vc[:, 0], (0, 1, 3, 2)).reshape(-1, D)[:L].astype(np.float64))
     mask = torch.ones(n, L, dtype=torch.bool).tril(diagonal=L - n)
     for h in range(H):
         Q = torch.from_numpy(q[:, h].astype(np.float64))
@@ -925,7 +925,7 @@ def check_mq_brute_force_int8():
     rng = np.random.default_rng(34)
     NB, Hkv, bs, D, H = 5, 1, 16, 8, 2
     kc = rng.integers(-127, 128, size=(NB, Hkv, bs, D)).astype(np.int8)
-    vc = rng.integers(-127, 128, size=(NB, Hkv, D, bs)).astype(np.int8)
+    vc = rng.integers(-127, 128, size=(NB, Hkv, bs // 4, D, 4)).astype(np.int8)
     ks = rng.uniform(0.001, 0.02, size=(NB, Hkv, bs)).astype(np.float32)
     vs = rng.uniform(0.001, 0.02, size=(NB, Hkv, bs)).astype(np.float32)
     tables = np.array([[3, 0, 4]], dtype=np.int32)
@@ -941,7 +941,7 @@ def check_mq_brute_force_int8():
                 blk, r = int(tables[0][t // bs]), t % bs
                 kr = [float(kc[blk, 0, r, d]) * float(ks[blk, 0, r]) for d in range(D)]
                 sc.append(0.5 * sum(float(q[i, h, d]) * kr[d] for d in range(D)))
-                rows.append([float(vc[blk, 0, d, r]) * float(vs[blk, 0, r]) for d in range(D)])
+                rows.append([float(vc[blk, 0, r // 4, d, r % 4]) * float(vs[blk, 0, r]) for d in range(D)])
             m = max(sc)
             ps = [math.exp(x - m) for x in sc]
             ref = [sum(p * row[d] for p, row in zip(ps, rows)) / sum(ps) for d in range(D)]

@@ -41,7 +41,7 @@ def main():
     rng = np.random.default_rng(11)
     bm = pkv.BlockManager(NB, bs, order=rng.permutation(NB))
     kc_np = np.zeros((NB, Hkv, bs, D), np.uint16)
-    vc_np = np.zeros((NB, Hkv, D, bs), np.uint16)
+    vc_np = np.zeros((NB, Hkv, bs // 4, D, 4), np.uint16)
     kc, vc = to_dev(kc_np, "bf16"), to_dev(vc_np, "bf16")
 
     def rows(n):
@@ -52,7 +52,8 @@ def main():
         for src, dst, nrows in copies:
             pkv.copy_blocks((kc, vc), (kc, vc), torch.tensor([[src, dst]], dtype=torch.int32, device=DEV))
             kc_np[dst, :, :nrows] = kc_np[src, :, :nrows]
-            vc_np[dst, :, :, :nrows] = vc_np[src, :, :, :nrows]
+            for r in range(nrows):
+                vc_np[dst, :, r // 4, :, r % 4] = vc_np[src, :, r // 4, :, r % 4]
         k, v = rows(len(seq_slots)), rows(len(seq_slots))
         pkv.kv_cache_write(to_dev(k, "bf16"), to_dev(v, "bf16"), kc, vc, torch.from_numpy(seq_slots).to(DEV))
         kc_np, vc_np = ocache.cache_write(k, v, kc_np, vc_np, seq_slots, bs)

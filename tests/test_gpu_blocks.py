@@ -31,7 +31,7 @@ def _pool(gen, NB, Hkv, bs, D, kind, device=DEV, pinned=False):
         return t
     W = D // 2 if kind == "i4" else D   # INT4: two dims per byte
     k = raw((NB, Hkv, bs, W), ESZ[kind]).view(TDT[kind]).view(NB, Hkv, bs, W)
-    v = raw((NB, Hkv, W, bs), ESZ[kind]).view(TDT[kind]).view(NB, Hkv, W, bs)
+    v = raw((NB, Hkv, bs // 4, W, 4), ESZ[kind]).view(TDT[kind]).view(NB, Hkv, bs // 4, W, 4)
     if kind in ("i8", "fp8", "e5m2", "i4"):
         ks = raw((NB, Hkv, bs), 4).view(torch.float32).view(NB, Hkv, bs)
         vs = raw((NB, Hkv, bs), 4).view(torch.float32).view(NB, Hkv, bs)
@@ -99,7 +99,7 @@ def test_manager_driven_decode_with_copy_on_write_and_swap():
     NB, NH, Hkv, H, D, bs = 96, 40, 2, 8, 128, 16
     bm = pkv.BlockManager(NB, bs, num_host_blocks=NH, order=rng.permutation(NB))
     kc_np = np.full((NB, Hkv, bs, D), workloads.BF16_NAN, np.uint16)
-    vc_np = np.full((NB, Hkv, D, bs), workloads.BF16_NAN, np.uint16)
+    vc_np = np.full((NB, Hkv, bs // 4, D, 4), workloads.BF16_NAN, np.uint16)
     kc, vc = to_dev(kc_np, "bf16"), to_dev(vc_np, "bf16")
 
     def write(sid, n):
@@ -109,7 +109,8 @@ def test_manager_driven_decode_with_copy_on_write_and_swap():
             pkv.copy_blocks((kc, vc), (kc, vc),
                             torch.tensor([[src, dst]], dtype=torch.int32, device=DEV))
             kc_np[dst, :, :rows] = kc_np[src, :, :rows]
-            vc_np[dst, :, :, :rows] = vc_np[src, :, :, :rows]
+            for r in range(rows):
+                vc_np[dst, :, r // 4, :, r % 4] = vc_np[src, :, r // 4, :, r % 4]
         k = workloads.bf16_bits(rng.standard_normal((n, Hkv, D)).astype(np.float32))
         v = workloads.bf16_bits(rng.standard_normal((n, Hkv, D)).astype(np.float32))
         pkv.kv_cache_write(to_dev(k, "bf16"), to_dev(v, "bf16"), kc, vc, torch.from_numpy(slots).to(DEV))
@@ -143,7 +144,7 @@ def test_manager_driven_decode_with_copy_on_write_and_swap():
     torch.cuda.synchronize()
 
     host = tuple(torch.zeros(s, dtype=torch.bfloat16).pin_memory()
-                 for s in ((NH, Hkv, bs, D), (NH, Hkv, D, bs)))
+                 for s in ((NH, Hkv, bs, D), (NH, Hkv, bs // 4, D, 4)))
     out_pairs, saved = {}, {}
     for s in (seqs[1], seqs[4]):
         p = bm.swap_out(s)

@@ -96,7 +96,7 @@ def test_needle_dominates():
     ref = oracle_out(w)
     assert_parity(got, ref, "bf16", "needle")
     for b, (blk, r) in targets.items():
-        vv = (v[blk, 0, :, r].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        vv = (v[blk, 0, r // 4, :, r % 4].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         assert np.allclose(got[b, 0], vv, atol=1e-2, rtol=1e-2)
 
 

@@ -49,7 +49,7 @@ def test_write_fp8_bitexact(D, bs):
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
     slots[10:20] = -3
     kc = np.full((NB, Hkv, bs, D), 0x7F, np.uint8)     # NaN codes where nothing is written
-    vc = np.full((NB, Hkv, D, bs), 0x7F, np.uint8)
+    vc = np.full((NB, Hkv, bs // 4, D, 4), 0x7F, np.uint8)
     ks = np.full((NB, Hkv, bs), np.nan, np.float32)
     vs = np.full((NB, Hkv, bs), np.nan, np.float32)
     rk, rv, rks, rvs = ofp8.cache_write_fp8(k, v, kc, vc, ks, vs, slots, bs)
@@ -80,9 +80,11 @@ def test_every_code_is_read_as_its_value():
     codes = np.arange(256, dtype=np.uint8)
     codes = np.where((codes & 0x7F) == 0x7F, 0, codes).astype(np.uint8)   # NaN codes -> 0
     kc = np.zeros((1, Hkv, bs, D), np.uint8)
-    vc = np.zeros((1, Hkv, D, bs), np.uint8)
+    vc = np.zeros((1, Hkv, bs // 4, D, 4), np.uint8)
     kc.reshape(-1)[:256] = codes[::-1]
-    vc.reshape(-1)[:256] = codes                        # dims 0..15, all 16 tokens
+    for e, code in enumerate(codes):                    # dims 0..15, all 16 tokens
+        r = e % 16
+        vc[0, 0, r // 4, e // 16, r % 4] = code
     ks = np.ones((1, Hkv, bs), np.float32)
     vs = np.ones((1, Hkv, bs), np.float32)
     q = np.zeros((1, H, D), np.uint16)                  # bf16 zeros
@@ -136,7 +138,7 @@ def test_write_e5m2_bitexact(D, bs):
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
     slots[10:20] = -2
     kc = np.full((NB, Hkv, bs, D), 0x7F, np.uint8)     # NaN codes where nothing is written
-    vc = np.full((NB, Hkv, D, bs), 0x7F, np.uint8)
+    vc = np.full((NB, Hkv, bs // 4, D, 4), 0x7F, np.uint8)
     ks = np.full((NB, Hkv, bs), np.nan, np.float32)
     vs = np.full((NB, Hkv, bs), np.nan, np.float32)
     rk, rv, rks, rvs = ofp8.cache_write_fp8_e5m2(k, v, kc, vc, ks, vs, slots, bs)
@@ -164,9 +166,11 @@ def test_every_e5m2_code_is_read_as_its_value():
     codes = np.arange(256, dtype=np.uint8)
     codes = np.where((codes & 0x7C) == 0x7C, 0, codes).astype(np.uint8)   # inf / NaN codes -> 0
     kc = np.zeros((1, Hkv, bs, D), np.uint8)
-    vc = np.zeros((1, Hkv, D, bs), np.uint8)
+    vc = np.zeros((1, Hkv, bs // 4, D, 4), np.uint8)
     kc.reshape(-1)[:256] = codes[::-1]
-    vc.reshape(-1)[:256] = codes
+    for e, code in enumerate(codes):                    # dims 0..15, all 16 tokens
+        r = e % 16
+        vc[0, 0, r // 4, e // 16, r % 4] = code
     ks = np.ones((1, Hkv, bs), np.float32)
     vs = np.ones((1, Hkv, bs), np.float32)
     q = np.zeros((1, H, D), np.uint16)

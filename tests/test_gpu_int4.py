@@ -44,7 +44,7 @@ def test_write_int4_bitexact(D, bs):
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
     slots[10:20] = -1
     kc = np.full((NB, Hkv, bs, D // 2), 0xAB, np.uint8)   # untouched bytes must stay
-    vc = np.full((NB, Hkv, D // 2, bs), 0xAB, np.uint8)
+    vc = np.full((NB, Hkv, bs // 4, D // 2, 4), 0xAB, np.uint8)
     ks = np.full((NB, Hkv, bs), np.nan, np.float32)
     vs = np.full((NB, Hkv, bs), np.nan, np.float32)
     rk, rv, rks, rvs = oint4.cache_write_int4(k, v, kc, vc, ks, vs, slots, bs)
@@ -72,7 +72,7 @@ def test_every_code_is_read_as_its_value():
     bs, D, Hkv, H, L = 16, 128, 2, 8, 16
     rng = np.random.default_rng(3)
     NB = 4
-    vc = rng.integers(0, 256, size=(NB, Hkv, D // 2, bs)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(NB, Hkv, bs // 4, D // 2, 4)).astype(np.uint8)
     kc = rng.integers(0, 256, size=(NB, Hkv, bs, D // 2)).astype(np.uint8)
     ks = np.ones((NB, Hkv, bs), np.float32)
     vs = np.ones((NB, Hkv, bs), np.float32)
@@ -85,10 +85,10 @@ def test_every_code_is_read_as_its_value():
                                k_scale=to_dev(ks, "f32"), v_scale=to_dev(vs, "f32"))
     torch.cuda.synchronize()
     got = bf16_bits_of(out)
-    codes = oint4.unpack_int4(vc, axis=2)               # [NB, Hkv, D, bs]
+    codes = oint4.unpack_int4(vc, axis=3)               # [NB, Hkv, bs/4, D, 4]
     for b in range(3):
         for h in range(H):
-            mean = codes[tables[b, 0], h // (H // Hkv)].astype(np.float64).sum(axis=1) / L
+            mean = codes[tables[b, 0], h // (H // Hkv)].astype(np.float64).sum(axis=(0, 2)) / L
             want = workloads.bf16_bits(mean.astype(np.float32))
             assert np.array_equal(got[b, h], want), (b, h)
 
@@ -103,7 +103,7 @@ def test_random_bytes_every_code(G, D, bs):
     w = workloads.make_custom(40 + G, lens, H, Hkv, D, bs, kv_dtype="i4")
     NB = w.num_blocks
     kc = rng.integers(0, 256, size=(NB, Hkv, bs, D // 2)).astype(np.uint8)
-    vc = rng.integers(0, 256, size=(NB, Hkv, D // 2, bs)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(NB, Hkv, bs // 4, D // 2, 4)).astype(np.uint8)
     ks = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
     vs = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
     ref = oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, H, Hkv, D,
@@ -132,8 +132,8 @@ def test_offsets_cancel_with_one_signed_query():
     NB = w.num_blocks
     kc = rng.integers(0, 256, size=(NB, Hkv, bs, D // 2)).astype(np.uint8)
     # V nibbles 0 .. 7 only (codes >= 0)
-    vc = (rng.integers(0, 8, size=(NB, Hkv, D // 2, bs)) |
-          (rng.integers(0, 8, size=(NB, Hkv, D // 2, bs)) << 4)).astype(np.uint8)
+    vc = (rng.integers(0, 8, size=(NB, Hkv, bs // 4, D // 2, 4)) |
+          (rng.integers(0, 8, size=(NB, Hkv, bs // 4, D // 2, 4)) << 4)).astype(np.uint8)
     ks = rng.uniform(0.002, 0.01, size=(NB, Hkv, bs)).astype(np.float32)
     vs = rng.uniform(0.5, 2.0, size=(NB, Hkv, bs)).astype(np.float32)
     ref = oracle.decode_attention(w.q, kc, vc, w.block_tables, w.context_lens, w.scale, H, Hkv, D,
@@ -149,7 +149,7 @@ def test_offsets_cancel_with_one_signed_query():
 
 def _random_int4_caches(rng, NB, Hkv, D, bs):
     kc = rng.integers(0, 256, size=(NB, Hkv, bs, D // 2)).astype(np.uint8)
-    vc = rng.integers(0, 256, size=(NB, Hkv, D // 2, bs)).astype(np.uint8)
+    vc = rng.integers(0, 256, size=(NB, Hkv, bs // 4, D // 2, 4)).astype(np.uint8)
     ks = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
     vs = rng.uniform(0.05, 0.4, size=(NB, Hkv, bs)).astype(np.float32)
     return kc, vc, ks, vs

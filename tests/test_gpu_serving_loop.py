@@ -33,7 +33,7 @@ def test_block_manager_decode_loop(G, bs):
     scale = 1 / np.sqrt(D)
     bm = pkv.BlockManager(NB, bs, order=rng.permutation(NB))
     kc_np = np.full((NB, Hkv, bs, D), workloads.BF16_NAN, np.uint16)
-    vc_np = np.full((NB, Hkv, D, bs), workloads.BF16_NAN, np.uint16)
+    vc_np = np.full((NB, Hkv, bs // 4, D, 4), workloads.BF16_NAN, np.uint16)
     kc, vc = to_dev(kc_np, "bf16"), to_dev(vc_np, "bf16")
 
     def rows(n):
@@ -44,7 +44,8 @@ def test_block_manager_decode_loop(G, bs):
         for src, dst, nrows in copies:
             pkv.copy_blocks((kc, vc), (kc, vc), torch.tensor([[src, dst]], dtype=torch.int32, device=DEV))
             kc_np[dst, :, :nrows] = kc_np[src, :, :nrows]
-            vc_np[dst, :, :, :nrows] = vc_np[src, :, :, :nrows]
+            for r in range(nrows):
+                vc_np[dst, :, r // 4, :, r % 4] = vc_np[src, :, r // 4, :, r % 4]
 
     def prefill(sid, n):
         nonlocal kc_np, vc_np
@@ -103,4 +104,5 @@ def test_block_manager_decode_loop(G, bs):
         for j, blk in enumerate(bm.block_table(s)):
             n = min(bs, L - j * bs)
             assert np.array_equal(dk[blk, :, :n], kc_np[blk, :, :n])
-            assert np.array_equal(dv[blk, :, :, :n], vc_np[blk, :, :, :n])
+            for r in range(n):
+                assert np.array_equal(dv[blk, :, r // 4, :, r % 4], vc_np[blk, :, r // 4, :, r % 4])

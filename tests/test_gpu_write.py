@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 def _pool(rng, NB, Hkv, bs, D, kind):
     k = rng.standard_normal((NB, Hkv, bs, D), dtype=np.float32)
-    v = rng.standard_normal((NB, Hkv, D, bs), dtype=np.float32)
+    v = rng.standard_normal((NB, Hkv, bs // 4, D, 4), dtype=np.float32)
     if kind == "bf16":
         return workloads.bf16_bits(k), workloads.bf16_bits(v)
     return k, v
@@ -77,7 +77,7 @@ def test_write_bulk_7b_fill():
     v = workloads.bf16_bits(rng.standard_normal((T, Hkv, D), dtype=np.float32))
     slots = rng.permutation(NB * bs)[:T].astype(np.int64)
     kc = np.full((NB, Hkv, bs, D), workloads.BF16_NAN, np.uint16)
-    vc = np.full((NB, Hkv, D, bs), workloads.BF16_NAN, np.uint16)
+    vc = np.full((NB, Hkv, bs // 4, D, 4), workloads.BF16_NAN, np.uint16)
     ref_k, ref_v = ocache.cache_write(k, v, kc, vc, slots, bs)
     dk, dv = to_dev(kc, "bf16"), to_dev(vc, "bf16")
     pkv.kv_cache_write(to_dev(k, "bf16"), to_dev(v, "bf16"), dk, dv, torch.from_numpy(slots).to(DEV))
@@ -107,7 +107,7 @@ def test_write_int8_bitexact(D, bs):
     slots = rng.choice(NB * bs, size=T, replace=False).astype(np.int64)
     slots[10:20] = -3
     kc = np.zeros((NB, Hkv, bs, D), np.int8)
-    vc = np.zeros((NB, Hkv, D, bs), np.int8)
+    vc = np.zeros((NB, Hkv, bs // 4, D, 4), np.int8)
     ks = np.full((NB, Hkv, bs), np.nan, np.float32)
     vs = np.full((NB, Hkv, bs), np.nan, np.float32)
     rk, rv, rks, rvs = ocache.cache_write_int8(k, v, kc, vc, ks, vs, slots, bs)
@@ -124,7 +124,7 @@ def test_write_int8_bitexact(D, bs):
 
 def test_write_zero_tokens_noop():
     dk = torch.zeros((4, 2, 16, 64), dtype=torch.bfloat16, device=DEV)
-    dv = torch.zeros((4, 2, 64, 16), dtype=torch.bfloat16, device=DEV)
+    dv = torch.zeros((4, 2, 4, 64, 4), dtype=torch.bfloat16, device=DEV)
     e = torch.empty((0, 2, 64), dtype=torch.bfloat16, device=DEV)
     pkv.kv_cache_write(e, e, dk, dv, torch.empty(0, dtype=torch.int64, device=DEV))
     torch.cuda.synchronize()
@@ -184,7 +184,7 @@ def test_write_codes_prefill_order_bitexact(kv, D, bs, bulk):
     v = (rng.standard_normal((T, Hkv, D)) * np.exp(rng.uniform(-5, 5, (T, Hkv, 1)))).astype(np.float32)
     W = D // 2 if kv == "i4" else D
     kc = np.full((NB, Hkv, bs, W), 0x5A, np.uint8)
-    vc = np.full((NB, Hkv, W, bs), 0x5A, np.uint8)
+    vc = np.full((NB, Hkv, bs // 4, W, 4), 0x5A, np.uint8)
     ks = np.full((NB, Hkv, bs), np.nan, np.float32)
     vs = np.full((NB, Hkv, bs), np.nan, np.float32)
     write = {"i8": ocache.cache_write_int8, "fp8": ofp8.cache_write_fp8,

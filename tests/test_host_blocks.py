@@ -74,7 +74,7 @@ def test_waste_at_most_one_partial_block():
 def test_config_shapes_small():
     w = workloads.make_config(1, 0)
     assert list(w.context_lens) == [47, 200, 16, 1]
-    assert w.k_cache.shape == (32, 4, 16, 64) and w.v_cache.shape == (32, 4, 64, 16)
+    assert w.k_cache.shape == (32, 4, 16, 64) and w.v_cache.shape == (32, 4, 4, 64, 4)
     used = w.block_tables[w.block_tables >= 0]
     assert len(used) == 18 and len(set(used.tolist())) == 18
     assert w.scale == 1.0 / 8.0
@@ -96,7 +96,7 @@ def test_poison_covers_unused_rows_and_new_slots():
     for blk in range(w.num_blocks):
         for r in range(bs):
             assert np.isnan(w.k_cache[blk, :, r, :]).all() == (not valid[blk, r])
-            assert np.isnan(w.v_cache[blk, :, :, r]).all() == (not valid[blk, r])
+            assert np.isnan(w.v_cache[blk, :, r // 4, :, r % 4]).all() == (not valid[blk, r])
     for b, L in enumerate(w.context_lens):
         t = int(L) - 1
         assert w.slot_new[b] == w.block_tables[b][t // bs] * bs + t % bs

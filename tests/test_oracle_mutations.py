@@ -27,7 +27,8 @@ def _gather_table_off_by_one(k_cache, v_cache, block_table, context_len, block_s
         rows = oatt.rows_in_block(L, bs, j)
         blk = int(block_table[min(j + 1, len(block_table) - 1)])
         K[j * bs:j * bs + rows] = oatt.widen(k_cache[blk, kv_head, :rows, :], kv_dtype)
-        V[j * bs:j * bs + rows] = oatt.widen(v_cache[blk, kv_head, :, :rows], kv_dtype).T
+        v_tok = np.swapaxes(v_cache[blk, kv_head], 1, 2).reshape(bs, D)[:rows]
+        V[j * bs:j * bs + rows] = oatt.widen(v_tok, kv_dtype)
     return K, V
 
 
@@ -45,13 +46,31 @@ def _gather_v_rows_as_columns(k_cache, v_cache, block_table, context_len, block_
     K, _ = _orig_gather(k_cache, v_cache, block_table, context_len, block_size, kv_head,
                         kv_dtype, k_scale, v_scale)
     L, bs = int(context_len), int(block_size)
-    D = v_cache.shape[2]
+    D = v_cache.shape[3]
     V = np.zeros((L, D))
     for j in range(oatt.n_blocks(L, bs)):
         rows = oatt.rows_in_block(L, bs, j)
         blk = int(block_table[j])
         flat = oatt.widen(v_cache[blk, kv_head], kv_dtype).reshape(-1)   # [D * bs]
         V[j * bs:j * bs + rows] = flat.reshape(bs, D)[:rows]
+    return K, V
+
+
+def _gather_v_group_index_swapped(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                                  kv_dtype, k_scale=None, v_scale=None):
+    # reads token r of a V tile at [r % (bs/4), :, r // (bs/4)]: the group and
+    # in-group indices exchanged
+    K, _ = _orig_gather(k_cache, v_cache, block_table, context_len, block_size, kv_head,
+                        kv_dtype, k_scale, v_scale)
+    L, bs = int(context_len), int(block_size)
+    D = v_cache.shape[3]
+    V = np.zeros((L, D))
+    for j in range(oatt.n_blocks(L, bs)):
+        rows = oatt.rows_in_block(L, bs, j)
+        blk = int(block_table[j])
+        tile = v_cache[blk, kv_head]
+        for r in range(rows):
+            V[j * bs + r] = oatt.widen(tile[r % (bs // 4), :, r // (bs // 4)], kv_dtype)
     return K, V
 
 
@@ -263,6 +282,7 @@ MUTATIONS = {
     "block_count_floor": [(oatt, "n_blocks", lambda L, bs: int(L) // int(bs))],
     "block_table_off_by_one": [(oatt, "gather_kv", _gather_table_off_by_one)],
     "v_tile_read_token_major": [(oatt, "gather_kv", _gather_v_rows_as_columns)],
+    "v_group_index_swapped": [(oatt, "gather_kv", _gather_v_group_index_swapped)],
     "int8_v_scale_dropped": [(oatt, "gather_kv", _gather_no_v_scale)],
     "scale_dropped": [(oatt, "attend_one", _attend_no_scale)],
     "normalised_by_length": [(oatt, "attend_one", _attend_mean_norm)],

@@ -84,7 +84,7 @@ def test_noalloc_refuses_sizes_beyond_its_scratch():
     q = torch.zeros((B, H, D), dtype=torch.bfloat16, device=DEV)
     out = torch.full_like(q, 7.0)
     kc = torch.zeros((1, Hkv, bs, D // 2), dtype=torch.uint8, device=DEV)
-    vc = torch.zeros((1, Hkv, D // 2, bs), dtype=torch.uint8, device=DEV)
+    vc = torch.zeros((1, Hkv, bs // 4, D // 2, 4), dtype=torch.uint8, device=DEV)
     ks = torch.zeros((1, Hkv, bs), dtype=torch.float32, device=DEV)
     vs = torch.zeros_like(ks)
     bt = torch.zeros((B, MB), dtype=torch.int32, device=DEV)
