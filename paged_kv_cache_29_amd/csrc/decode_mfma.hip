@@ -625,6 +625,12 @@ void decode_mfma_kernel(DecodeParams p) {
       const int bb = base + lane;
       const int Lb = bb < B ? max(p.context_lens[bb], 0) : 0;
       C += readlane64(wave_incl_scan((Lb + 31) >> 5), kWave - 1);
+      // an empty context is in no share: the unit records of sequence bb
+      // say so ({0, 0}: zero output), written by one workgroup of the grid
+      if (wave == 0 && bb < B && Lb == 0 && bb % static_cast<int>(gridDim.x) == static_cast<int>(blockIdx.x)) {
+        for (int kv = 0; kv < Hkv; ++kv)
+          *reinterpret_cast<int2*>(p.ws_unit + 2 * (static_cast<size_t>(bb) * Hkv + kv)) = int2{0, 0};
+      }
     }
     C *= Hkv;
     // shares: at least kMinShareChunks chunks each, at most one per

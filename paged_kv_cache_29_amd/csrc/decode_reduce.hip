@@ -34,32 +34,12 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
   if (bh >= (mq ? p.num_query_rows : p.num_seqs) * p.num_heads) return;  // the whole wave
   const int b = mq ? range_of(p.query_start, p.num_seqs, bh / p.num_heads) : bh / p.num_heads;
   const int L = p.context_lens[b];
-  // Partials i = 0 .. nparts-1 live in workspace rows idx(i): partitions of
-  // the context, or (cascade) npre shared-prefix partitions in slots
+  // Partials i = 0 .. nparts-1 live in workspace rows slot(i): partitions
+  // of the context, or (cascade) npre shared-prefix partitions in slots
   // 0 .. npre-1 followed by the partitions of the rest of the context from
-  // slot prefix_parts on, or (balanced shares) the share slots the unit's
-  // first workgroup recorded.
+  // slot prefix_parts on.
   int npre = 0, nparts, skip = 0;
-  int slot0 = 0, gh = 0;  // balanced: first slot of the unit; head within its group
-  if (p.bal_shares > 0) {
-    if (L <= 0) {  // empty context: no share attended it
-      for (int k = lane; k < D; k += kWave) {
-        const size_t idx = static_cast<size_t>(bh) * D + k;
-        if constexpr (kOutBf16)
-          static_cast<uint16_t*>(p.out)[idx] = 0;
-        else
-          static_cast<float*>(p.out)[idx] = 0.f;
-      }
-      return;
-    }
-    const int G = p.num_heads / p.num_kv_heads;
-    const int h = bh - b * p.num_heads;
-    gh = h % G;
-    const int2 u = *reinterpret_cast<const int2*>(p.ws_unit + 2 * (static_cast<size_t>(b) * p.num_kv_heads + h / G));
-    slot0 = __builtin_amdgcn_readfirstlane(u.x);
-    nparts = __builtin_amdgcn_readfirstlane(u.y);
-    if (nparts <= 1) return;  // written whole by the partition kernel
-  } else if (p.group_start != nullptr) {
+  if (p.group_start != nullptr) {  } else if (p.group_start != nullptr) {
     const int S = group_shared_tokens(p, group_of(p, b));
     npre = (S + p.prefix_part_tokens - 1) / p.prefix_part_tokens;
     nparts = npre + (L > S ? (L - S + p.part_tokens - 1) / p.part_tokens : 0);
@@ -82,14 +62,9 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
     nparts = (L + p.part_tokens - 1) / p.part_tokens;
     if (nparts <= 1) return;  // written by the partition kernel
   }
-  const bool bal = p.bal_shares > 0;
-  const int G = p.num_heads / p.num_kv_heads;
   const size_t base = static_cast<size_t>(bh) * p.num_parts;
   // workspace row (of ws_m / ws_l, and of D floats in ws_acc) of partial i
-  auto slot = [&](int i) -> size_t {
-    if (bal) return static_cast<size_t>(i == 0 ? slot0 : 2 * ((slot0 >> 1) + i)) * G + gh;
-    return base + (i < npre ? i : i + skip);
-  };
+  auto slot = [&](int i) -> size_t { return base + (i < npre ? i : i + skip); };
   const float* m = p.ws_m;
   const float* l = p.ws_l;
   const float* row = p.ws_acc + lane;
@@ -156,8 +131,108 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
   }
 }
 
+// Balanced shares: one wave per (sequence, kv-head) unit.  The unit's
+// record {first slot, splits} says where its partials are (split j >= 1 in
+// slot 2 (first / 2 + j)); 1 split: written whole by the partition kernel;
+// 0: an empty context, zero output.  The wave serves all G heads of the
+// unit: 64 / G lanes per head, each owning DPL = D G / 64 consecutive dims,
+// so a unit that needs nothing costs one load.  The splits' maxima are
+// loaded 8 at a time, then their rows in batches, all loads of a batch
+// issued before any is used.  (Balanced shares serve bf16 queries only, so
+// the output is bf16.)
+template <int D, int G>
+__global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_units_kernel(DecodeParams p) {
+  constexpr int LPH = kWave / G;  // lanes per head
+  constexpr int DPL = D / LPH;    // dims per lane
+  constexpr int NV = (DPL + 3) / 4;  // f32x4 (or shorter) pieces per row
+  constexpr int NBATCH = DPL >= 32 ? 2 : (DPL >= 16 ? 4 : 8);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int u = __builtin_amdgcn_readfirstlane(blockIdx.x * kReduceWaves + (threadIdx.x >> 6));
+  if (u >= p.num_seqs * p.num_kv_heads) return;  // the whole wave
+  const int2 rec = *reinterpret_cast<const int2*>(p.ws_unit + 2 * static_cast<size_t>(u));
+  const int first = __builtin_amdgcn_readfirstlane(rec.x);
+  const int nsplit = __builtin_amdgcn_readfirstlane(rec.y);
+  if (nsplit == 1) return;
+  const int gh = lane / LPH;  // head within the group
+  const int d0 = (lane % LPH) * DPL;
+  uint16_t* orow = static_cast<uint16_t*>(p.out) + (static_cast<size_t>(u) * G + gh) * D + d0;  // row b * H + h
+  if (nsplit <= 0) {  // empty context
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) orow[k] = 0;
+    return;
+  }
+  auto slot = [&](int j) -> size_t {
+    return static_cast<size_t>(j == 0 ? first : 2 * ((first >> 1) + j)) * G + gh;
+  };
+  auto load_row = [&](size_t r, float (&x)[NV * 4]) {
+    const float* a = p.ws_acc + r * D + d0;
+    if constexpr (DPL % 4 == 0) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(a + 4 * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * v + e] = w[e];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) x[k] = a[k];
+    }
+  };
+  float M = -INFINITY;
+  for (int j0 = 0; j0 < nsplit; j0 += 8) {
+    float mm[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) mm[q] = p.ws_m[slot(min(j0 + q, nsplit - 1))];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) M = fmaxf(M, mm[q]);
+  }
+  float num[NV * 4];
+#pragma unroll
+  for (int k = 0; k < NV * 4; ++k) num[k] = 0.f;
+  float den = 0.f;
+  for (int j0 = 0; j0 < nsplit; j0 += NBATCH) {
+    float x[NBATCH][NV * 4];
+    float mj[NBATCH], lj[NBATCH];
+#pragma unroll
+    for (int q = 0; q < NBATCH; ++q) {
+      const size_t r = slot(min(j0 + q, nsplit - 1));  // past the last split: weight 0 below
+      mj[q] = p.ws_m[r];
+      lj[q] = p.ws_l[r];
+      load_row(r, x[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < NBATCH; ++q) {
+      const float w = (j0 + q < nsplit) ? exp2f(mj[q] - M) : 0.f;
+      den = fmaf(w, lj[q], den);
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) num[k] = fmaf(w, x[q][k], num[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) orow[k] = f32_to_bf16(num[k] / den);
+}
+
+template <int D, int G>
+void launch_units(const DecodeParams& p, hipStream_t s) {
+  const int64_t waves = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads;
+  const dim3 grid(static_cast<unsigned>((waves + kReduceWaves - 1) / kReduceWaves));
+  hipLaunchKernelGGL((decode_reduce_units_kernel<D, G>), grid, dim3(kReduceWaves * kWave), 0, s, p);
+}
+
 template <int D>
 hipError_t launch_t(const DecodeParams& p, bool out_bf16, hipStream_t s) {
+  if (p.bal_shares > 0) {
+    if (!out_bf16) return hipErrorInvalidValue;  // balanced shares take bf16 queries only
+    switch (p.num_heads / p.num_kv_heads) {
+      case 1: launch_units<D, 1>(p, s); break;
+      case 2: launch_units<D, 2>(p, s); break;
+      case 4: launch_units<D, 4>(p, s); break;
+      case 8: launch_units<D, 8>(p, s); break;
+      case 16: launch_units<D, 16>(p, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const int rows = p.query_start != nullptr ? p.num_query_rows : p.num_seqs;
   const int64_t waves = static_cast<int64_t>(rows) * p.num_heads;
   const dim3 grid(static_cast<unsigned>((waves + kReduceWaves - 1) / kReduceWaves));
