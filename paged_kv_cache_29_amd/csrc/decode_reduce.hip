@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
   // 0 .. npre-1 followed by the partitions of the rest of the context from
   // slot prefix_parts on.
   int npre = 0, nparts, skip = 0;
-  if (p.group_start != nullptr) {  } else if (p.group_start != nullptr) {
+  if (p.group_start != nullptr) {
     const int S = group_shared_tokens(p, group_of(p, b));
     npre = (S + p.prefix_part_tokens - 1) / p.prefix_part_tokens;
     nparts = npre + (L > S ? (L - S + p.part_tokens - 1) / p.part_tokens : 0);
