@@ -118,7 +118,13 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
 // the last segment of each share it touches, so its partials go to that
 // share's two slots (2s, 2s + 1), and the workgroup holding its first chunk
 // records where they are ({first slot, count} in ws_unit) for the reduce.
-template <KvKind KV, int D, int BS, int W, bool kMQ, int NT, bool kBal>
+// kVec: one query head per kv-head (MHA), bf16.  A single column would use
+// 1 of the 16 of every matrix-core tile, so the contractions run on the
+// vector ALUs instead, over the same loaded chunk: lane (c, g) takes the
+// dot product of its 32 dims of token c of each sub-tile (v_dot2c_f32_bf16,
+// summed over the 4 lane groups), and for PV fetches the probabilities of
+// its V tokens 4g .. 4g+3 from the lanes that scored them (ds_bpermute).
+template <KvKind KV, int D, int BS, int W, bool kMQ, int NT, bool kBal, bool kVec = false>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, NT>, kWavesPerSimd<KV, NT>)))
 void decode_mfma_kernel(DecodeParams p) {
@@ -128,6 +134,7 @@ void decode_mfma_kernel(DecodeParams p) {
   using LoaderT = typename std::conditional<kI4, ChunkLoaderI4<D, BS>, ChunkLoader<kInt8, D, BS>>::type;
   static_assert(NT >= 1 && NT <= kMqDecodeMaxTiles && (kMQ || NT == 1), "column tiles");
   static_assert(!(kBal && kMQ), "balanced shares are a one-query mode");
+  static_assert(!kVec || (KV == KvKind::BF16 && NT == 1 && !kMQ), "vector-ALU path: bf16, one head");
   // the registers of the extra tiles' states replace the second chunk
   constexpr int NB = NT > 1 ? 1 : kBatch<KV>;
   static_assert(D == 64 || D == 128, "head_dim");
@@ -182,9 +189,10 @@ void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int col = 16 * (tile0 + t) + c;
+      // (vector-ALU path: every lane holds the one head's dims)
       const size_t qr = kMQ ? (static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G)
-                            : (static_cast<size_t>(b) * H + h0 + c);
-      const bool qvalid = kMQ ? (col < ncol) : (c < G);
+                            : (static_cast<size_t>(b) * H + h0 + (kVec ? 0 : c));
+      const bool qvalid = kMQ ? (col < ncol) : (kVec || c < G);
       const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + qr * D;
       k_off[t] = 0.f;
 #pragma unroll
@@ -212,6 +220,11 @@ void decode_mfma_kernel(DecodeParams p) {
     float m_run[NT], l_run[NT];
     float pv_run[NT];  // INT4: sum_t p_t v_scale_t (this lane's tokens)
     f32x4 acc[NT][NN];
+    // vector-ALU path: dims 32k + 2c + o (n = 2k + o) over the lane
+    // group's tokens
+    float vacc[kVec ? NN : 1];
+#pragma unroll
+    for (int n = 0; n < (kVec ? NN : 1); ++n) vacc[n] = 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       m_run[t] = -INFINITY;
@@ -262,6 +275,66 @@ void decode_mfma_kernel(DecodeParams p) {
       auto consume = [&](const ChunkT& cw, int ch, auto masked) {
         constexpr bool kMasked = decltype(masked)::value;
         const int t0 = pb + ch * 32;
+        if constexpr (kVec) {
+          // ---- scores of chunk tokens 16h + c (every lane group holds all)
+          float sc[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float a = 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+              const u32x4 qw = __builtin_bit_cast(u32x4, qf[0][j]);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) a = dot2_bf16(cw.k[h][j][w], qw[w], a);
+            }
+            sc[h] = groups_sum(a) * p.scale_log2;
+          }
+          const bool past_end = kMasked && (t0 + 32) > t_end;
+          if (past_end) {  // select, never multiply: masked rows may hold NaN
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              if (t0 + 16 * h + c >= t_end) sc[h] = -INFINITY;
+          }
+          // ---- online softmax: every row of 16 lanes holds the chunk's 32
+          // scores, so the maximum and the state are uniform
+          const float m_new = fmaxf(m_run[0], row16_max(fmaxf(sc[0], sc[1])));
+          if (m_new > m_run[0]) {
+            const float alpha = fast_exp2(m_run[0] - m_new);
+            l_run[0] *= alpha;
+#pragma unroll
+            for (int n = 0; n < NN; ++n) vacc[n] *= alpha;
+            m_run[0] = m_new;
+          }
+          float pr[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) pr[h] = fast_exp2(sc[h] - m_run[0]);
+          l_run[0] += pr[0] + pr[1];  // summed over the row at the end
+          // ---- PV: probabilities of sub-tile tokens 4g + i (lane 20g + i
+          // scored them), as bf16 hi + lo pairs as in the matrix-core path
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float pt[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pt[i] = lane_get(pr[h], 20 * g + i);
+            const uint32_t h01 = pack_bf16x2(pt[0], pt[1]), h23 = pack_bf16x2(pt[2], pt[3]);
+            const uint32_t l01 = pack_bf16x2(pt[0] - bf16_lo(h01), pt[1] - bf16_hi(h01));
+            const uint32_t l23 = pack_bf16x2(pt[2] - bf16_lo(h23), pt[3] - bf16_hi(h23));
+#pragma unroll
+            for (int n = 0; n < NN; ++n) {
+              u32x2 v = cw.v[h][n];
+              if (past_end) {  // masked tokens contribute exact zeros, even over NaN
+                v.x = mask_pair(v.x, t0 + 16 * h + 4 * g, t_end);
+                v.y = mask_pair(v.y, t0 + 16 * h + 4 * g + 2, t_end);
+              }
+              float a = vacc[n];
+              a = dot2_bf16(v.x, h01, a);
+              a = dot2_bf16(v.x, l01, a);
+              a = dot2_bf16(v.y, h23, a);
+              vacc[n] = dot2_bf16(v.y, l23, a);
+            }
+          }
+          return;
+        }
         // ---- scores: S^T of sub-tiles h = 0, 1 for every column tile; each K
         // operand is widened once and feeds the tiles' contractions
         f32x4 s[NT][2];
@@ -478,11 +551,24 @@ void decode_mfma_kernel(DecodeParams p) {
       }
     }
 
+    if constexpr (kVec) {
+      // to the matrix-core path's state: the sum over a row of lanes; the
+      // output dims summed over the lane groups and moved to the
+      // accumulator layout (element i of tile n = 2k + o in lane (c, g): dim
+      // 32k + 8g + 2i + o, i.e. column 4g + i here)
+      l_run[0] = row16_sum(l_run[0]);
+#pragma unroll
+      for (int n = 0; n < NN; ++n) {
+        const float v = groups_sum(vacc[n]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[0][n][i] = lane_get(v, 4 * g + i);
+      }
+    }
     // per-column sums over the 4 lane groups (each holds different tokens)
     float M[NT], Lsum[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      l_run[t] = groups_sum(l_run[t]);
+      if constexpr (!kVec) l_run[t] = groups_sum(l_run[t]);
       if constexpr (kI4) {  // remove the V offset of this wave's tokens
         const float v_off = kInt4Offset * groups_sum(pv_run[t]);
 #pragma unroll
@@ -753,6 +839,8 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   const int parts = p.group_start != nullptr ? p.num_parts - p.prefix_parts : p.num_parts;
   const unsigned units = static_cast<unsigned>(p.num_seqs * p.num_kv_heads);
   const dim3 block(kDecodeWaves * kWave);
+  // one head per kv-head, bf16: the vector-ALU contractions
+  const bool vec = KV == KvKind::BF16 && p.num_heads == p.num_kv_heads;
   if constexpr (kMQ) {
     if (p.mq_tiles < 1 || p.mq_tiles > kMqDecodeMaxTiles) return hipErrorInvalidValue;
     // (sequence, kv-head) units padded to whole groups of 8, x tile groups
@@ -779,10 +867,22 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
       return hipErrorInvalidValue;
     } else {
       const dim3 grid(static_cast<unsigned>(p.bal_shares));
+      if constexpr (KV == KvKind::BF16) {
+        if (vec) {
+          hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, true, true>), grid, block, 0, s, p);
+          return hipGetLastError();
+        }
+      }
       hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, true>), grid, block, 0, s, p);
     }
   } else {
     const dim3 grid(units, static_cast<unsigned>(parts));
+    if constexpr (KV == KvKind::BF16) {
+      if (vec) {
+        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, false, true>), grid, block, 0, s, p);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();

@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -42,6 +43,36 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// c + a.lo * b.lo + a.hi * b.hi over packed bf16 pairs (v_dot2c_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Max / sum over the 16 lanes of each row (lanes 16 r .. 16 r + 15), the
+// result in all of them: quad swaps, then the mirror inside each half row,
+// then the mirror of the row (DPP moves, no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm(1, 0, 3, 2)
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm(2, 3, 0, 1)
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  return fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  return v + dpp_f32<0x140>(v);
+}
+
+// Value of v in lane `src` (any lane of the wave), per lane.
+__device__ __forceinline__ float lane_get(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src * 4, __float_as_int(v)));
+}
 
 // Symmetric integer code of x for a row scale s = absmax / MAXC (IEEE fp32
 // division, round half to even, clamp to +-MAXC); s == 0 means an all-zero

@@ -45,7 +45,7 @@ def _log_uniform(seed, n, lo, hi):
 
 
 @pytest.mark.parametrize("kv", KINDS)
-@pytest.mark.parametrize("G,D,bs", [(1, 128, 16), (8, 128, 16), (4, 64, 32), (16, 128, 32), (2, 64, 16)])
+@pytest.mark.parametrize("G,D,bs", [(1, 128, 16), (1, 64, 32), (8, 128, 16), (4, 64, 32), (16, 128, 32), (2, 64, 16)])
 def test_balanced_ragged(kv, G, D, bs):
     Hkv = 2
     lens = [0] + _log_uniform(G + D + bs, 10, 1, 6000) + [0, 33, 2049, 0]
