@@ -269,7 +269,7 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
                                                     nbytes, ms_per_step)
     if w.meta.get("prefix"):
         res["cascade"] = run_cascade(w, args, torch, pkv, loop_time, write, out, q, kc, vc, bt, cl,
-                                     ks, vs, nbytes, uniq, ms_per_step)
+                                     ks, vs, nbytes, uniq, ms_per_step, k_new, v_new)
     res["bulk_fill"] = fill
     res["_w"] = w
     return res
@@ -341,10 +341,12 @@ def run_multi_query(w, args, torch, pkv, loop_time, q, kc, vc, bt, cl, nbytes, m
 
 
 def run_cascade(w, args, torch, pkv, loop_time, write, out, q, kc, vc, bt, cl, ks, vs, nbytes,
-                uniq, ms_fused):
-    """The same step with the shared blocks attended once per group: cache
-    write, then paged_attention_decode_cascade (prefix kernel, partition
-    kernel over each sequence's own tokens, reduce)."""
+                uniq, ms_fused, k_new, v_new):
+    """The same step with the shared blocks attended once per group: the
+    fused cascade step (one launch attends the shared blocks once per group
+    and each sequence's own tokens, writing its new token first; then the
+    reduce), and for reference the cache write followed by the plain cascade
+    call."""
     from paged_kv_cache_29_amd import blocks
     gs, gsb, mg, msb = blocks.cascade_groups(w.block_tables, w.context_lens, w.block_size)
     dev = q.device
@@ -354,19 +356,22 @@ def run_cascade(w, args, torch, pkv, loop_time, write, out, q, kc, vc, bt, cl, k
                                       args.partition_tokens, 0)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
 
-    def cascade():
+    def cascade(fused=False):
         pkv.paged_attention_decode_cascade(out, q, kc, vc, bt, cl, gs_d, gsb_d, w.scale,
                                            w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
                                            mg, msb, k_scale=ks, v_scale=vs,
-                                           partition_tokens=args.partition_tokens, workspace=ws)
+                                           partition_tokens=args.partition_tokens, workspace=ws,
+                                           k_new=k_new if fused else None, v_new=v_new if fused else None)
 
-    def step():
+    def unfused():
         write()
         cascade()
 
-    us = loop_time(step)
+    us = loop_time(lambda: cascade(True))
+    us_unfused = loop_time(unfused)
     us_attn = loop_time(cascade)
-    return {"us_per_step": us, "logical_kv_gbs": nbytes / (us * 1e-6) / 1e9,
+    return {"us_per_step": us, "us_per_step_write_then_cascade": us_unfused,
+            "logical_kv_gbs": nbytes / (us * 1e-6) / 1e9,
             "unique_gbs": uniq / (us * 1e-6) / 1e9,
             "frac_hbm_unique": uniq / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "attention_us": us_attn,

@@ -374,8 +374,35 @@ pkv_status pkv_paged_attention_decode_cascade(
     int32_t prefix_partition_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Workspace bytes of pkv_paged_attention_decode_cascade for these sizes
- * (0 for invalid sizes, or num_seqs == 0).
+ * Fused shared-prefix decode step: append each sequence's new token, then
+ * attend as pkv_paged_attention_decode_cascade.
+ *   The token at position L - 1 of every sequence with L = context_lens[b]
+ *   >= 1 receives k_new[b][h][:] and v_new[b][h][:] exactly as in
+ *   pkv_paged_attention_decode_step (same formats: [B][Hkv][D], the cache
+ *   element type, fp32 for a coded cache), and out is then computed as by
+ *   pkv_paged_attention_decode_cascade over the updated cache: the
+ *   workgroups that attend a sequence's own tokens write its token first.
+ *   out and the caches equal those of the write followed by the cascade
+ *   call, bit for bit.
+ *   The new token must lie past its group's shared span (L - 1 >= S_g, in
+ *   a block of this sequence alone): shared blocks are never written.  A
+ *   block manager that copies a shared tail block on write gives every
+ *   sequence such a block; PKV_DEBUG=1 checks it.
+ *   Other arguments, errors and the workspace as for
+ *   pkv_paged_attention_decode_cascade; the caches (and scales) are written.
+ */
+pkv_status pkv_paged_attention_decode_cascade_step(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    float* k_scale, float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* group_start, const int32_t* group_shared_blocks, float scale, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t max_shared_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t partition_tokens,
+    int32_t prefix_partition_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes of pkv_paged_attention_decode_cascade (and of the fused
+ * step) for these sizes (0 for invalid sizes, or num_seqs == 0).
  */
 size_t pkv_paged_attention_cascade_workspace_size(
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

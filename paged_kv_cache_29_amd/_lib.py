@@ -65,6 +65,10 @@ SIGNATURES = {
     "pkv_paged_attention_decode_cascade": (c_i32, _DECODE_ARGS[:8] + [c_vp, c_vp] + _DECODE_ARGS[8:16]
                                            + [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                               c_vp, c_size, c_vp]),
+    "pkv_paged_attention_decode_cascade_step": (c_i32, _DECODE_ARGS[:2] + [c_vp, c_vp] + _DECODE_ARGS[2:8]
+                                                + [c_vp, c_vp] + _DECODE_ARGS[8:16]
+                                                + [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                                   c_vp, c_size, c_vp]),
     "pkv_paged_attention_cascade_workspace_size": (c_size, [c_i32] * 11),
     "pkv_paged_attention_multi_query": (c_i32, _DECODE_ARGS[:8] + [c_vp] + _DECODE_ARGS[8:16]
                                         + [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp]),
@@ -323,13 +327,16 @@ def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, conte
                                    num_kv_heads, head_dim, block_size, max_group_size,
                                    max_shared_blocks, k_scale=None, v_scale=None,
                                    partition_tokens=0, prefix_partition_tokens=0,
-                                   workspace=None):
+                                   workspace=None, k_new=None, v_new=None):
     """Decode attention with each group's shared blocks read once for the group.
 
     ``group_start`` (int32 ``[num_groups + 1]``) and ``group_shared_blocks``
     (int32 ``[num_groups]``) are device tensors; ``max_group_size`` and
     ``max_shared_blocks`` are host-side bounds on them (see
-    ``blocks.cascade_groups``, which computes all four from block tables)."""
+    ``blocks.cascade_groups``, which computes all four from block tables).
+    With ``k_new`` and ``v_new`` ([B, Hkv, D], as for the fused step) it is
+    the fused step: each sequence's new token is written at position L-1
+    first (``pkv_paged_attention_decode_cascade_step``)."""
     dev = q.device
     for n, t in (("group_start", group_start), ("group_shared_blocks", group_shared_blocks)):
         _dense_on(t, dev, n)
@@ -349,11 +356,22 @@ def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, conte
         _dense_on(workspace, dev, "workspace")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     # decode's arguments up to num_blocks, then the cascade's
-    st = load().pkv_paged_attention_decode_cascade(
-        *args[:8], _ptr(group_start), _ptr(group_shared_blocks), *args[8:16], G,
-        int(max_group_size), int(max_shared_blocks), args[16], args[17], args[18],
-        int(prefix_partition_tokens), _ptr(workspace), ws_bytes, args[21])
-    _check(st, "paged_attention_decode_cascade")
+    tail = (*args[8:16], G, int(max_group_size), int(max_shared_blocks), args[16], args[17], args[18],
+            int(prefix_partition_tokens), _ptr(workspace), ws_bytes, args[21])
+    groups = (_ptr(group_start), _ptr(group_shared_blocks))
+    if k_new is None and v_new is None:
+        st = load().pkv_paged_attention_decode_cascade(*args[:8], *groups, *tail)
+        _check(st, "paged_attention_decode_cascade")
+        return
+    want = torch.float32 if _DTYPES.get(k_cache.dtype) in _CODED else k_cache.dtype
+    for n, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t is not None, "the fused step needs both k_new and v_new")
+        _dense_on(t, dev, n)
+        _need(tuple(t.shape) == (B, num_kv_heads, head_dim), f"{n} must be [B, Hkv, D]")
+        _need(t.dtype == want, f"{n} must be {want}")
+    st = load().pkv_paged_attention_decode_cascade_step(*args[:2], _ptr(k_new), _ptr(v_new), *args[2:8],
+                                                        *groups, *tail)
+    _check(st, "paged_attention_decode_cascade (fused step)")
 
 
 def multi_query_workspace_size(num_seqs, num_query_tokens, max_queries_per_seq, num_heads,

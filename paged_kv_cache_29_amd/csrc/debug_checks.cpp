@@ -190,13 +190,28 @@ pkv_status debug_check_groups(const int32_t* group_start, const int32_t* group_s
                               const std::vector<int32_t>& tables, const std::vector<int32_t>& lens,
                               int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
                               int32_t num_groups, int32_t max_group_size, int32_t max_shared_blocks,
-                              hipStream_t s) {
+                              hipStream_t s, bool step) {
   std::vector<int32_t> gs, gsb;
   pkv_status st = fetch(group_start, static_cast<size_t>(num_groups) + 1, s, &gs);
   if (st == PKV_OK) st = fetch(group_shared_blocks, static_cast<size_t>(num_groups), s, &gsb);
   if (st != PKV_OK) return st;
-  return pkv_check_groups(gs.data(), gsb.data(), tables.data(), lens.data(), num_seqs, max_blocks_per_seq,
-                          block_size, num_groups, max_group_size, max_shared_blocks);
+  st = pkv_check_groups(gs.data(), gsb.data(), tables.data(), lens.data(), num_seqs, max_blocks_per_seq,
+                        block_size, num_groups, max_group_size, max_shared_blocks);
+  if (st != PKV_OK || !step) return st;
+  // the fused step writes each member's new token at L - 1: never inside
+  // the span its group shares
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int32_t lead = gs[g];
+    if (lead >= gs[g + 1]) continue;
+    const int64_t span =
+        static_cast<int64_t>(std::min(std::min(std::max(gsb[g], 0), max_shared_blocks), lens[lead] / block_size)) *
+        block_size;
+    for (int32_t b = lead; b < gs[g + 1]; ++b)
+      if (lens[b] > 0 && lens[b] - 1 < span)
+        return fail(PKV_ERR_INVALID, "sequence %d: new token at %d lies in its group's shared span of %lld tokens",
+                    b, lens[b] - 1, static_cast<long long>(span));
+  }
+  return ok();
 }
 
 }  // namespace pkv

@@ -56,6 +56,7 @@
 #include "decode_tile.hpp"
 #include "pkv_device.hpp"
 #include "pkv_kernels.hpp"
+#include "prefix_body.hpp"
 
 namespace pkv {
 namespace {
@@ -124,10 +125,41 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
 // dot product of its 32 dims of token c of each sub-tile (v_dot2c_f32_bf16,
 // summed over the 4 lane groups), and for PV fetches the probabilities of
 // its V tokens 4g .. 4g+3 from the lanes that scored them (ds_bpermute).
-template <KvKind KV, int D, int BS, int W, bool kMQ, int NT, bool kBal, bool kVec = false>
+// kPrefixNT > 0: shared-prefix decode in one launch.  Workgroups [0,
+// p.fused_prefix_wgs) attend the groups' shared tokens (prefix_body.hpp
+// with kPrefixNT query tiles per wave; block coordinates from the linear
+// index, the (group, kv-head) index fastest so that one kv-head's shared
+// blocks stay on one XCD), the rest take balanced shares of the sequences'
+// own tokens.  One launch rather than two streams: a cross-stream fork and
+// join idle the GPU for longer than running the two side by side gains,
+// and the shared-prefix workgroups, dispatched first, leave the shares to
+// fill the GPU around them.  fused_prefix_wgs is a multiple of 8, so a
+// share's XCD follows its index as in the plain balanced launch.
+template <KvKind KV, int D, int BS, int W, bool kMQ, int NT, bool kBal, bool kVec = false, int kPrefixNT = 0>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, NT>, kWavesPerSimd<KV, NT>)))
 void decode_mfma_kernel(DecodeParams p) {
+  static_assert(kPrefixNT == 0 || (!kMQ && W == kDecodeWaves), "one-launch cascade: one query per sequence");
+
+  // the workgroup's share and the number of shares (balanced mode), or its
+  // (sequence, kv-head) and partition
+  int vbid = blockIdx.x, vgrid = gridDim.x, vpart = blockIdx.y;
+  if constexpr (kPrefixNT > 0) {
+    const int np = p.fused_prefix_wgs;
+    if (vbid < np) {
+      const int px = p.num_groups * p.num_kv_heads, py = p.fused_prefix_qtiles;
+      if (vbid < px * py * p.prefix_parts)  // else padding
+        prefix_body<KV, D, BS, kPrefixNT, false>(p, vbid % px, (vbid / px) % py, vbid / (px * py));
+      return;
+    }
+    vbid -= np;
+    vgrid -= np;
+    if constexpr (!kBal) {  // fixed partitions: (sequence, kv-head) fastest
+      const int units = p.num_seqs * p.num_kv_heads;
+      vpart = vbid / units;
+      vbid -= vpart * units;
+    }
+  }
   constexpr bool kInt8 = KV != KvKind::BF16;  // codes (int8, FP8, INT4) with scales
   constexpr bool kI4 = KV == KvKind::I4;
   using ChunkT = typename std::conditional<kI4, ChunkI4<D>, Chunk<kInt8, D>>::type;
@@ -165,6 +197,10 @@ void decode_mfma_kernel(DecodeParams p) {
   // written; otherwise the partial goes to slot pslot (fixed partitions:
   // slot pslot of the (row, head)'s num_parts; balanced: share slot pslot,
   // one row per head of the group).
+  // The piece whose block ids this wave's LDS slice holds (sequence, first
+  // and end token): the next segment of a share is mostly the next kv-head
+  // of the same sequence over the same tokens, whose block ids are the same.
+  int staged_b = -1, staged_pb = -1, staged_pe = -1;
   auto run = [&](int b, int kvh, int L, int t_begin, int t_end, int tile0, int qrow0, int nnew,
                  int ncol, bool final_out, int64_t pslot) {
     const int h0 = kvh * G;
@@ -241,13 +277,16 @@ void decode_mfma_kernel(DecodeParams p) {
       const int pe = min(t_end, pb + kPiece);
       // Physical block ids of the piece, staged in this wave's LDS slice so
       // that reading them later waits on LDS traffic only, never on the K/V
-      // loads in flight.
-      {
+      // loads in flight (unless the slice holds them already).
+      if (b != staged_b || pb != staged_pb || pe != staged_pe) {
         const int nblk = (pe - pb + BS - 1) / BS;  // <= kMaxPartBlocks
         const int32_t* bt = bt_row + pb / BS;
         for (int i = lane; i < nblk; i += kWave) blk_ids[wave][i] = bt[i];
+        __builtin_amdgcn_s_waitcnt(0);  // wave-private slice: own stores only
+        staged_b = b;
+        staged_pb = pb;
+        staged_pe = pe;
       }
-      __builtin_amdgcn_s_waitcnt(0);  // wave-private slice: own stores only
 
       // Block ids of chunk `ch` of the piece (uniform).  Past the end of the
       // range the second half reuses the first block: valid memory whose rows
@@ -546,6 +585,7 @@ void decode_mfma_kernel(DecodeParams p) {
               ld.load(cb[0], blk, row0);
               consume(cb[0], c2, std::true_type{});
             }
+            break;  // the rest of this wave's chunks are done
           }
         }
       }
@@ -625,7 +665,7 @@ void decode_mfma_kernel(DecodeParams p) {
       // output row: (sequence, head), or (query row, head) in multi-query mode
       const size_t bh = kMQ ? static_cast<size_t>(qrow0 + col / G) * H + h0 + col % G
                             : static_cast<size_t>(b) * H + h0 + c;
-      const size_t slot = kBal ? static_cast<size_t>(pslot) * G + c : bh * p.num_parts + pslot;
+      const size_t slot = kBal ? static_cast<size_t>(p.bal_row0 + pslot * G + c) : bh * p.num_parts + pslot;
       // Output maps: accumulator element i of tile n in lane (c, g) is row
       // 4g + i of that tile, and the row's dim follows the V operand loads
       // (decode_tile.hpp); each lane ends up with runs of consecutive dims.
@@ -701,31 +741,69 @@ void decode_mfma_kernel(DecodeParams p) {
   };
 
   if constexpr (kBal) {
-    // ---- the workgroup's share.  Unit u = b * Hkv + kvh holds n_b =
-    // ceil(L_b / 32) chunks; sequence b's units start at chunk Hkv * P_b,
-    // P_b = sum of n over the sequences before b.  Every wave computes the
-    // same (uniform) values.
+    // ---- the workgroup's share.  Unit u = b * Hkv + kvh covers tokens
+    // [S_b, L_b) of sequence b (S_b: its group's shared tokens in cascade
+    // mode, else 0) in n_b = ceil((L_b - S_b) / 32) chunks; sequence b's
+    // units start at chunk Hkv * P_b, P_b = sum of n over the sequences
+    // before b.  The waves read the sequences in rounds of W * 64, one per
+    // lane, and combine their sums through LDS; the values stay uniform.
     const int B = p.num_seqs;
-    int64_t C = 0;  // all chunks
-    for (int base = 0; base < B; base += kWave) {
-      const int bb = base + lane;
-      const int Lb = bb < B ? max(p.context_lens[bb], 0) : 0;
-      C += readlane64(wave_incl_scan((Lb + 31) >> 5), kWave - 1);
-      // an empty context is in no share: the unit records of sequence bb
-      // say so ({0, 0}: zero output), written by one workgroup of the grid
-      if (wave == 0 && bb < B && Lb == 0 && bb % static_cast<int>(gridDim.x) == static_cast<int>(blockIdx.x)) {
+    const bool cascade = p.group_start != nullptr;
+    auto own_begin = [&](int bb) { return cascade ? group_shared_tokens(p, group_of(p, bb)) : 0; };
+    constexpr int R = W * kWave;  // sequences per round
+    __shared__ int64_t bal_wsum[W];
+    __shared__ int64_t bal_found[4];  // b, L, S, first chunk of b's units
+    // one round from sequence `base`: this lane's sequence (length, own
+    // start, chunks, chunks of the round's sequences before it) and the
+    // round's total; every wave takes part
+    struct Round {
+      int L, S, n;
+      int64_t x, tot;
+    };
+    auto round_at = [&](int base) {
+      Round r;
+      const int bb = base + wave * kWave + lane;
+      r.L = bb < B ? max(p.context_lens[bb], 0) : 0;
+      r.S = bb < B ? own_begin(bb) : 0;
+      r.n = r.L > r.S ? (r.L - r.S + 31) >> 5 : 0;
+      const int64_t incl = wave_incl_scan(r.n);
+      if (lane == kWave - 1) bal_wsum[wave] = incl;
+      __syncthreads();
+      int64_t woff = 0;
+      r.tot = 0;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const int64_t t = bal_wsum[w];
+        woff += w < wave ? t : 0;
+        r.tot += t;
+      }
+      __syncthreads();  // bal_wsum is rewritten by the next round
+      r.x = woff + incl - r.n;
+      return r;
+    };
+    Round r0{};  // the first round's (all of them when B <= R)
+    int64_t C = 0;  // chunks of all units
+    for (int base = 0; base < B; base += R) {
+      const Round r = round_at(base);
+      if (base == 0) r0 = r;
+      // a sequence without tokens of its own is in no share: its unit
+      // records say so ({0, 0}: zero output, or the shared tokens' partials
+      // alone), written by one workgroup of the grid
+      const int bb = base + wave * kWave + lane;
+      if (bb < B && r.n == 0 && bb % vgrid == vbid) {
         for (int kv = 0; kv < Hkv; ++kv)
           *reinterpret_cast<int2*>(p.ws_unit + 2 * (static_cast<size_t>(bb) * Hkv + kv)) = int2{0, 0};
       }
+      C += r.tot;
     }
     C *= Hkv;
     // shares: at least kMinShareChunks chunks each, at most one per
     // workgroup, a multiple of 8 (the XCD count) once there are 8
-    int64_t se = min(static_cast<int64_t>(gridDim.x), C / kMinShareChunks);
+    int64_t se = min(static_cast<int64_t>(vgrid), C / kMinShareChunks);
     se = max(se, int64_t(1));
     if (se >= 8) se &= ~int64_t(7);
     const int Se = static_cast<int>(se);
-    const int bid = blockIdx.x;
+    const int bid = vbid;
     if (bid >= Se) return;
     // workgroups go to the XCDs round-robin; share s = XCD-major, so each
     // XCD takes a contiguous run of shares and the kv-heads whose scale rows
@@ -738,25 +816,31 @@ void decode_mfma_kernel(DecodeParams p) {
     // share holding chunk x: the largest s' with floor(s' C / Se) <= x
     auto share_of = [&](int64_t x) { return ((x + 1) * Se - 1) / C; };
 
-    // the sequence holding chunk a, and where its units start
-    int b = 0, L = 0;
-    int64_t pos = 0;
-    for (int base = 0; base < B; base += kWave) {
-      const int bb = base + lane;
-      const int Lb = bb < B ? max(p.context_lens[bb], 0) : 0;
-      const int64_t w = static_cast<int64_t>((Lb + 31) >> 5) * Hkv;
-      const int64_t incl = wave_incl_scan(w);
-      const int64_t tot = readlane64(incl, kWave - 1);
-      if (pos + tot > a) {
-        const int j = __builtin_ctzll(__ballot(pos + incl > a));
-        b = base + j;
-        L = __builtin_amdgcn_readlane(Lb, j);
-        pos += readlane64(incl - w, j);
+    // the sequence holding chunk a (exactly one lane's), and where its
+    // units start; from the kept first round, or (B > R) rounds read again
+    int64_t pos0 = 0;  // chunks of the units before the round
+    Round r = r0;
+    for (int base = 0;; base += R) {
+      if (base > 0) r = round_at(base);
+      if (pos0 + r.tot * Hkv > a || base + R >= B) {
+        const int bb = base + wave * kWave + lane;
+        const int64_t first = pos0 + r.x * Hkv;
+        if (bb < B && r.n > 0 && first <= a && a < first + static_cast<int64_t>(r.n) * Hkv) {
+          bal_found[0] = bb;
+          bal_found[1] = r.L;
+          bal_found[2] = r.S;
+          bal_found[3] = first;
+        }
         break;
       }
-      pos += tot;
+      pos0 += r.tot * Hkv;
     }
-    int nb = (L + 31) >> 5;
+    __syncthreads();
+    int b = __builtin_amdgcn_readfirstlane(static_cast<int>(bal_found[0]));
+    int L = __builtin_amdgcn_readfirstlane(static_cast<int>(bal_found[1]));
+    int S = __builtin_amdgcn_readfirstlane(static_cast<int>(bal_found[2]));
+    const int64_t pos = readlane64(bal_found[3], 0);
+    int nb = (L - S + 31) >> 5;
     int kvh = static_cast<int>((a - pos) / nb);
     int64_t cu = pos + static_cast<int64_t>(kvh) * nb;  // first chunk of unit (b, kvh)
     int64_t lo = a;
@@ -764,25 +848,33 @@ void decode_mfma_kernel(DecodeParams p) {
       const int64_t uend = cu + nb;
       const int64_t hi = min(uend, e);
       const bool whole = lo == cu && hi == uend;
-      const int64_t pslot = lo == a ? 2 * int64_t(s) : 2 * int64_t(s) + 1;
+      // split segments: the share's first or last slot; a whole unit of a
+      // cascade (which leaves a partial too) has a slot of its own after
+      // the shares' (several can lie inside one share)
+      const int64_t pslot = (whole && cascade) ? 2 * int64_t(p.bal_shares) + static_cast<int64_t>(b) * Hkv + kvh
+                            : lo == a           ? 2 * int64_t(s)
+                                                : 2 * int64_t(s) + 1;
       if (lo == cu && threadIdx.x == 0) {  // this share holds the unit's first chunk
         const int nsplit = whole ? 1 : static_cast<int>(share_of(uend - 1) - s + 1);
         *reinterpret_cast<int2*>(p.ws_unit + 2 * (static_cast<size_t>(b) * Hkv + kvh)) =
             int2{static_cast<int>(pslot), nsplit};
       }
-      run(b, kvh, L, static_cast<int>(lo - cu) * 32, min(L, static_cast<int>(hi - cu) * 32), 0, 0, 0, G,
-          whole, pslot);
+      // (cascade: never the final output, the shared tokens' partials remain)
+      run(b, kvh, L, S + static_cast<int>(lo - cu) * 32, min(L, S + static_cast<int>(hi - cu) * 32), 0, 0, 0,
+          G, whole && !cascade, pslot);
       if (uend >= e) break;
       __syncthreads();  // the merge buffers are reused by the next segment
       lo = cu = uend;
       if (++kvh == Hkv) {
-        // the next sequence with tokens (one exists: chunks remain before e)
+        // the next sequence with tokens of its own (one exists: chunks
+        // remain before e)
         kvh = 0;
         do {
           ++b;
           L = p.context_lens[b];
-        } while (L <= 0);
-        nb = (L + 31) >> 5;
+          S = own_begin(b);
+        } while (L <= S);
+        nb = (L - S + 31) >> 5;
       }
     }
   } else {
@@ -800,10 +892,10 @@ void decode_mfma_kernel(DecodeParams p) {
       b = u / Hkv;
       kvh = u - b * Hkv;
     } else {
-      b = blockIdx.x / Hkv;
-      kvh = blockIdx.x - b * Hkv;
+      b = vbid / Hkv;
+      kvh = vbid - b * Hkv;
     }
-    const int part = blockIdx.y;
+    const int part = vpart;
     const int PT = p.part_tokens;
 
     const int L = p.context_lens[b];
@@ -907,6 +999,68 @@ hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s) {
   if (kv == KvKind::E5M2) return launch_kv<KvKind::E5M2>(p, s);
   if (kv == KvKind::FP8) return launch_kv<KvKind::FP8>(p, s);
   return launch_kv<KvKind::BF16>(p, s);
+}
+
+template <KvKind KV, int D, int BS, bool kBal>
+void launch_fused_inst(const DecodeParams& p, dim3 grid, hipStream_t s) {
+  const dim3 block(kDecodeWaves * kWave);
+  const int G = p.num_heads / p.num_kv_heads;
+  const bool two = p.fused_prefix_tiles != 1;
+  if constexpr (KV == KvKind::BF16) {
+    if (G == 1) {  // one head per kv-head: the vector-ALU path
+      if (two)
+        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, true, 2>), grid, block, 0, s, p);
+      else
+        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, true, 1>), grid, block, 0, s, p);
+      return;
+    }
+  }
+  if (two)
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, false, 2>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, false, 1>), grid, block, 0, s, p);
+}
+
+template <KvKind KV, int D, int BS>
+hipError_t launch_fused_t(const DecodeParams& p, hipStream_t s) {
+  // balanced shares, or a workgroup per (sequence, kv-head, partition of the
+  // own tokens)
+  const int64_t own = p.bal_shares > 0
+                          ? p.bal_shares
+                          : static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * (p.num_parts - p.prefix_parts);
+  const int64_t total = static_cast<int64_t>(p.fused_prefix_wgs) + own;
+  if (own <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(total));
+  if (p.bal_shares > 0)
+    launch_fused_inst<KV, D, BS, true>(p, grid, s);
+  else
+    launch_fused_inst<KV, D, BS, false>(p, grid, s);
+  return hipGetLastError();
+}
+
+template <KvKind KV>
+hipError_t launch_fused_kv(const DecodeParams& p, hipStream_t s) {
+  if (p.head_dim == 128)
+    return p.block_size == 16 ? launch_fused_t<KV, 128, 16>(p, s) : launch_fused_t<KV, 128, 32>(p, s);
+  return p.block_size == 16 ? launch_fused_t<KV, 64, 16>(p, s) : launch_fused_t<KV, 64, 32>(p, s);
+}
+
+hipError_t launch_cascade_fused(DecodeParams p, KvKind kv, int max_group_size, hipStream_t s) {
+  // shared-prefix workgroups: (group, kv-head) x query tiles x partitions,
+  // padded to a multiple of 8
+  const int G = p.num_heads / p.num_kv_heads;
+  const int64_t cols = static_cast<int64_t>(max_group_size) * G;
+  const int64_t qtiles = (cols + prefix_queries_for(cols) - 1) / prefix_queries_for(cols);
+  const int64_t cells = static_cast<int64_t>(p.num_groups) * p.num_kv_heads * qtiles * p.prefix_parts;
+  if (qtiles > 0x7fffffff || cells > 0x7fffffff - 8) return hipErrorInvalidValue;
+  p.fused_prefix_wgs = static_cast<int32_t>((cells + 7) / 8 * 8);
+  p.fused_prefix_qtiles = static_cast<int32_t>(qtiles);
+  p.fused_prefix_tiles = prefix_tiles_for(cols);
+  if (kv == KvKind::I8) return launch_fused_kv<KvKind::I8>(p, s);
+  if (kv == KvKind::FP8) return launch_fused_kv<KvKind::FP8>(p, s);
+  if (kv == KvKind::E5M2) return launch_fused_kv<KvKind::E5M2>(p, s);
+  if (kv == KvKind::BF16) return launch_fused_kv<KvKind::BF16>(p, s);
+  return hipErrorInvalidValue;  // INT4 and fp32: two launches
 }
 
 hipError_t launch_multi_query_decode(const DecodeParams& p, KvKind kv, hipStream_t s) {

@@ -134,7 +134,9 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
 // Balanced shares: one wave per (sequence, kv-head) unit.  The unit's
 // record {first slot, splits} says where its partials are (split j >= 1 in
 // slot 2 (first / 2 + j)); 1 split: written whole by the partition kernel;
-// 0: an empty context, zero output.  The wave serves all G heads of the
+// 0: an empty context, zero output.  Shared-prefix decode: the partials of
+// the group's shared tokens (per head, in rows [0, bal_row0)) come first
+// and every unit is merged, whatever its count.  The wave serves all G heads of the
 // unit: 64 / G lanes per head, each owning DPL = D G / 64 consecutive dims,
 // so a unit that needs nothing costs one load.  The splits' maxima are
 // loaded 8 at a time, then their rows in batches, all loads of a batch
@@ -151,18 +153,28 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_units_kern
   if (u >= p.num_seqs * p.num_kv_heads) return;  // the whole wave
   const int2 rec = *reinterpret_cast<const int2*>(p.ws_unit + 2 * static_cast<size_t>(u));
   const int first = __builtin_amdgcn_readfirstlane(rec.x);
-  const int nsplit = __builtin_amdgcn_readfirstlane(rec.y);
-  if (nsplit == 1) return;
+  const int nsplit = max(__builtin_amdgcn_readfirstlane(rec.y), 0);
+  const bool cascade = p.group_start != nullptr;
+  if (!cascade && nsplit == 1) return;
+  // shared-prefix partials of the unit's sequence
+  const int npre = cascade ? (group_shared_tokens(p, group_of(p, u / p.num_kv_heads)) + p.prefix_part_tokens - 1) /
+                                 p.prefix_part_tokens
+                           : 0;
+  const int n = npre + nsplit;
   const int gh = lane / LPH;  // head within the group
   const int d0 = (lane % LPH) * DPL;
-  uint16_t* orow = static_cast<uint16_t*>(p.out) + (static_cast<size_t>(u) * G + gh) * D + d0;  // row b * H + h
-  if (nsplit <= 0) {  // empty context
+  const size_t hrow = static_cast<size_t>(u) * G + gh;  // output row b * H + h
+  uint16_t* orow = static_cast<uint16_t*>(p.out) + hrow * D + d0;
+  if (n == 0) {  // empty context
 #pragma unroll
     for (int k = 0; k < DPL; ++k) orow[k] = 0;
     return;
   }
+  // workspace row of partial j: the shared tokens' partitions, then the splits
   auto slot = [&](int j) -> size_t {
-    return static_cast<size_t>(j == 0 ? first : 2 * ((first >> 1) + j)) * G + gh;
+    if (j < npre) return hrow * p.num_parts + j;
+    j -= npre;
+    return static_cast<size_t>(p.bal_row0) + static_cast<size_t>(j == 0 ? first : 2 * ((first >> 1) + j)) * G + gh;
   };
   auto load_row = [&](size_t r, float (&x)[NV * 4]) {
     const float* a = p.ws_acc + r * D + d0;
@@ -179,10 +191,10 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_units_kern
     }
   };
   float M = -INFINITY;
-  for (int j0 = 0; j0 < nsplit; j0 += 8) {
+  for (int j0 = 0; j0 < n; j0 += 8) {
     float mm[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) mm[q] = p.ws_m[slot(min(j0 + q, nsplit - 1))];
+    for (int q = 0; q < 8; ++q) mm[q] = p.ws_m[slot(min(j0 + q, n - 1))];
 #pragma unroll
     for (int q = 0; q < 8; ++q) M = fmaxf(M, mm[q]);
   }
@@ -190,19 +202,19 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_units_kern
 #pragma unroll
   for (int k = 0; k < NV * 4; ++k) num[k] = 0.f;
   float den = 0.f;
-  for (int j0 = 0; j0 < nsplit; j0 += NBATCH) {
+  for (int j0 = 0; j0 < n; j0 += NBATCH) {
     float x[NBATCH][NV * 4];
     float mj[NBATCH], lj[NBATCH];
 #pragma unroll
     for (int q = 0; q < NBATCH; ++q) {
-      const size_t r = slot(min(j0 + q, nsplit - 1));  // past the last split: weight 0 below
+      const size_t r = slot(min(j0 + q, n - 1));  // past the last partial: weight 0 below
       mj[q] = p.ws_m[r];
       lj[q] = p.ws_l[r];
       load_row(r, x[q]);
     }
 #pragma unroll
     for (int q = 0; q < NBATCH; ++q) {
-      const float w = (j0 + q < nsplit) ? exp2f(mj[q] - M) : 0.f;
+      const float w = (j0 + q < n) ? exp2f(mj[q] - M) : 0.f;
       den = fmaf(w, lj[q], den);
 #pragma unroll
       for (int k = 0; k < DPL; ++k) num[k] = fmaf(w, x[q][k], num[k]);

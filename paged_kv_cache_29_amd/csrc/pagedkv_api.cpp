@@ -325,6 +325,8 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   p.ws_l = need ? reinterpret_cast<float*>(ws + acc_bytes + ml_bytes) : nullptr;
   p.bal_shares = shares;
   p.ws_unit = nullptr;
+  p.bal_row0 = 0;
+  p.fused_prefix_wgs = p.fused_prefix_qtiles = p.fused_prefix_tiles = 0;
   if (bal && need) {
     p.ws_acc = reinterpret_cast<float*>(ws);
     p.ws_m = reinterpret_cast<float*>(ws + bl.acc);
@@ -505,8 +507,8 @@ size_t mq_workspace_bytes(int32_t num_query_tokens, int32_t num_heads, int32_t h
   return acc + 2 * ml;
 }
 
-// Workspace of the cascade: every (sequence, head) has pparts + sparts
-// partial slots, and the reduce always runs.
+// Workspace of the cascade on fixed partitions: every (sequence, head) has
+// pparts + sparts partial slots, and the reduce always runs.
 size_t cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                const CascadeSizes& cs) {
   const size_t rows = static_cast<size_t>(num_seqs) * num_heads * (cs.pparts + cs.sparts);
@@ -514,6 +516,55 @@ size_t cascade_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head
   const size_t acc = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
   const size_t ml = (rows * sizeof(float) + 255) & ~size_t(255);
   return acc + 2 * ml;
+}
+
+// Shares of the sequences' own tokens in the one-launch cascade, in rounds
+// of the GPU's workgroup slots: the shared-prefix workgroups hold slots for
+// part of the launch, and smaller shares fill around them.
+constexpr int32_t kCascadeShareRounds = 2;
+int32_t cascade_shares_for(pkv::KvKind kv) { return kCascadeShareRounds * shares_for(kv); }
+
+// The sequences' own tokens in balanced shares (automatic partitioning,
+// the kinds the balanced walk serves): the shared tokens' pparts slots per
+// (sequence, head) come first, then the shares' 2 S slots and one slot per
+// (sequence, kv-head) unit, per head of a group, then the unit records.
+bool cascade_balanced_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                          int32_t block_size, int32_t partition_tokens, pkv::KvKind kv) {
+  if (partition_tokens != 0 || num_seqs <= 0) return false;
+  if (kv != pkv::KvKind::BF16 && kv != pkv::KvKind::I8 && kv != pkv::KvKind::FP8 && kv != pkv::KvKind::E5M2)
+    return false;
+  const int64_t ctx = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  return units * ((ctx + kChunk - 1) / kChunk) < (int64_t(1) << 40) &&
+         units + 2 * int64_t(kCascadeShareRounds) * max_shares() < 0x7fffffff;
+}
+
+// The automatic choice for the sequences' own tokens: balanced shares when
+// they may span several partitions (as for decode); short ones (a long
+// shared prefix, a short tail each) take a workgroup per (sequence,
+// kv-head), which measured faster there: 94-100 us against 112-118 us per
+// step on the 256 x (2000 shared + 50..500) token workload.
+bool cascade_own_balanced(int32_t num_seqs, int32_t num_kv_heads, int32_t max_blocks_per_seq, int32_t block_size,
+                          int32_t partition_tokens, int32_t max_shared_blocks, int32_t own_part_tokens,
+                          pkv::KvKind kv) {
+  return cascade_balanced_for(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens, kv) &&
+         (static_cast<int64_t>(max_blocks_per_seq) - max_shared_blocks) * block_size > own_part_tokens;
+}
+
+struct CascadeBalancedLayout {
+  size_t rows_pre, acc, ml, unit;
+  size_t total() const { return acc + 2 * ml + unit; }
+};
+CascadeBalancedLayout cascade_balanced_layout(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, int32_t pparts, int32_t shares) {
+  CascadeBalancedLayout l;
+  l.rows_pre = static_cast<size_t>(num_seqs) * num_heads * pparts;
+  const size_t rows = l.rows_pre + (static_cast<size_t>(2) * shares + static_cast<size_t>(num_seqs) * num_kv_heads) *
+                                       (num_heads / num_kv_heads);
+  l.acc = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
+  l.ml = (rows * sizeof(float) + 255) & ~size_t(255);
+  l.unit = (static_cast<size_t>(num_seqs) * num_kv_heads * 2 * sizeof(int32_t) + 255) & ~size_t(255);
+  return l;
 }
 
 pkv_status validate_write(const void* k, const void* v, const void* k_cache, const void* v_cache,
@@ -779,24 +830,37 @@ size_t pkv_paged_attention_cascade_workspace_size(
                                      prefix_partition_tokens, &cs);
   g_last_error = saved;  // a size query leaves the last error alone
   if (s != PKV_OK) return 0;
-  return cascade_workspace_bytes(num_seqs, num_heads, head_dim, cs);
+  const size_t fixed = cascade_workspace_bytes(num_seqs, num_heads, head_dim, cs);
+  // as the call chooses; the cache kind (INT4 keeps fixed partitions) is
+  // not known here, so enough for either layout
+  if (!cascade_own_balanced(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens,
+                            max_shared_blocks, cs.spt, pkv::KvKind::BF16))
+    return fixed;
+  return std::max(fixed, cascade_balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim, cs.pparts,
+                                                 kCascadeShareRounds * max_shares())
+                             .total());
 }
 
-pkv_status pkv_paged_attention_decode_cascade(
-    void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
-    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
-    const int32_t* group_start, const int32_t* group_shared_blocks, float scale, int32_t num_seqs,
-    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t num_groups, int32_t max_group_size,
-    int32_t max_shared_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t partition_tokens,
-    int32_t prefix_partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Shared-prefix decode, and (k_new set) the fused step that first writes
+// each sequence's new token at position L - 1.
+pkv_status cascade_call(void* out, const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                        const void* v_cache, const float* k_scale, const float* v_scale,
+                        const int32_t* block_tables, const int32_t* context_lens, const int32_t* group_start,
+                        const int32_t* group_shared_blocks, float scale, int32_t num_seqs, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                        int64_t num_blocks, int32_t num_groups, int32_t max_group_size, int32_t max_shared_blocks,
+                        pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t partition_tokens,
+                        int32_t prefix_partition_tokens, void* workspace, size_t workspace_bytes, void* stream,
+                        bool step) {
   // the plain checks first (sizes, dtypes, pointers); the workspace is
   // checked below against the cascade's own layout
   DecodeSetup st;
   pkv_status s = validate_decode(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                                  context_lens, scale, num_seqs, num_heads, num_kv_heads, head_dim,
                                  block_size, max_blocks_per_seq, num_blocks, q_dtype, kv_dtype,
-                                 partition_tokens, nullptr, 0, nullptr, nullptr, false, &st,
+                                 partition_tokens, nullptr, 0, k_new, v_new, step, &st,
                                  /*check_workspace=*/false);
   if (s != PKV_OK) return s;
   if (st.kv == pkv::KvKind::F32)
@@ -808,7 +872,12 @@ pkv_status pkv_paged_attention_decode_cascade(
   if (num_seqs == 0) return ok();
   if (!group_start || !group_shared_blocks)
     return fail(PKV_ERR_INVALID, "cascade decode needs group_start and group_shared_blocks");
-  const size_t need = cascade_workspace_bytes(num_seqs, num_heads, head_dim, cs);
+  const bool bal = cascade_own_balanced(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_tokens,
+                                        max_shared_blocks, cs.spt, st.kv);
+  const int32_t shares = bal ? cascade_shares_for(st.kv) : 0;
+  const CascadeBalancedLayout bl =
+      cascade_balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim, cs.pparts, shares);
+  const size_t need = bal ? bl.total() : cascade_workspace_bytes(num_seqs, num_heads, head_dim, cs);
   if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
   if (workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, workspace_bytes);
@@ -821,17 +890,29 @@ pkv_status pkv_paged_attention_decode_cascade(
     if (s == PKV_OK)
       s = pkv::debug_check_groups(group_start, group_shared_blocks, tables, lens, num_seqs, max_blocks_per_seq,
                                   block_size, num_groups, max_group_size, max_shared_blocks,
-                                  static_cast<hipStream_t>(stream));
+                                  static_cast<hipStream_t>(stream), step);
     if (s != PKV_OK) return s;
   }
   pkv::DecodeParams& p = st.p;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_heads * (cs.pparts + cs.sparts);
-  const size_t acc_bytes = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
-  const size_t ml_bytes = (rows * sizeof(float) + 255) & ~size_t(255);
   char* ws = static_cast<char*>(workspace);
-  p.ws_acc = reinterpret_cast<float*>(ws);
-  p.ws_m = reinterpret_cast<float*>(ws + acc_bytes);
-  p.ws_l = reinterpret_cast<float*>(ws + acc_bytes + ml_bytes);
+  if (bal) {
+    // shared tokens' partials in rows [B][H][pparts], then the shares' slots
+    p.ws_acc = reinterpret_cast<float*>(ws);
+    p.ws_m = reinterpret_cast<float*>(ws + bl.acc);
+    p.ws_l = reinterpret_cast<float*>(ws + bl.acc + bl.ml);
+    p.ws_unit = reinterpret_cast<int32_t*>(ws + bl.acc + 2 * bl.ml);
+    p.bal_shares = shares;
+    p.bal_row0 = static_cast<int64_t>(bl.rows_pre);
+    p.num_parts = cs.pparts;
+  } else {
+    const size_t rows = static_cast<size_t>(num_seqs) * num_heads * (cs.pparts + cs.sparts);
+    const size_t acc_bytes = (rows * head_dim * sizeof(float) + 255) & ~size_t(255);
+    const size_t ml_bytes = (rows * sizeof(float) + 255) & ~size_t(255);
+    p.ws_acc = reinterpret_cast<float*>(ws);
+    p.ws_m = reinterpret_cast<float*>(ws + acc_bytes);
+    p.ws_l = reinterpret_cast<float*>(ws + acc_bytes + ml_bytes);
+    p.num_parts = cs.pparts + cs.sparts;
+  }
   p.group_start = group_start;
   p.group_shared_blocks = group_shared_blocks;
   p.num_groups = num_groups;
@@ -839,10 +920,14 @@ pkv_status pkv_paged_attention_decode_cascade(
   p.prefix_part_tokens = cs.ppt;
   p.prefix_parts = cs.pparts;
   p.part_tokens = cs.spt;
-  p.num_parts = cs.pparts + cs.sparts;
   const hipStream_t strm = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  {
+  if (st.kv != pkv::KvKind::I4) {
+    // one launch: the shared-prefix workgroups and the shares of the
+    // sequences' own tokens
+    e = pkv::launch_cascade_fused(p, st.kv, max_group_size, strm);
+    if (e != hipSuccess) return fail(PKV_ERR_HIP, "cascade kernel launch failed: %s", hipGetErrorString(e));
+  } else {
     // prefix kernel on the side stream, partition kernel on the caller's,
     // joined before the reduce
     std::unique_lock<std::mutex> lock(g_side_mutex, std::defer_lock);
@@ -868,6 +953,38 @@ pkv_status pkv_paged_attention_decode_cascade(
   e = pkv::launch_decode_reduce(p, st.out_bf16, strm);
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "reduce kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+pkv_status pkv_paged_attention_decode_cascade(
+    void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+    const float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* group_start, const int32_t* group_shared_blocks, float scale, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t max_shared_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t partition_tokens,
+    int32_t prefix_partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  return cascade_call(out, q, nullptr, nullptr, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                      group_start, group_shared_blocks, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, num_groups, max_group_size, max_shared_blocks,
+                      q_dtype, kv_dtype, partition_tokens, prefix_partition_tokens, workspace, workspace_bytes,
+                      stream, false);
+}
+
+pkv_status pkv_paged_attention_decode_cascade_step(
+    void* out, const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+    float* k_scale, float* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+    const int32_t* group_start, const int32_t* group_shared_blocks, float scale, int32_t num_seqs,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+    int32_t max_blocks_per_seq, int64_t num_blocks, int32_t num_groups, int32_t max_group_size,
+    int32_t max_shared_blocks, pkv_dtype q_dtype, pkv_dtype kv_dtype, int32_t partition_tokens,
+    int32_t prefix_partition_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  return cascade_call(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                      group_start, group_shared_blocks, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, num_blocks, num_groups, max_group_size, max_shared_blocks,
+                      q_dtype, kv_dtype, partition_tokens, prefix_partition_tokens, workspace, workspace_bytes,
+                      stream, true);
 }
 
 pkv_status pkv_copy_blocks(void* dst_k, void* dst_v, float* dst_k_scale, float* dst_v_scale,

@@ -30,6 +30,6 @@ pkv_status debug_check_groups(const int32_t* group_start, const int32_t* group_s
                               const std::vector<int32_t>& tables, const std::vector<int32_t>& lens,
                               int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
                               int32_t num_groups, int32_t max_group_size, int32_t max_shared_blocks,
-                              hipStream_t s);
+                              hipStream_t s, bool step = false);
 
 }  // namespace pkv

@@ -70,9 +70,22 @@ struct DecodeParams {
   //   ws_unit [B * Hkv][2]: first slot of unit b * Hkv + kvh, and its
   //                          number of splits (1: written whole)
   // where split j >= 1 of a unit whose first slot is f lives in slot
-  // 2 * (f / 2 + j).
+  // 2 * (f / 2 + j).  Share slot r is workspace row bal_row0 + r * G + head
+  // (of D floats in ws_acc, of one float in ws_m / ws_l).  Shared-prefix
+  // decode: the units cover each sequence's tokens past its group's shared
+  // ones, every unit leaves partials (records count 1 too: a whole unit u
+  // uses slot 2 * bal_shares + u), and the shared tokens' partials come
+  // first, rows [0, bal_row0) = [B][H][num_parts] (num_parts = prefix_parts
+  // then).
   int32_t bal_shares;
   int32_t* ws_unit;
+  int64_t bal_row0;
+  // One-launch shared-prefix decode (set by its launcher): the number of
+  // leading workgroups that attend shared tokens, their query tiles per
+  // (group, kv-head) and their column tiles per wave.
+  int32_t fused_prefix_wgs;
+  int32_t fused_prefix_qtiles;
+  int32_t fused_prefix_tiles;
 };
 
 struct WriteParams {
@@ -161,6 +174,9 @@ int balanced_slots_per_cu(KvKind kv);
 hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, hipStream_t s);
 hipError_t launch_cascade_prefix(const DecodeParams& p, KvKind kv, int max_group_size, hipStream_t s);
+// Shared-prefix decode in one launch (balanced shares for the sequences'
+// own tokens, bal_shares set): the shared-prefix workgroups, then the shares.
+hipError_t launch_cascade_fused(DecodeParams p, KvKind kv, int max_group_size, hipStream_t s);
 // Multi-query attention partials (query_start set): every partition of every
 // sequence's context for up to max_queries new tokens per sequence.
 hipError_t launch_multi_query(const DecodeParams& p, KvKind kv, int max_queries, hipStream_t s);

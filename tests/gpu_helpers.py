@@ -105,9 +105,11 @@ class DeviceWorkload:
                                    v_scale=self.v_scale, partition_tokens=partition_tokens)
         return out
 
-    def cascade(self, partition_tokens=0, prefix_partition_tokens=0, min_shared_blocks=1, out=None):
+    def cascade(self, partition_tokens=0, prefix_partition_tokens=0, min_shared_blocks=1, out=None,
+                fused=False):
         """Decode with each group's shared blocks read once (groups found on
-        the host from the block tables)."""
+        the host from the block tables); fused: the step that first writes
+        the new tokens."""
         w = self.w
         gs, gsb, mg, ms = blocks.cascade_groups(w.block_tables, w.context_lens, w.block_size,
                                                 min_shared_blocks)
@@ -118,16 +120,18 @@ class DeviceWorkload:
             torch.from_numpy(gs).to(DEV), torch.from_numpy(gsb).to(DEV), w.scale, w.num_heads,
             w.num_kv_heads, w.head_dim, w.block_size, mg, ms, k_scale=self.k_scale,
             v_scale=self.v_scale, partition_tokens=partition_tokens,
-            prefix_partition_tokens=prefix_partition_tokens)
+            prefix_partition_tokens=prefix_partition_tokens,
+            k_new=self.k_new if fused else None, v_new=self.v_new if fused else None)
         return out
 
-    def step_cascade(self, **kw):
-        """Write the new tokens, then cascade decode."""
+    def step_cascade(self, fused=False, **kw):
+        """Write the new tokens, then cascade decode (fused: in one call)."""
         if self.w.kv_dtype in CODED and not getattr(self, "_filled", False):
             self.fill_int8()
             self._filled = True
-        self.write_new()
-        out = self.cascade(**kw)
+        if not fused:
+            self.write_new()
+        out = self.cascade(fused=fused, **kw)
         torch.cuda.synchronize()
         return out_f64(out)
 

@@ -115,6 +115,15 @@ def main():
         out, to_dev(q, "bf16"), kc, vc, torch.from_numpy(bad).to(DEV), cl, gs_d, gsb_d,
         scale, H, Hkv, D, bs, mg, ms), "sequence 2 of group 0")
     print("cascade parity; differing member rejected", flush=True)
+    # the fused step: a member whose new token would land inside its
+    # group's shared span (context ending exactly at it) is rejected
+    bad_lens = lens.copy()
+    bad_lens[1] = 3 * bs
+    kz = torch.zeros((B, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    expect_rejected(lambda: pkv.paged_attention_decode_cascade(
+        out, to_dev(q, "bf16"), kc, vc, bt, torch.from_numpy(bad_lens).to(DEV), gs_d, gsb_d,
+        scale, H, Hkv, D, bs, mg, ms, k_new=kz, v_new=kz), "shared span")
+    print("fused cascade step into a shared span rejected", flush=True)
 
     n_per = np.minimum(3, lens)
     qs = np.concatenate([[0], np.cumsum(n_per)]).astype(np.int32)

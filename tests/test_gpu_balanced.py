@@ -129,3 +129,33 @@ def test_balanced_workspace_reuse():
                                    workspace=ws)
         torch.cuda.synchronize()
         assert_parity(out_f64(dw.out), oracle_out(w), "bf16", f"call seed {seed}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_balanced_more_sequences_than_one_round(kv):
+    """600 sequences: the share walk reads the sequences in rounds of 256 (a
+    lane each of the workgroup's four waves), and most shares find their
+    first sequence in a later round."""
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.integers(0, 400, 600)]
+    lens[7] = 3000
+    lens[599] = 0
+    w = _build(31, lens, 4, 2, 64, 16, kv)
+    assert _shares(w) > 0
+    dw = DeviceWorkload(w)
+    got = dw.step()
+    assert_parity(got, oracle_out(w), kv, f"600 sequences {kv}")
+    assert np.all(got[599] == 0.0)
+
+
+def test_balanced_cascade_more_sequences_than_one_round():
+    """Shared-prefix decode over 300 sequences in groups of 7: the own-token
+    shares start each unit at its group's shared length."""
+    rng = np.random.default_rng(32)
+    lens = [65 + int(x) for x in rng.integers(0, 300, 300)]
+    w = workloads.make_custom(32, lens, 8, 2, 64, 16, prefix=64, prefix_group_size=7)
+    dw = DeviceWorkload(w)
+    got = dw.step_cascade()
+    gs, gsb, mg, ms = dw.groups
+    assert len(gsb) >= 40 and ms == 4
+    assert_parity(got, oracle_out(w), "bf16", "cascade, 300 sequences")

@@ -7,6 +7,7 @@ members' full block tables."""
 
 import numpy as np
 import pytest
+import torch
 
 from paged_kv_cache_29_amd import workloads
 
@@ -38,6 +39,35 @@ def test_cascade_partition_sizes(ppt, spt):
     dw = DeviceWorkload(w)
     got = dw.step_cascade(partition_tokens=spt, prefix_partition_tokens=ppt)
     assert_parity(got, oracle_out(w), "bf16", f"cascade ppt={ppt} spt={spt}")
+
+
+def _cache_bytes(dw):
+    out = [t.view(torch.uint8).cpu().numpy() for t in (dw.k_cache, dw.v_cache)]
+    if dw.k_scale is not None:
+        out += [t.view(torch.uint8).cpu().numpy() for t in (dw.k_scale, dw.v_scale)]
+    return out
+
+
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2", "i4"])
+@pytest.mark.parametrize("G,D,bs,own", [(4, 128, 16, RAGGED), (1, 64, 32, RAGGED),
+                                        (8, 128, 16, [1, 900, 3000, 40, 2200])])
+@pytest.mark.parametrize("spt", [0, 64])
+def test_cascade_fused_step_equals_write_then_cascade(kv, G, D, bs, own, spt):
+    """The fused step (new tokens written inside the call) gives the output
+    and the caches of kv_cache_write followed by cascade decode, bit for bit:
+    automatic and fixed partitions of the own tokens (short tails: one
+    workgroup per sequence and kv-head; long ones: balanced shares)."""
+    prefix = 96
+    lens = [prefix + x for x in own]
+    w = workloads.make_custom(500 + G + bs + len(own), lens, G * 2, 2, D, bs, kv_dtype=kv, prefix=prefix,
+                              prefix_group_size=3)
+    a, b = DeviceWorkload(w), DeviceWorkload(w)
+    ref = a.step_cascade(partition_tokens=spt)
+    got = b.step_cascade(fused=True, partition_tokens=spt)
+    assert np.array_equal(got.view(np.uint64), ref.view(np.uint64)), "outputs differ"
+    for x, y in zip(_cache_bytes(a), _cache_bytes(b)):
+        assert np.array_equal(x, y), "caches differ"
+    assert_parity(got, oracle_out(w), kv, f"fused cascade step {kv} G={G} bs={bs} spt={spt}")
 
 
 def test_cascade_equals_plain_decode_within_rounding():
