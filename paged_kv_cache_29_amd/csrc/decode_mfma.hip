@@ -585,7 +585,6 @@ void decode_mfma_kernel(DecodeParams p) {
               ld.load(cb[0], blk, row0);
               consume(cb[0], c2, std::true_type{});
             }
-            break;  // the rest of this wave's chunks are done
           }
         }
       }
@@ -672,65 +671,46 @@ void decode_mfma_kernel(DecodeParams p) {
       uint16_t* orow = out + bh * D;
       float* arow = p.ws_acc + slot * D;
       const float ls = Lsum[t];  // final outputs are acc / ls
-      if constexpr (kI4) {
-        // tile 2m + o: dim 2 (P r + m) + o, P = D/32 pairs per lane: the
-        // lane holds dims 8P g + 2P i + n for tile n, i = 0..3
+      if (!final_out) {
+        store_partial_row<KV, D>(arow, acc[t], g);
+      } else if constexpr (kI4) {
+        // the normalised output in bf16 over the same dims as the partial
+        // row (store_partial_row): 8P g + 2P i + n, P = D/32
         constexpr int P = D / 32;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d0 = 8 * P * g + 2 * P * i;
-          if (final_out) {
-            uint32_t wv[P];
+          uint32_t wv[P];
 #pragma unroll
-            for (int m = 0; m < P; ++m) wv[m] = pack_bf16x2(acc[t][2 * m][i] / ls, acc[t][2 * m + 1][i] / ls);
-            if constexpr (P == 4)
-              *reinterpret_cast<u32x4*>(orow + d0) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-            else
-              *reinterpret_cast<u32x2*>(orow + d0) = u32x2{wv[0], wv[1]};
-          } else {
-#pragma unroll
-            for (int n = 0; n < NN; n += 4)
-              *reinterpret_cast<f32x4*>(arow + d0 + n) =
-                  f32x4{acc[t][n][i], acc[t][n + 1][i], acc[t][n + 2][i], acc[t][n + 3][i]};
-          }
+          for (int m = 0; m < P; ++m) wv[m] = pack_bf16x2(acc[t][2 * m][i] / ls, acc[t][2 * m + 1][i] / ls);
+          if constexpr (P == 4)
+            *reinterpret_cast<u32x4*>(orow + d0) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+          else
+            *reinterpret_cast<u32x2*>(orow + d0) = u32x2{wv[0], wv[1]};
         }
       } else if constexpr (kInt8) {
-        // operand 4k + j: dim 64k + 4 r + j: the lane holds dims
-        // 64k + 16g + 4i + j
+        // byte codes: dims 64k + 16g + 4i + j
 #pragma unroll
         for (int k = 0; k < D / 64; ++k) {
           const int d0 = 64 * k + 16 * g;
-          if (final_out) {
-            uint32_t wv[8];
+          uint32_t wv[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              wv[2 * i] = pack_bf16x2(acc[t][4 * k][i] / ls, acc[t][4 * k + 1][i] / ls);
-              wv[2 * i + 1] = pack_bf16x2(acc[t][4 * k + 2][i] / ls, acc[t][4 * k + 3][i] / ls);
-            }
-            *reinterpret_cast<u32x4*>(orow + d0) = u32x4{wv[0], wv[1], wv[2], wv[3]};
-            *reinterpret_cast<u32x4*>(orow + d0 + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              *reinterpret_cast<f32x4*>(arow + d0 + 4 * i) =
-                  f32x4{acc[t][4 * k][i], acc[t][4 * k + 1][i], acc[t][4 * k + 2][i], acc[t][4 * k + 3][i]};
+          for (int i = 0; i < 4; ++i) {
+            wv[2 * i] = pack_bf16x2(acc[t][4 * k][i] / ls, acc[t][4 * k + 1][i] / ls);
+            wv[2 * i + 1] = pack_bf16x2(acc[t][4 * k + 2][i] / ls, acc[t][4 * k + 3][i] / ls);
           }
+          *reinterpret_cast<u32x4*>(orow + d0) = u32x4{wv[0], wv[1], wv[2], wv[3]};
+          *reinterpret_cast<u32x4*>(orow + d0 + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
         }
       } else {
-        // bf16, operand 2k + o: dim 32k + 2 r + o: the lane holds dims
-        // 32k + 8g + 2i + o
+        // bf16: dims 32k + 8g + 2i + o
 #pragma unroll
         for (int k = 0; k < NN / 2; ++k) {
           const int d0 = 32 * k + 8 * g;
           const f32x4 e = acc[t][2 * k], o = acc[t][2 * k + 1];
-          if (final_out) {
-            *reinterpret_cast<u32x4*>(orow + d0) =
-                u32x4{pack_bf16x2(e[0] / ls, o[0] / ls), pack_bf16x2(e[1] / ls, o[1] / ls),
-                      pack_bf16x2(e[2] / ls, o[2] / ls), pack_bf16x2(e[3] / ls, o[3] / ls)};
-          } else {
-            *reinterpret_cast<f32x4*>(arow + d0) = f32x4{e[0], o[0], e[1], o[1]};
-            *reinterpret_cast<f32x4*>(arow + d0 + 4) = f32x4{e[2], o[2], e[3], o[3]};
-          }
+          *reinterpret_cast<u32x4*>(orow + d0) =
+              u32x4{pack_bf16x2(e[0] / ls, o[0] / ls), pack_bf16x2(e[1] / ls, o[1] / ls),
+                    pack_bf16x2(e[2] / ls, o[2] / ls), pack_bf16x2(e[3] / ls, o[3] / ls)};
         }
       }
       if (!final_out && g == 0) {

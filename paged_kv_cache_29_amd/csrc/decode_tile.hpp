@@ -288,4 +288,45 @@ struct ChunkLoaderI4 {
   }
 };
 
+// One head's unnormalised output row (fp32, D dims in order) from the PV
+// accumulators of a lane (c, g), whose V operands came from the loaders
+// above: element i of output tile n is row 4g + i of that tile, whose dim
+// follows the lane-to-dim pairing of the V loads (dims
+//   bf16:        32k + 8g + 2i + o        for n = 2k + o,
+//   byte codes:  64k + 16g + 4i + j       for n = 4k + j,
+//   INT4:        8P g + 2P i + n          (P = D/32; n even: the low
+//                                          nibble dims, odd: the high ones)
+// so each lane writes runs of consecutive dims.
+template <KvKind KV, int D>
+__device__ __forceinline__ void store_partial_row(float* arow, const f32x4 (&acc)[D / 16], int g) {
+  constexpr int NN = D / 16;
+  if constexpr (KV == KvKind::I4) {
+    constexpr int P = D / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 8 * P * g + 2 * P * i;
+#pragma unroll
+      for (int n = 0; n < NN; n += 4)
+        *reinterpret_cast<f32x4*>(arow + d0 + n) = f32x4{acc[n][i], acc[n + 1][i], acc[n + 2][i], acc[n + 3][i]};
+    }
+  } else if constexpr (KV != KvKind::BF16) {
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int d0 = 64 * k + 16 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(arow + d0 + 4 * i) =
+            f32x4{acc[4 * k][i], acc[4 * k + 1][i], acc[4 * k + 2][i], acc[4 * k + 3][i]};
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < NN / 2; ++k) {
+      const int d0 = 32 * k + 8 * g;
+      const f32x4 e = acc[2 * k], o = acc[2 * k + 1];
+      *reinterpret_cast<f32x4*>(arow + d0) = f32x4{e[0], o[0], e[1], o[1]};
+      *reinterpret_cast<f32x4*>(arow + d0 + 4) = f32x4{e[2], o[2], e[3], o[3]};
+    }
+  }
+}
+
 }  // namespace pkv

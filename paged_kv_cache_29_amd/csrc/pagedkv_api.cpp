@@ -373,17 +373,19 @@ pkv_status launch_reduce(const DecodeSetup& st, hipStream_t stream) {
 }
 
 // Shared-prefix partition length: the longest of 2048 ... 32 tokens that
-// still gives the prefix kernel one workgroup per CU (256 CUs; at most
-// kMaxPartBlocks blocks; a multiple of 32, hence of the block size).  The
-// other half of each CU's workgroup slots is left to the partition kernel,
-// which runs beside it on the caller's stream (shared-prefix workload, bs
-// 16: 109-111 us per step against 118-121 us with one full round of 512).
+// still gives at least 128 shared-prefix workgroups, half a workgroup per
+// CU (at most kMaxPartBlocks blocks; a multiple of 32, hence of the block
+// size).  The rest of the GPU's workgroup slots go to the sequences' own
+// tokens, attended beside them; longer partitions also leave fewer
+// partials to merge.  Shared-prefix workload (256 x 2000 shared + 50..500
+// own tokens, one launch): 88-93 us per step at 128 workgroups (1024
+// tokens), 94-98 us at 256, 109-113 us at 512, 115-122 us at 64.
 int32_t auto_prefix_part_tokens(int64_t prefix_units, int32_t block_size, int32_t max_shared_blocks) {
   const int64_t span = static_cast<int64_t>(max_shared_blocks) * block_size;
   int32_t pt = 32;
   for (int32_t cand : {2048, 1024, 512, 256, 128, 64}) {
     if (cand > kMaxPartBlocks * block_size) continue;
-    if (prefix_units * ((span + cand - 1) / cand) >= 256) {
+    if (prefix_units * ((span + cand - 1) / cand) >= 128) {
       pt = cand;
       break;
     }

@@ -22,22 +22,28 @@
 // XCD's L2 serves one kv-head's shared blocks.
 //
 // Work split: every wave owns 16 NT queries (NT = 2, or 1 when the unit's
-// columns fit 64: prefix_tiles_for) and walks every
-// 32-token chunk of the partition.  A chunk is staged once in LDS: its four
-// pieces (K and V of the two 16-token sub-tiles, plus int8 scales) are
-// loaded by the four waves, one piece each, while the previous chunk is
-// being consumed (two LDS stages).  Each wave then reads its matrix-core
-// operands from LDS in the partition kernel's layouts (decode_tile.hpp) and,
-// for each of its query tiles t,
+// columns fit 64: prefix_tiles_for) and walks every 32-token chunk of the
+// partition.  A chunk is staged once in LDS: its four pieces (K and V of
+// the two 16-token sub-tiles, plus the scales of coded caches) are copied
+// by the four waves, one piece each, straight from global memory into LDS
+// (global_load_lds, 16 bytes per lane, no registers on the way), into a
+// ring of three stages: a chunk's copies are issued two chunks before it is
+// read, so each wave waits for its own copies of the current chunk only
+// (an explicit vmcnt count; the stages are separate LDS arrays, which lets
+// the compiler see that reading one does not wait on the copies into the
+// others) and one barrier per chunk publishes all four pieces.  Each wave
+// then reads its matrix-core operands from LDS in the partition kernel's
+// layouts (decode_tile.hpp) and, for each of its query tiles t,
 //   S^T[16 tok x 16 q] = K_sub . Q_t^T, online softmax per query, and
 //   O_t^T += V^T . P_t^T (P as a bf16 hi/lo pair),
-// sharing the chunk's K and V operands (and int8 widening) between tiles.
-// LDS layout per stage: K sub-tiles as token rows padded by 16 bytes (the
-// 16 rows a wave reads together fall in distinct banks); V sub-tiles
-// dim-major, one row of 16 tokens per dim (INT4: per dim pair), gathered
-// from the cache's groups of 4 tokens while staging; bf16 rows with their
-// 8-byte token quads 2k and 2k + 1 swapped on every other group of 8 dims
-// (same purpose).
+// sharing the chunk's K and V operands (and code widening) between tiles.
+// LDS layout per stage: a V sub-tile is the cache's bytes as they are
+// (groups of 4 tokens, dim-major inside a group), read at the partition
+// kernel's offsets (16 consecutive lanes read 256 consecutive bytes); a K
+// sub-tile holds the cache's token rows with the 16-byte units of row r
+// permuted (unit u stored at position u ^ f(r)), so that the 16 rows a wave
+// reads together fall in distinct banks; the copy lanes pick their source
+// units to match, since a copy lane's LDS destination is fixed.
 
 #pragma once
 
@@ -49,24 +55,48 @@ namespace pkv {
 namespace {
 
 
-// LDS stage of one 32-token chunk.  A token's K row is RB bytes (bf16: 2D,
-// byte codes: D, INT4: D/2); V is stored as VR rows (dims, INT4: dim pairs)
-// of one sub-tile's 16 tokens.
-template <KvKind KV, int D, int BS, int NT>
+// LDS stage of one 32-token chunk: pieces K0, K1, V0, V1 (the K and V
+// bytes of the two 16-token sub-tiles, SUB bytes each), then the coded
+// caches' scales (64 bytes per piece: k for the K pieces, v for the V ones).
+template <KvKind KV, int D>
 struct PrefixLds {
-  static constexpr int kElem = KV == KvKind::BF16 ? 2 : 1;
-  static constexpr int RB = KV == KvKind::I4 ? D / 2 : D * kElem;
-  static constexpr int VR = KV == KvKind::I4 ? D / 2 : D;
-  static constexpr int KROW = RB + 16;                // padded K token row
-  static constexpr int KSUB = 16 * KROW;              // one 16-token K sub-tile
-  static constexpr int VROW = 16 * kElem;             // one V row's 16 tokens
-  static constexpr int VSUB = VR * VROW;              // one 16-token V sub-tile
-  static constexpr int SC = KV != KvKind::BF16 ? 4 * 64 : 0;  // k/v scales of both sub-tiles
-  static constexpr int STAGE = 2 * KSUB + 2 * VSUB + SC;
-  static constexpr int PIECE = 16 * RB;               // bytes of one K or V sub-tile
-  // 16-byte loads per lane per piece (INT4 at D = 64: half the lanes load)
-  static constexpr int UNITS = (PIECE + 16 * kWave - 1) / (16 * kWave);
+  static constexpr bool kCoded = KV != KvKind::BF16;
+  static constexpr int RB = KV == KvKind::I4 ? D / 2 : D * (kCoded ? 1 : 2);  // bytes of a K token row
+  static constexpr int SUB = 16 * RB;        // one sub-tile of K or V
+  static constexpr int RU = RB / 16;         // 16-byte units per K row (2 .. 16)
+  // K row r's units are permuted by f(r) = (r >> SH) mod RU: over 16 rows the
+  // same unit lands on 16 different 16-byte bank groups of a 256-byte span
+  static constexpr int SH = RU >= 16 ? 0 : RU == 8 ? 1 : RU == 4 ? 2 : 3;
+  static constexpr int SC = kCoded ? 4 * 64 : 0;
+  static constexpr int STAGE = 4 * SUB + SC;
+  static constexpr int COPIES = (SUB + 16 * kWave - 1) / (16 * kWave);  // 1 KB copies per piece
+  static constexpr int PER_CHUNK = COPIES + (kCoded ? 1 : 0);         // copy instructions per wave
+  static_assert(RU >= 2 && RU <= 16 && SUB % 16 == 0, "K rows of whole 16-byte units");
 };
+
+// s_waitcnt with vmcnt(N) only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l
+// reads src (its own address) and writes lds_dst + 16 l (lds_dst uniform).
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_dst) {
+  using global_ptr = __attribute__((address_space(1))) const void*;
+  using lds_ptr = __attribute__((address_space(3))) void*;
+  __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)lds_dst, 16, 0, 0);
+}
+
+// The ring's barrier: this wave's LDS reads are complete (lgkmcnt(0)), then
+// the workgroup barrier, then an acquire fence that keeps later LDS reads
+// after it.  (A release fence would also wait for every copy in flight.)
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // Waves per SIMD: two tiles' states per wave take two waves' registers;
 // one tile's (at most 173 VGPRs) fit three, which hide more of the chunk
@@ -93,9 +123,12 @@ __device__ __forceinline__ void prefix_body(const DecodeParams& p, int bx, int b
   constexpr int NJ = D / 32;
   constexpr int NN = D / 16;
   constexpr int QW = 16 * NT;  // queries per wave
-  using L = PrefixLds<KV, D, BS, NT>;
+  using L = PrefixLds<KV, D>;
 
-  __shared__ __attribute__((aligned(16))) char lds[2][L::STAGE];
+  // the three stages of the chunk ring (separate arrays: see above)
+  __shared__ __attribute__((aligned(16))) char stage0[L::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage1[L::STAGE];
+  __shared__ __attribute__((aligned(16))) char stage2[L::STAGE];
   __shared__ int blk_ids[kMaxPartBlocks];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -182,112 +215,86 @@ __device__ __forceinline__ void prefix_body(const DecodeParams& p, int bx, int b
     }
   };
 
-  // ---- staging: wave w moves piece w of a chunk (0: K sub-tile 0, 1: K
-  // sub-tile 1, 2: V sub-tile 0, 3: V sub-tile 1; int8 also that piece's
-  // 16 scales, k for K pieces and v for V pieces)
+  // ---- staging: wave w copies piece w of a chunk (0: K sub-tile 0, 1: K
+  // sub-tile 1, 2: V sub-tile 0, 3: V sub-tile 1; coded caches also that
+  // piece's 16 scales, k for K pieces and v for V pieces) into a stage
   const int ph = wave & 1;
   const bool pv = wave >= 2;
-  u32x4 pu[L::UNITS];
-  u32x4 psc = {0u, 0u, 0u, 0u};
-  auto piece_load = [&](int ch) {
+  auto copy_chunk = [&](char* stage, int ch) {
     int blk[2], row0[2];
     chunk_blocks(ch, blk, row0);
     const size_t tile = static_cast<size_t>(blk[ph]) * Hkv + kvh;
-    const char* base = static_cast<const char*>(pv ? p.v_cache : p.k_cache) + tile * (BS * L::RB);
+    // K: 16 token rows; V: the sub-tile's 4 token groups (row0 is a multiple
+    // of 4): both SUB contiguous bytes from row0 * RB
+    const char* src = static_cast<const char*>(pv ? p.v_cache : p.k_cache) + tile * (BS * L::RB) +
+                      static_cast<size_t>(row0[ph]) * L::RB;
+    char* dst = stage + wave * L::SUB;
 #pragma unroll
-    for (int i = 0; i < L::UNITS; ++i) {
-      const int u = i * kWave + lane;  // 16-byte unit of the piece
-      if (u * 16 >= L::PIECE) break;   // INT4 at D = 64: half the lanes
-      // K: 16 token rows; V: the sub-tile's 4 token groups (row0 is a
-      // multiple of 4): both 16 * RB contiguous bytes from row0 * RB
-      const size_t off = static_cast<size_t>(row0[ph]) * L::RB + u * 16;
-      pu[i] = load_u32x4(base + off);
+    for (int i = 0; i < L::COPIES; ++i) {
+      const int q = i * kWave + lane;  // 16-byte unit of the piece this lane fills
+      if (q * 16 >= L::SUB) break;     // INT4 at D = 64: half the lanes
+      int off = q * 16;
+      if (!pv) {  // K: position q % RU of row r holds unit (q % RU) ^ f(r)
+        const int r = q / L::RU;
+        off = r * L::RB + (((q % L::RU) ^ (r >> L::SH)) & (L::RU - 1)) * 16;
+      }
+      copy16_to_lds(src + off, dst + i * (16 * kWave));
     }
-    if (kInt8 && lane < 4) {
-      const float* sc = pv ? p.v_scale : p.k_scale;
-      psc = load_u32x4(sc + tile * BS + row0[ph] + 4 * lane);
-    }
-  };
-  auto piece_store = [&](int st) {
-    char* dst = lds[st];
-#pragma unroll
-    for (int i = 0; i < L::UNITS; ++i) {
-      const int u = i * kWave + lane;
-      if (u * 16 >= L::PIECE) break;
-      if (!pv) {
-        const int row = (u * 16) / L::RB;
-        const int col = (u * 16) % L::RB;
-        *reinterpret_cast<u32x4*>(dst + ph * L::KSUB + row * L::KROW + col) = pu[i];
-      } else {
-        // unit u of the cache's V sub-tile: token group u / (VR / 4) (4 tokens)
-        // of rows 4 (u % (VR / 4)) .. + 3 (byte codes, INT4), or of dims
-        // 2 (u % (D / 2)) and + 1 (bf16); each row's 4 tokens go to that
-        // row of the dim-major stage
-        const u32x4 w = pu[i];
-        char* vt = dst + 2 * L::KSUB + ph * L::VSUB;
-        if constexpr (kInt8) {
-          const int gq = u / (L::VR / 4);
-          const int r = 4 * (u % (L::VR / 4));
-#pragma unroll
-          for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(vt + (r + j) * L::VROW + 4 * gq) = w[j];
-        } else {
-          const int gq = u / (D / 2);
-          const int d = 2 * (u % (D / 2));
-          const int slot = 8 * (gq ^ ((d >> 3) & 1));  // d and d + 1 share the 8-dim group
-          *reinterpret_cast<u32x2*>(vt + d * L::VROW + slot) = u32x2{w.x, w.y};
-          *reinterpret_cast<u32x2*>(vt + (d + 1) * L::VROW + slot) = u32x2{w.z, w.w};
-        }
+    if constexpr (kInt8) {
+      if (lane < 4) {
+        const float* sc = (pv ? p.v_scale : p.k_scale) + tile * BS + row0[ph] + 4 * lane;
+        copy16_to_lds(sc, stage + 4 * L::SUB + wave * 64);
       }
     }
-    if (kInt8 && lane < 4)
-      *reinterpret_cast<u32x4*>(dst + 2 * L::KSUB + 2 * L::VSUB + wave * 64 + lane * 16) = psc;
   };
   // this lane's operands of a staged chunk, in the partition kernel's layouts
-  auto lds_chunk = [&](int st, ChunkT& cw) {
-    const char* src = lds[st];
-    if constexpr (kI4) {
+  auto lds_chunk = [&](const char* stage, ChunkT& cw) {
+    const int kf = (c >> L::SH) & (L::RU - 1);  // the unit permutation of K row c
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // K: this lane's D/4 dims of row c; V: word m = tokens 4g .. 4g+3 of
-        // dim pair 16m + c
-        const char* kr = src + h * L::KSUB + c * L::KROW;
-        if constexpr (D == 128)
-          cw.k[h] = *reinterpret_cast<const u32x4*>(kr + 16 * g);
-        else
-          cw.k[h] = *reinterpret_cast<const u32x2*>(kr + 8 * g);
-        const char* vr = src + 2 * L::KSUB + h * L::VSUB;
+    for (int h = 0; h < 2; ++h) {
+      const char* kr = stage + h * L::SUB + c * L::RB;
+      const char* vt = stage + (2 + h) * L::SUB;
+      if constexpr (kI4) {
+        // K: this lane's D/4 dims of row c (unit g, or half unit at D = 64);
+        // V: tokens 4g .. 4g+3 of dim pairs (D/32) c .. + D/32 - 1
+        if constexpr (D == 128) {
+          cw.k[h] = *reinterpret_cast<const u32x4*>(kr + ((g ^ kf) & 3) * 16);
+          const u32x4 w = *reinterpret_cast<const u32x4*>(vt + g * (D / 2) * 4 + 16 * c);
 #pragma unroll
-        for (int m = 0; m < D / 32; ++m) cw.v[h][m] = *reinterpret_cast<const uint32_t*>(vr + (16 * m + c) * L::VROW + 4 * g);
-        const char* sc = src + 2 * L::KSUB + 2 * L::VSUB;
+          for (int m = 0; m < 4; ++m) cw.v[h][m] = w[m];
+        } else {
+          cw.k[h] = *reinterpret_cast<const u32x2*>(kr + (((g >> 1) ^ kf) & 1) * 16 + (g & 1) * 8);
+          const u32x2 w = *reinterpret_cast<const u32x2*>(vt + g * (D / 2) * 4 + 8 * c);
+          cw.v[h][0] = w.x;
+          cw.v[h][1] = w.y;
+        }
+      } else if constexpr (kInt8) {
+        // K: units 4jj + g of row c; V: tokens 4g .. 4g+3 of dims 64k + 4c + j
+#pragma unroll
+        for (int jj = 0; jj < NJ / 2; ++jj)
+          cw.k[h][jj] = *reinterpret_cast<const u32x4*>(kr + (((4 * jj + g) ^ kf) & (L::RU - 1)) * 16);
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(vt + g * D * 4 + 256 * k + 16 * c);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) cw.v[h][4 * k + j] = w[j];
+        }
+      } else {
+        // K: units 4j + g of row c; V: tokens 4g .. 4g+3 of dims 32k + 2c, + 1
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          cw.k[h][j] = *reinterpret_cast<const u32x4*>(kr + (((4 * j + g) ^ kf) & (L::RU - 1)) * 16);
+#pragma unroll
+        for (int k = 0; k < NN / 2; ++k) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(vt + g * D * 8 + 256 * k + 16 * c);
+          cw.v[h][2 * k] = u32x2{w.x, w.y};
+          cw.v[h][2 * k + 1] = u32x2{w.z, w.w};
+        }
+      }
+      if constexpr (kInt8) {
+        const char* sc = stage + 4 * L::SUB;
         cw.ks[h] = *reinterpret_cast<const f32x4*>(sc + h * 64 + 16 * g);
         cw.vs[h] = *reinterpret_cast<const f32x4*>(sc + (2 + h) * 64 + 16 * g);
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const char* kr = src + h * L::KSUB + c * L::KROW;
-        if constexpr (kInt8) {
-#pragma unroll
-          for (int jj = 0; jj < NJ / 2; ++jj) cw.k[h][jj] = *reinterpret_cast<const u32x4*>(kr + 16 * g + 64 * jj);
-        } else {
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) cw.k[h][j] = *reinterpret_cast<const u32x4*>(kr + (32 * j + 8 * g) * 2);
-        }
-        const char* vr = src + 2 * L::KSUB + h * L::VSUB;
-#pragma unroll
-        for (int n = 0; n < NN; ++n) {
-          if constexpr (kInt8) {
-            cw.v[h][n] = *reinterpret_cast<const uint32_t*>(vr + (16 * n + c) * L::VROW + 4 * g);
-          } else {
-            const int gg = g ^ ((c >> 3) & 1);
-            cw.v[h][n] = *reinterpret_cast<const u32x2*>(vr + (16 * n + c) * L::VROW + 8 * gg);
-          }
-        }
-        if constexpr (kInt8) {
-          const char* sc = src + 2 * L::KSUB + 2 * L::VSUB;
-          cw.ks[h] = *reinterpret_cast<const f32x4*>(sc + h * 64 + 16 * g);
-          cw.vs[h] = *reinterpret_cast<const f32x4*>(sc + (2 + h) * 64 + 16 * g);
-        }
       }
     }
   };
@@ -304,16 +311,11 @@ __device__ __forceinline__ void prefix_body(const DecodeParams& p, int bx, int b
     for (int n = 0; n < NN; ++n) acc[t][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // `masked` (compile time): the chunk may hold tokens past the end of the
-  // span or, multi-query, past a column's position; clean chunks take the
-  // instantiation without masking code (as a runtime branch the compiler
-  // turns the masking into selects that every chunk executes).
-  auto consume = [&](const ChunkT& cw, int ch, auto masked) {
-    constexpr bool kMasked = decltype(masked)::value;
+  auto consume = [&](const ChunkT& cw, int ch) {
     const int t0 = t_begin + ch * 32;
-    const bool tail = kMasked && (t0 + 32) > t_end;  // only a lone last block at bs = 16
+    const bool tail = (t0 + 32) > t_end;  // only a lone last block at bs = 16
     // V^T operands of the chunk, shared by the query tiles (INT4: operand
-    // 2m holds the even dims of dim pairs 16m + c, 2m + 1 the odd ones)
+    // 2m holds the even dims of the lane's dim pairs, 2m + 1 the odd ones)
     u32x4 vw[NN];
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
@@ -393,7 +395,7 @@ __device__ __forceinline__ void prefix_body(const DecodeParams& p, int bx, int b
           }
         }
       }
-      if constexpr (kMQ && kMasked) {  // causal: column c sees tokens up to lim[t]
+      if constexpr (kMQ) {  // causal: column c sees tokens up to lim[t]
         if (t0 + 31 > lim[t]) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -452,33 +454,34 @@ __device__ __forceinline__ void prefix_body(const DecodeParams& p, int bx, int b
   };
 
 
-  // ---- every chunk of the partition, two LDS stages: the next chunk's
-  // pieces are in flight while the current one is consumed
-  // Clean chunks (inside the span and, multi-query, at or before the
-  // workgroup's first column's position, hence every column's) first, then
-  // the rest; the bound is uniform across the workgroup, so every wave runs
-  // the same iterations between the barriers.
+  // ---- every chunk of the partition through the ring: at chunk ch, wait
+  // for this wave's copies of ch (those of ch + 1 may still be in flight),
+  // then a barrier (every piece of ch has landed, and every wave is done
+  // with the stage of ch - 1), then the copies of ch + 2 into that stage,
+  // then the arithmetic on ch.  One body serves every chunk: its masking
+  // (past the span's end or, multi-query, past a column's position) sits
+  // behind uniform branches; a second, unmasked copy per stage would not fit
+  // the registers.  The counts are uniform, so every wave runs the same
+  // barriers.
   const int nchunks = (t_end - t_begin + 31) / 32;
-  const int clean_end = kMQ ? min(t_end, S - nnew + qwg / G + 1) : t_end;
-  const int nclean = min(nchunks, max(0, (clean_end - t_begin) / 32));
-  auto run = [&](int ch0, int ch1, auto masked) {
-    for (int ch = ch0; ch < ch1; ++ch) {
-      const bool more = ch + 1 < nchunks;
-      if (more) piece_load(ch + 1);
-      {
-        ChunkT cw;
-        lds_chunk(ch & 1, cw);
-        consume(cw, ch, masked);
-      }
-      if (more) piece_store((ch + 1) & 1);
-      __syncthreads();
-    }
+  auto step = [&](int ch, const char* cur, char* ahead) {
+    if (ch + 1 < nchunks)
+      wait_vmcnt<L::PER_CHUNK>();
+    else
+      wait_vmcnt<0>();
+    ring_barrier();
+    if (ch + 2 < nchunks) copy_chunk(ahead, ch + 2);
+    ChunkT cw;
+    lds_chunk(cur, cw);
+    consume(cw, ch);
   };
-  piece_load(0);
-  piece_store(0);
-  __syncthreads();
-  run(0, nclean, std::false_type{});
-  run(nclean, nchunks, std::true_type{});
+  copy_chunk(stage0, 0);
+  if (nchunks > 1) copy_chunk(stage1, 1);
+  for (int ch = 0; ch < nchunks; ch += 3) {
+    step(ch, stage0, stage2);
+    if (ch + 1 < nchunks) step(ch + 1, stage1, stage0);
+    if (ch + 2 < nchunks) step(ch + 2, stage2, stage1);
+  }
 
   // ---- this wave's partials
 #pragma unroll
@@ -494,18 +497,7 @@ __device__ __forceinline__ void prefix_body(const DecodeParams& p, int bx, int b
     const size_t qr = kMQ ? static_cast<size_t>(qrow0 + r / G) : static_cast<size_t>(gs + r / G);
     const size_t bh = qr * H + kvh * G + r % G;
     const size_t slot = bh * p.num_parts + part;
-    float* arow = p.ws_acc + slot * D;
-    if constexpr (kI4) {  // lane holds dims 32m + 8g .. + 7: tiles 2m (even), 2m + 1 (odd)
-#pragma unroll
-      for (int m = 0; m < NN / 2; ++m) {
-        const f32x4 e = acc[t][2 * m], o = acc[t][2 * m + 1];
-        *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g) = f32x4{e[0], o[0], e[1], o[1]};
-        *reinterpret_cast<f32x4*>(arow + 32 * m + 8 * g + 4) = f32x4{e[2], o[2], e[3], o[3]};
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < NN; ++n) *reinterpret_cast<f32x4*>(arow + 16 * n + 4 * g) = acc[t][n];
-    }
+    store_partial_row<KV, D>(p.ws_acc + slot * D, acc[t], g);
     if (g == 0) {
       p.ws_m[slot] = m_run[t];
       p.ws_l[slot] = Lsum;
