@@ -240,13 +240,17 @@ int32_t pkv_paged_attention_shares(int32_t num_seqs, int32_t num_kv_heads, int32
  * each, whose partial results a second kernel combines.  0: the automatic
  * choice.  If every context fits the automatic partition length (as
  * max_blocks_per_seq * block_size bounds it), one workgroup per (sequence,
- * kv-head) attends it whole and no second kernel runs.  Otherwise (and for
- * every cache kind but fp32) the work is balanced: the 32-token chunks of
+ * kv-head) attends it whole and no second kernel runs.  Otherwise, for
+ * bf16, int8 and FP8 caches, the work is balanced: the 32-token chunks of
  * all (sequence, kv-head) pairs, laid end to end, are cut into equal
  * contiguous shares, one per workgroup of a grid sized to the GPU
  * (pkv_paged_attention_shares), so that ragged context lengths leave no
  * tail of idle CUs; pairs split between shares are combined by the second
- * kernel.  The result is the same softmax in every case, up to rounding.
+ * kernel.  fp32 and INT4 caches keep fixed partitions; for INT4 the
+ * automatic length may be longer than the query above reports (never
+ * giving more partitions, so the workspace size holds), chosen so that
+ * the partitions fill whole rounds of the GPU's workgroup slots.  The
+ * result is the same softmax in every case, up to rounding.
  * workspace / workspace_bytes: device scratch of at least
  * pkv_paged_attention_workspace_size(...) bytes, 256-byte aligned.
  */

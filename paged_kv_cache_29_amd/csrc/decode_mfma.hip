@@ -154,8 +154,8 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     vbid -= np;
     vgrid -= np;
-    if constexpr (!kBal) {  // fixed partitions: (sequence, kv-head) fastest
-      const int units = p.num_seqs * p.num_kv_heads;
+    if constexpr (!kBal) {  // fixed partitions: (sequence, kv-head) fastest, in whole slabs
+      const int units = (p.num_seqs * p.num_kv_heads + 15) & ~15;
       vpart = vbid / units;
       vbid -= vpart * units;
     }
@@ -872,8 +872,14 @@ void decode_mfma_kernel(DecodeParams p) {
       b = u / Hkv;
       kvh = u - b * Hkv;
     } else {
-      b = vbid / Hkv;
-      kvh = vbid - b * Hkv;
+      // slabs of 16 (sequence, kv-head) units: unit 16s + 2q + j runs as
+      // workgroup 16s + 8j + q, so units 2q and 2q + 1 (kv-heads whose scale
+      // rows share a 128-byte line) run on one XCD (workgroups go to the 8
+      // XCDs round-robin) and the line is fetched into one L2
+      const int u = (vbid & ~15) | ((vbid & 7) << 1) | ((vbid >> 3) & 1);
+      if (u >= p.num_seqs * Hkv) return;  // padding, uniform across the workgroup
+      b = u / Hkv;
+      kvh = u - b * Hkv;
     }
     const int part = vpart;
     const int PT = p.part_tokens;
@@ -948,7 +954,7 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
       hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, true>), grid, block, 0, s, p);
     }
   } else {
-    const dim3 grid(units, static_cast<unsigned>(parts));
+    const dim3 grid((units + 15u) & ~15u, static_cast<unsigned>(parts));  // whole slabs of 16 units
     if constexpr (KV == KvKind::BF16) {
       if (vec) {
         hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, false, true>), grid, block, 0, s, p);
@@ -1007,7 +1013,8 @@ hipError_t launch_fused_t(const DecodeParams& p, hipStream_t s) {
   // own tokens)
   const int64_t own = p.bal_shares > 0
                           ? p.bal_shares
-                          : static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * (p.num_parts - p.prefix_parts);
+                          : ((static_cast<int64_t>(p.num_seqs) * p.num_kv_heads + 15) & ~int64_t(15)) *
+                                (p.num_parts - p.prefix_parts);
   const int64_t total = static_cast<int64_t>(p.fused_prefix_wgs) + own;
   if (own <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(total));

@@ -143,6 +143,29 @@ int32_t auto_part_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t block_s
   return pt;
 }
 
+// Among partition lengths no shorter than pt (never more partitions, hence
+// never a larger workspace), the one whose workgroups fill `slots`
+// workgroup slots in whole rounds best: the fewest rounds x tokens per
+// workgroup, for contexts of ctx tokens.  (64 x 8192-token contexts, 8
+// kv-heads, 768 slots: 3 partitions of 2752 tokens, two full rounds,
+// instead of 4 of 2048 in 2.67 rounds.)
+int32_t refine_part_tokens(int32_t pt, int64_t units, int64_t ctx, int64_t slots) {
+  auto cost = [&](int64_t t) {
+    const int64_t w = units * ((ctx + t - 1) / t);
+    return ((w + slots - 1) / slots) * t;
+  };
+  int64_t best = pt, best_cost = cost(pt);
+  for (int64_t parts = (ctx + pt - 1) / pt - 1; parts >= 1; --parts) {
+    const int64_t t = ((ctx + parts - 1) / parts + kChunk - 1) / kChunk * kChunk;
+    const int64_t c = cost(t);
+    if (c < best_cost) {
+      best = t;
+      best_cost = c;
+    }
+  }
+  return static_cast<int32_t>(best);
+}
+
 // Validated partition length, or 0 if `requested` is not acceptable.
 int32_t part_tokens_for(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                         int32_t max_blocks_per_seq, int32_t requested) {
@@ -270,12 +293,21 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
     return fail(PKV_ERR_UNSUPPORTED, "(q_dtype, kv_dtype) = (%d, %d) is not supported",
                 static_cast<int>(q_dtype), static_cast<int>(kv_dtype));
   }
-  const int32_t pt = part_tokens_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
-                                     partition_tokens);
-  if (pt == 0)
+  const int32_t pt0 = part_tokens_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
+                                      partition_tokens);
+  if (pt0 == 0)
     return fail(PKV_ERR_INVALID,
                 "partition_tokens %d must be 0 or a multiple of %d in [%d, %d]",
                 partition_tokens, kChunk, kChunk, kMaxPartBlocks * block_size);
+  const bool bal = allow_balanced && balanced_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
+                                                  partition_tokens, kv);
+  // INT4 keeps fixed partitions: their automatic length is refined to fill
+  // whole rounds of the GPU's workgroup slots
+  const int32_t pt = allow_balanced && partition_tokens == 0 && kv == pkv::KvKind::I4
+                         ? refine_part_tokens(pt0, static_cast<int64_t>(num_seqs) * num_kv_heads,
+                                              static_cast<int64_t>(max_blocks_per_seq) * block_size,
+                                              static_cast<int64_t>(kNumCUs) * pkv::balanced_slots_per_cu(kv))
+                         : pt0;
   const int32_t nparts = num_parts_for(block_size, max_blocks_per_seq, pt);
   if (nparts > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many context partitions (%d)", nparts);
   if (static_cast<int64_t>(num_seqs) * num_kv_heads > 0x7fffffff)
@@ -292,8 +324,6 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   } else if (k_scale || v_scale) {
     return fail(PKV_ERR_INVALID, "k_scale / v_scale must be NULL for fp32 and bf16 caches");
   }
-  const bool bal = allow_balanced && balanced_for(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
-                                                  partition_tokens, kv);
   const int32_t shares = bal ? shares_for(kv) : 0;
   const BalancedLayout bl = balanced_layout(num_seqs, num_heads, num_kv_heads, head_dim, shares);
   const size_t need = !check_workspace ? 0
