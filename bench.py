@@ -31,7 +31,9 @@ Options: --steps K --warmup W (timed / untimed steps), --gpus N (only 1),
 block size), --partition-tokens, --cpu-seconds / --cpu-seconds-secondary
 (bound of the CPU oracle baseline of the headline / of each other workload;
 0 disables it), --copy-calibration (only run a 1 GiB device copy, for
-scaling rocprofv3 byte counters).
+scaling rocprofv3 byte counters), --counter-pass (per workload only fill
+the cache and run the fused step warm-up + steps times, so that a counter
+run's partition-kernel dispatches are all fused steps).
 """
 
 import argparse
@@ -46,7 +48,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "paged decode-attn KV read GB/s (% of HBM peak) + µs/step, 7B & 70B shapes"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 KERNEL_SOURCES = ["decode_mfma.hip", "decode_tile.hpp", "decode_append.hpp", "pkv_device.hpp",
-                  "pkv_kernels.hpp"]
+                  "pkv_kernels.hpp", "prefix_body.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.txt")
 CODED = ("i8", "fp8", "e5m2", "i4")  # caches of codes with per-(token, kv-head) scales
 CODE_BYTES = {"i8": 1.0, "fp8": 1.0, "e5m2": 1.0, "i4": 0.5, "bf16": 2.0, "f32": 4.0}  # per element
@@ -98,7 +100,7 @@ def torch_kv_dtype(torch, kind):
             "e5m2": torch.float8_e5m2, "i4": torch.uint8, "f32": torch.float32}[kind]
 
 
-def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
+def run_workload(cfg, args, torch, pkv, workloads, block_size=None, counter_only=False):
     w = workloads.make_config(cfg, seed=0, block_size=block_size)
     dev = torch.device("cuda:0")
     store = "bf16" if w.kv_dtype == "bf16" else "f32"
@@ -130,15 +132,14 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
         write_codes(kf, vf, kc, vc, ks, vs, sf)   # fill the cache once
         torch.cuda.synchronize()
         # the same fill again, timed: the quantising write at bulk size
-        fill = time_fill(torch, lambda: write_codes(kf, vf, kc, vc, ks, vs, sf),
-                         read_bytes=2 * kf.numel() * 4,
-                         write_bytes=int(2 * kf.shape[0] * Hkv * (D * CODE_BYTES[w.kv_dtype] + 4)),
-                         tokens=kf.shape[0])
+        fill = None if counter_only else time_fill(
+            torch, lambda: write_codes(kf, vf, kc, vc, ks, vs, sf), read_bytes=2 * kf.numel() * 4,
+            write_bytes=int(2 * kf.shape[0] * Hkv * (D * CODE_BYTES[w.kv_dtype] + 4)), tokens=kf.shape[0])
         del kf, vf, sf
     else:
         kc, vc = up(w.k_cache, store), up(w.v_cache, store)
         fill = None
-        if w.name == "mha7b_bf16":
+        if w.name == "mha7b_bf16" and not counter_only:
             fill = bulk_fill_bf16(torch, pkv, w, kc, vc)
     out = torch.empty_like(q)
     pt = args.partition_tokens
@@ -204,6 +205,15 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None):
         for _ in range(10):
             step_fused()
         torch.cuda.synchronize()
+
+    if counter_only:
+        # the fused step alone, warm-up + timed count, for counter runs: the
+        # partition kernel's dispatches are then all fused-step launches
+        for _ in range(args.warmup + args.steps):
+            step_fused()
+        torch.cuda.synchronize()
+        return {"config": cfg, "name": w.name, "fused_steps": args.warmup + args.steps,
+                "algorithmic_bytes": unique_tile_bytes(w) if w.meta.get("prefix") else kv_bytes(w)}
 
     ms_per_step = loop_time(step_fused) / 1e3
     ms_u = loop_time(step_unfused) / 1e3
@@ -608,6 +618,9 @@ def main():
     ap.add_argument("--settle-seconds", type=float, default=0.3,
                     help="untimed steps before each workload's first warm-up, so clocks have settled")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="per workload only fill the cache and run warm-up + steps fused steps "
+                         "(for rocprofv3 counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
@@ -627,6 +640,15 @@ def main():
     import paged_kv_cache_29_amd as pkv
     from paged_kv_cache_29_amd import workloads
     pkv.load_library()
+    if args.counter_pass:
+        runs = []
+        for c, bs in parse_configs(args.configs):
+            r = run_workload(c, args, torch, pkv, workloads, bs if c == 4 else None, counter_only=True)
+            print(f"[bench] config {c}: counter pass, {r['fused_steps']} fused steps", file=sys.stderr, flush=True)
+            runs.append(r)
+            torch.cuda.empty_cache()
+        print(json.dumps({"counter_pass": runs, "kernel_source_sha": kernel_source_sha()}))
+        return 0
     results = []
     for i, (c, bs) in enumerate(parse_configs(args.configs)):
         tag = f"{c}" + (f"@{bs}" if c == 4 else "")

@@ -47,11 +47,12 @@ __global__ __launch_bounds__(W * kWave) void decode_f32_kernel(DecodeParams p) {
   const int t_end = min(L, t_begin + PT);
   const bool single = L <= PT;
 
-  // Fused step: the partition holding the newest token writes it first.
-  if (p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
-    append_new_token<KvKind::F32, D, BS, W * kWave>(p, b, kvh, L - 1);
-    __threadfence_block();
-    __syncthreads();
+  // Fused step: the partition holding the newest token writes it, by the
+  // wave that reads token L - 1 (waves take tokens round-robin), which
+  // waits for its own stores; nothing else reads the token.
+  if (p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end && wave == (L - 1 - t_begin) % W) {
+    append_new_token<KvKind::F32, D, BS>(p, b, kvh, L - 1, lane);
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   float qv[kMaxGroup][ND];

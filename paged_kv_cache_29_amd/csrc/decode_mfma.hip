@@ -211,12 +211,16 @@ void decode_mfma_kernel(DecodeParams p) {
     for (int t = 0; t < NT; ++t) lim[t] = kMQ ? L - nnew + (16 * (tile0 + t) + c) / G : 0;
     const int lim_lo = kMQ ? L - nnew + (16 * tile0) / G : 0;  // the first column's
 
-    // Fused step: the range holding the newest token writes it first; the
-    // fence and barrier make the stores visible to this workgroup's loads.
+    // Fused step: the range holding the newest token writes it, and the
+    // wave that will attend it (chunk append_ch of the piece starting at
+    // append_pb; a piece's chunks go to the waves round-robin) is the one
+    // that writes: it waits for its own stores just before it loads that
+    // chunk, and nothing else waits.
+    int append_pb = -1, append_ch = -1;
     if (!kMQ && p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
-      append_new_token<KV, D, BS, W * kWave>(p, b, kvh, L - 1);
-      __threadfence_block();
-      __syncthreads();
+      append_pb = t_begin + (L - 1 - t_begin) / kPiece * kPiece;
+      append_ch = (L - 1 - append_pb) / 32;
+      if (wave == append_ch % W) append_new_token<KV, D, BS>(p, b, kvh, L - 1, lane);
     }
 
     // Q^T operand (B of the score MFMA): lane (c, g), tile t, MFMA j, 8 dims.
@@ -569,8 +573,14 @@ void decode_mfma_kernel(DecodeParams p) {
       {
         ChunkT cb[NB];
         int blk[2], row0[2];
+        // this wave holds the chunk written by the append in this piece, at
+        // or after chunk ch: wait for the append's stores before loading it
+        auto append_wait = [&](int ch) {
+          if (pb == append_pb && wave == append_ch % W && append_ch >= ch) __builtin_amdgcn_s_waitcnt(0);
+        };
         for (int ch = wave; ch < nchunks; ch += NB * W) {
           if (ch + (NB - 1) * W < nclean) {
+            if (ch + (NB - 1) * W >= append_ch) append_wait(ch);
 #pragma unroll
             for (int k = NB - 1; k >= 0; --k) {
               chunk_blocks(ch + k * W, blk, row0);
@@ -581,6 +591,7 @@ void decode_mfma_kernel(DecodeParams p) {
             for (int k = NB - 1; k >= 0; --k) consume(cb[k], ch + k * W, kBatchMasked{});
           } else {
             for (int c2 = ch; c2 < nchunks; c2 += W) {
+              if (c2 >= append_ch) append_wait(c2);
               chunk_blocks(c2, blk, row0);
               ld.load(cb[0], blk, row0);
               consume(cb[0], c2, std::true_type{});
