@@ -182,6 +182,36 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None, counter_only
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / args.steps * 1e3  # us
 
+    def graph_time(fn, per_graph=20):
+        """Average duration of fn replayed from a HIP graph of per_graph
+        back-to-back calls (events on the replay stream): the step without
+        the host's per-call cost (the binding's argument marshalling), as a
+        serving loop that captures its decode step would run it."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(per_graph):
+                fn()
+        reps = max(2, (args.steps + per_graph - 1) // per_graph)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) / (reps * per_graph) * 1e3
+        del g
+        return us
+
     def per_step(fn):
         """Per-step durations: one event between consecutive steps."""
         n = max(args.steps, 2)
@@ -226,6 +256,7 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None, counter_only
     red_us = max(0.0, ms_per_step * 1e3 - part_avg)
     write_us = max(0.0, ms_u * 1e3 - part_u_us - red_us)
     dist = per_step(step_fused)
+    us_graph = graph_time(step_fused)
     nbytes = kv_bytes(w)
     uniq = unique_tile_bytes(w)
     res = {
@@ -238,6 +269,7 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None, counter_only
         "pct_hbm_peak": 100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "tokens_per_s": w.attended_tokens / (ms_per_step * 1e-3),
         "us_per_step_events": dist,
+        "us_per_step_graph": us_graph,
         "kernel_us": {"decode_step_partitions": part_avg, "decode_reduce_share": red_us},
         "unfused": {"us_per_step": ms_u * 1e3,
                     "kv_gbs": nbytes / (ms_u * 1e-3) / 1e9,
@@ -271,6 +303,7 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None, counter_only
     if w.kv_dtype == "f32":
         res["roofline"]["note"] = ("the whole workload (540 KB of KV) stays in the caches: the step "
                                    "is bound by launch and dependent-load latency, so only us/step counts")
+
     res["shares"] = pkv.balanced_shares(w.num_seqs, w.num_kv_heads, w.block_size,
                                         w.block_tables.shape[1], torch_kv_dtype(torch, w.kv_dtype), pt) \
         if w.kv_dtype != "f32" else 0
@@ -707,6 +740,7 @@ def main():
         "bulk_fill": head.get("bulk_fill"),
         "roofline": head["roofline"],
         "us_per_step_events": head["us_per_step_events"],
+        "us_per_step_graph": head["us_per_step_graph"],
         "read_ceiling": ceiling,
         "block_moves": moves,
         "kernel_source_sha": kernel_source_sha(),

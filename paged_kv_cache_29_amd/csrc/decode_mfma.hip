@@ -214,14 +214,31 @@ void decode_mfma_kernel(DecodeParams p) {
     // Fused step: the range holding the newest token writes it, and the
     // wave that will attend it (chunk append_ch of the piece starting at
     // append_pb; a piece's chunks go to the waves round-robin) is the one
-    // that writes: it waits for its own stores just before it loads that
-    // chunk, and nothing else waits.
+    // that writes.  Its loads are issued here, beside the query's; its
+    // stores go out once the wave's first chunk loads are in flight (or,
+    // when that first load batch holds the chunk itself, just before it),
+    // and the wave waits for them only before it loads that chunk.  No other
+    // wave waits.
     int append_pb = -1, append_ch = -1;
+    bool append_pending = false;
+    AppendRegs<KV, D> app;
     if (!kMQ && p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
       append_pb = t_begin + (L - 1 - t_begin) / kPiece * kPiece;
       append_ch = (L - 1 - append_pb) / 32;
-      if (wave == append_ch % W) append_new_token<KV, D, BS>(p, b, kvh, L - 1, lane);
+      if (wave == append_ch % W) {
+        append_load<KV, D, BS>(p, b, kvh, L - 1, lane, app);
+        append_pending = true;
+      }
     }
+    auto append_flush = [&]() {
+      if (append_pending) {
+        append_store<KV, D, BS>(p, kvh, L - 1, lane, app);
+        append_pending = false;
+      }
+    };
+    // INT4 (three waves per SIMD) has no registers to carry the row: it
+    // stores at once
+    if constexpr (kI4) append_flush();
 
     // Q^T operand (B of the score MFMA): lane (c, g), tile t, MFMA j, 8 dims.
     bf16x8 qf[NT][NJ];
@@ -573,27 +590,33 @@ void decode_mfma_kernel(DecodeParams p) {
       {
         ChunkT cb[NB];
         int blk[2], row0[2];
-        // this wave holds the chunk written by the append in this piece, at
-        // or after chunk ch: wait for the append's stores before loading it
-        auto append_wait = [&](int ch) {
-          if (pb == append_pb && wave == append_ch % W && append_ch >= ch) __builtin_amdgcn_s_waitcnt(0);
+        // this wave holds the chunk written by the append in this piece,
+        // among chunks ch .. last: store now if not done yet, and wait for
+        // the append's stores before loading it
+        auto append_wait = [&](int ch, int last) {
+          if (pb == append_pb && wave == append_ch % W && append_ch >= ch && append_ch <= last) {
+            append_flush();
+            __builtin_amdgcn_s_waitcnt(0);
+          }
         };
         for (int ch = wave; ch < nchunks; ch += NB * W) {
           if (ch + (NB - 1) * W < nclean) {
-            if (ch + (NB - 1) * W >= append_ch) append_wait(ch);
+            append_wait(ch, ch + (NB - 1) * W);
 #pragma unroll
             for (int k = NB - 1; k >= 0; --k) {
               chunk_blocks(ch + k * W, blk, row0);
               ld.load(cb[k], blk, row0);
             }
             __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of the math
+            append_flush();  // the append's stores behind the batch's loads
 #pragma unroll
             for (int k = NB - 1; k >= 0; --k) consume(cb[k], ch + k * W, kBatchMasked{});
           } else {
             for (int c2 = ch; c2 < nchunks; c2 += W) {
-              if (c2 >= append_ch) append_wait(c2);
+              append_wait(c2, c2);
               chunk_blocks(c2, blk, row0);
               ld.load(cb[0], blk, row0);
+              append_flush();
               consume(cb[0], c2, std::true_type{});
             }
           }

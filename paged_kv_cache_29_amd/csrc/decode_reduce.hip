@@ -138,9 +138,11 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
 // the group's shared tokens (per head, in rows [0, bal_row0)) come first
 // and every unit is merged, whatever its count.  The wave serves all G heads of the
 // unit: 64 / G lanes per head, each owning DPL = D G / 64 consecutive dims,
-// so a unit that needs nothing costs one load.  The splits' maxima are
-// loaded 8 at a time, then their rows in batches, all loads of a batch
-// issued before any is used.  (Balanced shares serve bf16 queries only, so
+// so a unit that needs nothing costs one load.  The first batch of
+// partials (maxima, sums and rows) is loaded with the maxima of the rest,
+// and each later batch's loads are all issued before any is used, so a
+// merge of up to NBATCH partials waits on two dependent loads: the record,
+// then everything else.  (Balanced shares serve bf16 queries only, so
 // the output is bf16.)
 template <int D, int G>
 __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_units_kernel(DecodeParams p) {
@@ -190,24 +192,37 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_units_kern
       for (int k = 0; k < DPL; ++k) x[k] = a[k];
     }
   };
-  float M = -INFINITY;
-  for (int j0 = 0; j0 < n; j0 += 8) {
-    float mm[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) mm[q] = p.ws_m[slot(min(j0 + q, n - 1))];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) M = fmaxf(M, mm[q]);
-  }
+  // the first batch's maxima, sums and rows are loaded together with the
+  // maxima of any later partials, before the overall maximum is known
   float num[NV * 4];
 #pragma unroll
   for (int k = 0; k < NV * 4; ++k) num[k] = 0.f;
   float den = 0.f;
-  for (int j0 = 0; j0 < n; j0 += NBATCH) {
+  float x0[NBATCH][NV * 4], m0[NBATCH], l0[NBATCH];
+#pragma unroll
+  for (int q = 0; q < NBATCH; ++q) {
+    const size_t r = slot(min(q, n - 1));  // past the last partial: weight 0 below
+    m0[q] = p.ws_m[r];
+    l0[q] = p.ws_l[r];
+    load_row(r, x0[q]);
+  }
+  float M = -INFINITY;
+  for (int j = NBATCH; j < n; ++j) M = fmaxf(M, p.ws_m[slot(j)]);
+#pragma unroll
+  for (int q = 0; q < NBATCH; ++q) M = fmaxf(M, m0[q]);
+#pragma unroll
+  for (int q = 0; q < NBATCH; ++q) {
+    const float w = (q < n) ? exp2f(m0[q] - M) : 0.f;
+    den = fmaf(w, l0[q], den);
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) num[k] = fmaf(w, x0[q][k], num[k]);
+  }
+  for (int j0 = NBATCH; j0 < n; j0 += NBATCH) {
     float x[NBATCH][NV * 4];
     float mj[NBATCH], lj[NBATCH];
 #pragma unroll
     for (int q = 0; q < NBATCH; ++q) {
-      const size_t r = slot(min(j0 + q, n - 1));  // past the last partial: weight 0 below
+      const size_t r = slot(min(j0 + q, n - 1));
       mj[q] = p.ws_m[r];
       lj[q] = p.ws_l[r];
       load_row(r, x[q]);

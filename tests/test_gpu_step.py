@@ -47,3 +47,48 @@ def test_fused_step_full_size_7b():
     s = int(w.slot_new[3])
     k_row = bf16_bits_of(dw.k_cache[s // 16, :, s % 16, :])
     assert np.array_equal(k_row, w.k_new[3])
+
+
+@pytest.mark.parametrize("kv,G,D", [("f32", 1, 64), ("bf16", 8, 128), ("bf16", 1, 128), ("i8", 8, 128)])
+def test_fused_step_graph_replays_match_eager(kv, G, D):
+    """The fused step captured in a HIP graph: every replay (new queries and
+    new K/V rows copied in eagerly, synchronised between replays) equals an
+    eager call on the same inputs bit for bit, outputs and caches."""
+    import paged_kv_cache_29_amd as pkv
+    from gpu_helpers import DEV, out_f64
+
+    Hkv = 2
+    w = workloads.make_custom(300 + G, RAGGED, G * Hkv, Hkv, D, 16, kv_dtype=kv)
+    dw = DeviceWorkload(w)
+    dw.step_fused()                                      # coded caches filled; warm
+    need = pkv.workspace_size(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                              w.block_tables.shape[1], 0)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=DEV)
+
+    def call(o):
+        pkv.paged_attention_decode_step(o, dw.q, dw.k_new, dw.v_new, dw.k_cache, dw.v_cache,
+                                        dw.block_tables, dw.context_lens, w.scale, w.num_heads,
+                                        w.num_kv_heads, w.head_dim, w.block_size, k_scale=dw.k_scale,
+                                        v_scale=dw.v_scale, workspace=ws)
+
+    out = torch.empty_like(dw.q)
+    call(out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    for i in range(3):
+        for t in (dw.q, dw.k_new, dw.v_new):
+            t.copy_(torch.randn(t.shape, generator=gen).to(t.dtype).to(DEV))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out_f64(out)
+        caches = _cache_bytes(dw)
+        ref = torch.empty_like(dw.q)
+        call(ref)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, out_f64(ref)), f"replay {i} differs from the eager call"
+        for x, y in zip(caches, _cache_bytes(dw)):
+            assert np.array_equal(x, y), f"replay {i}: caches differ from the eager call's"
