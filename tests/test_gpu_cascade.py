@@ -70,6 +70,32 @@ def test_cascade_fused_step_equals_write_then_cascade(kv, G, D, bs, own, spt):
     assert_parity(got, oracle_out(w), kv, f"fused cascade step {kv} G={G} bs={bs} spt={spt}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2"])
+@pytest.mark.parametrize("G,D,bs,group", [(4, 128, 16, 3), (1, 64, 32, None), (8, 128, 16, 5)])
+def test_cascade_many_short_tails(kv, G, D, bs, group):
+    """Many short own tails (at least 1024 (sequence, kv-head) units, tails
+    of at most 512 tokens past the shared blocks): the one-launch cascade
+    gives each unit to one wave.  Tails of 1 .. 400 tokens against the
+    oracle; the fused step equals kv_cache_write followed by the cascade,
+    bit for bit."""
+    prefix, Hkv, B = 96, 8, 128
+    tails = [1, 2, 15, 16, 17, 33, 100, 255, 400, 7, 64]
+    lens = [prefix + tails[i % len(tails)] for i in range(B)]
+    assert B * Hkv >= 1024 and (-(-max(lens) // bs) - prefix // bs) * bs <= 512
+    w = workloads.make_custom(900 + G + bs, lens, G * Hkv, Hkv, D, bs, kv_dtype=kv, prefix=prefix,
+                              prefix_group_size=group)
+    a, b = DeviceWorkload(w), DeviceWorkload(w)
+    ref = a.step_cascade()
+    got = b.step_cascade(fused=True)
+    assert np.array_equal(got.view(np.uint64), ref.view(np.uint64)), "outputs differ"
+    for x, y in zip(_cache_bytes(a), _cache_bytes(b)):
+        assert np.array_equal(x, y), "caches differ"
+    samples = sample_pairs(w, n=32, seed=G + bs)
+    ref_o = oracle_out(w, samples=samples)
+    for bb, h in samples:
+        assert_parity(got[bb, h], ref_o[bb, h], kv, f"short tails {kv} G={G} bs={bs} (b={bb}, h={h})")
+
+
 def test_cascade_equals_plain_decode_within_rounding():
     w = workloads.make_custom(42, [500 + x for x in RAGGED], 32, 8, 128, 16, prefix=500)
     a, b = DeviceWorkload(w), DeviceWorkload(w)
