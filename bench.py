@@ -3,11 +3,11 @@
 
 One step = the hot path once over one batch: write each sequence's new
 token into its tail-block slot, then attend every sequence's new query over
-its whole paged context.  It is timed through the fused entry point
-(paged_attention_decode_step: the partition kernel appends the token and
-attends, then the split-context reduce runs when a context spans several
-partitions), and again as three launches (kv_cache_write or the int8
-quantising write, then paged_attention_decode's two kernels), reported under
+its whole paged context.  It is timed through the fused entry point, one
+call per step (paged_attention_decode_step: the partition kernel appends
+the token and attends, then the split-context reduce runs when a context
+spans several partitions), and again as two calls (kv_cache_write or the
+quantising write, then paged_attention_decode), reported under
 ``unfused``.  Inputs are seeded synthetic data already resident in HBM.
 
 Prints ONE JSON line.  ``value`` is the KV bytes a step must read divided by
@@ -159,15 +159,14 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None, counter_only
              w.head_dim, w.block_size)
 
     def step_fused():
-        # one step: append the new tokens and attend (+ reduce when split)
-        pkv.paged_attention_decode_step_partitions(*sargs, **dkw)
-        pkv.paged_attention_decode_reduce(*dargs, **dkw)
+        # one step, one call: append the new tokens and attend (the
+        # partition kernel, then the reduce when a context was split)
+        pkv.paged_attention_decode_step(*sargs, **dkw)
 
     def step_unfused():
-        # the same step as three launches: cache write, partitions, reduce
+        # the same step as the cache write, then decode (partitions + reduce)
         write()
-        pkv.paged_attention_decode_partitions(*dargs, **dkw)
-        pkv.paged_attention_decode_reduce(*dargs, **dkw)
+        pkv.paged_attention_decode(*dargs, **dkw)
 
     def loop_time(fn):
         """Average duration of fn over K back-to-back launches (events on the launch stream)."""

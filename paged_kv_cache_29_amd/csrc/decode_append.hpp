@@ -82,7 +82,7 @@ __device__ __forceinline__ void append_store(const DecodeParams& p, int kvh, int
 #pragma unroll
     for (int which = 0; which < 2; ++which) {  // K, then V
       const float x0 = which == 0 ? r.k[0] : r.v[0], x1 = which == 0 ? r.k[1] : r.v[1];
-      const float a = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+      const float a = groups_max(row16_max(fmaxf(fabsf(x0), fabsf(x1))));
       const float s = a / 7.0f;
       if (lane < D / 2) {
         const uint8_t byte = static_cast<uint8_t>(pack_int4_pair(quantize_sym<7>(x0, s), quantize_sym<7>(x1, s)));
@@ -102,7 +102,7 @@ __device__ __forceinline__ void append_store(const DecodeParams& p, int kvh, int
       float a = 0.f;
 #pragma unroll
       for (int i = 0; i < R::N; ++i) a = fmaxf(a, fabsf(which == 0 ? r.k[i] : r.v[i]));
-      a = wave_max(a);
+      a = groups_max(row16_max(a));  // the row's absmax (exact in any order)
       const float s = a / (KV == KvKind::FP8 ? 448.0f : (KV == KvKind::E5M2 ? 57344.0f : 127.0f));
 #pragma unroll
       for (int i = 0; i < R::N; ++i) {

@@ -135,8 +135,7 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
 // and the shared-prefix workgroups, dispatched first, leave the shares to
 // fill the GPU around them.  fused_prefix_wgs is a multiple of 8, so a
 // share's XCD follows its index as in the plain balanced launch.
-template <KvKind KV, int D, int BS, int W, bool kMQ, int NT, bool kBal, bool kVec = false, int kPrefixNT = 0,
-          bool kWU = false>
+template <KvKind KV, int D, int BS, int W, bool kMQ, int NT, bool kBal, bool kVec = false, int kPrefixNT = 0>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, NT>, kWavesPerSimd<KV, NT>)))
 void decode_mfma_kernel(DecodeParams p) {
@@ -156,8 +155,7 @@ void decode_mfma_kernel(DecodeParams p) {
     vbid -= np;
     vgrid -= np;
     if constexpr (!kBal) {  // fixed partitions: (sequence, kv-head) fastest, in whole slabs
-      // (wave units: W units per workgroup)
-      const int units = kWU ? (p.num_seqs * p.num_kv_heads + W - 1) / W : (p.num_seqs * p.num_kv_heads + 15) & ~15;
+      const int units = (p.num_seqs * p.num_kv_heads + 15) & ~15;
       vpart = vbid / units;
       vbid -= vpart * units;
     }
@@ -169,13 +167,6 @@ void decode_mfma_kernel(DecodeParams p) {
   static_assert(NT >= 1 && NT <= kMqDecodeMaxTiles && (kMQ || NT == 1), "column tiles");
   static_assert(!(kBal && kMQ), "balanced shares are a one-query mode");
   static_assert(!kVec || (KV == KvKind::BF16 && NT == 1 && !kMQ), "vector-ALU path: bf16, one head");
-  static_assert(!kWU || (!kBal && !kMQ && kPrefixNT > 0), "wave units: one-launch cascade, fixed partitions");
-  // kWU: every wave attends a range of its own, as a one-wave workgroup
-  // would (no chunk sharing, no merge, no barrier); wv / WW are the wave
-  // index and count the range is spread over
-  const int wv0 = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wv = kWU ? 0 : wv0;
-  constexpr int WW = kWU ? 1 : W;
   // the registers of the extra tiles' states replace the second chunk
   constexpr int NB = NT > 1 ? 1 : kBatch<KV>;
   static_assert(D == 64 || D == 128, "head_dim");
@@ -234,7 +225,7 @@ void decode_mfma_kernel(DecodeParams p) {
     if (!kMQ && p.k_new != nullptr && L - 1 >= t_begin && L - 1 < t_end) {
       append_pb = t_begin + (L - 1 - t_begin) / kPiece * kPiece;
       append_ch = (L - 1 - append_pb) / 32;
-      if (wv == append_ch % WW) {
+      if (wave == append_ch % W) {
         append_load<KV, D, BS>(p, b, kvh, L - 1, lane, app);
         append_pending = true;
       }
@@ -578,7 +569,7 @@ void decode_mfma_kernel(DecodeParams p) {
         }
       };
 
-      // ---- this wave's chunks ch = wv, wv + WW, ... of the piece in
+      // ---- this wave's chunks ch = wave, wave + W, ... of the piece in
       // batches of NB: the loads of the whole batch are issued before any
       // chunk is consumed, and no load stays pending across iterations, so
       // every wait counts exactly the loads behind it.  A batch is loaded and
@@ -603,25 +594,25 @@ void decode_mfma_kernel(DecodeParams p) {
         // among chunks ch .. last: store now if not done yet, and wait for
         // the append's stores before loading it
         auto append_wait = [&](int ch, int last) {
-          if (pb == append_pb && wv == append_ch % WW && append_ch >= ch && append_ch <= last) {
+          if (pb == append_pb && wave == append_ch % W && append_ch >= ch && append_ch <= last) {
             append_flush();
             __builtin_amdgcn_s_waitcnt(0);
           }
         };
-        for (int ch = wv; ch < nchunks; ch += NB * WW) {
-          if (ch + (NB - 1) * WW < nclean) {
-            append_wait(ch, ch + (NB - 1) * WW);
+        for (int ch = wave; ch < nchunks; ch += NB * W) {
+          if (ch + (NB - 1) * W < nclean) {
+            append_wait(ch, ch + (NB - 1) * W);
 #pragma unroll
             for (int k = NB - 1; k >= 0; --k) {
-              chunk_blocks(ch + k * WW, blk, row0);
+              chunk_blocks(ch + k * W, blk, row0);
               ld.load(cb[k], blk, row0);
             }
             __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of the math
             append_flush();  // the append's stores behind the batch's loads
 #pragma unroll
-            for (int k = NB - 1; k >= 0; --k) consume(cb[k], ch + k * WW, kBatchMasked{});
+            for (int k = NB - 1; k >= 0; --k) consume(cb[k], ch + k * W, kBatchMasked{});
           } else {
-            for (int c2 = ch; c2 < nchunks; c2 += WW) {
+            for (int c2 = ch; c2 < nchunks; c2 += W) {
               append_wait(c2, c2);
               chunk_blocks(c2, blk, row0);
               ld.load(cb[0], blk, row0);
@@ -660,7 +651,7 @@ void decode_mfma_kernel(DecodeParams p) {
       Lsum[t] = l_run[t];
     }
 
-    if constexpr (WW > 1) {
+    if constexpr (W > 1) {
       // the waves' states merge into wave 0 through LDS, one column tile at a
       // time (the buffers hold one tile)
 #pragma unroll
@@ -914,13 +905,6 @@ void decode_mfma_kernel(DecodeParams p) {
       if (u >= p.num_seqs * Hkv) return;  // uniform across the workgroup
       b = u / Hkv;
       kvh = u - b * Hkv;
-    } else if constexpr (kWU) {
-      // wave w of workgroup i: unit W i + w (kv-head pairs in one
-      // workgroup, so on one XCD)
-      const int u = vbid * W + wv0;
-      if (u >= p.num_seqs * Hkv) return;  // this wave only: wave units share no barrier
-      b = u / Hkv;
-      kvh = u - b * Hkv;
     } else {
       // slabs of 16 (sequence, kv-head) units: unit 16s + 2q + j runs as
       // workgroup 16s + 8j + q, so units 2q and 2q + 1 (kv-heads whose scale
@@ -946,10 +930,10 @@ void decode_mfma_kernel(DecodeParams p) {
     // cascade: the group's shared tokens are attended by the prefix kernel
     const bool cascade = !kMQ && p.group_start != nullptr;
     const int t_begin = (cascade ? group_shared_tokens(p, group_of(p, b)) : 0) + part * PT;
-    if ((kMQ || cascade || part != 0) && t_begin >= L) return;  // uniform across the workgroup (wave units: the wave)
+    if ((kMQ || cascade || part != 0) && t_begin >= L) return;  // uniform across the workgroup
 
     if (L <= 0) {  // empty context: zero output
-      for (int i = kWU ? lane : threadIdx.x; i < G * D; i += (kWU ? 1 : W) * kWave)
+      for (int i = threadIdx.x; i < G * D; i += W * kWave)
         out[(static_cast<size_t>(b) * H + kvh * G) * D + i] = 0;
       return;
     }
@@ -1037,7 +1021,7 @@ hipError_t launch_decode_mfma(const DecodeParams& p, KvKind kv, hipStream_t s) {
   return launch_kv<KvKind::BF16>(p, s);
 }
 
-template <KvKind KV, int D, int BS, bool kBal, bool kWU = false>
+template <KvKind KV, int D, int BS, bool kBal>
 void launch_fused_inst(const DecodeParams& p, dim3 grid, hipStream_t s) {
   const dim3 block(kDecodeWaves * kWave);
   const int G = p.num_heads / p.num_kv_heads;
@@ -1045,34 +1029,31 @@ void launch_fused_inst(const DecodeParams& p, dim3 grid, hipStream_t s) {
   if constexpr (KV == KvKind::BF16) {
     if (G == 1) {  // one head per kv-head: the vector-ALU path
       if (two)
-        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, true, 2, kWU>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, true, 2>), grid, block, 0, s, p);
       else
-        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, true, 1, kWU>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, true, 1>), grid, block, 0, s, p);
       return;
     }
   }
   if (two)
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, false, 2, kWU>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, false, 2>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, false, 1, kWU>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, false, 1>), grid, block, 0, s, p);
 }
 
 template <KvKind KV, int D, int BS>
 hipError_t launch_fused_t(const DecodeParams& p, hipStream_t s) {
   // balanced shares, or a workgroup per (sequence, kv-head, partition of the
-  // own tokens), or a wave per one (wave units, kDecodeWaves units per
-  // workgroup)
-  const int64_t units = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads;
-  const int64_t own = p.bal_shares > 0 ? p.bal_shares
-                      : p.wave_units   ? (units + kDecodeWaves - 1) / kDecodeWaves * (p.num_parts - p.prefix_parts)
-                                       : ((units + 15) & ~int64_t(15)) * (p.num_parts - p.prefix_parts);
+  // own tokens)
+  const int64_t own = p.bal_shares > 0
+                          ? p.bal_shares
+                          : ((static_cast<int64_t>(p.num_seqs) * p.num_kv_heads + 15) & ~int64_t(15)) *
+                                (p.num_parts - p.prefix_parts);
   const int64_t total = static_cast<int64_t>(p.fused_prefix_wgs) + own;
   if (own <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(total));
   if (p.bal_shares > 0)
     launch_fused_inst<KV, D, BS, true>(p, grid, s);
-  else if (p.wave_units)
-    launch_fused_inst<KV, D, BS, false, true>(p, grid, s);
   else
     launch_fused_inst<KV, D, BS, false>(p, grid, s);
   return hipGetLastError();

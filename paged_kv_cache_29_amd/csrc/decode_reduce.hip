@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
   const float l0 = lane < nparts ? l[slot(lane)] : 0.f;
   float M = m0;
   for (int i = lane + kWave; i < nparts; i += kWave) M = fmaxf(M, m[slot(i)]);
-  M = wave_max(M);
+  M = groups_max(row16_max(M));  // lane moves on the vector ALUs, no LDS
 
   float den = 0.f;
   for (int first = 0; first < nparts; first += kWave) {
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_kernel(Dec
       add8(x, j0, cnt, wv);
     }
   }
-  den = wave_sum(den);
+  den = groups_sum(row16_sum(den));
 #pragma unroll
   for (int k = 0; k < ND; ++k) {
     const float o = num[k] / den;

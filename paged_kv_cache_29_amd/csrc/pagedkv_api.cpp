@@ -357,7 +357,6 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   p.ws_unit = nullptr;
   p.bal_row0 = 0;
   p.fused_prefix_wgs = p.fused_prefix_qtiles = p.fused_prefix_tiles = 0;
-  p.wave_units = 0;
   if (bal && need) {
     p.ws_acc = reinterpret_cast<float*>(ws);
     p.ws_m = reinterpret_cast<float*>(ws + bl.acc);
@@ -571,14 +570,6 @@ bool cascade_balanced_for(int32_t num_seqs, int32_t num_kv_heads, int32_t max_bl
   return units * ((ctx + kChunk - 1) / kChunk) < (int64_t(1) << 40) &&
          units + 2 * int64_t(kCascadeShareRounds) * max_shares() < 0x7fffffff;
 }
-
-// Many short own tails (at most kWaveUnitMaxTokens past the shared blocks,
-// by the tables' width, over at least kWaveUnitMinUnits (sequence, kv-head)
-// units) on fixed partitions take a wave per unit in the one-launch
-// cascade: a workgroup per unit spends most of its time on the set-up, the
-// merge of its waves and their barriers around a few chunks each.
-constexpr int32_t kWaveUnitMaxTokens = 512;
-constexpr int64_t kWaveUnitMinUnits = 1024;
 
 // The automatic choice for the sequences' own tokens: balanced shares when
 // they may span several partitions (as for decode); short ones (a long
@@ -953,8 +944,6 @@ pkv_status cascade_call(void* out, const void* q, const void* k_new, const void*
     p.ws_m = reinterpret_cast<float*>(ws + acc_bytes);
     p.ws_l = reinterpret_cast<float*>(ws + acc_bytes + ml_bytes);
     p.num_parts = cs.pparts + cs.sparts;
-    p.wave_units = static_cast<int64_t>(num_seqs) * num_kv_heads >= kWaveUnitMinUnits &&
-                   (static_cast<int64_t>(max_blocks_per_seq) - max_shared_blocks) * block_size <= kWaveUnitMaxTokens;
   }
   p.group_start = group_start;
   p.group_shared_blocks = group_shared_blocks;

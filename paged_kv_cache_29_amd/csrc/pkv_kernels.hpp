@@ -86,11 +86,6 @@ struct DecodeParams {
   int32_t fused_prefix_wgs;
   int32_t fused_prefix_qtiles;
   int32_t fused_prefix_tiles;
-  // One-launch shared-prefix decode on fixed partitions: each wave attends
-  // one (sequence, kv-head) unit's partition alone (a workgroup holds W
-  // consecutive units), instead of a workgroup per unit (set by its
-  // launcher for many short own tails).
-  int32_t wave_units;
 };
 
 struct WriteParams {

@@ -73,15 +73,13 @@ def test_cascade_fused_step_equals_write_then_cascade(kv, G, D, bs, own, spt):
 @pytest.mark.parametrize("kv", ["bf16", "i8", "fp8", "e5m2"])
 @pytest.mark.parametrize("G,D,bs,group", [(4, 128, 16, 3), (1, 64, 32, None), (8, 128, 16, 5)])
 def test_cascade_many_short_tails(kv, G, D, bs, group):
-    """Many short own tails (at least 1024 (sequence, kv-head) units, tails
-    of at most 512 tokens past the shared blocks): the one-launch cascade
-    gives each unit to one wave.  Tails of 1 .. 400 tokens against the
-    oracle; the fused step equals kv_cache_write followed by the cascade,
-    bit for bit."""
+    """Many sequences with short own tails past a shared prefix (1024
+    (sequence, kv-head) units, tails of 1 .. 400 tokens): against the
+    oracle, and the fused step equals kv_cache_write followed by the
+    cascade, bit for bit."""
     prefix, Hkv, B = 96, 8, 128
     tails = [1, 2, 15, 16, 17, 33, 100, 255, 400, 7, 64]
     lens = [prefix + tails[i % len(tails)] for i in range(B)]
-    assert B * Hkv >= 1024 and (-(-max(lens) // bs) - prefix // bs) * bs <= 512
     w = workloads.make_custom(900 + G + bs, lens, G * Hkv, Hkv, D, bs, kv_dtype=kv, prefix=prefix,
                               prefix_group_size=group)
     a, b = DeviceWorkload(w), DeviceWorkload(w)
