@@ -202,7 +202,7 @@ def kv_cache_write_fp8_e5m2(k, v, k_cache, v_cache, k_scale, v_scale, slot_mappi
 def kv_cache_write_int4(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping):
     """Quantise fp32 K/V rows to INT4 codes in [-7, 7] + per-(token, kv-head)
     scale and scatter; the caches are uint8 tensors ``[NB, Hkv, bs, D/2]``
-    (K) and ``[NB, Hkv, D/2, bs]`` (V), two consecutive dims per byte."""
+    (K) and ``[NB, Hkv, bs/4, D/2, 4]`` (V), two consecutive dims per byte."""
     _write_codes(k, v, k_cache, v_cache, k_scale, v_scale, slot_mapping, torch.uint8,
                  "pkv_kv_cache_write_int4")
 

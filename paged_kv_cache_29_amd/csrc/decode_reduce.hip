@@ -149,7 +149,9 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void decode_reduce_units_kern
   constexpr int LPH = kWave / G;  // lanes per head
   constexpr int DPL = D / LPH;    // dims per lane
   constexpr int NV = (DPL + 3) / 4;  // f32x4 (or shorter) pieces per row
-  constexpr int NBATCH = DPL >= 32 ? 2 : (DPL >= 16 ? 4 : 8);
+  // partials per batch: a 70B-shaped unit splits over up to ~6 shares (G = 8),
+  // merged in one batch
+  constexpr int NBATCH = DPL >= 64 ? 2 : (DPL >= 32 ? 4 : 8);
   const int lane = threadIdx.x & (kWave - 1);
   const int u = __builtin_amdgcn_readfirstlane(blockIdx.x * kReduceWaves + (threadIdx.x >> 6));
   if (u >= p.num_seqs * p.num_kv_heads) return;  // the whole wave
