@@ -358,12 +358,15 @@ pkv_status pkv_paged_attention_decode_step_partitions(
  * (BF16, I4) with the sizes of decode; an fp32 cache returns
  * PKV_ERR_UNSUPPORTED.  The workspace size comes from
  * pkv_paged_attention_cascade_workspace_size with the same sizes and is
- * needed whenever num_seqs > 0.  Three launches: prefix kernel (skipped when
- * max_shared_blocks is 0) on a second stream of the library's (one per
- * device, created on first use, default priority), partition kernel on
- * `stream` beside it, then the reduce on `stream` after both (the second
- * stream is forked from and joined back into `stream` by events, so the
- * call orders like three launches on `stream`, also under graph capture).
+ * needed whenever num_seqs > 0.  Launches: for bf16 and byte-code caches,
+ * one kernel on `stream` holds the shared-prefix workgroups and the
+ * workgroups of the sequences' own tokens, then the reduce follows on
+ * `stream`.  INT4: the prefix kernel (skipped when max_shared_blocks is 0)
+ * on a second stream of the library's (one per device, created on first
+ * use, default priority), the partition kernel on `stream` beside it, then
+ * the reduce on `stream` after both (the second stream is forked from and
+ * joined back into `stream` by events, so the call orders like launches on
+ * `stream`, also under graph capture).
  * Not checked unless PKV_DEBUG=1 (device data): the group arrays as stated
  * above; every member's context_lens >= S_g; the shared entries really are
  * equal (if not, the first member's blocks are used for the whole group).

@@ -116,9 +116,9 @@ pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq, int32_t* pairs, in
 /*
  * Copy whole blocks between two pools of the layout in pagedkv.h: for each
  * pair i, block pairs[2i] of the source pool goes to block pairs[2i+1] of
- * the destination pool — its K tile rows [Hkv][bs][D], V tiles [Hkv][D][bs]
- * (INT4: [Hkv][bs][D/2] and [Hkv][D/2][bs] bytes) and, for int8 / FP8 /
- * INT4 caches, its k_scale / v_scale rows [Hkv][bs].
+ * the destination pool — its K tile rows [Hkv][bs][D], V tiles
+ * [Hkv][bs/4][D][4] (INT4: [Hkv][bs][D/2] and [Hkv][bs/4][D/2][4] bytes)
+ * and, for int8 / FP8 / INT4 caches, its k_scale / v_scale rows [Hkv][bs].
  * Pools may be the same (copy-on-write) or one of them pinned host memory
  * the device can address (swapping; e.g. hipHostMalloc'd, the kernel reads
  * or writes it over the host link).  pairs: device int32 [n][2].

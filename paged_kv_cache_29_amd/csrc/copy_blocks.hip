@@ -3,7 +3,7 @@
 // ("LLM Engineering (5)", "Block manager: how paging works").
 //
 // Block b of a pool is four contiguous byte ranges: its K tiles
-// k[b][Hkv][bs][D], its V tiles v[b][Hkv][D][bs] (INT4: half the bytes) and,
+// k[b][Hkv][bs][D], its V tiles v[b][Hkv][bs/4][D][4] (INT4: half the bytes) and,
 // for int8 / FP8 / INT4 caches, its scale rows k_scale[b][Hkv][bs],
 // v_scale[b][Hkv][bs].  Workgroup
 // (pair, part, piece) copies one 16 KB piece of one part of one pair with

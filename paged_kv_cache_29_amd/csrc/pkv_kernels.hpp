@@ -104,7 +104,7 @@ struct WriteParams {
 
 // FP8: E4M3 codes; E5M2: the other FP8 format.  I4: two 4-bit codes per
 // byte, two consecutive head dims of one token (K tiles [bs][D/2], V tiles
-// [D/2][bs]).
+// [bs/4][D/2][4]).
 enum class KvKind { F32 = 0, BF16 = 1, I8 = 2, FP8 = 3, I4 = 4, E5M2 = 5 };
 
 // Whole-block copies between two pools: parts 0..3 are the K tiles, the V
