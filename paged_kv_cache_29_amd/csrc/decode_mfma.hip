@@ -154,11 +154,8 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     vbid -= np;
     vgrid -= np;
-    if constexpr (!kBal) {  // fixed partitions: (sequence, kv-head) fastest, in whole slabs
-      const int units = (p.num_seqs * p.num_kv_heads + 15) & ~15;
-      vpart = vbid / units;
-      vbid -= vpart * units;
-    }
+    // (fixed partitions: a workgroup per unit, in whole slabs of 16 units;
+    // it attends the unit's partitions in turn, so vpart stays 0)
   }
   constexpr bool kInt8 = KV != KvKind::BF16;  // codes (int8, FP8, INT4) with scales
   constexpr bool kI4 = KV == KvKind::I4;
@@ -929,7 +926,18 @@ void decode_mfma_kernel(DecodeParams p) {
     }
     // cascade: the group's shared tokens are attended by the prefix kernel
     const bool cascade = !kMQ && p.group_start != nullptr;
-    const int t_begin = (cascade ? group_shared_tokens(p, group_of(p, b)) : 0) + part * PT;
+    const int S = cascade ? group_shared_tokens(p, group_of(p, b)) : 0;
+    if constexpr (kPrefixNT > 0) {
+      // one-launch cascade: the workgroup attends every partition of the
+      // sequence's own tokens in turn (the grid holds one workgroup per
+      // unit, so no workgroup is launched for a partition past a short tail)
+      for (int pt = 0; S + pt * PT < L; ++pt) {
+        if (pt > 0) __syncthreads();  // the merge buffers are reused
+        run(b, kvh, L, S + pt * PT, min(L, S + (pt + 1) * PT), 0, 0, 0, G, false, p.prefix_parts + pt);
+      }
+      return;
+    }
+    const int t_begin = S + part * PT;
     if ((kMQ || cascade || part != 0) && t_begin >= L) return;  // uniform across the workgroup
 
     if (L <= 0) {  // empty context: zero output
@@ -1043,12 +1051,11 @@ void launch_fused_inst(const DecodeParams& p, dim3 grid, hipStream_t s) {
 
 template <KvKind KV, int D, int BS>
 hipError_t launch_fused_t(const DecodeParams& p, hipStream_t s) {
-  // balanced shares, or a workgroup per (sequence, kv-head, partition of the
-  // own tokens)
+  // balanced shares, or a workgroup per (sequence, kv-head) that attends
+  // the partitions of its own tokens in turn
   const int64_t own = p.bal_shares > 0
                           ? p.bal_shares
-                          : ((static_cast<int64_t>(p.num_seqs) * p.num_kv_heads + 15) & ~int64_t(15)) *
-                                (p.num_parts - p.prefix_parts);
+                          : ((static_cast<int64_t>(p.num_seqs) * p.num_kv_heads + 15) & ~int64_t(15));
   const int64_t total = static_cast<int64_t>(p.fused_prefix_wgs) + own;
   if (own <= 0 || total > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(total));
