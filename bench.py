@@ -66,11 +66,21 @@ DESCRIPTIONS = {
 }
 
 
+def code_only(text):
+    """C++ source without its comments and blank lines, so that a comment
+    edit does not read as a kernel change (string literals in these sources
+    hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_sha():
+    """Hash of the partition kernel's sources (code only, comments dropped)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_cache_29_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_29_amd", "csrc", f)) as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

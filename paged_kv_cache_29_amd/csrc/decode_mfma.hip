@@ -8,16 +8,18 @@
 // characteristics").  int8, FP8 and INT4 caches hold codes with one fp32
 // scale per (token, kv-head) ([ENG5] "KV-cache quantization").
 //
-// Work decomposition.  One workgroup of kDecodeWaves waves owns one
-// (sequence, kv-head, context partition of part_tokens tokens).  The G query
-// heads of the kv-head share every K/V byte it loads: the tile feeds one
-// matrix-core contraction whose N dimension is the head group.  The waves of
-// the workgroup take 32-token chunks of the partition round-robin, each
-// keeping its own online-softmax state; the states are merged through LDS at
-// the end.  A sequence that fits one partition is finished here; longer ones
-// leave (max, sum, unnormalised output) partials for the reduce kernel.
-// Each wave issues the loads of a batch of two chunks before consuming
-// either.
+// Work decomposition.  A workgroup of kDecodeWaves waves attends token
+// ranges of (sequence, kv-head) units: one (unit, context partition of
+// part_tokens tokens) on fixed partitions, or the units its equal share of
+// all units' chunks covers (kBal, below).  The G query heads of the kv-head
+// share every K/V byte it loads: the tile feeds one matrix-core contraction
+// whose N dimension is the head group (one head per kv-head: the vector
+// ALUs instead, kVec).  The waves take 32-token chunks of a range
+// round-robin, each keeping its own online-softmax state; the states are
+// merged through LDS at the end.  A unit attended whole is finished here;
+// split ones leave (max, sum, unnormalised output) partials for the reduce
+// kernel.  Each wave issues the loads of a batch of two chunks before
+// consuming either.
 //
 // Per 32-token chunk (two 16-token sub-tiles: two blocks at bs=16, the two
 // halves of one block at bs=32), one wave does:
@@ -27,7 +29,7 @@
 //     are zero).  The accumulator gives lane group g = l / 16 the scores of
 //     sub-tile tokens 4g .. 4g+3 for head l % 16.
 //   online softmax on the 8 scores a lane holds, max across the 4 lane
-//     groups by shuffles.
+//     groups by lane swaps (v_permlane16/32_swap).
 //   O^T[D x 16 heads] += V^T[D x 32 tok] . P^T[32 tok x 16 heads]   2 * D/16 MFMAs
 //     A operand: V tiles are stored in groups of 4 tokens, dim-major inside
 //     a group (element (r, d) at ((r / 4) D + d) 4 + r % 4), so the 4 tokens
