@@ -24,15 +24,28 @@ def sample_seqs(w, n, seed):
     return sorted(seqs)
 
 
+CONFIGS = [(1, None), (2, None), (3, None), (4, 16), (4, 32), (5, None), (6, None), (7, None), (8, None)]
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
-@pytest.mark.parametrize("cfg,bs", [(1, None), (2, None), (3, None), (4, 16), (4, 32), (5, None),
-                                    (6, None), (7, None), (8, None)])
+@pytest.mark.parametrize("cfg,bs", CONFIGS)
 def test_full_size_sampled(cfg, bs, seed):
+    _full_size(cfg, bs, seed, fused=False)
+
+
+@pytest.mark.parametrize("cfg,bs", CONFIGS)
+def test_full_size_fused_step_sampled(cfg, bs):
+    """The fused step (the call the benchmark times: the partition kernel
+    appends each new token, then attends) at full size, seed 0."""
+    _full_size(cfg, bs, 0, fused=True)
+
+
+def _full_size(cfg, bs, seed, fused):
     w = workloads.make_config(cfg, seed, block_size=bs)
     print(f"\n[full] config {cfg} seed {seed} bs={w.block_size} B={w.num_seqs} H={w.num_heads} "
-          f"Hkv={w.num_kv_heads} tokens={w.attended_tokens}", flush=True)
+          f"Hkv={w.num_kv_heads} tokens={w.attended_tokens} fused={fused}", flush=True)
     dw = DeviceWorkload(w)
-    got = dw.step()
+    got = dw.step_fused() if fused else dw.step()
     assert np.all(np.isfinite(got))
     # every head of the sampled sequences (the oracle gathers each
     # (sequence, kv-head)'s K/V once and serves all its heads from it)
@@ -42,7 +55,7 @@ def test_full_size_sampled(cfg, bs, seed):
     ref = oracle_out(w, samples=samples, caches=caches)
     kind = w.kv_dtype
     for b in seqs:
-        assert_parity(got[b], ref[b], kind, f"config {cfg} seed {seed} (b={b}, all heads)")
+        assert_parity(got[b], ref[b], kind, f"config {cfg} seed {seed} fused={fused} (b={b}, all heads)")
     # the step's cache write landed bit-exactly in every sampled sequence's tail slot
     bs_ = w.block_size
     for b in seqs:
