@@ -313,6 +313,8 @@ def run_workload(cfg, args, torch, pkv, workloads, block_size=None, counter_only
         res["roofline"]["note"] = ("the whole workload (540 KB of KV) stays in the caches: the step "
                                    "is bound by launch and dependent-load latency, so only us/step counts")
 
+    res["roofline"]["load_policy"] = "non-temporal" if pkv.streams_cache(
+        w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, torch_kv_dtype(torch, w.kv_dtype)) else "default"
     res["shares"] = pkv.balanced_shares(w.num_seqs, w.num_kv_heads, w.block_size,
                                         w.block_tables.shape[1], torch_kv_dtype(torch, w.kv_dtype), pt) \
         if w.kv_dtype != "f32" else 0
@@ -448,31 +450,38 @@ def unique_tile_bytes(w):
 def read_ceiling(torch, pkv, steps=20):
     """The device's read rate for the decode kernel's access pattern: 2 GiB
     of 4 KB tiles gathered in a shuffled order by the tile-read probe (run
-    after the workloads, so the clocks are up; ids range-checked once)."""
+    after the workloads, so the clocks are up; ids range-checked once), with
+    the default load policy (``gbs``) and with the non-temporal hint that
+    decode takes over a large pool (``gbs_non_temporal``)."""
     import numpy as np
     n = 2 << 30
     pool = torch.empty(n, dtype=torch.uint8, device="cuda:0")
     ids = torch.from_numpy(np.random.default_rng(0).permutation(n // 4096).astype(np.int32)).to("cuda:0")
-    best = None
-    for grid in (2048, 4096, 8192):
-        sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda:0")
-        pkv.probe_tile_read(pool, ids, sink, grid, check_ids=True)
-        for _ in range(3):
-            pkv.probe_tile_read(pool, ids, sink, grid, check_ids=False)
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(steps):
-            pkv.probe_tile_read(pool, ids, sink, grid, check_ids=False)
-        t1.record()
-        torch.cuda.synchronize()
-        gbs = n / (t0.elapsed_time(t1) / steps * 1e-3) / 1e9
-        if best is None or gbs > best["gbs"]:
-            best = {"gbs": gbs, "grid": grid}
+    pkv.probe_tile_read(pool, ids, torch.empty(256, dtype=torch.int32, device="cuda:0"), 1, check_ids=True)
+    out = {}
+    for streaming in (False, True):
+        best = None
+        for grid in (2048, 4096, 8192):
+            sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda:0")
+            for _ in range(3):
+                pkv.probe_tile_read(pool, ids, sink, grid, check_ids=False, streaming=streaming)
+            torch.cuda.synchronize()
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(steps):
+                pkv.probe_tile_read(pool, ids, sink, grid, check_ids=False, streaming=streaming)
+            t1.record()
+            torch.cuda.synchronize()
+            gbs = n / (t0.elapsed_time(t1) / steps * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, grid)
+        key = "non_temporal" if streaming else ""
+        out["gbs" + ("_" + key if key else "")] = best[0]
+        out["grid" + ("_" + key if key else "")] = best[1]
     del pool, ids
     torch.cuda.empty_cache()
-    best["probe"] = "pkv_probe_tile_read: 2 GiB of shuffled 4 KB tiles, best grid"
-    return best
+    out["probe"] = "pkv_probe_tile_read: 2 GiB of shuffled 4 KB tiles, best grid, each load policy"
+    return out
 
 
 def block_moves(torch, pkv, steps=10):
@@ -717,7 +726,9 @@ def main():
     print("[bench] block moves ...", file=sys.stderr, flush=True)
     moves = block_moves(torch, pkv)
     for r in results:
-        r["roofline"]["frac_of_read_ceiling"] = r["roofline"]["achieved"] / ceiling["gbs"]
+        nt = r["roofline"].get("load_policy") == "non-temporal"
+        r["roofline"]["frac_of_read_ceiling"] = r["roofline"]["achieved"] / ceiling[
+            "gbs_non_temporal" if nt else "gbs"]
     head = results[0]
     shp = head.pop("_shape")
     for r in results[1:]:

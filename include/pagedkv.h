@@ -222,6 +222,23 @@ int32_t pkv_paged_attention_shares(int32_t num_seqs, int32_t num_kv_heads, int32
                                    pkv_dtype kv_dtype);
 
 /*
+ * 1 if one-query decode (pkv_paged_attention_decode, the fused step and the
+ * no-allocation variant) reads a cache pool of these sizes with the
+ * non-temporal load hint, else 0; 0 also for invalid sizes.  The pool is
+ * num_blocks blocks of num_kv_heads x block_size tokens, each token holding
+ * K and V of head_dim elements of kv_dtype (half a byte for I4) plus, for
+ * the coded caches, two fp32 scales.  The hint is taken when the pool is
+ * larger than 512 MiB, twice the GPU's memory-side cache: a step then reads
+ * more than that cache can keep until the next step, and loads that skip
+ * it sustain a higher rate.  A smaller pool keeps the default policy, so
+ * that blocks read again (the next step, or by the sequences that share
+ * them) can be served from that cache.  The cascade and multi-query calls
+ * always use the default policy.  The results are the same either way.
+ */
+int32_t pkv_paged_attention_streams_cache(int64_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                                          int32_t head_dim, pkv_dtype kv_dtype);
+
+/*
  * Single-token decode attention over the paged cache ([ENG5] "Two phases
  * with very different characteristics": each decode step attends the new
  * token over the whole cached context; [ENG5] "Paged attention").

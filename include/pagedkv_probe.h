@@ -30,14 +30,17 @@ extern "C" {
  *             pool (not checked: an id out of range is a memory fault)
  *   num_tiles >= 0 (0: no launch)
  *   grid      workgroups of 256 threads, in [1, 65536]
+ *   streaming 0: the default load policy; 1: loads with the non-temporal
+ *             hint, as decode issues them over a cache pool for which
+ *             pkv_paged_attention_streams_cache returns 1
  *   sink      device uint32 [grid * 256], caller-owned, overwritten
  *   stream    hipStream_t as void*, NULL = default stream
  * Returns PKV_ERR_INVALID (nothing launched) for a null pointer, a
- * misaligned pool, num_tiles < 0 or grid out of range; PKV_ERR_HIP if the
- * launch fails.
+ * misaligned pool, num_tiles < 0, grid out of range or streaming not 0 or
+ * 1; PKV_ERR_HIP if the launch fails.
  */
 pkv_status pkv_probe_tile_read(const void* pool, const int32_t* tile_ids, int64_t num_tiles,
-                               int32_t grid, uint32_t* sink, void* stream);
+                               int32_t grid, int32_t streaming, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

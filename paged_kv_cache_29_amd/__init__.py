@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     partition_tokens,
     balanced_shares,
     probe_tile_read,
+    streams_cache,
     workspace_size,
     load as load_library,
     LIB_PATH,

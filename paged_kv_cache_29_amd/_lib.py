@@ -56,6 +56,7 @@ SIGNATURES = {
                                                     c_i32]),
     "pkv_paged_attention_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_attention_shares": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pkv_paged_attention_streams_cache": (c_i32, [c_i64, c_i32, c_i32, c_i32, c_i32]),
     "pkv_paged_attention_decode": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_partitions": (c_i32, _DECODE_ARGS),
     "pkv_paged_attention_decode_noalloc": (c_i32, _DECODE_ARGS[:18] + [c_vp]),
@@ -73,7 +74,7 @@ SIGNATURES = {
     "pkv_paged_attention_multi_query": (c_i32, _DECODE_ARGS[:8] + [c_vp] + _DECODE_ARGS[8:16]
                                         + [c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_size, c_vp]),
     "pkv_paged_attention_multi_query_workspace_size": (c_size, [c_i32] * 9),
-    "pkv_probe_tile_read": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_vp, c_vp]),
+    "pkv_probe_tile_read": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_i32, c_vp, c_vp]),
     "pkv_bm_create": (c_i32, [c_i64, c_i32, c_i64, c_vp, ctypes.POINTER(c_vp)]),
     "pkv_bm_destroy": (None, [c_vp]),
     "pkv_bm_num_free": (c_i64, [c_vp]),
@@ -244,6 +245,14 @@ def balanced_shares(num_seqs, num_kv_heads, block_size, max_blocks_per_seq, kv_d
     (0: fixed partitions)."""
     return int(load().pkv_paged_attention_shares(num_seqs, num_kv_heads, block_size, max_blocks_per_seq,
                                                  requested, _DTYPES[kv_dtype]))
+
+
+def streams_cache(num_blocks, num_kv_heads, block_size, head_dim, kv_dtype):
+    """Whether one-query decode reads a cache pool of these sizes (torch
+    dtype ``kv_dtype``; for INT4 ``head_dim`` is the unpacked width) with the
+    non-temporal load hint."""
+    return bool(load().pkv_paged_attention_streams_cache(int(num_blocks), num_kv_heads, block_size, head_dim,
+                                                         _DTYPES[kv_dtype]))
 
 
 def workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
@@ -488,10 +497,11 @@ def paged_attention_decode_step_partitions(*args, **kwargs):
            "paged_attention_decode_step_partitions")
 
 
-def probe_tile_read(pool, tile_ids, sink, grid, check_ids=True):
+def probe_tile_read(pool, tile_ids, sink, grid, check_ids=True, streaming=False):
     """Measurement aid: read the 4096-byte tiles ``pool[4096*id : 4096*(id+1)]``
     for every id in ``tile_ids`` (the decode kernel's access pattern, no
     arithmetic); ``sink`` is uint32-sized ``[grid * 256]`` and is overwritten.
+    ``streaming`` loads with the non-temporal hint.
 
     ``check_ids`` range-checks the ids first (a device reduction and a
     synchronisation); a timing loop checks once and then passes False."""
@@ -506,7 +516,7 @@ def probe_tile_read(pool, tile_ids, sink, grid, check_ids=True):
         _need(int(tile_ids.min()) >= 0 and int(tile_ids.max()) < pool_tiles,
               "tile_ids must name tiles inside pool")
     st = load().pkv_probe_tile_read(_ptr(pool), _ptr(tile_ids), tile_ids.numel(), int(grid),
-                                    _ptr(sink), _stream(dev))
+                                    1 if streaming else 0, _ptr(sink), _stream(dev))
     _check(st, "probe_tile_read")
 
 

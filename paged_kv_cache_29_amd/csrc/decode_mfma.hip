@@ -137,7 +137,11 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
 // and the shared-prefix workgroups, dispatched first, leave the shares to
 // fill the GPU around them.  fused_prefix_wgs is a multiple of 8, so a
 // share's XCD follows its index as in the plain balanced launch.
-template <KvKind KV, int D, int BS, int W, bool kMQ, int NT, bool kBal, bool kVec = false, int kPrefixNT = 0>
+// kNT: the K/V tiles are loaded with the non-temporal hint (one-query
+// decode over a pool too large for the memory-side cache to keep between
+// steps; the host decides from the pool's size).
+template <KvKind KV, int D, int BS, int W, bool kMQ, int NT, bool kBal, bool kVec = false, int kPrefixNT = 0,
+          bool kNT = false>
 __global__ __launch_bounds__(W * kWave)
 __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<KV, NT>, kWavesPerSimd<KV, NT>)))
 void decode_mfma_kernel(DecodeParams p) {
@@ -162,7 +166,11 @@ void decode_mfma_kernel(DecodeParams p) {
   constexpr bool kInt8 = KV != KvKind::BF16;  // codes (int8, FP8, INT4) with scales
   constexpr bool kI4 = KV == KvKind::I4;
   using ChunkT = typename std::conditional<kI4, ChunkI4<D>, Chunk<kInt8, D>>::type;
-  using LoaderT = typename std::conditional<kI4, ChunkLoaderI4<D, BS>, ChunkLoader<kInt8, D, BS>>::type;
+  // kNT: K/V tiles loaded with the non-temporal hint (one-query decode over
+  // a pool too large to stay in the memory-side cache)
+  static_assert(!kNT || (!kMQ && kPrefixNT == 0), "non-temporal loads: plain decode and step");
+  constexpr int kPol = kNT ? kNonTemporal : 0;
+  using LoaderT = typename std::conditional<kI4, ChunkLoaderI4<D, BS, kPol>, ChunkLoader<kInt8, D, BS, kPol>>::type;
   static_assert(NT >= 1 && NT <= kMqDecodeMaxTiles && (kMQ || NT == 1), "column tiles");
   static_assert(!(kBal && kMQ), "balanced shares are a one-query mode");
   static_assert(!kVec || (KV == KvKind::BF16 && NT == 1 && !kMQ), "vector-ALU path: bf16, one head");
@@ -955,6 +963,23 @@ void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
+// One-query decode (and the fused step): balanced shares or fixed
+// partitions, the vector-ALU form for one bf16 head per kv-head, and the
+// K/V load policy.
+template <KvKind KV, int D, int BS, bool kBal, bool kNT>
+void launch_plain(dim3 grid, bool vec, const DecodeParams& p, hipStream_t s) {
+  const dim3 block(kDecodeWaves * kWave);
+  if constexpr (KV == KvKind::BF16) {
+    if (vec) {
+      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, true, 0, kNT>), grid, block, 0,
+                         s, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, kBal, false, 0, kNT>), grid, block, 0, s,
+                     p);
+}
+
 template <KvKind KV, int D, int BS, bool kMQ>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
   // cascade: slots [0, prefix_parts) belong to the shared-prefix kernel
@@ -989,23 +1014,17 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
       return hipErrorInvalidValue;
     } else {
       const dim3 grid(static_cast<unsigned>(p.bal_shares));
-      if constexpr (KV == KvKind::BF16) {
-        if (vec) {
-          hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, true, true>), grid, block, 0, s, p);
-          return hipGetLastError();
-        }
-      }
-      hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, true>), grid, block, 0, s, p);
+      if (p.stream_loads)
+        launch_plain<KV, D, BS, true, true>(grid, vec, p, s);
+      else
+        launch_plain<KV, D, BS, true, false>(grid, vec, p, s);
     }
   } else {
     const dim3 grid((units + 15u) & ~15u, static_cast<unsigned>(parts));  // whole slabs of 16 units
-    if constexpr (KV == KvKind::BF16) {
-      if (vec) {
-        hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, false, true>), grid, block, 0, s, p);
-        return hipGetLastError();
-      }
-    }
-    hipLaunchKernelGGL((decode_mfma_kernel<KV, D, BS, kDecodeWaves, false, 1, false>), grid, block, 0, s, p);
+    if (p.stream_loads)
+      launch_plain<KV, D, BS, false, true>(grid, vec, p, s);
+    else
+      launch_plain<KV, D, BS, false, false>(grid, vec, p, s);
   }
   return hipGetLastError();
 }

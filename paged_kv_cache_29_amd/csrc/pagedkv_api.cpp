@@ -241,6 +241,25 @@ size_t workspace_bytes_for(int32_t num_seqs, int32_t num_heads, int32_t head_dim
   return acc + 2 * ml;
 }
 
+// The K/V loads of one-query decode take the non-temporal hint when the
+// cache pool holds more than twice the GPU's memory-side cache (256 MiB on
+// MI355X): then the KV a step reads cannot stay cached until the next step,
+// and streaming it past that cache reads faster (7B MHA step 184.1 -> 168.7
+// us, 70B GQA bf16 361 -> 323 us, int8 202 -> 184 us, one box).  A smaller
+// pool may be served from that cache step after step, and so may blocks
+// that many sequences share (the 256-sequence shared-prefix workload, 338
+// MiB of pool: plain step 196 -> 342 us with the hint), so those keep the
+// default policy; shared prefixes have the cascade call, which always does.
+constexpr int64_t kMemorySideCacheBytes = int64_t(256) << 20;
+bool stream_loads_for(pkv::KvKind kv, int64_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                      int32_t head_dim) {
+  // K + V bytes per dim, and per token and kv-head (with the two scales)
+  const int64_t kv_bytes = kv == pkv::KvKind::F32 ? 8 : kv == pkv::KvKind::BF16 ? 4 : kv == pkv::KvKind::I4 ? 1 : 2;
+  const int64_t scales = kv == pkv::KvKind::F32 || kv == pkv::KvKind::BF16 ? 0 : 8;
+  const int64_t per_token = kv_bytes * head_dim + scales;
+  return num_blocks * num_kv_heads * block_size * per_token > 2 * kMemorySideCacheBytes;
+}
+
 struct DecodeSetup {
   pkv::DecodeParams p;
   pkv::KvKind kv;
@@ -357,6 +376,7 @@ pkv_status validate_decode(void* out, const void* q, const void* k_cache, const 
   p.ws_unit = nullptr;
   p.bal_row0 = 0;
   p.fused_prefix_wgs = p.fused_prefix_qtiles = p.fused_prefix_tiles = 0;
+  p.stream_loads = stream_loads_for(kv, num_blocks, num_kv_heads, block_size, head_dim) ? 1 : 0;
   if (bal && need) {
     p.ws_acc = reinterpret_cast<float*>(ws);
     p.ws_m = reinterpret_cast<float*>(ws + bl.acc);
@@ -763,6 +783,23 @@ int32_t pkv_paged_attention_shares(int32_t num_seqs, int32_t num_kv_heads, int32
                                                                                                      : 0;
 }
 
+int32_t pkv_paged_attention_streams_cache(int64_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                                          int32_t head_dim, pkv_dtype kv_dtype) {
+  if (num_blocks < 0 || num_kv_heads <= 0 || !block_size_ok(block_size) || (head_dim != 64 && head_dim != 128))
+    return 0;
+  pkv::KvKind kv;
+  switch (kv_dtype) {
+    case PKV_F32: kv = pkv::KvKind::F32; break;
+    case PKV_BF16: kv = pkv::KvKind::BF16; break;
+    case PKV_I8: kv = pkv::KvKind::I8; break;
+    case PKV_FP8: kv = pkv::KvKind::FP8; break;
+    case PKV_FP8_E5M2: kv = pkv::KvKind::E5M2; break;
+    case PKV_I4: kv = pkv::KvKind::I4; break;
+    default: return 0;
+  }
+  return stream_loads_for(kv, num_blocks, num_kv_heads, block_size, head_dim) ? 1 : 0;
+}
+
 #define PKV_DECODE_ARGS                                                                       \
   out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale, num_seqs,    \
       num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, q_dtype, \
@@ -950,6 +987,7 @@ pkv_status cascade_call(void* out, const void* q, const void* k_new, const void*
   p.num_groups = num_groups;
   p.max_shared_blocks = max_shared_blocks;
   p.prefix_part_tokens = cs.ppt;
+  p.stream_loads = 0;  // the shared blocks are read again from the memory-side cache
   p.prefix_parts = cs.pparts;
   p.part_tokens = cs.spt;
   const hipStream_t strm = static_cast<hipStream_t>(stream);
@@ -1202,14 +1240,16 @@ pkv_status pkv_paged_attention_decode_noalloc(void* out, const void* q, const vo
 }
 
 pkv_status pkv_probe_tile_read(const void* pool, const int32_t* tile_ids, int64_t num_tiles,
-                               int32_t grid, uint32_t* sink, void* stream) {
+                               int32_t grid, int32_t streaming, uint32_t* sink, void* stream) {
   if (!pool || !tile_ids || !sink) return fail(PKV_ERR_INVALID, "probe_tile_read: null pointer");
   if (reinterpret_cast<uintptr_t>(pool) % 4096 != 0)
     return fail(PKV_ERR_INVALID, "probe_tile_read: pool is not 4096-byte aligned");
   if (num_tiles < 0) return fail(PKV_ERR_INVALID, "probe_tile_read: num_tiles < 0");
   if (grid < 1 || grid > 65536) return fail(PKV_ERR_INVALID, "probe_tile_read: grid %d not in [1, 65536]", grid);
+  if (streaming != 0 && streaming != 1)
+    return fail(PKV_ERR_INVALID, "probe_tile_read: streaming must be 0 or 1, got %d", streaming);
   if (num_tiles == 0) return ok();
-  const hipError_t e = pkv::launch_tile_read(pool, tile_ids, num_tiles, grid, sink,
+  const hipError_t e = pkv::launch_tile_read(pool, tile_ids, num_tiles, grid, streaming != 0, sink,
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "probe_tile_read launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -86,6 +86,10 @@ struct DecodeParams {
   int32_t fused_prefix_wgs;
   int32_t fused_prefix_qtiles;
   int32_t fused_prefix_tiles;
+  // One-query decode and the fused step: load the K/V tiles with the
+  // non-temporal hint (set by the host when the pool is too large to stay
+  // in the memory-side cache between steps).
+  int32_t stream_loads;
 };
 
 struct WriteParams {
@@ -194,7 +198,7 @@ hipError_t launch_cache_write(const WriteParams& p, KvKind kind, hipStream_t s);
 // Quantising write of fp32 rows into an int8, FP8 or INT4 cache.
 hipError_t launch_cache_write_codes(const WriteParams& p, KvKind kind, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyParams& p, hipStream_t s);
-hipError_t launch_tile_read(const void* pool, const int32_t* ids, int64_t ntiles, int grid,
+hipError_t launch_tile_read(const void* pool, const int32_t* ids, int64_t ntiles, int grid, bool streaming,
                             uint32_t* sink, hipStream_t s);
 
 }  // namespace pkv

@@ -205,15 +205,56 @@ def test_python_binding_fails_loudly_without_library(tmp_path):
 def test_probe_rejects_bad_arguments(lib):
     f = lib.pkv_probe_tile_read
     pool, ids, sink = ctypes.c_void_p(0x10000), _fake(2), _fake(3)
-    assert f(None, ids, 1, 1, sink, None) == INVALID
-    assert f(pool, None, 1, 1, sink, None) == INVALID
-    assert f(pool, ids, 1, 1, None, None) == INVALID
-    assert f(ctypes.c_void_p(0x10010), ids, 1, 1, sink, None) == INVALID  # misaligned pool
+    assert f(None, ids, 1, 1, 0, sink, None) == INVALID
+    assert f(pool, None, 1, 1, 0, sink, None) == INVALID
+    assert f(pool, ids, 1, 1, 0, None, None) == INVALID
+    assert f(ctypes.c_void_p(0x10010), ids, 1, 1, 0, sink, None) == INVALID  # misaligned pool
     assert b"aligned" in lib.pkv_last_error()
-    assert f(pool, ids, -1, 1, sink, None) == INVALID
-    assert f(pool, ids, 1, 0, sink, None) == INVALID
-    assert f(pool, ids, 1, 65537, sink, None) == INVALID
-    assert f(pool, ids, 0, 1, sink, None) == OK  # nothing to read: no launch
+    assert f(pool, ids, -1, 1, 0, sink, None) == INVALID
+    assert f(pool, ids, 1, 0, 0, sink, None) == INVALID
+    assert f(pool, ids, 1, 65537, 0, sink, None) == INVALID
+    assert f(pool, ids, 1, 1, 2, sink, None) == INVALID
+    assert b"streaming" in lib.pkv_last_error()
+    assert f(pool, ids, 0, 1, 0, sink, None) == OK  # nothing to read: no launch
+    assert f(pool, ids, 0, 1, 1, sink, None) == OK
+
+
+MIB = 1 << 20
+
+
+@pytest.mark.parametrize("kv,per_token", [(F32, 8 * 128), (BF16, 4 * 128), (I8, 2 * 128 + 8),
+                                          (FP8, 2 * 128 + 8), (E5M2, 2 * 128 + 8), (I4, 128 + 8)])
+def test_streams_cache_threshold(lib, kv, per_token):
+    """The non-temporal hint is taken exactly when the pool (K + V codes and
+    scales of every token slot of every block) exceeds 512 MiB."""
+    f = lib.pkv_paged_attention_streams_cache
+    Hkv, bs, D = 8, 16, 128
+    per_block = Hkv * bs * per_token
+    at = (512 * MIB) // per_block  # largest pool not above the threshold
+    assert f(at, Hkv, bs, D, kv) == 0
+    assert f(at + 1, Hkv, bs, D, kv) == 1
+    # the same byte count laid out with other sizes gives the same answer
+    assert f(2 * at, Hkv // 2, bs, D, kv) == 0 and f(2 * at + 2, Hkv // 2, bs, D, kv) == 1
+    assert f(at + 1, Hkv, bs, D, kv) == f((at + 1) // 2 + 1, Hkv, 2 * bs, D, kv)
+
+
+@pytest.mark.parametrize("args", [(-1, 8, 16, 128, BF16), (1 << 30, 0, 16, 128, BF16),
+                                  (1 << 30, 8, 8, 128, BF16), (1 << 30, 8, 16, 96, BF16),
+                                  (1 << 30, 8, 16, 128, 99)])
+def test_streams_cache_invalid_sizes(lib, args):
+    assert lib.pkv_paged_attention_streams_cache(*args) == 0
+
+
+@pytest.mark.parametrize("name,num_blocks,Hkv,kv,expect", [
+    ("tiny_f32", 32, 4, F32, 0), ("mha7b_bf16", 4608, 32, BF16, 1), ("gqa70b_bf16", 34658, 8, BF16, 1),
+    ("prefix_bf16_bs16", 5407, 8, BF16, 0), ("int8_gqa70b", 36864, 8, I8, 1), ("int4_gqa70b", 36864, 8, I4, 1)])
+def test_streams_cache_workloads(lib, name, num_blocks, Hkv, kv, expect):
+    """The benchmark workloads' pools (block size 16; head_dim 64 for the
+    tiny fp32 one, 128 otherwise): the 7B and 70B-shaped ones (over 1 GiB)
+    stream; the 256-sequence shared-prefix pool (about 340 MiB) and the tiny
+    one do not."""
+    D = 64 if kv == F32 else 128
+    assert lib.pkv_paged_attention_streams_cache(num_blocks, Hkv, 16, D, kv) == expect
 
 
 def _cascade(lib, **over):

@@ -12,15 +12,16 @@ import paged_kv_cache_29_amd as pkv
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("streaming", [False, True])
 @pytest.mark.parametrize("ntiles,grid", [(3000, 64), (1, 1), (4096, 8), (517, 3)])
-def test_probe_reads_the_named_tiles(ntiles, grid):
+def test_probe_reads_the_named_tiles(ntiles, grid, streaming):
     rng = np.random.default_rng(ntiles)
     pool_tiles = 4096
     host = rng.integers(0, 2**32, size=pool_tiles * 1024, dtype=np.uint32)
     pool = torch.from_numpy(host.view(np.uint8)).to("cuda:0")
     ids = rng.choice(pool_tiles, size=ntiles, replace=False).astype(np.int32)
     sink = torch.zeros(grid * 256, dtype=torch.int32, device="cuda:0")
-    pkv.probe_tile_read(pool, torch.from_numpy(ids).to("cuda:0"), sink, grid)
+    pkv.probe_tile_read(pool, torch.from_numpy(ids).to("cuda:0"), sink, grid, streaming=streaming)
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(host.reshape(pool_tiles, 1024)[ids].ravel())
     assert got == want
