@@ -765,6 +765,7 @@ def main():
         "block_moves": moves,
         "kernel_source_sha": kernel_source_sha(),
         "cpu_baseline": head["cpu_baseline"],
+        **({"speculative_verify": head["speculative_verify"]} if "speculative_verify" in head else {}),
         "secondary": results[1:],
     }
     print(json.dumps(line))
